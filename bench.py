@@ -1,0 +1,258 @@
+#!/usr/bin/env python3
+"""Decode benchmark of the OSCAR INT2 KV path on one MI355X.
+
+One step = for every layer: append one token per sequence (rotate, clip,
+INT2-quantize, pack, bf16 windows) then decode attention over the mixed cache
+(q rotation, split-K INT2 flash-decode, bf16 window splits, LSE combine with
+V un-rotation).  Default workload: Qwen3-8B-shaped attention, 36 layers,
+batch 16, Hq 32, Hkv 8, head_dim 128, 32768 cached tokens per sequence, bf16
+sink 64 + recent 256, group 128, clip K 0.96 / V 0.92.  Inputs are seeded
+synthetic bf16 (N(0,1), 1% outlier channels x8) resident in HBM before timing.
+
+Prints one JSON line (rank 0, one GPU).
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import platform
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "INT2-KV decode attention tokens/s + effective KV GB/s (% HBM peak) at 32k ctx"
+HBM_PEAK_GBS = 8000.0
+
+WORKLOADS = {
+    # name: (layers, batch, Hq, Hkv, D, context, N, M, dist, outliers, v_dtype)
+    "qwen3-8b-attn-32k": (36, 16, 32, 8, 128, 32768, 64, 256, "normal", "percent", 0),
+    "qwen3-4b-attn-16k": (36, 1, 32, 8, 128, 16384, 512, 2048, "normal", "percent", 0),
+    "qwen3-32b-attn-128k": (64, 8, 64, 8, 128, 131072, 64, 256, "student_t3", "none", 0),
+    "wide-d512-attn-64k": (48, 4, 16, 8, 512, 65536, 512, 2048, "normal", "percent", 0),
+    "wide-d512-attn-64k-vbf16": (48, 4, 16, 8, 512, 65536, 512, 2048, "normal", "percent", 1),
+}
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def fill_layer_device(cache, layer, B, Hkv, D, T, seed=0, dist="normal", outliers="percent", chunk=4096):
+    """Append T synthetic tokens per sequence to `layer`, generated on the device."""
+    import torch
+    import synth
+    mask = torch.from_numpy(synth.outlier_mask(D, Hkv, seed, layer, outliers)).cuda()
+    t = 0
+    ci = 0
+    while t < T:
+        n = min(chunk, T - t)
+        k = synth.device_kv_fill((B, n, Hkv, D), synth.seed_of(seed, layer, "k", 1000 + ci), "cuda", mask, dist)
+        v = synth.device_kv_fill((B, n, Hkv, D), synth.seed_of(seed, layer, "v", 1000 + ci), "cuda", mask, dist)
+        cache.append(layer, k, v)
+        t += n
+        ci += 1
+    return mask
+
+
+def int2_bytes_per_token_head(D):
+    return D // 4 + 4 * (D // 128)
+
+
+def algorithmic_kv_bytes(B, Hkv, D, T, N, M, v_bf16):
+    """Bytes one decode-attention call must read: INT2 K (+ INT2 or bf16 V) for
+    the INT2 positions and bf16 K and V for the W = min(T, N+M) window tokens."""
+    W = min(T, N + M)
+    bk = int2_bytes_per_token_head(D)
+    bv = 2 * D if v_bf16 else bk
+    return B * Hkv * ((T - W) * (bk + bv) + W * 4 * D)
+
+
+def cpu_baseline(wl, budget_s=15.0):
+    """The oracle, as it stands, on a bounded sample of the workload: one
+    (layer, sequence) unit = append of one token + decode attention over the
+    full context for all query heads of that sequence."""
+    import oracle as orc
+    import synth
+    L, B, Hq, Hkv, D, T, N, M, dist, outl, vdt = wl
+    try:
+        from threadpoolctl import threadpool_info
+        blas_threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        blas_threads = os.cpu_count() or 1
+    cfg = orc.OracleConfig(num_layers=1, batch=1, num_q_heads=Hq, num_kv_heads=Hkv, head_dim=D,
+                           sink_tokens=N, recent_tokens=M, v_dtype=vdt)
+    rk = synth.rotations(1, D, 0, "rot_k")
+    rv = synth.rotations(1, D, 0, "rot_v")
+    c = orc.OracleKVCache(cfg, rk, rv)
+    mask = synth.outlier_mask(D, Hkv, 0, 0, outl)
+    step = 4096
+    t = 0
+    while t < T:
+        n = min(step, T - t)
+        c.append(0, synth.kv_bits(1, n, Hkv, D, 0, 0, "k", mask, dist, 2000 + t),
+                 synth.kv_bits(1, n, Hkv, D, 0, 0, "v", mask, dist, 2000 + t))
+        t += n
+    units = 0
+    t0 = time.perf_counter()
+    while True:
+        kb = synth.kv_bits(1, 1, Hkv, D, 0, 0, "k", mask, dist, 9000 + units)
+        vb = synth.kv_bits(1, 1, Hkv, D, 0, 0, "v", mask, dist, 9000 + units)
+        c.append(0, kb, vb)
+        q = synth.q_bits(1, Hq, Hkv, D, 0, 0, mask, dist, units)
+        c.attend(0, q)
+        units += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s or units >= 64:
+            break
+    per_unit = el / units
+    tok_s = 1.0 / (L * per_unit)          # B sequences x L layers units per B tokens
+    cpu = platform.processor() or ""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    cpu = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return {"value": tok_s, "unit": "tokens/s", "cores": int(blas_threads), "kind": "oracle",
+            "sample": f"{units} (layer, sequence) units of append(1 token) + decode attention at "
+                      f"context {T}+, {el:.1f} s; tokens/s = 1/(layers x s per unit); cpu {cpu}; "
+                      f"host cores {os.cpu_count()}"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=64)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="qwen3-8b-attn-32k", choices=sorted(WORKLOADS))
+    ap.add_argument("--splits", type=int, default=0, help="force INT2 splits (0 = auto)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=15.0)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this path runs on one GPU: the cache of one GPU's share is "
+                                   "benchmarked at N=1; multi-GPU sharding is a design note, not built"}))
+        sys.exit(2)
+
+    import torch
+    import synth
+    from bit_attention_oscar_amd import oscar_kv as ok
+
+    wl = WORKLOADS[args.workload]
+    L, B, Hq, Hkv, D, T0, N, M, dist, outl, vdt = wl
+    W, K = args.warmup, args.steps
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    log(f"workload {args.workload}: L={L} B={B} Hq={Hq} Hkv={Hkv} D={D} T0={T0} N={N} M={M}")
+    rk = synth.rotations(L, D, 0, "rot_k")
+    rv = synth.rotations(L, D, 0, "rot_v")
+    cap = T0 + W + K + 64
+    cache = ok.KVCache(L, B, Hq, Hkv, D, cap, N, M, 128, 0.96, 0.92, ok.KV_INT2, vdt, rk, rv, 0)
+    if args.splits:
+        cache.set_num_splits(args.splits)
+    log(f"cache {cache.device_bytes() / 2**30:.2f} GiB; filling {T0} tokens x {L} layers")
+    t_fill = time.perf_counter()
+    masks = []
+    for l in range(L):
+        masks.append(fill_layer_device(cache, l, B, Hkv, D, T0, seed=0, dist=dist, outliers=outl))
+    torch.cuda.synchronize()
+    log(f"filled in {time.perf_counter() - t_fill:.1f} s")
+
+    # per-step inputs, resident in HBM before timing
+    steps_total = W + K
+    g = torch.Generator(device=dev)
+    g.manual_seed(synth.seed_of(0, 0, "step"))
+    q_all = torch.randn((steps_total, L, B, Hq, D), generator=g, device=dev).to(torch.bfloat16)
+    k_all = torch.randn((steps_total, L, B, 1, Hkv, D), generator=g, device=dev).to(torch.bfloat16)
+    v_all = torch.randn((steps_total, L, B, 1, Hkv, D), generator=g, device=dev).to(torch.bfloat16)
+    out = torch.empty((B, Hq, D), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def step(i):
+        for l in range(L):
+            cache.append(l, k_all[i, l], v_all[i, l], stream)
+            cache.decode_attn(l, q_all[i, l], out, ok.OUT_F32, 0.0, stream)
+
+    for i in range(W):
+        step(i)
+    torch.cuda.synchronize()
+    log("warmup done")
+
+    # timed region: K steps, HIP events on the library's stream
+    cache.profile_enable(True)
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter()
+    e0.record(stream)
+    for i in range(W, W + K):
+        step(i)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_wall
+    ms_total = e0.elapsed_time(e1)
+    k_ms, k_n = cache.profile_read(0)
+    call_ms, call_n = cache.profile_read(1)
+    app_ms, app_n = cache.profile_read(2)
+    cache.profile_enable(False)
+    ms_per_step = ms_total / K
+    tokens_s = B * K / (ms_total / 1e3)
+    log(f"{K} steps: {ms_total:.2f} ms (wall {wall * 1e3:.1f} ms), {ms_per_step:.3f} ms/step")
+
+    # bytes: every layer call attends over T = T0 + W + i + 1 tokens at step i
+    Ts = [T0 + W + i + 1 for i in range(K)]
+    kv_bytes_calls = sum(algorithmic_kv_bytes(B, Hkv, D, T, N, M, vdt == 1) for T in Ts) * L
+    kv_gbs = kv_bytes_calls / (call_ms / 1e3) / 1e9 if call_ms > 0 else None
+    # dominant kernel: INT2 split-K, INT2 positions only
+    int2_bytes = sum(B * Hkv * max(0, T - N - M) * (2 * int2_bytes_per_token_head(D) if vdt == 0 else
+                                                     int2_bytes_per_token_head(D) + 2 * D) for T in Ts) * L
+    roof = None
+    if k_n > 0:
+        avg_ms = k_ms / k_n
+        per_launch = int2_bytes / k_n
+        achieved = per_launch / (avg_ms / 1e3) / 1e9
+        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                "kernel": "decode_mfma_kernel", "avg_launch_us": round(avg_ms * 1e3, 3),
+                "algorithmic_bytes_per_launch": int(per_launch)}
+    res = {
+        "metric": METRIC,
+        "value": round(tokens_s, 2),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": W,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16",
+        "data": "synthetic",
+        "config": {"workload": args.workload, "layers": L, "batch": B, "q_heads": Hq, "kv_heads": Hkv,
+                   "head_dim": D, "context": T0, "sink": N, "recent": M, "group": 128,
+                   "k_clip": 0.96, "v_clip": 0.92, "v_cache": "bf16" if vdt else "int2",
+                   "parallelism": "none (1 GPU)"},
+        "kv_gbps": None if kv_gbs is None else round(kv_gbs, 1),
+        "kv_hbm_frac": None if kv_gbs is None else round(kv_gbs / HBM_PEAK_GBS, 4),
+        "decode_attn_us_per_call": round(call_ms / max(call_n, 1) * 1e3, 3),
+        "append_us_per_call": round(app_ms / max(app_n, 1) * 1e3, 3),
+        "roofline": roof,
+    }
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle on a bounded sample")
+        res["cpu_baseline"] = cpu_baseline(wl, args.cpu_budget)
+    print(json.dumps(res), flush=True)
+    cache.close()
+
+
+if __name__ == "__main__":
+    main()

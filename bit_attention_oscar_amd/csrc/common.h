@@ -1,0 +1,153 @@
+// Internal definitions shared by the host library and the gfx950 kernels:
+// storage layout of the cache planes, number-format helpers, launcher
+// declarations.  Nothing here is part of the C ABI.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace oscar {
+
+constexpr int kGroup = 128;           // quantization group along head_dim
+constexpr int kTile = 64;             // tokens per decode tile / V storage block
+constexpr int kMaxSplits = 256;       // partial-result slots per (sequence, head)
+constexpr int kMaxGq = 16;            // query heads per kv head handled by the VALU kernel
+
+// ---------------------------------------------------------------------------
+// Storage layout (per layer; b = sequence, h = kv head, t = position, d = dim)
+//
+//  K INT2 codes : u8 [B][Hkv][cap][D/4], canonical packing (code d at byte
+//                 d/4, bits 2*(d%4)).  A decode lane owns one token row.
+//  K/V meta     : u32 [B][Hkv][cap][D/128] = fp16 scale (low) | fp16 zero (high)
+//  V INT2 codes : tiled for the PV matrix-core operand.  For every 64-token
+//                 block and every 128-wide slice of head_dim there is a 2 KiB
+//                 tile = 64 lane records of 32 bytes.  Within a slice,
+//                 dim ds = d % 128 belongs to lane 4*((ds%64)/4) + ds%4 and to
+//                 half hh = ds/64; token tb = t % 64 lives in 32-bit word tb/8
+//                 of that record at bit
+//                   16*(tb%2) + 8*hh + 2*(2*((tb/4)%2) + (tb/2)%2).
+//                 One AND mask of a word yields two fp16 operands (tokens tb,
+//                 tb^1) scaled by a power of four that depends only on (tb/2)%4.
+//  sink / ring  : bf16 [B][Hkv][N][D] and [B][Hkv][M][D]; position t of the
+//                 recent window lives in ring slot t % M.
+//  BF16 plane   : bf16 [B][Hkv][cap][D] for every position.
+//  V scale max  : f32 [B][Hkv], running max of stored V scales (the decode
+//                 kernel sizes its fp16 operand range from it).
+// cap is max_context rounded up to a multiple of 64.
+// ---------------------------------------------------------------------------
+
+__host__ __device__ inline size_t kcode_offset(int bh, int cap, int t, int D) {
+  return ((size_t)bh * cap + t) * (size_t)(D / 4);
+}
+
+__host__ __device__ inline size_t meta_offset(int bh, int cap, int t, int D) {
+  return ((size_t)bh * cap + t) * (size_t)(D / kGroup);
+}
+
+// byte offset and bit of the 2-bit V code (t, d) in the tiled layout
+__host__ __device__ inline size_t vcode_byte(int bh, int cap, int t, int d, int D, int* bit) {
+  const int tb = t & 63, ds = d & 127, slice = d >> 7;
+  const int hh = ds >> 6;
+  const int lane = 4 * ((ds & 63) >> 2) + (ds & 3);
+  const int bitpos = 16 * (tb & 1) + 8 * hh + 2 * (2 * ((tb >> 2) & 1) + ((tb >> 1) & 1));
+  *bit = bitpos & 7;
+  const size_t tile = ((size_t)bh * (cap / kTile) + (t >> 6)) * (size_t)(D / 128) + slice;
+  return tile * 2048 + (size_t)lane * 32 + (size_t)(tb >> 3) * 4 + (bitpos >> 3);
+}
+
+__host__ __device__ inline size_t row_offset(int bh, int rows, int t, int D) {
+  return ((size_t)bh * rows + t) * (size_t)D;
+}
+
+// ---------------------------------------------------------------------------
+// number formats
+// ---------------------------------------------------------------------------
+
+__host__ __device__ inline float bf16_to_f32(uint16_t b) {
+  union { uint32_t u; float f; } v;
+  v.u = (uint32_t)b << 16;
+  return v.f;
+}
+
+// float32 -> bf16, round to nearest even (finite inputs)
+__host__ __device__ inline uint16_t f32_to_bf16(float f) {
+  union { uint32_t u; float f; } v;
+  v.f = f;
+  const uint32_t lsb = (v.u >> 16) & 1u;
+  return (uint16_t)((v.u + 0x7FFFu + lsb) >> 16);
+}
+
+// ---------------------------------------------------------------------------
+// launch arguments
+// ---------------------------------------------------------------------------
+
+struct PlaneDev {
+  uint8_t* codes;     // INT2 codes (K canonical or V tiled); null for BF16 planes
+  uint32_t* meta;     // fp16 scale | fp16 zero per group
+  uint16_t* sink;     // bf16 [B][Hkv][N][D]
+  uint16_t* ring;     // bf16 [B][Hkv][M][D]
+  uint16_t* full;     // bf16 [B][Hkv][cap][D]; BF16 planes only
+  float* smax;        // [B][Hkv] running max of stored scales (V only)
+  float clip;
+  int is_bf16;
+  int tiled;          // 1 for the V code layout
+};
+
+struct AppendArgs {
+  PlaneDev k, v;
+  const uint16_t* kin;    // bf16 [batch][n_new][Hkv][D]
+  const uint16_t* vin;
+  const float* rk;        // fp32 [D][D] for this layer
+  const float* rv;
+  float* kdump;           // optional fp32 [batch][n_new][Hkv][D]
+  float* vdump;
+  int batch, n_new, Hkv, D, cap, N, M, T_old, T_new;
+};
+
+struct QRotArgs {
+  const uint16_t* q;      // bf16 [B][Hq][D]
+  const float* rk;        // fp32 [D][D]
+  float* qrot;            // fp32 [B][Hq][D], q @ R_K * scale * log2(e)
+  float* qaux;            // [B][Hq][8]: per-group sums of qrot (4), cK, 0...
+  uint16_t* qswz;         // fp16 operand registers for the matrix-core kernel
+  int B, Hq, Hkv, D;
+  float scale_log2;
+  int want_swz;
+};
+
+struct SegPlan {           // up to two token segments, split into `splits` chunks
+  int a0, b0, a1, b1;      // [a0, b0) then [a1, b1) (either may be empty)
+  int splits;              // blocks along y
+  int chunk;               // tokens of the concatenated segments per split (multiple of 64)
+  int slot0;               // first partial slot written by split 0
+};
+
+struct DecodeArgs {
+  PlaneDev k, v;
+  const float* qrot;
+  const float* qaux;
+  const uint16_t* qswz;
+  float* partials;         // [B][Hq][kMaxSplits][D+2]
+  int Hq, Hkv, D, cap, N, M, T;
+  SegPlan plan;
+};
+
+struct CombineArgs {
+  const float* partials;
+  const float* rvT;        // fp32 [D][D]: rvT[e][d] = R_V[d][e]
+  void* out;
+  int out_dtype;
+  int B, Hq, D, nslots;
+};
+
+// launchers (defined in the .hip files); return hipGetLastError()
+hipError_t launch_append(const AppendArgs& a, hipStream_t s);
+hipError_t launch_quantize_rows(const float* x, int rows, int D, float clip, uint8_t* codes,
+                                uint32_t* meta, hipStream_t s);
+hipError_t launch_qrot(const QRotArgs& a, hipStream_t s);
+hipError_t launch_decode_valu(const DecodeArgs& a, int B, hipStream_t s);
+hipError_t launch_decode_mfma(const DecodeArgs& a, int B, int waves_per_block, hipStream_t s);
+hipError_t launch_combine(const CombineArgs& a, hipStream_t s);
+hipError_t launch_export_vcodes(const uint8_t* tiled, uint8_t* canon, int BH, int cap, int T, int D,
+                                hipStream_t s);
+
+}  // namespace oscar

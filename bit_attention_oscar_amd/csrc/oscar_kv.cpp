@@ -1,0 +1,568 @@
+// Host side of the OSCAR INT2 KV library: argument validation, device memory,
+// the split plan of decode attention and the kernel launches.  Every launch
+// goes onto the caller's stream; nothing on the append/decode path
+// synchronises the device.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdio>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "../../include/oscar_kv.h"
+#include "common.h"
+
+using namespace oscar;
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int code, const std::string& msg) {
+  g_last_error = msg;
+  return code;
+}
+
+#define HIP_TRY(expr)                                                                   \
+  do {                                                                                  \
+    hipError_t _e = (expr);                                                             \
+    if (_e != hipSuccess)                                                               \
+      return fail(OSCAR_ERR_HIP, std::string(#expr) + ": " + hipGetErrorString(_e));    \
+  } while (0)
+
+struct Plane {
+  uint8_t* codes = nullptr;
+  uint32_t* meta = nullptr;
+  uint16_t* sink = nullptr;
+  uint16_t* ring = nullptr;
+  uint16_t* full = nullptr;
+  float* smax = nullptr;
+};
+
+struct Layer {
+  Plane k, v;
+  int32_t T = 0;
+  int32_t batch = 0;
+};
+
+int round_up(int x, int m) { return (x + m - 1) / m * m; }
+
+// HIP event pairs recorded around one kernel class (see oscar_kv_profile_*).
+struct ProfClass {
+  std::vector<std::pair<hipEvent_t, hipEvent_t>> ev;
+  size_t used = 0;
+};
+constexpr size_t kProfMax = 8192;
+
+}  // namespace
+
+struct oscar_kv {
+  oscar_kv_config cfg{};
+  int cap = 0;
+  std::vector<Layer> layers;
+  std::vector<void*> allocations;
+  float* rk = nullptr;     // [L][D][D]
+  float* rv = nullptr;     // [L][D][D]
+  float* rvT = nullptr;    // [L][D][D] transposed
+  float* qrot = nullptr;   // [B][Hq][D]
+  float* qaux = nullptr;   // [B][Hq][8]
+  uint16_t* qswz = nullptr;  // [B][Hkv][64][32]
+  float* partials = nullptr; // [B][Hq][kMaxSplits][D+2]
+  size_t bytes = 0;
+  int32_t forced_splits = 0;
+  int32_t decode_impl = 0;
+  int32_t mfma_waves = 4;
+  bool prof_on = false;
+  ProfClass prof[3];
+};
+
+namespace {
+
+int dev_alloc(oscar_kv* kv, void** p, size_t bytes) {
+  if (bytes == 0) {
+    *p = nullptr;
+    return OSCAR_OK;
+  }
+  hipError_t e = hipMalloc(p, bytes);
+  if (e != hipSuccess) {
+    *p = nullptr;
+    return fail(e == hipErrorOutOfMemory ? OSCAR_ERR_OUT_OF_MEMORY : OSCAR_ERR_HIP,
+                std::string("hipMalloc(") + std::to_string(bytes) + "): " + hipGetErrorString(e));
+  }
+  kv->allocations.push_back(*p);
+  kv->bytes += bytes;
+  return OSCAR_OK;
+}
+
+void free_all(oscar_kv* kv) {
+  for (void* p : kv->allocations) (void)hipFree(p);
+  kv->allocations.clear();
+  for (auto& pc : kv->prof) {
+    for (auto& e : pc.ev) {
+      (void)hipEventDestroy(e.first);
+      (void)hipEventDestroy(e.second);
+    }
+    pc.ev.clear();
+    pc.used = 0;
+  }
+}
+
+// returns the slot recorded before a launch of class c, or -1 when not profiling
+long prof_begin(oscar_kv* kv, int c, hipStream_t s) {
+  if (!kv->prof_on) return -1;
+  ProfClass& pc = kv->prof[c];
+  if (pc.used >= kProfMax) return -1;
+  if (pc.used == pc.ev.size()) {
+    hipEvent_t a, b;
+    if (hipEventCreate(&a) != hipSuccess) return -1;
+    if (hipEventCreate(&b) != hipSuccess) {
+      (void)hipEventDestroy(a);
+      return -1;
+    }
+    pc.ev.emplace_back(a, b);
+  }
+  if (hipEventRecord(pc.ev[pc.used].first, s) != hipSuccess) return -1;
+  return (long)pc.used;
+}
+
+void prof_end(oscar_kv* kv, int c, long slot, hipStream_t s) {
+  if (slot < 0) return;
+  ProfClass& pc = kv->prof[c];
+  if (hipEventRecord(pc.ev[(size_t)slot].second, s) == hipSuccess) pc.used = (size_t)slot + 1;
+}
+
+int validate_config(const oscar_kv_config* c) {
+  if (!c) return fail(OSCAR_ERR_INVALID_ARG, "config is NULL");
+  if (c->num_layers <= 0) return fail(OSCAR_ERR_INVALID_ARG, "num_layers must be > 0");
+  if (c->max_batch <= 0) return fail(OSCAR_ERR_INVALID_ARG, "max_batch must be > 0");
+  if (c->num_kv_heads <= 0 || c->num_q_heads <= 0)
+    return fail(OSCAR_ERR_INVALID_ARG, "head counts must be > 0");
+  if (c->num_q_heads % c->num_kv_heads != 0)
+    return fail(OSCAR_ERR_INVALID_ARG, "num_q_heads must be a multiple of num_kv_heads");
+  if (c->num_q_heads / c->num_kv_heads > kMaxGq)
+    return fail(OSCAR_ERR_UNSUPPORTED, "more than 16 query heads per kv head");
+  if (c->group_size != kGroup) return fail(OSCAR_ERR_UNSUPPORTED, "group_size must be 128");
+  if (c->head_dim != 128 && c->head_dim != 512)
+    return fail(OSCAR_ERR_UNSUPPORTED, "head_dim must be 128 or 512");
+  if (c->max_context <= 0) return fail(OSCAR_ERR_INVALID_ARG, "max_context must be > 0");
+  if (c->sink_tokens < 0 || c->recent_tokens < 0)
+    return fail(OSCAR_ERR_INVALID_ARG, "window sizes must be >= 0");
+  if (!(c->k_clip > 0.0f && c->k_clip <= 1.0f) || !(c->v_clip > 0.0f && c->v_clip <= 1.0f))
+    return fail(OSCAR_ERR_INVALID_ARG, "clip ratios must be in (0, 1]");
+  if ((c->k_dtype != OSCAR_KV_INT2 && c->k_dtype != OSCAR_KV_BF16) ||
+      (c->v_dtype != OSCAR_KV_INT2 && c->v_dtype != OSCAR_KV_BF16))
+    return fail(OSCAR_ERR_INVALID_ARG, "unknown kv dtype");
+  if ((long long)c->max_batch * c->num_q_heads > (1 << 30))
+    return fail(OSCAR_ERR_INVALID_ARG, "batch x heads too large");
+  return OSCAR_OK;
+}
+
+int alloc_plane(oscar_kv* kv, Plane* p, oscar_kv_dtype dt, bool is_v) {
+  const auto& c = kv->cfg;
+  const size_t BH = (size_t)c.max_batch * c.num_kv_heads;
+  const size_t D = c.head_dim;
+  int rc;
+  if (dt == OSCAR_KV_BF16) {
+    rc = dev_alloc(kv, (void**)&p->full, BH * kv->cap * D * 2);
+    return rc;
+  }
+  if ((rc = dev_alloc(kv, (void**)&p->codes, BH * kv->cap * (D / 4)))) return rc;
+  if ((rc = dev_alloc(kv, (void**)&p->meta, BH * kv->cap * (D / kGroup) * 4))) return rc;
+  if ((rc = dev_alloc(kv, (void**)&p->sink, BH * c.sink_tokens * D * 2))) return rc;
+  if ((rc = dev_alloc(kv, (void**)&p->ring, BH * c.recent_tokens * D * 2))) return rc;
+  // stale metadata of unwritten positions must be finite: zero it once
+  if (p->meta) HIP_TRY(hipMemset(p->meta, 0, BH * kv->cap * (D / kGroup) * 4));
+  if (p->codes) HIP_TRY(hipMemset(p->codes, 0, BH * kv->cap * (D / 4)));
+  if (is_v) {
+    if ((rc = dev_alloc(kv, (void**)&p->smax, BH * sizeof(float)))) return rc;
+    HIP_TRY(hipMemset(p->smax, 0, BH * sizeof(float)));
+  }
+  return OSCAR_OK;
+}
+
+PlaneDev plane_dev(const oscar_kv* kv, const Plane& p, bool is_v) {
+  PlaneDev d{};
+  d.codes = p.codes;
+  d.meta = p.meta;
+  d.sink = p.sink;
+  d.ring = p.ring;
+  d.full = p.full;
+  d.smax = p.smax;
+  d.clip = is_v ? kv->cfg.v_clip : kv->cfg.k_clip;
+  d.is_bf16 = (is_v ? kv->cfg.v_dtype : kv->cfg.k_dtype) == OSCAR_KV_BF16;
+  d.tiled = is_v ? 1 : 0;
+  return d;
+}
+
+int check_layer(const oscar_kv* kv, int32_t layer) {
+  if (!kv) return fail(OSCAR_ERR_INVALID_ARG, "handle is NULL");
+  if (layer < 0 || layer >= kv->cfg.num_layers)
+    return fail(OSCAR_ERR_INVALID_ARG, "layer " + std::to_string(layer) + " out of range");
+  return OSCAR_OK;
+}
+
+int do_append(oscar_kv* kv, int32_t layer, const void* k, const void* v, int32_t batch, int32_t n_new,
+              float* kdump, float* vdump, hipStream_t stream) {
+  int rc = check_layer(kv, layer);
+  if (rc) return rc;
+  if (!k || !v) return fail(OSCAR_ERR_INVALID_ARG, "k/v pointer is NULL");
+  if (batch <= 0 || batch > kv->cfg.max_batch)
+    return fail(OSCAR_ERR_INVALID_ARG, "batch must be in [1, max_batch]");
+  if (n_new <= 0) return fail(OSCAR_ERR_INVALID_ARG, "n_new must be > 0");
+  Layer& L = kv->layers[layer];
+  if (L.T > 0 && batch != L.batch)
+    return fail(OSCAR_ERR_INVALID_ARG, "batch differs from the batch this layer was filled with");
+  if ((long long)L.T + n_new > kv->cfg.max_context)
+    return fail(OSCAR_ERR_CAPACITY, "append of " + std::to_string(n_new) + " tokens to " +
+                                        std::to_string(L.T) + " exceeds max_context " +
+                                        std::to_string(kv->cfg.max_context));
+  const int groups = ((L.T + n_new - 1) >> 3) - (L.T >> 3) + 1;
+  if (groups > 65535) return fail(OSCAR_ERR_INVALID_ARG, "n_new too large for one call (max 524280)");
+  HIP_TRY(hipSetDevice(kv->cfg.device));
+  AppendArgs a{};
+  a.k = plane_dev(kv, L.k, false);
+  a.v = plane_dev(kv, L.v, true);
+  a.kin = static_cast<const uint16_t*>(k);
+  a.vin = static_cast<const uint16_t*>(v);
+  const size_t DD = (size_t)kv->cfg.head_dim * kv->cfg.head_dim;
+  a.rk = kv->rk + layer * DD;
+  a.rv = kv->rv + layer * DD;
+  a.kdump = kdump;
+  a.vdump = vdump;
+  a.batch = batch;
+  a.n_new = n_new;
+  a.Hkv = kv->cfg.num_kv_heads;
+  a.D = kv->cfg.head_dim;
+  a.cap = kv->cap;
+  a.N = kv->cfg.sink_tokens;
+  a.M = kv->cfg.recent_tokens;
+  a.T_old = L.T;
+  a.T_new = L.T + n_new;
+  const long ps = prof_begin(kv, 2, stream);
+  HIP_TRY(launch_append(a, stream));
+  prof_end(kv, 2, ps, stream);
+  L.T += n_new;
+  L.batch = batch;
+  return OSCAR_OK;
+}
+
+// Split count for the INT2 range: aim for about 8 resident waves per SIMD
+// worth of blocks (256 CUs x 4 SIMDs), never more tiles than exist.
+int auto_int2_splits(int BH, int ntiles, int waves) {
+  const int target_blocks = 2048 * 4 / std::max(1, waves);
+  int s = std::max(1, target_blocks / std::max(1, BH));
+  s = std::min(s, std::max(1, ntiles / std::max(1, waves)));
+  return std::min(s, kMaxSplits - 8);
+}
+
+SegPlan make_plan(int a0, int b0, int a1, int b1, int want_splits, int slot0) {
+  SegPlan p{};
+  p.a0 = a0;
+  p.b0 = b0;
+  p.a1 = a1;
+  p.b1 = b1;
+  const int len = std::max(0, b0 - a0) + std::max(0, b1 - a1);
+  int chunk = (len + want_splits - 1) / want_splits;
+  chunk = round_up(std::max(chunk, 1), kTile);
+  p.chunk = chunk;
+  p.splits = (len + chunk - 1) / chunk;
+  p.slot0 = slot0;
+  return p;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* oscar_last_error(void) { return g_last_error.c_str(); }
+
+int oscar_kv_create(const oscar_kv_config* cfg, oscar_kv** out) {
+  if (!out) return fail(OSCAR_ERR_INVALID_ARG, "out is NULL");
+  *out = nullptr;
+  int rc = validate_config(cfg);
+  if (rc) return rc;
+  int ndev = 0;
+  HIP_TRY(hipGetDeviceCount(&ndev));
+  if (cfg->device < 0 || cfg->device >= ndev) return fail(OSCAR_ERR_INVALID_ARG, "device out of range");
+  HIP_TRY(hipSetDevice(cfg->device));
+  oscar_kv* kv = new oscar_kv();
+  kv->cfg = *cfg;
+  kv->cfg.rot_k = nullptr;
+  kv->cfg.rot_v = nullptr;
+  kv->cap = round_up(cfg->max_context, kTile);
+  kv->layers.resize(cfg->num_layers);
+  const int L = cfg->num_layers, D = cfg->head_dim;
+  const size_t DD = (size_t)D * D;
+  auto bail = [&](int code) {
+    free_all(kv);
+    delete kv;
+    return code;
+  };
+  for (int l = 0; l < L; ++l) {
+    if ((rc = alloc_plane(kv, &kv->layers[l].k, cfg->k_dtype, false))) return bail(rc);
+    if ((rc = alloc_plane(kv, &kv->layers[l].v, cfg->v_dtype, true))) return bail(rc);
+  }
+  if ((rc = dev_alloc(kv, (void**)&kv->rk, L * DD * 4))) return bail(rc);
+  if ((rc = dev_alloc(kv, (void**)&kv->rv, L * DD * 4))) return bail(rc);
+  if ((rc = dev_alloc(kv, (void**)&kv->rvT, L * DD * 4))) return bail(rc);
+  std::vector<float> rk(L * DD), rv(L * DD), rvT(L * DD);
+  for (int l = 0; l < L; ++l)
+    for (int e = 0; e < D; ++e)
+      for (int d = 0; d < D; ++d) {
+        const size_t i = l * DD + (size_t)e * D + d;
+        rk[i] = cfg->rot_k ? cfg->rot_k[i] : (e == d ? 1.0f : 0.0f);
+        rv[i] = cfg->rot_v ? cfg->rot_v[i] : (e == d ? 1.0f : 0.0f);
+      }
+  for (int l = 0; l < L; ++l)
+    for (int e = 0; e < D; ++e)
+      for (int d = 0; d < D; ++d) rvT[l * DD + (size_t)e * D + d] = rv[l * DD + (size_t)d * D + e];
+  auto up = [&](void* dst, const void* src, size_t n) { return hipMemcpy(dst, src, n, hipMemcpyHostToDevice); };
+  if (up(kv->rk, rk.data(), L * DD * 4) != hipSuccess || up(kv->rv, rv.data(), L * DD * 4) != hipSuccess ||
+      up(kv->rvT, rvT.data(), L * DD * 4) != hipSuccess)
+    return bail(fail(OSCAR_ERR_HIP, "copy of rotations failed"));
+  const size_t B = cfg->max_batch, Hq = cfg->num_q_heads, Hkv = cfg->num_kv_heads;
+  if ((rc = dev_alloc(kv, (void**)&kv->qrot, B * Hq * D * 4))) return bail(rc);
+  if ((rc = dev_alloc(kv, (void**)&kv->qaux, B * Hq * 8 * 4))) return bail(rc);
+  if ((rc = dev_alloc(kv, (void**)&kv->qswz, B * Hkv * 64 * 32 * 2))) return bail(rc);
+  if ((rc = dev_alloc(kv, (void**)&kv->partials, B * Hq * kMaxSplits * (D + 2) * 4))) return bail(rc);
+  if (hipDeviceSynchronize() != hipSuccess) return bail(fail(OSCAR_ERR_HIP, "device sync after create failed"));
+  *out = kv;
+  g_last_error.clear();
+  return OSCAR_OK;
+}
+
+int oscar_kv_destroy(oscar_kv* kv) {
+  if (!kv) return OSCAR_OK;
+  (void)hipSetDevice(kv->cfg.device);
+  (void)hipDeviceSynchronize();
+  free_all(kv);
+  delete kv;
+  return OSCAR_OK;
+}
+
+int oscar_kv_append(oscar_kv* kv, int32_t layer, const void* k, const void* v, int32_t batch,
+                    int32_t n_new, hipStream_t stream) {
+  return do_append(kv, layer, k, v, batch, n_new, nullptr, nullptr, stream);
+}
+
+int oscar_kv_append_dump(oscar_kv* kv, int32_t layer, const void* k, const void* v, int32_t batch,
+                         int32_t n_new, float* k_rot, float* v_rot, hipStream_t stream) {
+  if (!k_rot || !v_rot) return fail(OSCAR_ERR_INVALID_ARG, "dump pointer is NULL");
+  return do_append(kv, layer, k, v, batch, n_new, k_rot, v_rot, stream);
+}
+
+int oscar_int2_decode_attn(oscar_kv* kv, int32_t layer, const void* q, void* out, int32_t out_dtype,
+                           int32_t batch, float softmax_scale, hipStream_t stream) {
+  int rc = check_layer(kv, layer);
+  if (rc) return rc;
+  if (!q || !out) return fail(OSCAR_ERR_INVALID_ARG, "q/out pointer is NULL");
+  if (out_dtype < 0 || out_dtype > 2) return fail(OSCAR_ERR_INVALID_ARG, "unknown out_dtype");
+  const Layer& L = kv->layers[layer];
+  if (L.T == 0) return fail(OSCAR_ERR_INVALID_ARG, "layer holds no tokens");
+  if (batch != L.batch) return fail(OSCAR_ERR_INVALID_ARG, "batch differs from the layer's batch");
+  if (!(softmax_scale == softmax_scale)) return fail(OSCAR_ERR_INVALID_ARG, "softmax_scale is NaN");
+  HIP_TRY(hipSetDevice(kv->cfg.device));
+  const auto& c = kv->cfg;
+  const int D = c.head_dim, Hq = c.num_q_heads, Hkv = c.num_kv_heads, Gq = Hq / Hkv;
+  const int T = L.T, N = c.sink_tokens, M = c.recent_tokens;
+  const float scale = softmax_scale > 0.0f ? softmax_scale : 1.0f / std::sqrt((float)D);
+  const bool fast = kv->decode_impl == 0 && D == 128 && Gq == 4 && c.k_dtype == OSCAR_KV_INT2 &&
+                    c.v_dtype == OSCAR_KV_INT2;
+  const size_t DD = (size_t)D * D;
+
+  QRotArgs qa{};
+  qa.q = static_cast<const uint16_t*>(q);
+  qa.rk = kv->rk + layer * DD;
+  qa.qrot = kv->qrot;
+  qa.qaux = kv->qaux;
+  qa.qswz = kv->qswz;
+  qa.B = batch;
+  qa.Hq = Hq;
+  qa.Hkv = Hkv;
+  qa.D = D;
+  qa.scale_log2 = scale * 1.4426950408889634f;
+  qa.want_swz = fast ? 1 : 0;
+
+  DecodeArgs da{};
+  da.k = plane_dev(kv, L.k, false);
+  da.v = plane_dev(kv, L.v, true);
+  da.qrot = kv->qrot;
+  da.qaux = kv->qaux;
+  da.qswz = kv->qswz;
+  da.partials = kv->partials;
+  da.Hq = Hq;
+  da.Hkv = Hkv;
+  da.D = D;
+  da.cap = kv->cap;
+  da.N = N;
+  da.M = M;
+  da.T = T;
+  const int BH = batch * Hkv;
+
+  // token sets: sink [0, min(N,T)), recent [max(N, T-M), T), INT2 [N, T-M)
+  const int sink_end = std::min(N, T);
+  const int rec_begin = std::max(N, T - M);
+  const int int2_lo = N, int2_hi = T - M;
+  int nslots = 0;
+  const long pcall = prof_begin(kv, 1, stream);
+  HIP_TRY(launch_qrot(qa, stream));
+  if (fast) {
+    if (int2_hi > int2_lo) {
+      const int ntiles = ((int2_hi - 1) >> 6) - (int2_lo >> 6) + 1;
+      const int waves = kv->mfma_waves;
+      int s = kv->forced_splits > 0 ? std::min(kv->forced_splits, ntiles) : auto_int2_splits(BH, ntiles, waves);
+      s = std::min(s, kMaxSplits - 8);
+      SegPlan p{};
+      p.a0 = int2_lo;
+      p.b0 = int2_hi;
+      p.a1 = p.b1 = 0;
+      const int tps = (ntiles + s - 1) / s;
+      p.chunk = tps * kTile;
+      p.splits = (ntiles + tps - 1) / tps;
+      p.slot0 = 0;
+      da.plan = p;
+      const long pk = prof_begin(kv, 0, stream);
+      HIP_TRY(launch_decode_mfma(da, batch, waves, stream));
+      prof_end(kv, 0, pk, stream);
+      nslots = p.splits;
+    }
+    const int hp_len = sink_end + (T - rec_begin);
+    if (hp_len > 0) {
+      const int ws = std::max(1, std::min(8, (hp_len + 255) / 256));
+      da.plan = make_plan(0, sink_end, rec_begin, T, ws, nslots);
+      HIP_TRY(launch_decode_valu(da, batch, stream));
+      nslots += da.plan.splits;
+    }
+  } else {
+    int want = kv->forced_splits > 0 ? kv->forced_splits
+                                     : std::max(1, std::min(64, 2048 / std::max(1, BH)));
+    want = std::min(want, kMaxSplits);
+    want = std::min(want, (T + kTile - 1) / kTile);
+    da.plan = make_plan(0, T, 0, 0, want, 0);
+    HIP_TRY(launch_decode_valu(da, batch, stream));
+    nslots = da.plan.splits;
+  }
+  if (nslots > kMaxSplits) return fail(OSCAR_ERR_HIP, "internal: too many partial slots");
+  CombineArgs ca{};
+  ca.partials = kv->partials;
+  ca.rvT = kv->rvT + layer * DD;
+  ca.out = out;
+  ca.out_dtype = out_dtype;
+  ca.B = batch;
+  ca.Hq = Hq;
+  ca.D = D;
+  ca.nslots = nslots;
+  HIP_TRY(launch_combine(ca, stream));
+  prof_end(kv, 1, pcall, stream);
+  return OSCAR_OK;
+}
+
+int oscar_kv_profile_enable(oscar_kv* kv, int32_t enable) {
+  if (!kv) return fail(OSCAR_ERR_INVALID_ARG, "handle is NULL");
+  for (auto& pc : kv->prof) pc.used = 0;
+  kv->prof_on = enable != 0;
+  return OSCAR_OK;
+}
+
+int oscar_kv_profile_read(oscar_kv* kv, int32_t kernel_class, double* total_ms, int64_t* launches) {
+  if (!kv || !total_ms || !launches) return fail(OSCAR_ERR_INVALID_ARG, "NULL argument");
+  if (kernel_class < 0 || kernel_class > 2) return fail(OSCAR_ERR_INVALID_ARG, "kernel_class must be 0..2");
+  HIP_TRY(hipSetDevice(kv->cfg.device));
+  ProfClass& pc = kv->prof[kernel_class];
+  double sum = 0.0;
+  for (size_t i = 0; i < pc.used; ++i) {
+    HIP_TRY(hipEventSynchronize(pc.ev[i].second));
+    float ms = 0.0f;
+    HIP_TRY(hipEventElapsedTime(&ms, pc.ev[i].first, pc.ev[i].second));
+    sum += ms;
+  }
+  *total_ms = sum;
+  *launches = (int64_t)pc.used;
+  return OSCAR_OK;
+}
+
+int oscar_kv_length(const oscar_kv* kv, int32_t layer, int32_t* tokens) {
+  int rc = check_layer(kv, layer);
+  if (rc) return rc;
+  if (!tokens) return fail(OSCAR_ERR_INVALID_ARG, "tokens is NULL");
+  *tokens = kv->layers[layer].T;
+  return OSCAR_OK;
+}
+
+int oscar_kv_device_bytes(const oscar_kv* kv, size_t* bytes) {
+  if (!kv || !bytes) return fail(OSCAR_ERR_INVALID_ARG, "NULL argument");
+  *bytes = kv->bytes;
+  return OSCAR_OK;
+}
+
+int oscar_kv_set_num_splits(oscar_kv* kv, int32_t num_splits) {
+  if (!kv) return fail(OSCAR_ERR_INVALID_ARG, "handle is NULL");
+  if (num_splits < 0 || num_splits > kMaxSplits - 8)
+    return fail(OSCAR_ERR_INVALID_ARG, "num_splits must be in [0, 248]");
+  kv->forced_splits = num_splits;
+  return OSCAR_OK;
+}
+
+int oscar_kv_set_decode_impl(oscar_kv* kv, int32_t impl) {
+  if (!kv) return fail(OSCAR_ERR_INVALID_ARG, "handle is NULL");
+  if (impl != 0 && impl != 1) return fail(OSCAR_ERR_INVALID_ARG, "impl must be 0 or 1");
+  kv->decode_impl = impl;
+  return OSCAR_OK;
+}
+
+int oscar_kv_export(oscar_kv* kv, int32_t layer, int32_t which, void* host_codes, void* host_meta,
+                    void* host_sink, void* host_ring) {
+  int rc = check_layer(kv, layer);
+  if (rc) return rc;
+  if (which != 0 && which != 1) return fail(OSCAR_ERR_INVALID_ARG, "which must be 0 (K) or 1 (V)");
+  HIP_TRY(hipSetDevice(kv->cfg.device));
+  HIP_TRY(hipDeviceSynchronize());
+  const auto& c = kv->cfg;
+  const Layer& L = kv->layers[layer];
+  const Plane& p = which ? L.v : L.k;
+  const bool bf16 = (which ? c.v_dtype : c.k_dtype) == OSCAR_KV_BF16;
+  const int BH = c.max_batch * c.num_kv_heads, D = c.head_dim, T = L.T, cap = kv->cap;
+  if (bf16) {
+    if (host_codes && T > 0)
+      HIP_TRY(hipMemcpy2D(host_codes, (size_t)T * D * 2, p.full, (size_t)cap * D * 2, (size_t)T * D * 2, BH,
+                          hipMemcpyDeviceToHost));
+    return OSCAR_OK;
+  }
+  if (host_codes && T > 0) {
+    if (which == 0) {
+      HIP_TRY(hipMemcpy2D(host_codes, (size_t)T * (D / 4), p.codes, (size_t)cap * (D / 4), (size_t)T * (D / 4),
+                          BH, hipMemcpyDeviceToHost));
+    } else {
+      uint8_t* tmp = nullptr;
+      HIP_TRY(hipMalloc(&tmp, (size_t)BH * T * (D / 4)));
+      hipError_t e = launch_export_vcodes(p.codes, tmp, BH, cap, T, D, nullptr);
+      if (e == hipSuccess) e = hipMemcpy(host_codes, tmp, (size_t)BH * T * (D / 4), hipMemcpyDeviceToHost);
+      (void)hipFree(tmp);
+      HIP_TRY(e);
+    }
+  }
+  if (host_meta && T > 0)
+    HIP_TRY(hipMemcpy2D(host_meta, (size_t)T * (D / kGroup) * 4, p.meta, (size_t)cap * (D / kGroup) * 4,
+                        (size_t)T * (D / kGroup) * 4, BH, hipMemcpyDeviceToHost));
+  if (host_sink && c.sink_tokens > 0)
+    HIP_TRY(hipMemcpy(host_sink, p.sink, (size_t)BH * c.sink_tokens * D * 2, hipMemcpyDeviceToHost));
+  if (host_ring && c.recent_tokens > 0)
+    HIP_TRY(hipMemcpy(host_ring, p.ring, (size_t)BH * c.recent_tokens * D * 2, hipMemcpyDeviceToHost));
+  return OSCAR_OK;
+}
+
+int oscar_quantize_rows(const float* x, int32_t rows, int32_t D, int32_t G, float clip, void* codes,
+                        void* meta, hipStream_t stream) {
+  if (rows < 0) return fail(OSCAR_ERR_INVALID_ARG, "rows must be >= 0");
+  if (G != kGroup) return fail(OSCAR_ERR_UNSUPPORTED, "group size must be 128");
+  if (D != 128 && D != 512) return fail(OSCAR_ERR_UNSUPPORTED, "D must be 128 or 512");
+  if (!(clip > 0.0f && clip <= 1.0f)) return fail(OSCAR_ERR_INVALID_ARG, "clip must be in (0, 1]");
+  if (rows > 0 && (!x || !codes || !meta)) return fail(OSCAR_ERR_INVALID_ARG, "NULL pointer");
+  HIP_TRY(launch_quantize_rows(x, rows, D, clip, static_cast<uint8_t*>(codes), static_cast<uint32_t*>(meta),
+                               stream));
+  return OSCAR_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,180 @@
+/*
+ * oscar_kv.h -- C ABI of the OSCAR INT2 KV-cache library for MI355X (gfx950).
+ *
+ * What it computes (sources are web pages on OSCAR, cited by title/section):
+ *  - append: every new post-RoPE K/V vector is rotated by a per-layer
+ *    head_dim x head_dim orthogonal matrix ("OSCAR-LLAMACPP-Qwen3-4B-Thinking-
+ *    2507-INT2-KV", section "Files", note on the OSCAR rotation; "OSCAR-
+ *    RotationZoo", section "File format": one matrix per layer), clipped per
+ *    group of 128 along head_dim by a ratio (K 0.96, V 0.92: "OSCAR-RotationZoo",
+ *    "How to use", step 2 launch flags), quantized to 2-bit codes with an fp16
+ *    scale and zero per group, and packed; the first N and last M positions are
+ *    also kept in bf16 (same card, section "Run", env-var table; "OSCAR: 2-bit
+ *    KV Cache Quantization for SGLang and llama.cpp", section "What OSCAR
+ *    compresses").
+ *  - decode attention: one query per sequence attends over the mixed cache,
+ *    reading the 2-bit codes directly (fused; the Qwen3-4B card's "Run" table
+ *    and the article's section "How the offline rotation is fit"), with the
+ *    query rotated by R_K and the output rotated back by R_V^T.
+ *
+ * Conventions shared by every call:
+ *  - vectors are rows: x_rot = x @ R with R row-major fp32 [D][D];
+ *  - query head j reads kv head j / (Hq / Hkv);
+ *  - a position t of a cache holding T tokens is high precision (bf16) when
+ *    t < N or t >= T - M, and INT2 otherwise;
+ *  - per group of G values: hi = r*max, lo = r*min, s = (hi - lo)/3 (fp32,
+ *    one rounding per op), s16 = fp16(s), z16 = fp16(lo),
+ *    c = clamp(rint((x - z16)/s16), 0, 3) (ties to even; c = 0 if s16 == 0);
+ *    -0.0 is mapped to +0.0 before the group min/max and before bf16 rounding;
+ *  - the canonical 2-bit packing puts code j of a row at byte j/4, bits 2*(j%4).
+ *
+ * Ownership: the library owns every cache byte (allocated in create, freed in
+ * destroy) and private copies of R_K, R_V.  The caller owns q, k, v, out and
+ * the stream; device pointers must stay valid until the stream reaches the
+ * call.  All calls on one handle must be ordered on one stream (the handle's
+ * scratch buffers are shared by its calls); a handle is not thread-safe.
+ *
+ * Errors: every function returns an oscar_status.  Arguments are validated on
+ * the host before anything is enqueued; on an error nothing is enqueued and
+ * the cache state is unchanged.  oscar_last_error() returns a thread-local
+ * message for the last failure.  Device faults surface at the caller's next
+ * synchronisation of the stream.
+ */
+#ifndef OSCAR_KV_H
+#define OSCAR_KV_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  OSCAR_OK = 0,
+  OSCAR_ERR_INVALID_ARG = -1,
+  OSCAR_ERR_OUT_OF_MEMORY = -2,
+  OSCAR_ERR_CAPACITY = -3,
+  OSCAR_ERR_HIP = -4,
+  OSCAR_ERR_UNSUPPORTED = -5
+} oscar_status;
+
+/* Storage of one of K or V.  BF16 keeps the rotated vector in bf16 at every
+ * position (the "--cache-type-v f16" option of the Qwen3-4B card's "Run"
+ * section keeps V in high precision). */
+typedef enum { OSCAR_KV_INT2 = 0, OSCAR_KV_BF16 = 1 } oscar_kv_dtype;
+
+typedef enum { OSCAR_OUT_F32 = 0, OSCAR_OUT_BF16 = 1, OSCAR_OUT_F16 = 2 } oscar_out_dtype;
+
+typedef struct {
+  int32_t num_layers;
+  int32_t max_batch;        /* sequences per layer                             */
+  int32_t num_q_heads;      /* Hq, a multiple of num_kv_heads                   */
+  int32_t num_kv_heads;     /* Hkv                                             */
+  int32_t head_dim;         /* D: 128 or 512 (a multiple of group_size)        */
+  int32_t max_context;      /* capacity per sequence, tokens (>= 1)            */
+  int32_t sink_tokens;      /* N: first N positions also kept in bf16 (>= 0)   */
+  int32_t recent_tokens;    /* M: last M positions also kept in bf16 (>= 0)    */
+  int32_t group_size;       /* G: must be 128                                  */
+  float k_clip;             /* clip ratio r for K, in (0, 1]; pages: 0.96      */
+  float v_clip;             /* clip ratio r for V, in (0, 1]; pages: 0.92      */
+  oscar_kv_dtype k_dtype;
+  oscar_kv_dtype v_dtype;
+  const float* rot_k;       /* host fp32 [num_layers][D][D], row-major; NULL = identity */
+  const float* rot_v;       /* host fp32 [num_layers][D][D], row-major; NULL = identity */
+  int32_t device;           /* HIP device ordinal                              */
+} oscar_kv_config;
+
+typedef struct oscar_kv oscar_kv;
+
+/* Create a cache for cfg on cfg->device.  Copies the rotations, allocates
+ * every plane for max_batch x max_context tokens per layer and zeroes the
+ * metadata.  May synchronise the device (set-up, not the hot path).
+ * Errors: INVALID_ARG (bad field, NULL cfg/out), OUT_OF_MEMORY, HIP. */
+int oscar_kv_create(const oscar_kv_config* cfg, oscar_kv** out);
+
+/* Append n_new tokens to sequences 0..batch-1 of `layer` (all sequences of a
+ * layer hold the same number of tokens T_l; the first append on a layer fixes
+ * its batch, later calls must pass the same batch).
+ *   k, v: device bf16 [batch][n_new][Hkv][D], post-RoPE, un-rotated.
+ * Per token and kv head: rotate, write the bf16 window copy if the position is
+ * in the sink or among the last M positions after this append, quantize and
+ * pack (INT2 planes) or store bf16 (BF16 planes).  T_l += n_new on success.
+ * Errors: INVALID_ARG, CAPACITY (T_l + n_new > max_context), HIP. */
+int oscar_kv_append(oscar_kv* kv, int32_t layer, const void* k, const void* v,
+                    int32_t batch, int32_t n_new, hipStream_t stream);
+
+/* One decode step of attention for `layer` over all T_l cached tokens.
+ *   q:   device bf16 [batch][Hq][D], post-RoPE, un-rotated;
+ *   out: device [batch][Hq][D] of out_dtype, un-rotated (o = o' @ R_V^T);
+ *   softmax_scale <= 0 selects 1/sqrt(D).
+ * The INT2 part runs as a split-K flash-decode; the partial results are merged
+ * with a log-sum-exp combine that also undoes the V rotation.
+ * Errors: INVALID_ARG (including T_l == 0 or batch != the layer's batch), HIP. */
+int oscar_int2_decode_attn(oscar_kv* kv, int32_t layer, const void* q, void* out,
+                           int32_t out_dtype, int32_t batch, float softmax_scale,
+                           hipStream_t stream);
+
+/* Free every device allocation of the handle.  destroy(NULL) is OK. */
+int oscar_kv_destroy(oscar_kv* kv);
+
+/* Thread-local text of the last failure ("" if none). */
+const char* oscar_last_error(void);
+
+/* ---- inspection and test hooks (not part of the four-call contract) ---- */
+
+/* Tokens currently held by `layer`. */
+int oscar_kv_length(const oscar_kv* kv, int32_t layer, int32_t* tokens);
+
+/* Device bytes held by the handle. */
+int oscar_kv_device_bytes(const oscar_kv* kv, size_t* bytes);
+
+/* Force the number of INT2 splits per (sequence, kv head) used by decode
+ * attention; 0 restores the automatic choice.  Errors: INVALID_ARG. */
+int oscar_kv_set_num_splits(oscar_kv* kv, int32_t num_splits);
+
+/* Select the decode kernel: 0 = automatic (fused MFMA kernel where supported),
+ * 1 = the general VALU kernel for every shape.  Errors: INVALID_ARG. */
+int oscar_kv_set_decode_impl(oscar_kv* kv, int32_t impl);
+
+/* Copy one plane of `layer` to host memory in canonical layout, for all
+ * max_batch sequences and the T_l tokens held (synchronises the device).
+ *   which: 0 = K, 1 = V.
+ *   INT2 plane:  host_codes u8 [max_batch][Hkv][T_l][D/4] (canonical packing),
+ *                host_meta  u16 [max_batch][Hkv][T_l][D/G][2] = {s16, z16} bits,
+ *                host_sink  u16 [max_batch][Hkv][N][D] bf16 bits,
+ *                host_ring  u16 [max_batch][Hkv][M][D] bf16 bits (position t in
+ *                slot t % M).
+ *   BF16 plane:  host_codes receives u16 [max_batch][Hkv][T_l][D] bf16 bits;
+ *                the other pointers are ignored.
+ * Any pointer may be NULL to skip that part.  Errors: INVALID_ARG, HIP. */
+int oscar_kv_export(oscar_kv* kv, int32_t layer, int32_t which, void* host_codes,
+                    void* host_meta, void* host_sink, void* host_ring);
+
+/* As oscar_kv_append, and also write the fp32 rotated vectors (the quantizer
+ * inputs) to k_rot / v_rot: device fp32 [batch][n_new][Hkv][D]. */
+int oscar_kv_append_dump(oscar_kv* kv, int32_t layer, const void* k, const void* v,
+                         int32_t batch, int32_t n_new, float* k_rot, float* v_rot,
+                         hipStream_t stream);
+
+/* The append kernel's quantizer on given fp32 rows (no rotation):
+ *   x: device fp32 [rows][D]; codes: device u8 [rows][D/4] (canonical packing);
+ *   meta: device u16 [rows][D/G][2] = {s16, z16}.
+ * Errors: INVALID_ARG (D or G unsupported, NULL pointer, rows < 0), HIP. */
+int oscar_quantize_rows(const float* x, int32_t rows, int32_t D, int32_t G, float clip,
+                        void* codes, void* meta, hipStream_t stream);
+
+/* Kernel timing with HIP events recorded on the caller's stream around the
+ * launches of one kernel class: 0 = the INT2 split-K decode kernel, 1 = one
+ * whole decode-attention call (q rotation to combine), 2 = append.
+ * profile_enable(kv, 1) clears and starts recording (up to 8192 launches per
+ * class); profile_read synchronises the recorded events and returns the sum
+ * of their durations in milliseconds and the launch count. */
+int oscar_kv_profile_enable(oscar_kv* kv, int32_t enable);
+int oscar_kv_profile_read(oscar_kv* kv, int32_t kernel_class, double* total_ms, int64_t* launches);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* OSCAR_KV_H */

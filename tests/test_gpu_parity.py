@@ -1,0 +1,369 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle.
+
+Bars: codes, scales/zeros and bf16 windows bit-exact given identical fp32
+rotated inputs (and end to end where the rotation is exact in fp32);
+attention output within 2e-3 relative L2 of the oracle on the identical cache.
+"""
+import numpy as np
+import pytest
+
+import oracle as orc
+import synth
+from tests.gpu_util import (Shape, gpu_cache, inputs, make_rotations, oracle_cache, oracle_on_exported,
+                            query, rel_l2, say)
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+ATTN_TOL = 2e-3
+
+
+@pytest.fixture(scope="module")
+def ok():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from bit_attention_oscar_amd import oscar_kv
+    return oscar_kv
+
+
+def dev(bits):
+    return synth.bits_to_torch_bf16(bits, "cuda")
+
+
+# ------------------------------------------------------------------ quantizer
+
+
+def _quant_rows(D, seed):
+    g = np.random.default_rng(seed)
+    x = g.standard_normal((300, D)).astype(np.float32)
+    x[:, 3] *= 8.0
+    x[10] = 0.0                              # degenerate: constant zero
+    x[11] = 1.25                             # degenerate: constant
+    x[12] = -0.0
+    x[13] = np.abs(x[13]) + 1                # one-signed groups
+    x[14] = -np.abs(x[14]) - 1
+    x[15, ::2] = -0.0
+    x[16] *= 1e-6                            # tiny range: fp16 denormal scales
+    x[17] *= 3000.0                          # large range
+    # exact ties of (x - z)/s at k + 1/2 under r = 1: group [0, 3] -> s = 1, z = 0
+    x[18] = np.tile(np.array([0.0, 3.0, 0.5, 1.5, 2.5, 1.0, 2.0, 0.25], np.float32), D // 8)
+    return x
+
+
+def _double_rounding_min(clip, seed=0):
+    """A group minimum whose clipped value r*min rounds to a different fp16 via
+    fp32 (the specified two roundings) than straight from the exact product:
+    a quantizer that fuses the multiply into the fp16 conversion fails on it."""
+    r = np.float32(clip)
+    g = np.random.default_rng(seed)
+    while True:
+        mn = np.float32(-g.uniform(0.5, 4.0))
+        if np.float16(np.float32(r * mn)) != np.float16(float(r) * float(mn)):
+            return mn
+
+
+@pytest.mark.parametrize("D", [128, 512])
+@pytest.mark.parametrize("clip", [0.96, 0.92, 1.0])
+def test_quantize_rows_bitexact(ok, D, clip):
+    say(f"[quantize_rows] D={D} clip={clip}")
+    x = _quant_rows(D, 7 + D)
+    if clip != 1.0:
+        x[19] = np.clip(x[19], -0.4, 0.4)
+        x[19, 5::128] = _double_rounding_min(clip)
+    rows = x.shape[0]
+    xd = torch.from_numpy(x).cuda()
+    codes = torch.zeros((rows, D // 4), dtype=torch.uint8, device="cuda")
+    meta = torch.zeros((rows, D // 128, 2), dtype=torch.int16, device="cuda")
+    ok.oscar_quantize_rows(xd, rows, D, 128, clip, codes, meta)
+    torch.cuda.synchronize()
+    q = orc.quantize_rows(x, 128, clip)
+    np.testing.assert_array_equal(codes.cpu().numpy(), orc.pack_codes(q.codes))
+    m = meta.cpu().numpy().view(np.uint16)
+    np.testing.assert_array_equal(m[..., 0], q.s16.view(np.uint16))
+    np.testing.assert_array_equal(m[..., 1], q.z16.view(np.uint16))
+
+
+# ------------------------------------------------------------------ append
+
+
+def _compare_planes(gp, op, T, N, M, label):
+    """GPU export (canonical) vs oracle logical planes, bit for bit."""
+    if "full" in gp:
+        np.testing.assert_array_equal(gp["full"], op.win, err_msg=f"{label} bf16 plane")
+        return
+    np.testing.assert_array_equal(gp["codes"], orc.pack_codes(op.codes), err_msg=f"{label} codes")
+    np.testing.assert_array_equal(gp["s16"].view(np.uint16), op.s16.view(np.uint16), err_msg=f"{label} s16")
+    np.testing.assert_array_equal(gp["z16"].view(np.uint16), op.z16.view(np.uint16), err_msg=f"{label} z16")
+    for t in range(min(N, T)):
+        np.testing.assert_array_equal(gp["sink"][:, :, t], op.win[:, :, t], err_msg=f"{label} sink {t}")
+    if M > 0:
+        for t in range(max(N, T - M), T):
+            np.testing.assert_array_equal(gp["ring"][:, :, t % M], op.win[:, :, t], err_msg=f"{label} ring {t}")
+
+
+@pytest.mark.parametrize("shape,chunks", [
+    (Shape(B=2, Hq=4, Hkv=1, D=128, N=64, M=256), [1000, 1, 23, 1]),
+    (Shape(B=1, Hq=8, Hkv=2, D=128, N=5, M=7), [3, 1, 1, 9, 64, 1]),
+    (Shape(B=2, Hq=4, Hkv=2, D=512, N=16, M=40), [77, 1, 2]),
+    (Shape(B=1, Hq=4, Hkv=1, D=128, N=0, M=0), [130, 1]),
+    (Shape(B=1, Hq=4, Hkv=1, D=128, N=8, M=16, v_dtype=1), [50, 1]),
+])
+def test_append_exact_rotation_bitexact(ok, shape, chunks):
+    """Rotations exact in fp32 (bit-reversal permutation for K, a signed
+    permutation for V): codes, scales, zeros and windows bit-exact end to end."""
+    say(f"[append exact] {shape} chunks={chunks}")
+    rk, rv = make_rotations(shape, "exact")
+    T = sum(chunks)
+    k, v, _ = inputs(shape, T)
+    gc = gpu_cache(ok, shape, rk, rv, T + 5)
+    oc = oracle_cache(shape, rk, rv)
+    t = 0
+    for n in chunks:
+        gc.append(0, dev(k[:, t:t + n]), dev(v[:, t:t + n]))
+        oc.append(0, k[:, t:t + n], v[:, t:t + n])
+        t += n
+    torch.cuda.synchronize()
+    assert gc.length(0) == T
+    _compare_planes(gc.export(0, 0), oc.k[0], T, shape.N, shape.M, "K")
+    _compare_planes(gc.export(0, 1), oc.v[0], T, shape.N, shape.M, "V")
+    gc.close()
+
+
+@pytest.mark.parametrize("D", [128, 512])
+def test_append_random_rotation_dump(ok, D):
+    """Random Haar rotations: the GPU's fp32 rotated vectors are within fp32
+    accumulation error of the fp64 rotation, and the stored codes/metadata/
+    windows equal the oracle quantizer applied to those same fp32 vectors."""
+    shape = Shape(B=2, Hq=4, Hkv=2, D=D, N=3, M=9)
+    say(f"[append dump] {shape}")
+    rk, rv = make_rotations(shape, "haar")
+    T = 70
+    k, v, _ = inputs(shape, T)
+    gc = gpu_cache(ok, shape, rk, rv, T)
+    kr = torch.zeros((shape.B, T, shape.Hkv, D), dtype=torch.float32, device="cuda")
+    vr = torch.zeros_like(kr)
+    gc.append_dump(0, dev(k), dev(v), kr, vr)
+    torch.cuda.synchronize()
+    kr, vr = kr.cpu().numpy(), vr.cpu().numpy()
+    for xr, bits, R, clip, which in ((kr, k, rk[0], 0.96, 0), (vr, v, rv[0], 0.92, 1)):
+        ref = orc.rotate_f64(bits, R)
+        err = np.abs(xr - ref).max() / np.abs(ref).max()
+        say(f"  which={which} max rel rotation err {err:.2e}")
+        assert err < 1e-5
+        x32 = np.ascontiguousarray(np.transpose(xr, (0, 2, 1, 3)))            # [B, H, T, D]
+        q = orc.quantize_rows(x32.reshape(-1, D), 128, clip)
+        exp = gc.export(0, which)
+        np.testing.assert_array_equal(exp["codes"].reshape(-1, D // 4), orc.pack_codes(q.codes))
+        np.testing.assert_array_equal(exp["s16"].reshape(-1, D // 128).view(np.uint16), q.s16.view(np.uint16))
+        np.testing.assert_array_equal(exp["z16"].reshape(-1, D // 128).view(np.uint16), q.z16.view(np.uint16))
+        win = orc.f32_to_bf16_bits(orc.canonical_zero(x32))
+        np.testing.assert_array_equal(exp["sink"], win[:, :, :shape.N])
+        for t in range(max(shape.N, T - shape.M), T):
+            np.testing.assert_array_equal(exp["ring"][:, :, t % shape.M], win[:, :, t])
+    gc.close()
+
+
+# ------------------------------------------------------------------ decode
+
+
+def _decode(ok, gc, layer, qbits, impl=0, splits=0, out_dtype=0):
+    gc.set_decode_impl(impl)
+    gc.set_num_splits(splits)
+    B, Hq, D = qbits.shape
+    dt = {0: torch.float32, 1: torch.bfloat16, 2: torch.float16}[out_dtype]
+    out = torch.zeros((B, Hq, D), dtype=dt, device="cuda")
+    gc.decode_attn(layer, dev(qbits), out, out_dtype)
+    torch.cuda.synchronize()
+    return out.float().cpu().numpy()
+
+
+def _fill(ok, shape, T, rot="haar", extra=8, chunks=None):
+    rk, rv = make_rotations(shape, rot)
+    k, v, mask = inputs(shape, T)
+    gc = gpu_cache(ok, shape, rk, rv, T + extra)
+    chunks = chunks or [T]
+    t = 0
+    for n in chunks:
+        gc.append(0, dev(k[:, t:t + n]), dev(v[:, t:t + n]))
+        t += n
+    return gc, rk, rv, k, v, mask
+
+
+@pytest.mark.parametrize("impl", [0, 1])
+def test_decode_tiny_identical_cache(ok, impl):
+    """Tiny workload: 1 layer, B=1, Hq=4, Hkv=1, D=128, 1024 tokens appended,
+    then one decode step with its append; attention vs the oracle over the
+    exported cache."""
+    shape = Shape()
+    say(f"[decode tiny] impl={impl}")
+    gc, rk, rv, k, v, mask = _fill(ok, shape, 1024, chunks=[512, 512])
+    k1, v1, _ = inputs(shape, 1, chunk=1)
+    gc.append(0, dev(k1), dev(v1))
+    qb = query(shape, mask)
+    got = _decode(ok, gc, 0, qb, impl=impl)
+    want = oracle_on_exported(gc, 0, qb, shape, rk, rv)
+    e = rel_l2(got, want)
+    say(f"  rel L2 {e:.3e}")
+    assert e <= ATTN_TOL
+    gc.close()
+
+
+def test_decode_end_to_end_vs_oracle_cache(ok):
+    """Against the oracle's own cache (fp64 rotation on its side): reported;
+    code flips from fp32-vs-fp64 rotation are allowed, so the gate is looser."""
+    shape = Shape()
+    say("[decode end-to-end]")
+    T = 1025
+    gc, rk, rv, k, v, mask = _fill(ok, shape, T)
+    oc = oracle_cache(shape, rk, rv)
+    oc.append(0, k, v)
+    qb = query(shape, mask)
+    got = _decode(ok, gc, 0, qb)
+    want = oc.attend(0, qb)
+    e = rel_l2(got, want)
+    say(f"  end-to-end rel L2 {e:.3e}")
+    assert e <= 1e-2
+    # with exact rotations the two caches are identical, so the bar is the tight one
+    gc2, rk2, rv2, *_ = _fill(ok, shape, T, rot="exact")
+    oc2 = oracle_cache(shape, rk2, rv2)
+    oc2.append(0, k, v)
+    e2 = rel_l2(_decode(ok, gc2, 0, qb), oc2.attend(0, qb))
+    say(f"  end-to-end exact-rotation rel L2 {e2:.3e}")
+    assert e2 <= ATTN_TOL
+    gc.close()
+    gc2.close()
+
+
+@pytest.mark.parametrize("T,N,M", [
+    (1, 64, 256), (40, 64, 256), (320, 64, 256), (321, 64, 256), (385, 64, 256),
+    (1000, 0, 256), (1000, 64, 0), (1000, 0, 0), (777, 13, 29), (64, 0, 0), (65, 1, 0),
+])
+def test_decode_window_edges(ok, T, N, M):
+    shape = Shape(B=2, Hq=4, Hkv=2, N=N, M=M)
+    say(f"[decode edges] T={T} N={N} M={M}")
+    gc, rk, rv, k, v, mask = _fill(ok, shape, T)
+    qb = query(shape, mask)
+    want = oracle_on_exported(gc, 0, qb, shape, rk, rv)
+    for impl in (0, 1):
+        e = rel_l2(_decode(ok, gc, 0, qb, impl=impl), want)
+        say(f"  impl={impl} rel L2 {e:.3e}")
+        assert e <= ATTN_TOL
+    gc.close()
+
+
+@pytest.mark.parametrize("impl,tol", [
+    (1, 1e-5),        # VALU kernel: fp32 throughout, only summation order changes
+    (0, 2 ** -12),    # matrix-core kernel: p*s_V enters as fp16 relative to each
+                      # split's running max, so splits move its rounding points;
+                      # bounded by fp16's half-ulp
+])
+def test_split_invariance(ok, impl, tol):
+    shape = Shape(B=2, Hq=8, Hkv=2, N=64, M=256)
+    say(f"[split invariance] impl={impl}")
+    gc, rk, rv, k, v, mask = _fill(ok, shape, 5000)
+    qb = query(shape, mask)
+    ref = _decode(ok, gc, 0, qb, impl=impl, splits=1)
+    for s in (2, 7, 64, 248):
+        e = rel_l2(_decode(ok, gc, 0, qb, impl=impl, splits=s), ref)
+        say(f"  splits={s} vs 1: {e:.2e}")
+        assert e <= tol
+    want = oracle_on_exported(gc, 0, qb, shape, rk, rv)
+    assert rel_l2(ref, want) <= ATTN_TOL
+    gc.close()
+
+
+@pytest.mark.parametrize("shape", [
+    Shape(B=2, Hq=2, Hkv=2, N=8, M=16),                         # MHA
+    Shape(B=1, Hq=16, Hkv=2, N=8, M=16),                        # GQA 8
+    Shape(B=2, Hq=4, Hkv=2, D=512, N=16, M=32),                 # wide head, GQA 2
+    Shape(B=1, Hq=4, Hkv=2, D=512, N=16, M=32, v_dtype=1),      # V kept bf16
+    Shape(B=1, Hq=4, Hkv=1, D=128, N=16, M=32, v_dtype=1),
+    Shape(B=2, Hq=8, Hkv=2, D=128, N=16, M=32, dist="student_t3", outliers="none"),
+])
+def test_decode_shapes(ok, shape):
+    say(f"[decode shapes] {shape}")
+    gc, rk, rv, k, v, mask = _fill(ok, shape, 700)
+    qb = query(shape, mask)
+    want = oracle_on_exported(gc, 0, qb, shape, rk, rv)
+    e = rel_l2(_decode(ok, gc, 0, qb), want)
+    say(f"  rel L2 {e:.3e}")
+    assert e <= ATTN_TOL
+    gc.close()
+
+
+def test_gqa_equals_replicated_heads(ok):
+    """GQA with Hkv=2, Gq=4 equals MHA over K/V replicated per query head."""
+    s1 = Shape(B=1, Hq=8, Hkv=2, N=8, M=16)
+    s2 = Shape(B=1, Hq=8, Hkv=8, N=8, M=16)
+    say("[gqa replicate]")
+    rk, rv = make_rotations(s1, "haar")
+    T = 300
+    k, v, mask = inputs(s1, T)
+    g1 = gpu_cache(ok, s1, rk, rv, T)
+    g2 = gpu_cache(ok, s2, rk, rv, T)
+    g1.append(0, dev(k), dev(v))
+    g2.append(0, dev(np.repeat(k, 4, axis=2)), dev(np.repeat(v, 4, axis=2)))
+    qb = query(s1, mask)
+    a = _decode(ok, g1, 0, qb)
+    b = _decode(ok, g2, 0, qb)
+    assert rel_l2(a, b) <= ATTN_TOL
+    g1.close()
+    g2.close()
+
+
+def test_output_dtypes(ok):
+    shape = Shape(B=2, Hq=4, Hkv=1)
+    say("[out dtypes]")
+    gc, rk, rv, k, v, mask = _fill(ok, shape, 900)
+    qb = query(shape, mask)
+    f32 = _decode(ok, gc, 0, qb, out_dtype=0)
+    for od, tol in ((1, 2 ** -8), (2, 2 ** -11)):
+        o = _decode(ok, gc, 0, qb, out_dtype=od)
+        assert np.all(np.abs(o - f32) <= tol * np.abs(f32) + 1e-30)
+    gc.close()
+
+
+def test_decode_after_many_single_appends(ok):
+    """Decode loop shape: token-by-token appends crossing tile and 8-token
+    group boundaries, attention after each."""
+    shape = Shape(B=2, Hq=4, Hkv=1, N=4, M=20)
+    say("[decode loop]")
+    gc, rk, rv, k, v, mask = _fill(ok, shape, 60, extra=40)
+    kk, vv, _ = inputs(shape, 30, chunk=3)
+    for i in range(30):
+        gc.append(0, dev(kk[:, i:i + 1]), dev(vv[:, i:i + 1]))
+        if i % 7 == 0 or i == 29:
+            qb = query(shape, mask, step=i)
+            want = oracle_on_exported(gc, 0, qb, shape, rk, rv)
+            e = rel_l2(_decode(ok, gc, 0, qb), want)
+            assert e <= ATTN_TOL, (i, e)
+    gc.close()
+
+
+# ------------------------------------------------------------------ full-size samples
+
+
+@pytest.mark.slow
+def test_full_size_32k_sampled(ok):
+    """The 32k-context benchmark shape (B=16, Hq=32, Hkv=8, D=128, N=64,
+    M=256) on one layer, filled on the device, decoded in the benchmark's
+    launch configuration; sequences 0 and 15 checked against the oracle over
+    the exported cache."""
+    from bench import fill_layer_device
+    shape = Shape(B=16, Hq=32, Hkv=8, D=128, N=64, M=256, outliers="percent")
+    T = 32768
+    say("[full 32k] filling")
+    rk, rv = make_rotations(shape, "haar")
+    gc = gpu_cache(ok, shape, rk, rv, T + 64)
+    fill_layer_device(gc, 0, shape.B, shape.Hkv, shape.D, T, seed=0, dist="normal", outliers="percent")
+    mask = synth.outlier_mask(shape.D, shape.Hkv, 0, 0, "percent")
+    k1, v1, _ = inputs(shape, 1, chunk=99)
+    gc.append(0, dev(k1), dev(v1))
+    qb = query(shape, mask, step=1)
+    got = _decode(ok, gc, 0, qb)
+    for b in (0, 15):
+        want = oracle_on_exported(gc, 0, qb, shape, rk, rv, batch_idx=slice(b, b + 1))
+        e = rel_l2(got[b:b + 1], want)
+        say(f"  seq {b}: rel L2 {e:.3e}")
+        assert e <= ATTN_TOL
+    gc.close()
