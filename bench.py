@@ -137,6 +137,9 @@ def main():
     ap.add_argument("--splits", type=int, default=0, help="force INT2 splits (0 = auto)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only run the plain 16-byte copy kernel over MIB MiB ten times and print its "
+                         "bandwidth (the reference for traffic counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(json.dumps({"error": "this path runs on one GPU: the cache of one GPU's share is "
@@ -146,6 +149,23 @@ def main():
     import torch
     import synth
     from bit_attention_oscar_amd import oscar_kv as ok
+
+    if args.copy_calibration:
+        n = args.copy_calibration << 20
+        src = torch.ones(n // 4, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        ok.oscar_stream_copy(src, dst, n)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(10):
+            ok.oscar_stream_copy(src, dst, n)
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / 10
+        print(json.dumps({"copy_bytes": n, "avg_ms": ms, "read_plus_write_GBps": 2 * n / ms / 1e6,
+                          "equal": bool(torch.equal(src, dst))}))
+        return
 
     wl = WORKLOADS[args.workload]
     L, B, Hq, Hkv, D, T0, N, M, dist, outl, vdt = wl
@@ -197,6 +217,7 @@ def main():
     for i in range(W, W + K):
         step(i)
     e1.record(stream)
+    enqueue = time.perf_counter() - t_wall
     torch.cuda.synchronize()
     wall = time.perf_counter() - t_wall
     ms_total = e0.elapsed_time(e1)
@@ -206,19 +227,19 @@ def main():
     cache.profile_enable(False)
     ms_per_step = ms_total / K
     tokens_s = B * K / (ms_total / 1e3)
-    log(f"{K} steps: {ms_total:.2f} ms (wall {wall * 1e3:.1f} ms), {ms_per_step:.3f} ms/step")
+    log(f"{K} steps: {ms_total:.2f} ms (wall {wall * 1e3:.1f} ms, host enqueue {enqueue * 1e3:.1f} ms), "
+        f"{ms_per_step:.3f} ms/step")
 
     # bytes: every layer call attends over T = T0 + W + i + 1 tokens at step i
     Ts = [T0 + W + i + 1 for i in range(K)]
     kv_bytes_calls = sum(algorithmic_kv_bytes(B, Hkv, D, T, N, M, vdt == 1) for T in Ts) * L
     kv_gbs = kv_bytes_calls / (call_ms / 1e3) / 1e9 if call_ms > 0 else None
-    # dominant kernel: INT2 split-K, INT2 positions only
-    int2_bytes = sum(B * Hkv * max(0, T - N - M) * (2 * int2_bytes_per_token_head(D) if vdt == 0 else
-                                                     int2_bytes_per_token_head(D) + 2 * D) for T in Ts) * L
+    # dominant kernel: the fused decode launch (INT2 splits on matrix cores, bf16
+    # window blocks, last-block combine); it reads every KV byte of the call
     roof = None
     if k_n > 0:
         avg_ms = k_ms / k_n
-        per_launch = int2_bytes / k_n
+        per_launch = kv_bytes_calls / k_n
         achieved = per_launch / (avg_ms / 1e3) / 1e9
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
@@ -245,6 +266,7 @@ def main():
         "kv_hbm_frac": None if kv_gbs is None else round(kv_gbs / HBM_PEAK_GBS, 4),
         "decode_attn_us_per_call": round(call_ms / max(call_n, 1) * 1e3, 3),
         "append_us_per_call": round(app_ms / max(app_n, 1) * 1e3, 3),
+        "host_enqueue_ms_per_step": round(enqueue * 1e3 / K, 4),
         "roofline": roof,
     }
     if not args.no_cpu_baseline:

@@ -22,6 +22,9 @@ BUILD_DIR = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "liboscar_kv.so")
 
 SOURCES = ["append.hip", "decode.hip", "oscar_kv.cpp"]
+# per-source extra flags: the decode kernels carry -inf but never NaN (NaN
+# inputs are outside the cache contract), so max/min need no NaN quieting
+EXTRA = {"decode.hip": ["-fno-honor-nans"]}
 COMMON_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++20", "-fPIC",
     "-ffp-contract=off", "-fhip-fp32-correctly-rounded-divide-sqrt",
@@ -52,7 +55,7 @@ def build(verbose: bool = False) -> str:
     objs = []
     for src in SOURCES:
         obj = os.path.join(BUILD_DIR, src + ".o")
-        out = _run([cc, *COMMON_FLAGS, "-c", os.path.join(CSRC, src), "-o", obj])
+        out = _run([cc, *COMMON_FLAGS, *EXTRA.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj])
         if verbose and out.strip():
             print(out)
         objs.append(obj)

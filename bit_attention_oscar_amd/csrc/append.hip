@@ -64,14 +64,34 @@ __device__ inline uint32_t quant_code(float x, const GroupQ& g) {
   return (uint32_t)t;
 }
 
-// One wave per (sequence, kv head, 8-token group); blockIdx.z: 0 = K, 1 = V.
-// Lane l owns dims l + 64 i, so it also owns the V tile bytes of those dims
-// for every token of the group (the tiled layout shares bytes only among
-// tokens of one group of 8 at the same dim).
-template <int D>
-__global__ __launch_bounds__(64) void append_kernel(AppendArgs a) {
+// Canonical packing through lane shuffles: lane l holds the code of dim
+// l + 64 i; word w (dims 16w..16w+15) is OR-reduced over the 16 lanes
+// 16 (w % 4) .. + 15 of element i = w / 4 and stored by its first lane.
+template <int PER>
+__device__ inline void store_canonical(const uint32_t* code, int lane, uint8_t* row) {
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    uint32_t v = code[i] << (2 * (lane & 15));
+    v |= __shfl_xor(v, 1);
+    v |= __shfl_xor(v, 2);
+    v |= __shfl_xor(v, 4);
+    v |= __shfl_xor(v, 8);
+    if ((lane & 15) == 0) *reinterpret_cast<uint32_t*>(row + 4 * (4 * i + (lane >> 4))) = v;
+  }
+}
+
+// Block per (sequence, kv head, 8-token group); blockIdx.z: 0 = K, 1 = V.
+// NT token slots (1 for a one-token append, 8 otherwise).  The reduction over
+// e of the rotation is split across WAVES waves (partial sums added in a fixed
+// order); wave 0 then quantizes and stores.  Wave 0's lane l owns dims
+// l + 64 i, so it also owns the V tile bytes of those dims for every token of
+// the group (tiled-layout bytes are shared only among tokens of one group of
+// 8 at one dim, and one block handles the whole group).
+template <int D, int WAVES, int NT>
+__global__ __launch_bounds__(64 * WAVES) void append_kernel(AppendArgs a) {
   constexpr int PER = D / 64;
-  const int lane = threadIdx.x;
+  constexpr int EW = D / WAVES;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int bh = blockIdx.x;
   const int b = bh / a.Hkv, h = bh - (bh / a.Hkv) * a.Hkv;
   const bool isv = blockIdx.z != 0;
@@ -80,14 +100,14 @@ __global__ __launch_bounds__(64) void append_kernel(AppendArgs a) {
   const float* R = isv ? a.rv : a.rk;
   float* dump = isv ? a.vdump : a.kdump;
   const int g8 = (a.T_old >> 3) + (int)blockIdx.y;
-  const int t_lo = max(a.T_old, g8 * 8);
-  const int t_hi = min(a.T_new, g8 * 8 + 8);
+  const int t_lo = NT == 1 ? a.T_old : max(a.T_old, g8 * 8);
+  const int t_hi = NT == 1 ? a.T_old + 1 : min(a.T_new, g8 * 8 + 8);
   const int ntok = t_hi - t_lo;
 
-  __shared__ float xs[8][D];
-  __shared__ uint8_t cs[D];
-  for (int i = lane; i < 8 * D; i += 64) {
-    const int tk = i / D, d = i - tk * D;
+  __shared__ float xs[NT][D];
+  __shared__ float part[WAVES][NT][D];
+  for (int i = tid; i < NT * D; i += 64 * WAVES) {
+    const int tk = i / D, d = i - (i / D) * D;
     float v = 0.0f;
     if (tk < ntok) {
       const int t = t_lo + tk;
@@ -98,31 +118,50 @@ __global__ __launch_bounds__(64) void append_kernel(AppendArgs a) {
   }
   __syncthreads();
 
-  // x_rot[d] = sum_e x[e] * R[e][d], e ascending, fp32 fused multiply-add
-  float acc[8][PER];
+  // partial x_rot[d] = sum over this wave's e of x[e] * R[e][d], e ascending
+  float acc[NT][PER];
 #pragma unroll
-  for (int tk = 0; tk < 8; ++tk)
+  for (int tk = 0; tk < NT; ++tk)
 #pragma unroll
     for (int i = 0; i < PER; ++i) acc[tk][i] = 0.0f;
-  for (int e = 0; e < D; ++e) {
+  const float* Rw = R + (size_t)(wave * EW) * D + lane;
+#pragma unroll 8
+  for (int e = 0; e < EW; ++e) {
     float r[PER];
 #pragma unroll
-    for (int i = 0; i < PER; ++i) r[i] = R[(size_t)e * D + lane + 64 * i];
+    for (int i = 0; i < PER; ++i) r[i] = Rw[(size_t)e * D + 64 * i];
 #pragma unroll
-    for (int tk = 0; tk < 8; ++tk) {
-      const float x = xs[tk][e];
+    for (int tk = 0; tk < NT; ++tk) {
+      const float x = xs[tk][wave * EW + e];
 #pragma unroll
       for (int i = 0; i < PER; ++i) acc[tk][i] = __builtin_fmaf(x, r[i], acc[tk][i]);
     }
   }
+  if (WAVES > 1) {
+#pragma unroll
+    for (int tk = 0; tk < NT; ++tk)
+#pragma unroll
+      for (int i = 0; i < PER; ++i) part[wave][tk][lane + 64 * i] = acc[tk][i];
+    __syncthreads();
+    if (wave != 0) return;
+  }
 
 #pragma unroll
-  for (int tk = 0; tk < 8; ++tk) {
+  for (int tk = 0; tk < NT; ++tk) {
     if (tk >= ntok) break;
     const int t = t_lo + tk;
     float x[PER];
 #pragma unroll
-    for (int i = 0; i < PER; ++i) x[i] = acc[tk][i] + 0.0f;   // -0 -> +0
+    for (int i = 0; i < PER; ++i) {
+      float v = acc[tk][i];
+      if (WAVES > 1) {
+        const int d = lane + 64 * i;
+        v = part[0][tk][d];
+#pragma unroll
+        for (int w = 1; w < WAVES; ++w) v = v + part[w][tk][d];
+      }
+      x[i] = v + 0.0f;   // -0 -> +0
+    }
     if (dump) {
       const size_t base = (((size_t)b * a.n_new + (t - a.T_old)) * a.Hkv + h) * D;
 #pragma unroll
@@ -159,16 +198,7 @@ __global__ __launch_bounds__(64) void append_kernel(AppendArgs a) {
       }
     }
     if (!P.tiled) {
-#pragma unroll
-      for (int i = 0; i < PER; ++i) cs[lane + 64 * i] = (uint8_t)code[i];
-      __syncthreads();
-      if (lane < D / 16) {
-        uint32_t w = 0;
-#pragma unroll
-        for (int k = 0; k < 16; ++k) w |= (uint32_t)cs[16 * lane + k] << (2 * k);
-        *reinterpret_cast<uint32_t*>(P.codes + kcode_offset(bh, a.cap, t, D) + 4 * lane) = w;
-      }
-      __syncthreads();
+      store_canonical<PER>(code, lane, P.codes + kcode_offset(bh, a.cap, t, D));
     } else {
 #pragma unroll
       for (int i = 0; i < PER; ++i) {
@@ -186,7 +216,6 @@ template <int D>
 __global__ __launch_bounds__(64) void quantize_rows_kernel(const float* x, float clip, uint8_t* codes,
                                                            uint32_t* meta) {
   constexpr int PER = D / 64;
-  __shared__ uint8_t cs[D];
   const int lane = threadIdx.x;
   const size_t row = blockIdx.x;
   float v[PER];
@@ -202,15 +231,7 @@ __global__ __launch_bounds__(64) void quantize_rows_kernel(const float* x, float
     code[2 * g + 1] = quant_code(v[2 * g + 1], q);
     if (lane == 0) meta[row * (D / kGroup) + g] = q.packed;
   }
-#pragma unroll
-  for (int i = 0; i < PER; ++i) cs[lane + 64 * i] = (uint8_t)code[i];
-  __syncthreads();
-  if (lane < D / 16) {
-    uint32_t w = 0;
-#pragma unroll
-    for (int k = 0; k < 16; ++k) w |= (uint32_t)cs[16 * lane + k] << (2 * k);
-    *reinterpret_cast<uint32_t*>(codes + row * (D / 4) + 4 * lane) = w;
-  }
+  store_canonical<PER>(code, lane, codes + row * (D / 4));
 }
 
 // Canonical export of the tiled V codes: one thread per output byte.
@@ -234,13 +255,36 @@ __global__ __launch_bounds__(256) void export_vcodes_kernel(const uint8_t* tiled
   }
 }
 
+// Plain 16-byte copy used to calibrate bandwidth and traffic counters.
+__global__ __launch_bounds__(256) void stream_copy_kernel(const uint4* src, uint4* dst, size_t n) {
+  for (size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x)
+    dst[i] = src[i];
+}
+
+hipError_t launch_stream_copy(const void* src, void* dst, size_t bytes, hipStream_t s) {
+  const size_t n = bytes / 16;
+  if (n == 0) return hipSuccess;
+  const unsigned blocks = (unsigned)std::min<size_t>((n + 255) / 256, 256 * 64);
+  hipLaunchKernelGGL(stream_copy_kernel, dim3(blocks), dim3(256), 0, s, static_cast<const uint4*>(src),
+                     static_cast<uint4*>(dst), n);
+  return hipGetLastError();
+}
+
 hipError_t launch_append(const AppendArgs& a, hipStream_t s) {
   const int groups = ((a.T_new - 1) >> 3) - (a.T_old >> 3) + 1;
   dim3 grid((unsigned)(a.batch * a.Hkv), (unsigned)groups, 2);
-  if (a.D == 128)
-    hipLaunchKernelGGL(append_kernel<128>, grid, dim3(64), 0, s, a);
-  else
-    hipLaunchKernelGGL(append_kernel<512>, grid, dim3(64), 0, s, a);
+  const bool one = a.n_new == 1;
+  if (a.D == 128) {
+    if (one)
+      hipLaunchKernelGGL((append_kernel<128, 4, 1>), grid, dim3(256), 0, s, a);
+    else
+      hipLaunchKernelGGL((append_kernel<128, 4, 8>), grid, dim3(256), 0, s, a);
+  } else {
+    if (one)
+      hipLaunchKernelGGL((append_kernel<512, 4, 1>), grid, dim3(256), 0, s, a);
+    else
+      hipLaunchKernelGGL((append_kernel<512, 1, 8>), grid, dim3(64), 0, s, a);
+  }
   return hipGetLastError();
 }
 

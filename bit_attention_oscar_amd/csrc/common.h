@@ -121,6 +121,14 @@ struct SegPlan {           // up to two token segments, split into `splits` chun
   int slot0;               // first partial slot written by split 0
 };
 
+struct CombineArgs {
+  const float* partials;
+  const float* rvT;        // fp32 [D][D]: rvT[e][d] = R_V[d][e]
+  void* out;
+  int out_dtype;
+  int B, Hq, Hkv, D, nslots;
+};
+
 struct DecodeArgs {
   PlaneDev k, v;
   const float* qrot;
@@ -128,15 +136,12 @@ struct DecodeArgs {
   const uint16_t* qswz;
   float* partials;         // [B][Hq][kMaxSplits][D+2]
   int Hq, Hkv, D, cap, N, M, T;
-  SegPlan plan;
-};
-
-struct CombineArgs {
-  const float* partials;
-  const float* rvT;        // fp32 [D][D]: rvT[e][d] = R_V[d][e]
-  void* out;
-  int out_dtype;
-  int B, Hq, D, nslots;
+  SegPlan plan;            // INT2 range (matrix-core kernel) or all tokens (VALU kernel)
+  SegPlan win;             // bf16 window segments handled by extra blocks of the
+                           // matrix-core launch (win.splits blocks of <= 64 tokens)
+  unsigned* counters;      // [B*Hkv] finished blocks per (sequence, kv head); every
+                           // entry is zero between launches (the last block resets it)
+  CombineArgs comb;        // merge done by the last block of each (sequence, kv head)
 };
 
 // launchers (defined in the .hip files); return hipGetLastError()
@@ -147,6 +152,7 @@ hipError_t launch_qrot(const QRotArgs& a, hipStream_t s);
 hipError_t launch_decode_valu(const DecodeArgs& a, int B, hipStream_t s);
 hipError_t launch_decode_mfma(const DecodeArgs& a, int B, int waves_per_block, hipStream_t s);
 hipError_t launch_combine(const CombineArgs& a, hipStream_t s);
+hipError_t launch_stream_copy(const void* src, void* dst, size_t bytes, hipStream_t s);
 hipError_t launch_export_vcodes(const uint8_t* tiled, uint8_t* canon, int BH, int cap, int T, int D,
                                 hipStream_t s);
 

@@ -28,6 +28,24 @@ typedef float f4 __attribute__((ext_vector_type(4)));
 
 #define NEG_INF (-__builtin_inff())
 
+// Scheduling fence between the phases of a tile (QK^T / softmax / PV): keeps
+// the compiler from hoisting a whole tile of code conversions ahead of the
+// softmax, which raises register pressure.
+#ifndef OSCAR_PHASE_FENCE
+#define OSCAR_PHASE_FENCE 1
+#endif
+#if OSCAR_PHASE_FENCE
+#define PHASE_FENCE() __builtin_amdgcn_sched_barrier(0)
+#else
+#define PHASE_FENCE() ((void)0)
+#endif
+#ifndef OSCAR_MFMA_WAVES_PER_EU
+#define OSCAR_MFMA_WAVES_PER_EU 4
+#endif
+#ifndef OSCAR_PREFETCH
+#define OSCAR_PREFETCH 1
+#endif
+
 __device__ inline float wmax(float v) {
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
@@ -54,69 +72,96 @@ __host__ __device__ inline int qk_dim(int w, int pp, int k) {
   return 16 * w + 2 * pp + (k & 2 ? 1 : 0) + (k & 1 ? 8 : 0);
 }
 
+// One block per (sequence, kv head); its query heads are processed in chunks
+// of four.  The 128- or 512-long reduction over e is split across the four
+// waves (64 independent R loads in flight per lane) and the partial sums are
+// added in a fixed order.
 template <int D>
-__global__ __launch_bounds__(128) void qrot_kernel(QRotArgs a) {
-  constexpr int PER = D / 128;
-  const int tid = threadIdx.x;
-  const int bq = blockIdx.x;                 // b * Hq + head
-  __shared__ float xs[D];
-  __shared__ float vs[D];
-  __shared__ float red[4][4];
-  for (int d = tid; d < D; d += 128) xs[d] = bf16_to_f32(a.q[(size_t)bq * D + d]);
-  __syncthreads();
-  float acc[PER];
-#pragma unroll
-  for (int i = 0; i < PER; ++i) acc[i] = 0.0f;
-  for (int e = 0; e < D; ++e) {
-    const float x = xs[e];
-#pragma unroll
-    for (int i = 0; i < PER; ++i) acc[i] = __builtin_fmaf(x, a.rk[(size_t)e * D + tid + 128 * i], acc[i]);
-  }
-  float amax = 0.0f;
-#pragma unroll
-  for (int i = 0; i < PER; ++i) {
-    const float v = acc[i] * a.scale_log2;
-    vs[tid + 128 * i] = v;
-    a.qrot[(size_t)bq * D + tid + 128 * i] = v;
-    amax = fmaxf(amax, fabsf(v));
-  }
-  // per-group sums (group g = dims [128 g, 128 g + 128) = element g of every thread)
-  const int wave = tid >> 6, lane = tid & 63;
-  float gs[4] = {0, 0, 0, 0};
-#pragma unroll
-  for (int i = 0; i < PER; ++i) gs[i] = wsum(acc[i] * a.scale_log2);
-  amax = wmax(amax);
-  if (lane == 0) {
-    for (int g = 0; g < 4; ++g) red[wave][g] = gs[g];
-    red[2 + wave][0] = amax;
-  }
-  __syncthreads();
-  const float gmax = fmaxf(red[2][0], red[3][0]);
-  int e2 = 0;
-  if (gmax > 0.0f) frexpf(gmax, &e2);
-  const int eq = (gmax > 0.0f) ? 15 - e2 : 0;          // |q| * 2^eq < 2^15
-  if (tid < 8) {
-    float v = 0.0f;
-    if (tid < PER) v = red[0][tid] + red[1][tid];
-    if (tid == 4) v = ldexpf(1.0f, 24 - eq);           // cK: undoes 2^eq and the 2^-24 code scale
-    a.qaux[(size_t)bq * 8 + tid] = v;
-  }
-  if (a.want_swz && D == 128) {
-    // fp16 operand registers: [b*Hkv + kvh][lane 64][w 8][k 4], lane = 4*blk + j
-    // holds query head j of the kv head; all four blocks of a lane group pp
-    // hold the same chunk (w, pp), broadcast by the instruction.
-    const int Gq = a.Hq / a.Hkv;
-    const int b = bq / a.Hq, head = bq - b * a.Hq;
-    const int kvh = head / Gq, j = head - kvh * Gq;
-    uint16_t* dst = a.qswz + ((size_t)(b * a.Hkv + kvh) * 64) * 32;
-    for (int e = tid; e < 16 * 32; e += 128) {
-      const int m = e >> 5, w = (e >> 2) & 7, k = e & 3;
-      const int lane_id = 4 * m + j;
-      const int pp = lane_id >> 4;
-      const int d = qk_dim(w, pp, k);
-      const float v = ldexpf(vs[d], eq - 2 * (d & 3));
-      dst[(size_t)lane_id * 32 + w * 4 + k] = __builtin_bit_cast(uint16_t, (_Float16)v);
+__global__ __launch_bounds__(256) void qrot_kernel(QRotArgs a) {
+  constexpr int PER = D / 64;       // dims per lane
+  constexpr int EW = D / 4;         // e values per wave
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int bh = blockIdx.x;        // b * Hkv + kvh
+  const int b = bh / a.Hkv, kvh = bh - (bh / a.Hkv) * a.Hkv;
+  const int Gq = a.Hq / a.Hkv;
+  __shared__ float xs[4][D];
+  __shared__ float part[4][4][D];
+  __shared__ float red[4][8];
+  for (int hc = 0; hc < Gq; hc += 4) {
+    const int nh = min(4, Gq - hc);
+    const int head0 = kvh * Gq + hc;
+    for (int i = tid; i < 4 * D; i += 256) {
+      const int j = i / D, d = i - (i / D) * D;
+      xs[j][d] = j < nh ? bf16_to_f32(a.q[((size_t)b * a.Hq + head0 + j) * D + d]) : 0.0f;
     }
+    __syncthreads();
+    float acc[4][PER];
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int i = 0; i < PER; ++i) acc[j][i] = 0.0f;
+    const float* R = a.rk + (size_t)(wave * EW) * D + lane;
+#pragma unroll 8
+    for (int e = 0; e < EW; ++e) {
+      float r[PER];
+#pragma unroll
+      for (int i = 0; i < PER; ++i) r[i] = R[(size_t)e * D + 64 * i];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float x = xs[j][wave * EW + e];
+#pragma unroll
+        for (int i = 0; i < PER; ++i) acc[j][i] = __builtin_fmaf(x, r[i], acc[j][i]);
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int i = 0; i < PER; ++i) part[wave][j][lane + 64 * i] = acc[j][i];
+    __syncthreads();
+    // wave j finishes head j: sum the four partials, scale, group sums and max |q|
+    if (wave < nh) {
+      const int j = wave, head = head0 + j;
+      float gs[4] = {0, 0, 0, 0};
+      float amax = 0.0f;
+#pragma unroll
+      for (int i = 0; i < PER; ++i) {
+        const int d = lane + 64 * i;
+        const float v = (((part[0][j][d] + part[1][j][d]) + part[2][j][d]) + part[3][j][d]) * a.scale_log2;
+        xs[j][d] = v;
+        a.qrot[((size_t)b * a.Hq + head) * D + d] = v;
+        gs[i / 2] += v;
+        amax = fmaxf(amax, fabsf(v));
+      }
+#pragma unroll
+      for (int g = 0; g < 4; ++g) gs[g] = wsum(gs[g]);
+      amax = wmax(amax);
+      int e2 = 0;
+      if (amax > 0.0f) frexpf(amax, &e2);
+      const int eq = (amax > 0.0f) ? 15 - e2 : 0;        // |q| * 2^eq < 2^15
+      if (lane < 8) {
+        float v = 0.0f;
+        if (lane < 4) v = gs[lane];
+        if (lane == 4) v = ldexpf(1.0f, 24 - eq);          // cK: undoes 2^eq and the 2^-24 code scale
+        a.qaux[((size_t)b * a.Hq + head) * 8 + lane] = v;
+      }
+      if (lane == 0) red[j][0] = (float)eq;
+    }
+    __syncthreads();
+    if (a.want_swz && D == 128 && Gq == 4) {
+      // fp16 operand registers: [b*Hkv + kvh][lane 64][w 8][k 4], lane = 4*blk + j
+      // holds query head j; the four blocks of lane group pp hold the same
+      // chunk (w, pp), broadcast by the instruction.
+      uint16_t* dst = a.qswz + (size_t)bh * 64 * 32;
+      for (int e = tid; e < 64 * 32; e += 256) {
+        const int lane_id = e >> 5, w = (e >> 2) & 7, k = e & 3;
+        const int j = lane_id & 3, pp = lane_id >> 4;
+        const int d = qk_dim(w, pp, k);
+        const int eq = (int)red[j][0];
+        const float v = ldexpf(xs[j][d], eq - 2 * (d & 3));
+        dst[e] = __builtin_bit_cast(uint16_t, (_Float16)v);
+      }
+    }
+    __syncthreads();
   }
 }
 
@@ -365,11 +410,357 @@ __device__ inline void pv_word(uint32_t word, h4 p, f4& o0, f4& o1) {
   o1 = __builtin_amdgcn_mfma_f32_4x4x4f16(p, as_h4(c[6], c[7]), o1, 4, 2 * W + 1, 0);
 }
 
+// ---------------------------------------------------------------------------
+// combine + V un-rotation
+// ---------------------------------------------------------------------------
+
+// One block per (sequence, kv head): merge the splits of its query heads
+// (chunks of four), then o = o' @ R_V^T with the reduction over e split across
+// the four waves.
+// Partial loads: plain, or device-scope (coherent across XCDs within a launch).
+template <bool COHERENT>
+__device__ inline float ld_partial(const float* p) {
+  if (COHERENT) return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  return *p;
+}
+
+template <int D, bool COHERENT = false>
+__device__ void combine_group(const CombineArgs& a, int bh) {
+  constexpr int PER = D / 64;
+  constexpr int EW = D / 4;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int b = bh / a.Hkv, kvh = bh - (bh / a.Hkv) * a.Hkv;
+  const int Gq = a.Hq / a.Hkv;
+  __shared__ float wsl[4][kMaxSplits];
+  __shared__ float linv[4];
+  __shared__ float os[4][D];
+  __shared__ float part[4][4][D];
+  for (int hc = 0; hc < Gq; hc += 4) {
+    const int nh = min(4, Gq - hc);
+    // split weights: wave j handles head j
+    if (wave < nh) {
+      const float* P = a.partials + ((size_t)b * a.Hq + kvh * Gq + hc + wave) * kMaxSplits * (D + 2);
+      float mx = NEG_INF;
+      for (int sl = lane; sl < a.nslots; sl += 64) mx = fmaxf(mx, ld_partial<COHERENT>(P + (size_t)sl * (D + 2) + D));
+      const float M = wmax(mx);
+      float L = 0.0f;
+      for (int sl = lane; sl < a.nslots; sl += 64) {
+        const float ms = ld_partial<COHERENT>(P + (size_t)sl * (D + 2) + D);
+        const float w = (ms == NEG_INF) ? 0.0f : exp2f(ms - M);
+        wsl[wave][sl] = w;
+        L = __builtin_fmaf(ld_partial<COHERENT>(P + (size_t)sl * (D + 2) + D + 1), w, L);
+      }
+      L = wsum(L);
+      if (lane == 0) linv[wave] = 1.0f / L;
+    }
+    __syncthreads();
+    for (int idx = tid; idx < 4 * D; idx += 256) {
+      const int j = idx / D, d = idx - (idx / D) * D;
+      float acc = 0.0f;
+      if (j < nh) {
+        const float* P = a.partials + ((size_t)b * a.Hq + kvh * Gq + hc + j) * kMaxSplits * (D + 2);
+        for (int sl = 0; sl < a.nslots; ++sl)
+          acc = __builtin_fmaf(ld_partial<COHERENT>(P + (size_t)sl * (D + 2) + d), wsl[j][sl], acc);
+        acc *= linv[j];
+      }
+      os[j][d] = acc;
+    }
+    __syncthreads();
+    float acc[4][PER];
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int i = 0; i < PER; ++i) acc[j][i] = 0.0f;
+    const float* R = a.rvT + (size_t)(wave * EW) * D + lane;
+#pragma unroll 8
+    for (int e = 0; e < EW; ++e) {
+      float r[PER];
+#pragma unroll
+      for (int i = 0; i < PER; ++i) r[i] = R[(size_t)e * D + 64 * i];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float x = os[j][wave * EW + e];
+#pragma unroll
+        for (int i = 0; i < PER; ++i) acc[j][i] = __builtin_fmaf(x, r[i], acc[j][i]);
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int i = 0; i < PER; ++i) part[wave][j][lane + 64 * i] = acc[j][i];
+    __syncthreads();
+    for (int idx = tid; idx < nh * D; idx += 256) {
+      const int j = idx / D, d = idx - (idx / D) * D;
+      const float v = ((part[0][j][d] + part[1][j][d]) + part[2][j][d]) + part[3][j][d];
+      const size_t o = ((size_t)b * a.Hq + kvh * Gq + hc + j) * D + d;
+      if (a.out_dtype == 0)
+        reinterpret_cast<float*>(a.out)[o] = v;
+      else if (a.out_dtype == 1)
+        reinterpret_cast<uint16_t*>(a.out)[o] = f32_to_bf16(v);
+      else
+        reinterpret_cast<uint16_t*>(a.out)[o] = __builtin_bit_cast(uint16_t, (_Float16)v);
+    }
+    __syncthreads();
+  }
+}
+
+template <int D>
+__global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
+  combine_group<D>(a, (int)blockIdx.x);
+}
+
+// Partial results of the matrix-core launch are written with device-scope
+// stores, which complete at the level shared by all XCDs.
+__device__ inline void st_partial(float* p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Called by every block of the matrix-core launch after it wrote its partial:
+// the last block to finish for a (sequence, kv head) merges all of them.
+// Every thread waits for its device-scope partial stores to complete before the
+// barrier, then one thread increments the counter; the last block reads the
+// partials with device-scope loads.  No cache-wide write-back or invalidation,
+// and no block ever waits for another.
+__device__ inline void finish_block(const DecodeArgs& a, int bh) {
+  __shared__ int is_last;
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const unsigned total = (unsigned)(a.plan.splits + a.win.splits);
+    const unsigned prev = __hip_atomic_fetch_add(a.counters + bh, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    is_last = (prev == total - 1u);
+  }
+  __syncthreads();
+  if (!is_last) return;
+  combine_group<128, true>(a.comb, bh);
+  if (threadIdx.x == 0) a.counters[bh] = 0u;
+}
+
+// bf16 window tokens (sink + recent) of one (sequence, kv head): one block of
+// 256 threads takes up to 64 of them with fp32 VALU arithmetic.  Every row load
+// of a phase is issued before its arithmetic.
+__device__ inline int win_token(const SegPlan& w, int vt) {
+  const int len0 = w.b0 - w.a0;
+  return vt < len0 ? w.a0 + vt : w.a1 + (vt - len0);
+}
+
+__device__ inline const uint16_t* win_row(const PlaneDev& P, int bh, int t, int N, int M, int D) {
+  return t < N ? P.sink + row_offset(bh, N, t, D) : P.ring + row_offset(bh, M, t % M, D);
+}
+
+__device__ inline void bf16x8(const uint4 u, float* x) {
+  const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    x[2 * k] = __uint_as_float(w[k] << 16);
+    x[2 * k + 1] = __uint_as_float(w[k] & 0xFFFF0000u);
+  }
+}
+
+__device__ void window_block(const DecodeArgs& a, int bh, int b, int h, int wblk) {
+  constexpr int D = 128;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int len = (a.win.b0 - a.win.a0) + (a.win.b1 - a.win.a1);
+  const int v_lo = wblk * a.win.chunk;
+  const int v_hi = min(len, v_lo + a.win.chunk);
+  __shared__ float qs[4][D + 4];
+  __shared__ float sc[4][64];
+  __shared__ float wm[4], wl[4], wa[4];
+  __shared__ float red[4][4][D];
+  for (int i = tid; i < 4 * D; i += 256)
+    qs[i >> 7][i & 127] = a.qrot[((size_t)b * a.Hq + h * 4 + (i >> 7)) * D + (i & 127)];
+  if (tid < 4) {
+    wm[tid] = NEG_INF;
+    wl[tid] = 0.0f;
+  }
+  const int g = tid >> 4, c = tid & 15;      // PV role: token group, 8-dim chunk
+  float o[4][8];
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+#pragma unroll
+    for (int k = 0; k < 8; ++k) o[j][k] = 0.0f;
+  __syncthreads();
+  for (int vt0 = v_lo; vt0 < v_hi; vt0 += 64) {
+    const int n = min(64, v_hi - vt0);
+    {  // scores: 4 lanes per token, 32 dims each
+      const int tok = tid >> 2, part = tid & 3;
+      float dots[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+      if (tok < n) {
+        const int t = win_token(a.win, vt0 + tok);
+        const uint4* rp = reinterpret_cast<const uint4*>(win_row(a.k, bh, t, a.N, a.M, D) + 32 * part);
+        const uint4 us[4] = {rp[0], rp[1], rp[2], rp[3]};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          float x[8];
+          bf16x8(us[i], x);
+#pragma unroll
+          for (int k = 0; k < 8; ++k)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) dots[j] = __builtin_fmaf(qs[j][32 * part + 8 * i + k], x[k], dots[j]);
+        }
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        dots[j] += __shfl_xor(dots[j], 1);
+        dots[j] += __shfl_xor(dots[j], 2);
+      }
+      if (part == 0)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) sc[j][tok] = tok < n ? dots[j] : NEG_INF;
+    }
+    __syncthreads();
+    {  // online softmax update, one wave per head
+      const float sv = sc[wave][lane];
+      const float mold = wm[wave];
+      const float mnew = fmaxf(mold, wmax(sv));
+      const float p = (sv == NEG_INF) ? 0.0f : exp2f(sv - mnew);
+      const float l = wsum(p);
+      sc[wave][lane] = p;
+      if (lane == 0) {
+        const float alpha = (mold == NEG_INF) ? 0.0f : exp2f(mold - mnew);
+        wa[wave] = alpha;
+        wm[wave] = mnew;
+        wl[wave] = wl[wave] * alpha + l;
+      }
+    }
+    __syncthreads();
+    {  // PV: thread (g, c) over tokens g, g+16, g+32, g+48 of the tile
+      uint4 u[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int tok = g + 16 * i;
+        u[i] = make_uint4(0, 0, 0, 0);
+        if (tok < n) {
+          const int t = win_token(a.win, vt0 + tok);
+          u[i] = *reinterpret_cast<const uint4*>(win_row(a.v, bh, t, a.N, a.M, D) + 8 * c);
+        }
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float al = wa[j];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) o[j][k] *= al;
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int tok = g + 16 * i;
+        if (tok < n) {
+          float x[8];
+          bf16x8(u[i], x);
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const float p = sc[j][tok];
+#pragma unroll
+            for (int k = 0; k < 8; ++k) o[j][k] = __builtin_fmaf(p, x[k], o[j][k]);
+          }
+        }
+      }
+    }
+    __syncthreads();
+  }
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      o[j][k] += __shfl_xor(o[j][k], 16);
+      o[j][k] += __shfl_xor(o[j][k], 32);
+    }
+  if (lane < 16)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int k = 0; k < 8; ++k) red[wave][j][8 * c + k] = o[j][k];
+  __syncthreads();
+  const int slot = a.win.slot0 + wblk;
+  for (int idx = tid; idx < 4 * D; idx += 256) {
+    const int j = idx >> 7, d = idx & 127;
+    float* dst = a.partials + (((size_t)b * a.Hq + h * 4 + j) * kMaxSplits + slot) * (D + 2);
+    st_partial(dst + d, ((red[0][j][d] + red[1][j][d]) + red[2][j][d]) + red[3][j][d]);
+    if (d == 0) {
+      st_partial(dst + D, wm[j]);
+      st_partial(dst + D + 1, wl[j]);
+    }
+  }
+}
+
+// Reductions over the 16 lanes of one query head (lanes with equal lane % 4):
+// rotations by 4 and 8 inside each 16-lane row, then the gfx950 row swaps.
+template <int CTRL>
+__device__ inline float dpp_row_ror(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
+}
+__device__ inline float head_max(float v) {
+  v = fmaxf(v, dpp_row_ror<0x124>(v));     // row_ror:4
+  v = fmaxf(v, dpp_row_ror<0x128>(v));     // row_ror:8
+  auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ inline float head_sum(float v) {
+  v += dpp_row_ror<0x124>(v);
+  v += dpp_row_ror<0x128>(v);
+  auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+  r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ inline float lane_value(float v, int lane) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), lane));
+}
+
+struct TileRegs {
+  uint4 k0, k1;   // K codes of token tile + lane (32 bytes)
+  uint4 km, vm;   // K and V scale|zero of tokens tile + 4 blk .. + 3
+  uint4 v0, v1;   // V code record of this lane (32 bytes)
+};
+
+// Per-wave stream pointers: uniform tile bases (scalar registers) plus fixed
+// per-lane offsets, advanced by a whole tile at a time.
+struct TileStreams {
+  const uint8_t* kc;    // K codes of the tile's first token
+  const uint8_t* km;    // K meta of the tile's first token
+  const uint8_t* vm;    // V meta
+  const uint8_t* vc;    // V code tile
+};
+
+__device__ inline TileRegs load_tile(const TileStreams& s, int lane_k, int lane_m, int lane_v) {
+  TileRegs r;
+  const uint4* kp = reinterpret_cast<const uint4*>(s.kc + lane_k);
+  r.k0 = kp[0];
+  r.k1 = kp[1];
+  r.km = *reinterpret_cast<const uint4*>(s.km + lane_m);
+  r.vm = *reinterpret_cast<const uint4*>(s.vm + lane_m);
+  const uint4* vp = reinterpret_cast<const uint4*>(s.vc + lane_v);
+  r.v0 = vp[0];
+  r.v1 = vp[1];
+  return r;
+}
+
+__device__ inline TileStreams tile_streams(const DecodeArgs& a, int bh, int t0) {
+  constexpr int D = 128;
+  TileStreams s;
+  s.kc = a.k.codes + kcode_offset(bh, a.cap, t0, D);
+  s.km = reinterpret_cast<const uint8_t*>(a.k.meta + meta_offset(bh, a.cap, t0, D));
+  s.vm = reinterpret_cast<const uint8_t*>(a.v.meta + meta_offset(bh, a.cap, t0, D));
+  s.vc = a.v.codes + ((size_t)bh * (a.cap / kTile) + (t0 >> 6)) * 2048;
+  return s;
+}
+
 template <int WPB>
-__global__ __launch_bounds__(64 * WPB) void decode_mfma_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(64 * WPB)
+#if OSCAR_MFMA_WAVES_PER_EU
+__attribute__((amdgpu_waves_per_eu(OSCAR_MFMA_WAVES_PER_EU, OSCAR_MFMA_WAVES_PER_EU)))
+#endif
+void decode_mfma_kernel(DecodeArgs a) {
   constexpr int D = 128;
   const int bh = blockIdx.x;
   const int b = bh / a.Hkv, h = bh - (bh / a.Hkv) * a.Hkv;
+  if ((int)blockIdx.y >= a.plan.splits) {          // bf16 window blocks
+    if (WPB == 4) window_block(a, bh, b, h, (int)blockIdx.y - a.plan.splits);
+    finish_block(a, bh);
+    return;
+  }
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int blk = lane >> 2, j = lane & 3;
   const int lo = a.plan.a0, hi = a.plan.b0;       // INT2 token range
@@ -386,7 +777,7 @@ __global__ __launch_bounds__(64 * WPB) void decode_mfma_kernel(DecodeArgs a) {
                     as_h4(q45.x, q45.y), as_h4(q45.z, q45.w), as_h4(q67.x, q67.y), as_h4(q67.z, q67.w)};
   const float* aux = a.qaux + ((size_t)b * a.Hq + h * 4 + j) * 8;
   const float cK = aux[4];
-  const float zq = aux[0] / cK;                    // sum(q_rot) in units of the raw dot
+  const float zq = aux[0] * (1.0f / cK);           // sum(q_rot) in units of the raw dot (cK is a power of 2)
   const float vmax = a.v.smax[bh];
   int ev2 = 0;
   if (vmax > 0.0f) frexpf(vmax, &ev2);
@@ -397,84 +788,110 @@ __global__ __launch_bounds__(64 * WPB) void decode_mfma_kernel(DecodeArgs a) {
 
   f4 o0 = {0, 0, 0, 0}, o1 = {0, 0, 0, 0};
   float m = NEG_INF, l = 0.0f, pz = 0.0f;
-  const size_t vtile_base = (size_t)bh * (a.cap / kTile);
 
-  for (int ti = s_t0 + wave; ti < s_t1; ti += WPB) {
-    const int t0 = (tile_first + ti) << 6;
-    const uint4* kp = reinterpret_cast<const uint4*>(a.k.codes + kcode_offset(bh, a.cap, t0 + lane, D));
-    const uint4 k0 = kp[0], k1 = kp[1];
-    const uint4 km = *reinterpret_cast<const uint4*>(a.k.meta + meta_offset(bh, a.cap, t0 + 4 * blk, D));
-    const uint4 vm = *reinterpret_cast<const uint4*>(a.v.meta + meta_offset(bh, a.cap, t0 + 4 * blk, D));
-    const uint4* vp = reinterpret_cast<const uint4*>(a.v.codes + (vtile_base + (t0 >> 6)) * 2048 + lane * 32);
-    const uint4 v0 = vp[0], v1 = vp[1];
-
+  // one 64-token tile: QK^T on matrix cores, online softmax, PV on matrix cores
+  auto process = [&](const TileRegs& cur, int t0) {
     f4 sa = {0, 0, 0, 0}, sb = {0, 0, 0, 0};
-    qk_word<0>(k0.x, qv[0], sa, sb);
-    qk_word<1>(k0.y, qv[1], sa, sb);
-    qk_word<2>(k0.z, qv[2], sa, sb);
-    qk_word<3>(k0.w, qv[3], sa, sb);
-    qk_word<4>(k1.x, qv[4], sa, sb);
-    qk_word<5>(k1.y, qv[5], sa, sb);
-    qk_word<6>(k1.z, qv[6], sa, sb);
-    qk_word<7>(k1.w, qv[7], sa, sb);
+    qk_word<0>(cur.k0.x, qv[0], sa, sb);
+    qk_word<1>(cur.k0.y, qv[1], sa, sb);
+    qk_word<2>(cur.k0.z, qv[2], sa, sb);
+    qk_word<3>(cur.k0.w, qv[3], sa, sb);
+    qk_word<4>(cur.k1.x, qv[4], sa, sb);
+    qk_word<5>(cur.k1.y, qv[5], sa, sb);
+    qk_word<6>(cur.k1.z, qv[6], sa, sb);
+    qk_word<7>(cur.k1.w, qv[7], sa, sb);
     const f4 sc = sa + sb;
+    PHASE_FENCE();
 
-    const uint32_t kmr[4] = {km.x, km.y, km.z, km.w};
-    const uint32_t vmr[4] = {vm.x, vm.y, vm.z, vm.w};
+    const uint32_t kmr[4] = {cur.km.x, cur.km.y, cur.km.z, cur.km.w};
+    const uint32_t vmr[4] = {cur.vm.x, cur.vm.y, cur.vm.z, cur.vm.w};
     float u[4];
 #pragma unroll
     for (int r = 0; r < 4; ++r) u[r] = __builtin_fmaf(lo_half(kmr[r]), sc[r], hi_half(kmr[r]) * zq);
-    if (t0 < lo || t0 + 64 > hi) {
+    if (t0 < lo || t0 + 64 > hi) {                 // boundary tile (wave-uniform)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int t = t0 + 4 * blk + r;
         if (t < lo || t >= hi) u[r] = NEG_INF;
       }
     }
-    float mt = fmaxf(fmaxf(u[0], u[1]), fmaxf(u[2], u[3]));
-    mt = fmaxf(mt, __shfl_xor(mt, 4));
-    mt = fmaxf(mt, __shfl_xor(mt, 8));
-    mt = fmaxf(mt, __shfl_xor(mt, 16));
-    mt = fmaxf(mt, __shfl_xor(mt, 32));
+    const float mt = head_max(fmaxf(fmaxf(u[0], u[1]), fmaxf(u[2], u[3])));
     const float mnew = fmaxf(m, cK * mt);
-    const float alpha = exp2f(m - mnew);
-    m = mnew;
+    if (__any(mnew > m)) {                         // some head's max moved: rescale
+      const float alpha = __builtin_amdgcn_exp2f(m - mnew);
+      l *= alpha;
+      pz *= alpha;
+      const f4 al = {lane_value(alpha, 0), lane_value(alpha, 1), lane_value(alpha, 2), lane_value(alpha, 3)};
+      o0 *= al;
+      o1 *= al;
+      m = mnew;
+    }
     float p[4];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) p[r] = exp2f(__builtin_fmaf(cK, u[r], -mnew));
-    l = __builtin_fmaf(l, alpha, (p[0] + p[1]) + (p[2] + p[3]));
+    for (int r = 0; r < 4; ++r) p[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(cK, u[r], -m));
+    l += (p[0] + p[1]) + (p[2] + p[3]);
     float pzt = 0.0f;
 #pragma unroll
     for (int r = 0; r < 4; ++r) pzt = __builtin_fmaf(p[r], hi_half(vmr[r]), pzt);
-    pz = __builtin_fmaf(pz, alpha, pzt);
-    const h4 pv = {(_Float16)(p[0] * lo_half(vmr[0]) * fvA), (_Float16)(p[1] * lo_half(vmr[1]) * fvA),
-                   (_Float16)(p[2] * lo_half(vmr[2]) * fvB), (_Float16)(p[3] * lo_half(vmr[3]) * fvB)};
-    const f4 al = {__shfl(alpha, 0), __shfl(alpha, 1), __shfl(alpha, 2), __shfl(alpha, 3)};
-    o0 *= al;
-    o1 *= al;
-    pv_word<0>(v0.x, pv, o0, o1);
-    pv_word<1>(v0.y, pv, o0, o1);
-    pv_word<2>(v0.z, pv, o0, o1);
-    pv_word<3>(v0.w, pv, o0, o1);
-    pv_word<4>(v1.x, pv, o0, o1);
-    pv_word<5>(v1.y, pv, o0, o1);
-    pv_word<6>(v1.z, pv, o0, o1);
-    pv_word<7>(v1.w, pv, o0, o1);
+    pz += pzt;
+    // p * s_V * 2^ev * 4^-s as fp16 (one rounding from fp32)
+    const h4 pv = {(_Float16)(p[0] * (lo_half(vmr[0]) * fvA)), (_Float16)(p[1] * (lo_half(vmr[1]) * fvA)),
+                   (_Float16)(p[2] * (lo_half(vmr[2]) * fvB)), (_Float16)(p[3] * (lo_half(vmr[3]) * fvB))};
+    PHASE_FENCE();
+    pv_word<0>(cur.v0.x, pv, o0, o1);
+    pv_word<1>(cur.v0.y, pv, o0, o1);
+    pv_word<2>(cur.v0.z, pv, o0, o1);
+    pv_word<3>(cur.v0.w, pv, o0, o1);
+    pv_word<4>(cur.v1.x, pv, o0, o1);
+    pv_word<5>(cur.v1.y, pv, o0, o1);
+    pv_word<6>(cur.v1.z, pv, o0, o1);
+    pv_word<7>(cur.v1.w, pv, o0, o1);
+  };
+
+  // two register sets in turn: the loads of the next tile are in flight while
+  // the current one is processed
+  const int lane_k = lane * 32, lane_m = blk * 16, lane_v = lane * 32;
+  const int ti0 = s_t0 + wave;
+  constexpr int kStep = 64 * WPB;                  // tokens between a wave's tiles
+  TileStreams st = tile_streams(a, bh, (tile_first + ti0) << 6);
+  auto advance = [&](TileStreams& x) {
+    x.kc += kStep * 32;
+    x.km += kStep * 4;
+    x.vm += kStep * 4;
+    x.vc += WPB * 2048;
+  };
+#if OSCAR_PREFETCH
+  TileRegs ra, rb;
+  if (ti0 < s_t1) ra = load_tile(st, lane_k, lane_m, lane_v);
+  for (int ti = ti0; ti < s_t1; ti += 2 * WPB) {
+    const int tB = ti + WPB;
+    advance(st);
+    if (tB < s_t1) rb = load_tile(st, lane_k, lane_m, lane_v);
+    process(ra, (tile_first + ti) << 6);
+    if (tB >= s_t1) break;
+    const int tA = tB + WPB;
+    advance(st);
+    if (tA < s_t1) ra = load_tile(st, lane_k, lane_m, lane_v);
+    process(rb, (tile_first + tB) << 6);
   }
+#else
+  for (int ti = ti0; ti < s_t1; ti += WPB) {
+    const TileRegs r = load_tile(st, lane_k, lane_m, lane_v);
+    advance(st);
+    process(r, (tile_first + ti) << 6);
+  }
+#endif
 
   // per-head totals of l and sum(p z_V) over the 16 lanes of each head
-#pragma unroll
-  for (int o = 4; o < 64; o <<= 1) {
-    l += __shfl_xor(l, o);
-    pz += __shfl_xor(pz, o);
-  }
+  l = head_sum(l);
+  pz = head_sum(pz);
   __shared__ float sm[WPB][4], sl[WPB][4];
   __shared__ float so[WPB][4][D];
   if (lane < 4) {
     sm[wave][lane] = m;
     sl[wave][lane] = l;
   }
-  const float pzr[4] = {__shfl(pz, 0), __shfl(pz, 1), __shfl(pz, 2), __shfl(pz, 3)};
+  const float pzr[4] = {lane_value(pz, 0), lane_value(pz, 1), lane_value(pz, 2), lane_value(pz, 3)};
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
     so[wave][r][4 * blk + j] = __builtin_fmaf(o0[r], cV, pzr[r]);
@@ -497,66 +914,13 @@ __global__ __launch_bounds__(64 * WPB) void decode_mfma_kernel(DecodeArgs a) {
       }
     }
     float* dst = a.partials + (((size_t)b * a.Hq + h * 4 + r) * kMaxSplits + slot) * (D + 2);
-    dst[d] = O;
+    st_partial(dst + d, O);
     if (d == 0) {
-      dst[D] = M;
-      dst[D + 1] = L;
+      st_partial(dst + D, M);
+      st_partial(dst + D + 1, L);
     }
   }
-}
-
-// ---------------------------------------------------------------------------
-// combine + V un-rotation
-// ---------------------------------------------------------------------------
-
-template <int D>
-__global__ __launch_bounds__(128) void combine_kernel(CombineArgs a) {
-  constexpr int PER = D / 128;
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const size_t row = blockIdx.x;                       // b * Hq + head
-  const float* P = a.partials + row * kMaxSplits * (D + 2);
-  __shared__ float wsl[kMaxSplits];
-  __shared__ float os[D];
-  __shared__ float red[2];
-  float mx = NEG_INF;
-  for (int s = tid; s < a.nslots; s += 128) mx = fmaxf(mx, P[(size_t)s * (D + 2) + D]);
-  mx = wmax(mx);
-  if (lane == 0) red[wave] = mx;
-  __syncthreads();
-  const float M = fmaxf(red[0], red[1]);
-  __syncthreads();
-  float L = 0.0f;
-  for (int s = tid; s < a.nslots; s += 128) {
-    const float ms = P[(size_t)s * (D + 2) + D];
-    const float w = (ms == NEG_INF) ? 0.0f : exp2f(ms - M);
-    wsl[s] = w;
-    L = __builtin_fmaf(P[(size_t)s * (D + 2) + D + 1], w, L);
-  }
-  L = wsum(L);
-  if (lane == 0) red[wave] = L;
-  __syncthreads();
-  const float inv = 1.0f / (red[0] + red[1]);
-#pragma unroll
-  for (int i = 0; i < PER; ++i) {
-    const int d = tid + 128 * i;
-    float acc = 0.0f;
-    for (int s = 0; s < a.nslots; ++s) acc = __builtin_fmaf(P[(size_t)s * (D + 2) + d], wsl[s], acc);
-    os[d] = acc * inv;
-  }
-  __syncthreads();
-#pragma unroll
-  for (int i = 0; i < PER; ++i) {
-    const int d = tid + 128 * i;
-    float acc = 0.0f;
-    for (int e = 0; e < D; ++e) acc = __builtin_fmaf(os[e], a.rvT[(size_t)e * D + d], acc);
-    const size_t o = row * D + d;
-    if (a.out_dtype == 0)
-      reinterpret_cast<float*>(a.out)[o] = acc;
-    else if (a.out_dtype == 1)
-      reinterpret_cast<uint16_t*>(a.out)[o] = f32_to_bf16(acc);
-    else
-      reinterpret_cast<uint16_t*>(a.out)[o] = __builtin_bit_cast(uint16_t, (_Float16)acc);
-  }
+  finish_block(a, bh);
 }
 
 // ---------------------------------------------------------------------------
@@ -564,11 +928,11 @@ __global__ __launch_bounds__(128) void combine_kernel(CombineArgs a) {
 // ---------------------------------------------------------------------------
 
 hipError_t launch_qrot(const QRotArgs& a, hipStream_t s) {
-  dim3 grid((unsigned)(a.B * a.Hq));
+  dim3 grid((unsigned)(a.B * a.Hkv));
   if (a.D == 128)
-    hipLaunchKernelGGL(qrot_kernel<128>, grid, dim3(128), 0, s, a);
+    hipLaunchKernelGGL(qrot_kernel<128>, grid, dim3(256), 0, s, a);
   else
-    hipLaunchKernelGGL(qrot_kernel<512>, grid, dim3(128), 0, s, a);
+    hipLaunchKernelGGL(qrot_kernel<512>, grid, dim3(256), 0, s, a);
   return hipGetLastError();
 }
 
@@ -582,22 +946,18 @@ hipError_t launch_decode_valu(const DecodeArgs& a, int B, hipStream_t s) {
 }
 
 hipError_t launch_decode_mfma(const DecodeArgs& a, int B, int waves_per_block, hipStream_t s) {
-  dim3 grid((unsigned)(B * a.Hkv), (unsigned)a.plan.splits);
-  switch (waves_per_block) {
-    case 1: hipLaunchKernelGGL(decode_mfma_kernel<1>, grid, dim3(64), 0, s, a); break;
-    case 2: hipLaunchKernelGGL(decode_mfma_kernel<2>, grid, dim3(128), 0, s, a); break;
-    case 8: hipLaunchKernelGGL(decode_mfma_kernel<8>, grid, dim3(512), 0, s, a); break;
-    default: hipLaunchKernelGGL(decode_mfma_kernel<4>, grid, dim3(256), 0, s, a); break;
-  }
+  (void)waves_per_block;   // the fused window blocks need 4 waves
+  dim3 grid((unsigned)(B * a.Hkv), (unsigned)(a.plan.splits + a.win.splits));
+  hipLaunchKernelGGL(decode_mfma_kernel<4>, grid, dim3(256), 0, s, a);
   return hipGetLastError();
 }
 
 hipError_t launch_combine(const CombineArgs& a, hipStream_t s) {
-  dim3 grid((unsigned)(a.B * a.Hq));
+  dim3 grid((unsigned)(a.B * a.Hkv));
   if (a.D == 128)
-    hipLaunchKernelGGL(combine_kernel<128>, grid, dim3(128), 0, s, a);
+    hipLaunchKernelGGL(combine_kernel<128>, grid, dim3(256), 0, s, a);
   else
-    hipLaunchKernelGGL(combine_kernel<512>, grid, dim3(128), 0, s, a);
+    hipLaunchKernelGGL(combine_kernel<512>, grid, dim3(256), 0, s, a);
   return hipGetLastError();
 }
 

@@ -55,6 +55,7 @@ struct ProfClass {
   size_t used = 0;
 };
 constexpr size_t kProfMax = 8192;
+constexpr int kMaxWinSplits = 32;   // bf16 window blocks per (sequence, kv head)
 
 }  // namespace
 
@@ -70,6 +71,7 @@ struct oscar_kv {
   float* qaux = nullptr;   // [B][Hq][8]
   uint16_t* qswz = nullptr;  // [B][Hkv][64][32]
   float* partials = nullptr; // [B][Hq][kMaxSplits][D+2]
+  unsigned* counters = nullptr; // [B][Hkv] blocks finished in the current decode launch
   size_t bytes = 0;
   int32_t forced_splits = 0;
   int32_t decode_impl = 0;
@@ -327,6 +329,9 @@ int oscar_kv_create(const oscar_kv_config* cfg, oscar_kv** out) {
   if ((rc = dev_alloc(kv, (void**)&kv->qaux, B * Hq * 8 * 4))) return bail(rc);
   if ((rc = dev_alloc(kv, (void**)&kv->qswz, B * Hkv * 64 * 32 * 2))) return bail(rc);
   if ((rc = dev_alloc(kv, (void**)&kv->partials, B * Hq * kMaxSplits * (D + 2) * 4))) return bail(rc);
+  if ((rc = dev_alloc(kv, (void**)&kv->counters, B * Hkv * sizeof(unsigned)))) return bail(rc);
+  if (hipMemset(kv->counters, 0, B * Hkv * sizeof(unsigned)) != hipSuccess)
+    return bail(fail(OSCAR_ERR_HIP, "clearing the decode counters failed"));
   if (hipDeviceSynchronize() != hipSuccess) return bail(fail(OSCAR_ERR_HIP, "device sync after create failed"));
   *out = kv;
   g_last_error.clear();
@@ -399,6 +404,16 @@ int oscar_int2_decode_attn(oscar_kv* kv, int32_t layer, const void* q, void* out
   da.N = N;
   da.M = M;
   da.T = T;
+  da.counters = kv->counters;
+  CombineArgs ca{};
+  ca.partials = kv->partials;
+  ca.rvT = kv->rvT + layer * DD;
+  ca.out = out;
+  ca.out_dtype = out_dtype;
+  ca.B = batch;
+  ca.Hq = Hq;
+  ca.Hkv = Hkv;
+  ca.D = D;
   const int BH = batch * Hkv;
 
   // token sets: sink [0, min(N,T)), recent [max(N, T-M), T), INT2 [N, T-M)
@@ -409,32 +424,34 @@ int oscar_int2_decode_attn(oscar_kv* kv, int32_t layer, const void* q, void* out
   const long pcall = prof_begin(kv, 1, stream);
   HIP_TRY(launch_qrot(qa, stream));
   if (fast) {
+    // one launch: INT2 splits (matrix cores) followed by bf16 window blocks
+    const int hp_len = sink_end + (T - rec_begin);
+    SegPlan w{};
+    if (hp_len > 0) {
+      const int want_w = std::max(1, std::min(kMaxWinSplits, (hp_len + kTile - 1) / kTile));
+      w = make_plan(0, sink_end, rec_begin, T, want_w, 0);
+    }
+    SegPlan p{};
     if (int2_hi > int2_lo) {
       const int ntiles = ((int2_hi - 1) >> 6) - (int2_lo >> 6) + 1;
       const int waves = kv->mfma_waves;
-      int s = kv->forced_splits > 0 ? std::min(kv->forced_splits, ntiles) : auto_int2_splits(BH, ntiles, waves);
-      s = std::min(s, kMaxSplits - 8);
-      SegPlan p{};
+      int s = kv->forced_splits > 0 ? kv->forced_splits : auto_int2_splits(BH, ntiles, waves);
+      s = std::max(1, std::min(s, std::min(ntiles, kMaxSplits - kMaxWinSplits)));
+      const int tps = (ntiles + s - 1) / s;
       p.a0 = int2_lo;
       p.b0 = int2_hi;
-      p.a1 = p.b1 = 0;
-      const int tps = (ntiles + s - 1) / s;
       p.chunk = tps * kTile;
       p.splits = (ntiles + tps - 1) / tps;
-      p.slot0 = 0;
-      da.plan = p;
-      const long pk = prof_begin(kv, 0, stream);
-      HIP_TRY(launch_decode_mfma(da, batch, waves, stream));
-      prof_end(kv, 0, pk, stream);
-      nslots = p.splits;
     }
-    const int hp_len = sink_end + (T - rec_begin);
-    if (hp_len > 0) {
-      const int ws = std::max(1, std::min(8, (hp_len + 255) / 256));
-      da.plan = make_plan(0, sink_end, rec_begin, T, ws, nslots);
-      HIP_TRY(launch_decode_valu(da, batch, stream));
-      nslots += da.plan.splits;
-    }
+    w.slot0 = p.splits;
+    da.plan = p;
+    da.win = w;
+    ca.nslots = p.splits + w.splits;
+    da.comb = ca;
+    const long pk = prof_begin(kv, 0, stream);
+    HIP_TRY(launch_decode_mfma(da, batch, kv->mfma_waves, stream));
+    prof_end(kv, 0, pk, stream);
+    nslots = p.splits + w.splits;
   } else {
     int want = kv->forced_splits > 0 ? kv->forced_splits
                                      : std::max(1, std::min(64, 2048 / std::max(1, BH)));
@@ -445,16 +462,10 @@ int oscar_int2_decode_attn(oscar_kv* kv, int32_t layer, const void* q, void* out
     nslots = da.plan.splits;
   }
   if (nslots > kMaxSplits) return fail(OSCAR_ERR_HIP, "internal: too many partial slots");
-  CombineArgs ca{};
-  ca.partials = kv->partials;
-  ca.rvT = kv->rvT + layer * DD;
-  ca.out = out;
-  ca.out_dtype = out_dtype;
-  ca.B = batch;
-  ca.Hq = Hq;
-  ca.D = D;
-  ca.nslots = nslots;
-  HIP_TRY(launch_combine(ca, stream));
+  if (!fast) {
+    ca.nslots = nslots;
+    HIP_TRY(launch_combine(ca, stream));
+  }
   prof_end(kv, 1, pcall, stream);
   return OSCAR_OK;
 }
@@ -499,8 +510,8 @@ int oscar_kv_device_bytes(const oscar_kv* kv, size_t* bytes) {
 
 int oscar_kv_set_num_splits(oscar_kv* kv, int32_t num_splits) {
   if (!kv) return fail(OSCAR_ERR_INVALID_ARG, "handle is NULL");
-  if (num_splits < 0 || num_splits > kMaxSplits - 8)
-    return fail(OSCAR_ERR_INVALID_ARG, "num_splits must be in [0, 248]");
+  if (num_splits < 0 || num_splits > kMaxSplits - kMaxWinSplits)
+    return fail(OSCAR_ERR_INVALID_ARG, "num_splits must be in [0, 224]");
   kv->forced_splits = num_splits;
   return OSCAR_OK;
 }
@@ -550,6 +561,13 @@ int oscar_kv_export(oscar_kv* kv, int32_t layer, int32_t which, void* host_codes
     HIP_TRY(hipMemcpy(host_sink, p.sink, (size_t)BH * c.sink_tokens * D * 2, hipMemcpyDeviceToHost));
   if (host_ring && c.recent_tokens > 0)
     HIP_TRY(hipMemcpy(host_ring, p.ring, (size_t)BH * c.recent_tokens * D * 2, hipMemcpyDeviceToHost));
+  return OSCAR_OK;
+}
+
+int oscar_stream_copy(const void* src, void* dst, size_t bytes, hipStream_t stream) {
+  if (bytes % 16 != 0) return fail(OSCAR_ERR_INVALID_ARG, "bytes must be a multiple of 16");
+  if (bytes > 0 && (!src || !dst)) return fail(OSCAR_ERR_INVALID_ARG, "NULL pointer");
+  HIP_TRY(launch_stream_copy(src, dst, bytes, stream));
   return OSCAR_OK;
 }
 

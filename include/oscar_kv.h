@@ -130,8 +130,10 @@ int oscar_kv_length(const oscar_kv* kv, int32_t layer, int32_t* tokens);
 /* Device bytes held by the handle. */
 int oscar_kv_device_bytes(const oscar_kv* kv, size_t* bytes);
 
-/* Force the number of INT2 splits per (sequence, kv head) used by decode
- * attention; 0 restores the automatic choice.  Errors: INVALID_ARG. */
+/* Force the number of splits per (sequence, kv head) used by decode attention
+ * (INT2 splits of the matrix-core kernel, or all-token splits of the VALU
+ * kernel), in [0, 224]; 0 restores the automatic choice.  The count is capped
+ * by the number of 64-token tiles.  Errors: INVALID_ARG. */
 int oscar_kv_set_num_splits(oscar_kv* kv, int32_t num_splits);
 
 /* Select the decode kernel: 0 = automatic (fused MFMA kernel where supported),
@@ -172,6 +174,12 @@ int oscar_quantize_rows(const float* x, int32_t rows, int32_t D, int32_t G, floa
  * class); profile_read synchronises the recorded events and returns the sum
  * of their durations in milliseconds and the launch count. */
 int oscar_kv_profile_enable(oscar_kv* kv, int32_t enable);
+
+/* Calibration kernel for bandwidth and hardware-counter measurements: a plain
+ * copy of `bytes` (a multiple of 16) from device buffer src to device buffer
+ * dst with 16-byte loads and stores, grid-strided.  Its algorithmic traffic is
+ * exactly `bytes` read and `bytes` written.  Errors: INVALID_ARG, HIP. */
+int oscar_stream_copy(const void* src, void* dst, size_t bytes, hipStream_t stream);
 int oscar_kv_profile_read(oscar_kv* kv, int32_t kernel_class, double* total_ms, int64_t* launches);
 
 #ifdef __cplusplus
