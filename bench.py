@@ -135,6 +135,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="qwen3-8b-attn-32k", choices=sorted(WORKLOADS))
     ap.add_argument("--splits", type=int, default=0, help="force INT2 splits (0 = auto)")
+    ap.add_argument("--separate", action="store_true",
+                    help="append and attention as two calls per layer instead of the fused step")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -175,7 +177,7 @@ def main():
     log(f"workload {args.workload}: L={L} B={B} Hq={Hq} Hkv={Hkv} D={D} T0={T0} N={N} M={M}")
     rk = synth.rotations(L, D, 0, "rot_k")
     rv = synth.rotations(L, D, 0, "rot_v")
-    cap = T0 + W + K + 64
+    cap = T0 + W + 2 * K + 64
     cache = ok.KVCache(L, B, Hq, Hkv, D, cap, N, M, 128, 0.96, 0.92, ok.KV_INT2, vdt, rk, rv, 0)
     if args.splits:
         cache.set_num_splits(args.splits)
@@ -188,7 +190,7 @@ def main():
     log(f"filled in {time.perf_counter() - t_fill:.1f} s")
 
     # per-step inputs, resident in HBM before timing
-    steps_total = W + K
+    steps_total = W + 2 * K
     g = torch.Generator(device=dev)
     g.manual_seed(synth.seed_of(0, 0, "step"))
     q_all = torch.randn((steps_total, L, B, Hq, D), generator=g, device=dev).to(torch.bfloat16)
@@ -198,17 +200,21 @@ def main():
     stream = torch.cuda.current_stream()
 
     def step(i):
+        # one decode step of the whole model's attention: per layer, append the
+        # new token's K/V and attend over the cache with the new q
         for l in range(L):
-            cache.append(l, k_all[i, l], v_all[i, l], stream)
-            cache.decode_attn(l, q_all[i, l], out, ok.OUT_F32, 0.0, stream)
+            if args.separate:
+                cache.append(l, k_all[i, l], v_all[i, l], stream)
+                cache.decode_attn(l, q_all[i, l], out, ok.OUT_F32, 0.0, stream)
+            else:
+                cache.decode_step(l, k_all[i, l], v_all[i, l], q_all[i, l], out, ok.OUT_F32, 0.0, stream)
 
     for i in range(W):
         step(i)
     torch.cuda.synchronize()
     log("warmup done")
 
-    # timed region: K steps, HIP events on the library's stream
-    cache.profile_enable(True)
+    # timed region: K steps, HIP events on the library's stream around them
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
@@ -221,17 +227,27 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t_wall
     ms_total = e0.elapsed_time(e1)
-    k_ms, k_n = cache.profile_read(0)
-    call_ms, call_n = cache.profile_read(1)
-    app_ms, app_n = cache.profile_read(2)
-    cache.profile_enable(False)
     ms_per_step = ms_total / K
     tokens_s = B * K / (ms_total / 1e3)
     log(f"{K} steps: {ms_total:.2f} ms (wall {wall * 1e3:.1f} ms, host enqueue {enqueue * 1e3:.1f} ms), "
         f"{ms_per_step:.3f} ms/step")
 
-    # bytes: every layer call attends over T = T0 + W + i + 1 tokens at step i
-    Ts = [T0 + W + i + 1 for i in range(K)]
+    # the same K steps again (the cache keeps growing) with per-launch HIP
+    # events that the library records on the stream it launches on: the
+    # dominant kernel's average duration, live
+    cache.profile_enable(True)
+    torch.cuda.synchronize()
+    for i in range(W + K, W + 2 * K):
+        step(i)
+    torch.cuda.synchronize()
+    k_ms, k_n = cache.profile_read(0)
+    call_ms, call_n = cache.profile_read(1)
+    app_ms, app_n = cache.profile_read(2)
+    cache.profile_enable(False)
+
+    # bytes: every layer call of the profiled pass attends over
+    # T = T0 + W + K + i + 1 tokens at its step i
+    Ts = [T0 + W + K + i + 1 for i in range(K)]
     kv_bytes_calls = sum(algorithmic_kv_bytes(B, Hkv, D, T, N, M, vdt == 1) for T in Ts) * L
     kv_gbs = kv_bytes_calls / (call_ms / 1e3) / 1e9 if call_ms > 0 else None
     # dominant kernel: the fused decode launch (INT2 splits on matrix cores, bf16
@@ -264,7 +280,8 @@ def main():
                    "parallelism": "none (1 GPU)"},
         "kv_gbps": None if kv_gbs is None else round(kv_gbs, 1),
         "kv_hbm_frac": None if kv_gbs is None else round(kv_gbs / HBM_PEAK_GBS, 4),
-        "decode_attn_us_per_call": round(call_ms / max(call_n, 1) * 1e3, 3),
+        "step_mode": "separate" if args.separate else "fused",
+        "attn_us_per_call": round(call_ms / max(call_n, 1) * 1e3, 3),
         "append_us_per_call": round(app_ms / max(app_n, 1) * 1e3, 3),
         "host_enqueue_ms_per_step": round(enqueue * 1e3 / K, 4),
         "roofline": roof,

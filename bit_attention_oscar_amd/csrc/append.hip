@@ -1,214 +1,22 @@
-// Append path: rotate, write the bf16 window copy, clip + INT2-quantize + pack.
-// Built with -ffp-contract=off and correctly rounded fp32 division so the
-// quantizer performs exactly one IEEE rounding per operation.
-//
-// Method (web pages on OSCAR): rotation of post-RoPE K and V by one orthogonal
-// head_dim x head_dim matrix per layer ("OSCAR-LLAMACPP-Qwen3-4B-Thinking-2507-
-// INT2-KV", "Files" note; "OSCAR-RotationZoo", "File format"); clip before
-// quantization (Qwen3-4B card, "Run" env-var table; K 0.96 / V 0.92 in the
-// RotationZoo card, "How to use" step 2); INT2 with group 128 along head_dim
-// (RotationZoo card, same flags); bf16 sink and recent window (Qwen3-4B card,
-// "Run" table; "OSCAR: 2-bit KV Cache Quantization for SGLang and llama.cpp",
-// "What OSCAR compresses").
+// Append kernels (rotate, bf16 window copy, clip + INT2-quantize + pack; the
+// device code is in append_impl.h), the quantizer test hook, the canonical
+// export of the tiled V codes and the copy calibration kernel.
 #include <algorithm>
-#include "common.h"
+#include "append_impl.h"
 
 namespace oscar {
 
-__device__ inline float wave_max(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
-  return v;
-}
-
-__device__ inline float wave_min(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v = fminf(v, __shfl_xor(v, o));
-  return v;
-}
-
-struct GroupQ {
-  float sf, zf;      // stored scale / zero widened to fp32
-  uint32_t packed;   // fp16 scale bits | fp16 zero bits << 16
-};
-
-// Keeps a value as a materialised fp32 register: stops the compiler from
-// folding the product into a mixed-precision fma that rounds straight to fp16
-// (one rounding of the exact product instead of fp32 then fp16).
-__device__ inline float as_f32(float v) {
-  asm volatile("" : "+v"(v));
-  return v;
-}
-
-// hi = r*max, lo = r*min, s = (hi - lo)/3; fp16 RNE of s and lo.
-__device__ inline GroupQ group_params(float mx, float mn, float r) {
-  const float hi = as_f32(r * mx);
-  const float lo = as_f32(r * mn);
-  const float s = as_f32((hi - lo) / 3.0f);
-  const _Float16 s16 = (_Float16)s;
-  const _Float16 z16 = (_Float16)lo;
-  GroupQ g;
-  g.sf = (float)s16;
-  g.zf = (float)z16;
-  g.packed = (uint32_t)__builtin_bit_cast(uint16_t, s16) |
-             ((uint32_t)__builtin_bit_cast(uint16_t, z16) << 16);
-  return g;
-}
-
-// c = clamp(rint((x - z)/s), 0, 3), round half to even; 0 when s == 0.
-__device__ inline uint32_t quant_code(float x, const GroupQ& g) {
-  if (g.sf == 0.0f) return 0u;
-  float t = (x - g.zf) / g.sf;
-  t = __builtin_rintf(t);
-  t = fminf(fmaxf(t, 0.0f), 3.0f);
-  return (uint32_t)t;
-}
-
-// Canonical packing through lane shuffles: lane l holds the code of dim
-// l + 64 i; word w (dims 16w..16w+15) is OR-reduced over the 16 lanes
-// 16 (w % 4) .. + 15 of element i = w / 4 and stored by its first lane.
-template <int PER>
-__device__ inline void store_canonical(const uint32_t* code, int lane, uint8_t* row) {
-#pragma unroll
-  for (int i = 0; i < PER; ++i) {
-    uint32_t v = code[i] << (2 * (lane & 15));
-    v |= __shfl_xor(v, 1);
-    v |= __shfl_xor(v, 2);
-    v |= __shfl_xor(v, 4);
-    v |= __shfl_xor(v, 8);
-    if ((lane & 15) == 0) *reinterpret_cast<uint32_t*>(row + 4 * (4 * i + (lane >> 4))) = v;
-  }
-}
-
 // Block per (sequence, kv head, 8-token group); blockIdx.z: 0 = K, 1 = V.
-// NT token slots (1 for a one-token append, 8 otherwise).  The reduction over
-// e of the rotation is split across WAVES waves (partial sums added in a fixed
-// order); wave 0 then quantizes and stores.  Wave 0's lane l owns dims
-// l + 64 i, so it also owns the V tile bytes of those dims for every token of
-// the group (tiled-layout bytes are shared only among tokens of one group of
-// 8 at one dim, and one block handles the whole group).
+// NT token slots (1 for a one-token append, 8 otherwise); the rotation's
+// reduction over e is split across WAVES waves.
 template <int D, int WAVES, int NT>
 __global__ __launch_bounds__(64 * WAVES) void append_kernel(AppendArgs a) {
-  constexpr int PER = D / 64;
-  constexpr int EW = D / WAVES;
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const int bh = blockIdx.x;
-  const int b = bh / a.Hkv, h = bh - (bh / a.Hkv) * a.Hkv;
-  const bool isv = blockIdx.z != 0;
-  const PlaneDev P = isv ? a.v : a.k;
-  const uint16_t* in = isv ? a.vin : a.kin;
-  const float* R = isv ? a.rv : a.rk;
-  float* dump = isv ? a.vdump : a.kdump;
+  __shared__ float xs[NT * D];
+  __shared__ float part[WAVES * NT * D];
   const int g8 = (a.T_old >> 3) + (int)blockIdx.y;
   const int t_lo = NT == 1 ? a.T_old : max(a.T_old, g8 * 8);
   const int t_hi = NT == 1 ? a.T_old + 1 : min(a.T_new, g8 * 8 + 8);
-  const int ntok = t_hi - t_lo;
-
-  __shared__ float xs[NT][D];
-  __shared__ float part[WAVES][NT][D];
-  for (int i = tid; i < NT * D; i += 64 * WAVES) {
-    const int tk = i / D, d = i - (i / D) * D;
-    float v = 0.0f;
-    if (tk < ntok) {
-      const int t = t_lo + tk;
-      const size_t idx = (((size_t)b * a.n_new + (t - a.T_old)) * a.Hkv + h) * D + d;
-      v = bf16_to_f32(in[idx]);
-    }
-    xs[tk][d] = v;
-  }
-  __syncthreads();
-
-  // partial x_rot[d] = sum over this wave's e of x[e] * R[e][d], e ascending
-  float acc[NT][PER];
-#pragma unroll
-  for (int tk = 0; tk < NT; ++tk)
-#pragma unroll
-    for (int i = 0; i < PER; ++i) acc[tk][i] = 0.0f;
-  const float* Rw = R + (size_t)(wave * EW) * D + lane;
-#pragma unroll 8
-  for (int e = 0; e < EW; ++e) {
-    float r[PER];
-#pragma unroll
-    for (int i = 0; i < PER; ++i) r[i] = Rw[(size_t)e * D + 64 * i];
-#pragma unroll
-    for (int tk = 0; tk < NT; ++tk) {
-      const float x = xs[tk][wave * EW + e];
-#pragma unroll
-      for (int i = 0; i < PER; ++i) acc[tk][i] = __builtin_fmaf(x, r[i], acc[tk][i]);
-    }
-  }
-  if (WAVES > 1) {
-#pragma unroll
-    for (int tk = 0; tk < NT; ++tk)
-#pragma unroll
-      for (int i = 0; i < PER; ++i) part[wave][tk][lane + 64 * i] = acc[tk][i];
-    __syncthreads();
-    if (wave != 0) return;
-  }
-
-#pragma unroll
-  for (int tk = 0; tk < NT; ++tk) {
-    if (tk >= ntok) break;
-    const int t = t_lo + tk;
-    float x[PER];
-#pragma unroll
-    for (int i = 0; i < PER; ++i) {
-      float v = acc[tk][i];
-      if (WAVES > 1) {
-        const int d = lane + 64 * i;
-        v = part[0][tk][d];
-#pragma unroll
-        for (int w = 1; w < WAVES; ++w) v = v + part[w][tk][d];
-      }
-      x[i] = v + 0.0f;   // -0 -> +0
-    }
-    if (dump) {
-      const size_t base = (((size_t)b * a.n_new + (t - a.T_old)) * a.Hkv + h) * D;
-#pragma unroll
-      for (int i = 0; i < PER; ++i) dump[base + lane + 64 * i] = x[i];
-    }
-    if (P.is_bf16) {
-      const size_t base = row_offset(bh, a.cap, t, D);
-#pragma unroll
-      for (int i = 0; i < PER; ++i) P.full[base + lane + 64 * i] = f32_to_bf16(x[i]);
-      continue;
-    }
-    if (t < a.N) {
-      const size_t base = row_offset(bh, a.N, t, D);
-#pragma unroll
-      for (int i = 0; i < PER; ++i) P.sink[base + lane + 64 * i] = f32_to_bf16(x[i]);
-    }
-    if (a.M > 0 && t >= a.N && t >= a.T_new - a.M) {
-      const size_t base = row_offset(bh, a.M, t % a.M, D);
-#pragma unroll
-      for (int i = 0; i < PER; ++i) P.ring[base + lane + 64 * i] = f32_to_bf16(x[i]);
-    }
-    uint32_t code[PER];
-#pragma unroll
-    for (int g = 0; g < D / kGroup; ++g) {
-      // group g = dims [128 g, 128 g + 128) = elements 2g, 2g+1 of every lane
-      const float mx = wave_max(fmaxf(x[2 * g], x[2 * g + 1]));
-      const float mn = wave_min(fminf(x[2 * g], x[2 * g + 1]));
-      const GroupQ q = group_params(mx, mn, P.clip);
-      code[2 * g] = quant_code(x[2 * g], q);
-      code[2 * g + 1] = quant_code(x[2 * g + 1], q);
-      if (lane == 0) {
-        P.meta[meta_offset(bh, a.cap, t, D) + g] = q.packed;
-        if (P.smax) atomicMax(reinterpret_cast<unsigned int*>(P.smax + bh), __float_as_uint(q.sf));
-      }
-    }
-    if (!P.tiled) {
-      store_canonical<PER>(code, lane, P.codes + kcode_offset(bh, a.cap, t, D));
-    } else {
-#pragma unroll
-      for (int i = 0; i < PER; ++i) {
-        int bit;
-        const size_t off = vcode_byte(bh, a.cap, t, lane + 64 * i, D, &bit);
-        const uint8_t old = P.codes[off];
-        P.codes[off] = (uint8_t)((old & ~(3u << bit)) | (code[i] << bit));
-      }
-    }
-  }
+  append_block<D, WAVES, NT>(a, (int)blockIdx.x, blockIdx.z != 0, t_lo, t_hi, xs, part);
 }
 
 // Test hook: the same quantizer on fp32 rows, canonical packing.

@@ -10,6 +10,7 @@ namespace oscar {
 constexpr int kGroup = 128;           // quantization group along head_dim
 constexpr int kTile = 64;             // tokens per decode tile / V storage block
 constexpr int kMaxSplits = 256;       // partial-result slots per (sequence, head)
+constexpr int kQPub = 4 * 128 + 8;    // published q of one (sequence, kv head): 4 heads x 128, sums, exponents
 constexpr int kMaxGq = 16;            // query heads per kv head handled by the VALU kernel
 
 // ---------------------------------------------------------------------------
@@ -107,11 +108,8 @@ struct QRotArgs {
   const uint16_t* q;      // bf16 [B][Hq][D]
   const float* rk;        // fp32 [D][D]
   float* qrot;            // fp32 [B][Hq][D], q @ R_K * scale * log2(e)
-  float* qaux;            // [B][Hq][8]: per-group sums of qrot (4), cK, 0...
-  uint16_t* qswz;         // fp16 operand registers for the matrix-core kernel
   int B, Hq, Hkv, D;
   float scale_log2;
-  int want_swz;
 };
 
 struct SegPlan {           // up to two token segments, split into `splits` chunks
@@ -131,9 +129,11 @@ struct CombineArgs {
 
 struct DecodeArgs {
   PlaneDev k, v;
-  const float* qrot;
-  const float* qaux;
-  const uint16_t* qswz;
+  const float* qrot;       // rotated q of the general kernel
+  float* qpub;             // [B*Hkv][kQPub]: rotated q published by the first attention
+                           // block of each (sequence, kv head) in a matrix-core launch
+  unsigned* qflag;         // [B*Hkv]: epoch of the launch whose q qpub holds
+  unsigned epoch;          // this launch's number (never 0)
   float* partials;         // [B][Hq][kMaxSplits][D+2]
   int Hq, Hkv, D, cap, N, M, T;
   SegPlan plan;            // INT2 range (matrix-core kernel) or all tokens (VALU kernel)
@@ -142,6 +142,11 @@ struct DecodeArgs {
   unsigned* counters;      // [B*Hkv] finished blocks per (sequence, kv head); every
                            // entry is zero between launches (the last block resets it)
   CombineArgs comb;        // merge done by the last block of each (sequence, kv head)
+  const uint16_t* q;       // bf16 [B][Hq][D] (matrix-core launch rotates q itself)
+  const float* rk;         // fp32 [D][D] of this layer
+  float scale_log2;        // softmax scale * log2(e)
+  int app_blocks;          // 2 when the launch also appends this step's token, else 0
+  AppendArgs app;          // that append (n_new = 1); T above counts the new token
 };
 
 // launchers (defined in the .hip files); return hipGetLastError()

@@ -19,7 +19,7 @@
 //                       4x4x4 f16 matrix-core QK^T and PV on raw codes
 //   combine_kernel      log-sum-exp merge of the splits and o = o' @ R_V^T
 #include <math.h>
-#include "common.h"
+#include "append_impl.h"
 
 namespace oscar {
 
@@ -41,9 +41,6 @@ typedef float f4 __attribute__((ext_vector_type(4)));
 #endif
 #ifndef OSCAR_MFMA_WAVES_PER_EU
 #define OSCAR_MFMA_WAVES_PER_EU 4
-#endif
-#ifndef OSCAR_PREFETCH
-#define OSCAR_PREFETCH 1
 #endif
 
 __device__ inline float wmax(float v) {
@@ -72,94 +69,30 @@ __host__ __device__ inline int qk_dim(int w, int pp, int k) {
   return 16 * w + 2 * pp + (k & 2 ? 1 : 0) + (k & 1 ? 8 : 0);
 }
 
-// One block per (sequence, kv head); its query heads are processed in chunks
-// of four.  The 128- or 512-long reduction over e is split across the four
-// waves (64 independent R loads in flight per lane) and the partial sums are
-// added in a fixed order.
+// q rotation for the general kernel: one block per (sequence, kv head), its
+// query heads in chunks of four, with the rotation routine of the append path
+// (reduction over e split across the four waves, fixed-order partial sums).
 template <int D>
 __global__ __launch_bounds__(256) void qrot_kernel(QRotArgs a) {
-  constexpr int PER = D / 64;       // dims per lane
-  constexpr int EW = D / 4;         // e values per wave
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int tid = threadIdx.x;
   const int bh = blockIdx.x;        // b * Hkv + kvh
   const int b = bh / a.Hkv, kvh = bh - (bh / a.Hkv) * a.Hkv;
   const int Gq = a.Hq / a.Hkv;
-  __shared__ float xs[4][D];
-  __shared__ float part[4][4][D];
-  __shared__ float red[4][8];
+  __shared__ float xs[4 * D];
+  __shared__ float part[4 * 4 * D];
   for (int hc = 0; hc < Gq; hc += 4) {
     const int nh = min(4, Gq - hc);
     const int head0 = kvh * Gq + hc;
     for (int i = tid; i < 4 * D; i += 256) {
       const int j = i / D, d = i - (i / D) * D;
-      xs[j][d] = j < nh ? bf16_to_f32(a.q[((size_t)b * a.Hq + head0 + j) * D + d]) : 0.0f;
+      xs[i] = j < nh ? bf16_to_f32(a.q[((size_t)b * a.Hq + head0 + j) * D + d]) : 0.0f;
     }
     __syncthreads();
-    float acc[4][PER];
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-#pragma unroll
-      for (int i = 0; i < PER; ++i) acc[j][i] = 0.0f;
-    const float* R = a.rk + (size_t)(wave * EW) * D + lane;
-#pragma unroll 8
-    for (int e = 0; e < EW; ++e) {
-      float r[PER];
-#pragma unroll
-      for (int i = 0; i < PER; ++i) r[i] = R[(size_t)e * D + 64 * i];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const float x = xs[j][wave * EW + e];
-#pragma unroll
-        for (int i = 0; i < PER; ++i) acc[j][i] = __builtin_fmaf(x, r[i], acc[j][i]);
-      }
-    }
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-#pragma unroll
-      for (int i = 0; i < PER; ++i) part[wave][j][lane + 64 * i] = acc[j][i];
+    rotate_rows<D, 4, 4>(xs, a.rk, part, 4);
     __syncthreads();
-    // wave j finishes head j: sum the four partials, scale, group sums and max |q|
-    if (wave < nh) {
-      const int j = wave, head = head0 + j;
-      float gs[4] = {0, 0, 0, 0};
-      float amax = 0.0f;
-#pragma unroll
-      for (int i = 0; i < PER; ++i) {
-        const int d = lane + 64 * i;
-        const float v = (((part[0][j][d] + part[1][j][d]) + part[2][j][d]) + part[3][j][d]) * a.scale_log2;
-        xs[j][d] = v;
-        a.qrot[((size_t)b * a.Hq + head) * D + d] = v;
-        gs[i / 2] += v;
-        amax = fmaxf(amax, fabsf(v));
-      }
-#pragma unroll
-      for (int g = 0; g < 4; ++g) gs[g] = wsum(gs[g]);
-      amax = wmax(amax);
-      int e2 = 0;
-      if (amax > 0.0f) frexpf(amax, &e2);
-      const int eq = (amax > 0.0f) ? 15 - e2 : 0;        // |q| * 2^eq < 2^15
-      if (lane < 8) {
-        float v = 0.0f;
-        if (lane < 4) v = gs[lane];
-        if (lane == 4) v = ldexpf(1.0f, 24 - eq);          // cK: undoes 2^eq and the 2^-24 code scale
-        a.qaux[((size_t)b * a.Hq + head) * 8 + lane] = v;
-      }
-      if (lane == 0) red[j][0] = (float)eq;
-    }
-    __syncthreads();
-    if (a.want_swz && D == 128 && Gq == 4) {
-      // fp16 operand registers: [b*Hkv + kvh][lane 64][w 8][k 4], lane = 4*blk + j
-      // holds query head j; the four blocks of lane group pp hold the same
-      // chunk (w, pp), broadcast by the instruction.
-      uint16_t* dst = a.qswz + (size_t)bh * 64 * 32;
-      for (int e = tid; e < 64 * 32; e += 256) {
-        const int lane_id = e >> 5, w = (e >> 2) & 7, k = e & 3;
-        const int j = lane_id & 3, pp = lane_id >> 4;
-        const int d = qk_dim(w, pp, k);
-        const int eq = (int)red[j][0];
-        const float v = ldexpf(xs[j][d], eq - 2 * (d & 3));
-        dst[e] = __builtin_bit_cast(uint16_t, (_Float16)v);
-      }
+    for (int i = tid; i < nh * D; i += 256) {
+      const int j = i / D, d = i - (i / D) * D;
+      a.qrot[((size_t)b * a.Hq + head0 + j) * D + d] = rot_sum<D, 4, 4>(part, j, d) * a.scale_log2;
     }
     __syncthreads();
   }
@@ -459,7 +392,16 @@ __device__ void combine_group(const CombineArgs& a, int bh) {
       float acc = 0.0f;
       if (j < nh) {
         const float* P = a.partials + ((size_t)b * a.Hq + kvh * Gq + hc + j) * kMaxSplits * (D + 2);
-        for (int sl = 0; sl < a.nslots; ++sl)
+        // eight independent loads in flight per step
+        int sl = 0;
+        for (; sl + 8 <= a.nslots; sl += 8) {
+          float v[8];
+#pragma unroll
+          for (int u = 0; u < 8; ++u) v[u] = ld_partial<COHERENT>(P + (size_t)(sl + u) * (D + 2) + d);
+#pragma unroll
+          for (int u = 0; u < 8; ++u) acc = __builtin_fmaf(v[u], wsl[j][sl + u], acc);
+        }
+        for (; sl < a.nslots; ++sl)
           acc = __builtin_fmaf(ld_partial<COHERENT>(P + (size_t)sl * (D + 2) + d), wsl[j][sl], acc);
         acc *= linv[j];
       }
@@ -557,18 +499,123 @@ __device__ inline void bf16x8(const uint4 u, float* x) {
   }
 }
 
-__device__ void window_block(const DecodeArgs& a, int bh, int b, int h, int wblk) {
+// Shared memory of the fused launch; each block role uses its own regions and
+// the scratch area is reused phase by phase.
+struct FusedSmem {
+  float qs[4][132];            // rotated q of the block's 4 heads (fp32, x scale*log2 e)
+  float qsum[4];               // per-head sums of qs
+  int qeq[4];                  // per-head exponent of the fp16 q operand
+  int ready;                   // the published q of this launch is available
+  uint16_t newtok[2][128];     // bf16 window values of the token appended by this launch
+  float scratch[2688];
+};
+
+// q rotation of the block's 4 query heads (same arithmetic for every block).
+__device__ void block_rotate_q(const DecodeArgs& a, int b, int h, FusedSmem& S) {
+  constexpr int D = 128;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  float* qraw = S.scratch;            // [4][128]
+  float* part = S.scratch + 512;      // [4 waves][4][128]
+  for (int i = tid; i < 4 * D; i += 256)
+    qraw[i] = bf16_to_f32(a.q[((size_t)b * a.Hq + h * 4 + (i >> 7)) * D + (i & 127)]);
+  __syncthreads();
+  rotate_rows<128, 4, 4>(qraw, a.rk, part, 4);
+  __syncthreads();
+  {
+    const int j = wave;                // wave j finishes head j
+    const float v0 = rot_sum<128, 4, 4>(part, j, lane) * a.scale_log2;
+    const float v1 = rot_sum<128, 4, 4>(part, j, lane + 64) * a.scale_log2;
+    S.qs[j][lane] = v0;
+    S.qs[j][lane + 64] = v1;
+    const float sum = wsum(v0 + v1);
+    const float amax = wmax(fmaxf(fabsf(v0), fabsf(v1)));
+    int e2 = 0;
+    if (amax > 0.0f) frexpf(amax, &e2);
+    if (lane == 0) {
+      S.qsum[j] = sum;
+      S.qeq[j] = (amax > 0.0f) ? 15 - e2 : 0;     // |q| * 2^eq < 2^15
+    }
+  }
+  __syncthreads();
+}
+
+// The first attention block of each (sequence, kv head) publishes its rotated
+// q for the other blocks of the launch: device-scope stores, a wait until they
+// have completed, then this launch's epoch in the flag.  A block that finds
+// the flag holding this launch's epoch reads q back with device-scope loads;
+// any other block rotates q itself.  No block ever waits for another, and both
+// routes give identical bits.
+__device__ void publish_q(const DecodeArgs& a, int bh, FusedSmem& S) {
+  float* dst = a.qpub + (size_t)bh * kQPub;
+  for (int i = threadIdx.x; i < 4 * 128; i += blockDim.x) st_partial(dst + i, S.qs[i >> 7][i & 127]);
+  if (threadIdx.x < 4) {
+    st_partial(dst + 512 + threadIdx.x, S.qsum[threadIdx.x]);
+    st_partial(dst + 516 + threadIdx.x, __int_as_float(S.qeq[threadIdx.x]));
+  }
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  if (threadIdx.x == 0) __hip_atomic_store(a.qflag + bh, a.epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ void obtain_q(const DecodeArgs& a, int b, int h, int bh, FusedSmem& S) {
+  if (threadIdx.x == 0)
+    S.ready = __hip_atomic_load(a.qflag + bh, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == a.epoch;
+  __syncthreads();
+  if (!S.ready) {
+    block_rotate_q(a, b, h, S);
+    return;
+  }
+  const float* src = a.qpub + (size_t)bh * kQPub;
+  for (int i = threadIdx.x; i < 4 * 128; i += blockDim.x) S.qs[i >> 7][i & 127] = ld_partial<true>(src + i);
+  if (threadIdx.x < 4) {
+    S.qsum[threadIdx.x] = ld_partial<true>(src + 512 + threadIdx.x);
+    S.qeq[threadIdx.x] = __float_as_int(ld_partial<true>(src + 516 + threadIdx.x));
+  }
+  __syncthreads();
+}
+
+// q of the block's 4 query heads: attention block 0 of the (sequence, kv head)
+// rotates and publishes it, the others take the published copy when it is there.
+__device__ inline void block_q(const DecodeArgs& a, int b, int h, int bh, int y, FusedSmem& S) {
+  if (y == 0) {
+    block_rotate_q(a, b, h, S);
+    publish_q(a, bh, S);
+  } else {
+    obtain_q(a, b, h, bh, S);
+  }
+}
+
+// bf16 window tokens (sink + recent) of one (sequence, kv head): a block takes
+// up to win.chunk of them (64 per step) with fp32 VALU arithmetic.  When the
+// launch also appends a token, that token is the last window position; its
+// window value is computed here from the input with the append's own
+// arithmetic instead of being read back (the append role writes it in this
+// same launch).
+__device__ void window_block(const DecodeArgs& a, int bh, int b, int h, int wblk, FusedSmem& S) {
   constexpr int D = 128;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int len = (a.win.b0 - a.win.a0) + (a.win.b1 - a.win.a1);
   const int v_lo = wblk * a.win.chunk;
   const int v_hi = min(len, v_lo + a.win.chunk);
-  __shared__ float qs[4][D + 4];
-  __shared__ float sc[4][64];
-  __shared__ float wm[4], wl[4], wa[4];
-  __shared__ float red[4][4][D];
-  for (int i = tid; i < 4 * D; i += 256)
-    qs[i >> 7][i & 127] = a.qrot[((size_t)b * a.Hq + h * 4 + (i >> 7)) * D + (i & 127)];
+  const int t_new = (a.app_blocks > 0 && v_hi == len) ? a.T - 1 : -1;
+  if (t_new >= 0) {
+    for (int which = 0; which < 2; ++which) {
+      const uint16_t* in = which ? a.app.vin : a.app.kin;
+      float* xs = S.scratch;          // [128]
+      float* part = S.scratch + 128;  // [4][128]
+      if (tid < D) xs[tid] = bf16_to_f32(in[((size_t)b * a.Hkv + h) * D + tid]);
+      __syncthreads();
+      rotate_rows<128, 4, 1>(xs, which ? a.app.rv : a.app.rk, part, 1);
+      __syncthreads();
+      if (tid < D) S.newtok[which][tid] = f32_to_bf16(rot_sum<128, 4, 1>(part, 0, tid));
+      __syncthreads();
+    }
+  }
+  float* sc = S.scratch;               // [4][64]
+  float* wm = S.scratch + 256;         // [4] running max
+  float* wl = S.scratch + 260;         // [4] running sum
+  float* wa = S.scratch + 264;         // [4] rescale factor
+  float* red = S.scratch + 272;        // [4 waves][4][128]
   if (tid < 4) {
     wm[tid] = NEG_INF;
     wl[tid] = 0.0f;
@@ -587,8 +634,14 @@ __device__ void window_block(const DecodeArgs& a, int bh, int b, int h, int wblk
       float dots[4] = {0.0f, 0.0f, 0.0f, 0.0f};
       if (tok < n) {
         const int t = win_token(a.win, vt0 + tok);
-        const uint4* rp = reinterpret_cast<const uint4*>(win_row(a.k, bh, t, a.N, a.M, D) + 32 * part);
-        const uint4 us[4] = {rp[0], rp[1], rp[2], rp[3]};
+        uint4 us[4];
+        if (t == t_new) {
+          const uint4* rp = reinterpret_cast<const uint4*>(&S.newtok[0][32 * part]);
+          us[0] = rp[0]; us[1] = rp[1]; us[2] = rp[2]; us[3] = rp[3];
+        } else {
+          const uint4* rp = reinterpret_cast<const uint4*>(win_row(a.k, bh, t, a.N, a.M, D) + 32 * part);
+          us[0] = rp[0]; us[1] = rp[1]; us[2] = rp[2]; us[3] = rp[3];
+        }
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           float x[8];
@@ -596,7 +649,7 @@ __device__ void window_block(const DecodeArgs& a, int bh, int b, int h, int wblk
 #pragma unroll
           for (int k = 0; k < 8; ++k)
 #pragma unroll
-            for (int j = 0; j < 4; ++j) dots[j] = __builtin_fmaf(qs[j][32 * part + 8 * i + k], x[k], dots[j]);
+            for (int j = 0; j < 4; ++j) dots[j] = __builtin_fmaf(S.qs[j][32 * part + 8 * i + k], x[k], dots[j]);
         }
       }
 #pragma unroll
@@ -606,16 +659,16 @@ __device__ void window_block(const DecodeArgs& a, int bh, int b, int h, int wblk
       }
       if (part == 0)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) sc[j][tok] = tok < n ? dots[j] : NEG_INF;
+        for (int j = 0; j < 4; ++j) sc[j * 64 + tok] = tok < n ? dots[j] : NEG_INF;
     }
     __syncthreads();
     {  // online softmax update, one wave per head
-      const float sv = sc[wave][lane];
+      const float sv = sc[wave * 64 + lane];
       const float mold = wm[wave];
       const float mnew = fmaxf(mold, wmax(sv));
       const float p = (sv == NEG_INF) ? 0.0f : exp2f(sv - mnew);
       const float l = wsum(p);
-      sc[wave][lane] = p;
+      sc[wave * 64 + lane] = p;
       if (lane == 0) {
         const float alpha = (mold == NEG_INF) ? 0.0f : exp2f(mold - mnew);
         wa[wave] = alpha;
@@ -632,7 +685,10 @@ __device__ void window_block(const DecodeArgs& a, int bh, int b, int h, int wblk
         u[i] = make_uint4(0, 0, 0, 0);
         if (tok < n) {
           const int t = win_token(a.win, vt0 + tok);
-          u[i] = *reinterpret_cast<const uint4*>(win_row(a.v, bh, t, a.N, a.M, D) + 8 * c);
+          if (t == t_new)
+            u[i] = *reinterpret_cast<const uint4*>(&S.newtok[1][8 * c]);
+          else
+            u[i] = *reinterpret_cast<const uint4*>(win_row(a.v, bh, t, a.N, a.M, D) + 8 * c);
         }
       }
 #pragma unroll
@@ -649,7 +705,7 @@ __device__ void window_block(const DecodeArgs& a, int bh, int b, int h, int wblk
           bf16x8(u[i], x);
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
-            const float p = sc[j][tok];
+            const float p = sc[j * 64 + tok];
 #pragma unroll
             for (int k = 0; k < 8; ++k) o[j][k] = __builtin_fmaf(p, x[k], o[j][k]);
           }
@@ -669,13 +725,13 @@ __device__ void window_block(const DecodeArgs& a, int bh, int b, int h, int wblk
 #pragma unroll
     for (int j = 0; j < 4; ++j)
 #pragma unroll
-      for (int k = 0; k < 8; ++k) red[wave][j][8 * c + k] = o[j][k];
+      for (int k = 0; k < 8; ++k) red[(wave * 4 + j) * D + 8 * c + k] = o[j][k];
   __syncthreads();
   const int slot = a.win.slot0 + wblk;
   for (int idx = tid; idx < 4 * D; idx += 256) {
     const int j = idx >> 7, d = idx & 127;
     float* dst = a.partials + (((size_t)b * a.Hq + h * 4 + j) * kMaxSplits + slot) * (D + 2);
-    st_partial(dst + d, ((red[0][j][d] + red[1][j][d]) + red[2][j][d]) + red[3][j][d]);
+    st_partial(dst + d, ((red[j * D + d] + red[(4 + j) * D + d]) + red[(8 + j) * D + d]) + red[(12 + j) * D + d]);
     if (d == 0) {
       st_partial(dst + D, wm[j]);
       st_partial(dst + D + 1, wl[j]);
@@ -709,42 +765,54 @@ __device__ inline float lane_value(float v, int lane) {
   return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), lane));
 }
 
+typedef uint32_t u4 __attribute__((ext_vector_type(4)));
+
 struct TileRegs {
-  uint4 k0, k1;   // K codes of token tile + lane (32 bytes)
-  uint4 km, vm;   // K and V scale|zero of tokens tile + 4 blk .. + 3
-  uint4 v0, v1;   // V code record of this lane (32 bytes)
+  u4 k0, k1;   // K codes of token tile + lane (32 bytes)
+  u4 km, vm;   // K and V scale|zero of tokens tile + 4 blk .. + 3
+  u4 v0, v1;   // V code record of this lane (32 bytes)
 };
 
-// Per-wave stream pointers: uniform tile bases (scalar registers) plus fixed
-// per-lane offsets, advanced by a whole tile at a time.
+// The four INT2 streams of one (sequence, kv head) as buffer resources: the
+// plane base is uniform (scalar registers), each lane adds a fixed 32-bit
+// offset and each tile a uniform one, so no 64-bit address arithmetic runs per
+// tile.  A resource covers exactly that (sequence, kv head)'s part of the plane.
 struct TileStreams {
-  const uint8_t* kc;    // K codes of the tile's first token
-  const uint8_t* km;    // K meta of the tile's first token
-  const uint8_t* vm;    // V meta
-  const uint8_t* vc;    // V code tile
+  __amdgpu_buffer_rsrc_t kc;   // K codes, 32 bytes per token
+  __amdgpu_buffer_rsrc_t km;   // K scale|zero, 4 bytes per token
+  __amdgpu_buffer_rsrc_t vm;   // V scale|zero
+  __amdgpu_buffer_rsrc_t vc;   // V code tiles, 2 KiB per 64 tokens (32 bytes per token)
 };
 
-__device__ inline TileRegs load_tile(const TileStreams& s, int lane_k, int lane_m, int lane_v) {
-  TileRegs r;
-  const uint4* kp = reinterpret_cast<const uint4*>(s.kc + lane_k);
-  r.k0 = kp[0];
-  r.k1 = kp[1];
-  r.km = *reinterpret_cast<const uint4*>(s.km + lane_m);
-  r.vm = *reinterpret_cast<const uint4*>(s.vm + lane_m);
-  const uint4* vp = reinterpret_cast<const uint4*>(s.vc + lane_v);
-  r.v0 = vp[0];
-  r.v1 = vp[1];
-  return r;
+constexpr int kBufferConfig = 0x00020000;   // raw 32-bit data, no swizzle (gfx9 family)
+
+__device__ inline __amdgpu_buffer_rsrc_t plane_rsrc(const void* base, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes, kBufferConfig);
 }
 
-__device__ inline TileStreams tile_streams(const DecodeArgs& a, int bh, int t0) {
+__device__ inline TileStreams tile_streams(const DecodeArgs& a, int bh) {
   constexpr int D = 128;
   TileStreams s;
-  s.kc = a.k.codes + kcode_offset(bh, a.cap, t0, D);
-  s.km = reinterpret_cast<const uint8_t*>(a.k.meta + meta_offset(bh, a.cap, t0, D));
-  s.vm = reinterpret_cast<const uint8_t*>(a.v.meta + meta_offset(bh, a.cap, t0, D));
-  s.vc = a.v.codes + ((size_t)bh * (a.cap / kTile) + (t0 >> 6)) * 2048;
+  s.kc = plane_rsrc(a.k.codes + kcode_offset(bh, a.cap, 0, D), a.cap * 32);
+  s.km = plane_rsrc(a.k.meta + meta_offset(bh, a.cap, 0, D), a.cap * 4);
+  s.vm = plane_rsrc(a.v.meta + meta_offset(bh, a.cap, 0, D), a.cap * 4);
+  s.vc = plane_rsrc(a.v.codes + (size_t)bh * (a.cap / kTile) * 2048, a.cap * 32);
   return s;
+}
+
+// Loads of the tile starting at token t0 (a multiple of 64).  Code streams:
+// lane l reads the 32 bytes of token t0 + l (K) and V record l of the tile;
+// metadata: lane (blk, j) reads tokens t0 + 4 blk .. + 3.
+__device__ inline TileRegs load_tile(const TileStreams& s, int t0, int lane_c, int lane_m) {
+  const int oc = t0 * 32, om = t0 * 4;
+  TileRegs r;
+  r.k0 = __builtin_amdgcn_raw_buffer_load_b128(s.kc, lane_c, oc, 0);
+  r.k1 = __builtin_amdgcn_raw_buffer_load_b128(s.kc, lane_c + 16, oc, 0);
+  r.km = __builtin_amdgcn_raw_buffer_load_b128(s.km, lane_m, om, 0);
+  r.vm = __builtin_amdgcn_raw_buffer_load_b128(s.vm, lane_m, om, 0);
+  r.v0 = __builtin_amdgcn_raw_buffer_load_b128(s.vc, lane_c, oc, 0);
+  r.v1 = __builtin_amdgcn_raw_buffer_load_b128(s.vc, lane_c + 16, oc, 0);
+  return r;
 }
 
 template <int WPB>
@@ -756,28 +824,60 @@ void decode_mfma_kernel(DecodeArgs a) {
   constexpr int D = 128;
   const int bh = blockIdx.x;
   const int b = bh / a.Hkv, h = bh - (bh / a.Hkv) * a.Hkv;
-  if ((int)blockIdx.y >= a.plan.splits) {          // bf16 window blocks
-    if (WPB == 4) window_block(a, bh, b, h, (int)blockIdx.y - a.plan.splits);
+  __shared__ FusedSmem S;
+  // Block roles along y, in dispatch order:
+  //   [0, app_blocks)                 append of the new token (K, then V)
+  //   [.., + win.splits)              bf16 window blocks
+  //   [.., + plan.splits)             INT2 splits
+  // Window blocks go before the INT2 ones so that they overlap them.
+  int y = (int)blockIdx.y;
+  if (y < a.app_blocks) {
+    append_block<128, 4, 1>(a.app, bh, y == 1, a.app.T_old, a.app.T_old + 1, S.scratch, S.scratch + 128);
+    return;
+  }
+  y -= a.app_blocks;
+  if (y < a.win.splits) {
+    block_q(a, b, h, bh, y, S);
+    window_block(a, bh, b, h, y, S);
     finish_block(a, bh);
     return;
   }
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int split = y - a.win.splits;
+  // wave index as a uniform value: the tile loop is controlled by scalar branches
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int blk = lane >> 2, j = lane & 3;
   const int lo = a.plan.a0, hi = a.plan.b0;       // INT2 token range
   const int tile_first = lo >> 6;
   const int ntiles = ((hi - 1) >> 6) - tile_first + 1;
   const int tps = a.plan.chunk >> 6;
-  const int s_t0 = (int)blockIdx.y * tps;
+  const int s_t0 = split * tps;
   const int s_t1 = min(s_t0 + tps, ntiles);
 
-  // q operands: 8 words x 4 fp16
-  const uint4* qp = reinterpret_cast<const uint4*>(a.qswz + ((size_t)bh * 64 + lane) * 32);
-  const uint4 q01 = qp[0], q23 = qp[1], q45 = qp[2], q67 = qp[3];
-  const h4 qv[8] = {as_h4(q01.x, q01.y), as_h4(q01.z, q01.w), as_h4(q23.x, q23.y), as_h4(q23.z, q23.w),
-                    as_h4(q45.x, q45.y), as_h4(q45.z, q45.w), as_h4(q67.x, q67.y), as_h4(q67.z, q67.w)};
-  const float* aux = a.qaux + ((size_t)b * a.Hq + h * 4 + j) * 8;
-  const float cK = aux[4];
-  const float zq = aux[0] * (1.0f / cK);           // sum(q_rot) in units of the raw dot (cK is a power of 2)
+  // Two register sets in turn: the loads of a tile are issued while the tile
+  // before it is processed.  The first two tiles' loads go out before the q
+  // rotation, so their latency overlaps it.
+  const int lane_c = lane * 32, lane_m = blk * 16;
+  const int ti0 = s_t0 + wave;
+  const TileStreams st = tile_streams(a, bh);
+  auto tile_t0 = [&](int ti) { return (tile_first + ti) << 6; };
+  TileRegs ra, rb;
+  if (ti0 < s_t1) ra = load_tile(st, tile_t0(ti0), lane_c, lane_m);
+  if (ti0 + WPB < s_t1) rb = load_tile(st, tile_t0(ti0 + WPB), lane_c, lane_m);
+  block_q(a, b, h, bh, y, S);
+
+  // q operands: 8 words x 4 fp16 of head j; the four lanes groups pp hold the
+  // k-slots of qk_dim(w, pp, k), each scaled by 2^eq 4^-(d % 4)
+  const int eq = S.qeq[j];
+  h4 qv[8];
+#pragma unroll
+  for (int w = 0; w < 8; ++w)
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int d = qk_dim(w, lane >> 4, k);
+      qv[w][k] = (_Float16)ldexpf(S.qs[j][d], eq - 2 * (d & 3));
+    }
+  const float cK = ldexpf(1.0f, 24 - eq);          // undoes 2^eq and the 2^-24 code scale
+  const float zq = ldexpf(S.qsum[j], eq - 24);     // sum(q_rot) in units of the raw dot
   const float vmax = a.v.smax[bh];
   int ev2 = 0;
   if (vmax > 0.0f) frexpf(vmax, &ev2);
@@ -848,69 +948,45 @@ void decode_mfma_kernel(DecodeArgs a) {
     pv_word<7>(cur.v1.w, pv, o0, o1);
   };
 
-  // two register sets in turn: the loads of the next tile are in flight while
-  // the current one is processed
-  const int lane_k = lane * 32, lane_m = blk * 16, lane_v = lane * 32;
-  const int ti0 = s_t0 + wave;
-  constexpr int kStep = 64 * WPB;                  // tokens between a wave's tiles
-  TileStreams st = tile_streams(a, bh, (tile_first + ti0) << 6);
-  auto advance = [&](TileStreams& x) {
-    x.kc += kStep * 32;
-    x.km += kStep * 4;
-    x.vm += kStep * 4;
-    x.vc += WPB * 2048;
-  };
-#if OSCAR_PREFETCH
-  TileRegs ra, rb;
-  if (ti0 < s_t1) ra = load_tile(st, lane_k, lane_m, lane_v);
   for (int ti = ti0; ti < s_t1; ti += 2 * WPB) {
-    const int tB = ti + WPB;
-    advance(st);
-    if (tB < s_t1) rb = load_tile(st, lane_k, lane_m, lane_v);
-    process(ra, (tile_first + ti) << 6);
-    if (tB >= s_t1) break;
-    const int tA = tB + WPB;
-    advance(st);
-    if (tA < s_t1) ra = load_tile(st, lane_k, lane_m, lane_v);
-    process(rb, (tile_first + tB) << 6);
+    process(ra, tile_t0(ti));
+    if (ti + 2 * WPB < s_t1) ra = load_tile(st, tile_t0(ti + 2 * WPB), lane_c, lane_m);
+    if (ti + WPB >= s_t1) break;
+    process(rb, tile_t0(ti + WPB));
+    if (ti + 3 * WPB < s_t1) rb = load_tile(st, tile_t0(ti + 3 * WPB), lane_c, lane_m);
   }
-#else
-  for (int ti = ti0; ti < s_t1; ti += WPB) {
-    const TileRegs r = load_tile(st, lane_k, lane_m, lane_v);
-    advance(st);
-    process(r, (tile_first + ti) << 6);
-  }
-#endif
 
   // per-head totals of l and sum(p z_V) over the 16 lanes of each head
   l = head_sum(l);
   pz = head_sum(pz);
-  __shared__ float sm[WPB][4], sl[WPB][4];
-  __shared__ float so[WPB][4][D];
+  static_assert(8 * WPB + WPB * 4 * D <= sizeof(S.scratch) / sizeof(float), "epilogue scratch");
+  float* sm = S.scratch;                 // [WPB][4]
+  float* sl = S.scratch + 4 * WPB;       // [WPB][4]
+  float* so = S.scratch + 8 * WPB;       // [WPB][4][D]
   if (lane < 4) {
-    sm[wave][lane] = m;
-    sl[wave][lane] = l;
+    sm[wave * 4 + lane] = m;
+    sl[wave * 4 + lane] = l;
   }
   const float pzr[4] = {lane_value(pz, 0), lane_value(pz, 1), lane_value(pz, 2), lane_value(pz, 3)};
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
-    so[wave][r][4 * blk + j] = __builtin_fmaf(o0[r], cV, pzr[r]);
-    so[wave][r][64 + 4 * blk + j] = __builtin_fmaf(o1[r], cV, pzr[r]);
+    so[(wave * 4 + r) * D + 4 * blk + j] = __builtin_fmaf(o0[r], cV, pzr[r]);
+    so[(wave * 4 + r) * D + 64 + 4 * blk + j] = __builtin_fmaf(o1[r], cV, pzr[r]);
   }
   __syncthreads();
-  const int slot = a.plan.slot0 + (int)blockIdx.y;
+  const int slot = a.plan.slot0 + split;
   for (int idx = threadIdx.x; idx < 4 * D; idx += 64 * WPB) {
     const int r = idx / D, d = idx - r * D;
     float M = NEG_INF;
 #pragma unroll
-    for (int w = 0; w < WPB; ++w) M = fmaxf(M, sm[w][r]);
+    for (int w = 0; w < WPB; ++w) M = fmaxf(M, sm[w * 4 + r]);
     float O = 0.0f, L = 0.0f;
     if (M != NEG_INF) {
 #pragma unroll
       for (int w = 0; w < WPB; ++w) {
-        const float sw = exp2f(sm[w][r] - M);
-        O = __builtin_fmaf(so[w][r][d], sw, O);
-        L = __builtin_fmaf(sl[w][r], sw, L);
+        const float sw = exp2f(sm[w * 4 + r] - M);
+        O = __builtin_fmaf(so[(w * 4 + r) * D + d], sw, O);
+        L = __builtin_fmaf(sl[w * 4 + r], sw, L);
       }
     }
     float* dst = a.partials + (((size_t)b * a.Hq + h * 4 + r) * kMaxSplits + slot) * (D + 2);
@@ -947,7 +1023,7 @@ hipError_t launch_decode_valu(const DecodeArgs& a, int B, hipStream_t s) {
 
 hipError_t launch_decode_mfma(const DecodeArgs& a, int B, int waves_per_block, hipStream_t s) {
   (void)waves_per_block;   // the fused window blocks need 4 waves
-  dim3 grid((unsigned)(B * a.Hkv), (unsigned)(a.plan.splits + a.win.splits));
+  dim3 grid((unsigned)(B * a.Hkv), (unsigned)(a.app_blocks + a.plan.splits + a.win.splits));
   hipLaunchKernelGGL(decode_mfma_kernel<4>, grid, dim3(256), 0, s, a);
   return hipGetLastError();
 }

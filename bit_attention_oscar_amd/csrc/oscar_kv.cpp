@@ -5,6 +5,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <climits>
 #include <cmath>
 #include <cstdio>
 #include <cstring>
@@ -68,8 +69,9 @@ struct oscar_kv {
   float* rv = nullptr;     // [L][D][D]
   float* rvT = nullptr;    // [L][D][D] transposed
   float* qrot = nullptr;   // [B][Hq][D]
-  float* qaux = nullptr;   // [B][Hq][8]
-  uint16_t* qswz = nullptr;  // [B][Hkv][64][32]
+  float* qpub = nullptr;    // [B][Hkv][kQPub]
+  unsigned* qflag = nullptr; // [B][Hkv]
+  unsigned epoch = 0;        // matrix-core launches so far (skips 0 on wrap)
   float* partials = nullptr; // [B][Hq][kMaxSplits][D+2]
   unsigned* counters = nullptr; // [B][Hkv] blocks finished in the current decode launch
   size_t bytes = 0;
@@ -111,15 +113,18 @@ void free_all(oscar_kv* kv) {
   }
 }
 
-// returns the slot recorded before a launch of class c, or -1 when not profiling
+// Returns the slot recorded before a launch of class c, or -1 when not
+// profiling.  The events only time work: they are created without the
+// system-scope fence (cache write-back and invalidation) that a default event
+// performs when it completes, which would slow the launches that follow.
 long prof_begin(oscar_kv* kv, int c, hipStream_t s) {
   if (!kv->prof_on) return -1;
   ProfClass& pc = kv->prof[c];
   if (pc.used >= kProfMax) return -1;
   if (pc.used == pc.ev.size()) {
     hipEvent_t a, b;
-    if (hipEventCreate(&a) != hipSuccess) return -1;
-    if (hipEventCreate(&b) != hipSuccess) {
+    if (hipEventCreateWithFlags(&a, hipEventDisableSystemFence) != hipSuccess) return -1;
+    if (hipEventCreateWithFlags(&b, hipEventDisableSystemFence) != hipSuccess) {
       (void)hipEventDestroy(a);
       return -1;
     }
@@ -326,8 +331,10 @@ int oscar_kv_create(const oscar_kv_config* cfg, oscar_kv** out) {
     return bail(fail(OSCAR_ERR_HIP, "copy of rotations failed"));
   const size_t B = cfg->max_batch, Hq = cfg->num_q_heads, Hkv = cfg->num_kv_heads;
   if ((rc = dev_alloc(kv, (void**)&kv->qrot, B * Hq * D * 4))) return bail(rc);
-  if ((rc = dev_alloc(kv, (void**)&kv->qaux, B * Hq * 8 * 4))) return bail(rc);
-  if ((rc = dev_alloc(kv, (void**)&kv->qswz, B * Hkv * 64 * 32 * 2))) return bail(rc);
+  if ((rc = dev_alloc(kv, (void**)&kv->qpub, B * Hkv * kQPub * 4))) return bail(rc);
+  if ((rc = dev_alloc(kv, (void**)&kv->qflag, B * Hkv * sizeof(unsigned)))) return bail(rc);
+  if (hipMemset(kv->qflag, 0, B * Hkv * sizeof(unsigned)) != hipSuccess)
+    return bail(fail(OSCAR_ERR_HIP, "clearing the q flags failed"));
   if ((rc = dev_alloc(kv, (void**)&kv->partials, B * Hq * kMaxSplits * (D + 2) * 4))) return bail(rc);
   if ((rc = dev_alloc(kv, (void**)&kv->counters, B * Hkv * sizeof(unsigned)))) return bail(rc);
   if (hipMemset(kv->counters, 0, B * Hkv * sizeof(unsigned)) != hipSuccess)
@@ -358,44 +365,48 @@ int oscar_kv_append_dump(oscar_kv* kv, int32_t layer, const void* k, const void*
   return do_append(kv, layer, k, v, batch, n_new, k_rot, v_rot, stream);
 }
 
-int oscar_int2_decode_attn(oscar_kv* kv, int32_t layer, const void* q, void* out, int32_t out_dtype,
-                           int32_t batch, float softmax_scale, hipStream_t stream) {
+}  // extern "C"
+
+namespace {
+
+bool fast_shape(const oscar_kv* kv) {
+  const auto& c = kv->cfg;
+  // the matrix-core kernel addresses one (sequence, kv head)'s code plane with
+  // 32-bit buffer offsets: cap * 32 bytes must fit
+  return kv->decode_impl == 0 && c.head_dim == 128 && c.num_q_heads == 4 * c.num_kv_heads &&
+         c.k_dtype == OSCAR_KV_INT2 && c.v_dtype == OSCAR_KV_INT2 && (long long)kv->cap * 32 <= INT32_MAX;
+}
+
+int check_decode_args(const oscar_kv* kv, int32_t layer, const void* q, void* out, int32_t out_dtype,
+                      float softmax_scale) {
   int rc = check_layer(kv, layer);
   if (rc) return rc;
   if (!q || !out) return fail(OSCAR_ERR_INVALID_ARG, "q/out pointer is NULL");
   if (out_dtype < 0 || out_dtype > 2) return fail(OSCAR_ERR_INVALID_ARG, "unknown out_dtype");
-  const Layer& L = kv->layers[layer];
-  if (L.T == 0) return fail(OSCAR_ERR_INVALID_ARG, "layer holds no tokens");
-  if (batch != L.batch) return fail(OSCAR_ERR_INVALID_ARG, "batch differs from the layer's batch");
   if (!(softmax_scale == softmax_scale)) return fail(OSCAR_ERR_INVALID_ARG, "softmax_scale is NaN");
+  return OSCAR_OK;
+}
+
+// Enqueue decode attention of `layer` over T tokens.  With `app` set (matrix-
+// core shapes only) the same launch also appends that one token, which is then
+// the last of the T tokens.
+int launch_decode(oscar_kv* kv, int32_t layer, const void* q, void* out, int32_t out_dtype, int32_t batch,
+                  float softmax_scale, int T, const AppendArgs* app, hipStream_t stream) {
+  const Layer& L = kv->layers[layer];
   HIP_TRY(hipSetDevice(kv->cfg.device));
   const auto& c = kv->cfg;
-  const int D = c.head_dim, Hq = c.num_q_heads, Hkv = c.num_kv_heads, Gq = Hq / Hkv;
-  const int T = L.T, N = c.sink_tokens, M = c.recent_tokens;
+  const int D = c.head_dim, Hq = c.num_q_heads, Hkv = c.num_kv_heads;
+  const int N = c.sink_tokens, M = c.recent_tokens;
   const float scale = softmax_scale > 0.0f ? softmax_scale : 1.0f / std::sqrt((float)D);
-  const bool fast = kv->decode_impl == 0 && D == 128 && Gq == 4 && c.k_dtype == OSCAR_KV_INT2 &&
-                    c.v_dtype == OSCAR_KV_INT2;
+  const bool fast = fast_shape(kv);
   const size_t DD = (size_t)D * D;
-
-  QRotArgs qa{};
-  qa.q = static_cast<const uint16_t*>(q);
-  qa.rk = kv->rk + layer * DD;
-  qa.qrot = kv->qrot;
-  qa.qaux = kv->qaux;
-  qa.qswz = kv->qswz;
-  qa.B = batch;
-  qa.Hq = Hq;
-  qa.Hkv = Hkv;
-  qa.D = D;
-  qa.scale_log2 = scale * 1.4426950408889634f;
-  qa.want_swz = fast ? 1 : 0;
 
   DecodeArgs da{};
   da.k = plane_dev(kv, L.k, false);
   da.v = plane_dev(kv, L.v, true);
   da.qrot = kv->qrot;
-  da.qaux = kv->qaux;
-  da.qswz = kv->qswz;
+  da.qpub = kv->qpub;
+  da.qflag = kv->qflag;
   da.partials = kv->partials;
   da.Hq = Hq;
   da.Hkv = Hkv;
@@ -405,6 +416,11 @@ int oscar_int2_decode_attn(oscar_kv* kv, int32_t layer, const void* q, void* out
   da.M = M;
   da.T = T;
   da.counters = kv->counters;
+  da.q = static_cast<const uint16_t*>(q);
+  da.rk = kv->rk + layer * DD;
+  da.scale_log2 = scale * 1.4426950408889634f;
+  da.app_blocks = app ? 2 : 0;
+  if (app) da.app = *app;
   CombineArgs ca{};
   ca.partials = kv->partials;
   ca.rvT = kv->rvT + layer * DD;
@@ -420,11 +436,10 @@ int oscar_int2_decode_attn(oscar_kv* kv, int32_t layer, const void* q, void* out
   const int sink_end = std::min(N, T);
   const int rec_begin = std::max(N, T - M);
   const int int2_lo = N, int2_hi = T - M;
-  int nslots = 0;
   const long pcall = prof_begin(kv, 1, stream);
-  HIP_TRY(launch_qrot(qa, stream));
   if (fast) {
-    // one launch: INT2 splits (matrix cores) followed by bf16 window blocks
+    // one launch: [append blocks] + bf16 window blocks + INT2 splits, q rotated
+    // in each attention block, merged by the last block of each (sequence, kv head)
     const int hp_len = sink_end + (T - rec_begin);
     SegPlan w{};
     if (hp_len > 0) {
@@ -443,30 +458,95 @@ int oscar_int2_decode_attn(oscar_kv* kv, int32_t layer, const void* q, void* out
       p.chunk = tps * kTile;
       p.splits = (ntiles + tps - 1) / tps;
     }
-    w.slot0 = p.splits;
+    p.slot0 = w.splits;      // window partials first, then the INT2 splits
+    w.slot0 = 0;
     da.plan = p;
     da.win = w;
     ca.nslots = p.splits + w.splits;
     da.comb = ca;
+    if (++kv->epoch == 0) kv->epoch = 1;   // a flag never holds a future launch's number
+    da.epoch = kv->epoch;
     const long pk = prof_begin(kv, 0, stream);
     HIP_TRY(launch_decode_mfma(da, batch, kv->mfma_waves, stream));
     prof_end(kv, 0, pk, stream);
-    nslots = p.splits + w.splits;
   } else {
+    QRotArgs qa{};
+    qa.q = static_cast<const uint16_t*>(q);
+    qa.rk = kv->rk + layer * DD;
+    qa.qrot = kv->qrot;
+    qa.B = batch;
+    qa.Hq = Hq;
+    qa.Hkv = Hkv;
+    qa.D = D;
+    qa.scale_log2 = da.scale_log2;
+    HIP_TRY(launch_qrot(qa, stream));
     int want = kv->forced_splits > 0 ? kv->forced_splits
                                      : std::max(1, std::min(64, 2048 / std::max(1, BH)));
     want = std::min(want, kMaxSplits);
     want = std::min(want, (T + kTile - 1) / kTile);
     da.plan = make_plan(0, T, 0, 0, want, 0);
     HIP_TRY(launch_decode_valu(da, batch, stream));
-    nslots = da.plan.splits;
-  }
-  if (nslots > kMaxSplits) return fail(OSCAR_ERR_HIP, "internal: too many partial slots");
-  if (!fast) {
-    ca.nslots = nslots;
+    ca.nslots = da.plan.splits;
     HIP_TRY(launch_combine(ca, stream));
   }
   prof_end(kv, 1, pcall, stream);
+  return OSCAR_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int oscar_int2_decode_attn(oscar_kv* kv, int32_t layer, const void* q, void* out, int32_t out_dtype,
+                           int32_t batch, float softmax_scale, hipStream_t stream) {
+  int rc = check_decode_args(kv, layer, q, out, out_dtype, softmax_scale);
+  if (rc) return rc;
+  const Layer& L = kv->layers[layer];
+  if (L.T == 0) return fail(OSCAR_ERR_INVALID_ARG, "layer holds no tokens");
+  if (batch != L.batch) return fail(OSCAR_ERR_INVALID_ARG, "batch differs from the layer's batch");
+  return launch_decode(kv, layer, q, out, out_dtype, batch, softmax_scale, L.T, nullptr, stream);
+}
+
+int oscar_kv_decode_step(oscar_kv* kv, int32_t layer, const void* k, const void* v, const void* q, void* out,
+                         int32_t out_dtype, int32_t batch, float softmax_scale, hipStream_t stream) {
+  int rc = check_decode_args(kv, layer, q, out, out_dtype, softmax_scale);
+  if (rc) return rc;
+  if (!k || !v) return fail(OSCAR_ERR_INVALID_ARG, "k/v pointer is NULL");
+  if (batch <= 0 || batch > kv->cfg.max_batch) return fail(OSCAR_ERR_INVALID_ARG, "batch must be in [1, max_batch]");
+  Layer& L = kv->layers[layer];
+  if (L.T > 0 && batch != L.batch)
+    return fail(OSCAR_ERR_INVALID_ARG, "batch differs from the batch this layer was filled with");
+  if ((long long)L.T + 1 > kv->cfg.max_context)
+    return fail(OSCAR_ERR_CAPACITY, "decode step at " + std::to_string(L.T) + " tokens exceeds max_context");
+  if (!fast_shape(kv) || kv->cfg.recent_tokens < 1) {
+    // separate launches: the appended token is not a bf16 window token here or
+    // the shape has no fused kernel
+    rc = do_append(kv, layer, k, v, batch, 1, nullptr, nullptr, stream);
+    if (rc) return rc;
+    return launch_decode(kv, layer, q, out, out_dtype, batch, softmax_scale, L.T, nullptr, stream);
+  }
+  HIP_TRY(hipSetDevice(kv->cfg.device));
+  AppendArgs a{};
+  a.k = plane_dev(kv, L.k, false);
+  a.v = plane_dev(kv, L.v, true);
+  a.kin = static_cast<const uint16_t*>(k);
+  a.vin = static_cast<const uint16_t*>(v);
+  const size_t DD = (size_t)kv->cfg.head_dim * kv->cfg.head_dim;
+  a.rk = kv->rk + layer * DD;
+  a.rv = kv->rv + layer * DD;
+  a.batch = batch;
+  a.n_new = 1;
+  a.Hkv = kv->cfg.num_kv_heads;
+  a.D = kv->cfg.head_dim;
+  a.cap = kv->cap;
+  a.N = kv->cfg.sink_tokens;
+  a.M = kv->cfg.recent_tokens;
+  a.T_old = L.T;
+  a.T_new = L.T + 1;
+  rc = launch_decode(kv, layer, q, out, out_dtype, batch, softmax_scale, L.T + 1, &a, stream);
+  if (rc) return rc;
+  L.T += 1;
+  L.batch = batch;
   return OSCAR_OK;
 }
 

@@ -340,6 +340,132 @@ def test_decode_after_many_single_appends(ok):
     gc.close()
 
 
+# ------------------------------------------------------------------ fused decode step
+
+
+def _step(ok, gc, layer, kb, vb, qbits, out_dtype=0):
+    B, Hq, D = qbits.shape
+    dt = {0: torch.float32, 1: torch.bfloat16, 2: torch.float16}[out_dtype]
+    out = torch.zeros((B, Hq, D), dtype=dt, device="cuda")
+    gc.decode_step(layer, dev(kb), dev(vb), dev(qbits), out, out_dtype)
+    torch.cuda.synchronize()
+    return out.float().cpu().numpy()
+
+
+def _exports_equal(g1, g2, layer, N, M):
+    """Every stored bit of positions [0, T) equal; sink rows past T and ring
+    slots not yet written hold no data and are skipped."""
+    T = g1.length(layer)
+    assert g2.length(layer) == T
+    for which in (0, 1):
+        e1, e2 = g1.export(layer, which), g2.export(layer, which)
+        assert sorted(e1) == sorted(e2)
+        for key in e1:
+            a, b = e1[key], e2[key]
+            if key == "sink":
+                a, b = a[:, :, :min(N, T)], b[:, :, :min(N, T)]
+            elif key == "ring":
+                slots = [t % M for t in range(max(N, T - M), T)]
+                a, b = a[:, :, slots], b[:, :, slots]
+            np.testing.assert_array_equal(np.ascontiguousarray(a).view(np.uint8), np.ascontiguousarray(b).view(np.uint8),
+                                          err_msg=f"plane {which} {key}")
+
+
+@pytest.mark.parametrize("shape,T0,steps", [
+    (Shape(B=2, Hq=4, Hkv=1, N=64, M=256), 1000, 5),           # INT2 range + both windows
+    (Shape(B=1, Hq=8, Hkv=2, N=4, M=20), 60, 70),              # ring wraps, tiles and 8-groups crossed
+    (Shape(B=2, Hq=4, Hkv=2, N=8, M=16), 0, 30),               # from an empty cache: sink, then ring
+    (Shape(B=1, Hq=4, Hkv=1, N=0, M=1), 130, 3),               # window = the new token only
+    (Shape(B=1, Hq=4, Hkv=1, N=64, M=256), 300, 4),            # every token still bf16
+])
+def test_decode_step_equals_append_then_decode(ok, shape, T0, steps):
+    """The fused step (append and attention in one launch) against the two
+    separate calls on a twin cache: identical stored cache bit for bit, output
+    within the matrix-core kernel's fp16 half-ulp, and within the attention bar
+    of the oracle over the exported cache."""
+    say(f"[decode step] {shape} T0={T0} steps={steps}")
+    rk, rv = make_rotations(shape, "haar")
+    k, v, mask = inputs(shape, T0 + steps)
+    g1 = gpu_cache(ok, shape, rk, rv, T0 + steps + 3)
+    g2 = gpu_cache(ok, shape, rk, rv, T0 + steps + 3)
+    if T0:
+        for g in (g1, g2):
+            g.append(0, dev(k[:, :T0]), dev(v[:, :T0]))
+    worst = 0.0
+    for i in range(steps):
+        t = T0 + i
+        qb = query(shape, mask, step=i)
+        got = _step(ok, g1, 0, k[:, t:t + 1], v[:, t:t + 1], qb)
+        g2.append(0, dev(k[:, t:t + 1]), dev(v[:, t:t + 1]))
+        ref = _decode(ok, g2, 0, qb)
+        assert g1.length(0) == g2.length(0) == t + 1
+        e = rel_l2(got, ref)
+        worst = max(worst, e)
+        assert e <= 2 ** -12, (i, e)
+        if i == 0 or i == steps - 1 or i % 16 == 0:
+            _exports_equal(g1, g2, 0, shape.N, shape.M)
+            want = oracle_on_exported(g1, 0, qb, shape, rk, rv)
+            eo = rel_l2(got, want)
+            assert eo <= ATTN_TOL, (i, eo)
+    say(f"  worst step-vs-separate rel L2 {worst:.2e}")
+    g1.close()
+    g2.close()
+
+
+def test_decode_step_exact_rotation_bitexact(ok):
+    """Fused steps with rotations exact in fp32: the stored cache equals the
+    oracle's bit for bit, and the output is within the bar of the oracle's
+    own attention."""
+    shape = Shape(B=2, Hq=4, Hkv=1, N=6, M=10)
+    say("[decode step exact]")
+    rk, rv = make_rotations(shape, "exact")
+    T0, steps = 70, 12
+    k, v, mask = inputs(shape, T0 + steps)
+    gc = gpu_cache(ok, shape, rk, rv, T0 + steps)
+    oc = oracle_cache(shape, rk, rv)
+    gc.append(0, dev(k[:, :T0]), dev(v[:, :T0]))
+    oc.append(0, k[:, :T0], v[:, :T0])
+    for i in range(steps):
+        t = T0 + i
+        qb = query(shape, mask, step=i)
+        got = _step(ok, gc, 0, k[:, t:t + 1], v[:, t:t + 1], qb)
+        oc.append(0, k[:, t:t + 1], v[:, t:t + 1])
+        e = rel_l2(got, oc.attend(0, qb))
+        assert e <= ATTN_TOL, (i, e)
+    T = T0 + steps
+    _compare_planes(gc.export(0, 0), oc.k[0], T, shape.N, shape.M, "K")
+    _compare_planes(gc.export(0, 1), oc.v[0], T, shape.N, shape.M, "V")
+    gc.close()
+
+
+@pytest.mark.parametrize("shape", [
+    Shape(B=1, Hq=16, Hkv=2, N=8, M=16),                       # GQA 8: separate launches
+    Shape(B=2, Hq=4, Hkv=2, D=512, N=16, M=32),                # wide head
+    Shape(B=1, Hq=4, Hkv=1, N=8, M=0),                         # no recent window
+    Shape(B=1, Hq=4, Hkv=1, N=8, M=16, v_dtype=1),             # V kept bf16
+])
+def test_decode_step_other_shapes(ok, shape):
+    """Shapes the fused launch does not take: the step still equals the two
+    separate calls."""
+    say(f"[decode step other] {shape}")
+    rk, rv = make_rotations(shape, "haar")
+    T0 = 200
+    k, v, mask = inputs(shape, T0 + 2)
+    g1 = gpu_cache(ok, shape, rk, rv, T0 + 2)
+    g2 = gpu_cache(ok, shape, rk, rv, T0 + 2)
+    for g in (g1, g2):
+        g.append(0, dev(k[:, :T0]), dev(v[:, :T0]))
+    for i in range(2):
+        t = T0 + i
+        qb = query(shape, mask, step=i)
+        got = _step(ok, g1, 0, k[:, t:t + 1], v[:, t:t + 1], qb)
+        g2.append(0, dev(k[:, t:t + 1]), dev(v[:, t:t + 1]))
+        assert rel_l2(got, _decode(ok, g2, 0, qb)) <= 1e-6
+    _exports_equal(g1, g2, 0, shape.N, shape.M)
+    g1.close()
+    g2.close()
+
+
 # ------------------------------------------------------------------ full-size samples
 
 
@@ -358,9 +484,12 @@ def test_full_size_32k_sampled(ok):
     fill_layer_device(gc, 0, shape.B, shape.Hkv, shape.D, T, seed=0, dist="normal", outliers="percent")
     mask = synth.outlier_mask(shape.D, shape.Hkv, 0, 0, "percent")
     k1, v1, _ = inputs(shape, 1, chunk=99)
-    gc.append(0, dev(k1), dev(v1))
     qb = query(shape, mask, step=1)
+    # the fused step (what the benchmark times), then the attention call alone
+    got_step = _step(ok, gc, 0, k1, v1, qb)
     got = _decode(ok, gc, 0, qb)
+    say(f"  step vs attention call: {rel_l2(got_step, got):.2e}")
+    assert rel_l2(got_step, got) <= 2 ** -12
     for b in (0, 15):
         want = oracle_on_exported(gc, 0, qb, shape, rk, rv, batch_idx=slice(b, b + 1))
         e = rel_l2(got[b:b + 1], want)
