@@ -146,6 +146,7 @@ struct DecodeArgs {
   const float* rk;         // fp32 [D][D] of this layer
   float scale_log2;        // softmax scale * log2(e)
   int app_blocks;          // 2 when the launch also appends this step's token, else 0
+  int int2_lead;           // INT2 splits dispatched before the window blocks
   AppendArgs app;          // that append (n_new = 1); T above counts the new token
 };
 
@@ -156,6 +157,7 @@ hipError_t launch_quantize_rows(const float* x, int rows, int D, float clip, uin
 hipError_t launch_qrot(const QRotArgs& a, hipStream_t s);
 hipError_t launch_decode_valu(const DecodeArgs& a, int B, hipStream_t s);
 hipError_t launch_decode_mfma(const DecodeArgs& a, int B, int waves_per_block, hipStream_t s);
+int decode_mfma_resident_blocks(int device);   // blocks of the matrix-core kernel resident at once
 hipError_t launch_combine(const CombineArgs& a, hipStream_t s);
 hipError_t launch_stream_copy(const void* src, void* dst, size_t bytes, hipStream_t s);
 hipError_t launch_export_vcodes(const uint8_t* tiled, uint8_t* canon, int BH, int cap, int T, int D,

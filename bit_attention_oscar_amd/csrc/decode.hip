@@ -42,6 +42,16 @@ typedef float f4 __attribute__((ext_vector_type(4)));
 #ifndef OSCAR_MFMA_WAVES_PER_EU
 #define OSCAR_MFMA_WAVES_PER_EU 4
 #endif
+// Register sets of tile data per wave: the loads of a tile are issued
+// kDepth - 1 tiles ahead of its processing.
+#ifndef OSCAR_TILE_DEPTH
+#define OSCAR_TILE_DEPTH 2
+#endif
+// QK^T accumulation in two interleaved chains instead of one
+#ifndef OSCAR_QK_TWO_CHAINS
+#define OSCAR_QK_TWO_CHAINS 0
+#endif
+constexpr int kDepth = OSCAR_TILE_DEPTH;
 
 __device__ inline float wmax(float v) {
 #pragma unroll
@@ -370,18 +380,33 @@ __device__ void combine_group(const CombineArgs& a, int bh) {
   __shared__ float part[4][4][D];
   for (int hc = 0; hc < Gq; hc += 4) {
     const int nh = min(4, Gq - hc);
-    // split weights: wave j handles head j
+    // split weights: wave j handles head j; every (m, l) pair of a lane is
+    // loaded in one round trip (at most kMaxSplits / 64 slots per lane)
     if (wave < nh) {
       const float* P = a.partials + ((size_t)b * a.Hq + kvh * Gq + hc + wave) * kMaxSplits * (D + 2);
+      constexpr int SPL = kMaxSplits / 64;
+      float ms[SPL], ls[SPL];
+#pragma unroll
+      for (int i = 0; i < SPL; ++i) {
+        const int sl = lane + 64 * i;
+        ms[i] = NEG_INF;
+        ls[i] = 0.0f;
+        if (sl < a.nslots) {
+          ms[i] = ld_partial<COHERENT>(P + (size_t)sl * (D + 2) + D);
+          ls[i] = ld_partial<COHERENT>(P + (size_t)sl * (D + 2) + D + 1);
+        }
+      }
       float mx = NEG_INF;
-      for (int sl = lane; sl < a.nslots; sl += 64) mx = fmaxf(mx, ld_partial<COHERENT>(P + (size_t)sl * (D + 2) + D));
+#pragma unroll
+      for (int i = 0; i < SPL; ++i) mx = fmaxf(mx, ms[i]);
       const float M = wmax(mx);
       float L = 0.0f;
-      for (int sl = lane; sl < a.nslots; sl += 64) {
-        const float ms = ld_partial<COHERENT>(P + (size_t)sl * (D + 2) + D);
-        const float w = (ms == NEG_INF) ? 0.0f : exp2f(ms - M);
-        wsl[wave][sl] = w;
-        L = __builtin_fmaf(ld_partial<COHERENT>(P + (size_t)sl * (D + 2) + D + 1), w, L);
+#pragma unroll
+      for (int i = 0; i < SPL; ++i) {
+        const int sl = lane + 64 * i;
+        const float w = (ms[i] == NEG_INF) ? 0.0f : exp2f(ms[i] - M);
+        if (sl < a.nslots) wsl[wave][sl] = w;
+        L = __builtin_fmaf(ls[i], w, L);
       }
       L = wsum(L);
       if (lane == 0) linv[wave] = 1.0f / L;
@@ -392,17 +417,19 @@ __device__ void combine_group(const CombineArgs& a, int bh) {
       float acc = 0.0f;
       if (j < nh) {
         const float* P = a.partials + ((size_t)b * a.Hq + kvh * Gq + hc + j) * kMaxSplits * (D + 2);
-        // eight independent loads in flight per step
-        int sl = 0;
-        for (; sl + 8 <= a.nslots; sl += 8) {
-          float v[8];
+        // sixteen independent loads in flight per step; past the last slot the
+        // index is clamped (a valid address) and the weight is zero
+        for (int sl = 0; sl < a.nslots; sl += 16) {
+          float v[16];
 #pragma unroll
-          for (int u = 0; u < 8; ++u) v[u] = ld_partial<COHERENT>(P + (size_t)(sl + u) * (D + 2) + d);
+          for (int u = 0; u < 16; ++u)
+            v[u] = ld_partial<COHERENT>(P + (size_t)min(sl + u, a.nslots - 1) * (D + 2) + d);
 #pragma unroll
-          for (int u = 0; u < 8; ++u) acc = __builtin_fmaf(v[u], wsl[j][sl + u], acc);
+          for (int u = 0; u < 16; ++u) {
+            const int su = min(sl + u, a.nslots - 1);
+            acc = __builtin_fmaf(v[u], sl + u < a.nslots ? wsl[j][su] : 0.0f, acc);
+          }
         }
-        for (; sl < a.nslots; ++sl)
-          acc = __builtin_fmaf(ld_partial<COHERENT>(P + (size_t)sl * (D + 2) + d), wsl[j][sl], acc);
         acc *= linv[j];
       }
       os[j][d] = acc;
@@ -414,7 +441,7 @@ __device__ void combine_group(const CombineArgs& a, int bh) {
 #pragma unroll
       for (int i = 0; i < PER; ++i) acc[j][i] = 0.0f;
     const float* R = a.rvT + (size_t)(wave * EW) * D + lane;
-#pragma unroll 8
+#pragma unroll 16
     for (int e = 0; e < EW; ++e) {
       float r[PER];
 #pragma unroll
@@ -836,13 +863,17 @@ void decode_mfma_kernel(DecodeArgs a) {
     return;
   }
   y -= a.app_blocks;
-  if (y < a.win.splits) {
+  // attention blocks: int2_lead INT2 splits, the window blocks, the other INT2
+  // splits.  The lead splits fill the compute units first; the window blocks
+  // start once slots free up, by when block 0 has published q.
+  const int lead = a.int2_lead;
+  if (y >= lead && y < lead + a.win.splits) {
     block_q(a, b, h, bh, y, S);
-    window_block(a, bh, b, h, y, S);
+    window_block(a, bh, b, h, y - lead, S);
     finish_block(a, bh);
     return;
   }
-  const int split = y - a.win.splits;
+  const int split = y < lead ? y : y - a.win.splits;
   // wave index as a uniform value: the tile loop is controlled by scalar branches
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int blk = lane >> 2, j = lane & 3;
@@ -853,16 +884,17 @@ void decode_mfma_kernel(DecodeArgs a) {
   const int s_t0 = split * tps;
   const int s_t1 = min(s_t0 + tps, ntiles);
 
-  // Two register sets in turn: the loads of a tile are issued while the tile
-  // before it is processed.  The first two tiles' loads go out before the q
-  // rotation, so their latency overlaps it.
+  // kDepth register sets in turn: the loads of a tile are issued kDepth - 1
+  // tiles before it is processed.  The first kDepth tiles' loads go out before
+  // the q rotation, so their latency overlaps it.
   const int lane_c = lane * 32, lane_m = blk * 16;
   const int ti0 = s_t0 + wave;
   const TileStreams st = tile_streams(a, bh);
   auto tile_t0 = [&](int ti) { return (tile_first + ti) << 6; };
-  TileRegs ra, rb;
-  if (ti0 < s_t1) ra = load_tile(st, tile_t0(ti0), lane_c, lane_m);
-  if (ti0 + WPB < s_t1) rb = load_tile(st, tile_t0(ti0 + WPB), lane_c, lane_m);
+  TileRegs r[kDepth];
+#pragma unroll
+  for (int k = 0; k < kDepth; ++k)
+    if (ti0 + k * WPB < s_t1) r[k] = load_tile(st, tile_t0(ti0 + k * WPB), lane_c, lane_m);
   block_q(a, b, h, bh, y, S);
 
   // q operands: 8 words x 4 fp16 of head j; the four lanes groups pp hold the
@@ -881,17 +913,30 @@ void decode_mfma_kernel(DecodeArgs a) {
   const float vmax = a.v.smax[bh];
   int ev2 = 0;
   if (vmax > 0.0f) frexpf(vmax, &ev2);
-  const int ev = (vmax > 0.0f) ? 15 - ev2 : 0;     // s_V * 2^ev < 2^15
-  const float fvA = ldexpf(1.0f, ev - 4 * (blk & 1));
-  const float fvB = ldexpf(1.0f, ev - 4 * (blk & 1) - 2);
+  // s_V * 2^ev < 2^15; capped so that p * 2^ev and its sums stay far from fp32
+  // overflow (a cap that binds only for V scales below 2^-45)
+  const int ev = (vmax > 0.0f) ? min(15 - ev2, 60) : 0;
+  // The softmax weights p of tokens 4 blk + r are computed pre-multiplied by
+  // 2^kA (r = 0, 1) or 2^(kA - 2) (r = 2, 3): 2^ev times the 4^-s of those
+  // tokens' bit position in the V tile, so that s_V * p' is the PV operand as
+  // it stands.  l and sum(p z_V) are kept in the same units per lane (r = 2, 3
+  // accumulated apart) and brought back by 2^-kA at the end.
+  const int kA = ev - 4 * (blk & 1);
+  const float kAf = (float)kA;
   const float cV = ldexpf(1.0f, 24 - ev);
 
   f4 o0 = {0, 0, 0, 0}, o1 = {0, 0, 0, 0};
-  float m = NEG_INF, l = 0.0f, pz = 0.0f;
+  float m = NEG_INF, lA = 0.0f, lB = 0.0f, pzA = 0.0f, pzB = 0.0f;
+  float cA = 0.0f, cB = 0.0f;                      // kA - m and kA - 2 - m
 
   // one 64-token tile: QK^T on matrix cores, online softmax, PV on matrix cores
   auto process = [&](const TileRegs& cur, int t0) {
+#if OSCAR_QK_TWO_CHAINS
     f4 sa = {0, 0, 0, 0}, sb = {0, 0, 0, 0};
+#else
+    f4 sa = {0, 0, 0, 0};
+    f4& sb = sa;                                   // one accumulation chain
+#endif
     qk_word<0>(cur.k0.x, qv[0], sa, sb);
     qk_word<1>(cur.k0.y, qv[1], sa, sb);
     qk_word<2>(cur.k0.z, qv[2], sa, sb);
@@ -900,14 +945,19 @@ void decode_mfma_kernel(DecodeArgs a) {
     qk_word<5>(cur.k1.y, qv[5], sa, sb);
     qk_word<6>(cur.k1.z, qv[6], sa, sb);
     qk_word<7>(cur.k1.w, qv[7], sa, sb);
+#if OSCAR_QK_TWO_CHAINS
     const f4 sc = sa + sb;
+#else
+    const f4 sc = sa;
+#endif
     PHASE_FENCE();
 
     const uint32_t kmr[4] = {cur.km.x, cur.km.y, cur.km.z, cur.km.w};
     const uint32_t vmr[4] = {cur.vm.x, cur.vm.y, cur.vm.z, cur.vm.w};
     float u[4];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) u[r] = __builtin_fmaf(lo_half(kmr[r]), sc[r], hi_half(kmr[r]) * zq);
+    for (int r = 0; r < 4; ++r)   // s_K * dot + z_K * sum(q), fp16 metadata read in place
+      u[r] = __builtin_fmaf(hi_half(kmr[r]), zq, __builtin_fmaf(lo_half(kmr[r]), sc[r], 0.0f));
     if (t0 < lo || t0 + 64 > hi) {                 // boundary tile (wave-uniform)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
@@ -915,28 +965,37 @@ void decode_mfma_kernel(DecodeArgs a) {
         if (t < lo || t >= hi) u[r] = NEG_INF;
       }
     }
-    const float mt = head_max(fmaxf(fmaxf(u[0], u[1]), fmaxf(u[2], u[3])));
-    const float mnew = fmaxf(m, cK * mt);
-    if (__any(mnew > m)) {                         // some head's max moved: rescale
+    // The head-wide maximum is only needed when some score exceeds its head's
+    // running maximum (every lane of a head holds that maximum).
+    const float tmax = cK * fmaxf(fmaxf(u[0], u[1]), fmaxf(u[2], u[3]));
+    if (__any(tmax > m)) {                         // some head's max moved: rescale
+      const float mnew = fmaxf(m, head_max(tmax));
       const float alpha = __builtin_amdgcn_exp2f(m - mnew);
-      l *= alpha;
-      pz *= alpha;
+      lA *= alpha;
+      lB *= alpha;
+      pzA *= alpha;
+      pzB *= alpha;
       const f4 al = {lane_value(alpha, 0), lane_value(alpha, 1), lane_value(alpha, 2), lane_value(alpha, 3)};
       o0 *= al;
       o1 *= al;
       m = mnew;
+      cA = kAf - m;
+      cB = cA - 2.0f;
     }
     float p[4];
-#pragma unroll
-    for (int r = 0; r < 4; ++r) p[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(cK, u[r], -m));
-    l += (p[0] + p[1]) + (p[2] + p[3]);
-    float pzt = 0.0f;
-#pragma unroll
-    for (int r = 0; r < 4; ++r) pzt = __builtin_fmaf(p[r], hi_half(vmr[r]), pzt);
-    pz += pzt;
-    // p * s_V * 2^ev * 4^-s as fp16 (one rounding from fp32)
-    const h4 pv = {(_Float16)(p[0] * (lo_half(vmr[0]) * fvA)), (_Float16)(p[1] * (lo_half(vmr[1]) * fvA)),
-                   (_Float16)(p[2] * (lo_half(vmr[2]) * fvB)), (_Float16)(p[3] * (lo_half(vmr[3]) * fvB))};
+    p[0] = __builtin_amdgcn_exp2f(__builtin_fmaf(cK, u[0], cA));
+    p[1] = __builtin_amdgcn_exp2f(__builtin_fmaf(cK, u[1], cA));
+    p[2] = __builtin_amdgcn_exp2f(__builtin_fmaf(cK, u[2], cB));
+    p[3] = __builtin_amdgcn_exp2f(__builtin_fmaf(cK, u[3], cB));
+    lA += p[0] + p[1];
+    lB += p[2] + p[3];
+    pzA = __builtin_fmaf(p[0], hi_half(vmr[0]), __builtin_fmaf(p[1], hi_half(vmr[1]), pzA));
+    pzB = __builtin_fmaf(p[2], hi_half(vmr[2]), __builtin_fmaf(p[3], hi_half(vmr[3]), pzB));
+    // s_V * p' as fp16 with one rounding (fp16 metadata read in place)
+    const h4 pv = {(_Float16)__builtin_fmaf(lo_half(vmr[0]), p[0], 0.0f),
+                   (_Float16)__builtin_fmaf(lo_half(vmr[1]), p[1], 0.0f),
+                   (_Float16)__builtin_fmaf(lo_half(vmr[2]), p[2], 0.0f),
+                   (_Float16)__builtin_fmaf(lo_half(vmr[3]), p[3], 0.0f)};
     PHASE_FENCE();
     pv_word<0>(cur.v0.x, pv, o0, o1);
     pv_word<1>(cur.v0.y, pv, o0, o1);
@@ -948,17 +1007,19 @@ void decode_mfma_kernel(DecodeArgs a) {
     pv_word<7>(cur.v1.w, pv, o0, o1);
   };
 
-  for (int ti = ti0; ti < s_t1; ti += 2 * WPB) {
-    process(ra, tile_t0(ti));
-    if (ti + 2 * WPB < s_t1) ra = load_tile(st, tile_t0(ti + 2 * WPB), lane_c, lane_m);
-    if (ti + WPB >= s_t1) break;
-    process(rb, tile_t0(ti + WPB));
-    if (ti + 3 * WPB < s_t1) rb = load_tile(st, tile_t0(ti + 3 * WPB), lane_c, lane_m);
+  for (int ti = ti0; ti < s_t1; ti += kDepth * WPB) {
+#pragma unroll
+    for (int k = 0; k < kDepth; ++k) {
+      const int t = ti + k * WPB;
+      if (t >= s_t1) break;
+      process(r[k], tile_t0(t));
+      if (t + kDepth * WPB < s_t1) r[k] = load_tile(st, tile_t0(t + kDepth * WPB), lane_c, lane_m);
+    }
   }
 
   // per-head totals of l and sum(p z_V) over the 16 lanes of each head
-  l = head_sum(l);
-  pz = head_sum(pz);
+  const float l = head_sum(ldexpf(__builtin_fmaf(4.0f, lB, lA), -kA));
+  const float pz = head_sum(ldexpf(__builtin_fmaf(4.0f, pzB, pzA), -kA));
   static_assert(8 * WPB + WPB * 4 * D <= sizeof(S.scratch) / sizeof(float), "epilogue scratch");
   float* sm = S.scratch;                 // [WPB][4]
   float* sl = S.scratch + 4 * WPB;       // [WPB][4]
@@ -1019,6 +1080,14 @@ hipError_t launch_decode_valu(const DecodeArgs& a, int B, hipStream_t s) {
   else
     hipLaunchKernelGGL(decode_valu_kernel<512>, grid, dim3(256), 0, s, a);
   return hipGetLastError();
+}
+
+int decode_mfma_resident_blocks(int device) {
+  int per_cu = 0, cus = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, decode_mfma_kernel<4>, 256, 0) != hipSuccess || per_cu < 1)
+    per_cu = 1;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, device) != hipSuccess || cus < 1) cus = 1;
+  return per_cu * cus;
 }
 
 hipError_t launch_decode_mfma(const DecodeArgs& a, int B, int waves_per_block, hipStream_t s) {

@@ -78,6 +78,7 @@ struct oscar_kv {
   int32_t forced_splits = 0;
   int32_t decode_impl = 0;
   int32_t mfma_waves = 4;
+  int resident = 1024;       // matrix-core kernel blocks resident at once on the device
   bool prof_on = false;
   ProfClass prof[3];
 };
@@ -257,8 +258,12 @@ int do_append(oscar_kv* kv, int32_t layer, const void* k, const void* v, int32_t
 
 // Split count for the INT2 range: aim for about 8 resident waves per SIMD
 // worth of blocks (256 CUs x 4 SIMDs), never more tiles than exist.
+// INT2 splits per (sequence, kv head): about 6 blocks of 4 waves per compute
+// unit in total (measured at 32k context, B = 16, Hkv = 8: 8-12 splits beat 4,
+// 6 and 16; fewer blocks leave compute units idle in the tail, more blocks
+// repeat each block's fixed start-up and merge work).
 int auto_int2_splits(int BH, int ntiles, int waves) {
-  const int target_blocks = 2048 * 4 / std::max(1, waves);
+  const int target_blocks = 1536 * 4 / std::max(1, waves);
   int s = std::max(1, target_blocks / std::max(1, BH));
   s = std::min(s, std::max(1, ntiles / std::max(1, waves)));
   return std::min(s, kMaxSplits - 8);
@@ -340,6 +345,7 @@ int oscar_kv_create(const oscar_kv_config* cfg, oscar_kv** out) {
   if (hipMemset(kv->counters, 0, B * Hkv * sizeof(unsigned)) != hipSuccess)
     return bail(fail(OSCAR_ERR_HIP, "clearing the decode counters failed"));
   if (hipDeviceSynchronize() != hipSuccess) return bail(fail(OSCAR_ERR_HIP, "device sync after create failed"));
+  kv->resident = decode_mfma_resident_blocks(cfg->device);
   *out = kv;
   g_last_error.clear();
   return OSCAR_OK;
@@ -462,6 +468,9 @@ int launch_decode(oscar_kv* kv, int32_t layer, const void* q, void* out, int32_t
     w.slot0 = 0;
     da.plan = p;
     da.win = w;
+    // INT2 splits that fill the first wave of resident blocks go before the
+    // window blocks (which then find q published instead of rotating it)
+    da.int2_lead = std::max(0, std::min(p.splits, kv->resident / std::max(1, BH) - da.app_blocks));
     ca.nslots = p.splits + w.splits;
     da.comb = ca;
     if (++kv->epoch == 0) kv->epoch = 1;   // a flag never holds a future launch's number
