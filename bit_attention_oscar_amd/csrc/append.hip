@@ -39,12 +39,12 @@ __global__ __launch_bounds__(64) void quantize_rows_kernel(const float* x, float
     code[2 * g + 1] = quant_code(v[2 * g + 1], q);
     if (lane == 0) meta[row * (D / kGroup) + g] = q.packed;
   }
-  store_canonical<PER>(code, lane, codes + row * (D / 4));
+  store_canonical<PER>(code, lane, [&](int w) { return reinterpret_cast<uint32_t*>(codes + row * (D / 4) + 4 * w); });
 }
 
-// Canonical export of the tiled V codes: one thread per output byte.
-__global__ __launch_bounds__(256) void export_vcodes_kernel(const uint8_t* tiled, uint8_t* canon, int BH,
-                                                            int cap, int T, int D) {
+// Canonical export of the stored K (isv = 0) or V codes: one thread per output byte.
+__global__ __launch_bounds__(256) void export_codes_kernel(const uint8_t* stored, uint8_t* canon, int BH,
+                                                           int cap, int T, int D, int isv) {
   const size_t nbytes = (size_t)BH * T * (D / 4);
   for (size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x; i < nbytes;
        i += (size_t)gridDim.x * blockDim.x) {
@@ -52,12 +52,16 @@ __global__ __launch_bounds__(256) void export_vcodes_kernel(const uint8_t* tiled
     const size_t rowi = i / (D / 4);
     const int t = (int)(rowi % T);
     const int bh = (int)(rowi / T);
+    if (!isv) {
+      canon[i] = stored[kcode_byte(bh, cap, t, byte, D)];
+      continue;
+    }
     uint32_t out = 0;
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
       int bit;
       const size_t off = vcode_byte(bh, cap, t, 4 * byte + k, D, &bit);
-      out |= (uint32_t)((tiled[off] >> bit) & 3u) << (2 * k);
+      out |= (uint32_t)((stored[off] >> bit) & 3u) << (2 * k);
     }
     canon[i] = (uint8_t)out;
   }
@@ -106,12 +110,12 @@ hipError_t launch_quantize_rows(const float* x, int rows, int D, float clip, uin
   return hipGetLastError();
 }
 
-hipError_t launch_export_vcodes(const uint8_t* tiled, uint8_t* canon, int BH, int cap, int T, int D,
-                                hipStream_t s) {
+hipError_t launch_export_codes(const uint8_t* stored, uint8_t* canon, int BH, int cap, int T, int D, int isv,
+                               hipStream_t s) {
   const size_t n = (size_t)BH * T * (D / 4);
   if (n == 0) return hipSuccess;
   const unsigned blocks = (unsigned)std::min<size_t>((n + 255) / 256, 65536);
-  hipLaunchKernelGGL(export_vcodes_kernel, dim3(blocks), dim3(256), 0, s, tiled, canon, BH, cap, T, D);
+  hipLaunchKernelGGL(export_codes_kernel, dim3(blocks), dim3(256), 0, s, stored, canon, BH, cap, T, D, isv);
   return hipGetLastError();
 }
 

@@ -70,9 +70,10 @@ __device__ inline uint32_t quant_code(float x, const GroupQ& g) {
 
 // Canonical packing through lane shuffles: lane l holds the code of dim
 // l + 64 i; word w (dims 16w..16w+15) is OR-reduced over the 16 lanes
-// 16 (w % 4) .. + 15 of element i = w / 4 and stored by its first lane.
-template <int PER>
-__device__ inline void store_canonical(const uint32_t* code, int lane, uint8_t* row) {
+// 16 (w % 4) .. + 15 of element i = w / 4 and stored by its first lane at
+// word_addr(w).
+template <int PER, class WordAddr>
+__device__ inline void store_canonical(const uint32_t* code, int lane, WordAddr word_addr) {
 #pragma unroll
   for (int i = 0; i < PER; ++i) {
     uint32_t v = code[i] << (2 * (lane & 15));
@@ -80,7 +81,7 @@ __device__ inline void store_canonical(const uint32_t* code, int lane, uint8_t* 
     v |= __shfl_xor(v, 2);
     v |= __shfl_xor(v, 4);
     v |= __shfl_xor(v, 8);
-    if ((lane & 15) == 0) *reinterpret_cast<uint32_t*>(row + 4 * (4 * i + (lane >> 4))) = v;
+    if ((lane & 15) == 0) *word_addr(4 * i + (lane >> 4)) = v;
   }
 }
 
@@ -203,7 +204,9 @@ __device__ inline void append_block(const AppendArgs& a, int bh, bool isv, int t
       }
     }
     if (!P.tiled) {
-      store_canonical<PER>(code, lane, P.codes + kcode_offset(bh, a.cap, t, D));
+      store_canonical<PER>(code, lane, [&](int w) {
+        return reinterpret_cast<uint32_t*>(P.codes + kcode_byte(bh, a.cap, t, 4 * w, D));
+      });
     } else {
 #pragma unroll
       for (int i = 0; i < PER; ++i) {

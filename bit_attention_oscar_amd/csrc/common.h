@@ -16,12 +16,19 @@ constexpr int kMaxGq = 16;            // query heads per kv head handled by the 
 // ---------------------------------------------------------------------------
 // Storage layout (per layer; b = sequence, h = kv head, t = position, d = dim)
 //
-//  K INT2 codes : u8 [B][Hkv][cap][D/4], canonical packing (code d at byte
-//                 d/4, bits 2*(d%4)).  A decode lane owns one token row.
+//  K INT2 codes : canonical packing within a token row (code d at byte d/4,
+//                 bits 2*(d%4)), rows stored by 64-token tile in 16-byte
+//                 chunks: byte i of token t sits in chunk i/16 of the tile,
+//                 and a chunk holds that 16-byte piece of the tile's 64 rows
+//                 (token t%64 at 16*(t%64)).  A decode lane owns one token
+//                 row and each of its 16-byte loads is contiguous across the
+//                 wave.
 //  K/V meta     : u32 [B][Hkv][cap][D/128] = fp16 scale (low) | fp16 zero (high)
 //  V INT2 codes : tiled for the PV matrix-core operand.  For every 64-token
 //                 block and every 128-wide slice of head_dim there is a 2 KiB
-//                 tile = 64 lane records of 32 bytes.  Within a slice,
+//                 tile of 64 lane records of 32 bytes, stored as two 1 KiB
+//                 halves (bytes 0-15 of every record, then bytes 16-31), so
+//                 each 16-byte load is contiguous across the wave.  Within a slice,
 //                 dim ds = d % 128 belongs to lane 4*((ds%64)/4) + ds%4 and to
 //                 half hh = ds/64; token tb = t % 64 lives in 32-bit word tb/8
 //                 of that record at bit
@@ -36,8 +43,10 @@ constexpr int kMaxGq = 16;            // query heads per kv head handled by the 
 // cap is max_context rounded up to a multiple of 64.
 // ---------------------------------------------------------------------------
 
-__host__ __device__ inline size_t kcode_offset(int bh, int cap, int t, int D) {
-  return ((size_t)bh * cap + t) * (size_t)(D / 4);
+// byte offset of byte i (0 <= i < D/4) of token t's K code row
+__host__ __device__ inline size_t kcode_byte(int bh, int cap, int t, int i, int D) {
+  const size_t tile = (size_t)bh * (cap / kTile) + (t >> 6);
+  return tile * (size_t)(kTile * D / 4) + (size_t)(i >> 4) * 1024 + (size_t)(t & 63) * 16 + (i & 15);
 }
 
 __host__ __device__ inline size_t meta_offset(int bh, int cap, int t, int D) {
@@ -52,7 +61,8 @@ __host__ __device__ inline size_t vcode_byte(int bh, int cap, int t, int d, int 
   const int bitpos = 16 * (tb & 1) + 8 * hh + 2 * (2 * ((tb >> 2) & 1) + ((tb >> 1) & 1));
   *bit = bitpos & 7;
   const size_t tile = ((size_t)bh * (cap / kTile) + (t >> 6)) * (size_t)(D / 128) + slice;
-  return tile * 2048 + (size_t)lane * 32 + (size_t)(tb >> 3) * 4 + (bitpos >> 3);
+  const int rec = (tb >> 3) * 4 + (bitpos >> 3);     // byte of the lane record, 0..31
+  return tile * 2048 + (size_t)(rec >> 4) * 1024 + (size_t)lane * 16 + (rec & 15);
 }
 
 __host__ __device__ inline size_t row_offset(int bh, int rows, int t, int D) {
@@ -160,7 +170,7 @@ hipError_t launch_decode_mfma(const DecodeArgs& a, int B, int waves_per_block, h
 int decode_mfma_resident_blocks(int device);   // blocks of the matrix-core kernel resident at once
 hipError_t launch_combine(const CombineArgs& a, hipStream_t s);
 hipError_t launch_stream_copy(const void* src, void* dst, size_t bytes, hipStream_t s);
-hipError_t launch_export_vcodes(const uint8_t* tiled, uint8_t* canon, int BH, int cap, int T, int D,
-                                hipStream_t s);
+hipError_t launch_export_codes(const uint8_t* stored, uint8_t* canon, int BH, int cap, int T, int D, int isv,
+                               hipStream_t s);
 
 }  // namespace oscar

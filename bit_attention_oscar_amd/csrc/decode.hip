@@ -135,9 +135,8 @@ __device__ inline void load_row_values(const PlaneDev& P, int bh, int t, int T, 
   const float s = (float)__builtin_bit_cast(_Float16, (uint16_t)(meta & 0xFFFFu));
   const float z = (float)__builtin_bit_cast(_Float16, (uint16_t)(meta >> 16));
   if (!P.tiled) {
-    const uint8_t* row = P.codes + kcode_offset(bh, cap, t, D);
     for (int i = 0; i < n; i += 16) {
-      const uint32_t w = *reinterpret_cast<const uint32_t*>(row + (d0 + i) / 4);
+      const uint32_t w = *reinterpret_cast<const uint32_t*>(P.codes + kcode_byte(bh, cap, t, (d0 + i) / 4, D));
 #pragma unroll
       for (int k = 0; k < 16; ++k) out[i + k] = __builtin_fmaf(s, (float)((w >> (2 * k)) & 3u), z);
     }
@@ -163,7 +162,7 @@ __device__ inline float load_value(const PlaneDev& P, int bh, int t, int T, int 
   const float z = (float)__builtin_bit_cast(_Float16, (uint16_t)(meta >> 16));
   uint32_t c;
   if (!P.tiled) {
-    c = (P.codes[kcode_offset(bh, cap, t, D) + d / 4] >> (2 * (d & 3))) & 3u;
+    c = (P.codes[kcode_byte(bh, cap, t, d / 4, D)] >> (2 * (d & 3))) & 3u;
   } else {
     int bit;
     const size_t off = vcode_byte(bh, cap, t, d, D, &bit);
@@ -820,7 +819,7 @@ __device__ inline __amdgpu_buffer_rsrc_t plane_rsrc(const void* base, int bytes)
 __device__ inline TileStreams tile_streams(const DecodeArgs& a, int bh) {
   constexpr int D = 128;
   TileStreams s;
-  s.kc = plane_rsrc(a.k.codes + kcode_offset(bh, a.cap, 0, D), a.cap * 32);
+  s.kc = plane_rsrc(a.k.codes + kcode_byte(bh, a.cap, 0, 0, D), a.cap * 32);
   s.km = plane_rsrc(a.k.meta + meta_offset(bh, a.cap, 0, D), a.cap * 4);
   s.vm = plane_rsrc(a.v.meta + meta_offset(bh, a.cap, 0, D), a.cap * 4);
   s.vc = plane_rsrc(a.v.codes + (size_t)bh * (a.cap / kTile) * 2048, a.cap * 32);
@@ -828,17 +827,21 @@ __device__ inline TileStreams tile_streams(const DecodeArgs& a, int bh) {
 }
 
 // Loads of the tile starting at token t0 (a multiple of 64).  Code streams:
-// lane l reads the 32 bytes of token t0 + l (K) and V record l of the tile;
-// metadata: lane (blk, j) reads tokens t0 + 4 blk .. + 3.
+// lane l reads the 32 bytes of token t0 + l (K) and V record l of the tile as
+// two 16-byte pieces, each contiguous across the wave (lane_c = 16 l), with
+// the non-temporal hint (every code byte is read once per launch); metadata:
+// lane (blk, j) reads tokens t0 + 4 blk .. + 3.
+constexpr int kStreamOnce = 2;   // cache policy bits of a buffer load: nt
+
 __device__ inline TileRegs load_tile(const TileStreams& s, int t0, int lane_c, int lane_m) {
   const int oc = t0 * 32, om = t0 * 4;
   TileRegs r;
-  r.k0 = __builtin_amdgcn_raw_buffer_load_b128(s.kc, lane_c, oc, 0);
-  r.k1 = __builtin_amdgcn_raw_buffer_load_b128(s.kc, lane_c + 16, oc, 0);
+  r.k0 = __builtin_amdgcn_raw_buffer_load_b128(s.kc, lane_c, oc, kStreamOnce);
+  r.k1 = __builtin_amdgcn_raw_buffer_load_b128(s.kc, lane_c + 1024, oc, kStreamOnce);
   r.km = __builtin_amdgcn_raw_buffer_load_b128(s.km, lane_m, om, 0);
   r.vm = __builtin_amdgcn_raw_buffer_load_b128(s.vm, lane_m, om, 0);
-  r.v0 = __builtin_amdgcn_raw_buffer_load_b128(s.vc, lane_c, oc, 0);
-  r.v1 = __builtin_amdgcn_raw_buffer_load_b128(s.vc, lane_c + 16, oc, 0);
+  r.v0 = __builtin_amdgcn_raw_buffer_load_b128(s.vc, lane_c, oc, kStreamOnce);
+  r.v1 = __builtin_amdgcn_raw_buffer_load_b128(s.vc, lane_c + 1024, oc, kStreamOnce);
   return r;
 }
 
@@ -887,7 +890,7 @@ void decode_mfma_kernel(DecodeArgs a) {
   // kDepth register sets in turn: the loads of a tile are issued kDepth - 1
   // tiles before it is processed.  The first kDepth tiles' loads go out before
   // the q rotation, so their latency overlaps it.
-  const int lane_c = lane * 32, lane_m = blk * 16;
+  const int lane_c = lane * 16, lane_m = blk * 16;
   const int ti0 = s_t0 + wave;
   const TileStreams st = tile_streams(a, bh);
   auto tile_t0 = [&](int ti) { return (tile_first + ti) << 6; };

@@ -631,17 +631,13 @@ int oscar_kv_export(oscar_kv* kv, int32_t layer, int32_t which, void* host_codes
     return OSCAR_OK;
   }
   if (host_codes && T > 0) {
-    if (which == 0) {
-      HIP_TRY(hipMemcpy2D(host_codes, (size_t)T * (D / 4), p.codes, (size_t)cap * (D / 4), (size_t)T * (D / 4),
-                          BH, hipMemcpyDeviceToHost));
-    } else {
-      uint8_t* tmp = nullptr;
-      HIP_TRY(hipMalloc(&tmp, (size_t)BH * T * (D / 4)));
-      hipError_t e = launch_export_vcodes(p.codes, tmp, BH, cap, T, D, nullptr);
-      if (e == hipSuccess) e = hipMemcpy(host_codes, tmp, (size_t)BH * T * (D / 4), hipMemcpyDeviceToHost);
-      (void)hipFree(tmp);
-      HIP_TRY(e);
-    }
+    // both planes are stored tiled; the export is canonical [BH][T][D/4]
+    uint8_t* tmp = nullptr;
+    HIP_TRY(hipMalloc(&tmp, (size_t)BH * T * (D / 4)));
+    hipError_t e = launch_export_codes(p.codes, tmp, BH, cap, T, D, which, nullptr);
+    if (e == hipSuccess) e = hipMemcpy(host_codes, tmp, (size_t)BH * T * (D / 4), hipMemcpyDeviceToHost);
+    (void)hipFree(tmp);
+    HIP_TRY(e);
   }
   if (host_meta && T > 0)
     HIP_TRY(hipMemcpy2D(host_meta, (size_t)T * (D / kGroup) * 4, p.meta, (size_t)cap * (D / kGroup) * 4,
