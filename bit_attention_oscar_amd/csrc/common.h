@@ -10,7 +10,7 @@ namespace oscar {
 constexpr int kGroup = 128;           // quantization group along head_dim
 constexpr int kTile = 64;             // tokens per decode tile / V storage block
 constexpr int kMaxSplits = 256;       // partial-result slots per (sequence, head)
-constexpr int kQPub = 4 * 128 + 8;    // published q of one (sequence, kv head): 4 heads x 128, sums, exponents
+constexpr int kQPub = 4 * 128 + 8 + 256;  // published q of one (sequence, kv head): fp32 q, sums, exponents, fp16 operands
 constexpr int kMaxGq = 16;            // query heads per kv head handled by the VALU kernel
 
 // ---------------------------------------------------------------------------
@@ -144,6 +144,7 @@ struct DecodeArgs {
                            // block of each (sequence, kv head) in a matrix-core launch
   unsigned* qflag;         // [B*Hkv]: epoch of the launch whose q qpub holds
   unsigned epoch;          // this launch's number (never 0)
+  unsigned qwait_ticks;    // longest wait for the published q, in wall-clock ticks
   float* partials;         // [B][Hq][kMaxSplits][D+2]
   int Hq, Hkv, D, cap, N, M, T;
   SegPlan plan;            // INT2 range (matrix-core kernel) or all tokens (VALU kernel)

@@ -489,7 +489,10 @@ __device__ inline void st_partial(float* p, float v) {
 // barrier, then one thread increments the counter; the last block reads the
 // partials with device-scope loads.  No cache-wide write-back or invalidation,
 // and no block ever waits for another.
-__device__ inline void finish_block(const DecodeArgs& a, int bh) {
+struct FusedSmem;
+__device__ void combine_fused(const CombineArgs& a, int bh, FusedSmem& S);
+
+__device__ inline void finish_block(const DecodeArgs& a, int bh, FusedSmem& S) {
   __shared__ int is_last;
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
@@ -500,7 +503,7 @@ __device__ inline void finish_block(const DecodeArgs& a, int bh) {
   }
   __syncthreads();
   if (!is_last) return;
-  combine_group<128, true>(a.comb, bh);
+  combine_fused(a.comb, bh, S);
   if (threadIdx.x == 0) a.counters[bh] = 0u;
 }
 
@@ -565,32 +568,133 @@ __device__ void block_rotate_q(const DecodeArgs& a, int b, int h, FusedSmem& S) 
   __syncthreads();
 }
 
-// The first attention block of each (sequence, kv head) publishes its rotated
-// q for the other blocks of the launch: device-scope stores, a wait until they
-// have completed, then this launch's epoch in the flag.  A block that finds
-// the flag holding this launch's epoch reads q back with device-scope loads;
-// any other block rotates q itself.  No block ever waits for another, and both
-// routes give identical bits.
+// fp16 matrix-core q operand: element k of word w for lane group pp of head j
+// is q_rot[d] * 2^(eq - 2 (d % 4)) with d = qk_dim(w, pp, k).
+__device__ inline _Float16 q_operand(const FusedSmem& S, int j, int pp, int w, int k) {
+  const int d = qk_dim(w, pp, k);
+  return (_Float16)ldexpf(S.qs[j][d], S.qeq[j] - 2 * (d & 3));
+}
+
+// Published q of one (sequence, kv head), kQPub floats:
+//   [0, 512)          fp32 rotated q of the 4 heads, head-major
+//   [512, 516)        per-head sums; [516, 520) per-head exponents eq (int bits)
+//   [kQPubOps, +256)  fp16 matrix-core operands: vector 4 pp + j holds the 32
+//                     values (word w, slot k at 4 w + k) of lane group pp, head j
+constexpr int kQPubOps = 520;
+static_assert(kQPubOps + 256 <= kQPub, "published q layout");
+
+// The first attention block of each (sequence, kv head) rotates q and
+// publishes it for the other blocks of the launch: device-scope stores, a
+// wait until they have completed, then this launch's epoch in the flag.
 __device__ void publish_q(const DecodeArgs& a, int bh, FusedSmem& S) {
   float* dst = a.qpub + (size_t)bh * kQPub;
-  for (int i = threadIdx.x; i < 4 * 128; i += blockDim.x) st_partial(dst + i, S.qs[i >> 7][i & 127]);
-  if (threadIdx.x < 4) {
-    st_partial(dst + 512 + threadIdx.x, S.qsum[threadIdx.x]);
-    st_partial(dst + 516 + threadIdx.x, __int_as_float(S.qeq[threadIdx.x]));
+  const int tid = threadIdx.x;
+  for (int i = tid; i < 4 * 128; i += blockDim.x) st_partial(dst + i, S.qs[i >> 7][i & 127]);
+  if (tid < 4) {
+    st_partial(dst + 512 + tid, S.qsum[tid]);
+    st_partial(dst + 516 + tid, __int_as_float(S.qeq[tid]));
+  }
+  if (tid < 256) {                      // one word (two fp16 operands) per thread
+    const int v = tid >> 4, e = 2 * (tid & 15);
+    const int pp = v >> 2, j = v & 3;
+    const uint32_t lo = __builtin_bit_cast(uint16_t, q_operand(S, j, pp, e >> 2, e & 3));
+    const uint32_t hi = __builtin_bit_cast(uint16_t, q_operand(S, j, pp, (e + 1) >> 2, (e + 1) & 3));
+    st_partial(dst + kQPubOps + tid, __uint_as_float(lo | (hi << 16)));
   }
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
-  if (threadIdx.x == 0) __hip_atomic_store(a.qflag + bh, a.epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (tid == 0) __hip_atomic_store(a.qflag + bh, a.epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-__device__ void obtain_q(const DecodeArgs& a, int b, int h, int bh, FusedSmem& S) {
-  if (threadIdx.x == 0)
-    S.ready = __hip_atomic_load(a.qflag + bh, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == a.epoch;
-  __syncthreads();
-  if (!S.ready) {
-    block_rotate_q(a, b, h, S);
-    return;
+// Merge of the (m, l, o') partials of one (sequence, kv head) by the last
+// block of the matrix-core launch, then o = o' @ R_V^T (4 query heads per kv
+// head, head_dim 128).  Wave j merges head j: lane l owns dims l and l + 64
+// and loads 16 slots at a time (their m and l, the same words in every lane,
+// and its two o' values) in one round trip, merging into a running maximum.
+// The rotation splits its reduction over e across the four waves and adds the
+// partial sums in a fixed order.
+__device__ void combine_fused(const CombineArgs& a, int bh, FusedSmem& S) {
+  constexpr int D = 128, SB = 16;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int b = bh / a.Hkv, kvh = bh - (bh / a.Hkv) * a.Hkv;
+  const float* P = a.partials + ((size_t)b * a.Hq + kvh * 4 + wave) * kMaxSplits * (D + 2);
+  float M = NEG_INF, L = 0.0f, o0 = 0.0f, o1 = 0.0f;
+  for (int s0 = 0; s0 < a.nslots; s0 += SB) {
+    float ms[SB], ls[SB], x0[SB], x1[SB];
+#pragma unroll
+    for (int u = 0; u < SB; ++u) {
+      const float* p = P + (size_t)min(s0 + u, a.nslots - 1) * (D + 2);
+      ms[u] = ld_partial<true>(p + D);
+      ls[u] = ld_partial<true>(p + D + 1);
+      x0[u] = ld_partial<true>(p + lane);
+      x1[u] = ld_partial<true>(p + lane + 64);
+    }
+    float mb = M;
+#pragma unroll
+    for (int u = 0; u < SB; ++u)
+      if (s0 + u < a.nslots) mb = fmaxf(mb, ms[u]);
+    if (mb == NEG_INF) continue;                    // no token in these slots yet
+    const float keep = exp2f(M - mb);               // 0 while M is -inf
+    L *= keep;
+    o0 *= keep;
+    o1 *= keep;
+#pragma unroll
+    for (int u = 0; u < SB; ++u) {
+      const float w = (s0 + u < a.nslots && ms[u] != NEG_INF) ? exp2f(ms[u] - mb) : 0.0f;
+      L = __builtin_fmaf(ls[u], w, L);
+      o0 = __builtin_fmaf(x0[u], w, o0);
+      o1 = __builtin_fmaf(x1[u], w, o1);
+    }
+    M = mb;
   }
+  const float inv = 1.0f / L;
+  float* os = S.scratch;                  // [4][128]
+  float* part = S.scratch + 4 * D;        // [4 waves][4][128]
+  os[wave * D + lane] = o0 * inv;
+  os[wave * D + lane + 64] = o1 * inv;
+  __syncthreads();
+  rotate_rows<D, 4, 4>(os, a.rvT, part, 4);
+  __syncthreads();
+  for (int idx = tid; idx < 4 * D; idx += 256) {
+    const int j = idx >> 7, d = idx & 127;
+    const float v = rot_sum<D, 4, 4>(part, j, d);
+    const size_t o = ((size_t)b * a.Hq + kvh * 4 + j) * D + d;
+    if (a.out_dtype == 0)
+      reinterpret_cast<float*>(a.out)[o] = v;
+    else if (a.out_dtype == 1)
+      reinterpret_cast<uint16_t*>(a.out)[o] = f32_to_bf16(v);
+    else
+      reinterpret_cast<uint16_t*>(a.out)[o] = __builtin_bit_cast(uint16_t, (_Float16)v);
+  }
+}
+
+// Thread 0's first read of the flag, issued before a block's tile loads so
+// that waiting for it does not wait for them.
+__device__ inline unsigned first_flag_read(const DecodeArgs& a, int bh) {
+  return threadIdx.x == 0 ? __hip_atomic_load(a.qflag + bh, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 0u;
+}
+
+// Bounded wait for this launch's published q: thread 0 polls the flag for at
+// most a.qwait_ticks of the constant-rate wall clock, then gives up (the block
+// rotates q itself).  The wait always ends, whatever the dispatch order.
+__device__ bool wait_published_q(const DecodeArgs& a, int bh, unsigned first, FusedSmem& S) {
+  if (threadIdx.x == 0) {
+    unsigned f = first;
+    if (f != a.epoch) {
+      const long long t0 = wall_clock64();
+      do {
+        __builtin_amdgcn_s_sleep(4);
+        f = __hip_atomic_load(a.qflag + bh, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      } while (f != a.epoch && wall_clock64() - t0 < (long long)a.qwait_ticks);
+    }
+    S.ready = f == a.epoch;
+  }
+  __syncthreads();
+  return S.ready != 0;
+}
+
+// fp32 published q into shared memory (window blocks).
+__device__ void load_published_q(const DecodeArgs& a, int bh, FusedSmem& S) {
   const float* src = a.qpub + (size_t)bh * kQPub;
   for (int i = threadIdx.x; i < 4 * 128; i += blockDim.x) S.qs[i >> 7][i & 127] = ld_partial<true>(src + i);
   if (threadIdx.x < 4) {
@@ -600,14 +704,16 @@ __device__ void obtain_q(const DecodeArgs& a, int b, int h, int bh, FusedSmem& S
   __syncthreads();
 }
 
-// q of the block's 4 query heads: attention block 0 of the (sequence, kv head)
-// rotates and publishes it, the others take the published copy when it is there.
-__device__ inline void block_q(const DecodeArgs& a, int b, int h, int bh, int y, FusedSmem& S) {
+// q of a window block: attention block 0 rotates and publishes, the others
+// take the published copy (bounded wait) or rotate themselves.
+__device__ inline void window_q(const DecodeArgs& a, int b, int h, int bh, int y, FusedSmem& S) {
   if (y == 0) {
     block_rotate_q(a, b, h, S);
     publish_q(a, bh, S);
+  } else if (wait_published_q(a, bh, first_flag_read(a, bh), S)) {
+    load_published_q(a, bh, S);
   } else {
-    obtain_q(a, b, h, bh, S);
+    block_rotate_q(a, b, h, S);
   }
 }
 
@@ -832,6 +938,7 @@ __device__ inline TileStreams tile_streams(const DecodeArgs& a, int bh) {
 // the non-temporal hint (every code byte is read once per launch); metadata:
 // lane (blk, j) reads tokens t0 + 4 blk .. + 3.
 constexpr int kStreamOnce = 2;   // cache policy bits of a buffer load: nt
+constexpr int kDeviceScope = 16; // cache policy bits of a buffer load: sc1 (coherent across the device)
 
 __device__ inline TileRegs load_tile(const TileStreams& s, int t0, int lane_c, int lane_m) {
   const int oc = t0 * 32, om = t0 * 4;
@@ -871,9 +978,9 @@ void decode_mfma_kernel(DecodeArgs a) {
   // start once slots free up, by when block 0 has published q.
   const int lead = a.int2_lead;
   if (y >= lead && y < lead + a.win.splits) {
-    block_q(a, b, h, bh, y, S);
+    window_q(a, b, h, bh, y, S);
     window_block(a, bh, b, h, y - lead, S);
-    finish_block(a, bh);
+    finish_block(a, bh, S);
     return;
   }
   const int split = y < lead ? y : y - a.win.splits;
@@ -894,25 +1001,50 @@ void decode_mfma_kernel(DecodeArgs a) {
   const int ti0 = s_t0 + wave;
   const TileStreams st = tile_streams(a, bh);
   auto tile_t0 = [&](int ti) { return (tile_first + ti) << 6; };
+  // q: attention block 0 rotates and publishes it before its tile loads; the
+  // others read the flag before theirs and take the published operands
+  unsigned flag0 = 0;
+  if (y == 0) {
+    block_rotate_q(a, b, h, S);
+    publish_q(a, bh, S);
+  } else {
+    flag0 = first_flag_read(a, bh);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  // The first loads are unconditional (a wave with fewer tiles re-reads its
+  // split's last tile), so the flag can be waited for on its own.
   TileRegs r[kDepth];
 #pragma unroll
-  for (int k = 0; k < kDepth; ++k)
-    if (ti0 + k * WPB < s_t1) r[k] = load_tile(st, tile_t0(ti0 + k * WPB), lane_c, lane_m);
-  block_q(a, b, h, bh, y, S);
+  for (int k = 0; k < kDepth; ++k) r[k] = load_tile(st, tile_t0(min(ti0 + k * WPB, s_t1 - 1)), lane_c, lane_m);
+  __builtin_amdgcn_sched_barrier(0);
 
-  // q operands: 8 words x 4 fp16 of head j; the four lanes groups pp hold the
-  // k-slots of qk_dim(w, pp, k), each scaled by 2^eq 4^-(d % 4)
-  const int eq = S.qeq[j];
+  // q operands: 8 words x 4 fp16 of head j; lane group pp holds the k-slots
+  // of qk_dim(w, pp, k), each scaled by 2^eq 4^-(d % 4)
   h4 qv[8];
+  int eq;
+  float qsum;
+  if (y != 0 && wait_published_q(a, bh, flag0, S)) {
+    const __amdgpu_buffer_rsrc_t qr = plane_rsrc(a.qpub + (size_t)bh * kQPub, kQPub * 4);
+    const int vbase = (kQPubOps + 16 * (4 * (lane >> 4) + j)) * 4;
 #pragma unroll
-  for (int w = 0; w < 8; ++w)
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const int d = qk_dim(w, lane >> 4, k);
-      qv[w][k] = (_Float16)ldexpf(S.qs[j][d], eq - 2 * (d & 3));
+    for (int i = 0; i < 4; ++i) {
+      const u4 wv = __builtin_amdgcn_raw_buffer_load_b128(qr, vbase + 16 * i, 0, kDeviceScope);
+      qv[2 * i] = as_h4(wv.x, wv.y);
+      qv[2 * i + 1] = as_h4(wv.z, wv.w);
     }
+    qsum = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(qr, (512 + j) * 4, 0, kDeviceScope));
+    eq = (int)__builtin_amdgcn_raw_buffer_load_b32(qr, (516 + j) * 4, 0, kDeviceScope);
+  } else {
+    if (y != 0) block_rotate_q(a, b, h, S);
+#pragma unroll
+    for (int w = 0; w < 8; ++w)
+#pragma unroll
+      for (int k = 0; k < 4; ++k) qv[w][k] = q_operand(S, j, lane >> 4, w, k);
+    qsum = S.qsum[j];
+    eq = S.qeq[j];
+  }
   const float cK = ldexpf(1.0f, 24 - eq);          // undoes 2^eq and the 2^-24 code scale
-  const float zq = ldexpf(S.qsum[j], eq - 24);     // sum(q_rot) in units of the raw dot
+  const float zq = ldexpf(qsum, eq - 24);          // sum(q_rot) in units of the raw dot
   const float vmax = a.v.smax[bh];
   int ev2 = 0;
   if (vmax > 0.0f) frexpf(vmax, &ev2);
@@ -1060,7 +1192,7 @@ void decode_mfma_kernel(DecodeArgs a) {
       st_partial(dst + D + 1, L);
     }
   }
-  finish_block(a, bh);
+  finish_block(a, bh, S);
 }
 
 // ---------------------------------------------------------------------------

@@ -79,6 +79,7 @@ struct oscar_kv {
   int32_t decode_impl = 0;
   int32_t mfma_waves = 4;
   int resident = 1024;       // matrix-core kernel blocks resident at once on the device
+  unsigned qwait_ticks = 2000;  // 20 us of the device wall clock (set from its rate at create)
   bool prof_on = false;
   ProfClass prof[3];
 };
@@ -346,6 +347,9 @@ int oscar_kv_create(const oscar_kv_config* cfg, oscar_kv** out) {
     return bail(fail(OSCAR_ERR_HIP, "clearing the decode counters failed"));
   if (hipDeviceSynchronize() != hipSuccess) return bail(fail(OSCAR_ERR_HIP, "device sync after create failed"));
   kv->resident = decode_mfma_resident_blocks(cfg->device);
+  int wall_khz = 0;
+  if (hipDeviceGetAttribute(&wall_khz, hipDeviceAttributeWallClockRate, cfg->device) == hipSuccess && wall_khz > 0)
+    kv->qwait_ticks = (unsigned)std::min<long long>(20LL * wall_khz / 1000, 1LL << 30);
   *out = kv;
   g_last_error.clear();
   return OSCAR_OK;
@@ -475,6 +479,7 @@ int launch_decode(oscar_kv* kv, int32_t layer, const void* q, void* out, int32_t
     da.comb = ca;
     if (++kv->epoch == 0) kv->epoch = 1;   // a flag never holds a future launch's number
     da.epoch = kv->epoch;
+    da.qwait_ticks = kv->qwait_ticks;
     const long pk = prof_begin(kv, 0, stream);
     HIP_TRY(launch_decode_mfma(da, batch, kv->mfma_waves, stream));
     prof_end(kv, 0, pk, stream);
