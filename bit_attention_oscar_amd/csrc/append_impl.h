@@ -120,6 +120,51 @@ __device__ inline void rotate_rows(const float* xs, const float* R, float* part,
   (void)ntok;
 }
 
+// The same rotation with this lane's rows of R loaded up front into
+// registers (head_dim 128: 32 rows of e, dims lane and lane + 64), so that a
+// block can issue them together with its other loads: one memory round trip
+// instead of one per chunk of e.  Identical arithmetic and bits.
+template <int D, int WAVES>
+struct RRows {
+  static constexpr int EW = D / WAVES, PER = D / 64;
+  float r[EW][PER];
+};
+
+template <int D, int WAVES>
+__device__ inline RRows<D, WAVES> load_r_rows(const float* R) {
+  RRows<D, WAVES> rr;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const float* Rw = R + (size_t)(wave * RRows<D, WAVES>::EW) * D + lane;
+#pragma unroll
+  for (int e = 0; e < RRows<D, WAVES>::EW; ++e)
+#pragma unroll
+    for (int i = 0; i < RRows<D, WAVES>::PER; ++i) rr.r[e][i] = Rw[(size_t)e * D + 64 * i];
+  return rr;
+}
+
+template <int D, int WAVES, int NT>
+__device__ inline void rotate_rows_regs(const float* xs, const RRows<D, WAVES>& rr, float* part) {
+  constexpr int PER = D / 64, EW = D / WAVES;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  float acc[NT][PER];
+#pragma unroll
+  for (int tk = 0; tk < NT; ++tk)
+#pragma unroll
+    for (int i = 0; i < PER; ++i) acc[tk][i] = 0.0f;
+#pragma unroll
+  for (int e = 0; e < EW; ++e)
+#pragma unroll
+    for (int tk = 0; tk < NT; ++tk) {
+      const float x = xs[tk * D + wave * EW + e];
+#pragma unroll
+      for (int i = 0; i < PER; ++i) acc[tk][i] = __builtin_fmaf(x, rr.r[e][i], acc[tk][i]);
+    }
+#pragma unroll
+  for (int tk = 0; tk < NT; ++tk)
+#pragma unroll
+    for (int i = 0; i < PER; ++i) part[(wave * NT + tk) * D + lane + 64 * i] = acc[tk][i];
+}
+
 template <int D, int WAVES, int NT>
 __device__ inline float rot_sum(const float* part, int tk, int d) {
   float v = part[tk * D + d];
@@ -146,18 +191,29 @@ __device__ inline void append_block(const AppendArgs& a, int bh, bool isv, int t
   float* dump = isv ? a.vdump : a.kdump;
   const int ntok = t_hi - t_lo;
 
-  for (int i = tid; i < NT * D; i += 64 * WAVES) {
-    const int tk = i / D, d = i - (i / D) * D;
-    float v = 0.0f;
-    if (tk < ntok) {
-      const int t = t_lo + tk;
-      const size_t idx = (((size_t)b * a.n_new + (t - a.T_old)) * a.Hkv + h) * D + d;
-      v = bf16_to_f32(in[idx]);
+  auto load_inputs = [&]() {
+    for (int i = tid; i < NT * D; i += 64 * WAVES) {
+      const int tk = i / D, d = i - (i / D) * D;
+      float v = 0.0f;
+      if (tk < ntok) {
+        const int t = t_lo + tk;
+        const size_t idx = (((size_t)b * a.n_new + (t - a.T_old)) * a.Hkv + h) * D + d;
+        v = bf16_to_f32(in[idx]);
+      }
+      xs[i] = v;
     }
-    xs[i] = v;
+  };
+  if constexpr (D == 128 && WAVES == 4) {
+    // R rows and inputs in one round trip
+    const RRows<D, WAVES> rr = load_r_rows<D, WAVES>(R);
+    load_inputs();
+    __syncthreads();
+    rotate_rows_regs<D, WAVES, NT>(xs, rr, part);
+  } else {
+    load_inputs();
+    __syncthreads();
+    rotate_rows<D, WAVES, NT>(xs, R, part, ntok);
   }
-  __syncthreads();
-  rotate_rows<D, WAVES, NT>(xs, R, part, ntok);
   __syncthreads();
   if (wave != 0) return;
 

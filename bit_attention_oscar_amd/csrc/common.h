@@ -158,6 +158,7 @@ struct DecodeArgs {
   float scale_log2;        // softmax scale * log2(e)
   int app_blocks;          // 2 when the launch also appends this step's token, else 0
   int int2_lead;           // INT2 splits dispatched before the window blocks
+  int win_blocks;          // window blocks of the launch (win.splits)
   AppendArgs app;          // that append (n_new = 1); T above counts the new token
 };
 

@@ -497,7 +497,7 @@ __device__ inline void finish_block(const DecodeArgs& a, int bh, FusedSmem& S) {
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   if (threadIdx.x == 0) {
-    const unsigned total = (unsigned)(a.plan.splits + a.win.splits);
+    const unsigned total = (unsigned)(a.plan.splits + a.win_blocks);
     const unsigned prev = __hip_atomic_fetch_add(a.counters + bh, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     is_last = (prev == total - 1u);
   }
@@ -539,16 +539,57 @@ struct FusedSmem {
   float scratch[2688];
 };
 
-// q rotation of the block's 4 query heads (same arithmetic for every block).
-__device__ void block_rotate_q(const DecodeArgs& a, int b, int h, FusedSmem& S) {
+// q rotation of the block's 4 query heads, in two steps so that a block can
+// issue every load it needs at once (one memory round trip) and put other
+// loads behind them before it waits: the raw q rows (two values per thread)
+// and this lane's rows of R_K (its wave's quarter of e, dims lane and
+// lane + 64).  The arithmetic is the append path's rotation routine's: fmas
+// over e ascending per wave, the four partial sums added in a fixed order.
+struct QRotLoads {
+  float q0, q1;
+  float r[32][2];
+};
+
+__device__ inline QRotLoads q_rotation_loads(const DecodeArgs& a, int b, int h) {
+  constexpr int D = 128;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  QRotLoads s;
+  const uint16_t* qb = a.q + ((size_t)b * a.Hq + h * 4) * D;     // the 4 heads' rows, contiguous
+  s.q0 = bf16_to_f32(qb[tid]);
+  s.q1 = bf16_to_f32(qb[tid + 256]);
+  const float* Rw = a.rk + (size_t)(wave * 32) * D + lane;
+#pragma unroll
+  for (int e = 0; e < 32; ++e) {
+    s.r[e][0] = Rw[(size_t)e * D];
+    s.r[e][1] = Rw[(size_t)e * D + 64];
+  }
+  return s;
+}
+
+__device__ void q_rotation_finish(const DecodeArgs& a, const QRotLoads& s, FusedSmem& S) {
   constexpr int D = 128;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   float* qraw = S.scratch;            // [4][128]
   float* part = S.scratch + 512;      // [4 waves][4][128]
-  for (int i = tid; i < 4 * D; i += 256)
-    qraw[i] = bf16_to_f32(a.q[((size_t)b * a.Hq + h * 4 + (i >> 7)) * D + (i & 127)]);
+  qraw[tid] = s.q0;
+  qraw[tid + 256] = s.q1;
   __syncthreads();
-  rotate_rows<128, 4, 4>(qraw, a.rk, part, 4);
+  float acc[4][2];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) acc[j][0] = acc[j][1] = 0.0f;
+#pragma unroll
+  for (int e = 0; e < 32; ++e)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const float x = qraw[j * D + wave * 32 + e];
+      acc[j][0] = __builtin_fmaf(x, s.r[e][0], acc[j][0]);
+      acc[j][1] = __builtin_fmaf(x, s.r[e][1], acc[j][1]);
+    }
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    part[(wave * 4 + j) * D + lane] = acc[j][0];
+    part[(wave * 4 + j) * D + lane + 64] = acc[j][1];
+  }
   __syncthreads();
   {
     const int j = wave;                // wave j finishes head j
@@ -564,6 +605,37 @@ __device__ void block_rotate_q(const DecodeArgs& a, int b, int h, FusedSmem& S) 
       S.qsum[j] = sum;
       S.qeq[j] = (amax > 0.0f) ? 15 - e2 : 0;     // |q| * 2^eq < 2^15
     }
+  }
+  __syncthreads();
+}
+
+__device__ inline void block_rotate_q(const DecodeArgs& a, int b, int h, FusedSmem& S) {
+  q_rotation_finish(a, q_rotation_loads(a, b, h), S);
+}
+
+// The same rotation with R_K read in chunks (few registers): for a block
+// whose tile registers are already live.  Identical arithmetic and bits.
+__device__ void block_rotate_q_chunked(const DecodeArgs& a, int b, int h, FusedSmem& S) {
+  constexpr int D = 128;
+  const int tid = threadIdx.x;
+  float* qraw = S.scratch;            // [4][128]
+  float* part = S.scratch + 512;      // [4 waves][4][128]
+  for (int i = tid; i < 4 * D; i += 256) qraw[i] = bf16_to_f32(a.q[((size_t)b * a.Hq + h * 4) * D + i]);
+  __syncthreads();
+  rotate_rows<128, 4, 4>(qraw, a.rk, part, 4);
+  __syncthreads();
+  const int wave = tid >> 6, lane = tid & 63, j = wave;
+  const float v0 = rot_sum<128, 4, 4>(part, j, lane) * a.scale_log2;
+  const float v1 = rot_sum<128, 4, 4>(part, j, lane + 64) * a.scale_log2;
+  S.qs[j][lane] = v0;
+  S.qs[j][lane + 64] = v1;
+  const float sum = wsum(v0 + v1);
+  const float amax = wmax(fmaxf(fabsf(v0), fabsf(v1)));
+  int e2 = 0;
+  if (amax > 0.0f) frexpf(amax, &e2);
+  if (lane == 0) {
+    S.qsum[j] = sum;
+    S.qeq[j] = (amax > 0.0f) ? 15 - e2 : 0;
   }
   __syncthreads();
 }
@@ -735,9 +807,10 @@ __device__ void window_block(const DecodeArgs& a, int bh, int b, int h, int wblk
       const uint16_t* in = which ? a.app.vin : a.app.kin;
       float* xs = S.scratch;          // [128]
       float* part = S.scratch + 128;  // [4][128]
+      const RRows<128, 4> rr = load_r_rows<128, 4>(which ? a.app.rv : a.app.rk);
       if (tid < D) xs[tid] = bf16_to_f32(in[((size_t)b * a.Hkv + h) * D + tid]);
       __syncthreads();
-      rotate_rows<128, 4, 1>(xs, which ? a.app.rv : a.app.rk, part, 1);
+      rotate_rows_regs<128, 4, 1>(xs, rr, part);
       __syncthreads();
       if (tid < D) S.newtok[which][tid] = f32_to_bf16(rot_sum<128, 4, 1>(part, 0, tid));
       __syncthreads();
@@ -964,9 +1037,8 @@ void decode_mfma_kernel(DecodeArgs a) {
   __shared__ FusedSmem S;
   // Block roles along y, in dispatch order:
   //   [0, app_blocks)                 append of the new token (K, then V)
-  //   [.., + win.splits)              bf16 window blocks
-  //   [.., + plan.splits)             INT2 splits
-  // Window blocks go before the INT2 ones so that they overlap them.
+  //   then the attention blocks: int2_lead INT2 splits, the win_blocks bf16
+  //   window blocks, the remaining INT2 splits.
   int y = (int)blockIdx.y;
   if (y < a.app_blocks) {
     append_block<128, 4, 1>(a.app, bh, y == 1, a.app.T_old, a.app.T_old + 1, S.scratch, S.scratch + 128);
@@ -977,13 +1049,13 @@ void decode_mfma_kernel(DecodeArgs a) {
   // splits.  The lead splits fill the compute units first; the window blocks
   // start once slots free up, by when block 0 has published q.
   const int lead = a.int2_lead;
-  if (y >= lead && y < lead + a.win.splits) {
+  if (y >= lead && y < lead + a.win_blocks) {
     window_q(a, b, h, bh, y, S);
     window_block(a, bh, b, h, y - lead, S);
     finish_block(a, bh, S);
     return;
   }
-  const int split = y < lead ? y : y - a.win.splits;
+  const int split = y < lead ? y : y - a.win_blocks;
   // wave index as a uniform value: the tile loop is controlled by scalar branches
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int blk = lane >> 2, j = lane & 3;
@@ -995,13 +1067,13 @@ void decode_mfma_kernel(DecodeArgs a) {
   const int s_t1 = min(s_t0 + tps, ntiles);
 
   // kDepth register sets in turn: the loads of a tile are issued kDepth - 1
-  // tiles before it is processed.  The first kDepth tiles' loads go out before
-  // the q rotation, so their latency overlaps it.
+  // tiles before it is processed.
   const int lane_c = lane * 16, lane_m = blk * 16;
   const int ti0 = s_t0 + wave;
   const TileStreams st = tile_streams(a, bh);
   auto tile_t0 = [&](int ti) { return (tile_first + ti) << 6; };
-  // q: attention block 0 rotates and publishes it before its tile loads; the
+  // q: attention block 0 rotates and publishes it before its tile loads (a
+  // rotation measured faster shared than repeated in every block); the
   // others read the flag before theirs and take the published operands
   unsigned flag0 = 0;
   if (y == 0) {
@@ -1012,7 +1084,7 @@ void decode_mfma_kernel(DecodeArgs a) {
   }
   __builtin_amdgcn_sched_barrier(0);
   // The first loads are unconditional (a wave with fewer tiles re-reads its
-  // split's last tile), so the flag can be waited for on its own.
+  // split's last tile), so the flag read before them is waited for on its own.
   TileRegs r[kDepth];
 #pragma unroll
   for (int k = 0; k < kDepth; ++k) r[k] = load_tile(st, tile_t0(min(ti0 + k * WPB, s_t1 - 1)), lane_c, lane_m);
@@ -1035,7 +1107,7 @@ void decode_mfma_kernel(DecodeArgs a) {
     qsum = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(qr, (512 + j) * 4, 0, kDeviceScope));
     eq = (int)__builtin_amdgcn_raw_buffer_load_b32(qr, (516 + j) * 4, 0, kDeviceScope);
   } else {
-    if (y != 0) block_rotate_q(a, b, h, S);
+    if (y != 0) block_rotate_q_chunked(a, b, h, S);
 #pragma unroll
     for (int w = 0; w < 8; ++w)
 #pragma unroll
@@ -1227,7 +1299,7 @@ int decode_mfma_resident_blocks(int device) {
 
 hipError_t launch_decode_mfma(const DecodeArgs& a, int B, int waves_per_block, hipStream_t s) {
   (void)waves_per_block;   // the fused window blocks need 4 waves
-  dim3 grid((unsigned)(B * a.Hkv), (unsigned)(a.app_blocks + a.plan.splits + a.win.splits));
+  dim3 grid((unsigned)(B * a.Hkv), (unsigned)(a.app_blocks + a.plan.splits + a.win_blocks));
   hipLaunchKernelGGL(decode_mfma_kernel<4>, grid, dim3(256), 0, s, a);
   return hipGetLastError();
 }

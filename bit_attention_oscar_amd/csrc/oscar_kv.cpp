@@ -453,7 +453,10 @@ int launch_decode(oscar_kv* kv, int32_t layer, const void* q, void* out, int32_t
     const int hp_len = sink_end + (T - rec_begin);
     SegPlan w{};
     if (hp_len > 0) {
-      const int want_w = std::max(1, std::min(kMaxWinSplits, (hp_len + kTile - 1) / kTile));
+      // about 3 tiles (192 tokens) per window block: at the 32k shape two
+      // blocks per (sequence, kv head) beat one (too long) and five (each
+      // block's fixed costs repeated)
+      const int want_w = std::max(1, std::min(kMaxWinSplits, (hp_len + 3 * kTile - 1) / (3 * kTile)));
       w = make_plan(0, sink_end, rec_begin, T, want_w, 0);
     }
     SegPlan p{};
@@ -474,6 +477,7 @@ int launch_decode(oscar_kv* kv, int32_t layer, const void* q, void* out, int32_t
     da.win = w;
     // INT2 splits that fill the first wave of resident blocks go before the
     // window blocks (which then find q published instead of rotating it)
+    da.win_blocks = w.splits;
     da.int2_lead = std::max(0, std::min(p.splits, kv->resident / std::max(1, BH) - da.app_blocks));
     ca.nslots = p.splits + w.splits;
     da.comb = ca;
