@@ -74,6 +74,41 @@ def algorithmic_kv_bytes(B, Hkv, D, T, N, M, v_bf16):
     return B * Hkv * ((T - W) * (bk + bv) + W * 4 * D)
 
 
+KERNEL_SOURCES = ("bit_attention_oscar_amd/csrc/decode.hip", "bit_attention_oscar_amd/csrc/append_impl.h",
+                  "bit_attention_oscar_amd/csrc/common.h")
+
+
+def kernel_sources_sha256() -> str:
+    import hashlib
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def profiled_traffic(workload: str):
+    """HBM bytes per launch of the fused decode kernel from the committed
+    rocprofv3 counter summary of this workload (FETCH_SIZE and WRITE_SIZE,
+    each scaled by what the counter reads for the plain copy kernel), or None
+    when there is none or the kernel sources changed since it was taken."""
+    path = os.path.join(ROOT, "profiles", f"decode_mfma_{workload}.md")
+    if not os.path.exists(path):
+        return None
+    fields = {}
+    with open(path) as f:
+        for line in f:
+            if ":" in line and line.startswith("- "):
+                k, v = line[2:].split(":", 1)
+                fields[k.strip()] = v.strip().strip("`")
+    if fields.get("kernel sources sha256") != kernel_sources_sha256():
+        return None
+    try:
+        return int(fields["HBM bytes per launch"])
+    except (KeyError, ValueError):
+        return None
+
+
 def cpu_baseline(wl, budget_s=15.0):
     """The oracle, as it stands, on a bounded sample of the workload: one
     (layer, sequence) unit = append of one token + decode attention over the
@@ -258,7 +293,7 @@ def main():
         per_launch = kv_bytes_calls / k_n
         achieved = per_launch / (avg_ms / 1e3) / 1e9
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": profiled_traffic(args.workload),
                 "kernel": "decode_mfma_kernel", "avg_launch_us": round(avg_ms * 1e3, 3),
                 "algorithmic_bytes_per_launch": int(per_launch)}
     res = {
