@@ -159,6 +159,7 @@ struct DecodeArgs {
   int app_blocks;          // 2 when the launch also appends this step's token, else 0
   int int2_lead;           // INT2 splits dispatched before the window blocks
   int win_blocks;          // window blocks of the launch (win.splits)
+  int ring0;               // ring slot of the first recent token win.a1 (win.a1 % M)
   AppendArgs app;          // that append (n_new = 1); T above counts the new token
 };
 

@@ -515,8 +515,15 @@ __device__ inline int win_token(const SegPlan& w, int vt) {
   return vt < len0 ? w.a0 + vt : w.a1 + (vt - len0);
 }
 
-__device__ inline const uint16_t* win_row(const PlaneDev& P, int bh, int t, int N, int M, int D) {
-  return t < N ? P.sink + row_offset(bh, N, t, D) : P.ring + row_offset(bh, M, t % M, D);
+// Row of window token t: sink row t, or ring slot t % M.  The recent tokens
+// are consecutive from win.a1, whose slot (ring0) the host computes, so no
+// division is needed.
+__device__ inline const uint16_t* win_row(const DecodeArgs& a, const PlaneDev& P, int bh, int t) {
+  constexpr int D = 128;
+  if (t < a.N) return P.sink + row_offset(bh, a.N, t, D);
+  int slot = a.ring0 + (t - a.win.a1);
+  if (slot >= a.M) slot -= a.M;
+  return P.ring + row_offset(bh, a.M, slot, D);
 }
 
 __device__ inline void bf16x8(const uint4 u, float* x) {
@@ -780,28 +787,85 @@ __device__ void load_published_q(const DecodeArgs& a, int bh, FusedSmem& S) {
 // take the published copy (bounded wait) or rotate themselves.
 __device__ inline void window_q(const DecodeArgs& a, int b, int h, int bh, int y, FusedSmem& S) {
   if (y == 0) {
-    block_rotate_q(a, b, h, S);
+    block_rotate_q_chunked(a, b, h, S);
     publish_q(a, bh, S);
   } else if (wait_published_q(a, bh, first_flag_read(a, bh), S)) {
     load_published_q(a, bh, S);
   } else {
-    block_rotate_q(a, b, h, S);
+    block_rotate_q_chunked(a, b, h, S);
   }
 }
 
-// bf16 window tokens (sink + recent) of one (sequence, kv head): a block takes
-// up to win.chunk of them (64 per step) with fp32 VALU arithmetic.  When the
-// launch also appends a token, that token is the last window position; its
-// window value is computed here from the input with the append's own
-// arithmetic instead of being read back (the append role writes it in this
-// same launch).
-__device__ void window_block(const DecodeArgs& a, int bh, int b, int h, int wblk, FusedSmem& S) {
+// Window blocks.  When the launch also appends a token, that token is the
+// last window position; its window value is computed by the window block from
+// the input with the append's own arithmetic instead of being read back (the
+// append blocks write it in this same launch).
+//
+// Row loads of one 64-token pass of a window block: the K pieces a thread
+// scores (token tid/4, dims 32 (tid%4) .. +32) and the V pieces it
+// accumulates (tokens tid/16 + 16 i, dims 8 (tid%16) .. +8).  Rows of the
+// token appended in this launch are not loaded (the block computes them);
+// slots past the pass are zero.
+struct WinRows {
+  uint4 k[4];
+  uint4 v[4];
+};
+
+__device__ inline int window_len(const DecodeArgs& a) {
+  return (a.win.b0 - a.win.a0) + (a.win.b1 - a.win.a1);
+}
+
+// the token appended by this launch when window block wblk holds it, else -1
+__device__ inline int window_new_token(const DecodeArgs& a, int wblk) {
+  const int len = window_len(a);
+  return (a.app_blocks > 0 && min(len, (wblk + 1) * a.win.chunk) == len) ? a.T - 1 : -1;
+}
+
+__device__ inline WinRows window_rows(const DecodeArgs& a, int bh, int vt0, int v_hi, int t_new) {
+  constexpr int D = 128;
+  const int tid = threadIdx.x, n = min(64, v_hi - vt0);
+  WinRows r;
+  const int tok = tid >> 2, part = tid & 3;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) r.k[i] = make_uint4(0, 0, 0, 0);
+  if (tok < n) {
+    const int t = win_token(a.win, vt0 + tok);
+    if (t != t_new) {
+      const uint4* rp = reinterpret_cast<const uint4*>(win_row(a, a.k, bh, t) + 32 * part);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) r.k[i] = rp[i];
+    }
+  }
+  const int g = tid >> 4, c = tid & 15;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int tk = g + 16 * i;
+    r.v[i] = make_uint4(0, 0, 0, 0);
+    if (tk < n) {
+      const int t = win_token(a.win, vt0 + tk);
+      if (t != t_new) r.v[i] = *reinterpret_cast<const uint4*>(win_row(a, a.v, bh, t) + 8 * c);
+    }
+  }
+  return r;
+}
+
+// The block's first pass of rows, issued before it waits for q.
+__device__ inline WinRows window_first_rows(const DecodeArgs& a, int bh, int wblk) {
+  const int v_lo = wblk * a.win.chunk;
+  return window_rows(a, bh, v_lo, min(window_len(a), v_lo + a.win.chunk), window_new_token(a, wblk));
+}
+
+// bf16 window tokens (sink + recent) of one (sequence, kv head), up to
+// win.chunk of them in 64-token passes with fp32 VALU arithmetic.  first: the
+// first pass's rows, already issued (later passes load theirs at their start).
+__device__ void window_block(const DecodeArgs& a, int bh, int b, int h, int wblk, FusedSmem& S,
+                             const WinRows& first) {
   constexpr int D = 128;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const int len = (a.win.b0 - a.win.a0) + (a.win.b1 - a.win.a1);
+  const int len = window_len(a);
   const int v_lo = wblk * a.win.chunk;
   const int v_hi = min(len, v_lo + a.win.chunk);
-  const int t_new = (a.app_blocks > 0 && v_hi == len) ? a.T - 1 : -1;
+  const int t_new = window_new_token(a, wblk);
   if (t_new >= 0) {
     for (int which = 0; which < 2; ++which) {
       const uint16_t* in = which ? a.app.vin : a.app.kin;
@@ -832,19 +896,17 @@ __device__ void window_block(const DecodeArgs& a, int bh, int b, int h, int wblk
 #pragma unroll
     for (int k = 0; k < 8; ++k) o[j][k] = 0.0f;
   __syncthreads();
+  WinRows cur = first;
   for (int vt0 = v_lo; vt0 < v_hi; vt0 += 64) {
     const int n = min(64, v_hi - vt0);
+    if (vt0 != v_lo) cur = window_rows(a, bh, vt0, v_hi, t_new);
     {  // scores: 4 lanes per token, 32 dims each
       const int tok = tid >> 2, part = tid & 3;
       float dots[4] = {0.0f, 0.0f, 0.0f, 0.0f};
       if (tok < n) {
-        const int t = win_token(a.win, vt0 + tok);
-        uint4 us[4];
-        if (t == t_new) {
+        uint4 us[4] = {cur.k[0], cur.k[1], cur.k[2], cur.k[3]};
+        if (win_token(a.win, vt0 + tok) == t_new) {
           const uint4* rp = reinterpret_cast<const uint4*>(&S.newtok[0][32 * part]);
-          us[0] = rp[0]; us[1] = rp[1]; us[2] = rp[2]; us[3] = rp[3];
-        } else {
-          const uint4* rp = reinterpret_cast<const uint4*>(win_row(a.k, bh, t, a.N, a.M, D) + 32 * part);
           us[0] = rp[0]; us[1] = rp[1]; us[2] = rp[2]; us[3] = rp[3];
         }
 #pragma unroll
@@ -883,19 +945,6 @@ __device__ void window_block(const DecodeArgs& a, int bh, int b, int h, int wblk
     }
     __syncthreads();
     {  // PV: thread (g, c) over tokens g, g+16, g+32, g+48 of the tile
-      uint4 u[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int tok = g + 16 * i;
-        u[i] = make_uint4(0, 0, 0, 0);
-        if (tok < n) {
-          const int t = win_token(a.win, vt0 + tok);
-          if (t == t_new)
-            u[i] = *reinterpret_cast<const uint4*>(&S.newtok[1][8 * c]);
-          else
-            u[i] = *reinterpret_cast<const uint4*>(win_row(a.v, bh, t, a.N, a.M, D) + 8 * c);
-        }
-      }
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const float al = wa[j];
@@ -906,8 +955,10 @@ __device__ void window_block(const DecodeArgs& a, int bh, int b, int h, int wblk
       for (int i = 0; i < 4; ++i) {
         const int tok = g + 16 * i;
         if (tok < n) {
+          uint4 u = cur.v[i];
+          if (win_token(a.win, vt0 + tok) == t_new) u = *reinterpret_cast<const uint4*>(&S.newtok[1][8 * c]);
           float x[8];
-          bf16x8(u[i], x);
+          bf16x8(u, x);
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
             const float p = sc[j * 64 + tok];
@@ -1050,8 +1101,9 @@ void decode_mfma_kernel(DecodeArgs a) {
   // start once slots free up, by when block 0 has published q.
   const int lead = a.int2_lead;
   if (y >= lead && y < lead + a.win_blocks) {
+    const WinRows rows = window_first_rows(a, bh, y - lead);   // in flight during the q wait
     window_q(a, b, h, bh, y, S);
-    window_block(a, bh, b, h, y - lead, S);
+    window_block(a, bh, b, h, y - lead, S, rows);
     finish_block(a, bh, S);
     return;
   }

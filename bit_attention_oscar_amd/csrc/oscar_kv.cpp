@@ -263,6 +263,14 @@ int do_append(oscar_kv* kv, int32_t layer, const void* k, const void* v, int32_t
 // unit in total (measured at 32k context, B = 16, Hkv = 8: 8-12 splits beat 4,
 // 6 and 16; fewer blocks leave compute units idle in the tail, more blocks
 // repeat each block's fixed start-up and merge work).
+// Window tokens per window block (a multiple of 64).  At the 32k shape (320
+// window tokens) 192 and 256 measured best: 66 and 65 us per launch against
+// 70 us with 64 and 74 us with all 320 in one block.
+#ifndef OSCAR_WIN_TOKENS
+#define OSCAR_WIN_TOKENS 192
+#endif
+constexpr int kWinTokens = OSCAR_WIN_TOKENS;
+
 int auto_int2_splits(int BH, int ntiles, int waves) {
   const int target_blocks = 1536 * 4 / std::max(1, waves);
   int s = std::max(1, target_blocks / std::max(1, BH));
@@ -453,10 +461,7 @@ int launch_decode(oscar_kv* kv, int32_t layer, const void* q, void* out, int32_t
     const int hp_len = sink_end + (T - rec_begin);
     SegPlan w{};
     if (hp_len > 0) {
-      // about 3 tiles (192 tokens) per window block: at the 32k shape two
-      // blocks per (sequence, kv head) beat one (too long) and five (each
-      // block's fixed costs repeated)
-      const int want_w = std::max(1, std::min(kMaxWinSplits, (hp_len + 3 * kTile - 1) / (3 * kTile)));
+      const int want_w = std::max(1, std::min(kMaxWinSplits, (hp_len + kWinTokens - 1) / kWinTokens));
       w = make_plan(0, sink_end, rec_begin, T, want_w, 0);
     }
     SegPlan p{};
@@ -478,6 +483,7 @@ int launch_decode(oscar_kv* kv, int32_t layer, const void* q, void* out, int32_t
     // INT2 splits that fill the first wave of resident blocks go before the
     // window blocks (which then find q published instead of rotating it)
     da.win_blocks = w.splits;
+    da.ring0 = M > 0 ? w.a1 % M : 0;
     da.int2_lead = std::max(0, std::min(p.splits, kv->resident / std::max(1, BH) - da.app_blocks));
     ca.nslots = p.splits + w.splits;
     da.comb = ca;
