@@ -1124,30 +1124,40 @@ void decode_mfma_kernel(DecodeArgs a) {
   const int ti0 = s_t0 + wave;
   const TileStreams st = tile_streams(a, bh);
   auto tile_t0 = [&](int ti) { return (tile_first + ti) << 6; };
-  // q: attention block 0 rotates and publishes it before its tile loads (a
-  // rotation measured faster shared than repeated in every block); the
-  // others read the flag before theirs and take the published operands
+  // q: attention block 0 rotates and publishes it (its loads issued before
+  // its first tile's); the others read the flag before their tile loads and
+  // take the published operands.  Measured: every block rotating costs more
+  // than sharing; first-wave blocks rotating gave the same time as this.
+  const bool self_rotate = y == 0;
+  // The first loads are unconditional (a wave with fewer tiles re-reads its
+  // split's last tile), so what was issued before them is waited for on its
+  // own.  A rotating block issues one tile before rotating (its R rows hold
+  // the registers of the other) and the rest after.
   unsigned flag0 = 0;
-  if (y == 0) {
-    block_rotate_q(a, b, h, S);
-    publish_q(a, bh, S);
+  TileRegs r[kDepth];
+  if (self_rotate) {
+    const QRotLoads qload = q_rotation_loads(a, b, h);
+    __builtin_amdgcn_sched_barrier(0);
+    r[0] = load_tile(st, tile_t0(min(ti0, s_t1 - 1)), lane_c, lane_m);
+    __builtin_amdgcn_sched_barrier(0);
+    q_rotation_finish(a, qload, S);
+    if (y == 0) publish_q(a, bh, S);
+#pragma unroll
+    for (int k = 1; k < kDepth; ++k) r[k] = load_tile(st, tile_t0(min(ti0 + k * WPB, s_t1 - 1)), lane_c, lane_m);
   } else {
     flag0 = first_flag_read(a, bh);
-  }
-  __builtin_amdgcn_sched_barrier(0);
-  // The first loads are unconditional (a wave with fewer tiles re-reads its
-  // split's last tile), so the flag read before them is waited for on its own.
-  TileRegs r[kDepth];
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-  for (int k = 0; k < kDepth; ++k) r[k] = load_tile(st, tile_t0(min(ti0 + k * WPB, s_t1 - 1)), lane_c, lane_m);
-  __builtin_amdgcn_sched_barrier(0);
+    for (int k = 0; k < kDepth; ++k) r[k] = load_tile(st, tile_t0(min(ti0 + k * WPB, s_t1 - 1)), lane_c, lane_m);
+    __builtin_amdgcn_sched_barrier(0);
+  }
 
   // q operands: 8 words x 4 fp16 of head j; lane group pp holds the k-slots
   // of qk_dim(w, pp, k), each scaled by 2^eq 4^-(d % 4)
   h4 qv[8];
   int eq;
   float qsum;
-  if (y != 0 && wait_published_q(a, bh, flag0, S)) {
+  if (!self_rotate && wait_published_q(a, bh, flag0, S)) {
     const __amdgpu_buffer_rsrc_t qr = plane_rsrc(a.qpub + (size_t)bh * kQPub, kQPub * 4);
     const int vbase = (kQPubOps + 16 * (4 * (lane >> 4) + j)) * 4;
 #pragma unroll
@@ -1159,7 +1169,7 @@ void decode_mfma_kernel(DecodeArgs a) {
     qsum = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(qr, (512 + j) * 4, 0, kDeviceScope));
     eq = (int)__builtin_amdgcn_raw_buffer_load_b32(qr, (516 + j) * 4, 0, kDeviceScope);
   } else {
-    if (y != 0) block_rotate_q_chunked(a, b, h, S);
+    if (!self_rotate) block_rotate_q_chunked(a, b, h, S);
 #pragma unroll
     for (int w = 0; w < 8; ++w)
 #pragma unroll
