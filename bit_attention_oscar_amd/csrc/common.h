@@ -158,6 +158,7 @@ struct DecodeArgs {
   float scale_log2;        // softmax scale * log2(e)
   int app_blocks;          // 2 when the launch also appends this step's token, else 0
   int int2_lead;           // INT2 splits dispatched before the window blocks
+  float split_ramp;        // INT2 split sizes fall linearly by this fraction from first to last
   int win_blocks;          // window blocks of the launch (win.splits)
   int ring0;               // ring slot of the first recent token win.a1 (win.a1 % M)
   AppendArgs app;          // that append (n_new = 1); T above counts the new token

@@ -688,14 +688,16 @@ __device__ void publish_q(const DecodeArgs& a, int bh, FusedSmem& S) {
 // Merge of the (m, l, o') partials of one (sequence, kv head) by the last
 // block of the matrix-core launch, then o = o' @ R_V^T (4 query heads per kv
 // head, head_dim 128).  Wave j merges head j: lane l owns dims l and l + 64
-// and loads 16 slots at a time (their m and l, the same words in every lane,
+// and loads 8 slots at a time (their m and l, the same words in every lane,
 // and its two o' values) in one round trip, merging into a running maximum.
 // The rotation splits its reduction over e across the four waves and adds the
-// partial sums in a fixed order.
+// partial sums in a fixed order; its R_V^T rows are loaded first, in flight
+// with the partials.
 __device__ void combine_fused(const CombineArgs& a, int bh, FusedSmem& S) {
-  constexpr int D = 128, SB = 16;
+  constexpr int D = 128, SB = 8;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int b = bh / a.Hkv, kvh = bh - (bh / a.Hkv) * a.Hkv;
+  const RRows<D, 4> rr = load_r_rows<D, 4>(a.rvT);
   const float* P = a.partials + ((size_t)b * a.Hq + kvh * 4 + wave) * kMaxSplits * (D + 2);
   float M = NEG_INF, L = 0.0f, o0 = 0.0f, o1 = 0.0f;
   for (int s0 = 0; s0 < a.nslots; s0 += SB) {
@@ -732,7 +734,7 @@ __device__ void combine_fused(const CombineArgs& a, int bh, FusedSmem& S) {
   os[wave * D + lane] = o0 * inv;
   os[wave * D + lane + 64] = o1 * inv;
   __syncthreads();
-  rotate_rows<D, 4, 4>(os, a.rvT, part, 4);
+  rotate_rows_regs<D, 4, 4>(os, rr, part);
   __syncthreads();
   for (int idx = tid; idx < 4 * D; idx += 256) {
     const int j = idx >> 7, d = idx & 127;
@@ -1114,9 +1116,19 @@ void decode_mfma_kernel(DecodeArgs a) {
   const int lo = a.plan.a0, hi = a.plan.b0;       // INT2 token range
   const int tile_first = lo >> 6;
   const int ntiles = ((hi - 1) >> 6) - tile_first + 1;
-  const int tps = a.plan.chunk >> 6;
-  const int s_t0 = split * tps;
-  const int s_t1 = min(s_t0 + tps, ntiles);
+  // Split s covers tiles [start(s), start(s + 1)): shares of the range whose
+  // weights fall linearly by a.split_ramp from the first split to the last
+  // (blocks dispatched later start later and get less)
+  auto split_start = [&](int s) -> int {
+    const int S = a.plan.splits;
+    if (s >= S) return ntiles;
+    const float fs = (float)s, al = a.split_ramp;
+    const float F = (fs * (1.0f + al) - al * fs * (fs - 1.0f) / (float)max(S - 1, 1)) / (float)S;
+    return min(ntiles, (int)(F * (float)ntiles));
+  };
+  const int s_t0 = split_start(split);
+  const int s_t1 = split_start(split + 1);
+  const int t_last = max(s_t1 - 1, 0);            // a valid tile for clamped loads
 
   // kDepth register sets in turn: the loads of a tile are issued kDepth - 1
   // tiles before it is processed.
@@ -1138,17 +1150,17 @@ void decode_mfma_kernel(DecodeArgs a) {
   if (self_rotate) {
     const QRotLoads qload = q_rotation_loads(a, b, h);
     __builtin_amdgcn_sched_barrier(0);
-    r[0] = load_tile(st, tile_t0(min(ti0, s_t1 - 1)), lane_c, lane_m);
+    r[0] = load_tile(st, tile_t0(min(ti0, t_last)), lane_c, lane_m);
     __builtin_amdgcn_sched_barrier(0);
     q_rotation_finish(a, qload, S);
     if (y == 0) publish_q(a, bh, S);
 #pragma unroll
-    for (int k = 1; k < kDepth; ++k) r[k] = load_tile(st, tile_t0(min(ti0 + k * WPB, s_t1 - 1)), lane_c, lane_m);
+    for (int k = 1; k < kDepth; ++k) r[k] = load_tile(st, tile_t0(min(ti0 + k * WPB, t_last)), lane_c, lane_m);
   } else {
     flag0 = first_flag_read(a, bh);
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int k = 0; k < kDepth; ++k) r[k] = load_tile(st, tile_t0(min(ti0 + k * WPB, s_t1 - 1)), lane_c, lane_m);
+    for (int k = 0; k < kDepth; ++k) r[k] = load_tile(st, tile_t0(min(ti0 + k * WPB, t_last)), lane_c, lane_m);
     __builtin_amdgcn_sched_barrier(0);
   }
 

@@ -271,6 +271,14 @@ int do_append(oscar_kv* kv, int32_t layer, const void* k, const void* v, int32_t
 #endif
 constexpr int kWinTokens = OSCAR_WIN_TOKENS;
 
+// Linear fall of INT2 split sizes from the first split to the last: blocks
+// dispatched later start later, so they get less.  At the 32k shape 0.4
+// measured best (65.1 us per launch; 66.5 with equal splits, 65.9 with 0.6).
+#ifndef OSCAR_SPLIT_RAMP
+#define OSCAR_SPLIT_RAMP 0.4f
+#endif
+constexpr float kSplitRamp = OSCAR_SPLIT_RAMP;
+
 int auto_int2_splits(int BH, int ntiles, int waves) {
   const int target_blocks = 1536 * 4 / std::max(1, waves);
   int s = std::max(1, target_blocks / std::max(1, BH));
@@ -485,6 +493,7 @@ int launch_decode(oscar_kv* kv, int32_t layer, const void* q, void* out, int32_t
     da.win_blocks = w.splits;
     da.ring0 = M > 0 ? w.a1 % M : 0;
     da.int2_lead = std::max(0, std::min(p.splits, kv->resident / std::max(1, BH) - da.app_blocks));
+    da.split_ramp = p.splits > 1 ? kSplitRamp : 0.0f;
     ca.nslots = p.splits + w.splits;
     da.comb = ca;
     if (++kv->epoch == 0) kv->epoch = 1;   // a flag never holds a future launch's number
