@@ -10,7 +10,7 @@ namespace oscar {
 constexpr int kGroup = 128;           // quantization group along head_dim
 constexpr int kTile = 64;             // tokens per decode tile / V storage block
 constexpr int kMaxSplits = 256;       // partial-result slots per (sequence, head)
-constexpr int kQPub = 4 * 128 + 8 + 256;  // published q of one (sequence, kv head): fp32 q, sums, exponents, fp16 operands
+constexpr int kQPub = 4 * 128 + 8 + 256;  // published q of 4 query heads: fp32 q, sums, exponents, fp16 operands
 constexpr int kMaxGq = 16;            // query heads per kv head handled by the VALU kernel
 
 // ---------------------------------------------------------------------------
@@ -140,13 +140,14 @@ struct CombineArgs {
 struct DecodeArgs {
   PlaneDev k, v;
   const float* qrot;       // rotated q of the general kernel
-  float* qpub;             // [B*Hkv][kQPub]: rotated q published by the first attention
-                           // block of each (sequence, kv head) in a matrix-core launch
+  float* qpub;             // [B*Hkv*G][kQPub]: rotated q of each head group, published by the
+                           // first attention block of each (sequence, kv head) in a matrix-core launch
   unsigned* qflag;         // [B*Hkv]: epoch of the launch whose q qpub holds
   unsigned epoch;          // this launch's number (never 0)
   unsigned qwait_ticks;    // longest wait for the published q, in wall-clock ticks
   float* partials;         // [B][Hq][kMaxSplits][D+2]
   int Hq, Hkv, D, cap, N, M, T;
+  int Gq, G;               // query heads per kv head; head groups of 4 (matrix-core kernel)
   SegPlan plan;            // INT2 range (matrix-core kernel) or all tokens (VALU kernel)
   SegPlan win;             // bf16 window segments handled by extra blocks of the
                            // matrix-core launch (win.splits blocks of <= 64 tokens)
@@ -171,7 +172,7 @@ hipError_t launch_quantize_rows(const float* x, int rows, int D, float clip, uin
 hipError_t launch_qrot(const QRotArgs& a, hipStream_t s);
 hipError_t launch_decode_valu(const DecodeArgs& a, int B, hipStream_t s);
 hipError_t launch_decode_mfma(const DecodeArgs& a, int B, int waves_per_block, hipStream_t s);
-int decode_mfma_resident_blocks(int device);   // blocks of the matrix-core kernel resident at once
+int decode_mfma_resident_blocks(int device, int G);   // blocks of the matrix-core kernel resident at once
 hipError_t launch_combine(const CombineArgs& a, hipStream_t s);
 hipError_t launch_stream_copy(const void* src, void* dst, size_t bytes, hipStream_t s);
 hipError_t launch_export_codes(const uint8_t* stored, uint8_t* canon, int BH, int cap, int T, int D, int isv,

@@ -42,14 +42,15 @@ typedef float f4 __attribute__((ext_vector_type(4)));
 #ifndef OSCAR_MFMA_WAVES_PER_EU
 #define OSCAR_MFMA_WAVES_PER_EU 4
 #endif
+// Two head groups per wave hold twice the q operands and accumulators: 3 waves
+// per SIMD leave them room without spills.
+#ifndef OSCAR_MFMA_WAVES_PER_EU_G2
+#define OSCAR_MFMA_WAVES_PER_EU_G2 3
+#endif
 // Register sets of tile data per wave: the loads of a tile are issued
 // kDepth - 1 tiles ahead of its processing.
 #ifndef OSCAR_TILE_DEPTH
 #define OSCAR_TILE_DEPTH 2
-#endif
-// QK^T accumulation in two interleaved chains instead of one
-#ifndef OSCAR_QK_TWO_CHAINS
-#define OSCAR_QK_TWO_CHAINS 0
 #endif
 constexpr int kDepth = OSCAR_TILE_DEPTH;
 
@@ -330,26 +331,38 @@ __device__ inline void split_codes(uint32_t w, uint32_t c[8]) {
 __device__ inline float lo_half(uint32_t m) { return (float)__builtin_bit_cast(_Float16, (uint16_t)(m & 0xFFFFu)); }
 __device__ inline float hi_half(uint32_t m) { return (float)__builtin_bit_cast(_Float16, (uint16_t)(m >> 16)); }
 
-template <int W>
-__device__ inline void qk_word(uint32_t word, h4 q, f4& sa, f4& sb) {
+// Word w of a lane's K codes against the q operands of every head group: the
+// codes are unpacked once, each group has its own accumulation chain.
+template <int G>
+__device__ inline void qk_word(uint32_t word, const h4 (&q)[G][8], int w, f4 (&s)[G]) {
   uint32_t c[8];
   split_codes(word, c);
-  sa = __builtin_amdgcn_mfma_f32_4x4x4f16(as_h4(c[0], c[1]), q, sa, 0, 0, 4);
-  sb = __builtin_amdgcn_mfma_f32_4x4x4f16(as_h4(c[2], c[3]), q, sb, 0, 0, 5);
-  sa = __builtin_amdgcn_mfma_f32_4x4x4f16(as_h4(c[4], c[5]), q, sa, 0, 0, 6);
-  sb = __builtin_amdgcn_mfma_f32_4x4x4f16(as_h4(c[6], c[7]), q, sb, 0, 0, 7);
+#pragma unroll
+  for (int g = 0; g < G; ++g) s[g] = __builtin_amdgcn_mfma_f32_4x4x4f16(as_h4(c[0], c[1]), q[g][w], s[g], 0, 0, 4);
+#pragma unroll
+  for (int g = 0; g < G; ++g) s[g] = __builtin_amdgcn_mfma_f32_4x4x4f16(as_h4(c[2], c[3]), q[g][w], s[g], 0, 0, 5);
+#pragma unroll
+  for (int g = 0; g < G; ++g) s[g] = __builtin_amdgcn_mfma_f32_4x4x4f16(as_h4(c[4], c[5]), q[g][w], s[g], 0, 0, 6);
+#pragma unroll
+  for (int g = 0; g < G; ++g) s[g] = __builtin_amdgcn_mfma_f32_4x4x4f16(as_h4(c[6], c[7]), q[g][w], s[g], 0, 0, 7);
 }
 
-template <int W>
-__device__ inline void pv_word(uint32_t word, h4 p, f4& o0, f4& o1) {
+template <int G, int W>
+__device__ inline void pv_word(uint32_t word, const h4 (&p)[G], f4 (&o0)[G], f4 (&o1)[G]) {
   uint32_t c[8];
   split_codes(word, c);
   // word W holds tokens 8W..8W+7 = blocks beta 2W (pairs 0,1) and 2W+1 (pairs 2,3);
   // positions 0-3 are the low half of head_dim, 4-7 the high half
-  o0 = __builtin_amdgcn_mfma_f32_4x4x4f16(p, as_h4(c[0], c[1]), o0, 4, 2 * W, 0);
-  o1 = __builtin_amdgcn_mfma_f32_4x4x4f16(p, as_h4(c[4], c[5]), o1, 4, 2 * W, 0);
-  o0 = __builtin_amdgcn_mfma_f32_4x4x4f16(p, as_h4(c[2], c[3]), o0, 4, 2 * W + 1, 0);
-  o1 = __builtin_amdgcn_mfma_f32_4x4x4f16(p, as_h4(c[6], c[7]), o1, 4, 2 * W + 1, 0);
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    o0[g] = __builtin_amdgcn_mfma_f32_4x4x4f16(p[g], as_h4(c[0], c[1]), o0[g], 4, 2 * W, 0);
+    o1[g] = __builtin_amdgcn_mfma_f32_4x4x4f16(p[g], as_h4(c[4], c[5]), o1[g], 4, 2 * W, 0);
+  }
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    o0[g] = __builtin_amdgcn_mfma_f32_4x4x4f16(p[g], as_h4(c[2], c[3]), o0[g], 4, 2 * W + 1, 0);
+    o1[g] = __builtin_amdgcn_mfma_f32_4x4x4f16(p[g], as_h4(c[6], c[7]), o1[g], 4, 2 * W + 1, 0);
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -490,8 +503,13 @@ __device__ inline void st_partial(float* p, float v) {
 // partials with device-scope loads.  No cache-wide write-back or invalidation,
 // and no block ever waits for another.
 struct FusedSmem;
+template <int D, int WAVES>
+struct RRows;
+template <int G>
 __device__ void combine_fused(const CombineArgs& a, int bh, FusedSmem& S);
+__device__ __forceinline__ void combine_group4(const CombineArgs& a, int b, int hq0, const RRows<128, 4>& rr, FusedSmem& S);
 
+template <int G>
 __device__ inline void finish_block(const DecodeArgs& a, int bh, FusedSmem& S) {
   __shared__ int is_last;
   __builtin_amdgcn_s_waitcnt(0);
@@ -503,7 +521,7 @@ __device__ inline void finish_block(const DecodeArgs& a, int bh, FusedSmem& S) {
   }
   __syncthreads();
   if (!is_last) return;
-  combine_fused(a.comb, bh, S);
+  combine_fused<G>(a.comb, bh, S);
   if (threadIdx.x == 0) a.counters[bh] = 0u;
 }
 
@@ -557,11 +575,11 @@ struct QRotLoads {
   float r[32][2];
 };
 
-__device__ inline QRotLoads q_rotation_loads(const DecodeArgs& a, int b, int h) {
+__device__ inline QRotLoads q_rotation_loads(const DecodeArgs& a, int b, int hq0) {
   constexpr int D = 128;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   QRotLoads s;
-  const uint16_t* qb = a.q + ((size_t)b * a.Hq + h * 4) * D;     // the 4 heads' rows, contiguous
+  const uint16_t* qb = a.q + ((size_t)b * a.Hq + hq0) * D;       // the group's 4 heads' rows, contiguous
   s.q0 = bf16_to_f32(qb[tid]);
   s.q1 = bf16_to_f32(qb[tid + 256]);
   const float* Rw = a.rk + (size_t)(wave * 32) * D + lane;
@@ -616,18 +634,18 @@ __device__ void q_rotation_finish(const DecodeArgs& a, const QRotLoads& s, Fused
   __syncthreads();
 }
 
-__device__ inline void block_rotate_q(const DecodeArgs& a, int b, int h, FusedSmem& S) {
-  q_rotation_finish(a, q_rotation_loads(a, b, h), S);
+__device__ inline void block_rotate_q(const DecodeArgs& a, int b, int hq0, FusedSmem& S) {
+  q_rotation_finish(a, q_rotation_loads(a, b, hq0), S);
 }
 
 // The same rotation with R_K read in chunks (few registers): for a block
 // whose tile registers are already live.  Identical arithmetic and bits.
-__device__ void block_rotate_q_chunked(const DecodeArgs& a, int b, int h, FusedSmem& S) {
+__device__ void block_rotate_q_chunked(const DecodeArgs& a, int b, int hq0, FusedSmem& S) {
   constexpr int D = 128;
   const int tid = threadIdx.x;
   float* qraw = S.scratch;            // [4][128]
   float* part = S.scratch + 512;      // [4 waves][4][128]
-  for (int i = tid; i < 4 * D; i += 256) qraw[i] = bf16_to_f32(a.q[((size_t)b * a.Hq + h * 4) * D + i]);
+  for (int i = tid; i < 4 * D; i += 256) qraw[i] = bf16_to_f32(a.q[((size_t)b * a.Hq + hq0) * D + i]);
   __syncthreads();
   rotate_rows<128, 4, 4>(qraw, a.rk, part, 4);
   __syncthreads();
@@ -654,7 +672,8 @@ __device__ inline _Float16 q_operand(const FusedSmem& S, int j, int pp, int w, i
   return (_Float16)ldexpf(S.qs[j][d], S.qeq[j] - 2 * (d & 3));
 }
 
-// Published q of one (sequence, kv head), kQPub floats:
+// Published q of one head group (4 query heads) of a (sequence, kv head), at
+// index (b Hkv + h) G + g, kQPub floats:
 //   [0, 512)          fp32 rotated q of the 4 heads, head-major
 //   [512, 516)        per-head sums; [516, 520) per-head exponents eq (int bits)
 //   [kQPubOps, +256)  fp16 matrix-core operands: vector 4 pp + j holds the 32
@@ -663,10 +682,11 @@ constexpr int kQPubOps = 520;
 static_assert(kQPubOps + 256 <= kQPub, "published q layout");
 
 // The first attention block of each (sequence, kv head) rotates q and
-// publishes it for the other blocks of the launch: device-scope stores, a
-// wait until they have completed, then this launch's epoch in the flag.
-__device__ void publish_q(const DecodeArgs& a, int bh, FusedSmem& S) {
-  float* dst = a.qpub + (size_t)bh * kQPub;
+// publishes it for the other blocks of the launch: device-scope stores of
+// every head group (publish_q), a wait until they have completed, then this
+// launch's epoch in the flag (publish_flag).
+__device__ void publish_q(const DecodeArgs& a, int pidx, FusedSmem& S) {
+  float* dst = a.qpub + (size_t)pidx * kQPub;
   const int tid = threadIdx.x;
   for (int i = tid; i < 4 * 128; i += blockDim.x) st_partial(dst + i, S.qs[i >> 7][i & 127]);
   if (tid < 4) {
@@ -680,9 +700,21 @@ __device__ void publish_q(const DecodeArgs& a, int bh, FusedSmem& S) {
     const uint32_t hi = __builtin_bit_cast(uint16_t, q_operand(S, j, pp, (e + 1) >> 2, (e + 1) & 3));
     st_partial(dst + kQPubOps + tid, __uint_as_float(lo | (hi << 16)));
   }
+}
+
+__device__ void publish_flag(const DecodeArgs& a, int bh) {
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
-  if (tid == 0) __hip_atomic_store(a.qflag + bh, a.epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (threadIdx.x == 0) __hip_atomic_store(a.qflag + bh, a.epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Rotation (R_K read in chunks) and publication of every head group of (b, h).
+__device__ void rotate_and_publish(const DecodeArgs& a, int b, int h, int bh, FusedSmem& S) {
+  for (int g = 0; g < a.G; ++g) {
+    block_rotate_q_chunked(a, b, h * a.Gq + 4 * g, S);
+    publish_q(a, bh * a.G + g, S);
+  }
+  publish_flag(a, bh);
 }
 
 // Merge of the (m, l, o') partials of one (sequence, kv head) by the last
@@ -693,12 +725,20 @@ __device__ void publish_q(const DecodeArgs& a, int bh, FusedSmem& S) {
 // The rotation splits its reduction over e across the four waves and adds the
 // partial sums in a fixed order; its R_V^T rows are loaded first, in flight
 // with the partials.
+template <int G>
 __device__ void combine_fused(const CombineArgs& a, int bh, FusedSmem& S) {
-  constexpr int D = 128, SB = 8;
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  constexpr int D = 128;
   const int b = bh / a.Hkv, kvh = bh - (bh / a.Hkv) * a.Hkv;
   const RRows<D, 4> rr = load_r_rows<D, 4>(a.rvT);
-  const float* P = a.partials + ((size_t)b * a.Hq + kvh * 4 + wave) * kMaxSplits * (D + 2);
+#pragma unroll
+  for (int g = 0; g < G; ++g) combine_group4(a, b, kvh * 4 * G + 4 * g, rr, S);
+}
+
+// Merge and un-rotation of query heads hq0 .. hq0 + 3.
+__device__ __forceinline__ void combine_group4(const CombineArgs& a, int b, int hq0, const RRows<128, 4>& rr, FusedSmem& S) {
+  constexpr int D = 128, SB = 8;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const float* P = a.partials + ((size_t)b * a.Hq + hq0 + wave) * kMaxSplits * (D + 2);
   float M = NEG_INF, L = 0.0f, o0 = 0.0f, o1 = 0.0f;
   for (int s0 = 0; s0 < a.nslots; s0 += SB) {
     float ms[SB], ls[SB], x0[SB], x1[SB];
@@ -739,7 +779,7 @@ __device__ void combine_fused(const CombineArgs& a, int bh, FusedSmem& S) {
   for (int idx = tid; idx < 4 * D; idx += 256) {
     const int j = idx >> 7, d = idx & 127;
     const float v = rot_sum<D, 4, 4>(part, j, d);
-    const size_t o = ((size_t)b * a.Hq + kvh * 4 + j) * D + d;
+    const size_t o = ((size_t)b * a.Hq + hq0 + j) * D + d;
     if (a.out_dtype == 0)
       reinterpret_cast<float*>(a.out)[o] = v;
     else if (a.out_dtype == 1)
@@ -747,6 +787,7 @@ __device__ void combine_fused(const CombineArgs& a, int bh, FusedSmem& S) {
     else
       reinterpret_cast<uint16_t*>(a.out)[o] = __builtin_bit_cast(uint16_t, (_Float16)v);
   }
+  __syncthreads();                        // os / part are rewritten by the next group
 }
 
 // Thread 0's first read of the flag, issued before a block's tile loads so
@@ -774,9 +815,9 @@ __device__ bool wait_published_q(const DecodeArgs& a, int bh, unsigned first, Fu
   return S.ready != 0;
 }
 
-// fp32 published q into shared memory (window blocks).
-__device__ void load_published_q(const DecodeArgs& a, int bh, FusedSmem& S) {
-  const float* src = a.qpub + (size_t)bh * kQPub;
+// fp32 published q of one head group into shared memory (window blocks).
+__device__ void load_published_q(const DecodeArgs& a, int pidx, FusedSmem& S) {
+  const float* src = a.qpub + (size_t)pidx * kQPub;
   for (int i = threadIdx.x; i < 4 * 128; i += blockDim.x) S.qs[i >> 7][i & 127] = ld_partial<true>(src + i);
   if (threadIdx.x < 4) {
     S.qsum[threadIdx.x] = ld_partial<true>(src + 512 + threadIdx.x);
@@ -785,17 +826,24 @@ __device__ void load_published_q(const DecodeArgs& a, int bh, FusedSmem& S) {
   __syncthreads();
 }
 
-// q of a window block: attention block 0 rotates and publishes, the others
-// take the published copy (bounded wait) or rotate themselves.
-__device__ inline void window_q(const DecodeArgs& a, int b, int h, int bh, int y, FusedSmem& S) {
+// q of a window block: attention block 0 rotates and publishes every head
+// group; the others take the published copy (bounded wait), or rotate q
+// themselves.  Returns whether the published copy is there.
+__device__ inline bool window_q_ready(const DecodeArgs& a, int b, int h, int bh, int y, FusedSmem& S) {
   if (y == 0) {
-    block_rotate_q_chunked(a, b, h, S);
-    publish_q(a, bh, S);
-  } else if (wait_published_q(a, bh, first_flag_read(a, bh), S)) {
-    load_published_q(a, bh, S);
-  } else {
-    block_rotate_q_chunked(a, b, h, S);
+    rotate_and_publish(a, b, h, bh, S);
+    return true;
   }
+  return wait_published_q(a, bh, first_flag_read(a, bh), S);
+}
+
+// q of head group g of a window block into shared memory.
+__device__ inline void window_q_group(const DecodeArgs& a, int b, int h, int bh, int g, bool published,
+                                      FusedSmem& S) {
+  if (published)
+    load_published_q(a, bh * a.G + g, S);
+  else
+    block_rotate_q_chunked(a, b, h * a.Gq + 4 * g, S);
 }
 
 // Window blocks.  When the launch also appends a token, that token is the
@@ -858,15 +906,20 @@ __device__ inline WinRows window_first_rows(const DecodeArgs& a, int bh, int wbl
 }
 
 // bf16 window tokens (sink + recent) of one (sequence, kv head), up to
-// win.chunk of them in 64-token passes with fp32 VALU arithmetic.  first: the
-// first pass's rows, already issued (later passes load theirs at their start).
+// win.chunk of them in 64-token passes with fp32 VALU arithmetic, for each
+// head group of 4 query heads in turn.  first: the first pass's rows, already
+// issued (later passes, and the passes of later groups, load theirs at their
+// start; a later group loads its first pass's rows again, from cache, rather
+// than hold them in registers).  published: whether the launch's published q
+// is there.
+__device__ __forceinline__ void window_group(const DecodeArgs& a, int bh, int b, int hq0, int wblk, int t_new, FusedSmem& S,
+                             const WinRows& first);
+
+template <int G>
 __device__ void window_block(const DecodeArgs& a, int bh, int b, int h, int wblk, FusedSmem& S,
-                             const WinRows& first) {
+                             const WinRows& first, bool published) {
   constexpr int D = 128;
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const int len = window_len(a);
-  const int v_lo = wblk * a.win.chunk;
-  const int v_hi = min(len, v_lo + a.win.chunk);
+  const int tid = threadIdx.x;
   const int t_new = window_new_token(a, wblk);
   if (t_new >= 0) {
     for (int which = 0; which < 2; ++which) {
@@ -882,6 +935,24 @@ __device__ void window_block(const DecodeArgs& a, int bh, int b, int h, int wblk
       __syncthreads();
     }
   }
+  window_q_group(a, b, h, bh, 0, published, S);
+  window_group(a, bh, b, h * 4 * G, wblk, t_new, S, first);
+#pragma unroll
+  for (int g = 1; g < G; ++g) {
+    __syncthreads();                  // shared memory is reused by the next group
+    const WinRows again = window_first_rows(a, bh, wblk);
+    window_q_group(a, b, h, bh, g, published, S);
+    window_group(a, bh, b, h * 4 * G + 4 * g, wblk, t_new, S, again);
+  }
+}
+
+__device__ __forceinline__ void window_group(const DecodeArgs& a, int bh, int b, int hq0, int wblk, int t_new, FusedSmem& S,
+                             const WinRows& first) {
+  constexpr int D = 128;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int len = window_len(a);
+  const int v_lo = wblk * a.win.chunk;
+  const int v_hi = min(len, v_lo + a.win.chunk);
   float* sc = S.scratch;               // [4][64]
   float* wm = S.scratch + 256;         // [4] running max
   float* wl = S.scratch + 260;         // [4] running sum
@@ -988,7 +1059,7 @@ __device__ void window_block(const DecodeArgs& a, int bh, int b, int h, int wblk
   const int slot = a.win.slot0 + wblk;
   for (int idx = tid; idx < 4 * D; idx += 256) {
     const int j = idx >> 7, d = idx & 127;
-    float* dst = a.partials + (((size_t)b * a.Hq + h * 4 + j) * kMaxSplits + slot) * (D + 2);
+    float* dst = a.partials + (((size_t)b * a.Hq + hq0 + j) * kMaxSplits + slot) * (D + 2);
     st_partial(dst + d, ((red[j * D + d] + red[(4 + j) * D + d]) + red[(8 + j) * D + d]) + red[(12 + j) * D + d]);
     if (d == 0) {
       st_partial(dst + D, wm[j]);
@@ -1078,11 +1149,13 @@ __device__ inline TileRegs load_tile(const TileStreams& s, int t0, int lane_c, i
   return r;
 }
 
-template <int WPB>
+// G: head groups of 4 query heads per kv head (G = Hq / Hkv / 4).  Every wave
+// scores a tile's tokens for all G groups: the codes are unpacked once and
+// feed G matrix-core chains.
+template <int WPB, int G>
 __global__ __launch_bounds__(64 * WPB)
-#if OSCAR_MFMA_WAVES_PER_EU
-__attribute__((amdgpu_waves_per_eu(OSCAR_MFMA_WAVES_PER_EU, OSCAR_MFMA_WAVES_PER_EU)))
-#endif
+__attribute__((amdgpu_waves_per_eu(G == 1 ? OSCAR_MFMA_WAVES_PER_EU : OSCAR_MFMA_WAVES_PER_EU_G2,
+                                   G == 1 ? OSCAR_MFMA_WAVES_PER_EU : OSCAR_MFMA_WAVES_PER_EU_G2)))
 void decode_mfma_kernel(DecodeArgs a) {
   constexpr int D = 128;
   const int bh = blockIdx.x;
@@ -1104,9 +1177,9 @@ void decode_mfma_kernel(DecodeArgs a) {
   const int lead = a.int2_lead;
   if (y >= lead && y < lead + a.win_blocks) {
     const WinRows rows = window_first_rows(a, bh, y - lead);   // in flight during the q wait
-    window_q(a, b, h, bh, y, S);
-    window_block(a, bh, b, h, y - lead, S, rows);
-    finish_block(a, bh, S);
+    const bool published = window_q_ready(a, b, h, bh, y, S);
+    window_block<G>(a, bh, b, h, y - lead, S, rows, published);
+    finish_block<G>(a, bh, S);
     return;
   }
   const int split = y < lead ? y : y - a.win_blocks;
@@ -1141,6 +1214,20 @@ void decode_mfma_kernel(DecodeArgs a) {
   // take the published operands.  Measured: every block rotating costs more
   // than sharing; first-wave blocks rotating gave the same time as this.
   const bool self_rotate = y == 0;
+  auto hq_of = [&](int g) { return h * 4 * G + 4 * g; };   // first query head of group g
+  // q operands: 8 words x 4 fp16 of head j of each group; lane group pp holds
+  // the k-slots of qk_dim(w, pp, k), each scaled by 2^eq 4^-(d % 4)
+  h4 qv[G][8];
+  int eq[G];
+  float qsum[G];
+  auto operands_from_smem = [&](int g) {
+#pragma unroll
+    for (int w = 0; w < 8; ++w)
+#pragma unroll
+      for (int k = 0; k < 4; ++k) qv[g][w][k] = q_operand(S, j, lane >> 4, w, k);
+    qsum[g] = S.qsum[j];
+    eq[g] = S.qeq[j];
+  };
   // The first loads are unconditional (a wave with fewer tiles re-reads its
   // split's last tile), so what was issued before them is waited for on its
   // own.  A rotating block issues one tile before rotating (its R rows hold
@@ -1148,49 +1235,56 @@ void decode_mfma_kernel(DecodeArgs a) {
   unsigned flag0 = 0;
   TileRegs r[kDepth];
   if (self_rotate) {
-    const QRotLoads qload = q_rotation_loads(a, b, h);
+    const QRotLoads qload = q_rotation_loads(a, b, hq_of(0));
     __builtin_amdgcn_sched_barrier(0);
     r[0] = load_tile(st, tile_t0(min(ti0, t_last)), lane_c, lane_m);
     __builtin_amdgcn_sched_barrier(0);
     q_rotation_finish(a, qload, S);
-    if (y == 0) publish_q(a, bh, S);
+    publish_q(a, bh * G, S);
+#pragma unroll
+    for (int g = 1; g < G; ++g) {
+      operands_from_smem(g - 1);
+      block_rotate_q_chunked(a, b, hq_of(g), S);
+      publish_q(a, bh * G + g, S);
+    }
+    publish_flag(a, bh);
 #pragma unroll
     for (int k = 1; k < kDepth; ++k) r[k] = load_tile(st, tile_t0(min(ti0 + k * WPB, t_last)), lane_c, lane_m);
+    operands_from_smem(G - 1);
   } else {
     flag0 = first_flag_read(a, bh);
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int k = 0; k < kDepth; ++k) r[k] = load_tile(st, tile_t0(min(ti0 + k * WPB, t_last)), lane_c, lane_m);
     __builtin_amdgcn_sched_barrier(0);
-  }
-
-  // q operands: 8 words x 4 fp16 of head j; lane group pp holds the k-slots
-  // of qk_dim(w, pp, k), each scaled by 2^eq 4^-(d % 4)
-  h4 qv[8];
-  int eq;
-  float qsum;
-  if (!self_rotate && wait_published_q(a, bh, flag0, S)) {
-    const __amdgpu_buffer_rsrc_t qr = plane_rsrc(a.qpub + (size_t)bh * kQPub, kQPub * 4);
-    const int vbase = (kQPubOps + 16 * (4 * (lane >> 4) + j)) * 4;
+    if (wait_published_q(a, bh, flag0, S)) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const u4 wv = __builtin_amdgcn_raw_buffer_load_b128(qr, vbase + 16 * i, 0, kDeviceScope);
-      qv[2 * i] = as_h4(wv.x, wv.y);
-      qv[2 * i + 1] = as_h4(wv.z, wv.w);
+      for (int g = 0; g < G; ++g) {
+        const __amdgpu_buffer_rsrc_t qr = plane_rsrc(a.qpub + (size_t)(bh * G + g) * kQPub, kQPub * 4);
+        const int vbase = (kQPubOps + 16 * (4 * (lane >> 4) + j)) * 4;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const u4 wv = __builtin_amdgcn_raw_buffer_load_b128(qr, vbase + 16 * i, 0, kDeviceScope);
+          qv[g][2 * i] = as_h4(wv.x, wv.y);
+          qv[g][2 * i + 1] = as_h4(wv.z, wv.w);
+        }
+        qsum[g] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(qr, (512 + j) * 4, 0, kDeviceScope));
+        eq[g] = (int)__builtin_amdgcn_raw_buffer_load_b32(qr, (516 + j) * 4, 0, kDeviceScope);
+      }
+    } else {
+#pragma unroll
+      for (int g = 0; g < G; ++g) {
+        block_rotate_q_chunked(a, b, hq_of(g), S);
+        operands_from_smem(g);
+      }
     }
-    qsum = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(qr, (512 + j) * 4, 0, kDeviceScope));
-    eq = (int)__builtin_amdgcn_raw_buffer_load_b32(qr, (516 + j) * 4, 0, kDeviceScope);
-  } else {
-    if (!self_rotate) block_rotate_q_chunked(a, b, h, S);
-#pragma unroll
-    for (int w = 0; w < 8; ++w)
-#pragma unroll
-      for (int k = 0; k < 4; ++k) qv[w][k] = q_operand(S, j, lane >> 4, w, k);
-    qsum = S.qsum[j];
-    eq = S.qeq[j];
   }
-  const float cK = ldexpf(1.0f, 24 - eq);          // undoes 2^eq and the 2^-24 code scale
-  const float zq = ldexpf(qsum, eq - 24);          // sum(q_rot) in units of the raw dot
+  float cK[G], zq[G];
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    cK[g] = ldexpf(1.0f, 24 - eq[g]);              // undoes 2^eq and the 2^-24 code scale
+    zq[g] = ldexpf(qsum[g], eq[g] - 24);           // sum(q_rot) in units of the raw dot
+  }
   const float vmax = a.v.smax[bh];
   int ev2 = 0;
   if (vmax > 0.0f) frexpf(vmax, &ev2);
@@ -1206,86 +1300,91 @@ void decode_mfma_kernel(DecodeArgs a) {
   const float kAf = (float)kA;
   const float cV = ldexpf(1.0f, 24 - ev);
 
-  f4 o0 = {0, 0, 0, 0}, o1 = {0, 0, 0, 0};
-  float m = NEG_INF, lA = 0.0f, lB = 0.0f, pzA = 0.0f, pzB = 0.0f;
-  float cA = 0.0f, cB = 0.0f;                      // kA - m and kA - 2 - m
+  f4 o0[G], o1[G];
+  float m[G], lA[G], lB[G], pzA[G], pzB[G];
+  float cA[G], cB[G];                              // kA - m and kA - 2 - m
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    o0[g] = f4{0, 0, 0, 0};
+    o1[g] = f4{0, 0, 0, 0};
+    m[g] = NEG_INF;
+    lA[g] = lB[g] = pzA[g] = pzB[g] = 0.0f;
+    cA[g] = cB[g] = 0.0f;
+  }
 
   // one 64-token tile: QK^T on matrix cores, online softmax, PV on matrix cores
   auto process = [&](const TileRegs& cur, int t0) {
-#if OSCAR_QK_TWO_CHAINS
-    f4 sa = {0, 0, 0, 0}, sb = {0, 0, 0, 0};
-#else
-    f4 sa = {0, 0, 0, 0};
-    f4& sb = sa;                                   // one accumulation chain
-#endif
-    qk_word<0>(cur.k0.x, qv[0], sa, sb);
-    qk_word<1>(cur.k0.y, qv[1], sa, sb);
-    qk_word<2>(cur.k0.z, qv[2], sa, sb);
-    qk_word<3>(cur.k0.w, qv[3], sa, sb);
-    qk_word<4>(cur.k1.x, qv[4], sa, sb);
-    qk_word<5>(cur.k1.y, qv[5], sa, sb);
-    qk_word<6>(cur.k1.z, qv[6], sa, sb);
-    qk_word<7>(cur.k1.w, qv[7], sa, sb);
-#if OSCAR_QK_TWO_CHAINS
-    const f4 sc = sa + sb;
-#else
-    const f4 sc = sa;
-#endif
+    f4 sc[G];
+#pragma unroll
+    for (int g = 0; g < G; ++g) sc[g] = f4{0, 0, 0, 0};
+    qk_word<G>(cur.k0.x, qv, 0, sc);
+    qk_word<G>(cur.k0.y, qv, 1, sc);
+    qk_word<G>(cur.k0.z, qv, 2, sc);
+    qk_word<G>(cur.k0.w, qv, 3, sc);
+    qk_word<G>(cur.k1.x, qv, 4, sc);
+    qk_word<G>(cur.k1.y, qv, 5, sc);
+    qk_word<G>(cur.k1.z, qv, 6, sc);
+    qk_word<G>(cur.k1.w, qv, 7, sc);
     PHASE_FENCE();
 
     const uint32_t kmr[4] = {cur.km.x, cur.km.y, cur.km.z, cur.km.w};
     const uint32_t vmr[4] = {cur.vm.x, cur.vm.y, cur.vm.z, cur.vm.w};
-    float u[4];
+    const bool edge = t0 < lo || t0 + 64 > hi;     // boundary tile (wave-uniform)
+    h4 pv[G];
 #pragma unroll
-    for (int r = 0; r < 4; ++r)   // s_K * dot + z_K * sum(q), fp16 metadata read in place
-      u[r] = __builtin_fmaf(hi_half(kmr[r]), zq, __builtin_fmaf(lo_half(kmr[r]), sc[r], 0.0f));
-    if (t0 < lo || t0 + 64 > hi) {                 // boundary tile (wave-uniform)
+    for (int g = 0; g < G; ++g) {
+      float u[4];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int t = t0 + 4 * blk + r;
-        if (t < lo || t >= hi) u[r] = NEG_INF;
+      for (int r = 0; r < 4; ++r)   // s_K * dot + z_K * sum(q), fp16 metadata read in place
+        u[r] = __builtin_fmaf(hi_half(kmr[r]), zq[g], __builtin_fmaf(lo_half(kmr[r]), sc[g][r], 0.0f));
+      if (edge) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int t = t0 + 4 * blk + r;
+          if (t < lo || t >= hi) u[r] = NEG_INF;
+        }
       }
+      // The head-wide maximum is only needed when some score exceeds its head's
+      // running maximum (every lane of a head holds that maximum).
+      const float tmax = cK[g] * fmaxf(fmaxf(u[0], u[1]), fmaxf(u[2], u[3]));
+      if (__any(tmax > m[g])) {                    // some head's max moved: rescale
+        const float mnew = fmaxf(m[g], head_max(tmax));
+        const float alpha = __builtin_amdgcn_exp2f(m[g] - mnew);
+        lA[g] *= alpha;
+        lB[g] *= alpha;
+        pzA[g] *= alpha;
+        pzB[g] *= alpha;
+        const f4 al = {lane_value(alpha, 0), lane_value(alpha, 1), lane_value(alpha, 2), lane_value(alpha, 3)};
+        o0[g] *= al;
+        o1[g] *= al;
+        m[g] = mnew;
+        cA[g] = kAf - mnew;
+        cB[g] = cA[g] - 2.0f;
+      }
+      float p[4];
+      p[0] = __builtin_amdgcn_exp2f(__builtin_fmaf(cK[g], u[0], cA[g]));
+      p[1] = __builtin_amdgcn_exp2f(__builtin_fmaf(cK[g], u[1], cA[g]));
+      p[2] = __builtin_amdgcn_exp2f(__builtin_fmaf(cK[g], u[2], cB[g]));
+      p[3] = __builtin_amdgcn_exp2f(__builtin_fmaf(cK[g], u[3], cB[g]));
+      lA[g] += p[0] + p[1];
+      lB[g] += p[2] + p[3];
+      pzA[g] = __builtin_fmaf(p[0], hi_half(vmr[0]), __builtin_fmaf(p[1], hi_half(vmr[1]), pzA[g]));
+      pzB[g] = __builtin_fmaf(p[2], hi_half(vmr[2]), __builtin_fmaf(p[3], hi_half(vmr[3]), pzB[g]));
+      // s_V * p' as fp16 with one rounding (fp16 metadata read in place)
+      pv[g] = h4{(_Float16)__builtin_fmaf(lo_half(vmr[0]), p[0], 0.0f),
+                 (_Float16)__builtin_fmaf(lo_half(vmr[1]), p[1], 0.0f),
+                 (_Float16)__builtin_fmaf(lo_half(vmr[2]), p[2], 0.0f),
+                 (_Float16)__builtin_fmaf(lo_half(vmr[3]), p[3], 0.0f)};
     }
-    // The head-wide maximum is only needed when some score exceeds its head's
-    // running maximum (every lane of a head holds that maximum).
-    const float tmax = cK * fmaxf(fmaxf(u[0], u[1]), fmaxf(u[2], u[3]));
-    if (__any(tmax > m)) {                         // some head's max moved: rescale
-      const float mnew = fmaxf(m, head_max(tmax));
-      const float alpha = __builtin_amdgcn_exp2f(m - mnew);
-      lA *= alpha;
-      lB *= alpha;
-      pzA *= alpha;
-      pzB *= alpha;
-      const f4 al = {lane_value(alpha, 0), lane_value(alpha, 1), lane_value(alpha, 2), lane_value(alpha, 3)};
-      o0 *= al;
-      o1 *= al;
-      m = mnew;
-      cA = kAf - m;
-      cB = cA - 2.0f;
-    }
-    float p[4];
-    p[0] = __builtin_amdgcn_exp2f(__builtin_fmaf(cK, u[0], cA));
-    p[1] = __builtin_amdgcn_exp2f(__builtin_fmaf(cK, u[1], cA));
-    p[2] = __builtin_amdgcn_exp2f(__builtin_fmaf(cK, u[2], cB));
-    p[3] = __builtin_amdgcn_exp2f(__builtin_fmaf(cK, u[3], cB));
-    lA += p[0] + p[1];
-    lB += p[2] + p[3];
-    pzA = __builtin_fmaf(p[0], hi_half(vmr[0]), __builtin_fmaf(p[1], hi_half(vmr[1]), pzA));
-    pzB = __builtin_fmaf(p[2], hi_half(vmr[2]), __builtin_fmaf(p[3], hi_half(vmr[3]), pzB));
-    // s_V * p' as fp16 with one rounding (fp16 metadata read in place)
-    const h4 pv = {(_Float16)__builtin_fmaf(lo_half(vmr[0]), p[0], 0.0f),
-                   (_Float16)__builtin_fmaf(lo_half(vmr[1]), p[1], 0.0f),
-                   (_Float16)__builtin_fmaf(lo_half(vmr[2]), p[2], 0.0f),
-                   (_Float16)__builtin_fmaf(lo_half(vmr[3]), p[3], 0.0f)};
     PHASE_FENCE();
-    pv_word<0>(cur.v0.x, pv, o0, o1);
-    pv_word<1>(cur.v0.y, pv, o0, o1);
-    pv_word<2>(cur.v0.z, pv, o0, o1);
-    pv_word<3>(cur.v0.w, pv, o0, o1);
-    pv_word<4>(cur.v1.x, pv, o0, o1);
-    pv_word<5>(cur.v1.y, pv, o0, o1);
-    pv_word<6>(cur.v1.z, pv, o0, o1);
-    pv_word<7>(cur.v1.w, pv, o0, o1);
+    pv_word<G, 0>(cur.v0.x, pv, o0, o1);
+    pv_word<G, 1>(cur.v0.y, pv, o0, o1);
+    pv_word<G, 2>(cur.v0.z, pv, o0, o1);
+    pv_word<G, 3>(cur.v0.w, pv, o0, o1);
+    pv_word<G, 4>(cur.v1.x, pv, o0, o1);
+    pv_word<G, 5>(cur.v1.y, pv, o0, o1);
+    pv_word<G, 6>(cur.v1.z, pv, o0, o1);
+    pv_word<G, 7>(cur.v1.w, pv, o0, o1);
   };
 
   for (int ti = ti0; ti < s_t1; ti += kDepth * WPB) {
@@ -1298,47 +1397,51 @@ void decode_mfma_kernel(DecodeArgs a) {
     }
   }
 
-  // per-head totals of l and sum(p z_V) over the 16 lanes of each head
-  const float l = head_sum(ldexpf(__builtin_fmaf(4.0f, lB, lA), -kA));
-  const float pz = head_sum(ldexpf(__builtin_fmaf(4.0f, pzB, pzA), -kA));
   static_assert(8 * WPB + WPB * 4 * D <= sizeof(S.scratch) / sizeof(float), "epilogue scratch");
   float* sm = S.scratch;                 // [WPB][4]
   float* sl = S.scratch + 4 * WPB;       // [WPB][4]
   float* so = S.scratch + 8 * WPB;       // [WPB][4][D]
-  if (lane < 4) {
-    sm[wave * 4 + lane] = m;
-    sl[wave * 4 + lane] = l;
-  }
-  const float pzr[4] = {lane_value(pz, 0), lane_value(pz, 1), lane_value(pz, 2), lane_value(pz, 3)};
-#pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    so[(wave * 4 + r) * D + 4 * blk + j] = __builtin_fmaf(o0[r], cV, pzr[r]);
-    so[(wave * 4 + r) * D + 64 + 4 * blk + j] = __builtin_fmaf(o1[r], cV, pzr[r]);
-  }
-  __syncthreads();
   const int slot = a.plan.slot0 + split;
-  for (int idx = threadIdx.x; idx < 4 * D; idx += 64 * WPB) {
-    const int r = idx / D, d = idx - r * D;
-    float M = NEG_INF;
 #pragma unroll
-    for (int w = 0; w < WPB; ++w) M = fmaxf(M, sm[w * 4 + r]);
-    float O = 0.0f, L = 0.0f;
-    if (M != NEG_INF) {
+  for (int g = 0; g < G; ++g) {
+    // per-head totals of l and sum(p z_V) over the 16 lanes of each head
+    const float l = head_sum(ldexpf(__builtin_fmaf(4.0f, lB[g], lA[g]), -kA));
+    const float pz = head_sum(ldexpf(__builtin_fmaf(4.0f, pzB[g], pzA[g]), -kA));
+    if (g > 0) __syncthreads();          // the previous group's merge has read the scratch
+    if (lane < 4) {
+      sm[wave * 4 + lane] = m[g];
+      sl[wave * 4 + lane] = l;
+    }
+    const float pzr[4] = {lane_value(pz, 0), lane_value(pz, 1), lane_value(pz, 2), lane_value(pz, 3)};
 #pragma unroll
-      for (int w = 0; w < WPB; ++w) {
-        const float sw = exp2f(sm[w * 4 + r] - M);
-        O = __builtin_fmaf(so[(w * 4 + r) * D + d], sw, O);
-        L = __builtin_fmaf(sl[w * 4 + r], sw, L);
+    for (int r = 0; r < 4; ++r) {
+      so[(wave * 4 + r) * D + 4 * blk + j] = __builtin_fmaf(o0[g][r], cV, pzr[r]);
+      so[(wave * 4 + r) * D + 64 + 4 * blk + j] = __builtin_fmaf(o1[g][r], cV, pzr[r]);
+    }
+    __syncthreads();
+    for (int idx = threadIdx.x; idx < 4 * D; idx += 64 * WPB) {
+      const int r = idx / D, d = idx - r * D;
+      float M = NEG_INF;
+#pragma unroll
+      for (int w = 0; w < WPB; ++w) M = fmaxf(M, sm[w * 4 + r]);
+      float O = 0.0f, L = 0.0f;
+      if (M != NEG_INF) {
+#pragma unroll
+        for (int w = 0; w < WPB; ++w) {
+          const float sw = exp2f(sm[w * 4 + r] - M);
+          O = __builtin_fmaf(so[(w * 4 + r) * D + d], sw, O);
+          L = __builtin_fmaf(sl[w * 4 + r], sw, L);
+        }
+      }
+      float* dst = a.partials + (((size_t)b * a.Hq + hq_of(g) + r) * kMaxSplits + slot) * (D + 2);
+      st_partial(dst + d, O);
+      if (d == 0) {
+        st_partial(dst + D, M);
+        st_partial(dst + D + 1, L);
       }
     }
-    float* dst = a.partials + (((size_t)b * a.Hq + h * 4 + r) * kMaxSplits + slot) * (D + 2);
-    st_partial(dst + d, O);
-    if (d == 0) {
-      st_partial(dst + D, M);
-      st_partial(dst + D + 1, L);
-    }
   }
-  finish_block(a, bh, S);
+  finish_block<G>(a, bh, S);
 }
 
 // ---------------------------------------------------------------------------
@@ -1363,10 +1466,12 @@ hipError_t launch_decode_valu(const DecodeArgs& a, int B, hipStream_t s) {
   return hipGetLastError();
 }
 
-int decode_mfma_resident_blocks(int device) {
+int decode_mfma_resident_blocks(int device, int G) {
   int per_cu = 0, cus = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, decode_mfma_kernel<4>, 256, 0) != hipSuccess || per_cu < 1)
-    per_cu = 1;
+  const hipError_t e =
+      G == 2 ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, decode_mfma_kernel<4, 2>, 256, 0)
+             : hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, decode_mfma_kernel<4, 1>, 256, 0);
+  if (e != hipSuccess || per_cu < 1) per_cu = 1;
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, device) != hipSuccess || cus < 1) cus = 1;
   return per_cu * cus;
 }
@@ -1374,7 +1479,10 @@ int decode_mfma_resident_blocks(int device) {
 hipError_t launch_decode_mfma(const DecodeArgs& a, int B, int waves_per_block, hipStream_t s) {
   (void)waves_per_block;   // the fused window blocks need 4 waves
   dim3 grid((unsigned)(B * a.Hkv), (unsigned)(a.app_blocks + a.plan.splits + a.win_blocks));
-  hipLaunchKernelGGL(decode_mfma_kernel<4>, grid, dim3(256), 0, s, a);
+  if (a.G == 2)
+    hipLaunchKernelGGL((decode_mfma_kernel<4, 2>), grid, dim3(256), 0, s, a);
+  else
+    hipLaunchKernelGGL((decode_mfma_kernel<4, 1>), grid, dim3(256), 0, s, a);
   return hipGetLastError();
 }
 

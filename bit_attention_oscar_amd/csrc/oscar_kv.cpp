@@ -69,7 +69,7 @@ struct oscar_kv {
   float* rv = nullptr;     // [L][D][D]
   float* rvT = nullptr;    // [L][D][D] transposed
   float* qrot = nullptr;   // [B][Hq][D]
-  float* qpub = nullptr;    // [B][Hkv][kQPub]
+  float* qpub = nullptr;    // [B][Hkv][G][kQPub]
   unsigned* qflag = nullptr; // [B][Hkv]
   unsigned epoch = 0;        // matrix-core launches so far (skips 0 on wrap)
   float* partials = nullptr; // [B][Hq][kMaxSplits][D+2]
@@ -353,7 +353,7 @@ int oscar_kv_create(const oscar_kv_config* cfg, oscar_kv** out) {
     return bail(fail(OSCAR_ERR_HIP, "copy of rotations failed"));
   const size_t B = cfg->max_batch, Hq = cfg->num_q_heads, Hkv = cfg->num_kv_heads;
   if ((rc = dev_alloc(kv, (void**)&kv->qrot, B * Hq * D * 4))) return bail(rc);
-  if ((rc = dev_alloc(kv, (void**)&kv->qpub, B * Hkv * kQPub * 4))) return bail(rc);
+  if ((rc = dev_alloc(kv, (void**)&kv->qpub, B * std::max(Hkv, Hq / 4) * kQPub * 4))) return bail(rc);
   if ((rc = dev_alloc(kv, (void**)&kv->qflag, B * Hkv * sizeof(unsigned)))) return bail(rc);
   if (hipMemset(kv->qflag, 0, B * Hkv * sizeof(unsigned)) != hipSuccess)
     return bail(fail(OSCAR_ERR_HIP, "clearing the q flags failed"));
@@ -362,7 +362,7 @@ int oscar_kv_create(const oscar_kv_config* cfg, oscar_kv** out) {
   if (hipMemset(kv->counters, 0, B * Hkv * sizeof(unsigned)) != hipSuccess)
     return bail(fail(OSCAR_ERR_HIP, "clearing the decode counters failed"));
   if (hipDeviceSynchronize() != hipSuccess) return bail(fail(OSCAR_ERR_HIP, "device sync after create failed"));
-  kv->resident = decode_mfma_resident_blocks(cfg->device);
+  kv->resident = decode_mfma_resident_blocks(cfg->device, std::max(1, (int)(Hq / Hkv / 4)));
   int wall_khz = 0;
   if (hipDeviceGetAttribute(&wall_khz, hipDeviceAttributeWallClockRate, cfg->device) == hipSuccess && wall_khz > 0)
     kv->qwait_ticks = (unsigned)std::min<long long>(20LL * wall_khz / 1000, 1LL << 30);
@@ -399,7 +399,8 @@ bool fast_shape(const oscar_kv* kv) {
   const auto& c = kv->cfg;
   // the matrix-core kernel addresses one (sequence, kv head)'s code plane with
   // 32-bit buffer offsets: cap * 32 bytes must fit
-  return kv->decode_impl == 0 && c.head_dim == 128 && c.num_q_heads == 4 * c.num_kv_heads &&
+  return kv->decode_impl == 0 && c.head_dim == 128 &&
+         (c.num_q_heads == 4 * c.num_kv_heads || c.num_q_heads == 8 * c.num_kv_heads) &&
          c.k_dtype == OSCAR_KV_INT2 && c.v_dtype == OSCAR_KV_INT2 && (long long)kv->cap * 32 <= INT32_MAX;
 }
 
@@ -441,6 +442,8 @@ int launch_decode(oscar_kv* kv, int32_t layer, const void* q, void* out, int32_t
   da.N = N;
   da.M = M;
   da.T = T;
+  da.Gq = Hq / Hkv;
+  da.G = std::max(1, da.Gq / 4);
   da.counters = kv->counters;
   da.q = static_cast<const uint16_t*>(q);
   da.rk = kv->rk + layer * DD;

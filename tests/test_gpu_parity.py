@@ -257,9 +257,10 @@ def test_decode_window_edges(ok, T, N, M):
                       # split's running max, so splits move its rounding points;
                       # bounded by fp16's half-ulp
 ])
-def test_split_invariance(ok, impl, tol):
-    shape = Shape(B=2, Hq=8, Hkv=2, N=64, M=256)
-    say(f"[split invariance] impl={impl}")
+@pytest.mark.parametrize("gq", [4, 8])
+def test_split_invariance(ok, impl, tol, gq):
+    shape = Shape(B=2, Hq=2 * gq, Hkv=2, N=64, M=256)
+    say(f"[split invariance] impl={impl} gq={gq}")
     gc, rk, rv, k, v, mask = _fill(ok, shape, 5000)
     qb = query(shape, mask)
     ref = _decode(ok, gc, 0, qb, impl=impl, splits=1)
@@ -377,6 +378,8 @@ def _exports_equal(g1, g2, layer, N, M):
     (Shape(B=2, Hq=4, Hkv=2, N=8, M=16), 0, 30),               # from an empty cache: sink, then ring
     (Shape(B=1, Hq=4, Hkv=1, N=0, M=1), 130, 3),               # window = the new token only
     (Shape(B=1, Hq=4, Hkv=1, N=64, M=256), 300, 4),            # every token still bf16
+    (Shape(B=2, Hq=16, Hkv=2, N=8, M=40), 700, 6),             # GQA 8: two head groups per kv head
+    (Shape(B=1, Hq=8, Hkv=1, N=3, M=5), 66, 40),               # GQA 8, ring wraps, tile edges crossed
 ])
 def test_decode_step_equals_append_then_decode(ok, shape, T0, steps):
     """The fused step (append and attention in one launch) against the two
@@ -439,7 +442,8 @@ def test_decode_step_exact_rotation_bitexact(ok):
 
 
 @pytest.mark.parametrize("shape", [
-    Shape(B=1, Hq=16, Hkv=2, N=8, M=16),                       # GQA 8: separate launches
+    Shape(B=1, Hq=32, Hkv=2, N=8, M=16),                       # GQA 16: separate launches
+    Shape(B=1, Hq=4, Hkv=2, N=8, M=16),                        # GQA 2
     Shape(B=2, Hq=4, Hkv=2, D=512, N=16, M=32),                # wide head
     Shape(B=1, Hq=4, Hkv=1, N=8, M=0),                         # no recent window
     Shape(B=1, Hq=4, Hkv=1, N=8, M=16, v_dtype=1),             # V kept bf16
@@ -491,6 +495,34 @@ def test_full_size_32k_sampled(ok):
     say(f"  step vs attention call: {rel_l2(got_step, got):.2e}")
     assert rel_l2(got_step, got) <= 2 ** -12
     for b in (0, 15):
+        want = oracle_on_exported(gc, 0, qb, shape, rk, rv, batch_idx=slice(b, b + 1))
+        e = rel_l2(got[b:b + 1], want)
+        say(f"  seq {b}: rel L2 {e:.3e}")
+        assert e <= ATTN_TOL
+    gc.close()
+
+
+@pytest.mark.slow
+def test_full_size_128k_gqa8_sampled(ok):
+    """The 128k-context GQA-8 shape (B=8, Hq=64, Hkv=8, D=128, N=64, M=256,
+    Student-t(3) values) on one layer, filled on the device, one fused step
+    in the benchmark's launch configuration; sequences 0 and 7 checked against
+    the oracle over the exported cache."""
+    from bench import fill_layer_device
+    shape = Shape(B=8, Hq=64, Hkv=8, D=128, N=64, M=256, dist="student_t3", outliers="none")
+    T = 131072
+    say("[full 128k gqa8] filling")
+    rk, rv = make_rotations(shape, "haar")
+    gc = gpu_cache(ok, shape, rk, rv, T + 64)
+    fill_layer_device(gc, 0, shape.B, shape.Hkv, shape.D, T, seed=0, dist="student_t3", outliers="none")
+    mask = synth.outlier_mask(shape.D, shape.Hkv, 0, 0, "none")
+    k1, v1, _ = inputs(shape, 1, chunk=99)
+    qb = query(shape, mask, step=1)
+    got_step = _step(ok, gc, 0, k1, v1, qb)
+    got = _decode(ok, gc, 0, qb)
+    say(f"  step vs attention call: {rel_l2(got_step, got):.2e}")
+    assert rel_l2(got_step, got) <= 2 ** -12
+    for b in (0, 7):
         want = oracle_on_exported(gc, 0, qb, shape, rk, rv, batch_idx=slice(b, b + 1))
         e = rel_l2(got[b:b + 1], want)
         say(f"  seq {b}: rel L2 {e:.3e}")
