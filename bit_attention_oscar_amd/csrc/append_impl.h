@@ -255,7 +255,7 @@ __device__ inline void append_block(const AppendArgs& a, int bh, bool isv, int t
       code[2 * g] = quant_code(x[2 * g], q);
       code[2 * g + 1] = quant_code(x[2 * g + 1], q);
       if (lane == 0) {
-        P.meta[meta_offset(bh, a.cap, t, D) + g] = q.packed;
+        P.meta[meta_index(bh, a.cap, t, g, D)] = q.packed;
         if (P.smax) atomicMax(reinterpret_cast<unsigned int*>(P.smax + bh), __float_as_uint(q.sf));
       }
     }

@@ -23,7 +23,9 @@ constexpr int kMaxGq = 16;            // query heads per kv head handled by the 
 //                 (token t%64 at 16*(t%64)).  A decode lane owns one token
 //                 row and each of its 16-byte loads is contiguous across the
 //                 wave.
-//  K/V meta     : u32 [B][Hkv][cap][D/128] = fp16 scale (low) | fp16 zero (high)
+//  K/V meta     : u32 [B][Hkv][D/128][cap] = fp16 scale (low) | fp16 zero (high);
+//                 group-major, so the scales of one 128-wide group are
+//                 contiguous over tokens
 //  V INT2 codes : tiled for the PV matrix-core operand.  For every 64-token
 //                 block and every 128-wide slice of head_dim there is a 2 KiB
 //                 tile of 64 lane records of 32 bytes, stored as two 1 KiB
@@ -49,8 +51,9 @@ __host__ __device__ inline size_t kcode_byte(int bh, int cap, int t, int i, int 
   return tile * (size_t)(kTile * D / 4) + (size_t)(i >> 4) * 1024 + (size_t)(t & 63) * 16 + (i & 15);
 }
 
-__host__ __device__ inline size_t meta_offset(int bh, int cap, int t, int D) {
-  return ((size_t)bh * cap + t) * (size_t)(D / kGroup);
+// index of the scale|zero word of group g of token t
+__host__ __device__ inline size_t meta_index(int bh, int cap, int t, int g, int D) {
+  return ((size_t)bh * (D / kGroup) + g) * (size_t)cap + t;
 }
 
 // byte offset and bit of the 2-bit V code (t, d) in the tiled layout
@@ -174,6 +177,8 @@ hipError_t launch_decode_valu(const DecodeArgs& a, int B, hipStream_t s);
 hipError_t launch_decode_mfma(const DecodeArgs& a, int B, int waves_per_block, hipStream_t s);
 int decode_mfma_resident_blocks(int device, int G);   // blocks of the matrix-core kernel resident at once
 hipError_t launch_combine(const CombineArgs& a, hipStream_t s);
+hipError_t launch_wide_qrot(const DecodeArgs& a, int B, hipStream_t s);     // head_dim 512: rotated q records
+hipError_t launch_decode_wide(const DecodeArgs& a, int B, hipStream_t s);   // head_dim 512: INT2 + window partials
 hipError_t launch_stream_copy(const void* src, void* dst, size_t bytes, hipStream_t s);
 hipError_t launch_export_codes(const uint8_t* stored, uint8_t* canon, int BH, int cap, int T, int D, int isv,
                                hipStream_t s);

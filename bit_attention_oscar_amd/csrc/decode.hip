@@ -132,7 +132,7 @@ __device__ inline void load_row_values(const PlaneDev& P, int bh, int t, int T, 
     }
     return;
   }
-  const uint32_t meta = P.meta[meta_offset(bh, cap, t, D) + d0 / kGroup];
+  const uint32_t meta = P.meta[meta_index(bh, cap, t, d0 / kGroup, D)];
   const float s = (float)__builtin_bit_cast(_Float16, (uint16_t)(meta & 0xFFFFu));
   const float z = (float)__builtin_bit_cast(_Float16, (uint16_t)(meta >> 16));
   if (!P.tiled) {
@@ -158,7 +158,7 @@ __device__ inline float load_value(const PlaneDev& P, int bh, int t, int T, int 
                           : (t < N ? P.sink + row_offset(bh, N, t, D) : P.ring + row_offset(bh, M, t % M, D));
     return bf16_to_f32(row[d]);
   }
-  const uint32_t meta = P.meta[meta_offset(bh, cap, t, D) + d / kGroup];
+  const uint32_t meta = P.meta[meta_index(bh, cap, t, d / kGroup, D)];
   const float s = (float)__builtin_bit_cast(_Float16, (uint16_t)(meta & 0xFFFFu));
   const float z = (float)__builtin_bit_cast(_Float16, (uint16_t)(meta >> 16));
   uint32_t c;
@@ -544,6 +544,16 @@ __device__ inline const uint16_t* win_row(const DecodeArgs& a, const PlaneDev& P
   return P.ring + row_offset(bh, a.M, slot, D);
 }
 
+__device__ inline void bf16x8(const uint4 u, float* x);
+typedef uint32_t u4 __attribute__((ext_vector_type(4)));
+__device__ inline void bf16x8(const u4 u, float* x) {
+  const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    x[2 * k] = __uint_as_float(w[k] << 16);
+    x[2 * k + 1] = __uint_as_float(w[k] & 0xFFFF0000u);
+  }
+}
 __device__ inline void bf16x8(const uint4 u, float* x) {
   const uint32_t w[4] = {u.x, u.y, u.z, u.w};
 #pragma unroll
@@ -1094,8 +1104,6 @@ __device__ inline float lane_value(float v, int lane) {
   return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), lane));
 }
 
-typedef uint32_t u4 __attribute__((ext_vector_type(4)));
-
 struct TileRegs {
   u4 k0, k1;   // K codes of token tile + lane (32 bytes)
   u4 km, vm;   // K and V scale|zero of tokens tile + 4 blk .. + 3
@@ -1123,8 +1131,8 @@ __device__ inline TileStreams tile_streams(const DecodeArgs& a, int bh) {
   constexpr int D = 128;
   TileStreams s;
   s.kc = plane_rsrc(a.k.codes + kcode_byte(bh, a.cap, 0, 0, D), a.cap * 32);
-  s.km = plane_rsrc(a.k.meta + meta_offset(bh, a.cap, 0, D), a.cap * 4);
-  s.vm = plane_rsrc(a.v.meta + meta_offset(bh, a.cap, 0, D), a.cap * 4);
+  s.km = plane_rsrc(a.k.meta + meta_index(bh, a.cap, 0, 0, D), a.cap * 4);
+  s.vm = plane_rsrc(a.v.meta + meta_index(bh, a.cap, 0, 0, D), a.cap * 4);
   s.vc = plane_rsrc(a.v.codes + (size_t)bh * (a.cap / kTile) * 2048, a.cap * 32);
   return s;
 }
@@ -1445,6 +1453,447 @@ void decode_mfma_kernel(DecodeArgs a) {
 }
 
 // ---------------------------------------------------------------------------
+// head_dim 512 (four 128-wide quantization groups per head), at most 4 query
+// heads per kv head
+// ---------------------------------------------------------------------------
+//
+// Three launches: wide_qrot_kernel rotates q and writes, per (sequence, kv
+// head, 128-dim slice s), the record of the 128-dim path (fp32 q of the 4
+// heads over the slice, per-head sums and exponents, fp16 matrix-core
+// operands); decode_wide_kernel streams the INT2 range and the bf16 windows
+// into split partials; combine_kernel merges them and undoes the V rotation.
+// In decode_wide_kernel the four waves of a block share every 64-token tile
+// and wave w owns dims [128 w, 128 w + 128) = quantization group w: its K and
+// V code tiles, its scales, its part of the scores and of the output.  The
+// four partial scores meet in shared memory once per tile.
+
+// q rotation of one 128-dim slice of the rotated q, all heads of a kv head
+// (zero-padded to 4).  Grid: (sequence x kv head, slice).
+__global__ __launch_bounds__(256) void wide_qrot_kernel(DecodeArgs a) {
+  constexpr int D = 512;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int bh = blockIdx.x, s = blockIdx.y;
+  const int b = bh / a.Hkv, h = bh - (bh / a.Hkv) * a.Hkv;
+  __shared__ FusedSmem S;
+  __shared__ float qraw[4 * D];
+  __shared__ float parts[4][4][128];
+  for (int i = tid; i < 4 * D; i += 256) {
+    const int j = i / D, e = i - j * D;
+    qraw[i] = j < a.Gq ? bf16_to_f32(a.q[((size_t)b * a.Hq + h * a.Gq + j) * D + e]) : 0.0f;
+  }
+  __syncthreads();
+  // wave w reduces over input dims e in [128 w, 128 w + 128); lane owns output
+  // dims 128 s + lane and 128 s + lane + 64
+  float acc[4][2];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) acc[j][0] = acc[j][1] = 0.0f;
+  const float* Rw = a.rk + (size_t)(wave * 128) * D + 128 * s + lane;
+#pragma unroll 8
+  for (int e = 0; e < 128; ++e) {
+    const float r0 = Rw[(size_t)e * D], r1 = Rw[(size_t)e * D + 64];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const float x = qraw[j * D + wave * 128 + e];
+      acc[j][0] = __builtin_fmaf(x, r0, acc[j][0]);
+      acc[j][1] = __builtin_fmaf(x, r1, acc[j][1]);
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    parts[wave][j][lane] = acc[j][0];
+    parts[wave][j][lane + 64] = acc[j][1];
+  }
+  __syncthreads();
+  {
+    const int j = wave;                // wave j finishes head j
+    float v[2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int d = lane + 64 * i;
+      v[i] = ((((parts[0][j][d] + parts[1][j][d]) + parts[2][j][d]) + parts[3][j][d]) + 0.0f) * a.scale_log2;
+    }
+    S.qs[j][lane] = v[0];
+    S.qs[j][lane + 64] = v[1];
+    const float sum = wsum(v[0] + v[1]);
+    const float amax = wmax(fmaxf(fabsf(v[0]), fabsf(v[1])));
+    int e2 = 0;
+    if (amax > 0.0f) frexpf(amax, &e2);
+    if (lane == 0) {
+      S.qsum[j] = sum;
+      S.qeq[j] = (amax > 0.0f) ? 15 - e2 : 0;
+    }
+  }
+  __syncthreads();
+  publish_q(a, bh * 4 + s, S);
+}
+
+struct WideSmem {
+  f4 u[2][4][64];              // per-wave partial scores of a tile (two buffers)
+  float4 q[4][4][16][2];       // window: q of [slice][head][dims 8c .. 8c + 7]
+  float sc[4][4][32];          // window: [wave][head][token] partial scores
+  float p[4][32];              // window: softmax weights [head][token]
+  float wm[4], wl[4], wa[4];   // window: running max, sum, rescale factor per head
+};
+
+// bf16 window tokens of one (sequence, kv head) with fp32 VALU arithmetic, in
+// 32-token passes.  Window blocks take chunks of win.chunk tokens of the sink
+// segment [a0, b0) first, then of the recent segment [a1, b1), so a block
+// reads rows of one plane only: consecutive sink rows, or consecutive ring
+// slots from (ring0 + its first index) mod M.  Wave w owns dims [128 w,
+// 128 w + 128); lane (tq, c) owns dims 8 c .. 8 c + 7 of that slice for
+// tokens tq + 4 i of a pass, so every row load is contiguous across 16 lanes.
+template <int NH>
+__device__ void wide_window_block(const DecodeArgs& a, int bh, int b, int h, int wblk, WideSmem& W) {
+  constexpr int D = 512, PT = 32, RI = PT / 4;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int tq = lane >> 4, c = lane & 15;
+  const int len0 = a.win.b0 - a.win.a0, len1 = a.win.b1 - a.win.a1;
+  const int nb0 = (len0 + a.win.chunk - 1) / a.win.chunk;
+  const bool ring = wblk >= nb0;
+  const int i_lo = (ring ? wblk - nb0 : wblk) * a.win.chunk;
+  const int i_hi = min(ring ? len1 : len0, i_lo + a.win.chunk);
+  // first row of the block and the plane's rows (elements): sink row a0 + i,
+  // or ring slot (ring0 + i) mod M
+  const int rows = ring ? a.M : a.N;
+  const int nbytes = rows * D * 2;
+  // the block's plane rows as buffer resources: a load at offset nbytes (past
+  // them) returns zero
+  const __amdgpu_buffer_rsrc_t kp =
+      plane_rsrc(ring ? a.k.ring + row_offset(bh, a.M, 0, D) : a.k.sink + row_offset(bh, a.N, 0, D), nbytes);
+  const __amdgpu_buffer_rsrc_t vp =
+      plane_rsrc(ring ? a.v.ring + row_offset(bh, a.M, 0, D) : a.v.sink + row_offset(bh, a.N, 0, D), nbytes);
+  int row0 = ring ? a.ring0 + i_lo : a.win.a0 + i_lo;
+  if (row0 >= rows) row0 -= rows;
+  const int col = 128 * wave + 8 * c;
+  // q of the slice (4 heads, fp32 x scale * log2 e) into shared memory; read
+  // back at each use, through an offset the compiler cannot see as constant,
+  // so that it is not held in registers across the pass
+  if (lane < 8 * NH) {
+    const float* rec = a.qpub + (size_t)(bh * 4 + wave) * kQPub;
+    const int j = lane >> 3, cc = 2 * (lane & 7);
+#pragma unroll
+    for (int e = 0; e < 2; ++e)
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf)
+        W.q[wave][j][cc + e][hf] = *reinterpret_cast<const float4*>(rec + j * 128 + 8 * (cc + e) + 4 * hf);
+  }
+  if (tid < 4) {
+    W.wm[tid] = NEG_INF;
+    W.wl[tid] = 0.0f;
+  }
+  float o[NH][8];
+#pragma unroll
+  for (int j = 0; j < NH; ++j)
+#pragma unroll
+    for (int k = 0; k < 8; ++k) o[j][k] = 0.0f;
+  __syncthreads();
+  for (int p0 = i_lo; p0 < i_hi; p0 += PT) {
+    const int n = min(PT, i_hi - p0);
+    // byte offset of this lane's row i of the pass (nbytes, so loaded as
+    // zero, for rows past the pass); rows wrap at most once
+    auto roff = [&](int i) -> int {
+      int r = row0 + (p0 - i_lo) + tq + 4 * i;
+      if (r >= rows) r -= rows;
+      return (tq + 4 * i < n) ? (r * D + col) * 2 : nbytes;
+    };
+    {  // partial scores of this slice
+      u4 kr[RI];
+#pragma unroll
+      for (int i = 0; i < RI; ++i) kr[i] = __builtin_amdgcn_raw_buffer_load_b128(kp, roff(i), 0, 0);
+#pragma unroll
+      for (int i = 0; i < RI; ++i) {
+        float x[8];
+        bf16x8(kr[i], x);
+        int qc = c;
+        asm volatile("" : "+v"(qc));
+        float dots[NH];
+#pragma unroll
+        for (int j = 0; j < NH; ++j) {
+          const float4 q0 = W.q[wave][j][qc][0], q1 = W.q[wave][j][qc][1];
+          const float qq[8] = {q0.x, q0.y, q0.z, q0.w, q1.x, q1.y, q1.z, q1.w};
+          dots[j] = 0.0f;
+#pragma unroll
+          for (int k = 0; k < 8; ++k) dots[j] = __builtin_fmaf(qq[k], x[k], dots[j]);
+        }
+#pragma unroll
+        for (int j = 0; j < NH; ++j) {   // sum over the 16 lanes of the row (rotations by 8, 4, 2, 1)
+          dots[j] += dpp_row_ror<0x128>(dots[j]);
+          dots[j] += dpp_row_ror<0x124>(dots[j]);
+          dots[j] += dpp_row_ror<0x122>(dots[j]);
+          dots[j] += dpp_row_ror<0x121>(dots[j]);
+        }
+        if (c == 0)
+#pragma unroll
+          for (int j = 0; j < NH; ++j) W.sc[wave][j][tq + 4 * i] = dots[j];
+        __builtin_amdgcn_sched_barrier(0);   // one row at a time
+      }
+    }
+    // this pass's V rows, in flight during the softmax
+    u4 vr[RI];
+#pragma unroll
+    for (int i = 0; i < RI; ++i) vr[i] = __builtin_amdgcn_raw_buffer_load_b128(vp, roff(i), 0, 0);
+    __syncthreads();
+    if (wave < NH && lane < PT) {  // online softmax update, wave j for head j
+      const int j = wave;
+      const float sv = lane < n ? ((W.sc[0][j][lane] + W.sc[1][j][lane]) + W.sc[2][j][lane]) + W.sc[3][j][lane]
+                                : NEG_INF;
+      const float mold = W.wm[j];
+      float mx = sv;
+#pragma unroll
+      for (int o2 = 16; o2 > 0; o2 >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o2));
+      const float mnew = fmaxf(mold, mx);
+      const float p = (sv == NEG_INF) ? 0.0f : exp2f(sv - mnew);
+      float l = p;
+#pragma unroll
+      for (int o2 = 16; o2 > 0; o2 >>= 1) l += __shfl_xor(l, o2);
+      W.p[j][lane] = p;
+      if (lane == 0) {
+        const float alpha = (mold == NEG_INF) ? 0.0f : exp2f(mold - mnew);
+        W.wa[j] = alpha;
+        W.wm[j] = mnew;
+        W.wl[j] = W.wl[j] * alpha + l;
+      }
+    }
+    __syncthreads();
+    {  // PV over this slice
+#pragma unroll
+      for (int j = 0; j < NH; ++j) {
+        const float al = W.wa[j];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) o[j][k] *= al;
+      }
+#pragma unroll
+      for (int i = 0; i < RI; ++i) {
+        const int tk = tq + 4 * i;
+        float x[8];
+        bf16x8(vr[i], x);
+#pragma unroll
+        for (int j = 0; j < NH; ++j) {
+          const float p = tk < n ? W.p[j][tk] : 0.0f;
+#pragma unroll
+          for (int k = 0; k < 8; ++k) o[j][k] = __builtin_fmaf(p, x[k], o[j][k]);
+        }
+        __builtin_amdgcn_sched_barrier(0);   // one row's conversions at a time
+      }
+    }
+    __syncthreads();
+  }
+#pragma unroll
+  for (int j = 0; j < NH; ++j)
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      o[j][k] += __shfl_xor(o[j][k], 16);
+      o[j][k] += __shfl_xor(o[j][k], 32);
+    }
+  const int slot = a.win.slot0 + wblk;
+  if (tq == 0)
+#pragma unroll
+    for (int j = 0; j < NH; ++j) {
+      if (j >= a.Gq) break;
+      float* dst = a.partials + (((size_t)b * a.Hq + h * a.Gq + j) * kMaxSplits + slot) * (D + 2);
+#pragma unroll
+      for (int k = 0; k < 8; ++k) dst[col + k] = o[j][k];
+      if (wave == 0 && c == 0) {
+        dst[D] = W.wm[j];
+        dst[D + 1] = W.wl[j];
+      }
+    }
+}
+
+// INT2 streams of wave `wave`'s slice (quantization group) of one (sequence,
+// kv head): K code chunks 2 wave and 2 wave + 1 of every 8 KiB tile, the
+// group's scale|zero words, the slice's 2 KiB V code tile.
+__device__ inline TileStreams wide_tile_streams(const DecodeArgs& a, int bh, int wave) {
+  constexpr int D = 512;
+  TileStreams s;
+  s.kc = plane_rsrc(a.k.codes + kcode_byte(bh, a.cap, 0, 0, D), a.cap * 128);
+  s.km = plane_rsrc(a.k.meta + meta_index(bh, a.cap, 0, wave, D), a.cap * 4);
+  s.vm = plane_rsrc(a.v.meta + meta_index(bh, a.cap, 0, wave, D), a.cap * 4);
+  s.vc = plane_rsrc(a.v.codes + (size_t)bh * (a.cap / kTile) * (4 * 2048), a.cap * 128);
+  return s;
+}
+
+// Loads of tile t0 for one slice: lane_k = 2048 wave + 16 lane (K chunk
+// 2 wave), lane_v = 2048 wave + 16 lane (V slice tile), lane_m = 16 blk.
+__device__ inline TileRegs wide_load_tile(const TileStreams& s, int t0, int lane_c, int lane_m) {
+  const int oc = t0 * 128, om = t0 * 4;
+  TileRegs r;
+  r.k0 = __builtin_amdgcn_raw_buffer_load_b128(s.kc, lane_c, oc, kStreamOnce);
+  r.k1 = __builtin_amdgcn_raw_buffer_load_b128(s.kc, lane_c + 1024, oc, kStreamOnce);
+  r.km = __builtin_amdgcn_raw_buffer_load_b128(s.km, lane_m, om, 0);
+  r.vm = __builtin_amdgcn_raw_buffer_load_b128(s.vm, lane_m, om, 0);
+  r.v0 = __builtin_amdgcn_raw_buffer_load_b128(s.vc, lane_c, oc, kStreamOnce);
+  r.v1 = __builtin_amdgcn_raw_buffer_load_b128(s.vc, lane_c + 1024, oc, kStreamOnce);
+  return r;
+}
+
+// Grid: (sequence x kv head, plan.splits INT2 splits + win_blocks window
+// blocks).  NH: query heads per kv head rounded up to 2 or 4 (the window
+// blocks' register arrays; the matrix-core part always has 4 columns).
+template <int NH>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4, 4)))
+void decode_wide_kernel(DecodeArgs a) {
+  constexpr int D = 512;
+  const int bh = blockIdx.x;
+  const int b = bh / a.Hkv, h = bh - (bh / a.Hkv) * a.Hkv;
+  __shared__ WideSmem W;
+  const int y = (int)blockIdx.y;
+  if (y >= a.plan.splits) {
+    wide_window_block<NH>(a, bh, b, h, y - a.plan.splits, W);
+    return;
+  }
+  const int split = y;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+  const int blk = lane >> 2, j = lane & 3;
+  const int lo = a.plan.a0, hi = a.plan.b0;
+  const int tile_first = lo >> 6;
+  const int ntiles = ((hi - 1) >> 6) - tile_first + 1;
+  auto split_start = [&](int s) -> int {
+    const int S = a.plan.splits;
+    if (s >= S) return ntiles;
+    const float fs = (float)s, al = a.split_ramp;
+    const float F = (fs * (1.0f + al) - al * fs * (fs - 1.0f) / (float)max(S - 1, 1)) / (float)S;
+    return min(ntiles, (int)(F * (float)ntiles));
+  };
+  const int s_t0 = split_start(split);
+  const int s_t1 = split_start(split + 1);
+  const int t_last = max(s_t1 - 1, 0);
+  const TileStreams st = wide_tile_streams(a, bh, wave);
+  const int lane_c = 2048 * wave + lane * 16, lane_m = blk * 16;
+  auto tile_t0 = [&](int ti) { return (tile_first + ti) << 6; };
+  TileRegs r[kDepth];
+#pragma unroll
+  for (int k = 0; k < kDepth; ++k) r[k] = wide_load_tile(st, tile_t0(min(s_t0 + k, t_last)), lane_c, lane_m);
+
+  // this slice's q operands (written by the rotation launch before this one)
+  h4 qv[1][8];
+  float qsum;
+  int eq;
+  {
+    const __amdgpu_buffer_rsrc_t qr = plane_rsrc(a.qpub + (size_t)(bh * 4 + wave) * kQPub, kQPub * 4);
+    const int vbase = (kQPubOps + 16 * (4 * (lane >> 4) + j)) * 4;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const u4 wv = __builtin_amdgcn_raw_buffer_load_b128(qr, vbase + 16 * i, 0, 0);
+      qv[0][2 * i] = as_h4(wv.x, wv.y);
+      qv[0][2 * i + 1] = as_h4(wv.z, wv.w);
+    }
+    qsum = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(qr, (512 + j) * 4, 0, 0));
+    eq = (int)__builtin_amdgcn_raw_buffer_load_b32(qr, (516 + j) * 4, 0, 0);
+  }
+  const float cK = ldexpf(1.0f, 24 - eq);
+  const float zq = ldexpf(qsum, eq - 24);
+  const float vmax = a.v.smax[bh];
+  int ev2 = 0;
+  if (vmax > 0.0f) frexpf(vmax, &ev2);
+  const int ev = (vmax > 0.0f) ? min(15 - ev2, 60) : 0;
+  const int kA = ev - 4 * (blk & 1);
+  const float kAf = (float)kA;
+  const float cV = ldexpf(1.0f, 24 - ev);
+
+  f4 o0[1] = {{0, 0, 0, 0}}, o1[1] = {{0, 0, 0, 0}};
+  float m = NEG_INF, lA = 0.0f, lB = 0.0f, pzA = 0.0f, pzB = 0.0f;
+  float cA = 0.0f, cB = 0.0f;
+
+  // one 64-token tile: this slice's QK^T, the four slices' scores summed in
+  // shared memory (fixed order, identical in every wave), the online softmax
+  // (the same in every wave), this slice's PV
+  auto process = [&](const TileRegs& cur, int t0, int buf) {
+    f4 sa[1] = {{0, 0, 0, 0}};
+    qk_word<1>(cur.k0.x, qv, 0, sa);
+    qk_word<1>(cur.k0.y, qv, 1, sa);
+    qk_word<1>(cur.k0.z, qv, 2, sa);
+    qk_word<1>(cur.k0.w, qv, 3, sa);
+    qk_word<1>(cur.k1.x, qv, 4, sa);
+    qk_word<1>(cur.k1.y, qv, 5, sa);
+    qk_word<1>(cur.k1.z, qv, 6, sa);
+    qk_word<1>(cur.k1.w, qv, 7, sa);
+    PHASE_FENCE();
+    const uint32_t kmr[4] = {cur.km.x, cur.km.y, cur.km.z, cur.km.w};
+    const uint32_t vmr[4] = {cur.vm.x, cur.vm.y, cur.vm.z, cur.vm.w};
+    f4 part;
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+      part[r] = cK * __builtin_fmaf(hi_half(kmr[r]), zq, __builtin_fmaf(lo_half(kmr[r]), sa[0][r], 0.0f));
+    W.u[buf][wave][lane] = part;
+    __syncthreads();
+    f4 u = ((W.u[buf][0][lane] + W.u[buf][1][lane]) + W.u[buf][2][lane]) + W.u[buf][3][lane];
+    if (t0 < lo || t0 + 64 > hi) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int t = t0 + 4 * blk + r;
+        if (t < lo || t >= hi) u[r] = NEG_INF;
+      }
+    }
+    const float tmax = fmaxf(fmaxf(u[0], u[1]), fmaxf(u[2], u[3]));
+    if (__any(tmax > m)) {
+      const float mnew = fmaxf(m, head_max(tmax));
+      const float alpha = __builtin_amdgcn_exp2f(m - mnew);
+      lA *= alpha;
+      lB *= alpha;
+      pzA *= alpha;
+      pzB *= alpha;
+      const f4 al = {lane_value(alpha, 0), lane_value(alpha, 1), lane_value(alpha, 2), lane_value(alpha, 3)};
+      o0[0] *= al;
+      o1[0] *= al;
+      m = mnew;
+      cA = kAf - m;
+      cB = cA - 2.0f;
+    }
+    float p[4];
+    p[0] = __builtin_amdgcn_exp2f(u[0] + cA);
+    p[1] = __builtin_amdgcn_exp2f(u[1] + cA);
+    p[2] = __builtin_amdgcn_exp2f(u[2] + cB);
+    p[3] = __builtin_amdgcn_exp2f(u[3] + cB);
+    lA += p[0] + p[1];
+    lB += p[2] + p[3];
+    pzA = __builtin_fmaf(p[0], hi_half(vmr[0]), __builtin_fmaf(p[1], hi_half(vmr[1]), pzA));
+    pzB = __builtin_fmaf(p[2], hi_half(vmr[2]), __builtin_fmaf(p[3], hi_half(vmr[3]), pzB));
+    const h4 pv1[1] = {h4{(_Float16)__builtin_fmaf(lo_half(vmr[0]), p[0], 0.0f),
+                          (_Float16)__builtin_fmaf(lo_half(vmr[1]), p[1], 0.0f),
+                          (_Float16)__builtin_fmaf(lo_half(vmr[2]), p[2], 0.0f),
+                          (_Float16)__builtin_fmaf(lo_half(vmr[3]), p[3], 0.0f)}};
+    PHASE_FENCE();
+    pv_word<1, 0>(cur.v0.x, pv1, o0, o1);
+    pv_word<1, 1>(cur.v0.y, pv1, o0, o1);
+    pv_word<1, 2>(cur.v0.z, pv1, o0, o1);
+    pv_word<1, 3>(cur.v0.w, pv1, o0, o1);
+    pv_word<1, 4>(cur.v1.x, pv1, o0, o1);
+    pv_word<1, 5>(cur.v1.y, pv1, o0, o1);
+    pv_word<1, 6>(cur.v1.z, pv1, o0, o1);
+    pv_word<1, 7>(cur.v1.w, pv1, o0, o1);
+  };
+
+  int buf = 0;
+  for (int ti = s_t0; ti < s_t1; ti += kDepth) {
+#pragma unroll
+    for (int k = 0; k < kDepth; ++k) {
+      const int t = ti + k;
+      if (t >= s_t1) break;
+      process(r[k], tile_t0(t), buf);
+      buf ^= 1;
+      if (t + kDepth < s_t1) r[k] = wide_load_tile(st, tile_t0(t + kDepth), lane_c, lane_m);
+    }
+  }
+
+  const float l = head_sum(ldexpf(__builtin_fmaf(4.0f, lB, lA), -kA));
+  const float pz = head_sum(ldexpf(__builtin_fmaf(4.0f, pzB, pzA), -kA));
+  const float pzr[4] = {lane_value(pz, 0), lane_value(pz, 1), lane_value(pz, 2), lane_value(pz, 3)};
+  const int slot = a.plan.slot0 + split;
+#pragma unroll
+  for (int r2 = 0; r2 < 4; ++r2) {
+    if (r2 >= a.Gq) break;
+    float* dst = a.partials + (((size_t)b * a.Hq + h * a.Gq + r2) * kMaxSplits + slot) * (D + 2);
+    dst[128 * wave + 4 * blk + j] = __builtin_fmaf(o0[0][r2], cV, pzr[r2]);
+    dst[128 * wave + 64 + 4 * blk + j] = __builtin_fmaf(o1[0][r2], cV, pzr[r2]);
+    if (wave == 0 && lane == r2) {
+      dst[D] = m;
+      dst[D + 1] = l;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
 // launchers
 // ---------------------------------------------------------------------------
 
@@ -1483,6 +1932,20 @@ hipError_t launch_decode_mfma(const DecodeArgs& a, int B, int waves_per_block, h
     hipLaunchKernelGGL((decode_mfma_kernel<4, 2>), grid, dim3(256), 0, s, a);
   else
     hipLaunchKernelGGL((decode_mfma_kernel<4, 1>), grid, dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_wide_qrot(const DecodeArgs& a, int B, hipStream_t s) {
+  hipLaunchKernelGGL(wide_qrot_kernel, dim3((unsigned)(B * a.Hkv), 4), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_decode_wide(const DecodeArgs& a, int B, hipStream_t s) {
+  dim3 grid((unsigned)(B * a.Hkv), (unsigned)(a.plan.splits + a.win_blocks));
+  if (a.Gq <= 2)
+    hipLaunchKernelGGL(decode_wide_kernel<2>, grid, dim3(256), 0, s, a);
+  else
+    hipLaunchKernelGGL(decode_wide_kernel<4>, grid, dim3(256), 0, s, a);
   return hipGetLastError();
 }
 

@@ -270,6 +270,15 @@ int do_append(oscar_kv* kv, int32_t layer, const void* k, const void* v, int32_t
 #define OSCAR_WIN_TOKENS 192
 #endif
 constexpr int kWinTokens = OSCAR_WIN_TOKENS;
+// head_dim 512: bf16 window tokens per window block, INT2 blocks per launch
+#ifndef OSCAR_WIDE_WIN_TOKENS
+#define OSCAR_WIDE_WIN_TOKENS 256
+#endif
+#ifndef OSCAR_WIDE_TARGET_BLOCKS
+#define OSCAR_WIDE_TARGET_BLOCKS 1536
+#endif
+constexpr int kWideWinTokens = OSCAR_WIDE_WIN_TOKENS;
+constexpr int kWideTargetBlocks = OSCAR_WIDE_TARGET_BLOCKS;
 
 // Linear fall of INT2 split sizes from the first split to the last: blocks
 // dispatched later start later, so they get less.  At the 32k shape 0.4
@@ -353,7 +362,9 @@ int oscar_kv_create(const oscar_kv_config* cfg, oscar_kv** out) {
     return bail(fail(OSCAR_ERR_HIP, "copy of rotations failed"));
   const size_t B = cfg->max_batch, Hq = cfg->num_q_heads, Hkv = cfg->num_kv_heads;
   if ((rc = dev_alloc(kv, (void**)&kv->qrot, B * Hq * D * 4))) return bail(rc);
-  if ((rc = dev_alloc(kv, (void**)&kv->qpub, B * std::max(Hkv, Hq / 4) * kQPub * 4))) return bail(rc);
+  // q records: one per 4 query heads (head_dim 128), one per 128-dim slice (head_dim 512)
+  const size_t qrecs = std::max(std::max(Hkv, Hq / 4), D == 512 ? 4 * Hkv : (size_t)0);
+  if ((rc = dev_alloc(kv, (void**)&kv->qpub, B * qrecs * kQPub * 4))) return bail(rc);
   if ((rc = dev_alloc(kv, (void**)&kv->qflag, B * Hkv * sizeof(unsigned)))) return bail(rc);
   if (hipMemset(kv->qflag, 0, B * Hkv * sizeof(unsigned)) != hipSuccess)
     return bail(fail(OSCAR_ERR_HIP, "clearing the q flags failed"));
@@ -402,6 +413,15 @@ bool fast_shape(const oscar_kv* kv) {
   return kv->decode_impl == 0 && c.head_dim == 128 &&
          (c.num_q_heads == 4 * c.num_kv_heads || c.num_q_heads == 8 * c.num_kv_heads) &&
          c.k_dtype == OSCAR_KV_INT2 && c.v_dtype == OSCAR_KV_INT2 && (long long)kv->cap * 32 <= INT32_MAX;
+}
+
+// head_dim 512 with at most 4 query heads per kv head, INT2 K and V: the
+// three-launch matrix-core path (32-bit buffer offsets: cap * 128 bytes must fit)
+bool wide_shape(const oscar_kv* kv) {
+  const auto& c = kv->cfg;
+  const int gq = c.num_q_heads / c.num_kv_heads;
+  return kv->decode_impl == 0 && c.head_dim == 512 && (gq == 1 || gq == 2 || gq == 4) &&
+         c.k_dtype == OSCAR_KV_INT2 && c.v_dtype == OSCAR_KV_INT2 && (long long)kv->cap * 128 <= INT32_MAX;
 }
 
 int check_decode_args(const oscar_kv* kv, int32_t layer, const void* q, void* out, int32_t out_dtype,
@@ -505,6 +525,41 @@ int launch_decode(oscar_kv* kv, int32_t layer, const void* q, void* out, int32_t
     const long pk = prof_begin(kv, 0, stream);
     HIP_TRY(launch_decode_mfma(da, batch, kv->mfma_waves, stream));
     prof_end(kv, 0, pk, stream);
+  } else if (wide_shape(kv)) {
+    // q rotation records, then INT2 splits + bf16 window blocks, then the merge
+    SegPlan w{};
+    w.a0 = 0;
+    w.b0 = sink_end;
+    w.a1 = rec_begin;
+    w.b1 = T;
+    const int len0 = sink_end, len1 = T - rec_begin;
+    int chunk = kWideWinTokens;
+    auto nwin = [&](int ch) { return (len0 + ch - 1) / ch + (len1 + ch - 1) / ch; };
+    while (nwin(chunk) > kMaxWinSplits) chunk *= 2;
+    w.chunk = chunk;
+    w.splits = nwin(chunk);
+    w.slot0 = 0;
+    SegPlan p{};
+    if (int2_hi > int2_lo) {
+      const int ntiles = ((int2_hi - 1) >> 6) - (int2_lo >> 6) + 1;
+      int s = kv->forced_splits > 0 ? kv->forced_splits : std::max(1, kWideTargetBlocks / std::max(1, BH));
+      s = std::max(1, std::min(s, std::min(ntiles, kMaxSplits - kMaxWinSplits)));
+      p.a0 = int2_lo;
+      p.b0 = int2_hi;
+      p.splits = s;
+    }
+    p.slot0 = w.splits;
+    da.plan = p;
+    da.win = w;
+    da.win_blocks = w.splits;
+    da.ring0 = M > 0 ? rec_begin % M : 0;
+    da.split_ramp = 0.0f;
+    ca.nslots = p.splits + w.splits;
+    HIP_TRY(launch_wide_qrot(da, batch, stream));
+    const long pk = prof_begin(kv, 0, stream);
+    HIP_TRY(launch_decode_wide(da, batch, stream));
+    prof_end(kv, 0, pk, stream);
+    HIP_TRY(launch_combine(ca, stream));
   } else {
     QRotArgs qa{};
     qa.q = static_cast<const uint16_t*>(q);
@@ -666,9 +721,17 @@ int oscar_kv_export(oscar_kv* kv, int32_t layer, int32_t which, void* host_codes
     (void)hipFree(tmp);
     HIP_TRY(e);
   }
-  if (host_meta && T > 0)
-    HIP_TRY(hipMemcpy2D(host_meta, (size_t)T * (D / kGroup) * 4, p.meta, (size_t)cap * (D / kGroup) * 4,
-                        (size_t)T * (D / kGroup) * 4, BH, hipMemcpyDeviceToHost));
+  if (host_meta && T > 0) {
+    // stored group-major [BH][D/128][cap]; the export is [BH][T][D/128]
+    const int G = D / kGroup;
+    std::vector<uint32_t> tmp((size_t)BH * G * T);
+    HIP_TRY(hipMemcpy2D(tmp.data(), (size_t)T * 4, p.meta, (size_t)cap * 4, (size_t)T * 4, (size_t)BH * G,
+                        hipMemcpyDeviceToHost));
+    uint32_t* dst = static_cast<uint32_t*>(host_meta);
+    for (size_t bh = 0; bh < (size_t)BH; ++bh)
+      for (int g = 0; g < G; ++g)
+        for (int t = 0; t < T; ++t) dst[(bh * T + t) * G + g] = tmp[(bh * G + g) * T + t];
+  }
   if (host_sink && c.sink_tokens > 0)
     HIP_TRY(hipMemcpy(host_sink, p.sink, (size_t)BH * c.sink_tokens * D * 2, hipMemcpyDeviceToHost));
   if (host_ring && c.recent_tokens > 0)

@@ -251,16 +251,36 @@ def test_decode_window_edges(ok, T, N, M):
     gc.close()
 
 
+@pytest.mark.parametrize("T,N,M,gq", [
+    (1, 64, 256, 2), (40, 64, 256, 2), (321, 64, 256, 2), (700, 300, 300, 2), (1000, 0, 256, 2),
+    (1000, 64, 0, 2), (1000, 0, 0, 1), (777, 13, 29, 4), (64, 0, 0, 2), (65, 1, 0, 1), (2000, 40, 600, 2),
+])
+def test_decode_wide_window_edges(ok, T, N, M, gq):
+    """head_dim 512 (three-launch matrix-core path) at the window edges, the
+    ring past its wrap, 1, 2 and 4 query heads per kv head; the VALU kernel on
+    the same cache as a second check."""
+    shape = Shape(B=2, Hq=2 * gq, Hkv=2, D=512, N=N, M=M)
+    say(f"[decode wide edges] T={T} N={N} M={M} gq={gq}")
+    gc, rk, rv, k, v, mask = _fill(ok, shape, T, chunks=[T // 2, T - T // 2] if T > 1 else None)
+    qb = query(shape, mask)
+    want = oracle_on_exported(gc, 0, qb, shape, rk, rv)
+    for impl in (0, 1):
+        e = rel_l2(_decode(ok, gc, 0, qb, impl=impl), want)
+        say(f"  impl={impl} rel L2 {e:.3e}")
+        assert e <= ATTN_TOL
+    gc.close()
+
+
 @pytest.mark.parametrize("impl,tol", [
     (1, 1e-5),        # VALU kernel: fp32 throughout, only summation order changes
     (0, 2 ** -12),    # matrix-core kernel: p*s_V enters as fp16 relative to each
                       # split's running max, so splits move its rounding points;
                       # bounded by fp16's half-ulp
 ])
-@pytest.mark.parametrize("gq", [4, 8])
-def test_split_invariance(ok, impl, tol, gq):
-    shape = Shape(B=2, Hq=2 * gq, Hkv=2, N=64, M=256)
-    say(f"[split invariance] impl={impl} gq={gq}")
+@pytest.mark.parametrize("gq,D", [(4, 128), (8, 128), (2, 512)])
+def test_split_invariance(ok, impl, tol, gq, D):
+    shape = Shape(B=2, Hq=2 * gq, Hkv=2, D=D, N=64, M=256)
+    say(f"[split invariance] impl={impl} gq={gq} D={D}")
     gc, rk, rv, k, v, mask = _fill(ok, shape, 5000)
     qb = query(shape, mask)
     ref = _decode(ok, gc, 0, qb, impl=impl, splits=1)
@@ -523,6 +543,32 @@ def test_full_size_128k_gqa8_sampled(ok):
     say(f"  step vs attention call: {rel_l2(got_step, got):.2e}")
     assert rel_l2(got_step, got) <= 2 ** -12
     for b in (0, 7):
+        want = oracle_on_exported(gc, 0, qb, shape, rk, rv, batch_idx=slice(b, b + 1))
+        e = rel_l2(got[b:b + 1], want)
+        say(f"  seq {b}: rel L2 {e:.3e}")
+        assert e <= ATTN_TOL
+    gc.close()
+
+
+@pytest.mark.slow
+def test_full_size_wide_64k_sampled(ok):
+    """The wide-head shape (B=4, Hq=16, Hkv=8, D=512, N=512, M=2048) at 64k
+    context on one layer, filled on the device, decoded in the benchmark's
+    launch configuration; sequences 0 and 3 checked against the oracle over
+    the exported cache."""
+    from bench import fill_layer_device
+    shape = Shape(B=4, Hq=16, Hkv=8, D=512, N=512, M=2048, outliers="percent")
+    T = 65536
+    say("[full wide 64k] filling")
+    rk, rv = make_rotations(shape, "haar")
+    gc = gpu_cache(ok, shape, rk, rv, T + 64)
+    fill_layer_device(gc, 0, shape.B, shape.Hkv, shape.D, T, seed=0, dist="normal", outliers="percent")
+    mask = synth.outlier_mask(shape.D, shape.Hkv, 0, 0, "percent")
+    k1, v1, _ = inputs(shape, 1, chunk=99)
+    qb = query(shape, mask, step=1)
+    _step(ok, gc, 0, k1, v1, qb)
+    got = _decode(ok, gc, 0, qb)
+    for b in (0, 3):
         want = oracle_on_exported(gc, 0, qb, shape, rk, rv, batch_idx=slice(b, b + 1))
         e = rel_l2(got[b:b + 1], want)
         say(f"  seq {b}: rel L2 {e:.3e}")
