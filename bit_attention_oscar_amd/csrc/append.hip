@@ -19,6 +19,13 @@ __global__ __launch_bounds__(64 * WAVES) void append_kernel(AppendArgs a) {
   append_block<D, WAVES, NT>(a, (int)blockIdx.x, blockIdx.z != 0, t_lo, t_hi, xs, part);
 }
 
+// One-token append at head_dim 512: grid (sequence x kv head, group, K/V).
+__global__ __launch_bounds__(256) void append_one_wide_kernel(AppendArgs a) {
+  __shared__ float xs[512];
+  __shared__ float part[4 * 128];
+  append_slice_block(a, (int)blockIdx.x, blockIdx.z != 0, (int)blockIdx.y, xs, part);
+}
+
 // Test hook: the same quantizer on fp32 rows, canonical packing.
 template <int D>
 __global__ __launch_bounds__(64) void quantize_rows_kernel(const float* x, float clip, uint8_t* codes,
@@ -73,6 +80,42 @@ __global__ __launch_bounds__(256) void stream_copy_kernel(const uint4* src, uint
     dst[i] = src[i];
 }
 
+// Read-only streaming: XOR of every 16-byte word (non-temporal loads, eight in
+// flight per thread), folded per block into *out with one atomic XOR.
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+__global__ __launch_bounds__(256) void stream_read_kernel(const u32x4* __restrict__ src, size_t n,
+                                                          unsigned* out) {
+  constexpr int U = 8;
+  const size_t stride = (size_t)gridDim.x * blockDim.x;
+  size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x;
+  unsigned acc = 0;
+  for (; i + (U - 1) * stride < n; i += U * stride) {
+    u32x4 v[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) v[u] = __builtin_nontemporal_load(src + i + u * stride);
+#pragma unroll
+    for (int u = 0; u < U; ++u) acc ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
+  }
+  for (; i < n; i += stride) {
+    const u32x4 v = src[i];
+    acc ^= v.x ^ v.y ^ v.z ^ v.w;
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) acc ^= __shfl_xor(acc, o);
+  __shared__ unsigned wacc[4];
+  if ((threadIdx.x & 63) == 0) wacc[threadIdx.x >> 6] = acc;
+  __syncthreads();
+  if (threadIdx.x == 0) atomicXor(out, (wacc[0] ^ wacc[1]) ^ (wacc[2] ^ wacc[3]));
+}
+
+hipError_t launch_stream_read(const void* src, size_t bytes, unsigned* out, hipStream_t s) {
+  const size_t n = bytes / 16;
+  if (n == 0) return hipSuccess;
+  const unsigned blocks = (unsigned)std::min<size_t>((n + 255) / 256, 256 * 32);
+  hipLaunchKernelGGL(stream_read_kernel, dim3(blocks), dim3(256), 0, s, static_cast<const u32x4*>(src), n, out);
+  return hipGetLastError();
+}
+
 hipError_t launch_stream_copy(const void* src, void* dst, size_t bytes, hipStream_t s) {
   const size_t n = bytes / 16;
   if (n == 0) return hipSuccess;
@@ -93,7 +136,7 @@ hipError_t launch_append(const AppendArgs& a, hipStream_t s) {
       hipLaunchKernelGGL((append_kernel<128, 4, 8>), grid, dim3(256), 0, s, a);
   } else {
     if (one)
-      hipLaunchKernelGGL((append_kernel<512, 4, 1>), grid, dim3(256), 0, s, a);
+      hipLaunchKernelGGL(append_one_wide_kernel, dim3((unsigned)(a.batch * a.Hkv), 4, 2), dim3(256), 0, s, a);
     else
       hipLaunchKernelGGL((append_kernel<512, 1, 8>), grid, dim3(64), 0, s, a);
   }

@@ -275,4 +275,107 @@ __device__ inline void append_block(const AppendArgs& a, int bh, bool isv, int t
   }
 }
 
+// acc[j][c] += xs[j * xstride + e] * R[e][col + c] for e in [e0, e0 + EW)
+// ascending (fused multiply-adds), c = 0, 1: one lane's share of a wave's
+// part of a rotation whose reduction over e is split across waves.  The two
+// columns are one 8-byte load per row; rows are loaded 32 at a time (one
+// memory round trip per 32 rows).
+template <int NX, int D, int EW = 128>
+__device__ inline void rot_rows_cols2(const float* xs, int xstride, const float* R, int e0, int col,
+                                      float (&acc)[NX][2]) {
+  static_assert(EW % 32 == 0, "rows in batches of 32");
+  const float* Rp = R + (size_t)e0 * D + col;
+#pragma unroll 1
+  for (int eb = 0; eb < EW; eb += 32) {
+    float2 r[32];
+#pragma unroll
+    for (int e = 0; e < 32; ++e) r[e] = *reinterpret_cast<const float2*>(Rp + (size_t)(eb + e) * D);
+#pragma unroll
+    for (int e = 0; e < 32; ++e)
+#pragma unroll
+      for (int j = 0; j < NX; ++j) {
+        const float x = xs[j * xstride + e0 + eb + e];
+        acc[j][0] = __builtin_fmaf(x, r[e].x, acc[j][0]);
+        acc[j][1] = __builtin_fmaf(x, r[e].y, acc[j][1]);
+      }
+  }
+}
+
+// One-token append, head_dim 512, split by quantization group: the block
+// computes dims [128 s, 128 s + 128) (group s) of one token row of plane K
+// (isv = false) or V for one (sequence, kv head).  The rotation is the one of
+// rotate_rows<512, 4, 1> for those dims (same waves, same order, same bits);
+// the group's statistics, codes, scale|zero word and window values follow.
+// Blocks of different groups touch disjoint bytes of every plane.  xs holds
+// 512 floats and part 4 * 128 floats of shared memory.
+__device__ inline void append_slice_block(const AppendArgs& a, int bh, bool isv, int s, float* xs, float* part) {
+  constexpr int D = 512;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int b = bh / a.Hkv, h = bh - (bh / a.Hkv) * a.Hkv;
+  const PlaneDev P = isv ? a.v : a.k;
+  const uint16_t* in = isv ? a.vin : a.kin;
+  const float* R = isv ? a.rv : a.rk;
+  float* dump = isv ? a.vdump : a.kdump;
+  const int t = a.T_old;
+  const size_t in_base = ((size_t)b * a.n_new * a.Hkv + h) * D;   // n_new == 1
+  for (int i = tid; i < D; i += 256) xs[i] = bf16_to_f32(in[in_base + i]);
+  __syncthreads();
+  // lane computes columns 2 lane, 2 lane + 1 of the group's 128
+  float acc[1][2] = {{0.0f, 0.0f}};
+  rot_rows_cols2<1, D>(xs, 0, R, wave * 128, 128 * s + 2 * lane, acc);
+  part[wave * 128 + 2 * lane] = acc[0][0];
+  part[wave * 128 + 2 * lane + 1] = acc[0][1];
+  __syncthreads();
+  if (wave != 0) return;
+  float x[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int d = lane + 64 * i;
+    x[i] = (((part[d] + part[128 + d]) + part[256 + d]) + part[384 + d]) + 0.0f;
+  }
+  const int d0 = 128 * s + lane;      // dims d0 and d0 + 64 of the row
+  if (dump) {
+    const size_t base = ((size_t)b * a.n_new * a.Hkv + h) * D;
+    dump[base + d0] = x[0];
+    dump[base + d0 + 64] = x[1];
+  }
+  if (P.is_bf16) {
+    const size_t base = row_offset(bh, a.cap, t, D);
+    P.full[base + d0] = f32_to_bf16(x[0]);
+    P.full[base + d0 + 64] = f32_to_bf16(x[1]);
+    return;
+  }
+  if (t < a.N) {
+    const size_t base = row_offset(bh, a.N, t, D);
+    P.sink[base + d0] = f32_to_bf16(x[0]);
+    P.sink[base + d0 + 64] = f32_to_bf16(x[1]);
+  }
+  if (a.M > 0 && t >= a.N && t >= a.T_new - a.M) {
+    const size_t base = row_offset(bh, a.M, t % a.M, D);
+    P.ring[base + d0] = f32_to_bf16(x[0]);
+    P.ring[base + d0 + 64] = f32_to_bf16(x[1]);
+  }
+  const float mx = wave_max(fmaxf(x[0], x[1]));
+  const float mn = wave_min(fminf(x[0], x[1]));
+  const GroupQ q = group_params(mx, mn, P.clip);
+  const uint32_t code[2] = {quant_code(x[0], q), quant_code(x[1], q)};
+  if (lane == 0) {
+    P.meta[meta_index(bh, a.cap, t, s, D)] = q.packed;
+    if (P.smax) atomicMax(reinterpret_cast<unsigned int*>(P.smax + bh), __float_as_uint(q.sf));
+  }
+  if (!P.tiled) {
+    store_canonical<2>(code, lane, [&](int w) {
+      return reinterpret_cast<uint32_t*>(P.codes + kcode_byte(bh, a.cap, t, 32 * s + 4 * w, D));
+    });
+  } else {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      int bit;
+      const size_t off = vcode_byte(bh, a.cap, t, d0 + 64 * i, D, &bit);
+      const uint8_t old = P.codes[off];
+      P.codes[off] = (uint8_t)((old & ~(3u << bit)) | (code[i] << bit));
+    }
+  }
+}
+
 }  // namespace oscar

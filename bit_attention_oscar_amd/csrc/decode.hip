@@ -52,6 +52,9 @@ typedef float f4 __attribute__((ext_vector_type(4)));
 #ifndef OSCAR_TILE_DEPTH
 #define OSCAR_TILE_DEPTH 2
 #endif
+#ifndef OSCAR_WIDE_WIN_FIRST
+#define OSCAR_WIDE_WIN_FIRST 1
+#endif
 constexpr int kDepth = OSCAR_TILE_DEPTH;
 
 __device__ inline float wmax(float v) {
@@ -379,17 +382,22 @@ __device__ inline float ld_partial(const float* p) {
   return *p;
 }
 
-template <int D, bool COHERENT = false>
-__device__ void combine_group(const CombineArgs& a, int bh) {
-  constexpr int PER = D / 64;
+// CC > 1: the block computes output columns [cc D / CC, (cc + 1) D / CC) only
+// (it still merges every dim of o', which the un-rotation reduces over).
+template <int D, bool COHERENT = false, int CC = 1>
+__device__ void combine_group(const CombineArgs& a, int bh, int cc = 0) {
+  constexpr int NC = D / CC;          // output columns of the block
+  constexpr int PER = NC / 64;
   constexpr int EW = D / 4;
+  static_assert(NC % 64 == 0, "column chunk");
+  const int c0 = cc * NC;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int b = bh / a.Hkv, kvh = bh - (bh / a.Hkv) * a.Hkv;
   const int Gq = a.Hq / a.Hkv;
   __shared__ float wsl[4][kMaxSplits];
   __shared__ float linv[4];
   __shared__ float os[4][D];
-  __shared__ float part[4][4][D];
+  __shared__ float part[4][4][NC];
   for (int hc = 0; hc < Gq; hc += 4) {
     const int nh = min(4, Gq - hc);
     // split weights: wave j handles head j; every (m, l) pair of a lane is
@@ -424,56 +432,53 @@ __device__ void combine_group(const CombineArgs& a, int bh) {
       if (lane == 0) linv[wave] = 1.0f / L;
     }
     __syncthreads();
-    for (int idx = tid; idx < 4 * D; idx += 256) {
-      const int j = idx / D, d = idx - (idx / D) * D;
-      float acc = 0.0f;
+    // merged o': thread (j, d pair); 32 slots' loads in flight per step; past
+    // the last slot the index is clamped (a valid address) and the weight is zero
+    for (int idx = tid; idx < 2 * D; idx += 256) {
+      const int j = idx / (D / 2), d = 2 * (idx - j * (D / 2));
+      float acc0 = 0.0f, acc1 = 0.0f;
       if (j < nh) {
         const float* P = a.partials + ((size_t)b * a.Hq + kvh * Gq + hc + j) * kMaxSplits * (D + 2);
-        // sixteen independent loads in flight per step; past the last slot the
-        // index is clamped (a valid address) and the weight is zero
-        for (int sl = 0; sl < a.nslots; sl += 16) {
-          float v[16];
+        for (int sl = 0; sl < a.nslots; sl += 32) {
+          float v[32][2];
 #pragma unroll
-          for (int u = 0; u < 16; ++u)
-            v[u] = ld_partial<COHERENT>(P + (size_t)min(sl + u, a.nslots - 1) * (D + 2) + d);
+          for (int u = 0; u < 32; ++u) {
+            const float* src = P + (size_t)min(sl + u, a.nslots - 1) * (D + 2) + d;
+            v[u][0] = ld_partial<COHERENT>(src);
+            v[u][1] = ld_partial<COHERENT>(src + 1);
+          }
 #pragma unroll
-          for (int u = 0; u < 16; ++u) {
-            const int su = min(sl + u, a.nslots - 1);
-            acc = __builtin_fmaf(v[u], sl + u < a.nslots ? wsl[j][su] : 0.0f, acc);
+          for (int u = 0; u < 32; ++u) {
+            const float w = sl + u < a.nslots ? wsl[j][min(sl + u, a.nslots - 1)] : 0.0f;
+            acc0 = __builtin_fmaf(v[u][0], w, acc0);
+            acc1 = __builtin_fmaf(v[u][1], w, acc1);
           }
         }
-        acc *= linv[j];
+        acc0 *= linv[j];
+        acc1 *= linv[j];
       }
-      os[j][d] = acc;
+      os[j][d] = acc0;
+      os[j][d + 1] = acc1;
     }
     __syncthreads();
-    float acc[4][PER];
+    // o = o' @ R_V^T for this block's columns: lane pair-columns 2 lane + 128 i
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int i = 0; i < PER / 2; ++i) {
+      float acc[4][2];
 #pragma unroll
-      for (int i = 0; i < PER; ++i) acc[j][i] = 0.0f;
-    const float* R = a.rvT + (size_t)(wave * EW) * D + lane;
-#pragma unroll 16
-    for (int e = 0; e < EW; ++e) {
-      float r[PER];
-#pragma unroll
-      for (int i = 0; i < PER; ++i) r[i] = R[(size_t)e * D + 64 * i];
+      for (int j = 0; j < 4; ++j) acc[j][0] = acc[j][1] = 0.0f;
+      rot_rows_cols2<4, D, EW>(&os[0][0], D, a.rvT, wave * EW, c0 + 128 * i + 2 * lane, acc);
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const float x = os[j][wave * EW + e];
-#pragma unroll
-        for (int i = 0; i < PER; ++i) acc[j][i] = __builtin_fmaf(x, r[i], acc[j][i]);
+        part[wave][j][128 * i + 2 * lane] = acc[j][0];
+        part[wave][j][128 * i + 2 * lane + 1] = acc[j][1];
       }
     }
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-#pragma unroll
-      for (int i = 0; i < PER; ++i) part[wave][j][lane + 64 * i] = acc[j][i];
     __syncthreads();
-    for (int idx = tid; idx < nh * D; idx += 256) {
-      const int j = idx / D, d = idx - (idx / D) * D;
+    for (int idx = tid; idx < nh * NC; idx += 256) {
+      const int j = idx / NC, d = idx - (idx / NC) * NC;
       const float v = ((part[0][j][d] + part[1][j][d]) + part[2][j][d]) + part[3][j][d];
-      const size_t o = ((size_t)b * a.Hq + kvh * Gq + hc + j) * D + d;
+      const size_t o = ((size_t)b * a.Hq + kvh * Gq + hc + j) * D + c0 + d;
       if (a.out_dtype == 0)
         reinterpret_cast<float*>(a.out)[o] = v;
       else if (a.out_dtype == 1)
@@ -485,9 +490,10 @@ __device__ void combine_group(const CombineArgs& a, int bh) {
   }
 }
 
-template <int D>
+// Grid: (sequence x kv head, CC column chunks of the output).
+template <int D, int CC>
 __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
-  combine_group<D>(a, (int)blockIdx.x);
+  combine_group<D, false, CC>(a, (int)blockIdx.x, (int)blockIdx.y);
 }
 
 // Partial results of the matrix-core launch are written with device-scope
@@ -1482,26 +1488,16 @@ __global__ __launch_bounds__(256) void wide_qrot_kernel(DecodeArgs a) {
     qraw[i] = j < a.Gq ? bf16_to_f32(a.q[((size_t)b * a.Hq + h * a.Gq + j) * D + e]) : 0.0f;
   }
   __syncthreads();
-  // wave w reduces over input dims e in [128 w, 128 w + 128); lane owns output
-  // dims 128 s + lane and 128 s + lane + 64
+  // wave w reduces over input dims e in [128 w, 128 w + 128)
+  // dims 128 s + 2 lane, + 1
   float acc[4][2];
 #pragma unroll
   for (int j = 0; j < 4; ++j) acc[j][0] = acc[j][1] = 0.0f;
-  const float* Rw = a.rk + (size_t)(wave * 128) * D + 128 * s + lane;
-#pragma unroll 8
-  for (int e = 0; e < 128; ++e) {
-    const float r0 = Rw[(size_t)e * D], r1 = Rw[(size_t)e * D + 64];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const float x = qraw[j * D + wave * 128 + e];
-      acc[j][0] = __builtin_fmaf(x, r0, acc[j][0]);
-      acc[j][1] = __builtin_fmaf(x, r1, acc[j][1]);
-    }
-  }
+  rot_rows_cols2<4, D>(qraw, D, a.rk, wave * 128, 128 * s + 2 * lane, acc);
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-    parts[wave][j][lane] = acc[j][0];
-    parts[wave][j][lane + 64] = acc[j][1];
+    parts[wave][j][2 * lane] = acc[j][0];
+    parts[wave][j][2 * lane + 1] = acc[j][1];
   }
   __syncthreads();
   {
@@ -1738,11 +1734,21 @@ void decode_wide_kernel(DecodeArgs a) {
   const int b = bh / a.Hkv, h = bh - (bh / a.Hkv) * a.Hkv;
   __shared__ WideSmem W;
   const int y = (int)blockIdx.y;
+#if OSCAR_WIDE_WIN_FIRST
+  // window blocks first: their passes are latency-bound, so they start early
+  // and run beside the INT2 streaming
+  if (y < a.win_blocks) {
+    wide_window_block<NH>(a, bh, b, h, y, W);
+    return;
+  }
+  const int split = y - a.win_blocks;
+#else
   if (y >= a.plan.splits) {
     wide_window_block<NH>(a, bh, b, h, y - a.plan.splits, W);
     return;
   }
   const int split = y;
+#endif
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int blk = lane >> 2, j = lane & 3;
   const int lo = a.plan.a0, hi = a.plan.b0;
@@ -1950,11 +1956,10 @@ hipError_t launch_decode_wide(const DecodeArgs& a, int B, hipStream_t s) {
 }
 
 hipError_t launch_combine(const CombineArgs& a, hipStream_t s) {
-  dim3 grid((unsigned)(a.B * a.Hkv));
   if (a.D == 128)
-    hipLaunchKernelGGL(combine_kernel<128>, grid, dim3(256), 0, s, a);
+    hipLaunchKernelGGL((combine_kernel<128, 1>), dim3((unsigned)(a.B * a.Hkv)), dim3(256), 0, s, a);
   else
-    hipLaunchKernelGGL(combine_kernel<512>, grid, dim3(256), 0, s, a);
+    hipLaunchKernelGGL((combine_kernel<512, 4>), dim3((unsigned)(a.B * a.Hkv), 4), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 

@@ -746,6 +746,13 @@ int oscar_stream_copy(const void* src, void* dst, size_t bytes, hipStream_t stre
   return OSCAR_OK;
 }
 
+int oscar_stream_read(const void* src, size_t bytes, void* xor_out, hipStream_t stream) {
+  if (bytes % 16 != 0) return fail(OSCAR_ERR_INVALID_ARG, "bytes must be a multiple of 16");
+  if (!xor_out || (bytes > 0 && !src)) return fail(OSCAR_ERR_INVALID_ARG, "NULL pointer");
+  HIP_TRY(launch_stream_read(src, bytes, static_cast<unsigned*>(xor_out), stream));
+  return OSCAR_OK;
+}
+
 int oscar_quantize_rows(const float* x, int32_t rows, int32_t D, int32_t G, float clip, void* codes,
                         void* meta, hipStream_t stream) {
   if (rows < 0) return fail(OSCAR_ERR_INVALID_ARG, "rows must be >= 0");

@@ -31,7 +31,8 @@ EXPORTED = [
     "oscar_kv_create", "oscar_kv_append", "oscar_int2_decode_attn", "oscar_kv_destroy",
     "oscar_last_error", "oscar_kv_length", "oscar_kv_device_bytes", "oscar_kv_set_num_splits",
     "oscar_kv_set_decode_impl", "oscar_kv_export", "oscar_kv_append_dump", "oscar_quantize_rows",
-    "oscar_kv_profile_enable", "oscar_kv_profile_read", "oscar_stream_copy", "oscar_kv_decode_step",
+    "oscar_kv_profile_enable", "oscar_kv_profile_read", "oscar_stream_copy", "oscar_stream_read",
+    "oscar_kv_decode_step",
 ]
 
 
@@ -74,6 +75,7 @@ def load_library(path: str = LIB_PATH) -> C.CDLL:
         "oscar_kv_profile_enable": ([vp, i32], C.c_int),
         "oscar_kv_profile_read": ([vp, i32, C.POINTER(C.c_double), C.POINTER(C.c_int64)], C.c_int),
         "oscar_stream_copy": ([vp, vp, C.c_size_t, vp], C.c_int),
+        "oscar_stream_read": ([vp, C.c_size_t, vp, vp], C.c_int),
         "oscar_kv_decode_step": ([vp, i32, vp, vp, vp, vp, i32, i32, f32, vp], C.c_int),
     }
     for name, (args, res) in sig.items():
@@ -175,6 +177,10 @@ def oscar_kv_profile_read(kv, kernel_class):
 
 def oscar_stream_copy(src, dst, nbytes, stream=None):
     _check(_lib.oscar_stream_copy(_ptr(src), _ptr(dst), nbytes, _stream(stream)))
+
+
+def oscar_stream_read(src, nbytes, xor_out, stream=None):
+    _check(_lib.oscar_stream_read(_ptr(src), nbytes, _ptr(xor_out), _stream(stream)))
 
 
 def oscar_kv_export(kv, layer, which, codes, meta, sink, ring):

@@ -574,3 +574,17 @@ def test_full_size_wide_64k_sampled(ok):
         say(f"  seq {b}: rel L2 {e:.3e}")
         assert e <= ATTN_TOL
     gc.close()
+
+
+def test_stream_read_calibration(ok):
+    """The read-only calibration kernel reads every word once: its XOR equals
+    the host XOR of the buffer (odd and even sizes of the grid-stride tail)."""
+    rng = np.random.default_rng(7)
+    for nwords in (4, 4 * 1000 + 4, 4 * (1 << 18)):
+        host = rng.integers(0, 2 ** 31 - 1, size=nwords, dtype=np.int64).astype(np.int32)
+        src = torch.from_numpy(host).cuda()
+        acc = torch.zeros(1, dtype=torch.int32, device="cuda")
+        ok.oscar_stream_read(src, nwords * 4, acc)
+        torch.cuda.synchronize()
+        want = np.bitwise_xor.reduce(host.view(np.uint32))
+        assert int(acc.cpu().numpy().view(np.uint32)[0]) == int(want), nwords
