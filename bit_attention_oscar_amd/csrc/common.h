@@ -68,6 +68,11 @@ __host__ __device__ inline size_t vcode_byte(int bh, int cap, int t, int d, int 
   return tile * 2048 + (size_t)(rec >> 4) * 1024 + (size_t)lane * 16 + (rec & 15);
 }
 
+// first byte of the 2 KiB V code tile of the 64-token tile holding t and slice g
+__host__ __device__ inline size_t vcode_tile_base(int bh, int cap, int t, int g, int D) {
+  return (((size_t)bh * (cap / kTile) + (t >> 6)) * (size_t)(D / 128) + g) * 2048;
+}
+
 __host__ __device__ inline size_t row_offset(int bh, int rows, int t, int D) {
   return ((size_t)bh * rows + t) * (size_t)D;
 }
@@ -112,6 +117,8 @@ struct AppendArgs {
   const uint16_t* vin;
   const float* rk;        // fp32 [D][D] for this layer
   const float* rv;
+  const uint16_t* rk3;    // bf16 [3][D][D]: R_K^T as three pieces summing to it (matrix-core prefill)
+  const uint16_t* rv3;
   float* kdump;           // optional fp32 [batch][n_new][Hkv][D]
   float* vdump;
   int batch, n_new, Hkv, D, cap, N, M, T_old, T_new;
@@ -170,6 +177,7 @@ struct DecodeArgs {
 
 // launchers (defined in the .hip files); return hipGetLastError()
 hipError_t launch_append(const AppendArgs& a, hipStream_t s);
+hipError_t launch_append_prefill(const AppendArgs& a, hipStream_t s);   // n_new > 1, rotation on matrix cores
 hipError_t launch_quantize_rows(const float* x, int rows, int D, float clip, uint8_t* codes,
                                 uint32_t* meta, hipStream_t s);
 hipError_t launch_qrot(const QRotArgs& a, hipStream_t s);

@@ -68,6 +68,8 @@ struct oscar_kv {
   float* rk = nullptr;     // [L][D][D]
   float* rv = nullptr;     // [L][D][D]
   float* rvT = nullptr;    // [L][D][D] transposed
+  uint16_t* rk3 = nullptr; // [L][3][D][D] bf16 pieces of R_K^T (R_K = sum of the three, transposed)
+  uint16_t* rv3 = nullptr; // [L][3][D][D] the same for R_V
   float* qrot = nullptr;   // [B][Hq][D]
   float* qpub = nullptr;    // [B][Hkv][G][kQPub]
   unsigned* qflag = nullptr; // [B][Hkv]
@@ -238,6 +240,8 @@ int do_append(oscar_kv* kv, int32_t layer, const void* k, const void* v, int32_t
   const size_t DD = (size_t)kv->cfg.head_dim * kv->cfg.head_dim;
   a.rk = kv->rk + layer * DD;
   a.rv = kv->rv + layer * DD;
+  a.rk3 = kv->rk3 + layer * 3 * DD;
+  a.rv3 = kv->rv3 + layer * 3 * DD;
   a.kdump = kdump;
   a.vdump = vdump;
   a.batch = batch;
@@ -250,7 +254,10 @@ int do_append(oscar_kv* kv, int32_t layer, const void* k, const void* v, int32_t
   a.T_old = L.T;
   a.T_new = L.T + n_new;
   const long ps = prof_begin(kv, 2, stream);
-  HIP_TRY(launch_append(a, stream));
+  if (n_new > 1)
+    HIP_TRY(launch_append_prefill(a, stream));
+  else
+    HIP_TRY(launch_append(a, stream));
   prof_end(kv, 2, ps, stream);
   L.T += n_new;
   L.batch = batch;
@@ -357,8 +364,30 @@ int oscar_kv_create(const oscar_kv_config* cfg, oscar_kv** out) {
     for (int e = 0; e < D; ++e)
       for (int d = 0; d < D; ++d) rvT[l * DD + (size_t)e * D + d] = rv[l * DD + (size_t)d * D + e];
   auto up = [&](void* dst, const void* src, size_t n) { return hipMemcpy(dst, src, n, hipMemcpyHostToDevice); };
+  // bf16 pieces for the matrix-core prefill: R = R1 + R2 + R3 with R1 = bf16(R),
+  // R2 = bf16(R - R1), R3 = bf16(R - R1 - R2) (each difference exact in fp32),
+  // stored transposed ([column][row]) so that a lane's 8 consecutive rows are
+  // one 16-byte load
+  if ((rc = dev_alloc(kv, (void**)&kv->rk3, L * 3 * DD * 2))) return bail(rc);
+  if ((rc = dev_alloc(kv, (void**)&kv->rv3, L * 3 * DD * 2))) return bail(rc);
+  std::vector<uint16_t> rk3(L * 3 * DD), rv3(L * 3 * DD);
+  for (int which = 0; which < 2; ++which) {
+    const std::vector<float>& R = which ? rv : rk;
+    std::vector<uint16_t>& out = which ? rv3 : rk3;
+    for (size_t l = 0; l < L; ++l)
+      for (int e = 0; e < D; ++e)
+        for (int d = 0; d < D; ++d) {
+          float r = R[l * DD + (size_t)e * D + d];
+          for (int s = 0; s < 3; ++s) {
+            const uint16_t p = f32_to_bf16(r);
+            out[(l * 3 + s) * DD + (size_t)d * D + e] = p;
+            r = r - bf16_to_f32(p);
+          }
+        }
+  }
   if (up(kv->rk, rk.data(), L * DD * 4) != hipSuccess || up(kv->rv, rv.data(), L * DD * 4) != hipSuccess ||
-      up(kv->rvT, rvT.data(), L * DD * 4) != hipSuccess)
+      up(kv->rvT, rvT.data(), L * DD * 4) != hipSuccess || up(kv->rk3, rk3.data(), L * 3 * DD * 2) != hipSuccess ||
+      up(kv->rv3, rv3.data(), L * 3 * DD * 2) != hipSuccess)
     return bail(fail(OSCAR_ERR_HIP, "copy of rotations failed"));
   const size_t B = cfg->max_batch, Hq = cfg->num_q_heads, Hkv = cfg->num_kv_heads;
   if ((rc = dev_alloc(kv, (void**)&kv->qrot, B * Hq * D * 4))) return bail(rc);

@@ -1,0 +1,206 @@
+// Multi-token append (chunked prefill) with the rotation on matrix cores.
+//
+// The append path rotates every new K and V row by the layer's R_K / R_V,
+// then clips, quantizes to 2 bits and packs each 128-wide group ("OSCAR: 2-bit
+// KV Cache Quantization for SGLang and llama.cpp", "How the offline rotation
+// is fit"; the clip ratios and group size in the Qwen3-4B card's "Run" table).
+// For a prefill chunk the rotation is a dense product X (rows = tokens) times
+// R (head_dim x head_dim), done here with v_mfma_f32_16x16x32_bf16:
+//
+//   X is bf16 already, so it enters the matrix cores unchanged.  R is fp32;
+//   it is held as three bf16 matrices R = R1 + R2 + R3 (R1 = bf16(R), R2 =
+//   bf16(R - R1), R3 = R - R1 - R2, which is exact for every finite fp32 R
+//   outside the subnormal range).  Each product of a bf16 x and a bf16 piece
+//   is exact in fp32, so X R is computed in fp32 with only the accumulation
+//   order differing from a plain fp32 loop.
+//
+// Block = 4 waves, one (sequence, kv head), one 64-token tile (aligned to the
+// cache's 64-token tiles) and one 128-wide group: 64 rows x 128 columns, the
+// reduction over head_dim in steps of 32.  Wave w owns columns [32 w, 32 w +
+// 32) of the group: 4 row blocks x 2 column blocks of 16 x 16 accumulators.
+// The rotated tile goes through shared memory to the quantizer (one row per
+// wave at a time, as in the one-token append), and the V code tile of the 64
+// tokens and 128 dims is assembled there and written whole (2 KiB), merging
+// the bits of tokens stored before this chunk.
+#include "append_impl.h"
+
+namespace oscar {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+
+struct PrefillSmem {
+  float tile[64][132];          // rotated rows, 128 columns (+4: bank offset)
+  uint8_t codes[64][128];       // 2-bit codes of the tile
+  float smax[4];
+};
+
+template <int D>
+__global__ __launch_bounds__(256) void append_prefill_kernel(AppendArgs a) {
+  constexpr int KS = D / 32;           // reduction steps
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int bh = blockIdx.x;
+  const int b = bh / a.Hkv, h = bh - (bh / a.Hkv) * a.Hkv;
+  const int g = blockIdx.z >> 1;       // 128-wide group
+  const bool isv = (blockIdx.z & 1) != 0;
+  const int t0 = ((a.T_old >> 6) + (int)blockIdx.y) << 6;   // first position of the 64-token tile
+  const PlaneDev P = isv ? a.v : a.k;
+  const uint16_t* in = isv ? a.vin : a.kin;
+  const uint16_t* RT = isv ? a.rv3 : a.rk3;   // [3][D (column n)][D (row k)] bf16
+  float* dump = isv ? a.vdump : a.kdump;
+  __shared__ PrefillSmem S;
+
+  // operand addresses: A = rows t0 + 16 rb + (lane & 15), k = 8 (lane >> 4) + 32 step;
+  // B = column 128 g + 32 wave + 16 cb + (lane & 15), same k, piece s
+  const int m = lane & 15, kq = 8 * (lane >> 4);
+  const uint16_t* arow[4];
+  bool aval[4];
+#pragma unroll
+  for (int rb = 0; rb < 4; ++rb) {
+    const int t = t0 + 16 * rb + m;
+    aval[rb] = t >= a.T_old && t < a.T_new;
+    arow[rb] = in + ((((size_t)b * a.n_new + (aval[rb] ? t - a.T_old : 0)) * a.Hkv + h) * D) + kq;
+  }
+  const uint16_t* bcol[2][3];
+#pragma unroll
+  for (int cb = 0; cb < 2; ++cb)
+#pragma unroll
+    for (int s = 0; s < 3; ++s)
+      bcol[cb][s] = RT + ((size_t)s * D + 128 * g + 32 * wave + 16 * cb + m) * D + kq;
+
+  f32x4 acc[4][2];
+#pragma unroll
+  for (int rb = 0; rb < 4; ++rb)
+#pragma unroll
+    for (int cb = 0; cb < 2; ++cb) acc[rb][cb] = f32x4{0, 0, 0, 0};
+
+  // two register stages: the next step's operands load during this step's products
+  u32x4_t A[2][4], B[2][2][3];
+  auto load = [&](int st, int k0) {
+#pragma unroll
+    for (int rb = 0; rb < 4; ++rb)
+      A[st][rb] = aval[rb] ? *reinterpret_cast<const u32x4_t*>(arow[rb] + k0) : u32x4_t{0, 0, 0, 0};
+#pragma unroll
+    for (int cb = 0; cb < 2; ++cb)
+#pragma unroll
+      for (int s = 0; s < 3; ++s) B[st][cb][s] = *reinterpret_cast<const u32x4_t*>(bcol[cb][s] + k0);
+  };
+  load(0, 0);
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) {
+    const int st = ks & 1;
+    if (ks + 1 < KS) load(st ^ 1, 32 * (ks + 1));
+#pragma unroll
+    for (int s = 0; s < 3; ++s)
+#pragma unroll
+      for (int rb = 0; rb < 4; ++rb)
+#pragma unroll
+        for (int cb = 0; cb < 2; ++cb)
+          acc[rb][cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, A[st][rb]),
+                                                                __builtin_bit_cast(bf16x8_t, B[st][cb][s]),
+                                                                acc[rb][cb], 0, 0, 0);
+  }
+
+  // accumulator (rb, cb) register i: row 16 rb + 4 (lane >> 4) + i, column 16 cb + (lane & 15)
+#pragma unroll
+  for (int rb = 0; rb < 4; ++rb)
+#pragma unroll
+    for (int cb = 0; cb < 2; ++cb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) S.tile[16 * rb + 4 * (lane >> 4) + i][32 * wave + 16 * cb + m] = acc[rb][cb][i];
+  if (tid < 4) S.smax[tid] = 0.0f;
+  __syncthreads();
+
+  // quantizer, one row per wave at a time: lane owns dims lane and lane + 64
+  // of the group (the one-token append's arithmetic from here on)
+  float wsmax = 0.0f;
+  for (int r = wave; r < 64; r += 4) {
+    const int t = t0 + r;
+    if (t < a.T_old || t >= a.T_new) continue;       // wave-uniform
+    float x[2];
+    x[0] = S.tile[r][lane] + 0.0f;
+    x[1] = S.tile[r][lane + 64] + 0.0f;
+    const int d0 = 128 * g + lane;
+    if (dump) {
+      const size_t base = (((size_t)b * a.n_new + (t - a.T_old)) * a.Hkv + h) * D;
+      dump[base + d0] = x[0];
+      dump[base + d0 + 64] = x[1];
+    }
+    if (P.is_bf16) {
+      const size_t base = row_offset(bh, a.cap, t, D);
+      P.full[base + d0] = f32_to_bf16(x[0]);
+      P.full[base + d0 + 64] = f32_to_bf16(x[1]);
+      continue;
+    }
+    if (t < a.N) {
+      const size_t base = row_offset(bh, a.N, t, D);
+      P.sink[base + d0] = f32_to_bf16(x[0]);
+      P.sink[base + d0 + 64] = f32_to_bf16(x[1]);
+    }
+    if (a.M > 0 && t >= a.N && t >= a.T_new - a.M) {
+      const size_t base = row_offset(bh, a.M, t % a.M, D);
+      P.ring[base + d0] = f32_to_bf16(x[0]);
+      P.ring[base + d0 + 64] = f32_to_bf16(x[1]);
+    }
+    const float mx = wave_max(fmaxf(x[0], x[1]));
+    const float mn = wave_min(fminf(x[0], x[1]));
+    const GroupQ q = group_params(mx, mn, P.clip);
+    const uint32_t code[2] = {quant_code(x[0], q), quant_code(x[1], q)};
+    if (lane == 0) P.meta[meta_index(bh, a.cap, t, g, D)] = q.packed;
+    wsmax = fmaxf(wsmax, q.sf);
+    if (!P.tiled) {
+      store_canonical<2>(code, lane, [&](int w) {
+        return reinterpret_cast<uint32_t*>(P.codes + kcode_byte(bh, a.cap, t, 32 * g + 4 * w, D));
+      });
+    } else {
+      S.codes[r][lane] = (uint8_t)code[0];
+      S.codes[r][lane + 64] = (uint8_t)code[1];
+    }
+  }
+  if (P.is_bf16) return;
+  if (P.smax && lane == 0) atomicMax(reinterpret_cast<unsigned int*>(&S.smax[0]), __float_as_uint(wsmax));
+  __syncthreads();
+  if (P.smax && tid == 0 && S.smax[0] > 0.0f)
+    atomicMax(reinterpret_cast<unsigned int*>(P.smax + bh), __float_as_uint(S.smax[0]));
+  if (!P.tiled) return;
+
+  // V code tile of tokens [t0, t0 + 64), dims [128 g, 128 g + 128): 2 KiB, 8
+  // bytes per thread.  Byte p: half p >> 10, lane record (p >> 4) & 63, record
+  // byte rec = 16 half + (p & 15) holds dim 64 (rec & 1) + 4 (l >> 2) + (l & 3)
+  // of the four tokens 8 (rec >> 2) + ((rec & 3) >> 1) + 2 (q & 1) + 4 (q >> 1)
+  // (q = 0..3) at bits 2 q.  Tokens outside [T_old, T_new) keep their bits.
+  uint8_t* vt = P.codes + vcode_tile_base(bh, a.cap, t0, g, D);
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const int p = 8 * tid + j;
+    const int half = p >> 10, l = (p >> 4) & 63, rec = 16 * half + (p & 15);
+    const int ds = 64 * (rec & 1) + 4 * (l >> 2) + (l & 3);
+    const int tb0 = 8 * (rec >> 2) + ((rec & 3) >> 1);
+    uint32_t byte = 0, keep = 0;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int tb = tb0 + 2 * (q & 1) + 4 * (q >> 1);
+      const int t = t0 + tb;
+      if (t >= a.T_old && t < a.T_new)
+        byte |= (uint32_t)S.codes[tb][ds] << (2 * q);
+      else
+        keep |= 3u << (2 * q);
+    }
+    if (keep == 0xFFu) continue;          // no token of this chunk in the byte
+    if (keep) byte |= vt[p] & keep;
+    vt[p] = (uint8_t)byte;
+  }
+}
+
+hipError_t launch_append_prefill(const AppendArgs& a, hipStream_t s) {
+  const int tiles = ((a.T_new - 1) >> 6) - (a.T_old >> 6) + 1;
+  dim3 grid((unsigned)(a.batch * a.Hkv), (unsigned)tiles, (unsigned)(2 * (a.D / 128)));
+  if (a.D == 128)
+    hipLaunchKernelGGL(append_prefill_kernel<128>, grid, dim3(256), 0, s, a);
+  else
+    hipLaunchKernelGGL(append_prefill_kernel<512>, grid, dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace oscar
