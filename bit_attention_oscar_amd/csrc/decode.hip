@@ -1528,6 +1528,7 @@ struct WideSmem {
   float4 q[4][4][16][2];       // window: q of [slice][head][dims 8c .. 8c + 7]
   float sc[4][4][32];          // window: [wave][head][token] partial scores
   float p[4][32];              // window: softmax weights [head][token]
+  float pv[4][4][64];          // bf16-V splits: [wave][head][token] softmax weights of the tile
   float wm[4], wl[4], wa[4];   // window: running max, sum, rescale factor per head
 };
 
@@ -1538,7 +1539,7 @@ struct WideSmem {
 // slots from (ring0 + its first index) mod M.  Wave w owns dims [128 w,
 // 128 w + 128); lane (tq, c) owns dims 8 c .. 8 c + 7 of that slice for
 // tokens tq + 4 i of a pass, so every row load is contiguous across 16 lanes.
-template <int NH>
+template <int NH, bool VB>
 __device__ void wide_window_block(const DecodeArgs& a, int bh, int b, int h, int wblk, WideSmem& W) {
   constexpr int D = 512, PT = 32, RI = PT / 4;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
@@ -1556,8 +1557,11 @@ __device__ void wide_window_block(const DecodeArgs& a, int bh, int b, int h, int
   // them) returns zero
   const __amdgpu_buffer_rsrc_t kp =
       plane_rsrc(ring ? a.k.ring + row_offset(bh, a.M, 0, D) : a.k.sink + row_offset(bh, a.N, 0, D), nbytes);
+  // V kept bf16 (VB): rows of the full plane by position (a.cap rows)
   const __amdgpu_buffer_rsrc_t vp =
-      plane_rsrc(ring ? a.v.ring + row_offset(bh, a.M, 0, D) : a.v.sink + row_offset(bh, a.N, 0, D), nbytes);
+      VB ? plane_rsrc(a.v.full + row_offset(bh, a.cap, 0, D), a.cap * D * 2)
+         : plane_rsrc(ring ? a.v.ring + row_offset(bh, a.M, 0, D) : a.v.sink + row_offset(bh, a.N, 0, D), nbytes);
+  const int pos0 = ring ? a.win.a1 + i_lo : a.win.a0 + i_lo;   // position of the block's first token
   int row0 = ring ? a.ring0 + i_lo : a.win.a0 + i_lo;
   if (row0 >= rows) row0 -= rows;
   const int col = 128 * wave + 8 * c;
@@ -1627,7 +1631,11 @@ __device__ void wide_window_block(const DecodeArgs& a, int bh, int b, int h, int
     // this pass's V rows, in flight during the softmax
     u4 vr[RI];
 #pragma unroll
-    for (int i = 0; i < RI; ++i) vr[i] = __builtin_amdgcn_raw_buffer_load_b128(vp, roff(i), 0, 0);
+    for (int i = 0; i < RI; ++i) {
+      const int vo = VB ? ((tq + 4 * i < n) ? ((pos0 + (p0 - i_lo) + tq + 4 * i) * D + col) * 2 : a.cap * D * 2)
+                        : roff(i);
+      vr[i] = __builtin_amdgcn_raw_buffer_load_b128(vp, vo, 0, 0);
+    }
     __syncthreads();
     if (wave < NH && lane < PT) {  // online softmax update, wave j for head j
       const int j = wave;
@@ -1723,11 +1731,189 @@ __device__ inline TileRegs wide_load_tile(const TileStreams& s, int t0, int lane
   return r;
 }
 
+// INT2 split with V kept bf16: QK^T as in the INT2 path (wave w = K group w,
+// partial scores summed in shared memory), then the softmax weights of the
+// tile go to the wave's own shared-memory row and PV runs in fp32 on the VALU
+// over the tile's V rows (row-major, dims [128 w, 128 w + 128) of each):
+// lane (tq, c) takes dims 8 c .. 8 c + 7 of rows tq + 4 i, i = 0..15, every
+// load contiguous across 16 lanes; the tile's V rows are issued first and
+// land during QK^T and the softmax.
+template <int NH>
+__device__ void wide_split_bf16v(const DecodeArgs& a, int bh, int b, int h, int split, WideSmem& W) {
+  constexpr int D = 512;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+  const int blk = lane >> 2, j = lane & 3;
+  const int tq = lane >> 4, c = lane & 15;
+  const int lo = a.plan.a0, hi = a.plan.b0;
+  const int tile_first = lo >> 6;
+  const int ntiles = ((hi - 1) >> 6) - tile_first + 1;
+  const int S_ = a.plan.splits;
+  auto split_start = [&](int s) -> int {
+    if (s >= S_) return ntiles;
+    const float fs = (float)s, al = a.split_ramp;
+    const float F = (fs * (1.0f + al) - al * fs * (fs - 1.0f) / (float)max(S_ - 1, 1)) / (float)S_;
+    return min(ntiles, (int)(F * (float)ntiles));
+  };
+  const int s_t0 = split_start(split);
+  const int s_t1 = split_start(split + 1);
+  const int t_last = max(s_t1 - 1, 0);
+  const TileStreams st = wide_tile_streams(a, bh, wave);
+  const __amdgpu_buffer_rsrc_t vfull = plane_rsrc(a.v.full + row_offset(bh, a.cap, 0, D), a.cap * D * 2);
+  const int vnull = a.cap * D * 2;        // past the plane: loads zero
+  const int lane_c = 2048 * wave + lane * 16, lane_m = blk * 16;
+  const int col = 128 * wave + 8 * c;
+  auto tile_t0 = [&](int ti) { return (tile_first + ti) << 6; };
+  struct KRegs {
+    u4 k0, k1, km;
+  };
+  auto load_k = [&](int t0) {
+    KRegs r;
+    r.k0 = __builtin_amdgcn_raw_buffer_load_b128(st.kc, lane_c, t0 * 128, kStreamOnce);
+    r.k1 = __builtin_amdgcn_raw_buffer_load_b128(st.kc, lane_c + 1024, t0 * 128, kStreamOnce);
+    r.km = __builtin_amdgcn_raw_buffer_load_b128(st.km, lane_m, t0 * 4, 0);
+    return r;
+  };
+  KRegs r[kDepth];
+#pragma unroll
+  for (int k = 0; k < kDepth; ++k) r[k] = load_k(tile_t0(min(s_t0 + k, t_last)));
+
+  h4 qv[1][8];
+  float qsum;
+  int eq;
+  {
+    const __amdgpu_buffer_rsrc_t qr = plane_rsrc(a.qpub + (size_t)(bh * 4 + wave) * kQPub, kQPub * 4);
+    const int vbase = (kQPubOps + 16 * (4 * (lane >> 4) + j)) * 4;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const u4 wv = __builtin_amdgcn_raw_buffer_load_b128(qr, vbase + 16 * i, 0, 0);
+      qv[0][2 * i] = as_h4(wv.x, wv.y);
+      qv[0][2 * i + 1] = as_h4(wv.z, wv.w);
+    }
+    qsum = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(qr, (512 + j) * 4, 0, 0));
+    eq = (int)__builtin_amdgcn_raw_buffer_load_b32(qr, (516 + j) * 4, 0, 0);
+  }
+  const float cK = ldexpf(1.0f, 24 - eq);
+  const float zq = ldexpf(qsum, eq - 24);
+  float m = NEG_INF, l = 0.0f;
+  float o[NH][8];
+#pragma unroll
+  for (int jj = 0; jj < NH; ++jj)
+#pragma unroll
+    for (int k = 0; k < 8; ++k) o[jj][k] = 0.0f;
+
+  int buf = 0;
+  auto process = [&](const KRegs& cur, int t0) {
+    // V rows of the tile (zero outside [lo, hi))
+    u4 vr[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int t = t0 + tq + 4 * i;
+      vr[i] = __builtin_amdgcn_raw_buffer_load_b128(vfull, (t >= lo && t < hi) ? (t * D + col) * 2 : vnull, 0,
+                                                    kStreamOnce);
+    }
+    f4 sa[1] = {{0, 0, 0, 0}};
+    qk_word<1>(cur.k0.x, qv, 0, sa);
+    qk_word<1>(cur.k0.y, qv, 1, sa);
+    qk_word<1>(cur.k0.z, qv, 2, sa);
+    qk_word<1>(cur.k0.w, qv, 3, sa);
+    qk_word<1>(cur.k1.x, qv, 4, sa);
+    qk_word<1>(cur.k1.y, qv, 5, sa);
+    qk_word<1>(cur.k1.z, qv, 6, sa);
+    qk_word<1>(cur.k1.w, qv, 7, sa);
+    const uint32_t kmr[4] = {cur.km.x, cur.km.y, cur.km.z, cur.km.w};
+    f4 part;
+#pragma unroll
+    for (int rr = 0; rr < 4; ++rr)
+      part[rr] = cK * __builtin_fmaf(hi_half(kmr[rr]), zq, __builtin_fmaf(lo_half(kmr[rr]), sa[0][rr], 0.0f));
+    W.u[buf][wave][lane] = part;
+    __syncthreads();
+    f4 u = ((W.u[buf][0][lane] + W.u[buf][1][lane]) + W.u[buf][2][lane]) + W.u[buf][3][lane];
+    buf ^= 1;
+    if (t0 < lo || t0 + 64 > hi) {
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) {
+        const int t = t0 + 4 * blk + rr;
+        if (t < lo || t >= hi) u[rr] = NEG_INF;
+      }
+    }
+    const float tmax = fmaxf(fmaxf(u[0], u[1]), fmaxf(u[2], u[3]));
+    if (__any(tmax > m)) {
+      const float mnew = fmaxf(m, head_max(tmax));
+      const float alpha = __builtin_amdgcn_exp2f(m - mnew);
+      l *= alpha;
+      m = mnew;
+#pragma unroll
+      for (int jj = 0; jj < NH; ++jj) {
+        const float al = lane_value(alpha, jj);
+#pragma unroll
+        for (int k = 0; k < 8; ++k) o[jj][k] *= al;
+      }
+    }
+    float p[4];
+#pragma unroll
+    for (int rr = 0; rr < 4; ++rr) p[rr] = __builtin_amdgcn_exp2f(u[rr] - m);
+    l += (p[0] + p[1]) + (p[2] + p[3]);
+    // weights to this wave's row of shared memory: head j, token 4 blk + rr
+    *reinterpret_cast<f4*>(&W.pv[wave][j][4 * blk]) = f4{p[0], p[1], p[2], p[3]};
+    __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0): the wave's own writes are visible to its reads
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int tk = tq + 4 * i;
+      float x[8];
+      bf16x8(vr[i], x);
+#pragma unroll
+      for (int jj = 0; jj < NH; ++jj) {
+        const float pw = W.pv[wave][jj][tk];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) o[jj][k] = __builtin_fmaf(pw, x[k], o[jj][k]);
+      }
+      __builtin_amdgcn_sched_barrier(0);   // one row's conversions at a time
+    }
+  };
+
+  for (int ti = s_t0; ti < s_t1; ti += kDepth) {
+#pragma unroll
+    for (int k = 0; k < kDepth; ++k) {
+      const int t = ti + k;
+      if (t >= s_t1) break;
+      process(r[k], tile_t0(t));
+      if (t + kDepth < s_t1) r[k] = load_k(tile_t0(t + kDepth));
+    }
+  }
+
+  const float lt = head_sum(l);
+#pragma unroll
+  for (int jj = 0; jj < NH; ++jj)
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      o[jj][k] += __shfl_xor(o[jj][k], 16);
+      o[jj][k] += __shfl_xor(o[jj][k], 32);
+    }
+  const int slot = a.plan.slot0 + split;
+  if (tq == 0)
+#pragma unroll
+    for (int jj = 0; jj < NH; ++jj) {
+      if (jj >= a.Gq) break;
+      float* dst = a.partials + (((size_t)b * a.Hq + h * a.Gq + jj) * kMaxSplits + slot) * (D + 2);
+#pragma unroll
+      for (int k = 0; k < 8; ++k) dst[col + k] = o[jj][k];
+    }
+  if (wave == 0 && lane < a.Gq) {
+    float* dst = a.partials + (((size_t)b * a.Hq + h * a.Gq + lane) * kMaxSplits + slot) * (D + 2);
+    dst[D] = m;
+    dst[D + 1] = lt;
+  }
+}
+
 // Grid: (sequence x kv head, plan.splits INT2 splits + win_blocks window
 // blocks).  NH: query heads per kv head rounded up to 2 or 4 (the window
-// blocks' register arrays; the matrix-core part always has 4 columns).
-template <int NH>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4, 4)))
+// blocks' register arrays; the matrix-core part always has 4 columns).  VB: V
+// kept bf16 for every position (INT2 K only); each wave then holds a whole
+// tile of V rows (64 registers, 16 KiB per wave in flight) and runs at 2 waves
+// per SIMD.
+template <int NH, bool VB>
+__global__ __launch_bounds__(256)
+__attribute__((amdgpu_waves_per_eu(VB ? 2 : 4, VB ? 2 : 4)))
 void decode_wide_kernel(DecodeArgs a) {
   constexpr int D = 512;
   const int bh = blockIdx.x;
@@ -1738,17 +1924,21 @@ void decode_wide_kernel(DecodeArgs a) {
   // window blocks first: their passes are latency-bound, so they start early
   // and run beside the INT2 streaming
   if (y < a.win_blocks) {
-    wide_window_block<NH>(a, bh, b, h, y, W);
+    wide_window_block<NH, VB>(a, bh, b, h, y, W);
     return;
   }
   const int split = y - a.win_blocks;
 #else
   if (y >= a.plan.splits) {
-    wide_window_block<NH>(a, bh, b, h, y - a.plan.splits, W);
+    wide_window_block<NH, VB>(a, bh, b, h, y - a.plan.splits, W);
     return;
   }
   const int split = y;
 #endif
+  if constexpr (VB) {
+    wide_split_bf16v<NH>(a, bh, b, h, split, W);
+    return;
+  }
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int blk = lane >> 2, j = lane & 3;
   const int lo = a.plan.a0, hi = a.plan.b0;
@@ -1948,10 +2138,18 @@ hipError_t launch_wide_qrot(const DecodeArgs& a, int B, hipStream_t s) {
 
 hipError_t launch_decode_wide(const DecodeArgs& a, int B, hipStream_t s) {
   dim3 grid((unsigned)(B * a.Hkv), (unsigned)(a.plan.splits + a.win_blocks));
-  if (a.Gq <= 2)
-    hipLaunchKernelGGL(decode_wide_kernel<2>, grid, dim3(256), 0, s, a);
-  else
-    hipLaunchKernelGGL(decode_wide_kernel<4>, grid, dim3(256), 0, s, a);
+  const bool vb = a.v.is_bf16 != 0;
+  if (a.Gq <= 2) {
+    if (vb)
+      hipLaunchKernelGGL((decode_wide_kernel<2, true>), grid, dim3(256), 0, s, a);
+    else
+      hipLaunchKernelGGL((decode_wide_kernel<2, false>), grid, dim3(256), 0, s, a);
+  } else {
+    if (vb)
+      hipLaunchKernelGGL((decode_wide_kernel<4, true>), grid, dim3(256), 0, s, a);
+    else
+      hipLaunchKernelGGL((decode_wide_kernel<4, false>), grid, dim3(256), 0, s, a);
+  }
   return hipGetLastError();
 }
 

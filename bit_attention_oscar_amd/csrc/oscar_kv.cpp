@@ -444,13 +444,14 @@ bool fast_shape(const oscar_kv* kv) {
          c.k_dtype == OSCAR_KV_INT2 && c.v_dtype == OSCAR_KV_INT2 && (long long)kv->cap * 32 <= INT32_MAX;
 }
 
-// head_dim 512 with at most 4 query heads per kv head, INT2 K and V: the
-// three-launch matrix-core path (32-bit buffer offsets: cap * 128 bytes must fit)
+// head_dim 512 with at most 4 query heads per kv head, INT2 K, V INT2 or
+// bf16: the three-launch matrix-core path (32-bit buffer offsets: a (sequence,
+// kv head)'s V plane, cap * 128 bytes INT2 or cap * 1024 bytes bf16, must fit)
 bool wide_shape(const oscar_kv* kv) {
   const auto& c = kv->cfg;
   const int gq = c.num_q_heads / c.num_kv_heads;
   return kv->decode_impl == 0 && c.head_dim == 512 && (gq == 1 || gq == 2 || gq == 4) &&
-         c.k_dtype == OSCAR_KV_INT2 && c.v_dtype == OSCAR_KV_INT2 && (long long)kv->cap * 128 <= INT32_MAX;
+         c.k_dtype == OSCAR_KV_INT2 && (long long)kv->cap * (c.v_dtype == OSCAR_KV_BF16 ? 1024 : 128) <= INT32_MAX;
 }
 
 int check_decode_args(const oscar_kv* kv, int32_t layer, const void* q, void* out, int32_t out_dtype,

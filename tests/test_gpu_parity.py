@@ -251,16 +251,18 @@ def test_decode_window_edges(ok, T, N, M):
     gc.close()
 
 
-@pytest.mark.parametrize("T,N,M,gq", [
-    (1, 64, 256, 2), (40, 64, 256, 2), (321, 64, 256, 2), (700, 300, 300, 2), (1000, 0, 256, 2),
-    (1000, 64, 0, 2), (1000, 0, 0, 1), (777, 13, 29, 4), (64, 0, 0, 2), (65, 1, 0, 1), (2000, 40, 600, 2),
+@pytest.mark.parametrize("T,N,M,gq,vdt", [
+    (1, 64, 256, 2, 0), (40, 64, 256, 2, 0), (321, 64, 256, 2, 0), (700, 300, 300, 2, 0), (1000, 0, 256, 2, 0),
+    (1000, 64, 0, 2, 0), (1000, 0, 0, 1, 0), (777, 13, 29, 4, 0), (64, 0, 0, 2, 0), (65, 1, 0, 1, 0),
+    (2000, 40, 600, 2, 0),
+    (1, 64, 256, 2, 1), (321, 64, 256, 2, 1), (1000, 0, 0, 1, 1), (777, 13, 29, 4, 1), (2000, 40, 600, 2, 1),
 ])
-def test_decode_wide_window_edges(ok, T, N, M, gq):
+def test_decode_wide_window_edges(ok, T, N, M, gq, vdt):
     """head_dim 512 (three-launch matrix-core path) at the window edges, the
-    ring past its wrap, 1, 2 and 4 query heads per kv head; the VALU kernel on
-    the same cache as a second check."""
-    shape = Shape(B=2, Hq=2 * gq, Hkv=2, D=512, N=N, M=M)
-    say(f"[decode wide edges] T={T} N={N} M={M} gq={gq}")
+    ring past its wrap, 1, 2 and 4 query heads per kv head, V INT2 or kept
+    bf16; the VALU kernel on the same cache as a second check."""
+    shape = Shape(B=2, Hq=2 * gq, Hkv=2, D=512, N=N, M=M, v_dtype=vdt)
+    say(f"[decode wide edges] T={T} N={N} M={M} gq={gq} v_dtype={vdt}")
     gc, rk, rv, k, v, mask = _fill(ok, shape, T, chunks=[T // 2, T - T // 2] if T > 1 else None)
     qb = query(shape, mask)
     want = oracle_on_exported(gc, 0, qb, shape, rk, rv)
@@ -277,10 +279,10 @@ def test_decode_wide_window_edges(ok, T, N, M, gq):
                       # split's running max, so splits move its rounding points;
                       # bounded by fp16's half-ulp
 ])
-@pytest.mark.parametrize("gq,D", [(4, 128), (8, 128), (2, 512)])
-def test_split_invariance(ok, impl, tol, gq, D):
-    shape = Shape(B=2, Hq=2 * gq, Hkv=2, D=D, N=64, M=256)
-    say(f"[split invariance] impl={impl} gq={gq} D={D}")
+@pytest.mark.parametrize("gq,D,vdt", [(4, 128, 0), (8, 128, 0), (2, 512, 0), (2, 512, 1)])
+def test_split_invariance(ok, impl, tol, gq, D, vdt):
+    shape = Shape(B=2, Hq=2 * gq, Hkv=2, D=D, N=64, M=256, v_dtype=vdt)
+    say(f"[split invariance] impl={impl} gq={gq} D={D} v_dtype={vdt}")
     gc, rk, rv, k, v, mask = _fill(ok, shape, 5000)
     qb = query(shape, mask)
     ref = _decode(ok, gc, 0, qb, impl=impl, splits=1)
@@ -588,3 +590,27 @@ def test_stream_read_calibration(ok):
         torch.cuda.synchronize()
         want = np.bitwise_xor.reduce(host.view(np.uint32))
         assert int(acc.cpu().numpy().view(np.uint32)[0]) == int(want), nwords
+
+
+@pytest.mark.slow
+def test_full_size_wide_64k_vbf16_sampled(ok):
+    """The wide-head shape with V kept bf16 (INT2 K only) at 64k context on
+    one layer; sequences 0 and 3 against the oracle over the exported cache."""
+    from bench import fill_layer_device
+    shape = Shape(B=4, Hq=16, Hkv=8, D=512, N=512, M=2048, outliers="percent", v_dtype=1)
+    T = 65536
+    say("[full wide 64k bf16 V] filling")
+    rk, rv = make_rotations(shape, "haar")
+    gc = gpu_cache(ok, shape, rk, rv, T + 64)
+    fill_layer_device(gc, 0, shape.B, shape.Hkv, shape.D, T, seed=0, dist="normal", outliers="percent")
+    mask = synth.outlier_mask(shape.D, shape.Hkv, 0, 0, "percent")
+    k1, v1, _ = inputs(shape, 1, chunk=99)
+    qb = query(shape, mask, step=1)
+    _step(ok, gc, 0, k1, v1, qb)
+    got = _decode(ok, gc, 0, qb)
+    for b in (0, 3):
+        want = oracle_on_exported(gc, 0, qb, shape, rk, rv, batch_idx=slice(b, b + 1))
+        e = rel_l2(got[b:b + 1], want)
+        say(f"  seq {b}: rel L2 {e:.3e}")
+        assert e <= ATTN_TOL
+    gc.close()
