@@ -44,7 +44,7 @@ def measure_read_rate(torch, ok, nbytes, reps=5):
     """Best-of-reps rate of the library's read-only streaming kernel over a
     fresh nbytes buffer, timed with HIP events on the current stream."""
     src = torch.full((nbytes // 4,), 0x01020304, dtype=torch.int32, device="cuda")
-    acc = torch.zeros(1, dtype=torch.int32, device="cuda")
+    acc = torch.zeros(8192, dtype=torch.int32, device="cuda")
     stream = torch.cuda.current_stream()
     ok.oscar_stream_read(src, nbytes, acc, stream)
     best = None

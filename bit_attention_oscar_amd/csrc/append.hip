@@ -81,37 +81,38 @@ __global__ __launch_bounds__(256) void stream_copy_kernel(const uint4* src, uint
 }
 
 // Read-only streaming: XOR of every 16-byte word (non-temporal loads, eight in
-// flight per thread), folded per block into *out with one atomic XOR.
+// flight per thread), one result word per block in out[blockIdx.x] (no atomics:
+// thousands of same-address atomics would serialise at the cache).
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 __global__ __launch_bounds__(256) void stream_read_kernel(const u32x4* __restrict__ src, size_t n,
                                                           unsigned* out) {
   constexpr int U = 8;
   const size_t stride = (size_t)gridDim.x * blockDim.x;
   size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x;
-  unsigned acc = 0;
+  // word-wise XOR into a vector accumulator: four short independent chains,
+  // so the arithmetic never holds back the next loads
+  u32x4 accv = {0, 0, 0, 0};
   for (; i + (U - 1) * stride < n; i += U * stride) {
     u32x4 v[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) v[u] = __builtin_nontemporal_load(src + i + u * stride);
 #pragma unroll
-    for (int u = 0; u < U; ++u) acc ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
+    for (int u = 0; u < U; ++u) accv ^= v[u];
   }
-  for (; i < n; i += stride) {
-    const u32x4 v = src[i];
-    acc ^= v.x ^ v.y ^ v.z ^ v.w;
-  }
+  for (; i < n; i += stride) accv ^= src[i];
+  unsigned acc = (accv.x ^ accv.y) ^ (accv.z ^ accv.w);
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) acc ^= __shfl_xor(acc, o);
   __shared__ unsigned wacc[4];
   if ((threadIdx.x & 63) == 0) wacc[threadIdx.x >> 6] = acc;
   __syncthreads();
-  if (threadIdx.x == 0) atomicXor(out, (wacc[0] ^ wacc[1]) ^ (wacc[2] ^ wacc[3]));
+  if (threadIdx.x == 0) out[blockIdx.x] = (wacc[0] ^ wacc[1]) ^ (wacc[2] ^ wacc[3]);
 }
 
 hipError_t launch_stream_read(const void* src, size_t bytes, unsigned* out, hipStream_t s) {
   const size_t n = bytes / 16;
   if (n == 0) return hipSuccess;
-  const unsigned blocks = (unsigned)std::min<size_t>((n + 255) / 256, 256 * 32);
+  const unsigned blocks = (unsigned)std::min<size_t>((n + 255) / 256, kStreamReadBlocks);
   hipLaunchKernelGGL(stream_read_kernel, dim3(blocks), dim3(256), 0, s, static_cast<const u32x4*>(src), n, out);
   return hipGetLastError();
 }

@@ -188,6 +188,7 @@ hipError_t launch_combine(const CombineArgs& a, hipStream_t s);
 hipError_t launch_wide_qrot(const DecodeArgs& a, int B, hipStream_t s);     // head_dim 512: rotated q records
 hipError_t launch_decode_wide(const DecodeArgs& a, int B, hipStream_t s);   // head_dim 512: INT2 + window partials
 hipError_t launch_stream_copy(const void* src, void* dst, size_t bytes, hipStream_t s);
+constexpr int kStreamReadBlocks = 8192;   // result words of the read calibration kernel
 hipError_t launch_stream_read(const void* src, size_t bytes, unsigned* out, hipStream_t s);
 hipError_t launch_export_codes(const uint8_t* stored, uint8_t* canon, int BH, int cap, int T, int D, int isv,
                                hipStream_t s);

@@ -202,10 +202,11 @@ int oscar_kv_profile_enable(oscar_kv* kv, int32_t enable);
 int oscar_stream_copy(const void* src, void* dst, size_t bytes, hipStream_t stream);
 
 /* Calibration kernel for the achievable HBM read rate: reads `bytes` (a
- * multiple of 16) of device buffer src once, with 16-byte non-temporal loads,
- * and XORs every 32-bit word of it into the device uint32 *xor_out (which the
- * caller initialises; the result is independent of the order).  Its
- * algorithmic traffic is exactly `bytes` read.  Errors: INVALID_ARG, HIP. */
+ * multiple of 16) of device buffer src once, with 16-byte non-temporal loads.
+ * xor_out is a device uint32 array of 8192 entries that the caller zeroes;
+ * block b of the launch writes entry b, and the XOR of all entries is the XOR
+ * of every 32-bit word of src.  Its algorithmic traffic is exactly `bytes`
+ * read (plus at most 32 KiB written).  Errors: INVALID_ARG, HIP. */
 int oscar_stream_read(const void* src, size_t bytes, void* xor_out, hipStream_t stream);
 int oscar_kv_profile_read(oscar_kv* kv, int32_t kernel_class, double* total_ms, int64_t* launches);
 

@@ -585,11 +585,12 @@ def test_stream_read_calibration(ok):
     for nwords in (4, 4 * 1000 + 4, 4 * (1 << 18)):
         host = rng.integers(0, 2 ** 31 - 1, size=nwords, dtype=np.int64).astype(np.int32)
         src = torch.from_numpy(host).cuda()
-        acc = torch.zeros(1, dtype=torch.int32, device="cuda")
+        acc = torch.zeros(8192, dtype=torch.int32, device="cuda")
         ok.oscar_stream_read(src, nwords * 4, acc)
         torch.cuda.synchronize()
         want = np.bitwise_xor.reduce(host.view(np.uint32))
-        assert int(acc.cpu().numpy().view(np.uint32)[0]) == int(want), nwords
+        got = np.bitwise_xor.reduce(acc.cpu().numpy().view(np.uint32))
+        assert int(got) == int(want), nwords
 
 
 @pytest.mark.slow
