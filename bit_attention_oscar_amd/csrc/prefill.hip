@@ -14,14 +14,14 @@
 //   is exact in fp32, so X R is computed in fp32 with only the accumulation
 //   order differing from a plain fp32 loop.
 //
-// Block = 4 waves, one (sequence, kv head), one 64-token tile (aligned to the
-// cache's 64-token tiles) and one 128-wide group: 64 rows x 128 columns, the
-// reduction over head_dim in steps of 32.  Wave w owns columns [32 w, 32 w +
-// 32) of the group: 4 row blocks x 2 column blocks of 16 x 16 accumulators.
-// The rotated tile goes through shared memory to the quantizer (one row per
-// wave at a time, as in the one-token append), and the V code tile of the 64
-// tokens and 128 dims is assembled there and written whole (2 KiB), merging
-// the bits of tokens stored before this chunk.
+// Block = 4 waves, one (sequence, kv head), one 128-token chunk (two of the
+// cache's 64-token tiles) and one 128-wide group: a 128 x 128 output tile with
+// the operands of each reduction step staged in shared memory (details at the
+// kernel).  The rotated tile goes through shared memory to the quantizer, one
+// 64-token half at a time (one row per wave at a time, as in the one-token
+// append), and the V code tile of each half's 64 tokens and 128 dims is
+// assembled there and written whole (2 KiB), merging the bits of tokens
+// stored before this chunk.
 #include "append_impl.h"
 
 namespace oscar {
@@ -30,97 +30,23 @@ typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
-struct PrefillSmem {
-  float tile[64][132];          // rotated rows, 128 columns (+4: bank offset)
-  uint8_t codes[64][128];       // 2-bit codes of the tile
-  float smax[4];
-};
-
-template <int D>
-__global__ __launch_bounds__(256) void append_prefill_kernel(AppendArgs a) {
-  constexpr int KS = D / 32;           // reduction steps
+// Quantizer epilogue of one 64-token cache tile [t0, t0 + 64) of group g:
+// rows in tile[64][132] (fp32, rotated), codes staged in codes[64][128].
+// One row per wave at a time; lane owns dims lane and lane + 64 of the group
+// (the one-token append's arithmetic).  Then the V code tile of those 64
+// tokens and 128 dims (2 KiB) is assembled and written whole.  Returns the
+// largest V scale stored (0 for K or bf16 planes).
+__device__ float prefill_epilogue(const AppendArgs& a, const PlaneDev& P, float* dump, int bh, int b, int h, int g,
+                                  int t0, float (*tile)[132], uint8_t (*codes)[128]) {
+  const int D = a.D;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const int bh = blockIdx.x;
-  const int b = bh / a.Hkv, h = bh - (bh / a.Hkv) * a.Hkv;
-  const int g = blockIdx.z >> 1;       // 128-wide group
-  const bool isv = (blockIdx.z & 1) != 0;
-  const int t0 = ((a.T_old >> 6) + (int)blockIdx.y) << 6;   // first position of the 64-token tile
-  const PlaneDev P = isv ? a.v : a.k;
-  const uint16_t* in = isv ? a.vin : a.kin;
-  const uint16_t* RT = isv ? a.rv3 : a.rk3;   // [3][D (column n)][D (row k)] bf16
-  float* dump = isv ? a.vdump : a.kdump;
-  __shared__ PrefillSmem S;
-
-  // operand addresses: A = rows t0 + 16 rb + (lane & 15), k = 8 (lane >> 4) + 32 step;
-  // B = column 128 g + 32 wave + 16 cb + (lane & 15), same k, piece s
-  const int m = lane & 15, kq = 8 * (lane >> 4);
-  const uint16_t* arow[4];
-  bool aval[4];
-#pragma unroll
-  for (int rb = 0; rb < 4; ++rb) {
-    const int t = t0 + 16 * rb + m;
-    aval[rb] = t >= a.T_old && t < a.T_new;
-    arow[rb] = in + ((((size_t)b * a.n_new + (aval[rb] ? t - a.T_old : 0)) * a.Hkv + h) * D) + kq;
-  }
-  const uint16_t* bcol[2][3];
-#pragma unroll
-  for (int cb = 0; cb < 2; ++cb)
-#pragma unroll
-    for (int s = 0; s < 3; ++s)
-      bcol[cb][s] = RT + ((size_t)s * D + 128 * g + 32 * wave + 16 * cb + m) * D + kq;
-
-  f32x4 acc[4][2];
-#pragma unroll
-  for (int rb = 0; rb < 4; ++rb)
-#pragma unroll
-    for (int cb = 0; cb < 2; ++cb) acc[rb][cb] = f32x4{0, 0, 0, 0};
-
-  // two register stages: the next step's operands load during this step's products
-  u32x4_t A[2][4], B[2][2][3];
-  auto load = [&](int st, int k0) {
-#pragma unroll
-    for (int rb = 0; rb < 4; ++rb)
-      A[st][rb] = aval[rb] ? *reinterpret_cast<const u32x4_t*>(arow[rb] + k0) : u32x4_t{0, 0, 0, 0};
-#pragma unroll
-    for (int cb = 0; cb < 2; ++cb)
-#pragma unroll
-      for (int s = 0; s < 3; ++s) B[st][cb][s] = *reinterpret_cast<const u32x4_t*>(bcol[cb][s] + k0);
-  };
-  load(0, 0);
-#pragma unroll
-  for (int ks = 0; ks < KS; ++ks) {
-    const int st = ks & 1;
-    if (ks + 1 < KS) load(st ^ 1, 32 * (ks + 1));
-#pragma unroll
-    for (int s = 0; s < 3; ++s)
-#pragma unroll
-      for (int rb = 0; rb < 4; ++rb)
-#pragma unroll
-        for (int cb = 0; cb < 2; ++cb)
-          acc[rb][cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, A[st][rb]),
-                                                                __builtin_bit_cast(bf16x8_t, B[st][cb][s]),
-                                                                acc[rb][cb], 0, 0, 0);
-  }
-
-  // accumulator (rb, cb) register i: row 16 rb + 4 (lane >> 4) + i, column 16 cb + (lane & 15)
-#pragma unroll
-  for (int rb = 0; rb < 4; ++rb)
-#pragma unroll
-    for (int cb = 0; cb < 2; ++cb)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) S.tile[16 * rb + 4 * (lane >> 4) + i][32 * wave + 16 * cb + m] = acc[rb][cb][i];
-  if (tid < 4) S.smax[tid] = 0.0f;
-  __syncthreads();
-
-  // quantizer, one row per wave at a time: lane owns dims lane and lane + 64
-  // of the group (the one-token append's arithmetic from here on)
   float wsmax = 0.0f;
   for (int r = wave; r < 64; r += 4) {
     const int t = t0 + r;
     if (t < a.T_old || t >= a.T_new) continue;       // wave-uniform
     float x[2];
-    x[0] = S.tile[r][lane] + 0.0f;
-    x[1] = S.tile[r][lane + 64] + 0.0f;
+    x[0] = tile[r][lane] + 0.0f;
+    x[1] = tile[r][lane + 64] + 0.0f;
     const int d0 = 128 * g + lane;
     if (dump) {
       const size_t base = (((size_t)b * a.n_new + (t - a.T_old)) * a.Hkv + h) * D;
@@ -154,17 +80,12 @@ __global__ __launch_bounds__(256) void append_prefill_kernel(AppendArgs a) {
         return reinterpret_cast<uint32_t*>(P.codes + kcode_byte(bh, a.cap, t, 32 * g + 4 * w, D));
       });
     } else {
-      S.codes[r][lane] = (uint8_t)code[0];
-      S.codes[r][lane + 64] = (uint8_t)code[1];
+      codes[r][lane] = (uint8_t)code[0];
+      codes[r][lane + 64] = (uint8_t)code[1];
     }
   }
-  if (P.is_bf16) return;
-  if (P.smax && lane == 0) atomicMax(reinterpret_cast<unsigned int*>(&S.smax[0]), __float_as_uint(wsmax));
+  if (P.is_bf16 || !P.tiled) return wsmax;
   __syncthreads();
-  if (P.smax && tid == 0 && S.smax[0] > 0.0f)
-    atomicMax(reinterpret_cast<unsigned int*>(P.smax + bh), __float_as_uint(S.smax[0]));
-  if (!P.tiled) return;
-
   // V code tile of tokens [t0, t0 + 64), dims [128 g, 128 g + 128): 2 KiB, 8
   // bytes per thread.  Byte p: half p >> 10, lane record (p >> 4) & 63, record
   // byte rec = 16 half + (p & 15) holds dim 64 (rec & 1) + 4 (l >> 2) + (l & 3)
@@ -183,7 +104,7 @@ __global__ __launch_bounds__(256) void append_prefill_kernel(AppendArgs a) {
       const int tb = tb0 + 2 * (q & 1) + 4 * (q >> 1);
       const int t = t0 + tb;
       if (t >= a.T_old && t < a.T_new)
-        byte |= (uint32_t)S.codes[tb][ds] << (2 * q);
+        byte |= (uint32_t)codes[tb][ds] << (2 * q);
       else
         keep |= 3u << (2 * q);
     }
@@ -191,10 +112,148 @@ __global__ __launch_bounds__(256) void append_prefill_kernel(AppendArgs a) {
     if (keep) byte |= vt[p] & keep;
     vt[p] = (uint8_t)byte;
   }
+  return wsmax;
+}
+
+// Shared memory: the operand stage of one reduction step (A: 128 rows x 32
+// k, B: 3 pieces x 128 columns x 32 k, bf16, rows padded to 40 elements so
+// that 16 lanes reading 16 rows at one k offset hit distinct banks), reused
+// after the product for one 64-row half of the rotated tile and its codes.
+struct PrefillSmem {
+  union {
+    struct {
+      uint16_t A[128][40];
+      uint16_t B[3][128][40];
+    } st;
+    struct {
+      float tile[64][132];
+      uint8_t codes[64][128];
+    } ep;
+  };
+  float smax[4];
+};
+
+// Block = 4 waves, one (sequence, kv head), one 128-token chunk (two of the
+// cache's 64-token tiles) and one 128-wide group of K or V: a 128 x 128 output
+// tile, the reduction over head_dim in steps of 32.  Each step's operands are
+// loaded from memory by all 256 threads into registers (8 x 16 bytes each),
+// written to shared memory, and read back by the waves: wave (wr, wc) owns rows
+// [64 wr, 64 wr + 64) and columns [64 wc, 64 wc + 64), 4 x 4 accumulators of
+// 16 x 16; 48 products per wave per step.  The next step's loads are in
+// flight during this step's products.
+template <int D>
+__global__ __launch_bounds__(256) void append_prefill_kernel(AppendArgs a) {
+  constexpr int KS = D / 32;           // reduction steps
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int bh = blockIdx.x;
+  const int b = bh / a.Hkv, h = bh - (bh / a.Hkv) * a.Hkv;
+  const int g = blockIdx.z >> 1;       // 128-wide group
+  const bool isv = (blockIdx.z & 1) != 0;
+  const int t0 = ((a.T_old >> 7) + (int)blockIdx.y) << 7;   // first position of the 128-token chunk
+  const PlaneDev P = isv ? a.v : a.k;
+  const uint16_t* in = isv ? a.vin : a.kin;
+  const uint16_t* RT = isv ? a.rv3 : a.rk3;   // [3][D (column n)][D (row k)] bf16
+  float* dump = isv ? a.vdump : a.kdump;
+  __shared__ PrefillSmem S;
+
+  // global -> register staging: A chunks j = tid, tid + 256 (row j >> 2, 16-byte
+  // piece j & 3 of its 32 k); B chunks j = tid + 256 i, i < 6 (piece j / 512,
+  // column (j >> 2) & 127, 16-byte piece j & 3)
+  const uint16_t* asrc[2];
+  bool aval[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int j = tid + 256 * i, row = j >> 2, t = t0 + row;
+    aval[i] = t >= a.T_old && t < a.T_new;
+    asrc[i] = in + ((((size_t)b * a.n_new + (aval[i] ? t - a.T_old : 0)) * a.Hkv + h) * D) + 8 * (j & 3);
+  }
+  const uint16_t* bsrc[6];
+#pragma unroll
+  for (int i = 0; i < 6; ++i) {
+    const int j = tid + 256 * i, s = j >> 9, col = (j >> 2) & 127;
+    bsrc[i] = RT + ((size_t)s * D + 128 * g + col) * D + 8 * (j & 3);
+  }
+  u32x4_t ra[2], rb_[6];
+  auto gload = [&](int k0) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+      ra[i] = aval[i] ? *reinterpret_cast<const u32x4_t*>(asrc[i] + k0) : u32x4_t{0, 0, 0, 0};
+#pragma unroll
+    for (int i = 0; i < 6; ++i) rb_[i] = *reinterpret_cast<const u32x4_t*>(bsrc[i] + k0);
+  };
+  auto sstore = [&]() {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int j = tid + 256 * i;
+      *reinterpret_cast<u32x4_t*>(&S.st.A[j >> 2][8 * (j & 3)]) = ra[i];
+    }
+#pragma unroll
+    for (int i = 0; i < 6; ++i) {
+      const int j = tid + 256 * i;
+      *reinterpret_cast<u32x4_t*>(&S.st.B[j >> 9][(j >> 2) & 127][8 * (j & 3)]) = rb_[i];
+    }
+  };
+
+  const int wr = wave >> 1, wc = wave & 1;
+  const int m = lane & 15, kq = 8 * (lane >> 4);
+  f32x4 acc[4][4];
+#pragma unroll
+  for (int rb = 0; rb < 4; ++rb)
+#pragma unroll
+    for (int cb = 0; cb < 4; ++cb) acc[rb][cb] = f32x4{0, 0, 0, 0};
+
+  gload(0);
+  sstore();
+  __syncthreads();
+  for (int ks = 0; ks < KS; ++ks) {
+    if (ks + 1 < KS) gload(32 * (ks + 1));
+    u32x4_t fa[4];
+#pragma unroll
+    for (int rb = 0; rb < 4; ++rb) fa[rb] = *reinterpret_cast<const u32x4_t*>(&S.st.A[64 * wr + 16 * rb + m][kq]);
+#pragma unroll
+    for (int s = 0; s < 3; ++s)
+#pragma unroll
+      for (int cb = 0; cb < 4; ++cb) {
+        const u32x4_t fb = *reinterpret_cast<const u32x4_t*>(&S.st.B[s][64 * wc + 16 * cb + m][kq]);
+#pragma unroll
+        for (int rb = 0; rb < 4; ++rb)
+          acc[rb][cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, fa[rb]),
+                                                                __builtin_bit_cast(bf16x8_t, fb), acc[rb][cb], 0, 0, 0);
+      }
+    __syncthreads();                     // every wave has read this step's operands
+    if (ks + 1 < KS) {
+      sstore();
+      __syncthreads();
+    }
+  }
+
+  // two halves of 64 rows (one cache tile each): accumulator (rb, cb)
+  // register i is row 64 wr + 16 rb + 4 (lane >> 4) + i, column 64 wc + 16 cb + m
+  if (tid < 4) S.smax[tid] = 0.0f;
+  float wsmax = 0.0f;
+  for (int half = 0; half < 2; ++half) {
+    if (wr == half) {
+#pragma unroll
+      for (int rb = 0; rb < 4; ++rb)
+#pragma unroll
+        for (int cb = 0; cb < 4; ++cb)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) S.ep.tile[16 * rb + 4 * (lane >> 4) + i][64 * wc + 16 * cb + m] = acc[rb][cb][i];
+    }
+    __syncthreads();
+    const int th = t0 + 64 * half;
+    if (th < a.T_new && th + 64 > a.T_old)
+      wsmax = fmaxf(wsmax, prefill_epilogue(a, P, dump, bh, b, h, g, th, S.ep.tile, S.ep.codes));
+    __syncthreads();                     // the tile and codes are rewritten by the next half
+  }
+  if (P.smax && lane == 0 && wsmax > 0.0f) atomicMax(reinterpret_cast<unsigned int*>(&S.smax[0]), __float_as_uint(wsmax));
+  __syncthreads();
+  if (P.smax && tid == 0 && S.smax[0] > 0.0f)
+    atomicMax(reinterpret_cast<unsigned int*>(P.smax + bh), __float_as_uint(S.smax[0]));
 }
 
 hipError_t launch_append_prefill(const AppendArgs& a, hipStream_t s) {
-  const int tiles = ((a.T_new - 1) >> 6) - (a.T_old >> 6) + 1;
+  const int tiles = ((a.T_new - 1) >> 7) - (a.T_old >> 7) + 1;   // 128-token chunks
   dim3 grid((unsigned)(a.batch * a.Hkv), (unsigned)tiles, (unsigned)(2 * (a.D / 128)));
   if (a.D == 128)
     hipLaunchKernelGGL(append_prefill_kernel<128>, grid, dim3(256), 0, s, a);
