@@ -40,6 +40,22 @@ WORKLOADS = {
 }
 
 
+def prefill_summary(timings, B, Hkv, D):
+    """The last fill chunk of every layer is a chunked-prefill append timed
+    with HIP events: its rotation is a dense product (2 n B Hkv D^2 flops for K
+    and the same for V) that runs on the matrix cores as three bf16 products
+    (R held as three bf16 pieces)."""
+    if not timings:
+        return None
+    n = timings[0][0]
+    ms = sorted(t for _, t in timings)[len(timings) // 2]
+    useful = 2 * 2 * n * B * Hkv * D * D / (ms / 1e3) / 1e12
+    return {"tokens_per_chunk": n, "median_ms_per_layer": round(ms, 4), "layers": len(timings),
+            "useful_TFLOPs": round(useful, 1), "mfma_TFLOPs": round(3 * useful, 1),
+            "mfma_peak_TFLOPs": 2500.0, "mfma_util": round(3 * useful / 2500.0, 4),
+            "kernel": "append_prefill_kernel"}
+
+
 def measure_read_rate(torch, ok, nbytes, reps=5):
     """Best-of-reps rate of the library's read-only streaming kernel over a
     fresh nbytes buffer, timed with HIP events on the current stream."""
@@ -66,8 +82,11 @@ def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
-def fill_layer_device(cache, layer, B, Hkv, D, T, seed=0, dist="normal", outliers="percent", chunk=4096):
-    """Append T synthetic tokens per sequence to `layer`, generated on the device."""
+def fill_layer_device(cache, layer, B, Hkv, D, T, seed=0, dist="normal", outliers="percent", chunk=4096,
+                      timings=None):
+    """Append T synthetic tokens per sequence to `layer`, generated on the
+    device.  With `timings` (a list), the last chunk's append is timed with HIP
+    events and its (tokens, ms) appended."""
     import torch
     import synth
     mask = torch.from_numpy(synth.outlier_mask(D, Hkv, seed, layer, outliers)).cuda()
@@ -77,7 +96,16 @@ def fill_layer_device(cache, layer, B, Hkv, D, T, seed=0, dist="normal", outlier
         n = min(chunk, T - t)
         k = synth.device_kv_fill((B, n, Hkv, D), synth.seed_of(seed, layer, "k", 1000 + ci), "cuda", mask, dist)
         v = synth.device_kv_fill((B, n, Hkv, D), synth.seed_of(seed, layer, "v", 1000 + ci), "cuda", mask, dist)
-        cache.append(layer, k, v)
+        last = t + n >= T
+        if timings is not None and last:
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            cache.append(layer, k, v)
+            e1.record()
+            torch.cuda.synchronize()
+            timings.append((n, e0.elapsed_time(e1)))
+        else:
+            cache.append(layer, k, v)
         t += n
         ci += 1
     return mask
@@ -251,8 +279,9 @@ def main():
     log(f"cache {cache.device_bytes() / 2**30:.2f} GiB; filling {T0} tokens x {L} layers")
     t_fill = time.perf_counter()
     masks = []
+    prefill_t = []
     for l in range(L):
-        masks.append(fill_layer_device(cache, l, B, Hkv, D, T0, seed=0, dist=dist, outliers=outl))
+        masks.append(fill_layer_device(cache, l, B, Hkv, D, T0, seed=0, dist=dist, outliers=outl, timings=prefill_t))
     torch.cuda.synchronize()
     log(f"filled in {time.perf_counter() - t_fill:.1f} s")
 
@@ -355,6 +384,7 @@ def main():
         "append_us_per_call": round(app_ms / max(app_n, 1) * 1e3, 3),
         "host_enqueue_ms_per_step": round(enqueue * 1e3 / K, 4),
         "hbm_read_measured": read_cal,
+        "prefill": prefill_summary(prefill_t, B, Hkv, D),
         "roofline": roof,
     }
     if not args.no_cpu_baseline:
