@@ -152,7 +152,7 @@ int oscar_kv_device_bytes(const oscar_kv* kv, size_t* bytes);
 
 /* Force the number of splits per (sequence, kv head) used by decode attention
  * (INT2 splits of the matrix-core kernel, or all-token splits of the VALU
- * kernel), in [0, 224]; 0 restores the automatic choice.  The count is capped
+ * kernel), in [0, 208]; 0 restores the automatic choice.  The count is capped
  * by the number of 64-token tiles.  Errors: INVALID_ARG. */
 int oscar_kv_set_num_splits(oscar_kv* kv, int32_t num_splits);
 
