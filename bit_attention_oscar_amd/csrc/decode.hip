@@ -55,6 +55,12 @@ typedef float f4 __attribute__((ext_vector_type(4)));
 #ifndef OSCAR_WIDE_WIN_FIRST
 #define OSCAR_WIDE_WIN_FIRST 1
 #endif
+// The q-publishing block issues its first tile's loads after the flag: the
+// flag waits for every earlier memory operation of the block to complete, so
+// a tile issued before it would delay every waiting block by an HBM latency.
+#ifndef OSCAR_PUBLISH_FIRST
+#define OSCAR_PUBLISH_FIRST 1
+#endif
 constexpr int kDepth = OSCAR_TILE_DEPTH;
 
 __device__ inline float wmax(float v) {
@@ -1250,8 +1256,10 @@ void decode_mfma_kernel(DecodeArgs a) {
   TileRegs r[kDepth];
   if (self_rotate) {
     const QRotLoads qload = q_rotation_loads(a, b, hq_of(0));
+#if !OSCAR_PUBLISH_FIRST
     __builtin_amdgcn_sched_barrier(0);
     r[0] = load_tile(st, tile_t0(min(ti0, t_last)), lane_c, lane_m);
+#endif
     __builtin_amdgcn_sched_barrier(0);
     q_rotation_finish(a, qload, S);
     publish_q(a, bh * G, S);
@@ -1262,6 +1270,9 @@ void decode_mfma_kernel(DecodeArgs a) {
       publish_q(a, bh * G + g, S);
     }
     publish_flag(a, bh);
+#if OSCAR_PUBLISH_FIRST
+    r[0] = load_tile(st, tile_t0(min(ti0, t_last)), lane_c, lane_m);
+#endif
 #pragma unroll
     for (int k = 1; k < kDepth; ++k) r[k] = load_tile(st, tile_t0(min(ti0 + k * WPB, t_last)), lane_c, lane_m);
     operands_from_smem(G - 1);
