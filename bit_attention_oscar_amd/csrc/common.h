@@ -186,6 +186,7 @@ hipError_t launch_decode_mfma(const DecodeArgs& a, int B, int waves_per_block, h
 int decode_mfma_resident_blocks(int device, int G);   // blocks of the matrix-core kernel resident at once
 hipError_t launch_combine(const CombineArgs& a, hipStream_t s);
 hipError_t launch_wide_qrot(const DecodeArgs& a, int B, hipStream_t s);     // head_dim 512: rotated q records
+                                                                            // (and the step's append when a.app_blocks)
 hipError_t launch_decode_wide(const DecodeArgs& a, int B, hipStream_t s);   // head_dim 512: INT2 + window partials
 hipError_t launch_stream_copy(const void* src, void* dst, size_t bytes, hipStream_t s);
 constexpr int kStreamReadBlocks = 8192;   // result words of the read calibration kernel

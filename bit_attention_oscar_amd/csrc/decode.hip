@@ -1484,16 +1484,13 @@ void decode_mfma_kernel(DecodeArgs a) {
 // V code tiles, its scales, its part of the scores and of the output.  The
 // four partial scores meet in shared memory once per tile.
 
-// q rotation of one 128-dim slice of the rotated q, all heads of a kv head
-// (zero-padded to 4).  Grid: (sequence x kv head, slice).
-__global__ __launch_bounds__(256) void wide_qrot_kernel(DecodeArgs a) {
+// q rotation of one 128-dim slice s of the rotated q, all heads of a kv head
+// (zero-padded to 4), published as the slice's record.
+__device__ void wide_qrot_block(const DecodeArgs& a, int bh, int s, FusedSmem& S, float* qraw,
+                                float (*parts)[4][128]) {
   constexpr int D = 512;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const int bh = blockIdx.x, s = blockIdx.y;
   const int b = bh / a.Hkv, h = bh - (bh / a.Hkv) * a.Hkv;
-  __shared__ FusedSmem S;
-  __shared__ float qraw[4 * D];
-  __shared__ float parts[4][4][128];
   for (int i = tid; i < 4 * D; i += 256) {
     const int j = i / D, e = i - j * D;
     qraw[i] = j < a.Gq ? bf16_to_f32(a.q[((size_t)b * a.Hq + h * a.Gq + j) * D + e]) : 0.0f;
@@ -1532,6 +1529,28 @@ __global__ __launch_bounds__(256) void wide_qrot_kernel(DecodeArgs a) {
   }
   __syncthreads();
   publish_q(a, bh * 4 + s, S);
+}
+
+// Grid: (sequence x kv head, slice).
+__global__ __launch_bounds__(256) void wide_qrot_kernel(DecodeArgs a) {
+  __shared__ FusedSmem S;
+  __shared__ float qraw[4 * 512];
+  __shared__ float parts[4][4][128];
+  wide_qrot_block(a, (int)blockIdx.x, (int)blockIdx.y, S, qraw, parts);
+}
+
+// The decode step's first launch at head_dim 512: blocks y < 4 write the q
+// records (slice y), blocks 4 + 2 g + v append the new token's group g of K
+// (v = 0) or V (v = 1).  The attention launch that follows reads both.
+__global__ __launch_bounds__(256) void wide_prologue_kernel(DecodeArgs a) {
+  __shared__ FusedSmem S;
+  __shared__ float qraw[4 * 512];
+  __shared__ float parts[4][4][128];
+  const int y = (int)blockIdx.y;
+  if (y < 4)
+    wide_qrot_block(a, (int)blockIdx.x, y, S, qraw, parts);
+  else
+    append_slice_block(a.app, (int)blockIdx.x, ((y - 4) & 1) != 0, (y - 4) >> 1, qraw, &parts[0][0][0]);
 }
 
 struct WideSmem {
@@ -2143,7 +2162,10 @@ hipError_t launch_decode_mfma(const DecodeArgs& a, int B, int waves_per_block, h
 }
 
 hipError_t launch_wide_qrot(const DecodeArgs& a, int B, hipStream_t s) {
-  hipLaunchKernelGGL(wide_qrot_kernel, dim3((unsigned)(B * a.Hkv), 4), dim3(256), 0, s, a);
+  if (a.app_blocks > 0)
+    hipLaunchKernelGGL(wide_prologue_kernel, dim3((unsigned)(B * a.Hkv), 4 + 8), dim3(256), 0, s, a);
+  else
+    hipLaunchKernelGGL(wide_qrot_kernel, dim3((unsigned)(B * a.Hkv), 4), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 

@@ -655,9 +655,10 @@ int oscar_kv_decode_step(oscar_kv* kv, int32_t layer, const void* k, const void*
     return fail(OSCAR_ERR_INVALID_ARG, "batch differs from the batch this layer was filled with");
   if ((long long)L.T + 1 > kv->cfg.max_context)
     return fail(OSCAR_ERR_CAPACITY, "decode step at " + std::to_string(L.T) + " tokens exceeds max_context");
-  if (!fast_shape(kv) || kv->cfg.recent_tokens < 1) {
+  if (!(fast_shape(kv) && kv->cfg.recent_tokens >= 1) && !wide_shape(kv)) {
     // separate launches: the appended token is not a bf16 window token here or
-    // the shape has no fused kernel
+    // the shape has no fused kernel (head_dim 512 fuses the append with its q
+    // rotation launch instead)
     rc = do_append(kv, layer, k, v, batch, 1, nullptr, nullptr, stream);
     if (rc) return rc;
     return launch_decode(kv, layer, q, out, out_dtype, batch, softmax_scale, L.T, nullptr, stream);

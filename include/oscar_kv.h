@@ -123,15 +123,17 @@ int oscar_int2_decode_attn(oscar_kv* kv, int32_t layer, const void* q, void* out
  * n_new = 1) followed by oscar_int2_decode_attn(q, out); the stored cache is
  * identical bit for bit.
  *   k, v: device bf16 [batch][1][Hkv][D]; q, out as in decode_attn.
- * Where the shape has the matrix-core kernel (head_dim 128, 4 query heads per
- * kv head, INT2 K and V) and recent_tokens >= 1, append and attention run in
- * one launch.  The new token is then a bf16 window token: the attention
+ * Where the shape has the head_dim 128 matrix-core kernel (4 or 8 query heads
+ * per kv head, INT2 K and V) and recent_tokens >= 1, append and attention run
+ * in one launch.  The new token is then a bf16 window token: the attention
  * blocks compute its window value from k, v themselves, and of what the
  * append writes they read only bytes whose bits for other tokens it leaves
  * unchanged (a V code tile it shares with older tokens) or a running maximum
  * that only grows (the V scale maximum, which only sets a power-of-two operand
- * scale), so every order of the blocks gives a correct result.  Other shapes
- * run the two calls' launches in turn. */
+ * scale), so every order of the blocks gives a correct result.  At head_dim
+ * 512 (matrix-core path) the append runs in the same launch as the q
+ * rotation, before the attention launch.  Other shapes run the two calls'
+ * launches in turn. */
 int oscar_kv_decode_step(oscar_kv* kv, int32_t layer, const void* k, const void* v, const void* q,
                          void* out, int32_t out_dtype, int32_t batch, float softmax_scale,
                          hipStream_t stream);
