@@ -1260,13 +1260,23 @@ void decode_mfma_kernel(DecodeArgs a) {
     __builtin_amdgcn_sched_barrier(0);
     r[0] = load_tile(st, tile_t0(min(ti0, t_last)), lane_c, lane_m);
 #endif
+#if OSCAR_PUBLISH_FIRST
+    // with no tile registers live yet, the second group's loads go out in the
+    // same round trip as the first's
+    QRotLoads qload1;
+    if constexpr (G > 1) qload1 = q_rotation_loads(a, b, hq_of(1));
+#endif
     __builtin_amdgcn_sched_barrier(0);
     q_rotation_finish(a, qload, S);
     publish_q(a, bh * G, S);
 #pragma unroll
     for (int g = 1; g < G; ++g) {
       operands_from_smem(g - 1);
+#if OSCAR_PUBLISH_FIRST
+      q_rotation_finish(a, qload1, S);
+#else
       block_rotate_q_chunked(a, b, hq_of(g), S);
+#endif
       publish_q(a, bh * G + g, S);
     }
     publish_flag(a, bh);

@@ -282,6 +282,10 @@ int do_append(oscar_kv* kv, int32_t layer, const void* k, const void* v, int32_t
 #define OSCAR_WIN_TOKENS 192
 #endif
 constexpr int kWinTokens = OSCAR_WIN_TOKENS;
+#ifndef OSCAR_WIN_TOKENS_G2
+#define OSCAR_WIN_TOKENS_G2 128
+#endif
+constexpr int kWinTokensG2 = OSCAR_WIN_TOKENS_G2;
 // head_dim 512: bf16 window tokens per window block, INT2 blocks per launch
 #ifndef OSCAR_WIDE_WIN_TOKENS
 #define OSCAR_WIDE_WIN_TOKENS 256
@@ -533,7 +537,9 @@ int launch_decode(oscar_kv* kv, int32_t layer, const void* q, void* out, int32_t
       // the launch leaves compute units idle (small batches, long windows), one
       // pass per block shortens the critical path.  Measured at batch 1, 16k
       // context, 2560 window tokens: 26.9 us per launch against 36.7 us.
-      int want_w = (hp_len + kWinTokens - 1) / kWinTokens;
+      // two head groups double a window block's passes: shorter blocks
+      const int wt = da.Gq == 8 ? kWinTokensG2 : kWinTokens;
+      int want_w = (hp_len + wt - 1) / wt;
       const int int2_len = std::max(0, int2_hi - int2_lo);
       if ((long long)hp_len * 16 >= int2_len &&
           (long long)BH * ((hp_len + kSmallWinTokens - 1) / kSmallWinTokens) * 2 <= kv->resident)

@@ -402,6 +402,8 @@ def _exports_equal(g1, g2, layer, N, M):
     (Shape(B=1, Hq=4, Hkv=1, N=64, M=256), 300, 4),            # every token still bf16
     (Shape(B=2, Hq=16, Hkv=2, N=8, M=40), 700, 6),             # GQA 8: two head groups per kv head
     (Shape(B=1, Hq=8, Hkv=1, N=3, M=5), 66, 40),               # GQA 8, ring wraps, tile edges crossed
+    (Shape(B=2, Hq=4, Hkv=2, D=512, N=8, M=16), 0, 40),        # head_dim 512 from an empty cache, ring wraps
+    (Shape(B=1, Hq=4, Hkv=2, D=512, N=8, M=16, v_dtype=1), 60, 10),  # head_dim 512, V kept bf16
 ])
 def test_decode_step_equals_append_then_decode(ok, shape, T0, steps):
     """The fused step (append and attention in one launch) against the two
