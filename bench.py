@@ -220,6 +220,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="qwen3-8b-attn-32k", choices=sorted(WORKLOADS))
     ap.add_argument("--splits", type=int, default=0, help="force INT2 splits (0 = auto)")
+    ap.add_argument("--absorb-v", action="store_true",
+                    help="V rotation absorbed into the caller's output projection: outputs stay in the "
+                         "V-rotated basis (no un-rotation in the merge)")
     ap.add_argument("--separate", action="store_true",
                     help="append and attention as two calls per layer instead of the fused step")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -273,7 +276,8 @@ def main():
     rk = synth.rotations(L, D, 0, "rot_k")
     rv = synth.rotations(L, D, 0, "rot_v")
     cap = T0 + W + 2 * K + 64
-    cache = ok.KVCache(L, B, Hq, Hkv, D, cap, N, M, 128, 0.96, 0.92, ok.KV_INT2, vdt, rk, rv, 0)
+    cache = ok.KVCache(L, B, Hq, Hkv, D, cap, N, M, 128, 0.96, 0.92, ok.KV_INT2, vdt, rk, rv, 0,
+                       1 if args.absorb_v else 0)
     if args.splits:
         cache.set_num_splits(args.splits)
     log(f"cache {cache.device_bytes() / 2**30:.2f} GiB; filling {T0} tokens x {L} layers")
@@ -382,6 +386,7 @@ def main():
         "config": {"workload": args.workload, "layers": L, "batch": B, "q_heads": Hq, "kv_heads": Hkv,
                    "head_dim": D, "context": T0, "sink": N, "recent": M, "group": 128,
                    "k_clip": 0.96, "v_clip": 0.92, "v_cache": "bf16" if vdt else "int2",
+                   "absorb_v_rotation": bool(args.absorb_v),
                    "parallelism": "none (1 GPU)"},
         "kv_gbps": round(kv_gbs, 1),
         "kv_hbm_frac": round(kv_gbs / HBM_PEAK_GBS, 4),

@@ -145,6 +145,7 @@ struct CombineArgs {
   void* out;
   int out_dtype;
   int B, Hq, Hkv, D, nslots;
+  int absorb_v;            // 1: write the merged o' (V-rotated basis), no un-rotation
 };
 
 struct DecodeArgs {

@@ -388,6 +388,16 @@ __device__ inline float ld_partial(const float* p) {
   return *p;
 }
 
+// One output element in the requested dtype.
+__device__ inline void store_out(const CombineArgs& a, size_t o, float v) {
+  if (a.out_dtype == 0)
+    reinterpret_cast<float*>(a.out)[o] = v;
+  else if (a.out_dtype == 1)
+    reinterpret_cast<uint16_t*>(a.out)[o] = f32_to_bf16(v);
+  else
+    reinterpret_cast<uint16_t*>(a.out)[o] = __builtin_bit_cast(uint16_t, (_Float16)v);
+}
+
 // CC > 1: the block computes output columns [cc D / CC, (cc + 1) D / CC) only
 // (it still merges every dim of o', which the un-rotation reduces over).
 template <int D, bool COHERENT = false, int CC = 1>
@@ -467,6 +477,14 @@ __device__ void combine_group(const CombineArgs& a, int bh, int cc = 0) {
       os[j][d + 1] = acc1;
     }
     __syncthreads();
+    if (a.absorb_v) {                     // o' in the V-rotated basis, this block's columns
+      for (int idx = tid; idx < nh * NC; idx += 256) {
+        const int j = idx / NC, d = idx - (idx / NC) * NC;
+        store_out(a, ((size_t)b * a.Hq + kvh * Gq + hc + j) * D + c0 + d, os[j][c0 + d]);
+      }
+      __syncthreads();
+      continue;
+    }
     // o = o' @ R_V^T for this block's columns: lane pair-columns 2 lane + 128 i
 #pragma unroll
     for (int i = 0; i < PER / 2; ++i) {
@@ -484,13 +502,7 @@ __device__ void combine_group(const CombineArgs& a, int bh, int cc = 0) {
     for (int idx = tid; idx < nh * NC; idx += 256) {
       const int j = idx / NC, d = idx - (idx / NC) * NC;
       const float v = ((part[0][j][d] + part[1][j][d]) + part[2][j][d]) + part[3][j][d];
-      const size_t o = ((size_t)b * a.Hq + kvh * Gq + hc + j) * D + c0 + d;
-      if (a.out_dtype == 0)
-        reinterpret_cast<float*>(a.out)[o] = v;
-      else if (a.out_dtype == 1)
-        reinterpret_cast<uint16_t*>(a.out)[o] = f32_to_bf16(v);
-      else
-        reinterpret_cast<uint16_t*>(a.out)[o] = __builtin_bit_cast(uint16_t, (_Float16)v);
+      store_out(a, ((size_t)b * a.Hq + kvh * Gq + hc + j) * D + c0 + d, v);
     }
     __syncthreads();
   }
@@ -751,7 +763,8 @@ template <int G>
 __device__ void combine_fused(const CombineArgs& a, int bh, FusedSmem& S) {
   constexpr int D = 128;
   const int b = bh / a.Hkv, kvh = bh - (bh / a.Hkv) * a.Hkv;
-  const RRows<D, 4> rr = load_r_rows<D, 4>(a.rvT);
+  RRows<D, 4> rr;
+  if (!a.absorb_v) rr = load_r_rows<D, 4>(a.rvT);
 #pragma unroll
   for (int g = 0; g < G; ++g) combine_group4(a, b, kvh * 4 * G + 4 * g, rr, S);
 }
@@ -791,6 +804,11 @@ __device__ __forceinline__ void combine_group4(const CombineArgs& a, int b, int 
     M = mb;
   }
   const float inv = 1.0f / L;
+  if (a.absorb_v) {                       // o' in the V-rotated basis
+    store_out(a, ((size_t)b * a.Hq + hq0 + wave) * D + lane, o0 * inv);
+    store_out(a, ((size_t)b * a.Hq + hq0 + wave) * D + lane + 64, o1 * inv);
+    return;
+  }
   float* os = S.scratch;                  // [4][128]
   float* part = S.scratch + 4 * D;        // [4 waves][4][128]
   os[wave * D + lane] = o0 * inv;
@@ -800,14 +818,7 @@ __device__ __forceinline__ void combine_group4(const CombineArgs& a, int b, int 
   __syncthreads();
   for (int idx = tid; idx < 4 * D; idx += 256) {
     const int j = idx >> 7, d = idx & 127;
-    const float v = rot_sum<D, 4, 4>(part, j, d);
-    const size_t o = ((size_t)b * a.Hq + hq0 + j) * D + d;
-    if (a.out_dtype == 0)
-      reinterpret_cast<float*>(a.out)[o] = v;
-    else if (a.out_dtype == 1)
-      reinterpret_cast<uint16_t*>(a.out)[o] = f32_to_bf16(v);
-    else
-      reinterpret_cast<uint16_t*>(a.out)[o] = __builtin_bit_cast(uint16_t, (_Float16)v);
+    store_out(a, ((size_t)b * a.Hq + hq0 + j) * D + d, rot_sum<D, 4, 4>(part, j, d));
   }
   __syncthreads();                        // os / part are rewritten by the next group
 }

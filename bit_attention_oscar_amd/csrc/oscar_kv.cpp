@@ -172,6 +172,8 @@ int validate_config(const oscar_kv_config* c) {
     return fail(OSCAR_ERR_INVALID_ARG, "unknown kv dtype");
   if ((long long)c->max_batch * c->num_q_heads > (1 << 30))
     return fail(OSCAR_ERR_INVALID_ARG, "batch x heads too large");
+  if (c->absorb_v_rotation != 0 && c->absorb_v_rotation != 1)
+    return fail(OSCAR_ERR_INVALID_ARG, "absorb_v_rotation must be 0 or 1");
   return OSCAR_OK;
 }
 
@@ -519,6 +521,7 @@ int launch_decode(oscar_kv* kv, int32_t layer, const void* q, void* out, int32_t
   ca.Hq = Hq;
   ca.Hkv = Hkv;
   ca.D = D;
+  ca.absorb_v = c.absorb_v_rotation != 0;
   const int BH = batch * Hkv;
 
   // token sets: sink [0, min(N,T)), recent [max(N, T-M), T), INT2 [N, T-M)

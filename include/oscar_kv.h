@@ -84,6 +84,10 @@ typedef struct {
   const float* rot_k;       /* host fp32 [num_layers][D][D], row-major; NULL = identity */
   const float* rot_v;       /* host fp32 [num_layers][D][D], row-major; NULL = identity */
   int32_t device;           /* HIP device ordinal                              */
+  int32_t absorb_v_rotation; /* 1: decode attention returns o' = the output in the
+                              * V-rotated basis (the caller folds R_V^T into its
+                              * output projection: RotationZoo "How to use", the
+                              * sglang flag that absorbs the V rotation); 0: o = o' R_V^T */
 } oscar_kv_config;
 
 typedef struct oscar_kv oscar_kv;

@@ -351,7 +351,7 @@ def softmax_attention_f64(q: np.ndarray, K: np.ndarray, V: np.ndarray, scale: fl
 def decode_attention(q_bits: np.ndarray, kp: OracleLayerPlanes, vp: OracleLayerPlanes,
                      rot_k: np.ndarray, rot_v: np.ndarray, num_kv_heads: int, N: int, M: int,
                      group: int, k_dtype: int, v_dtype: int,
-                     scale: float | None = None) -> np.ndarray:
+                     scale: float | None = None, absorb_v: bool = False) -> np.ndarray:
     """One decode step for every sequence: q bf16 bits [B, Hq, D] (post-RoPE,
     un-rotated) -> output float64 [B, Hq, D] (un-rotated).
 
@@ -359,6 +359,9 @@ def decode_attention(q_bits: np.ndarray, kp: OracleLayerPlanes, vp: OracleLayerP
         o'_j  = softmax(scale * K_hat q_rot_j) V_hat   over all T cached tokens,
                 with query head j reading kv head j // (Hq/Hkv)
         o_j   = o'_j @ R_V^T
+    absorb_v: return o' itself, the output still in the V-rotated basis, for a
+    caller that folds R_V^T into its output projection (RotationZoo "How to
+    use", the sglang flag that absorbs the V rotation).
     Pinned by: all-window equality with a library attention routine, rotation
     invariance with quantization off, GQA == replicated MHA, brute-force loops.
     """
@@ -378,7 +381,7 @@ def decode_attention(q_bits: np.ndarray, kp: OracleLayerPlanes, vp: OracleLayerP
             Vh = mixed_values(vp, b, h, T, N, M, group, v_dtype)
             for j in range(h * Gq, (h + 1) * Gq):
                 out[b, j] = softmax_attention_f64(qr[b, j], Kh, Vh, scale)
-    return out @ Rv.T
+    return out if absorb_v else out @ Rv.T
 
 
 # ----------------------------------------------------------------------------

@@ -72,9 +72,9 @@ def query(shape: Shape, mask, layer: int = 0, step: int = 0):
     return synth.q_bits(shape.B, shape.Hq, shape.Hkv, shape.D, shape.seed, layer, mask, shape.dist, step)
 
 
-def gpu_cache(ok, shape: Shape, rk, rv, max_context: int):
+def gpu_cache(ok, shape: Shape, rk, rv, max_context: int, absorb_v: int = 0):
     return ok.KVCache(shape.L, shape.B, shape.Hq, shape.Hkv, shape.D, max_context, shape.N, shape.M,
-                      128, shape.k_clip, shape.v_clip, shape.k_dtype, shape.v_dtype, rk, rv, 0)
+                      128, shape.k_clip, shape.v_clip, shape.k_dtype, shape.v_dtype, rk, rv, 0, absorb_v)
 
 
 def oracle_cache(shape: Shape, rk, rv):
@@ -91,7 +91,7 @@ def planes_from_export(exp: dict, T: int, N: int, M: int):
     return orc.planes_from_storage(exp["codes"], exp["s16"], exp["z16"], exp["sink"], exp["ring"], T, N, M)
 
 
-def oracle_on_exported(cache, layer, q_bits, shape: Shape, rk, rv, batch_idx=None):
+def oracle_on_exported(cache, layer, q_bits, shape: Shape, rk, rv, batch_idx=None, absorb_v=False):
     """Oracle attention over the cache exported from the GPU (identical cache)."""
     T = cache.length(layer)
     ek, ev = cache.export(layer, 0), cache.export(layer, 1)
@@ -104,4 +104,4 @@ def oracle_on_exported(cache, layer, q_bits, shape: Shape, rk, rv, batch_idx=Non
     Rv = rv[layer] if rv is not None else np.eye(D, dtype=np.float32)
     qb = q_bits if batch_idx is None else q_bits[batch_idx]
     return orc.decode_attention(qb, kp, vp, Rk, Rv, shape.Hkv, shape.N, shape.M, 128,
-                                shape.k_dtype, shape.v_dtype)
+                                shape.k_dtype, shape.v_dtype, absorb_v=absorb_v)

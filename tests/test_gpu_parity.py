@@ -617,3 +617,41 @@ def test_full_size_wide_64k_vbf16_sampled(ok):
         say(f"  seq {b}: rel L2 {e:.3e}")
         assert e <= ATTN_TOL
     gc.close()
+
+
+@pytest.mark.parametrize("shape,impl", [
+    (Shape(B=2, Hq=8, Hkv=2, N=16, M=64), 0),                   # fused matrix-core step, 4 heads per kv head
+    (Shape(B=1, Hq=16, Hkv=2, N=16, M=64), 0),                  # 8 heads per kv head
+    (Shape(B=2, Hq=8, Hkv=2, N=16, M=64), 1),                   # VALU kernel + standalone merge
+    (Shape(B=2, Hq=4, Hkv=2, D=512, N=16, M=64), 0),            # head_dim 512
+    (Shape(B=1, Hq=4, Hkv=2, D=512, N=16, M=64, v_dtype=1), 0), # head_dim 512, bf16 V
+])
+def test_absorbed_v_rotation(ok, shape, impl):
+    """absorb_v_rotation = 1: the output is o' (V-rotated basis), within the bar
+    of the oracle's o', and o' @ R_V^T matches an ordinary cache's output."""
+    say(f"[absorbed V rotation] {shape} impl={impl}")
+    rk, rv = make_rotations(shape, "haar")
+    T = 900
+    k, v, mask = inputs(shape, T)
+    ga = gpu_cache(ok, shape, rk, rv, T + 4, absorb_v=1)
+    gn = gpu_cache(ok, shape, rk, rv, T + 4)
+    for g in (ga, gn):
+        g.append(0, dev(k[:, :T - 1]), dev(v[:, :T - 1]))
+    qb = query(shape, mask)
+    # one fused step each (the merge paths of the step), then plain decodes
+    got_a = _step(ok, ga, 0, k[:, T - 1:T], v[:, T - 1:T], qb)
+    got_n = _step(ok, gn, 0, k[:, T - 1:T], v[:, T - 1:T], qb)
+    want = oracle_on_exported(ga, 0, qb, shape, rk, rv, absorb_v=True)
+    e = rel_l2(got_a, want)
+    say(f"  step: rel L2 vs oracle o' {e:.3e}")
+    assert e <= ATTN_TOL
+    Rv = rv[0].astype(np.float64)
+    assert rel_l2(got_a.astype(np.float64) @ Rv.T, got_n) <= 1e-5
+    got_a = _decode(ok, ga, 0, qb, impl=impl)
+    got_n = _decode(ok, gn, 0, qb, impl=impl)
+    e = rel_l2(got_a, want)
+    say(f"  decode impl={impl}: rel L2 vs oracle o' {e:.3e}")
+    assert e <= ATTN_TOL
+    assert rel_l2(got_a.astype(np.float64) @ Rv.T, got_n) <= 1e-5
+    ga.close()
+    gn.close()

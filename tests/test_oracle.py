@@ -266,6 +266,21 @@ def test_rotation_invariance_without_quantization():
     assert np.abs(R32 @ R32.T - np.eye(D)).max() < 1e-6
 
 
+def test_absorbed_v_rotation_output():
+    """With the V rotation absorbed into the caller's output projection the
+    library returns o' (the V-rotated basis): o' @ R_V^T is the ordinary output
+    and, with R_V orthogonal, o' = o @ R_V; the brute-force loops agree."""
+    T, Hq, Hkv, D, N, M = 11, 4, 2, 128, 2, 3
+    c, qb, kb, vb, rk, rv = _mk_cache(T, Hq, Hkv, D, N=N, M=M, batch=1, seed=23)
+    o = c.attend(0, qb)
+    oa = orc.decode_attention(qb, c.k[0], c.v[0], rk[0], rv[0], Hkv, N, M, 128, 0, 0, absorb_v=True)
+    Rv = rv[0].astype(np.float64)
+    np.testing.assert_allclose(oa @ Rv.T, o, rtol=1e-10, atol=1e-12)
+    assert np.abs(oa - o).max() > 1e-3                  # the rotation is not the identity
+    want = _brute_attention(qb, kb, vb, rk[0], rv[0], Hkv, N, M, 128, 0.96, 0.92)
+    np.testing.assert_allclose(oa @ Rv.T, want, rtol=1e-9, atol=1e-9)
+
+
 def _brute_attention(q_bits, k_bits, v_bits, rk, rv, Hkv, N, M, G, kclip, vclip):
     """Pure-Python loops for tiny shapes, written straight from the definition."""
     B, Hq, D = q_bits.shape
