@@ -433,6 +433,45 @@ def bit_reversal_permutation(D: int) -> np.ndarray:
     return P
 
 
+def block_hadamard(D: int, order: int = 128) -> np.ndarray:
+    """The orthonormal Walsh-Hadamard matrix of the given order in Sylvester's
+    construction, entry (i, j) = (-1)^popcount(i & j) / sqrt(order), placed
+    D / order times along the diagonal (float64 [D, D]).
+
+    The in-quant Hadamard: the llama.cpp fork's quantizer applies a Hadamard
+    transform unless the rotation already sits in the graph ([Qwen3-4B card]
+    "Run", env-var table), the sglang launch sets its order to 128
+    ([RotationZoo] "How to use", step 2), and the shipped rotations themselves
+    contain a head-dim Hadamard factor ([RotationZoo] "File format").
+    Pinned by: equality with scipy's Sylvester Hadamard, orthogonality, the
+    two-block recursion and the transform of a unit vector.
+    """
+    assert order > 0 and order & (order - 1) == 0 and D % order == 0
+    i = np.arange(order)
+    bits = np.bitwise_and.outer(i, i)
+    pop = np.zeros_like(bits)
+    while bits.any():
+        pop += bits & 1
+        bits >>= 1
+    H = np.where(pop % 2 == 0, 1.0, -1.0) / math.sqrt(order)
+    return np.kron(np.eye(D // order), H)
+
+
+def with_in_quant_hadamard(R32: np.ndarray, order: int = 128) -> np.ndarray:
+    """Rotations followed by the in-quant Hadamard: fp32(R @ H) per layer, the
+    product taken in fp64 and rounded once (R32: fp32 [..., D, D]).  The
+    quantizer input becomes fp32(x @ R @ H) up to that one rounding of the
+    matrix, q is rotated by the same product and the output un-rotated by its
+    transpose, so every other step is unchanged.
+    Pinned by: the identity rotation giving the Hadamard itself, orthogonality
+    of the product, and equality of the product applied to a vector with the
+    rotation followed by an explicit fast Walsh-Hadamard transform.
+    """
+    R = np.asarray(R32, np.float32).astype(np.float64)
+    H = block_hadamard(R.shape[-1], order)
+    return (R @ H).astype(np.float32)
+
+
 def compressed_bytes_per_token_head(D: int, group: int) -> int:
     """INT2 storage per token and head for one of K or V: D/4 code bytes plus an
     fp16 scale and an fp16 zero per group."""

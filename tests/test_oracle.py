@@ -420,3 +420,75 @@ def test_bit_reversal_permutation():
     x = np.arange(128, dtype=np.float64)
     y = x @ P
     assert y[1] == 64 and y[64] == 1 and y[3] == 96 and y[127] == 127
+
+
+# --------------------------------------------------------------------------- in-quant Hadamard
+
+
+def _fwht(x):
+    """Walsh-Hadamard butterflies over the last axis (length a power of two),
+    orthonormal scaling; independent of the matrix form."""
+    y = np.array(x, np.float64, copy=True)
+    n = y.shape[-1]
+    h = 1
+    while h < n:
+        for i in range(0, n, 2 * h):
+            a = y[..., i:i + h].copy()
+            b = y[..., i + h:i + 2 * h].copy()
+            y[..., i:i + h] = a + b
+            y[..., i + h:i + 2 * h] = a - b
+        h *= 2
+    return y / math.sqrt(n)
+
+
+def test_block_hadamard_matches_library_and_recursion():
+    """The order-128 matrix is scipy's Sylvester Hadamard scaled to unit rows;
+    it is orthogonal; order 256 is the two-block recursion of order 128; a
+    head_dim of 512 repeats the order-128 block along the diagonal."""
+    import scipy.linalg
+    H = orc.block_hadamard(128)
+    np.testing.assert_array_equal(H, scipy.linalg.hadamard(128) / math.sqrt(128))
+    np.testing.assert_allclose(H @ H.T, np.eye(128), atol=1e-14)
+    H256 = orc.block_hadamard(256, 256)
+    np.testing.assert_allclose(H256, np.block([[H, H], [H, -H]]) / math.sqrt(2), atol=1e-15)
+    Hb = orc.block_hadamard(512)
+    for g in range(4):
+        for g2 in range(4):
+            blk = Hb[128 * g:128 * (g + 1), 128 * g2:128 * (g2 + 1)]
+            np.testing.assert_array_equal(blk, H if g == g2 else np.zeros((128, 128)))
+    e0 = np.zeros(128)
+    e0[0] = 1.0
+    np.testing.assert_allclose(e0 @ H, np.full(128, 1 / math.sqrt(128)), atol=1e-16)
+
+
+@pytest.mark.parametrize("D", [128, 512])
+def test_in_quant_hadamard_rotation(D):
+    """fp32(R @ H): the identity rotation gives the Hadamard itself; the product
+    stays orthogonal to fp32 accuracy; applied to a vector it equals the
+    rotation followed by butterflies over each 128-group."""
+    R = synth.rotations(1, D, 5, "rot_k")[0]
+    RH = orc.with_in_quant_hadamard(R)
+    assert RH.dtype == np.float32 and RH.shape == (D, D)
+    np.testing.assert_array_equal(orc.with_in_quant_hadamard(np.eye(D, dtype=np.float32)),
+                                  orc.block_hadamard(D).astype(np.float32))
+    P = RH.astype(np.float64)
+    np.testing.assert_allclose(P @ P.T, np.eye(D), atol=1e-6)
+    x = np.random.default_rng(3).standard_normal((5, D))
+    via_fwht = _fwht((x @ R.astype(np.float64)).reshape(5, D // 128, 128)).reshape(5, D)
+    np.testing.assert_allclose(x @ P, via_fwht, rtol=0, atol=1e-5)
+
+
+def test_in_quant_hadamard_spreads_an_outlier():
+    """Closed form: a group whose energy sits in one channel j comes out of the
+    transform flat, entry i = x_j (-1)^popcount(i & j) / sqrt(128), so the
+    quantizer sees two levels instead of one outlier over zeros."""
+    D, j, amp = 128, 7, 48.0
+    x = np.zeros((1, D), np.float32)
+    x[0, j] = amp
+    bits = orc.f32_to_bf16_bits(x)
+    I = np.eye(D, dtype=np.float32)
+    xh = orc.rotated_fp32(bits, orc.with_in_quant_hadamard(I))[0].astype(np.float64)
+    signs = np.array([(-1.0) ** bin(i & j).count("1") for i in range(D)])
+    np.testing.assert_allclose(xh, amp * signs / math.sqrt(D), rtol=1e-6)
+    q = orc.quantize_rows(xh.astype(np.float32)[None], 128, 1.0)
+    assert set(np.unique(q.codes)) == {0, 3}
