@@ -174,7 +174,32 @@ int validate_config(const oscar_kv_config* c) {
     return fail(OSCAR_ERR_INVALID_ARG, "batch x heads too large");
   if (c->absorb_v_rotation != 0 && c->absorb_v_rotation != 1)
     return fail(OSCAR_ERR_INVALID_ARG, "absorb_v_rotation must be 0 or 1");
+  if (c->in_quant_hadamard != 0 && c->in_quant_hadamard != kGroup)
+    return fail(OSCAR_ERR_INVALID_ARG, "in_quant_hadamard must be 0 or 128");
   return OSCAR_OK;
+}
+
+// The in-quant Hadamard folded into a rotation: every row r of R (rows of length D)
+// becomes r H, H = the orthonormal Sylvester Walsh-Hadamard matrix of the given
+// order on each order-wide block of the row, entry (i, j) = (-1)^popcount(i & j) /
+// sqrt(order).  The butterflies (a, b) -> (a + b, a - b) run in fp64, the scale is
+// applied once and the result is rounded to fp32 once.
+void fold_hadamard(std::vector<float>& R, size_t rows, int D, int order) {
+  const double scale = 1.0 / std::sqrt((double)order);
+  std::vector<double> x(D);
+  for (size_t r = 0; r < rows; ++r) {
+    float* row = &R[r * D];
+    for (int i = 0; i < D; ++i) x[i] = row[i];
+    for (int base = 0; base < D; base += order)
+      for (int h = 1; h < order; h <<= 1)
+        for (int i = base; i < base + order; i += 2 * h)
+          for (int j = i; j < i + h; ++j) {
+            const double a = x[j], b = x[j + h];
+            x[j] = a + b;
+            x[j + h] = a - b;
+          }
+    for (int i = 0; i < D; ++i) row[i] = (float)(x[i] * scale);
+  }
 }
 
 int alloc_plane(oscar_kv* kv, Plane* p, oscar_kv_dtype dt, bool is_v) {
@@ -372,6 +397,10 @@ int oscar_kv_create(const oscar_kv_config* cfg, oscar_kv** out) {
         rk[i] = cfg->rot_k ? cfg->rot_k[i] : (e == d ? 1.0f : 0.0f);
         rv[i] = cfg->rot_v ? cfg->rot_v[i] : (e == d ? 1.0f : 0.0f);
       }
+  if (cfg->in_quant_hadamard) {
+    fold_hadamard(rk, (size_t)L * D, D, cfg->in_quant_hadamard);
+    fold_hadamard(rv, (size_t)L * D, D, cfg->in_quant_hadamard);
+  }
   for (int l = 0; l < L; ++l)
     for (int e = 0; e < D; ++e)
       for (int d = 0; d < D; ++d) rvT[l * DD + (size_t)e * D + d] = rv[l * DD + (size_t)d * D + e];

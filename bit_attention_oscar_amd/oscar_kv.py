@@ -49,7 +49,7 @@ class oscar_kv_config(C.Structure):
         ("sink_tokens", C.c_int32), ("recent_tokens", C.c_int32), ("group_size", C.c_int32),
         ("k_clip", C.c_float), ("v_clip", C.c_float), ("k_dtype", C.c_int32),
         ("v_dtype", C.c_int32), ("rot_k", C.POINTER(C.c_float)), ("rot_v", C.POINTER(C.c_float)),
-        ("device", C.c_int32), ("absorb_v_rotation", C.c_int32),
+        ("device", C.c_int32), ("absorb_v_rotation", C.c_int32), ("in_quant_hadamard", C.c_int32),
     ]
 
 
@@ -197,7 +197,8 @@ class KVCache:
 
     def __init__(self, num_layers, max_batch, num_q_heads, num_kv_heads, head_dim, max_context,
                  sink_tokens, recent_tokens, group_size=128, k_clip=0.96, v_clip=0.92,
-                 k_dtype=KV_INT2, v_dtype=KV_INT2, rot_k=None, rot_v=None, device=0, absorb_v_rotation=0):
+                 k_dtype=KV_INT2, v_dtype=KV_INT2, rot_k=None, rot_v=None, device=0, absorb_v_rotation=0,
+                 in_quant_hadamard=0):
         self.num_layers, self.max_batch = num_layers, max_batch
         self.num_q_heads, self.num_kv_heads, self.head_dim = num_q_heads, num_kv_heads, head_dim
         self.max_context, self.N, self.M, self.G = max_context, sink_tokens, recent_tokens, group_size
@@ -207,7 +208,8 @@ class KVCache:
         fp = lambda a: None if a is None else a.ctypes.data_as(C.POINTER(C.c_float))
         cfg = oscar_kv_config(num_layers, max_batch, num_q_heads, num_kv_heads, head_dim,
                               max_context, sink_tokens, recent_tokens, group_size, k_clip, v_clip,
-                              k_dtype, v_dtype, fp(self._rk), fp(self._rv), device, absorb_v_rotation)
+                              k_dtype, v_dtype, fp(self._rk), fp(self._rv), device, absorb_v_rotation,
+                              in_quant_hadamard)
         self.handle = oscar_kv_create(cfg)
 
     def close(self):

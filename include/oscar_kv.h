@@ -88,6 +88,15 @@ typedef struct {
                               * V-rotated basis (the caller folds R_V^T into its
                               * output projection: RotationZoo "How to use", the
                               * sglang flag that absorbs the V rotation); 0: o = o' R_V^T */
+  int32_t in_quant_hadamard; /* 0: off; 128: the in-quant Hadamard of order 128 (the
+                              * quantizer's Hadamard transform of the Qwen3-4B card's
+                              * "Run" env-var table; order 128 in the RotationZoo "How to
+                              * use" sglang launch).  Both rotations become fp32(R H), H the
+                              * orthonormal Sylvester Walsh-Hadamard matrix of order 128 on
+                              * each 128-group along head_dim, taken row by row at create
+                              * with fast Walsh-Hadamard butterflies in fp64 and rounded
+                              * once, so every later step (q rotation, window values, the
+                              * quantizer, the V un-rotation by the transpose) is unchanged */
 } oscar_kv_config;
 
 typedef struct oscar_kv oscar_kv;

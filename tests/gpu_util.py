@@ -72,9 +72,10 @@ def query(shape: Shape, mask, layer: int = 0, step: int = 0):
     return synth.q_bits(shape.B, shape.Hq, shape.Hkv, shape.D, shape.seed, layer, mask, shape.dist, step)
 
 
-def gpu_cache(ok, shape: Shape, rk, rv, max_context: int, absorb_v: int = 0):
+def gpu_cache(ok, shape: Shape, rk, rv, max_context: int, absorb_v: int = 0, hadamard: int = 0):
     return ok.KVCache(shape.L, shape.B, shape.Hq, shape.Hkv, shape.D, max_context, shape.N, shape.M,
-                      128, shape.k_clip, shape.v_clip, shape.k_dtype, shape.v_dtype, rk, rv, 0, absorb_v)
+                      128, shape.k_clip, shape.v_clip, shape.k_dtype, shape.v_dtype, rk, rv, 0, absorb_v,
+                      hadamard)
 
 
 def oracle_cache(shape: Shape, rk, rv):

@@ -46,7 +46,8 @@ def _cfg(ok, **kw):
     ("num_layers", 0, -1), ("max_batch", 0, -1), ("num_kv_heads", 3, -1), ("num_kv_heads", 0, -1),
     ("head_dim", 96, -5), ("head_dim", 256, -5), ("group_size", 64, -5), ("max_context", 0, -1),
     ("sink_tokens", -1, -1), ("recent_tokens", -3, -1), ("k_clip", 0.0, -1), ("v_clip", 1.5, -1),
-    ("k_dtype", 7, -1), ("num_q_heads", 64, -5),
+    ("k_dtype", 7, -1), ("num_q_heads", 64, -5), ("absorb_v_rotation", 2, -1),
+    ("in_quant_hadamard", 64, -1), ("in_quant_hadamard", 1, -1),
 ])
 def test_create_rejects_bad_config(ok, field, value, code):
     cfg = _cfg(ok, **{field: value})

@@ -655,3 +655,58 @@ def test_absorbed_v_rotation(ok, shape, impl):
     assert rel_l2(got_a.astype(np.float64) @ Rv.T, got_n) <= 1e-5
     ga.close()
     gn.close()
+
+
+@pytest.mark.parametrize("shape", [
+    Shape(B=2, Hq=8, Hkv=2, N=16, M=64),                        # fused matrix-core step, 4 heads per kv head
+    Shape(B=1, Hq=16, Hkv=2, N=16, M=64),                       # 8 heads per kv head
+    Shape(B=2, Hq=4, Hkv=2, D=512, N=16, M=64),                 # head_dim 512: four 128-blocks
+    Shape(B=1, Hq=4, Hkv=2, D=512, N=16, M=64, v_dtype=1),      # head_dim 512, bf16 V
+])
+def test_in_quant_hadamard(ok, shape):
+    """in_quant_hadamard = 128 on the GPU against the oracle run with the
+    rotations fp32(R @ H): the GPU's fp32 rotated vectors are within fp32
+    accumulation error of x @ R @ H in fp64, its codes and metadata equal the
+    oracle quantizer on those vectors, and attention (one fused step, then a
+    plain decode) is within the bar over the identical cache."""
+    say(f"[in-quant Hadamard] {shape}")
+    rk, rv = make_rotations(shape, "haar")
+    rkh = np.stack([orc.with_in_quant_hadamard(r) for r in rk])
+    rvh = np.stack([orc.with_in_quant_hadamard(r) for r in rv])
+    T = 600
+    k, v, mask = inputs(shape, T)
+    gc = gpu_cache(ok, shape, rk, rv, T + 4, hadamard=128)
+    D = shape.D
+    kr = torch.zeros((shape.B, T - 1, shape.Hkv, D), dtype=torch.float32, device="cuda")
+    vr = torch.zeros_like(kr)
+    gc.append_dump(0, dev(k[:, :T - 1]), dev(v[:, :T - 1]), kr, vr)
+    torch.cuda.synchronize()
+    kr, vr = kr.cpu().numpy(), vr.cpu().numpy()
+    planes = ((kr, k, rk[0], 0.96, 0),) + (((vr, v, rv[0], 0.92, 1),) if shape.v_dtype == 0 else ())
+    for xr, bits, R, clip, which in planes:
+        ref = orc.rotate_f64(bits[:, :T - 1], R) @ orc.block_hadamard(D)
+        err = np.abs(xr - ref).max() / np.abs(ref).max()
+        say(f"  which={which} max rel rotation err vs x R H {err:.2e}")
+        assert err < 1e-5
+        x32 = np.ascontiguousarray(np.transpose(xr, (0, 2, 1, 3)))            # [B, H, T, D]
+        q = orc.quantize_rows(x32.reshape(-1, D), 128, clip)
+        exp = gc.export(0, which)
+        np.testing.assert_array_equal(exp["codes"].reshape(-1, D // 4), orc.pack_codes(q.codes))
+        np.testing.assert_array_equal(exp["s16"].reshape(-1, D // 128).view(np.uint16), q.s16.view(np.uint16))
+        np.testing.assert_array_equal(exp["z16"].reshape(-1, D // 128).view(np.uint16), q.z16.view(np.uint16))
+    qb = query(shape, mask)
+    got = _step(ok, gc, 0, k[:, T - 1:T], v[:, T - 1:T], qb)
+    want = oracle_on_exported(gc, 0, qb, shape, rkh, rvh)
+    e = rel_l2(got, want)
+    say(f"  step: rel L2 vs oracle over the identical cache {e:.3e}")
+    assert e <= ATTN_TOL
+    got = _decode(ok, gc, 0, qb)
+    e = rel_l2(got, want)
+    say(f"  decode: rel L2 {e:.3e}")
+    assert e <= ATTN_TOL
+    oc = oracle_cache(shape, rkh, rvh)
+    oc.append(0, k, v)
+    e2e = rel_l2(got, oc.attend(0, qb))
+    say(f"  end to end vs the oracle's own cache: rel L2 {e2e:.3e}")
+    assert e2e <= 1e-2
+    gc.close()
