@@ -26,7 +26,8 @@ __global__ __launch_bounds__(256) void append_one_wide_kernel(AppendArgs a) {
   append_slice_block(a, (int)blockIdx.x, blockIdx.z != 0, (int)blockIdx.y, xs, part);
 }
 
-// Test hook: the same quantizer on fp32 rows, canonical packing.
+// Test hook: the quantizer of the multi-token append (the reciprocal fast path
+// with its exact fallback) on fp32 rows, canonical packing.
 template <int D>
 __global__ __launch_bounds__(64) void quantize_rows_kernel(const float* x, float clip, uint8_t* codes,
                                                            uint32_t* meta) {
@@ -42,8 +43,9 @@ __global__ __launch_bounds__(64) void quantize_rows_kernel(const float* x, float
     const float mx = wave_max(fmaxf(v[2 * g], v[2 * g + 1]));
     const float mn = wave_min(fminf(v[2 * g], v[2 * g + 1]));
     const GroupQ q = group_params(mx, mn, clip);
-    code[2 * g] = quant_code(v[2 * g], q);
-    code[2 * g + 1] = quant_code(v[2 * g + 1], q);
+    const float inv = __builtin_amdgcn_rcpf(q.sf);
+    code[2 * g] = quant_code_fast(v[2 * g], q, inv);
+    code[2 * g + 1] = quant_code_fast(v[2 * g + 1], q, inv);
     if (lane == 0) meta[row * (D / kGroup) + g] = q.packed;
   }
   store_canonical<PER>(code, lane, [&](int w) { return reinterpret_cast<uint32_t*>(codes + row * (D / 4) + 4 * w); });

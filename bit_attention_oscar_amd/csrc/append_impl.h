@@ -68,6 +68,27 @@ __device__ inline uint32_t quant_code(float x, const GroupQ& g) {
   return (uint32_t)t;
 }
 
+// quant_code with the division replaced where that provably changes nothing:
+// inv = v_rcp_f32(s) (1 ulp), so qa = (x - z) * inv is within 2^-20 of the
+// exact quotient Q = (x - z) / s for |Q| < 4, and the correctly rounded
+// quotient q is within 2^-23 of Q.  If qa is at least 2^-17 away from 0.5,
+// 1.5 and 2.5, Q and q lie strictly on the side of that half-integer where qa
+// lies, so rint(q) = rint(qa); otherwise (rare) the correctly rounded division
+// decides.  Outside (0, 3) the clamp gives the same code either way.
+__device__ inline uint32_t quant_code_fast(float x, const GroupQ& g, float inv) {
+  if (g.sf == 0.0f) return 0u;
+  const float d = x - g.zf;
+  const float qa = d * inv;
+  const float fr = qa - __builtin_floorf(qa);
+  float t;
+  if (qa > 0.0f && qa < 3.0f && __builtin_fabsf(fr - 0.5f) < 0x1p-17f)
+    t = __builtin_rintf(d / g.sf);
+  else
+    t = __builtin_rintf(qa);
+  t = fminf(fmaxf(t, 0.0f), 3.0f);
+  return (uint32_t)t;
+}
+
 // Canonical packing through lane shuffles: lane l holds the code of dim
 // l + 64 i; word w (dims 16w..16w+15) is OR-reduced over the 16 lanes
 // 16 (w % 4) .. + 15 of element i = w / 4 and stored by its first lane at

@@ -47,6 +47,21 @@ def _quant_rows(D, seed):
     x[17] *= 3000.0                          # large range
     # exact ties of (x - z)/s at k + 1/2 under r = 1: group [0, 3] -> s = 1, z = 0
     x[18] = np.tile(np.array([0.0, 3.0, 0.5, 1.5, 2.5, 1.0, 2.0, 0.25], np.float32), D // 8)
+    # near ties under r = 1: groups [0, mx] give z = 0 and s = fp16(mx / 3);
+    # values within a few ulps of (k + 1/2) s on both sides, where a quotient
+    # through an approximate reciprocal can land on the other side of the tie
+    for row, mx in zip(range(20, 26), (9.0, 2.1, 7.3, 0.77, 5.5, 100.3)):
+        sf = np.float32(np.float16(np.float32(np.float32(mx) / np.float32(3.0))))
+        vals = [0.0, mx]
+        for k in (0.5, 1.5, 2.5):
+            c = np.float32(np.float32(k) * sf)
+            for n in range(-3, 4):
+                v = c
+                for _ in range(abs(n)):
+                    v = np.nextafter(v, np.float32(np.inf if n > 0 else -np.inf), dtype=np.float32)
+                vals.append(v)
+        vals = np.array(vals, np.float32)
+        x[row] = np.resize(vals, D)
     return x
 
 
