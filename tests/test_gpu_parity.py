@@ -542,6 +542,75 @@ def test_full_size_32k_sampled(ok):
 
 
 @pytest.mark.slow
+def test_full_size_16k_batch1_sampled(ok):
+    """The 16k-context batch-1 shape (B=1, Hq=32, Hkv=8, D=128, N=512,
+    M=2048) on one layer, filled on the device, then several fused steps in
+    the benchmark's launch configuration; every head against the oracle over
+    the exported cache after the last step."""
+    from bench import fill_layer_device
+    shape = Shape(B=1, Hq=32, Hkv=8, D=128, N=512, M=2048, outliers="percent")
+    T = 16384
+    say("[full 16k batch 1] filling")
+    rk, rv = make_rotations(shape, "haar")
+    gc = gpu_cache(ok, shape, rk, rv, T + 64)
+    fill_layer_device(gc, 0, shape.B, shape.Hkv, shape.D, T, seed=0, dist="normal", outliers="percent")
+    mask = synth.outlier_mask(shape.D, shape.Hkv, 0, 0, "percent")
+    for i in range(4):
+        k1, v1, _ = inputs(shape, 1, chunk=90 + i)
+        qb = query(shape, mask, step=i)
+        got = _step(ok, gc, 0, k1, v1, qb)
+    want = oracle_on_exported(gc, 0, qb, shape, rk, rv)
+    e = rel_l2(got, want)
+    say(f"  after 4 steps (T={gc.length(0)}): rel L2 {e:.3e}")
+    assert e <= ATTN_TOL
+    gc.close()
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("D,B,vdt", [(128, 16, 0), (512, 4, 0), (512, 4, 1)])
+def test_prefill_chunk_full_size(ok, D, B, vdt):
+    """A 4096-token prefill append at the benchmark shapes (head_dim 128, B=16
+    and head_dim 512, B=4; 8 kv heads), behind 4096 stored tokens so the
+    chunk starts mid-cache: the GPU's fp32 rotated rows (dump hook) are within
+    fp32 accumulation error of the fp64 rotation, and for sampled (sequence,
+    kv head) pairs every stored code, scale, zero and window value of the
+    chunk equals the oracle quantizer applied to those rows."""
+    from bench import fill_layer_device
+    shape = Shape(B=B, Hq=2 * 8, Hkv=8, D=D, N=512, M=2048, outliers="percent", v_dtype=vdt)
+    n, T0 = 4096, 4096
+    say(f"[prefill chunk full size] D={D} B={B} v_dtype={vdt}")
+    rk, rv = make_rotations(shape, "haar")
+    gc = gpu_cache(ok, shape, rk, rv, T0 + n + 64)
+    fill_layer_device(gc, 0, B, 8, D, T0, seed=0, dist="normal", outliers="percent")
+    k, v, _ = inputs(shape, n, chunk=77)
+    kr = torch.zeros((B, n, 8, D), dtype=torch.float32, device="cuda")
+    vr = torch.zeros_like(kr)
+    gc.append_dump(0, dev(k), dev(v), kr, vr)
+    torch.cuda.synchronize()
+    ek, ev = gc.export(0, 0), gc.export(0, 1)
+    pairs = [(0, 0), (B - 1, 7), (B // 2, 3)]
+    T = T0 + n
+    for xr_dev, bits, R, clip, exp, which in ((kr, k, rk[0], 0.96, ek, 0), (vr, v, rv[0], 0.92, ev, 1)):
+        for b, h in pairs:
+            xr = xr_dev[b, :, h].cpu().numpy()                                    # [n, D]
+            ref = orc.rotate_f64(bits[b:b + 1, :, h:h + 1], R)[0, :, 0]
+            err = np.abs(xr - ref).max() / np.abs(ref).max()
+            assert err < 1e-5, (which, b, h, err)
+            win = orc.f32_to_bf16_bits(orc.canonical_zero(xr))
+            if "full" in exp:
+                np.testing.assert_array_equal(exp["full"][b, h, T0:T], win)
+                continue
+            q = orc.quantize_rows(np.ascontiguousarray(xr), 128, clip)
+            np.testing.assert_array_equal(exp["codes"][b, h, T0:T], orc.pack_codes(q.codes))
+            np.testing.assert_array_equal(exp["s16"][b, h, T0:T].view(np.uint16), q.s16.view(np.uint16))
+            np.testing.assert_array_equal(exp["z16"][b, h, T0:T].view(np.uint16), q.z16.view(np.uint16))
+            for t in range(max(shape.N, T - shape.M), T):
+                np.testing.assert_array_equal(exp["ring"][b, h, t % shape.M], win[t - T0])
+        say(f"  which={which}: sampled pairs bit-exact")
+    gc.close()
+
+
+@pytest.mark.slow
 def test_full_size_128k_gqa8_sampled(ok):
     """The 128k-context GQA-8 shape (B=8, Hq=64, Hkv=8, D=128, N=64, M=256,
     Student-t(3) values) on one layer, filled on the device, one fused step
