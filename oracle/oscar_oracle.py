@@ -384,6 +384,50 @@ def decode_attention(q_bits: np.ndarray, kp: OracleLayerPlanes, vp: OracleLayerP
     return out if absorb_v else out @ Rv.T
 
 
+def prefill_attention(q_bits: np.ndarray, kp: OracleLayerPlanes, vp: OracleLayerPlanes,
+                      rot_k: np.ndarray, rot_v: np.ndarray, num_kv_heads: int, N: int, M: int,
+                      group: int, k_dtype: int, v_dtype: int,
+                      scale: float | None = None, absorb_v: bool = False) -> np.ndarray:
+    """Chunked-prefill attention over the mixed cache ([RotationZoo] "How to
+    use": the serving host runs a separate prefill backend beside the decode
+    one).  q bf16 bits [B, n, Hq, D] are the queries of the last n cached
+    positions T - n .. T - 1 (post-RoPE, un-rotated).  Query i, at position
+    p = T - n + i, attends causally over positions [0, p] of the cache as it
+    stands after the chunk was appended: the sink and recent windows of the
+    current length T read their bf16 values, every other position its INT2
+    dequantization.  Each query is the decode step's arithmetic over its
+    causal prefix:
+
+        q_rot = q @ R_K                      (fp64)
+        o'    = softmax(scale * K_hat[:p+1] q_rot) V_hat[:p+1]
+        o     = o' @ R_V^T                   (o' itself with absorb_v)
+
+    Returns float64 [B, n, Hq, D].
+    Pinned by: n = 1 equal to decode_attention, an all-window cache with
+    R = I equal to a library attention routine under an explicit causal mask,
+    and brute-force loops on tiny shapes.
+    """
+    B, n, Hq, D = q_bits.shape
+    Gq = Hq // num_kv_heads
+    assert Gq * num_kv_heads == Hq
+    T = kp.x32.shape[2]
+    assert 0 < n <= T, "the queries are the last n of the T cached positions"
+    if scale is None or scale <= 0:
+        scale = 1.0 / math.sqrt(D)
+    qr = rotate_f64(q_bits, rot_k)                       # [B, n, Hq, D]
+    Rv = np.asarray(rot_v, np.float32).astype(np.float64)
+    out = np.zeros((B, n, Hq, D), dtype=np.float64)
+    for b in range(B):
+        for h in range(num_kv_heads):
+            Kh = mixed_values(kp, b, h, T, N, M, group, k_dtype)
+            Vh = mixed_values(vp, b, h, T, N, M, group, v_dtype)
+            for i in range(n):
+                p = T - n + i
+                for j in range(h * Gq, (h + 1) * Gq):
+                    out[b, i, j] = softmax_attention_f64(qr[b, i, j], Kh[:p + 1], Vh[:p + 1], scale)
+    return out if absorb_v else out @ Rv.T
+
+
 # ----------------------------------------------------------------------------
 # importing a cache held in storage layout (sink array + recent ring)
 # ----------------------------------------------------------------------------

@@ -281,10 +281,13 @@ def test_absorbed_v_rotation_output():
     np.testing.assert_allclose(oa @ Rv.T, want, rtol=1e-9, atol=1e-9)
 
 
-def _brute_attention(q_bits, k_bits, v_bits, rk, rv, Hkv, N, M, G, kclip, vclip):
-    """Pure-Python loops for tiny shapes, written straight from the definition."""
+def _brute_attention(q_bits, k_bits, v_bits, rk, rv, Hkv, N, M, G, kclip, vclip, ntok=None):
+    """Pure-Python loops for tiny shapes, written straight from the definition.
+    The windows are those of the full length T; the query attends over the
+    first ntok positions (all T by default)."""
     B, Hq, D = q_bits.shape
     T = k_bits.shape[1]
+    ntok = T if ntok is None else ntok
     Gq = Hq // Hkv
     f = lambda bits: float(orc.bf16_bits_to_f64(np.array([bits], np.uint16))[0])
     out = np.zeros((B, Hq, D))
@@ -319,13 +322,13 @@ def _brute_attention(q_bits, k_bits, v_bits, rk, rv, Hkv, N, M, G, kclip, vclip)
         for j in range(Hq):
             h = j // Gq
             qv = rot(q_bits[b, j], rk)
-            Ks = [vec_for(k_bits[b, t, h], rk, t, kclip) for t in range(T)]
-            Vs = [vec_for(v_bits[b, t, h], rv, t, vclip) for t in range(T)]
+            Ks = [vec_for(k_bits[b, t, h], rk, t, kclip) for t in range(ntok)]
+            Vs = [vec_for(v_bits[b, t, h], rv, t, vclip) for t in range(ntok)]
             sc = [sum(qv[d] * Kt[d] for d in range(D)) / math.sqrt(D) for Kt in Ks]
             mx = max(sc)
             w = [math.exp(s_ - mx) for s_ in sc]
             tot = sum(w)
-            o = [sum(w[t] * Vs[t][d] for t in range(T)) / tot for d in range(D)]
+            o = [sum(w[t] * Vs[t][d] for t in range(ntok)) / tot for d in range(D)]
             out[b, j] = [sum(o[e] * float(rv[d][e]) for e in range(D)) for d in range(D)]
     return out
 
@@ -492,3 +495,59 @@ def test_in_quant_hadamard_spreads_an_outlier():
     np.testing.assert_allclose(xh, amp * signs / math.sqrt(D), rtol=1e-6)
     q = orc.quantize_rows(xh.astype(np.float32)[None], 128, 1.0)
     assert set(np.unique(q.codes)) == {0, 3}
+
+
+# --------------------------------------------------------------------------- chunked-prefill attention
+
+
+def _prefill_queries(batch, n, Hq, Hkv, D, seed, mask=None):
+    mask = synth.outlier_mask(D, Hkv, seed, 0, "fixed", 2) if mask is None else mask
+    return np.stack([synth.q_bits(batch, Hq, Hkv, D, seed, 0, mask, "normal", step=i) for i in range(n)], axis=1)
+
+
+def test_prefill_attention_single_query_is_decode():
+    """n = 1: the one query sits at position T - 1 and attends over the whole
+    cache, which is the decode step."""
+    T, Hq, Hkv, D = 30, 4, 2, 128
+    c, q, k, v, rk, rv = _mk_cache(T, Hq, Hkv, D, N=3, M=5)
+    got = orc.prefill_attention(q[:, None], c.k[0], c.v[0], rk[0], rv[0], Hkv, 3, 5, 128, 0, 0)
+    np.testing.assert_allclose(got[:, 0], c.attend(0, q), rtol=1e-13, atol=1e-13)
+
+
+@pytest.mark.parametrize("rot", [False, True])
+def test_prefill_attention_all_window_equals_library(rot):
+    """N + M >= T: every position is read at bf16, and the chunk's queries
+    (the last n positions) equal a library attention over the bf16 K/V under
+    an explicit causal mask (query i sees keys 0 .. T - n + i), with q R_K and
+    the output un-rotated by R_V^T."""
+    T, n, Hq, Hkv, D = 12, 5, 4, 2, 128
+    c, _, k, v, rk, rv = _mk_cache(T, Hq, Hkv, D, N=5, M=7, rot=rot)
+    qb = _prefill_queries(2, n, Hq, Hkv, D, 5)
+    got = orc.prefill_attention(qb, c.k[0], c.v[0], rk[0] if rot else np.eye(D, dtype=np.float32),
+                                rv[0] if rot else np.eye(D, dtype=np.float32), Hkv, 5, 7, 128, 0, 0)
+    eye = np.eye(D)
+    Rk = rk[0].astype(np.float64) if rot else eye
+    Rv = rv[0].astype(np.float64) if rot else eye
+    kw = torch.from_numpy((orc.bf16_bits_to_f64(k) @ Rk).astype(np.float32)).to(torch.bfloat16).double().numpy()
+    vw = torch.from_numpy((orc.bf16_bits_to_f64(v) @ Rv).astype(np.float32)).to(torch.bfloat16).double().numpy()
+    Gq = Hq // Hkv
+    K = torch.from_numpy(np.repeat(np.transpose(kw, (0, 2, 1, 3)), Gq, axis=1))      # [B, Hq, T, D]
+    V = torch.from_numpy(np.repeat(np.transpose(vw, (0, 2, 1, 3)), Gq, axis=1))
+    qr = torch.from_numpy(np.transpose(orc.bf16_bits_to_f64(qb) @ Rk, (0, 2, 1, 3)).copy())  # [B, Hq, n, D]
+    allowed = torch.from_numpy(np.arange(T)[None, :] <= (T - n + np.arange(n))[:, None])  # [n, T]
+    want = torch.nn.functional.scaled_dot_product_attention(qr, K, V, attn_mask=allowed, scale=1.0 / math.sqrt(D))
+    want = np.transpose(want.numpy(), (0, 2, 1, 3)) @ Rv.T
+    np.testing.assert_allclose(got, want, rtol=1e-10, atol=1e-12)
+
+
+def test_prefill_attention_brute_force_tiny():
+    """INT2 positions inside the chunk and before it, random rotations: every
+    query equals the pure-Python loops over its causal prefix, with the
+    windows of the full length."""
+    T, n, Hq, Hkv, D, N, M = 11, 4, 4, 2, 128, 2, 3
+    c, _, k, v, rk, rv = _mk_cache(T, Hq, Hkv, D, N=N, M=M, batch=1, seed=21)
+    qb = _prefill_queries(1, n, Hq, Hkv, D, 21)
+    got = orc.prefill_attention(qb, c.k[0], c.v[0], rk[0], rv[0], Hkv, N, M, 128, 0, 0)
+    for i in range(n):
+        want = _brute_attention(qb[:, i], k, v, rk[0], rv[0], Hkv, N, M, 128, 0.96, 0.92, ntok=T - n + i + 1)
+        np.testing.assert_allclose(got[:, i], want, rtol=1e-9, atol=1e-9)
