@@ -682,6 +682,44 @@ int oscar_int2_decode_attn(oscar_kv* kv, int32_t layer, const void* q, void* out
   return launch_decode(kv, layer, q, out, out_dtype, batch, softmax_scale, L.T, nullptr, stream);
 }
 
+int oscar_prefill_attn(oscar_kv* kv, int32_t layer, const void* q, void* out, int32_t out_dtype,
+                       int32_t batch, int32_t n_q, float softmax_scale, hipStream_t stream) {
+  int rc = check_decode_args(kv, layer, q, out, out_dtype, softmax_scale);
+  if (rc) return rc;
+  const Layer& L = kv->layers[layer];
+  const auto& c = kv->cfg;
+  if (c.head_dim != 128) return fail(OSCAR_ERR_UNSUPPORTED, "prefill attention needs head_dim 128");
+  if (64 % (c.num_q_heads / c.num_kv_heads) != 0)
+    return fail(OSCAR_ERR_UNSUPPORTED, "prefill attention needs a power-of-two number of query heads per kv head");
+  if (L.T == 0) return fail(OSCAR_ERR_INVALID_ARG, "layer holds no tokens");
+  if (batch != L.batch) return fail(OSCAR_ERR_INVALID_ARG, "batch differs from the layer's batch");
+  if (n_q < 1 || n_q > L.T) return fail(OSCAR_ERR_INVALID_ARG, "n_q must be in [1, tokens of the layer]");
+  HIP_TRY(hipSetDevice(c.device));
+  const size_t DD = (size_t)c.head_dim * c.head_dim;
+  PrefillAttnArgs a{};
+  a.k = plane_dev(kv, L.k, false);
+  a.v = plane_dev(kv, L.v, true);
+  a.q = static_cast<const uint16_t*>(q);
+  a.out = out;
+  a.out_dtype = out_dtype;
+  a.rk = kv->rk + layer * DD;
+  a.rvT = kv->rvT + layer * DD;
+  a.absorb_v = c.absorb_v_rotation;
+  a.B = batch;
+  a.n = n_q;
+  a.Hq = c.num_q_heads;
+  a.Hkv = c.num_kv_heads;
+  a.Gq = c.num_q_heads / c.num_kv_heads;
+  a.cap = kv->cap;
+  a.N = c.sink_tokens;
+  a.M = c.recent_tokens;
+  a.T = L.T;
+  const float scale = softmax_scale > 0.0f ? softmax_scale : 1.0f / std::sqrt((float)c.head_dim);
+  a.scale_log2 = scale * 1.4426950408889634f;
+  HIP_TRY(launch_prefill_attn(a, stream));
+  return OSCAR_OK;
+}
+
 int oscar_kv_decode_step(oscar_kv* kv, int32_t layer, const void* k, const void* v, const void* q, void* out,
                          int32_t out_dtype, int32_t batch, float softmax_scale, hipStream_t stream) {
   int rc = check_decode_args(kv, layer, q, out, out_dtype, softmax_scale);

@@ -1,0 +1,374 @@
+// Chunked-prefill attention over the mixed INT2 + bf16 cache (head_dim 128).
+//
+// The serving hosts run a prefill backend beside the decode one (RotationZoo
+// "How to use", the sglang launch's attention backends).  Here the queries of
+// the last n cached positions T - n .. T - 1 attend causally over the cache as
+// it stands after their chunk was appended: query i, at position p = T - n + i,
+// reads positions [0, p]; the sink and recent windows of the current length T
+// give their bf16 values, every other position its INT2 codes with the
+// per-group fp16 scale and zero ("OSCAR: 2-bit KV Cache Quantization for
+// SGLang and llama.cpp", "What OSCAR compresses").  q is rotated by R_K and the
+// output un-rotated by R_V^T, as in the decode step.
+//
+// Block = 4 waves, one (sequence, kv head) and 64 query rows (64 / Gq queries
+// x Gq heads of the kv head; wave w owns rows [16 w, 16 w + 16)).  Per 64-token
+// key tile:
+//   - the block stages the K tile [token][dim] and the V tile transposed
+//     [dim][token] in shared memory as bf16 operands: INT2 positions as their
+//     codes (0..3, exact in bf16) with the token's scale and zero kept aside,
+//     window positions as their bf16 values (scale 1, zero 0);
+//   - S = q K^T on v_mfma_f32_16x16x32_bf16, with q split into two bf16 pieces
+//     (hi = bf16(q), lo = bf16(q - hi)) so that q keeps 16 significant bits;
+//     the score of an INT2 token is s_K (q . c) + z_K (sum of q), in log2 units
+//     (q carries softmax scale x log2 e);
+//   - causal mask, online softmax per row;
+//   - O += (p s_V) V on the matrix cores, p s_V split into two bf16 pieces the
+//     same way; the zero's share (sum of p z_V per row) is added at the end.
+// Last, o' = O / l, and o = o' R_V^T (or o' itself when the V rotation is
+// absorbed).
+#include "append_impl.h"
+
+namespace oscar {
+
+namespace {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+
+constexpr float kNegInf = -__builtin_huge_valf();
+
+struct PASmem {
+  union {
+    float rows[64][132];           // q rows before the rotation; o' rows before the un-rotation
+    struct {
+      uint16_t kt[64][136];        // K operand tile [token][dim], bf16 bits
+      uint16_t vt[128][72];        // V operand tile [dim][token], bf16 bits
+      uint16_t ph[64][72];         // p s_V, high bf16 piece [row][token]
+      uint16_t pl[64][72];         // p s_V, low bf16 piece
+    } t;
+  };
+  float ks[64], kz[64], vs[64], vz[64];   // per-token scale and zero of the tile
+  float qsum[64];                         // per row: sum of q over dims (both pieces)
+};
+
+// bf16 bits of the code value c in {0, 1, 2, 3}
+__device__ inline uint32_t code_bf16(uint32_t c) {
+  // 0 -> 0x0000, 1 -> 0x3F80, 2 -> 0x4000, 3 -> 0x4040
+  return c == 0 ? 0u : (c == 1 ? 0x3F80u : (c == 2 ? 0x4000u : 0x4040u));
+}
+
+__device__ inline void split_bf16(float x, uint16_t& hi, uint16_t& lo) {
+  hi = f32_to_bf16(x);
+  lo = f32_to_bf16(x - bf16_to_f32(hi));
+}
+
+__device__ inline void store_prefill_out(const PrefillAttnArgs& a, size_t o, float v) {
+  if (a.out_dtype == 0)
+    reinterpret_cast<float*>(a.out)[o] = v;
+  else if (a.out_dtype == 1)
+    reinterpret_cast<uint16_t*>(a.out)[o] = f32_to_bf16(v);
+  else
+    reinterpret_cast<uint16_t*>(a.out)[o] = __builtin_bit_cast(uint16_t, (_Float16)v);
+}
+
+// row r of the block -> query index (clamped to the last query) and query head
+__device__ inline int row_query(const PrefillAttnArgs& a, int i0, int r) { return min(i0 + r / a.Gq, a.n - 1); }
+
+}  // namespace
+
+__global__ __launch_bounds__(256) void prefill_attn_kernel(PrefillAttnArgs a) {
+  constexpr int D = 128;
+  __shared__ PASmem S;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int bh = blockIdx.x;
+  const int b = bh / a.Hkv, h = bh - (bh / a.Hkv) * a.Hkv;
+  const int QB = 64 / a.Gq;                       // queries per block
+  const int i0 = (int)blockIdx.y * QB;
+  const int T = a.T;
+  const int sink_end = min(a.N, T), rec_begin = max(a.N, T - a.M);
+
+  // ---- q rows (bf16 -> fp32), rotation by R_K, scale x log2 e
+  for (int idx = tid; idx < 64 * D; idx += 256) {
+    const int r = idx >> 7, d = idx & 127;
+    const int i = row_query(a, i0, r), hq = h * a.Gq + r % a.Gq;
+    S.rows[r][d] = bf16_to_f32(a.q[(((size_t)b * a.n + i) * a.Hq + hq) * D + d]);
+  }
+  __syncthreads();
+  {
+    const int d = tid & 127, r0 = tid >> 7;       // rows r0, r0 + 2, ..., 32 of them
+    float acc[32];
+#pragma unroll
+    for (int k = 0; k < 32; ++k) acc[k] = 0.0f;
+    for (int e = 0; e < D; ++e) {
+      const float re = a.rk[e * D + d];
+#pragma unroll
+      for (int k = 0; k < 32; ++k) acc[k] = __builtin_fmaf(S.rows[r0 + 2 * k][e], re, acc[k]);
+    }
+    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < 32; ++k) S.rows[r0 + 2 * k][d] = acc[k] * a.scale_log2;
+  }
+  __syncthreads();
+  // A operands: lane (m, kq) holds row 16 wave + m, dims 32 ks + kq .. + 8
+  const int m = lane & 15, kq = 8 * (lane >> 4);
+  u32x4_t qh[4], ql[4];
+  float qpart = 0.0f;
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      uint16_t h0, l0, h1, l1;
+      split_bf16(S.rows[16 * wave + m][32 * ks + kq + 2 * e], h0, l0);
+      split_bf16(S.rows[16 * wave + m][32 * ks + kq + 2 * e + 1], h1, l1);
+      qh[ks][e] = (uint32_t)h0 | ((uint32_t)h1 << 16);
+      ql[ks][e] = (uint32_t)l0 | ((uint32_t)l1 << 16);
+      qpart += (bf16_to_f32(h0) + bf16_to_f32(l0)) + (bf16_to_f32(h1) + bf16_to_f32(l1));
+    }
+  }
+  qpart += __shfl_xor(qpart, 16);
+  qpart += __shfl_xor(qpart, 32);
+  if (lane < 16) S.qsum[16 * wave + m] = qpart;
+  // (the first tile's barrier orders these writes before their reads)
+
+  // ---- key tiles
+  // accumulator layout (S and O): register i of a 16 x 16 block is row
+  // 16 wave + 4 (lane >> 4) + i, column 16 cb + (lane & 15)
+  int prow[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) prow[i] = T - a.n + row_query(a, i0, 16 * wave + 4 * (lane >> 4) + i);
+  const int p_max = T - a.n + min(i0 + QB - 1, a.n - 1);
+  const int ntiles = (p_max >> 6) + 1;
+  float mrun[4], lrun[4], zrun[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    mrun[i] = kNegInf;
+    lrun[i] = 0.0f;
+    zrun[i] = 0.0f;
+  }
+  f32x4 oacc[8];
+#pragma unroll
+  for (int db = 0; db < 8; ++db) oacc[db] = f32x4{0, 0, 0, 0};
+
+  const PlaneDev& K = a.k;
+  const PlaneDev& V = a.v;
+  for (int tt = 0; tt < ntiles; ++tt) {
+    const int t0 = tt << 6;
+    __syncthreads();                              // the previous tile's operands are consumed
+    // token tk = tid / 4, dims [32 qd, 32 qd + 32)
+    {
+      const int tk = tid >> 2, qd = tid & 3, t = t0 + tk;
+      const bool in = t < T;
+      const bool win = in && (t < sink_end || t >= rec_begin);
+      // K
+      if (!in) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) *reinterpret_cast<u32x4_t*>(&S.t.kt[tk][32 * qd + 8 * i]) = u32x4_t{0, 0, 0, 0};
+        if (qd == 0) { S.ks[tk] = 0.0f; S.kz[tk] = 0.0f; }
+      } else if (win || K.is_bf16) {
+        const uint16_t* src = K.is_bf16 ? K.full + row_offset(bh, a.cap, t, D)
+                            : t < sink_end ? K.sink + row_offset(bh, a.N, t, D)
+                                           : K.ring + row_offset(bh, a.M, t % a.M, D);
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          *reinterpret_cast<u32x4_t*>(&S.t.kt[tk][32 * qd + 8 * i]) =
+              *reinterpret_cast<const u32x4_t*>(src + 32 * qd + 8 * i);
+        if (qd == 0) { S.ks[tk] = 1.0f; S.kz[tk] = 0.0f; }
+      } else {
+        const u32x2_t w = *reinterpret_cast<const u32x2_t*>(K.codes + kcode_byte(bh, a.cap, t, 8 * qd, D));
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {               // dims 32 qd + 8 i .. + 8 = code bits 16 i .. 16 i + 16 of w
+          const uint32_t word = (i < 2 ? w[0] : w[1]) >> (16 * (i & 1));
+          u32x4_t o;
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            o[e] = code_bf16((word >> (4 * e)) & 3u) | (code_bf16((word >> (4 * e + 2)) & 3u) << 16);
+          *reinterpret_cast<u32x4_t*>(&S.t.kt[tk][32 * qd + 8 * i]) = o;
+        }
+        if (qd == 0) {
+          const uint32_t mw = K.meta[meta_index(bh, a.cap, t, 0, D)];
+          S.ks[tk] = (float)__builtin_bit_cast(_Float16, (uint16_t)(mw & 0xFFFFu));
+          S.kz[tk] = (float)__builtin_bit_cast(_Float16, (uint16_t)(mw >> 16));
+        }
+      }
+      // V: INT2 codes of the whole tile from the tiled layout (8 bytes per
+      // thread), then the window (or bf16-plane) tokens overwrite their columns
+      if (!V.is_bf16) {
+        const u32x2_t w = *reinterpret_cast<const u32x2_t*>(V.codes + vcode_tile_base(bh, a.cap, t0, 0, D) + 8 * tid);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const int p8 = 8 * tid + j;
+          const int hh = p8 >> 10, l = (p8 >> 4) & 63, rec = 16 * hh + (p8 & 15);
+          const int ds = 64 * (rec & 1) + 4 * (l >> 2) + (l & 3);
+          const int tb0 = 8 * (rec >> 2) + ((rec & 3) >> 1);
+          const uint32_t byte = ((j < 4 ? w[0] : w[1]) >> (8 * (j & 3))) & 0xFFu;
+#pragma unroll
+          for (int qq = 0; qq < 4; ++qq) S.t.vt[ds][tb0 + 2 * (qq & 1) + 4 * (qq >> 1)] = (uint16_t)code_bf16((byte >> (2 * qq)) & 3u);
+        }
+      }
+      if (qd == 0) {
+        if (!in) { S.vs[tk] = 0.0f; S.vz[tk] = 0.0f; }
+        else if (win || V.is_bf16) { S.vs[tk] = 1.0f; S.vz[tk] = 0.0f; }
+        else {
+          const uint32_t mw = V.meta[meta_index(bh, a.cap, t, 0, D)];
+          S.vs[tk] = (float)__builtin_bit_cast(_Float16, (uint16_t)(mw & 0xFFFFu));
+          S.vz[tk] = (float)__builtin_bit_cast(_Float16, (uint16_t)(mw >> 16));
+        }
+      }
+    }
+    const bool tile_has_window = V.is_bf16 || t0 < sink_end || t0 + 64 > rec_begin || t0 + 64 > T;   // block-uniform
+    if (tile_has_window) {
+      __syncthreads();                            // the code pass has written every column
+      const int tk = tid >> 2, qd = tid & 3, t = t0 + tk;
+      if (t >= T) {
+#pragma unroll
+        for (int e = 0; e < 32; ++e) S.t.vt[32 * qd + e][tk] = 0;
+      } else if (V.is_bf16 || t < sink_end || t >= rec_begin) {
+        const uint16_t* src = V.is_bf16 ? V.full + row_offset(bh, a.cap, t, D)
+                            : t < sink_end ? V.sink + row_offset(bh, a.N, t, D)
+                                           : V.ring + row_offset(bh, a.M, t % a.M, D);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const u32x4_t w = *reinterpret_cast<const u32x4_t*>(src + 32 * qd + 8 * i);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            S.t.vt[32 * qd + 8 * i + 2 * e][tk] = (uint16_t)(w[e] & 0xFFFFu);
+            S.t.vt[32 * qd + 8 * i + 2 * e + 1][tk] = (uint16_t)(w[e] >> 16);
+          }
+        }
+      }
+    }
+    __syncthreads();
+
+    // S = q K^T for the wave's 16 rows and the tile's 64 tokens
+    f32x4 sacc[4];
+#pragma unroll
+    for (int cb = 0; cb < 4; ++cb) {
+      sacc[cb] = f32x4{0, 0, 0, 0};
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        const u32x4_t fb = *reinterpret_cast<const u32x4_t*>(&S.t.kt[16 * cb + m][32 * ks + kq]);
+        sacc[cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, qh[ks]),
+                                                           __builtin_bit_cast(bf16x8_t, fb), sacc[cb], 0, 0, 0);
+        sacc[cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, ql[ks]),
+                                                           __builtin_bit_cast(bf16x8_t, fb), sacc[cb], 0, 0, 0);
+      }
+    }
+    // scores, mask, online softmax
+    float sc[4][4];
+    float tmax[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) tmax[i] = kNegInf;
+#pragma unroll
+    for (int cb = 0; cb < 4; ++cb) {
+      const int tk = 16 * cb + m, t = t0 + tk;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = 16 * wave + 4 * (lane >> 4) + i;
+        const float v = __builtin_fmaf(S.ks[tk], sacc[cb][i], S.kz[tk] * S.qsum[r]);
+        sc[cb][i] = t <= prow[i] ? v : kNegInf;
+        tmax[i] = fmaxf(tmax[i], sc[cb][i]);
+      }
+    }
+    float alpha[4], mnew[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      float x = tmax[i];
+      x = fmaxf(x, __shfl_xor(x, 1));
+      x = fmaxf(x, __shfl_xor(x, 2));
+      x = fmaxf(x, __shfl_xor(x, 4));
+      x = fmaxf(x, __shfl_xor(x, 8));
+      mnew[i] = fmaxf(mrun[i], x);
+      alpha[i] = mnew[i] == kNegInf ? 1.0f : exp2f(mrun[i] - mnew[i]);
+      mrun[i] = mnew[i];
+      lrun[i] *= alpha[i];
+      zrun[i] *= alpha[i];
+    }
+#pragma unroll
+    for (int db = 0; db < 8; ++db)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) oacc[db][i] *= alpha[i];
+#pragma unroll
+    for (int cb = 0; cb < 4; ++cb) {
+      const int tk = 16 * cb + m;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = 16 * wave + 4 * (lane >> 4) + i;
+        const float p = sc[cb][i] == kNegInf ? 0.0f : exp2f(sc[cb][i] - mnew[i]);
+        lrun[i] += p;
+        zrun[i] = __builtin_fmaf(p, S.vz[tk], zrun[i]);
+        uint16_t hi, lo;
+        split_bf16(p * S.vs[tk], hi, lo);
+        S.t.ph[r][tk] = hi;
+        S.t.pl[r][tk] = lo;
+      }
+    }
+    __syncthreads();                              // p s_V rows are complete
+    // O += (p s_V) V: A = rows of p s_V (tokens 32 ks + kq .. + 8), B = V^T
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      const u32x4_t ah = *reinterpret_cast<const u32x4_t*>(&S.t.ph[16 * wave + m][32 * ks + kq]);
+      const u32x4_t al = *reinterpret_cast<const u32x4_t*>(&S.t.pl[16 * wave + m][32 * ks + kq]);
+#pragma unroll
+      for (int db = 0; db < 8; ++db) {
+        const u32x4_t fb = *reinterpret_cast<const u32x4_t*>(&S.t.vt[16 * db + m][32 * ks + kq]);
+        oacc[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, ah),
+                                                           __builtin_bit_cast(bf16x8_t, fb), oacc[db], 0, 0, 0);
+        oacc[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, al),
+                                                           __builtin_bit_cast(bf16x8_t, fb), oacc[db], 0, 0, 0);
+      }
+    }
+  }
+
+  // ---- o' = (O + sum p z_V) / l, then o = o' R_V^T
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    float l = lrun[i], z = zrun[i];
+    l += __shfl_xor(l, 1); z += __shfl_xor(z, 1);
+    l += __shfl_xor(l, 2); z += __shfl_xor(z, 2);
+    l += __shfl_xor(l, 4); z += __shfl_xor(z, 4);
+    l += __shfl_xor(l, 8); z += __shfl_xor(z, 8);
+    lrun[i] = 1.0f / l;
+    zrun[i] = z;
+  }
+  __syncthreads();                                // the tiles are consumed: rows[] is free
+#pragma unroll
+  for (int db = 0; db < 8; ++db)
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      S.rows[16 * wave + 4 * (lane >> 4) + i][16 * db + m] = (oacc[db][i] + zrun[i]) * lrun[i];
+  __syncthreads();
+  const int d = tid & 127, r0 = tid >> 7;
+  if (a.absorb_v) {
+    for (int k = 0; k < 32; ++k) {
+      const int r = r0 + 2 * k, i = i0 + r / a.Gq;
+      if (i < a.n && i < i0 + QB)
+        store_prefill_out(a, (((size_t)b * a.n + i) * a.Hq + h * a.Gq + r % a.Gq) * D + d, S.rows[r][d]);
+    }
+    return;
+  }
+  float acc[32];
+#pragma unroll
+  for (int k = 0; k < 32; ++k) acc[k] = 0.0f;
+  for (int e = 0; e < D; ++e) {
+    const float re = a.rvT[e * D + d];
+#pragma unroll
+    for (int k = 0; k < 32; ++k) acc[k] = __builtin_fmaf(S.rows[r0 + 2 * k][e], re, acc[k]);
+  }
+#pragma unroll
+  for (int k = 0; k < 32; ++k) {
+    const int r = r0 + 2 * k, i = i0 + r / a.Gq;
+    if (i < a.n && i < i0 + QB)
+      store_prefill_out(a, (((size_t)b * a.n + i) * a.Hq + h * a.Gq + r % a.Gq) * D + d, acc[k]);
+  }
+}
+
+hipError_t launch_prefill_attn(const PrefillAttnArgs& a, hipStream_t s) {
+  const int QB = 64 / a.Gq;
+  dim3 grid((unsigned)(a.B * a.Hkv), (unsigned)((a.n + QB - 1) / QB));
+  hipLaunchKernelGGL(prefill_attn_kernel, grid, dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace oscar

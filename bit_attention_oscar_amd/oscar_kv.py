@@ -32,7 +32,7 @@ EXPORTED = [
     "oscar_last_error", "oscar_kv_length", "oscar_kv_device_bytes", "oscar_kv_set_num_splits",
     "oscar_kv_set_decode_impl", "oscar_kv_export", "oscar_kv_append_dump", "oscar_quantize_rows",
     "oscar_kv_profile_enable", "oscar_kv_profile_read", "oscar_stream_copy", "oscar_stream_read",
-    "oscar_kv_decode_step",
+    "oscar_kv_decode_step", "oscar_prefill_attn",
 ]
 
 
@@ -77,6 +77,7 @@ def load_library(path: str = LIB_PATH) -> C.CDLL:
         "oscar_stream_copy": ([vp, vp, C.c_size_t, vp], C.c_int),
         "oscar_stream_read": ([vp, C.c_size_t, vp, vp], C.c_int),
         "oscar_kv_decode_step": ([vp, i32, vp, vp, vp, vp, i32, i32, f32, vp], C.c_int),
+        "oscar_prefill_attn": ([vp, i32, vp, vp, i32, i32, i32, f32, vp], C.c_int),
     }
     for name, (args, res) in sig.items():
         fn = getattr(lib, name)
@@ -128,6 +129,11 @@ def oscar_int2_decode_attn(kv, layer, q, out, out_dtype, batch, softmax_scale=0.
 def oscar_kv_decode_step(kv, layer, k, v, q, out, out_dtype, batch, softmax_scale=0.0, stream=None):
     _check(_lib.oscar_kv_decode_step(kv, layer, _ptr(k), _ptr(v), _ptr(q), _ptr(out), out_dtype, batch,
                                      float(softmax_scale), _stream(stream)))
+
+
+def oscar_prefill_attn(kv, layer, q, out, out_dtype, batch, n_q, softmax_scale=0.0, stream=None):
+    _check(_lib.oscar_prefill_attn(kv, layer, _ptr(q), _ptr(out), out_dtype, batch, n_q,
+                                   float(softmax_scale), _stream(stream)))
 
 
 def oscar_kv_destroy(kv):
@@ -236,6 +242,10 @@ class KVCache:
 
     def decode_attn(self, layer, q, out, out_dtype=OUT_F32, softmax_scale=0.0, stream=None):
         oscar_int2_decode_attn(self.handle, layer, q, out, out_dtype, q.shape[0], softmax_scale, stream)
+
+    def prefill_attn(self, layer, q, out, out_dtype=OUT_F32, softmax_scale=0.0, stream=None):
+        """Causal attention of the last q.shape[1] cached positions' queries over the cache."""
+        oscar_prefill_attn(self.handle, layer, q, out, out_dtype, q.shape[0], q.shape[1], softmax_scale, stream)
 
     def decode_step(self, layer, k, v, q, out, out_dtype=OUT_F32, softmax_scale=0.0, stream=None):
         """append(k, v) of one token then decode_attn(q) -> out, fused where possible."""

@@ -147,6 +147,25 @@ int oscar_int2_decode_attn(oscar_kv* kv, int32_t layer, const void* q, void* out
  * 512 (matrix-core path) the append runs in the same launch as the q
  * rotation, before the attention launch.  Other shapes run the two calls'
  * launches in turn. */
+/* Chunked-prefill attention over the mixed cache (RotationZoo "How to use":
+ * the serving host runs a prefill backend beside the decode one).  The n_q
+ * queries are those of the last n_q cached positions of `layer` (normally the
+ * chunk just appended with oscar_kv_append): query i, at position
+ * p = T_l - n_q + i, attends causally over positions [0, p] of the cache as it
+ * stands, i.e. the sink and recent windows of the current length T_l read their
+ * bf16 values and every other position its INT2 codes with the group's scale
+ * and zero.  q is rotated by R_K; the output is un-rotated by R_V^T (or left in
+ * the V-rotated basis with absorb_v_rotation).
+ *   q:   device bf16 [batch][n_q][Hq][D], post-RoPE, un-rotated;
+ *   out: device [batch][n_q][Hq][D] of out_dtype;
+ *   softmax_scale <= 0 selects 1/sqrt(D).
+ * head_dim 128 only (UNSUPPORTED otherwise).  Nothing is allocated; the cache
+ * is read only.
+ * Errors: INVALID_ARG (including n_q < 1, n_q > T_l, batch != the layer's
+ * batch), UNSUPPORTED, HIP. */
+int oscar_prefill_attn(oscar_kv* kv, int32_t layer, const void* q, void* out, int32_t out_dtype,
+                       int32_t batch, int32_t n_q, float softmax_scale, hipStream_t stream);
+
 int oscar_kv_decode_step(oscar_kv* kv, int32_t layer, const void* k, const void* v, const void* q,
                          void* out, int32_t out_dtype, int32_t batch, float softmax_scale,
                          hipStream_t stream);

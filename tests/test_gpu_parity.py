@@ -9,7 +9,7 @@ import pytest
 
 import oracle as orc
 import synth
-from tests.gpu_util import (Shape, gpu_cache, inputs, make_rotations, oracle_cache, oracle_on_exported,
+from tests.gpu_util import (Shape, gpu_cache, inputs, make_rotations, oracle_cache, oracle_on_exported, planes_from_export,
                             query, rel_l2, say)
 
 torch = pytest.importorskip("torch")
@@ -794,3 +794,126 @@ def test_in_quant_hadamard(ok, shape):
     say(f"  end to end vs the oracle's own cache: rel L2 {e2e:.3e}")
     assert e2e <= 1e-2
     gc.close()
+
+
+# ------------------------------------------------------------------ chunked-prefill attention
+
+
+def _prefill_q(shape, mask, n, step0=0):
+    return np.stack([query(shape, mask, step=step0 + i) for i in range(n)], axis=1)   # [B, n, Hq, D]
+
+
+def _prefill_gpu(gc, qb, out_dtype=0):
+    B, n, Hq, D = qb.shape
+    dt = {0: torch.float32, 1: torch.bfloat16, 2: torch.float16}[out_dtype]
+    out = torch.zeros((B, n, Hq, D), dtype=dt, device="cuda")
+    gc.prefill_attn(0, dev(qb), out, out_dtype)
+    torch.cuda.synchronize()
+    return out.float().cpu().numpy()
+
+
+def _prefill_oracle(gc, qb, shape, rk, rv, absorb_v=False):
+    T = gc.length(0)
+    kp = planes_from_export(gc.export(0, 0), T, shape.N, shape.M)
+    vp = planes_from_export(gc.export(0, 1), T, shape.N, shape.M)
+    D = shape.D
+    Rk = rk[0] if rk is not None else np.eye(D, dtype=np.float32)
+    Rv = rv[0] if rv is not None else np.eye(D, dtype=np.float32)
+    return orc.prefill_attention(qb, kp, vp, Rk, Rv, shape.Hkv, shape.N, shape.M, 128,
+                                 shape.k_dtype, shape.v_dtype, absorb_v=absorb_v)
+
+
+@pytest.mark.parametrize("shape,T0,n", [
+    (Shape(B=2, Hq=8, Hkv=2, N=16, M=64), 500, 200),            # 4 query heads per kv head, INT2 inside the chunk
+    (Shape(B=1, Hq=16, Hkv=2, N=16, M=64), 300, 130),           # 8 per kv head
+    (Shape(B=2, Hq=2, Hkv=2, N=16, M=64), 200, 70),             # 1 per kv head
+    (Shape(B=1, Hq=8, Hkv=2, N=16, M=64, v_dtype=1), 300, 100), # bf16 V plane
+    (Shape(B=1, Hq=8, Hkv=2, N=0, M=0), 150, 67),               # no windows: INT2 everywhere
+    (Shape(B=1, Hq=8, Hkv=2, N=40, M=60), 0, 100),              # the whole sequence is the chunk, all window
+    (Shape(B=1, Hq=8, Hkv=2, N=3, M=500), 700, 129),            # recent window longer than the chunk
+])
+def test_prefill_attn_vs_oracle(ok, shape, T0, n):
+    """Chunked-prefill attention through the C ABI against the oracle over the
+    identical (exported) cache: every query of the chunk, rel L2 <= 2e-3."""
+    say(f"[prefill attention] {shape} T0={T0} n={n}")
+    rk, rv = make_rotations(shape, "haar")
+    k, v, mask = inputs(shape, T0 + n)
+    gc = gpu_cache(ok, shape, rk, rv, T0 + n + 8)
+    if T0:
+        gc.append(0, dev(k[:, :T0]), dev(v[:, :T0]))
+    gc.append(0, dev(k[:, T0:]), dev(v[:, T0:]))
+    qb = _prefill_q(shape, mask, n)
+    got = _prefill_gpu(gc, qb)
+    want = _prefill_oracle(gc, qb, shape, rk, rv)
+    e = rel_l2(got, want)
+    worst = max(rel_l2(got[:, i], want[:, i]) for i in range(n))
+    say(f"  rel L2 {e:.3e} (worst query {worst:.3e})")
+    assert e <= ATTN_TOL and worst <= ATTN_TOL
+    gc.close()
+
+
+def test_prefill_attn_last_query_is_decode(ok):
+    """The chunk's last query attends over the whole cache: it equals the
+    decode attention call for the same q (two kernels, one definition), and a
+    chunk of one query is that call."""
+    shape = Shape(B=2, Hq=8, Hkv=2, N=16, M=64)
+    say("[prefill attention] last query vs decode")
+    rk, rv = make_rotations(shape, "haar")
+    T = 900
+    k, v, mask = inputs(shape, T)
+    gc = gpu_cache(ok, shape, rk, rv, T + 8)
+    gc.append(0, dev(k), dev(v))
+    qb = _prefill_q(shape, mask, 3)
+    got = _prefill_gpu(gc, qb)
+    dec = _decode(ok, gc, 0, qb[:, -1])
+    say(f"  last query vs decode: {rel_l2(got[:, -1], dec):.2e}")
+    assert rel_l2(got[:, -1], dec) <= 1e-3
+    one = _prefill_gpu(gc, qb[:, -1:])
+    assert rel_l2(one[:, 0], dec) <= 1e-3
+    gc.close()
+
+
+def test_prefill_attn_absorbed_and_dtypes(ok):
+    """absorb_v_rotation = 1 returns o' (the oracle's o'); bf16 and fp16
+    outputs are the fp32 output rounded."""
+    shape = Shape(B=1, Hq=8, Hkv=2, N=16, M=64)
+    say("[prefill attention] absorbed V rotation, output dtypes")
+    rk, rv = make_rotations(shape, "haar")
+    T0, n = 300, 90
+    k, v, mask = inputs(shape, T0 + n)
+    ga = gpu_cache(ok, shape, rk, rv, T0 + n, absorb_v=1)
+    ga.append(0, dev(k), dev(v))
+    qb = _prefill_q(shape, mask, n)
+    got = _prefill_gpu(ga, qb)
+    want = _prefill_oracle(ga, qb, shape, rk, rv, absorb_v=True)
+    assert rel_l2(got, want) <= ATTN_TOL
+    for dt, tol in ((1, 2.0 ** -8), (2, 2.0 ** -11)):
+        o = _prefill_gpu(ga, qb, dt)
+        assert np.abs(o - got).max() <= tol * np.abs(got).max() + 1e-6
+    ga.close()
+
+
+def test_prefill_attn_rejects(ok):
+    """Argument checks before anything is enqueued: n_q beyond the cached
+    tokens, a batch other than the layer's, head_dim 512."""
+    shape = Shape(B=1, Hq=8, Hkv=2, N=16, M=64)
+    rk, rv = make_rotations(shape, "haar")
+    k, v, mask = inputs(shape, 40)
+    gc = gpu_cache(ok, shape, rk, rv, 64)
+    gc.append(0, dev(k), dev(v))
+    q = torch.zeros((1, 41, 8, 128), dtype=torch.bfloat16, device="cuda")
+    out = torch.zeros((1, 41, 8, 128), dtype=torch.float32, device="cuda")
+    with pytest.raises(ok.OscarError):
+        gc.prefill_attn(0, q, out)
+    with pytest.raises(ok.OscarError):
+        ok.oscar_prefill_attn(gc.handle, 0, q, out, 0, 2, 4)
+    gc.close()
+    wide = Shape(B=1, Hq=4, Hkv=2, D=512, N=16, M=64)
+    gw = gpu_cache(ok, wide, None, None, 64)
+    kw, vw, _ = inputs(wide, 10)
+    gw.append(0, dev(kw), dev(vw))
+    qw = torch.zeros((1, 2, 4, 512), dtype=torch.bfloat16, device="cuda")
+    ow = torch.zeros((1, 2, 4, 512), dtype=torch.float32, device="cuda")
+    with pytest.raises(ok.OscarError):
+        gw.prefill_attn(0, qw, ow)
+    gw.close()
