@@ -111,6 +111,36 @@ def fill_layer_device(cache, layer, B, Hkv, D, T, seed=0, dist="normal", outlier
     return mask
 
 
+def time_prefill_attention(cache, B, Hq, Hkv, D, T, n, reps=3):
+    """Chunked-prefill attention of the last n cached positions' queries
+    (oscar_prefill_attn) on layer 0, timed with HIP events; median of reps.
+    Useful flops: QK^T and PV over each query's causal prefix, 4 D per
+    (query head, key); the matrix cores do twice that (q and p s_V each enter
+    as two bf16 pieces)."""
+    import torch
+    if D != 128 or n <= 0:
+        return None
+    g = torch.Generator(device="cuda")
+    g.manual_seed(12345)
+    q = torch.randn((B, n, Hq, D), generator=g, device="cuda").to(torch.bfloat16)
+    out = torch.empty((B, n, Hq, D), dtype=torch.float32, device="cuda")
+    ts = []
+    for _ in range(reps + 1):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        cache.prefill_attn(0, q, out)
+        e1.record()
+        torch.cuda.synchronize()
+        ts.append(e0.elapsed_time(e1))
+    ms = float(sorted(ts[1:])[len(ts[1:]) // 2])
+    keys = n * (T - n) + n * (n + 1) / 2
+    useful = 4.0 * D * B * Hq * keys
+    return {"queries": n, "context": T, "median_ms": round(ms, 3),
+            "useful_TFLOPs": round(useful / ms / 1e9, 1), "mfma_TFLOPs": round(2 * useful / ms / 1e9, 1),
+            "mfma_peak_TFLOPs": 2500.0, "mfma_util": round(2 * useful / ms / 1e9 / 2500.0, 4),
+            "kernel": "prefill_attn_kernel"}
+
+
 def int2_bytes_per_token_head(D):
     return D // 4 + 4 * (D // 128)
 
@@ -288,6 +318,9 @@ def main():
         masks.append(fill_layer_device(cache, l, B, Hkv, D, T0, seed=0, dist=dist, outliers=outl, timings=prefill_t))
     torch.cuda.synchronize()
     log(f"filled in {time.perf_counter() - t_fill:.1f} s")
+    prefill_attn = time_prefill_attention(cache, B, Hq, Hkv, D, T0, min(4096, T0))
+    if prefill_attn:
+        log(f"prefill attention: {prefill_attn}")
 
     # per-step inputs, resident in HBM before timing
     steps_total = W + 2 * K
@@ -397,6 +430,7 @@ def main():
         "host_enqueue_ms_per_step": round(enqueue * 1e3 / K, 4),
         "hbm_read_measured": read_cal,
         "prefill": prefill_summary(prefill_t, B, Hkv, D),
+        "prefill_attention": prefill_attn,
         "roofline": roof,
     }
     if not args.no_cpu_baseline:
