@@ -176,18 +176,6 @@ struct DecodeArgs {
   AppendArgs app;          // that append (n_new = 1); T above counts the new token
 };
 
-struct PrefillAttnArgs {
-  PlaneDev k, v;
-  const uint16_t* q;       // bf16 [B][n][Hq][D]
-  void* out;               // [B][n][Hq][D] of out_dtype
-  int out_dtype;
-  const float* rk;         // fp32 [D][D] of this layer
-  const float* rvT;        // fp32 [D][D]: rvT[e][d] = R_V[d][e]
-  int absorb_v;
-  int B, n, Hq, Hkv, Gq, cap, N, M, T;
-  float scale_log2;        // softmax scale * log2(e)
-};
-
 // launchers (defined in the .hip files); return hipGetLastError()
 hipError_t launch_append(const AppendArgs& a, hipStream_t s);
 hipError_t launch_append_prefill(const AppendArgs& a, hipStream_t s);   // n_new > 1, rotation on matrix cores
@@ -196,7 +184,6 @@ hipError_t launch_quantize_rows(const float* x, int rows, int D, float clip, uin
 hipError_t launch_qrot(const QRotArgs& a, hipStream_t s);
 hipError_t launch_decode_valu(const DecodeArgs& a, int B, hipStream_t s);
 hipError_t launch_decode_mfma(const DecodeArgs& a, int B, int waves_per_block, hipStream_t s);
-hipError_t launch_prefill_attn(const PrefillAttnArgs& a, hipStream_t s);   // chunked-prefill attention
 int decode_mfma_resident_blocks(int device, int G);   // blocks of the matrix-core kernel resident at once
 hipError_t launch_combine(const CombineArgs& a, hipStream_t s);
 hipError_t launch_wide_qrot(const DecodeArgs& a, int B, hipStream_t s);     // head_dim 512: rotated q records

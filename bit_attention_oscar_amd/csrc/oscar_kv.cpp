@@ -14,6 +14,7 @@
 
 #include "../../include/oscar_kv.h"
 #include "common.h"
+#include "prefill_attn.h"
 
 using namespace oscar;
 

@@ -27,6 +27,7 @@
 // Last, o' = O / l, and o = o' R_V^T (or o' itself when the V rotation is
 // absorbed).
 #include "append_impl.h"
+#include "prefill_attn.h"
 
 namespace oscar {
 
