@@ -40,24 +40,36 @@ typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 
 constexpr float kNegInf = -__builtin_huge_valf();
 
-struct PASmem {
+struct alignas(16) PASmem {
   union {
     float rows[64][132];           // q rows before the rotation; o' rows before the un-rotation
     struct {
       uint16_t kt[64][136];        // K operand tile [token][dim], bf16 bits
       uint16_t vt[128][72];        // V operand tile [dim][token], bf16 bits
-      uint16_t ph[64][72];         // p s_V, high bf16 piece [row][token]
-      uint16_t pl[64][72];         // p s_V, low bf16 piece
+      float pf[64][68];            // p s_V [row][token], split into bf16 pieces when read
     } t;
   };
   float ks[64], kz[64], vs[64], vz[64];   // per-token scale and zero of the tile
   float qsum[64];                         // per row: sum of q over dims (both pieces)
 };
 
-// bf16 bits of the code value c in {0, 1, 2, 3}
-__device__ inline uint32_t code_bf16(uint32_t c) {
-  // 0 -> 0x0000, 1 -> 0x3F80, 2 -> 0x4000, 3 -> 0x4040
-  return c == 0 ? 0u : (c == 1 ? 0x3F80u : (c == 2 ? 0x4000u : 0x4040u));
+// Two codes as bf16 operands in one word: x holds code c0 in bits 0-1 and c1
+// in bits 16-17; the result is bf16(c0) | bf16(c1) << 16, through a byte
+// permutation of a table of the bf16 bytes of 0, 1, 2, 3 (low bytes 00 80 00
+// 40, high bytes 00 3F 40 40): selector byte i picks table byte c or 4 + c.
+__device__ inline uint32_t codes2_bf16(uint32_t x) {
+  const uint32_t sel = x * 0x0101u + 0x04000400u;
+  return __builtin_amdgcn_perm(0x40403F00u, 0x40008000u, sel);
+}
+
+// bf16 operand words of the 8 codes at bits 2k of a 16-bit chunk w (values in
+// order: word e holds codes 2e and 2e + 1)
+__device__ inline u32x4_t codes8_bf16(uint32_t w) {
+  const uint32_t v = (w & 0xFFFFu) | (((w & 0xFFFFu) >> 2) << 16);   // code 2e at bit 4e, code 2e+1 at bit 4e + 16
+  u32x4_t o;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) o[e] = codes2_bf16((v >> (4 * e)) & 0x00030003u);
+  return o;
 }
 
 __device__ inline void split_bf16(float x, uint16_t& hi, uint16_t& lo) {
@@ -79,7 +91,7 @@ __device__ inline int row_query(const PrefillAttnArgs& a, int i0, int r) { retur
 
 }  // namespace
 
-__global__ __launch_bounds__(256) void prefill_attn_kernel(PrefillAttnArgs a) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void prefill_attn_kernel(PrefillAttnArgs a) {
   constexpr int D = 128;
   __shared__ PASmem S;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
@@ -154,72 +166,84 @@ __global__ __launch_bounds__(256) void prefill_attn_kernel(PrefillAttnArgs a) {
 
   const PlaneDev& K = a.k;
   const PlaneDev& V = a.v;
+  auto half_f32 = [](uint32_t bits) { return (float)__builtin_bit_cast(_Float16, (uint16_t)bits); };
   for (int tt = 0; tt < ntiles; ++tt) {
     const int t0 = tt << 6;
     __syncthreads();                              // the previous tile's operands are consumed
-    // token tk = tid / 4, dims [32 qd, 32 qd + 32)
-    {
-      const int tk = tid >> 2, qd = tid & 3, t = t0 + tk;
-      const bool in = t < T;
-      const bool win = in && (t < sink_end || t >= rec_begin);
-      // K
-      if (!in) {
+    if (tid < 128) {
+      // V codes: thread (record l = tid % 64, dim half dh = tid / 64) writes dim
+      // ds = l + 64 dh of all 64 tokens.  The 2 KiB tile holds 64 lane records
+      // of 32 bytes in two 1 KiB halves; record byte rec (= 2 k + dh for
+      // dim ds) carries tokens 8 (k / 2) + (k % 2) + {0, 2, 4, 6} at bits
+      // {0, 2, 4, 6}: bytes k = 2G and 2G + 1 give tokens 8G .. 8G + 7.
+      const int l = tid & 63, dh = tid >> 6, ds = l + 64 * dh;
+      if (!V.is_bf16) {
+        const uint8_t* vt = V.codes + vcode_tile_base(bh, a.cap, t0, 0, D);
+        const u32x4_t c0 = *reinterpret_cast<const u32x4_t*>(vt + 16 * l);          // rec 0..15
+        const u32x4_t c1 = *reinterpret_cast<const u32x4_t*>(vt + 1024 + 16 * l);   // rec 16..31
 #pragma unroll
-        for (int i = 0; i < 4; ++i) *reinterpret_cast<u32x4_t*>(&S.t.kt[tk][32 * qd + 8 * i]) = u32x4_t{0, 0, 0, 0};
-        if (qd == 0) { S.ks[tk] = 0.0f; S.kz[tk] = 0.0f; }
-      } else if (win || K.is_bf16) {
+        for (int G = 0; G < 8; ++G) {
+          const int re = 4 * G + dh, ro = 4 * G + 2 + dh;            // record bytes of the even / odd tokens
+          const u32x4_t& c = G < 4 ? c0 : c1;
+          const uint32_t be = (c[(re & 15) >> 2] >> (8 * (re & 3))) & 0xFFu;
+          const uint32_t bo = (c[(ro & 15) >> 2] >> (8 * (ro & 3))) & 0xFFu;
+          const uint32_t v = be | (bo << 16);                        // token 8G + 2e at bit 2e, 8G + 2e + 1 at 16 + 2e
+          u32x4_t o;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) o[e] = codes2_bf16((v >> (2 * e)) & 0x00030003u);
+          *reinterpret_cast<u32x4_t*>(&S.t.vt[ds][8 * G]) = o;
+        }
+      }
+      if (tid < 64) {
+        const int t = t0 + tid;
+        float sv = 0.0f, zv = 0.0f;
+        if (t < T) {
+          if (V.is_bf16 || t < sink_end || t >= rec_begin) {
+            sv = 1.0f;
+          } else {
+            const uint32_t mw = V.meta[meta_index(bh, a.cap, t, 0, D)];
+            sv = half_f32(mw & 0xFFFFu);
+            zv = half_f32(mw >> 16);
+          }
+        }
+        S.vs[tid] = sv;
+        S.vz[tid] = zv;
+      }
+    } else {
+      // K: thread (token tk = (tid - 128) / 2, dim half kh) writes dims
+      // [64 kh, 64 kh + 64) of token tk: 16 code bytes, or the bf16 row piece
+      const int tk = (tid - 128) >> 1, kh = tid & 1, t = t0 + tk;
+      uint16_t* dst = &S.t.kt[tk][64 * kh];
+      float sk = 0.0f, zk = 0.0f;
+      if (t >= T) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) *reinterpret_cast<u32x4_t*>(dst + 8 * i) = u32x4_t{0, 0, 0, 0};
+      } else if (K.is_bf16 || t < sink_end || t >= rec_begin) {
         const uint16_t* src = K.is_bf16 ? K.full + row_offset(bh, a.cap, t, D)
                             : t < sink_end ? K.sink + row_offset(bh, a.N, t, D)
                                            : K.ring + row_offset(bh, a.M, t % a.M, D);
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-          *reinterpret_cast<u32x4_t*>(&S.t.kt[tk][32 * qd + 8 * i]) =
-              *reinterpret_cast<const u32x4_t*>(src + 32 * qd + 8 * i);
-        if (qd == 0) { S.ks[tk] = 1.0f; S.kz[tk] = 0.0f; }
+        for (int i = 0; i < 8; ++i)
+          *reinterpret_cast<u32x4_t*>(dst + 8 * i) = *reinterpret_cast<const u32x4_t*>(src + 64 * kh + 8 * i);
+        sk = 1.0f;
       } else {
-        const u32x2_t w = *reinterpret_cast<const u32x2_t*>(K.codes + kcode_byte(bh, a.cap, t, 8 * qd, D));
+        const u32x4_t w = *reinterpret_cast<const u32x4_t*>(K.codes + kcode_byte(bh, a.cap, t, 16 * kh, D));
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {               // dims 32 qd + 8 i .. + 8 = code bits 16 i .. 16 i + 16 of w
-          const uint32_t word = (i < 2 ? w[0] : w[1]) >> (16 * (i & 1));
-          u32x4_t o;
-#pragma unroll
-          for (int e = 0; e < 4; ++e)
-            o[e] = code_bf16((word >> (4 * e)) & 3u) | (code_bf16((word >> (4 * e + 2)) & 3u) << 16);
-          *reinterpret_cast<u32x4_t*>(&S.t.kt[tk][32 * qd + 8 * i]) = o;
-        }
-        if (qd == 0) {
-          const uint32_t mw = K.meta[meta_index(bh, a.cap, t, 0, D)];
-          S.ks[tk] = (float)__builtin_bit_cast(_Float16, (uint16_t)(mw & 0xFFFFu));
-          S.kz[tk] = (float)__builtin_bit_cast(_Float16, (uint16_t)(mw >> 16));
-        }
+        for (int i = 0; i < 8; ++i) *reinterpret_cast<u32x4_t*>(dst + 8 * i) = codes8_bf16(w[i >> 1] >> (16 * (i & 1)));
+        const uint32_t mw = K.meta[meta_index(bh, a.cap, t, 0, D)];
+        sk = half_f32(mw & 0xFFFFu);
+        zk = half_f32(mw >> 16);
       }
-      // V: INT2 codes of the whole tile from the tiled layout (8 bytes per
-      // thread), then the window (or bf16-plane) tokens overwrite their columns
-      if (!V.is_bf16) {
-        const u32x2_t w = *reinterpret_cast<const u32x2_t*>(V.codes + vcode_tile_base(bh, a.cap, t0, 0, D) + 8 * tid);
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const int p8 = 8 * tid + j;
-          const int hh = p8 >> 10, l = (p8 >> 4) & 63, rec = 16 * hh + (p8 & 15);
-          const int ds = 64 * (rec & 1) + 4 * (l >> 2) + (l & 3);
-          const int tb0 = 8 * (rec >> 2) + ((rec & 3) >> 1);
-          const uint32_t byte = ((j < 4 ? w[0] : w[1]) >> (8 * (j & 3))) & 0xFFu;
-#pragma unroll
-          for (int qq = 0; qq < 4; ++qq) S.t.vt[ds][tb0 + 2 * (qq & 1) + 4 * (qq >> 1)] = (uint16_t)code_bf16((byte >> (2 * qq)) & 3u);
-        }
-      }
-      if (qd == 0) {
-        if (!in) { S.vs[tk] = 0.0f; S.vz[tk] = 0.0f; }
-        else if (win || V.is_bf16) { S.vs[tk] = 1.0f; S.vz[tk] = 0.0f; }
-        else {
-          const uint32_t mw = V.meta[meta_index(bh, a.cap, t, 0, D)];
-          S.vs[tk] = (float)__builtin_bit_cast(_Float16, (uint16_t)(mw & 0xFFFFu));
-          S.vz[tk] = (float)__builtin_bit_cast(_Float16, (uint16_t)(mw >> 16));
-        }
+      if (kh == 0) {
+        S.ks[tk] = sk;
+        S.kz[tk] = zk;
       }
     }
     const bool tile_has_window = V.is_bf16 || t0 < sink_end || t0 + 64 > rec_begin || t0 + 64 > T;   // block-uniform
     if (tile_has_window) {
+      // V rows of window tokens (every token of a bf16 plane) overwrite their
+      // columns; positions past T are zeroed.  Thread: token tid / 4, dims
+      // [32 (tid % 4), + 32).
       __syncthreads();                            // the code pass has written every column
       const int tk = tid >> 2, qd = tid & 3, t = t0 + tk;
       if (t >= T) {
@@ -299,18 +323,24 @@ __global__ __launch_bounds__(256) void prefill_attn_kernel(PrefillAttnArgs a) {
         const float p = sc[cb][i] == kNegInf ? 0.0f : exp2f(sc[cb][i] - mnew[i]);
         lrun[i] += p;
         zrun[i] = __builtin_fmaf(p, S.vz[tk], zrun[i]);
-        uint16_t hi, lo;
-        split_bf16(p * S.vs[tk], hi, lo);
-        S.t.ph[r][tk] = hi;
-        S.t.pl[r][tk] = lo;
+        S.t.pf[r][tk] = p * S.vs[tk];
       }
     }
     __syncthreads();                              // p s_V rows are complete
     // O += (p s_V) V: A = rows of p s_V (tokens 32 ks + kq .. + 8), B = V^T
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
-      const u32x4_t ah = *reinterpret_cast<const u32x4_t*>(&S.t.ph[16 * wave + m][32 * ks + kq]);
-      const u32x4_t al = *reinterpret_cast<const u32x4_t*>(&S.t.pl[16 * wave + m][32 * ks + kq]);
+      const f32x4 p0 = *reinterpret_cast<const f32x4*>(&S.t.pf[16 * wave + m][32 * ks + kq]);
+      const f32x4 p1 = *reinterpret_cast<const f32x4*>(&S.t.pf[16 * wave + m][32 * ks + kq + 4]);
+      u32x4_t ah, al;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        uint16_t h0, l0, h1, l1;
+        split_bf16(e < 2 ? p0[2 * e] : p1[2 * e - 4], h0, l0);
+        split_bf16(e < 2 ? p0[2 * e + 1] : p1[2 * e - 3], h1, l1);
+        ah[e] = (uint32_t)h0 | ((uint32_t)h1 << 16);
+        al[e] = (uint32_t)l0 | ((uint32_t)l1 << 16);
+      }
 #pragma unroll
       for (int db = 0; db < 8; ++db) {
         const u32x4_t fb = *reinterpret_cast<const u32x4_t*>(&S.t.vt[16 * db + m][32 * ks + kq]);
