@@ -72,9 +72,11 @@ __device__ inline u32x4_t codes8_bf16(uint32_t w) {
   return o;
 }
 
+// x = hi + lo to 16 significant bits: hi = bf16(x), lo = bf16(x - hi), both
+// round to nearest even (the hardware conversion)
 __device__ inline void split_bf16(float x, uint16_t& hi, uint16_t& lo) {
-  hi = f32_to_bf16(x);
-  lo = f32_to_bf16(x - bf16_to_f32(hi));
+  hi = __builtin_bit_cast(uint16_t, (__bf16)x);
+  lo = __builtin_bit_cast(uint16_t, (__bf16)(x - bf16_to_f32(hi)));
 }
 
 __device__ inline void store_prefill_out(const PrefillAttnArgs& a, size_t o, float v) {
@@ -305,7 +307,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       x = fmaxf(x, __shfl_xor(x, 4));
       x = fmaxf(x, __shfl_xor(x, 8));
       mnew[i] = fmaxf(mrun[i], x);
-      alpha[i] = mnew[i] == kNegInf ? 1.0f : exp2f(mrun[i] - mnew[i]);
+      alpha[i] = mnew[i] == kNegInf ? 1.0f : __builtin_amdgcn_exp2f(mrun[i] - mnew[i]);
       mrun[i] = mnew[i];
       lrun[i] *= alpha[i];
       zrun[i] *= alpha[i];
@@ -320,7 +322,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int r = 16 * wave + 4 * (lane >> 4) + i;
-        const float p = sc[cb][i] == kNegInf ? 0.0f : exp2f(sc[cb][i] - mnew[i]);
+        const float p = sc[cb][i] == kNegInf ? 0.0f : __builtin_amdgcn_exp2f(sc[cb][i] - mnew[i]);
         lrun[i] += p;
         zrun[i] = __builtin_fmaf(p, S.vz[tk], zrun[i]);
         S.t.pf[r][tk] = p * S.vs[tk];
