@@ -831,6 +831,8 @@ def _prefill_oracle(gc, qb, shape, rk, rv, absorb_v=False):
     (Shape(B=1, Hq=8, Hkv=2, N=0, M=0), 150, 67),               # no windows: INT2 everywhere
     (Shape(B=1, Hq=8, Hkv=2, N=40, M=60), 0, 100),              # the whole sequence is the chunk, all window
     (Shape(B=1, Hq=8, Hkv=2, N=3, M=500), 700, 129),            # recent window longer than the chunk
+    (Shape(B=1, Hq=32, Hkv=2, N=16, M=64), 250, 37),            # 16 query heads per kv head (4 queries per block)
+    (Shape(B=3, Hq=8, Hkv=2, N=16, M=64, outliers="percent", dist="student_t3"), 1000, 300),  # heavy tails
 ])
 def test_prefill_attn_vs_oracle(ok, shape, T0, n):
     """Chunked-prefill attention through the C ABI against the oracle over the
@@ -917,3 +919,27 @@ def test_prefill_attn_rejects(ok):
     with pytest.raises(ok.OscarError):
         gw.prefill_attn(0, qw, ow)
     gw.close()
+
+
+def test_prefill_attn_after_decode_steps(ok):
+    """A cache filled in several chunks and single-token decode steps (the
+    recent ring wrapped several times), then one more chunk: its queries
+    against the oracle over the identical cache."""
+    shape = Shape(B=2, Hq=8, Hkv=2, N=16, M=64)
+    say("[prefill attention] after decode steps")
+    rk, rv = make_rotations(shape, "haar")
+    T = 700
+    k, v, mask = inputs(shape, T)
+    gc = gpu_cache(ok, shape, rk, rv, T + 8)
+    gc.append(0, dev(k[:, :300]), dev(v[:, :300]))
+    for t in range(300, 340):
+        _step(ok, gc, 0, k[:, t:t + 1], v[:, t:t + 1], query(shape, mask, step=t))
+    gc.append(0, dev(k[:, 340:500]), dev(v[:, 340:500]))
+    gc.append(0, dev(k[:, 500:]), dev(v[:, 500:]))
+    qb = _prefill_q(shape, mask, T - 500, step0=7)
+    got = _prefill_gpu(gc, qb)
+    want = _prefill_oracle(gc, qb, shape, rk, rv)
+    e = rel_l2(got, want)
+    say(f"  rel L2 {e:.3e}")
+    assert e <= ATTN_TOL
+    gc.close()
