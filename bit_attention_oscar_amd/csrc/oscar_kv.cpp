@@ -601,8 +601,8 @@ int launch_decode(oscar_kv* kv, int32_t layer, const void* q, void* out, int32_t
     da.win_blocks = w.splits;
     da.ring0 = M > 0 ? w.a1 % M : 0;
     // (8 query heads per kv head: the append blocks' slots also go to INT2
-    // splits, measured 845 against 812 tokens/s at the 128k shape; at 4 heads
-    // that costs 9% at the 32k shape)
+    // splits, measured 831 against 815 tokens/s at the 128k shape, alternating
+    // runs on one box; at 4 heads that costs 9% at the 32k shape)
     da.int2_lead = std::max(0, std::min(p.splits, kv->resident / std::max(1, BH) - (da.G == 2 ? 0 : da.app_blocks)));
     da.split_ramp = p.splits > 1 ? kSplitRamp : 0.0f;
     ca.nslots = p.splits + w.splits;
