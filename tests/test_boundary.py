@@ -69,6 +69,8 @@ def test_null_arguments(ok):
     assert lib.oscar_kv_set_num_splits(None, 1) == ok.OSCAR_ERR_INVALID_ARG
     assert lib.oscar_kv_export(None, 0, 0, None, None, None, None) == ok.OSCAR_ERR_INVALID_ARG
     assert lib.oscar_kv_profile_enable(None, 1) == ok.OSCAR_ERR_INVALID_ARG
+    assert lib.oscar_prefill_attn(None, 0, None, None, 0, 1, 1, 0.0, None) == ok.OSCAR_ERR_INVALID_ARG
+    assert lib.oscar_kv_decode_step(None, 0, None, None, None, None, 0, 1, 0.0, None) == ok.OSCAR_ERR_INVALID_ARG
 
 
 @pytest.mark.parametrize("rows,D,G,clip,code", [
