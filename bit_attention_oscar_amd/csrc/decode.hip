@@ -400,8 +400,9 @@ __device__ inline void store_out(const CombineArgs& a, size_t o, float v) {
 
 // CC > 1: the block computes output columns [cc D / CC, (cc + 1) D / CC) only
 // (it still merges every dim of o', which the un-rotation reduces over).
+// Query heads [h_begin, h_end) of the kv head (all of them by default).
 template <int D, bool COHERENT = false, int CC = 1>
-__device__ void combine_group(const CombineArgs& a, int bh, int cc = 0) {
+__device__ void combine_group(const CombineArgs& a, int bh, int cc = 0, int h_begin = 0, int h_end = -1) {
   constexpr int NC = D / CC;          // output columns of the block
   constexpr int PER = NC / 64;
   constexpr int EW = D / 4;
@@ -414,8 +415,9 @@ __device__ void combine_group(const CombineArgs& a, int bh, int cc = 0) {
   __shared__ float linv[4];
   __shared__ float os[4][D];
   __shared__ float part[4][4][NC];
-  for (int hc = 0; hc < Gq; hc += 4) {
-    const int nh = min(4, Gq - hc);
+  if (h_end < 0) h_end = Gq;
+  for (int hc = h_begin; hc < h_end; hc += 4) {
+    const int nh = min(4, h_end - hc);
     // split weights: wave j handles head j; every (m, l) pair of a lane is
     // loaded in one round trip (at most kMaxSplits / 64 slots per lane)
     if (wave < nh) {
@@ -508,10 +510,14 @@ __device__ void combine_group(const CombineArgs& a, int bh, int cc = 0) {
   }
 }
 
-// Grid: (sequence x kv head, CC column chunks of the output).
-template <int D, int CC>
+// Grid: (sequence x kv head, CC column chunks of the output, query-head
+// blocks of HB heads).  At head_dim 512 one head per block: a merge is a few
+// dependent memory round trips long, and more, smaller blocks fill more of the
+// compute units.
+template <int D, int CC, int HB>
 __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
-  combine_group<D, false, CC>(a, (int)blockIdx.x, (int)blockIdx.y);
+  const int h0 = (int)blockIdx.z * HB;
+  combine_group<D, false, CC>(a, (int)blockIdx.x, (int)blockIdx.y, h0, min(h0 + HB, a.Hq / a.Hkv));
 }
 
 // Partial results of the matrix-core launch are written with device-scope
@@ -2209,9 +2215,10 @@ hipError_t launch_decode_wide(const DecodeArgs& a, int B, hipStream_t s) {
 
 hipError_t launch_combine(const CombineArgs& a, hipStream_t s) {
   if (a.D == 128)
-    hipLaunchKernelGGL((combine_kernel<128, 1>), dim3((unsigned)(a.B * a.Hkv)), dim3(256), 0, s, a);
+    hipLaunchKernelGGL((combine_kernel<128, 1, kMaxGq>), dim3((unsigned)(a.B * a.Hkv)), dim3(256), 0, s, a);
   else
-    hipLaunchKernelGGL((combine_kernel<512, 4>), dim3((unsigned)(a.B * a.Hkv), 4), dim3(256), 0, s, a);
+    hipLaunchKernelGGL((combine_kernel<512, 4, 1>), dim3((unsigned)(a.B * a.Hkv), 4, (unsigned)(a.Hq / a.Hkv)),
+                       dim3(256), 0, s, a);
   return hipGetLastError();
 }
 
