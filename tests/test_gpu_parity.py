@@ -943,3 +943,56 @@ def test_prefill_attn_after_decode_steps(ok):
     say(f"  rel L2 {e:.3e}")
     assert e <= ATTN_TOL
     gc.close()
+
+
+@pytest.mark.parametrize("shape,impl", [
+    (Shape(B=2, Hq=8, Hkv=2, N=16, M=64), 0),                   # matrix-core kernel, 4 heads per kv head
+    (Shape(B=1, Hq=16, Hkv=2, N=16, M=64), 0),                  # 8 heads per kv head
+    (Shape(B=2, Hq=8, Hkv=2, N=16, M=64), 1),                   # VALU kernel
+    (Shape(B=1, Hq=4, Hkv=2, D=512, N=16, M=64), 0),            # head_dim 512
+    (Shape(B=1, Hq=4, Hkv=2, D=512, N=16, M=64, v_dtype=1), 0), # head_dim 512, bf16 V
+])
+def test_softmax_scale_argument(ok, shape, impl):
+    """A caller-given softmax scale (not 1/sqrt(D)) reaches every kernel: the
+    fused step, the attention call and (head_dim 128) prefill attention,
+    against the oracle with the same scale over the identical cache."""
+    say(f"[softmax scale] {shape} impl={impl}")
+    rk, rv = make_rotations(shape, "haar")
+    T, sc = 700, 0.031
+    k, v, mask = inputs(shape, T)
+    gc = gpu_cache(ok, shape, rk, rv, T + 4)
+    gc.append(0, dev(k[:, :T - 1]), dev(v[:, :T - 1]))
+    qb = query(shape, mask)
+    B, Hq, D = qb.shape
+    out = torch.zeros((B, Hq, D), dtype=torch.float32, device="cuda")
+    gc.set_decode_impl(impl)
+    gc.decode_step(0, dev(k[:, T - 1:T]), dev(v[:, T - 1:T]), dev(qb), out, 0, sc)
+    torch.cuda.synchronize()
+    got_step = out.cpu().numpy()
+    out.zero_()
+    gc.decode_attn(0, dev(qb), out, 0, sc)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy()
+    T1 = gc.length(0)
+    kp = planes_from_export(gc.export(0, 0), T1, shape.N, shape.M)
+    vp = planes_from_export(gc.export(0, 1), T1, shape.N, shape.M)
+    want = orc.decode_attention(qb, kp, vp, rk[0], rv[0], shape.Hkv, shape.N, shape.M, 128,
+                                shape.k_dtype, shape.v_dtype, scale=sc)
+    default = orc.decode_attention(qb, kp, vp, rk[0], rv[0], shape.Hkv, shape.N, shape.M, 128,
+                                   shape.k_dtype, shape.v_dtype)
+    assert rel_l2(default, want) > 1e-2                 # the scale matters on this input
+    for name, g in (("step", got_step), ("call", got)):
+        e = rel_l2(g, want)
+        say(f"  {name}: rel L2 {e:.3e}")
+        assert e <= ATTN_TOL
+    if D == 128:
+        qp = _prefill_q(shape, mask, 20)
+        outp = torch.zeros((B, 20, Hq, D), dtype=torch.float32, device="cuda")
+        gc.prefill_attn(0, dev(qp), outp, 0, sc)
+        torch.cuda.synchronize()
+        wantp = orc.prefill_attention(qp, kp, vp, rk[0], rv[0], shape.Hkv, shape.N, shape.M, 128,
+                                      shape.k_dtype, shape.v_dtype, scale=sc)
+        e = rel_l2(outp.cpu().numpy(), wantp)
+        say(f"  prefill: rel L2 {e:.3e}")
+        assert e <= ATTN_TOL
+    gc.close()
