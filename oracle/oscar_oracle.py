@@ -1,5 +1,7 @@
 """Plain CPU oracle for OSCAR's serving-time KV path: append (rotate, clip, INT2
-quantize, pack) and decode attention over the mixed INT2 + BF16 cache.
+quantize, pack), decode attention and chunked-prefill attention over the mixed
+INT2 + BF16 cache, and the rotation variants (in-quant Hadamard, absorbed V
+rotation).
 
 TEST INFRASTRUCTURE ONLY.  Only the test suite, the package smoke check and the
 benchmark's CPU-baseline leg may import or run this module.  It shares no code
@@ -31,7 +33,11 @@ Readings taken where the pages are silent (each is listed in the design notes):
     [lo, hi] with fp16 scale s = (hi - lo)/3 and fp16 zero z = lo; codes use
     the stored fp16 values; ties round to even; s16 == 0 gives all-zero codes;
   * -0.0 is canonicalised to +0.0 before min/max and before the bf16 window;
-  * 2-bit codes packed little-endian, 4 per byte, in head_dim order.
+  * 2-bit codes packed little-endian, 4 per byte, in head_dim order;
+  * prefill attention: the queries of the last n cached positions attend
+    causally over the cache as it stands (windows of the current length);
+  * in-quant Hadamard: fp32(R @ H), H the orthonormal Sylvester Walsh-Hadamard
+    matrix of order 128 on each 128-group.
 Parity status of every function is in the function docstring ("pinned by").
 """
 from __future__ import annotations
