@@ -328,7 +328,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         S.t.pf[r][tk] = p * S.vs[tk];
       }
     }
-    __syncthreads();                              // p s_V rows are complete
+    // each wave reads back only the rows of p s_V it wrote: its shared-memory
+    // operations complete in issue order, so no block barrier is needed
+    __builtin_amdgcn_wave_barrier();
     // O += (p s_V) V: A = rows of p s_V (tokens 32 ks + kq .. + 8), B = V^T
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
