@@ -147,6 +147,10 @@ int oscar_int2_decode_attn(oscar_kv* kv, int32_t layer, const void* q, void* out
  * 512 (matrix-core path) the append runs in the same launch as the q
  * rotation, before the attention launch.  Other shapes run the two calls'
  * launches in turn. */
+int oscar_kv_decode_step(oscar_kv* kv, int32_t layer, const void* k, const void* v, const void* q,
+                         void* out, int32_t out_dtype, int32_t batch, float softmax_scale,
+                         hipStream_t stream);
+
 /* Chunked-prefill attention over the mixed cache (RotationZoo "How to use":
  * the serving host runs a prefill backend beside the decode one).  The n_q
  * queries are those of the last n_q cached positions of `layer` (normally the
@@ -165,10 +169,6 @@ int oscar_int2_decode_attn(oscar_kv* kv, int32_t layer, const void* q, void* out
  * batch), UNSUPPORTED, HIP. */
 int oscar_prefill_attn(oscar_kv* kv, int32_t layer, const void* q, void* out, int32_t out_dtype,
                        int32_t batch, int32_t n_q, float softmax_scale, hipStream_t stream);
-
-int oscar_kv_decode_step(oscar_kv* kv, int32_t layer, const void* k, const void* v, const void* q,
-                         void* out, int32_t out_dtype, int32_t batch, float softmax_scale,
-                         hipStream_t stream);
 
 /* Free every device allocation of the handle.  destroy(NULL) is OK. */
 int oscar_kv_destroy(oscar_kv* kv);
