@@ -793,6 +793,13 @@ def test_in_quant_hadamard(ok, shape):
     e2e = rel_l2(got, oc.attend(0, qb))
     say(f"  end to end vs the oracle's own cache: rel L2 {e2e:.3e}")
     assert e2e <= 1e-2
+    if D == 128:                      # chunked-prefill attention reads the same rotations
+        qp = _prefill_q(shape, mask, 50)
+        gotp = _prefill_gpu(gc, qp)
+        wantp = _prefill_oracle(gc, qp, shape, rkh, rvh)
+        e = rel_l2(gotp, wantp)
+        say(f"  prefill attention: rel L2 {e:.3e}")
+        assert e <= ATTN_TOL
     gc.close()
 
 
