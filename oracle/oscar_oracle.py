@@ -393,7 +393,8 @@ def decode_attention(q_bits: np.ndarray, kp: OracleLayerPlanes, vp: OracleLayerP
 def prefill_attention(q_bits: np.ndarray, kp: OracleLayerPlanes, vp: OracleLayerPlanes,
                       rot_k: np.ndarray, rot_v: np.ndarray, num_kv_heads: int, N: int, M: int,
                       group: int, k_dtype: int, v_dtype: int,
-                      scale: float | None = None, absorb_v: bool = False) -> np.ndarray:
+                      scale: float | None = None, absorb_v: bool = False,
+                      query_ids=None) -> np.ndarray:
     """Chunked-prefill attention over the mixed cache ([RotationZoo] "How to
     use": the serving host runs a separate prefill backend beside the decode
     one).  q bf16 bits [B, n, Hq, D] are the queries of the last n cached
@@ -408,7 +409,8 @@ def prefill_attention(q_bits: np.ndarray, kp: OracleLayerPlanes, vp: OracleLayer
         o'    = softmax(scale * K_hat[:p+1] q_rot) V_hat[:p+1]
         o     = o' @ R_V^T                   (o' itself with absorb_v)
 
-    Returns float64 [B, n, Hq, D].
+    Returns float64 [B, n, Hq, D], or [B, len(query_ids), Hq, D] for the listed
+    query indices only (the same arithmetic for each listed query).
     Pinned by: n = 1 equal to decode_attention, an all-window cache with
     R = I equal to a library attention routine under an explicit causal mask,
     and brute-force loops on tiny shapes.
@@ -420,17 +422,19 @@ def prefill_attention(q_bits: np.ndarray, kp: OracleLayerPlanes, vp: OracleLayer
     assert 0 < n <= T, "the queries are the last n of the T cached positions"
     if scale is None or scale <= 0:
         scale = 1.0 / math.sqrt(D)
-    qr = rotate_f64(q_bits, rot_k)                       # [B, n, Hq, D]
+    ids = list(range(n)) if query_ids is None else [int(i) for i in query_ids]
+    assert all(0 <= i < n for i in ids)
+    qr = rotate_f64(q_bits[:, ids], rot_k)               # [B, len(ids), Hq, D]
     Rv = np.asarray(rot_v, np.float32).astype(np.float64)
-    out = np.zeros((B, n, Hq, D), dtype=np.float64)
+    out = np.zeros((B, len(ids), Hq, D), dtype=np.float64)
     for b in range(B):
         for h in range(num_kv_heads):
             Kh = mixed_values(kp, b, h, T, N, M, group, k_dtype)
             Vh = mixed_values(vp, b, h, T, N, M, group, v_dtype)
-            for i in range(n):
+            for r, i in enumerate(ids):
                 p = T - n + i
                 for j in range(h * Gq, (h + 1) * Gq):
-                    out[b, i, j] = softmax_attention_f64(qr[b, i, j], Kh[:p + 1], Vh[:p + 1], scale)
+                    out[b, r, j] = softmax_attention_f64(qr[b, r, j], Kh[:p + 1], Vh[:p + 1], scale)
     return out if absorb_v else out @ Rv.T
 
 

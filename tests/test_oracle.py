@@ -551,3 +551,13 @@ def test_prefill_attention_brute_force_tiny():
     for i in range(n):
         want = _brute_attention(qb[:, i], k, v, rk[0], rv[0], Hkv, N, M, 128, 0.96, 0.92, ntok=T - n + i + 1)
         np.testing.assert_allclose(got[:, i], want, rtol=1e-9, atol=1e-9)
+
+
+def test_prefill_attention_query_subset():
+    """Listed queries only: the same values as the full computation's rows."""
+    T, n, Hq, Hkv, D, N, M = 40, 9, 4, 2, 128, 3, 7
+    c, _, k, v, rk, rv = _mk_cache(T, Hq, Hkv, D, N=N, M=M, batch=2, seed=31)
+    qb = _prefill_queries(2, n, Hq, Hkv, D, 31)
+    full = orc.prefill_attention(qb, c.k[0], c.v[0], rk[0], rv[0], Hkv, N, M, 128, 0, 0)
+    sub = orc.prefill_attention(qb, c.k[0], c.v[0], rk[0], rv[0], Hkv, N, M, 128, 0, 0, query_ids=[8, 0, 4])
+    np.testing.assert_array_equal(sub, full[:, [8, 0, 4]])
