@@ -611,6 +611,33 @@ def test_prefill_chunk_full_size(ok, D, B, vdt):
 
 
 @pytest.mark.slow
+def test_prefill_attn_full_size_16k_sampled(ok):
+    """Chunked-prefill attention in the benchmark's configuration: 4096 queries
+    of the last 4096 positions at the 16k batch-1 shape (Hq=32, Hkv=8, sink
+    512, recent 2048); the first, middle and last queries of the chunk, every
+    head, against the oracle over the exported cache."""
+    from bench import fill_layer_device
+    shape = Shape(B=1, Hq=32, Hkv=8, D=128, N=512, M=2048, outliers="percent")
+    T, n = 16384, 4096
+    say("[full prefill attention 16k] filling")
+    rk, rv = make_rotations(shape, "haar")
+    gc = gpu_cache(ok, shape, rk, rv, T + 64)
+    fill_layer_device(gc, 0, shape.B, shape.Hkv, shape.D, T, seed=0, dist="normal", outliers="percent")
+    mask = synth.outlier_mask(shape.D, shape.Hkv, 0, 0, "percent")
+    qb = _prefill_q(shape, mask, n)
+    got = _prefill_gpu(gc, qb)
+    ids = [0, 1, n // 2, n - 2, n - 1]
+    kp = planes_from_export(gc.export(0, 0), T, shape.N, shape.M)
+    vp = planes_from_export(gc.export(0, 1), T, shape.N, shape.M)
+    want = orc.prefill_attention(qb, kp, vp, rk[0], rv[0], shape.Hkv, shape.N, shape.M, 128, 0, 0,
+                                 query_ids=ids)
+    e = rel_l2(got[:, ids], want)
+    say(f"  sampled queries {ids}: rel L2 {e:.3e}")
+    assert e <= ATTN_TOL
+    gc.close()
+
+
+@pytest.mark.slow
 def test_full_size_128k_gqa8_sampled(ok):
     """The 128k-context GQA-8 shape (B=8, Hq=64, Hkv=8, D=128, N=64, M=256,
     Student-t(3) values) on one layer, filled on the device, one fused step
