@@ -866,6 +866,8 @@ def _prefill_oracle(gc, qb, shape, rk, rv, absorb_v=False):
     (Shape(B=1, Hq=8, Hkv=2, N=40, M=60), 0, 100),              # the whole sequence is the chunk, all window
     (Shape(B=1, Hq=8, Hkv=2, N=3, M=500), 700, 129),            # recent window longer than the chunk
     (Shape(B=1, Hq=32, Hkv=2, N=16, M=64), 250, 37),            # 16 query heads per kv head (4 queries per block)
+    (Shape(B=1, Hq=8, Hkv=2, N=16, M=64, k_dtype=1), 300, 90),  # bf16 K plane, INT2 V
+    (Shape(B=1, Hq=8, Hkv=2, N=16, M=64, k_dtype=1, v_dtype=1), 300, 90),  # both planes bf16
     (Shape(B=3, Hq=8, Hkv=2, N=16, M=64, outliers="percent", dist="student_t3"), 1000, 300),  # heavy tails
 ])
 def test_prefill_attn_vs_oracle(ok, shape, T0, n):
