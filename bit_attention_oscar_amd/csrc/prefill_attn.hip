@@ -29,6 +29,8 @@
 #include "append_impl.h"
 #include "prefill_attn.h"
 
+#include <type_traits>
+
 namespace oscar {
 
 namespace {
@@ -155,6 +157,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   for (int i = 0; i < 4; ++i) prow[i] = T - a.n + row_query(a, i0, 16 * wave + 4 * (lane >> 4) + i);
   const int p_max = T - a.n + min(i0 + QB - 1, a.n - 1);
   const int ntiles = (p_max >> 6) + 1;
+  // a tile whose last token is at or before the block's first query position
+  // needs no causal mask: every score in it is finite
+  const int p_min = T - a.n + i0;
+  // per-row q sums in registers (rows of this wave, written by this wave)
+  __builtin_amdgcn_wave_barrier();
+  float qs[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) qs[i] = S.qsum[16 * wave + 4 * (lane >> 4) + i];
   float mrun[4], lrun[4], zrun[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
@@ -283,51 +293,60 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       }
     }
     // scores, mask, online softmax
-    float sc[4][4];
-    float tmax[4];
+    auto softmax_tile = [&](auto masked_c) {
+      constexpr bool kMasked = decltype(masked_c)::value;
+      float sc[4][4];
+      float tmax[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) tmax[i] = kNegInf;
+      for (int i = 0; i < 4; ++i) tmax[i] = kNegInf;
 #pragma unroll
-    for (int cb = 0; cb < 4; ++cb) {
-      const int tk = 16 * cb + m, t = t0 + tk;
+      for (int cb = 0; cb < 4; ++cb) {
+        const int tk = 16 * cb + m, t = t0 + tk;
+        const float sk = S.ks[tk], zk = S.kz[tk];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float v = __builtin_fmaf(sk, sacc[cb][i], zk * qs[i]);
+          sc[cb][i] = (!kMasked || t <= prow[i]) ? v : kNegInf;
+          tmax[i] = fmaxf(tmax[i], sc[cb][i]);
+        }
+      }
+      float alpha[4], mnew[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int r = 16 * wave + 4 * (lane >> 4) + i;
-        const float v = __builtin_fmaf(S.ks[tk], sacc[cb][i], S.kz[tk] * S.qsum[r]);
-        sc[cb][i] = t <= prow[i] ? v : kNegInf;
-        tmax[i] = fmaxf(tmax[i], sc[cb][i]);
+        float x = tmax[i];
+        x = fmaxf(x, __shfl_xor(x, 1));
+        x = fmaxf(x, __shfl_xor(x, 2));
+        x = fmaxf(x, __shfl_xor(x, 4));
+        x = fmaxf(x, __shfl_xor(x, 8));
+        mnew[i] = fmaxf(mrun[i], x);
+        // unmasked: mnew is finite, and exp2(-inf) = 0 covers a first tile
+        alpha[i] = (kMasked && mnew[i] == kNegInf) ? 1.0f : __builtin_amdgcn_exp2f(mrun[i] - mnew[i]);
+        mrun[i] = mnew[i];
+        lrun[i] *= alpha[i];
+        zrun[i] *= alpha[i];
       }
-    }
-    float alpha[4], mnew[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      float x = tmax[i];
-      x = fmaxf(x, __shfl_xor(x, 1));
-      x = fmaxf(x, __shfl_xor(x, 2));
-      x = fmaxf(x, __shfl_xor(x, 4));
-      x = fmaxf(x, __shfl_xor(x, 8));
-      mnew[i] = fmaxf(mrun[i], x);
-      alpha[i] = mnew[i] == kNegInf ? 1.0f : __builtin_amdgcn_exp2f(mrun[i] - mnew[i]);
-      mrun[i] = mnew[i];
-      lrun[i] *= alpha[i];
-      zrun[i] *= alpha[i];
-    }
+      for (int db = 0; db < 8; ++db)
 #pragma unroll
-    for (int db = 0; db < 8; ++db)
+        for (int i = 0; i < 4; ++i) oacc[db][i] *= alpha[i];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) oacc[db][i] *= alpha[i];
+      for (int cb = 0; cb < 4; ++cb) {
+        const int tk = 16 * cb + m;
+        const float sv = S.vs[tk], zv = S.vz[tk];
 #pragma unroll
-    for (int cb = 0; cb < 4; ++cb) {
-      const int tk = 16 * cb + m;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int r = 16 * wave + 4 * (lane >> 4) + i;
-        const float p = sc[cb][i] == kNegInf ? 0.0f : __builtin_amdgcn_exp2f(sc[cb][i] - mnew[i]);
-        lrun[i] += p;
-        zrun[i] = __builtin_fmaf(p, S.vz[tk], zrun[i]);
-        S.t.pf[r][tk] = p * S.vs[tk];
+        for (int i = 0; i < 4; ++i) {
+          const int r = 16 * wave + 4 * (lane >> 4) + i;
+          const float p = (kMasked && sc[cb][i] == kNegInf) ? 0.0f : __builtin_amdgcn_exp2f(sc[cb][i] - mnew[i]);
+          lrun[i] += p;
+          zrun[i] = __builtin_fmaf(p, zv, zrun[i]);
+          S.t.pf[r][tk] = p * sv;
+        }
       }
-    }
+    };
+    if (t0 + 63 <= p_min)
+      softmax_tile(std::integral_constant<bool, false>{});
+    else
+      softmax_tile(std::integral_constant<bool, true>{});
     // each wave reads back only the rows of p s_V it wrote: its shared-memory
     // operations complete in issue order, so no block barrier is needed
     __builtin_amdgcn_wave_barrier();
