@@ -869,6 +869,11 @@ def _prefill_oracle(gc, qb, shape, rk, rv, absorb_v=False):
     (Shape(B=1, Hq=8, Hkv=2, N=16, M=64, k_dtype=1), 300, 90),  # bf16 K plane, INT2 V
     (Shape(B=1, Hq=8, Hkv=2, N=16, M=64, k_dtype=1, v_dtype=1), 300, 90),  # both planes bf16
     (Shape(B=3, Hq=8, Hkv=2, N=16, M=64, outliers="percent", dist="student_t3"), 1000, 300),  # heavy tails
+    # key tiles that end at or before a block's first query position skip the
+    # causal compare: the first block's first query sits at the edge of tile 0
+    (Shape(B=1, Hq=8, Hkv=2, N=16, M=64), 63, 80),              # at position 63: tile 0 unmasked, exactly full
+    (Shape(B=1, Hq=8, Hkv=2, N=16, M=64), 62, 81),              # at position 62: tile 0 still masked
+    (Shape(B=2, Hq=2, Hkv=2, N=0, M=0), 127, 64),               # 1 head, at position 127: two unmasked INT2 tiles first
 ])
 def test_prefill_attn_vs_oracle(ok, shape, T0, n):
     """Chunked-prefill attention through the C ABI against the oracle over the
