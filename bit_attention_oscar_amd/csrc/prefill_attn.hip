@@ -278,7 +278,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     }
     __syncthreads();
 
-    // S = q K^T for the wave's 16 rows and the tile's 64 tokens
+    // S = q K^T for the wave's 16 rows and the tile's 64 tokens.  A wave
+    // issuing matrix-core work runs at raised priority, so the other block's
+    // waves fill the gaps with their softmax and code conversion
+    __builtin_amdgcn_s_setprio(1);
     f32x4 sacc[4];
 #pragma unroll
     for (int cb = 0; cb < 4; ++cb) {
@@ -292,6 +295,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
                                                            __builtin_bit_cast(bf16x8_t, fb), sacc[cb], 0, 0, 0);
       }
     }
+    __builtin_amdgcn_s_setprio(0);
     // scores, mask, online softmax
     auto softmax_tile = [&](auto masked_c) {
       constexpr bool kMasked = decltype(masked_c)::value;
@@ -350,6 +354,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     // each wave reads back only the rows of p s_V it wrote: its shared-memory
     // operations complete in issue order, so no block barrier is needed
     __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_s_setprio(1);
     // O += (p s_V) V: A = rows of p s_V (tokens 32 ks + kq .. + 8), B = V^T
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
@@ -373,6 +378,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
                                                            __builtin_bit_cast(bf16x8_t, fb), oacc[db], 0, 0, 0);
       }
     }
+    __builtin_amdgcn_s_setprio(0);
   }
 
   // ---- o' = (O + sum p z_V) / l, then o = o' R_V^T
