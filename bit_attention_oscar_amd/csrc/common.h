@@ -10,7 +10,8 @@ namespace oscar {
 constexpr int kGroup = 128;           // quantization group along head_dim
 constexpr int kTile = 64;             // tokens per decode tile / V storage block
 constexpr int kMaxSplits = 256;       // partial-result slots per (sequence, head)
-constexpr int kQPub = 4 * 128 + 8 + 256;  // published q of 4 query heads: fp32 q, sums, exponents, fp16 operands
+constexpr int kQPub = 4 * 128 + 8 + 512;  // published q of 4 query heads: fp32 q, sums, exponents,
+                                          // two-piece fp16 operands
 constexpr int kMaxGq = 16;            // query heads per kv head handled by the VALU kernel
 
 // ---------------------------------------------------------------------------
@@ -156,6 +157,7 @@ struct DecodeArgs {
   unsigned* qflag;         // [B*Hkv]: epoch of the launch whose q qpub holds
   unsigned epoch;          // this launch's number (never 0)
   unsigned qwait_ticks;    // longest wait for the published q, in wall-clock ticks
+  int q_self;              // 1: no block waits for the published q (each rotates it itself)
   float* partials;         // [B][Hq][kMaxSplits][D+2]
   int Hq, Hkv, D, cap, N, M, T;
   int Gq, G;               // query heads per kv head; head groups of 4 (matrix-core kernel)

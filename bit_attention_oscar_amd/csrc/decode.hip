@@ -340,12 +340,32 @@ __device__ inline void split_codes(uint32_t w, uint32_t c[8]) {
 __device__ inline float lo_half(uint32_t m) { return (float)__builtin_bit_cast(_Float16, (uint16_t)(m & 0xFFFFu)); }
 __device__ inline float hi_half(uint32_t m) { return (float)__builtin_bit_cast(_Float16, (uint16_t)(m >> 16)); }
 
+// Two-piece fp16 operands.  A value x that enters a product as fp16 is
+// carried as hi = fp16(x) and lo = fp16(x - hi) (x - hi is exact in fp32), so
+// the operand keeps 22 significant bits instead of 11; both pieces multiply
+// the same exact code operand and accumulate into the same fp32 chain.  With
+// one fp16 piece the scores of large-magnitude q (outlier channels) carry an
+// absolute error proportional to their size, which the softmax exponentiates.
+__device__ inline void split_f16(float x, _Float16& hi, _Float16& lo) {
+  hi = (_Float16)x;
+  lo = (_Float16)(x - (float)hi);
+}
+
 // Word w of a lane's K codes against the q operands of every head group: the
-// codes are unpacked once, each group has its own accumulation chain.
+// codes are unpacked once, each group has its own accumulation chain, which
+// takes the high pieces (registers) and then the low pieces (read from the
+// block's shared copy, qlo[g] = this lane's 8 words of group g).
 template <int G>
-__device__ inline void qk_word(uint32_t word, const h4 (&q)[G][8], int w, f4 (&s)[G]) {
+__device__ inline void qk_word(uint32_t word, const h4 (&q)[G][8], const uint2* const (&qlo)[G], int w,
+                               f4 (&s)[G]) {
   uint32_t c[8];
   split_codes(word, c);
+  h4 ql[G];
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    const uint2 u = qlo[g][w];
+    ql[g] = as_h4(u.x, u.y);
+  }
 #pragma unroll
   for (int g = 0; g < G; ++g) s[g] = __builtin_amdgcn_mfma_f32_4x4x4f16(as_h4(c[0], c[1]), q[g][w], s[g], 0, 0, 4);
 #pragma unroll
@@ -354,10 +374,20 @@ __device__ inline void qk_word(uint32_t word, const h4 (&q)[G][8], int w, f4 (&s
   for (int g = 0; g < G; ++g) s[g] = __builtin_amdgcn_mfma_f32_4x4x4f16(as_h4(c[4], c[5]), q[g][w], s[g], 0, 0, 6);
 #pragma unroll
   for (int g = 0; g < G; ++g) s[g] = __builtin_amdgcn_mfma_f32_4x4x4f16(as_h4(c[6], c[7]), q[g][w], s[g], 0, 0, 7);
+#pragma unroll
+  for (int g = 0; g < G; ++g) s[g] = __builtin_amdgcn_mfma_f32_4x4x4f16(as_h4(c[0], c[1]), ql[g], s[g], 0, 0, 4);
+#pragma unroll
+  for (int g = 0; g < G; ++g) s[g] = __builtin_amdgcn_mfma_f32_4x4x4f16(as_h4(c[2], c[3]), ql[g], s[g], 0, 0, 5);
+#pragma unroll
+  for (int g = 0; g < G; ++g) s[g] = __builtin_amdgcn_mfma_f32_4x4x4f16(as_h4(c[4], c[5]), ql[g], s[g], 0, 0, 6);
+#pragma unroll
+  for (int g = 0; g < G; ++g) s[g] = __builtin_amdgcn_mfma_f32_4x4x4f16(as_h4(c[6], c[7]), ql[g], s[g], 0, 0, 7);
 }
 
+// PV for word W of a lane's V record with the two-piece weights p (high) and
+// pl (low) of every head group.
 template <int G, int W>
-__device__ inline void pv_word(uint32_t word, const h4 (&p)[G], f4 (&o0)[G], f4 (&o1)[G]) {
+__device__ inline void pv_word(uint32_t word, const h4 (&p)[G], const h4 (&pl)[G], f4 (&o0)[G], f4 (&o1)[G]) {
   uint32_t c[8];
   split_codes(word, c);
   // word W holds tokens 8W..8W+7 = blocks beta 2W (pairs 0,1) and 2W+1 (pairs 2,3);
@@ -371,6 +401,28 @@ __device__ inline void pv_word(uint32_t word, const h4 (&p)[G], f4 (&o0)[G], f4 
   for (int g = 0; g < G; ++g) {
     o0[g] = __builtin_amdgcn_mfma_f32_4x4x4f16(p[g], as_h4(c[2], c[3]), o0[g], 4, 2 * W + 1, 0);
     o1[g] = __builtin_amdgcn_mfma_f32_4x4x4f16(p[g], as_h4(c[6], c[7]), o1[g], 4, 2 * W + 1, 0);
+  }
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    o0[g] = __builtin_amdgcn_mfma_f32_4x4x4f16(pl[g], as_h4(c[0], c[1]), o0[g], 4, 2 * W, 0);
+    o1[g] = __builtin_amdgcn_mfma_f32_4x4x4f16(pl[g], as_h4(c[4], c[5]), o1[g], 4, 2 * W, 0);
+  }
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    o0[g] = __builtin_amdgcn_mfma_f32_4x4x4f16(pl[g], as_h4(c[2], c[3]), o0[g], 4, 2 * W + 1, 0);
+    o1[g] = __builtin_amdgcn_mfma_f32_4x4x4f16(pl[g], as_h4(c[6], c[7]), o1[g], 4, 2 * W + 1, 0);
+  }
+}
+
+// The softmax weights of four tokens as two-piece PV operands: s_V * p' with
+// one fp32 rounding (the fp16 scale read in place), split into hi and lo.
+__device__ inline void pv_operands(const uint32_t (&vmr)[4], const float (&p)[4], h4& hi, h4& lo) {
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    _Float16 h, l;
+    split_f16(__builtin_fmaf(lo_half(vmr[r]), p[r], 0.0f), h, l);
+    hi[r] = h;
+    lo[r] = l;
   }
 }
 
@@ -601,6 +653,8 @@ struct FusedSmem {
   int qeq[4];                  // per-head exponent of the fp16 q operand
   int ready;                   // the published q of this launch is available
   uint16_t newtok[2][128];     // bf16 window values of the token appended by this launch
+  uint32_t qlo[2][256];        // low pieces of the q operands of up to two head groups
+                               // (vector 4 pp + j at 16 (4 pp + j), as published)
   float scratch[2688];
 };
 
@@ -705,21 +759,38 @@ __device__ void block_rotate_q_chunked(const DecodeArgs& a, int b, int hq0, Fuse
   __syncthreads();
 }
 
-// fp16 matrix-core q operand: element k of word w for lane group pp of head j
-// is q_rot[d] * 2^(eq - 2 (d % 4)) with d = qk_dim(w, pp, k).
-__device__ inline _Float16 q_operand(const FusedSmem& S, int j, int pp, int w, int k) {
+// fp16 matrix-core q operand pieces: element k of word w for lane group pp of
+// head j is x = q_rot[d] * 2^(eq - 2 (d % 4)) with d = qk_dim(w, pp, k), as
+// hi = fp16(x) and lo = fp16(x - hi).
+__device__ inline void q_operand(const FusedSmem& S, int j, int pp, int w, int k, _Float16& hi, _Float16& lo) {
   const int d = qk_dim(w, pp, k);
-  return (_Float16)ldexpf(S.qs[j][d], S.qeq[j] - 2 * (d & 3));
+  split_f16(ldexpf(S.qs[j][d], S.qeq[j] - 2 * (d & 3)), hi, lo);
 }
 
 // Published q of one head group (4 query heads) of a (sequence, kv head), at
 // index (b Hkv + h) G + g, kQPub floats:
 //   [0, 512)          fp32 rotated q of the 4 heads, head-major
 //   [512, 516)        per-head sums; [516, 520) per-head exponents eq (int bits)
-//   [kQPubOps, +256)  fp16 matrix-core operands: vector 4 pp + j holds the 32
-//                     values (word w, slot k at 4 w + k) of lane group pp, head j
+//   [kQPubOps, +256)  high pieces of the fp16 matrix-core operands: vector
+//                     4 pp + j holds the 32 values (word w, slot k at 4 w + k)
+//                     of lane group pp, head j (16 words per vector)
+//   [kQPubLo, +256)   the low pieces, same order
 constexpr int kQPubOps = 520;
-static_assert(kQPubOps + 256 <= kQPub, "published q layout");
+constexpr int kQPubLo = kQPubOps + 256;
+static_assert(kQPubLo + 256 <= kQPub, "published q layout");
+
+// Word i (0 <= i < 256) of the operand vectors of the block's 4 heads, as
+// published: vector v = i / 16 = 4 pp + j, operands 2 (i % 16) and
+// 2 (i % 16) + 1 of that vector; hw packs the two high pieces, lw the two low.
+__device__ inline void q_operand_word(const FusedSmem& S, int i, uint32_t& hw, uint32_t& lw) {
+  const int v = i >> 4, e = 2 * (i & 15);
+  const int pp = v >> 2, j = v & 3;
+  _Float16 h0, l0, h1, l1;
+  q_operand(S, j, pp, e >> 2, e & 3, h0, l0);
+  q_operand(S, j, pp, (e + 1) >> 2, (e + 1) & 3, h1, l1);
+  hw = (uint32_t)__builtin_bit_cast(uint16_t, h0) | ((uint32_t)__builtin_bit_cast(uint16_t, h1) << 16);
+  lw = (uint32_t)__builtin_bit_cast(uint16_t, l0) | ((uint32_t)__builtin_bit_cast(uint16_t, l1) << 16);
+}
 
 // The first attention block of each (sequence, kv head) rotates q and
 // publishes it for the other blocks of the launch: device-scope stores of
@@ -733,12 +804,11 @@ __device__ void publish_q(const DecodeArgs& a, int pidx, FusedSmem& S) {
     st_partial(dst + 512 + tid, S.qsum[tid]);
     st_partial(dst + 516 + tid, __int_as_float(S.qeq[tid]));
   }
-  if (tid < 256) {                      // one word (two fp16 operands) per thread
-    const int v = tid >> 4, e = 2 * (tid & 15);
-    const int pp = v >> 2, j = v & 3;
-    const uint32_t lo = __builtin_bit_cast(uint16_t, q_operand(S, j, pp, e >> 2, e & 3));
-    const uint32_t hi = __builtin_bit_cast(uint16_t, q_operand(S, j, pp, (e + 1) >> 2, (e + 1) & 3));
-    st_partial(dst + kQPubOps + tid, __uint_as_float(lo | (hi << 16)));
+  if (tid < 256) {                      // one word (two fp16 operands) of each piece per thread
+    uint32_t hw, lw;
+    q_operand_word(S, tid, hw, lw);
+    st_partial(dst + kQPubOps + tid, __uint_as_float(hw));
+    st_partial(dst + kQPubLo + tid, __uint_as_float(lw));
   }
 }
 
@@ -838,17 +908,19 @@ __device__ inline unsigned first_flag_read(const DecodeArgs& a, int bh) {
 // Bounded wait for this launch's published q: thread 0 polls the flag for at
 // most a.qwait_ticks of the constant-rate wall clock, then gives up (the block
 // rotates q itself).  The wait always ends, whatever the dispatch order.
+// With a.q_self set (a host test switch) no block waits: every block that did
+// not publish takes the path of a block whose wait ran out.
 __device__ bool wait_published_q(const DecodeArgs& a, int bh, unsigned first, FusedSmem& S) {
   if (threadIdx.x == 0) {
     unsigned f = first;
-    if (f != a.epoch) {
+    if (f != a.epoch && !a.q_self) {
       const long long t0 = wall_clock64();
       do {
         __builtin_amdgcn_s_sleep(4);
         f = __hip_atomic_load(a.qflag + bh, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       } while (f != a.epoch && wall_clock64() - t0 < (long long)a.qwait_ticks);
     }
-    S.ready = f == a.epoch;
+    S.ready = f == a.epoch && !a.q_self;
   }
   __syncthreads();
   return S.ready != 0;
@@ -1257,11 +1329,22 @@ void decode_mfma_kernel(DecodeArgs a) {
   h4 qv[G][8];
   int eq[G];
   float qsum[G];
+  // (high pieces into registers; the low pieces into the block's shared copy,
+  // word i by thread i, read back after the barrier that ends the set-up)
   auto operands_from_smem = [&](int g) {
 #pragma unroll
     for (int w = 0; w < 8; ++w)
 #pragma unroll
-      for (int k = 0; k < 4; ++k) qv[g][w][k] = q_operand(S, j, lane >> 4, w, k);
+      for (int k = 0; k < 4; ++k) {
+        _Float16 hi, lo;
+        q_operand(S, j, lane >> 4, w, k, hi, lo);
+        qv[g][w][k] = hi;
+      }
+    for (int i = threadIdx.x; i < 256; i += 64 * WPB) {
+      uint32_t hw, lw;
+      q_operand_word(S, i, hw, lw);
+      S.qlo[g][i] = lw;
+    }
     qsum[g] = S.qsum[j];
     eq[g] = S.qeq[j];
   };
@@ -1322,15 +1405,22 @@ void decode_mfma_kernel(DecodeArgs a) {
         }
         qsum[g] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(qr, (512 + j) * 4, 0, kDeviceScope));
         eq[g] = (int)__builtin_amdgcn_raw_buffer_load_b32(qr, (516 + j) * 4, 0, kDeviceScope);
+        for (int i = threadIdx.x; i < 256; i += 64 * WPB)
+          S.qlo[g][i] = __builtin_amdgcn_raw_buffer_load_b32(qr, (kQPubLo + i) * 4, 0, kDeviceScope);
       }
     } else {
 #pragma unroll
       for (int g = 0; g < G; ++g) {
+        if (g > 0) __syncthreads();        // the previous group's S.qs has been read
         block_rotate_q_chunked(a, b, hq_of(g), S);
         operands_from_smem(g);
       }
     }
   }
+  __syncthreads();                         // S.qlo complete
+  const uint2* qlp[G];
+#pragma unroll
+  for (int g = 0; g < G; ++g) qlp[g] = reinterpret_cast<const uint2*>(&S.qlo[g][16 * (4 * (lane >> 4) + j)]);
   float cK[G], zq[G];
 #pragma unroll
   for (int g = 0; g < G; ++g) {
@@ -1369,20 +1459,20 @@ void decode_mfma_kernel(DecodeArgs a) {
     f4 sc[G];
 #pragma unroll
     for (int g = 0; g < G; ++g) sc[g] = f4{0, 0, 0, 0};
-    qk_word<G>(cur.k0.x, qv, 0, sc);
-    qk_word<G>(cur.k0.y, qv, 1, sc);
-    qk_word<G>(cur.k0.z, qv, 2, sc);
-    qk_word<G>(cur.k0.w, qv, 3, sc);
-    qk_word<G>(cur.k1.x, qv, 4, sc);
-    qk_word<G>(cur.k1.y, qv, 5, sc);
-    qk_word<G>(cur.k1.z, qv, 6, sc);
-    qk_word<G>(cur.k1.w, qv, 7, sc);
+    qk_word<G>(cur.k0.x, qv, qlp, 0, sc);
+    qk_word<G>(cur.k0.y, qv, qlp, 1, sc);
+    qk_word<G>(cur.k0.z, qv, qlp, 2, sc);
+    qk_word<G>(cur.k0.w, qv, qlp, 3, sc);
+    qk_word<G>(cur.k1.x, qv, qlp, 4, sc);
+    qk_word<G>(cur.k1.y, qv, qlp, 5, sc);
+    qk_word<G>(cur.k1.z, qv, qlp, 6, sc);
+    qk_word<G>(cur.k1.w, qv, qlp, 7, sc);
     PHASE_FENCE();
 
     const uint32_t kmr[4] = {cur.km.x, cur.km.y, cur.km.z, cur.km.w};
     const uint32_t vmr[4] = {cur.vm.x, cur.vm.y, cur.vm.z, cur.vm.w};
     const bool edge = t0 < lo || t0 + 64 > hi;     // boundary tile (wave-uniform)
-    h4 pv[G];
+    h4 pv[G], pl[G];
 #pragma unroll
     for (int g = 0; g < G; ++g) {
       float u[4];
@@ -1422,21 +1512,18 @@ void decode_mfma_kernel(DecodeArgs a) {
       lB[g] += p[2] + p[3];
       pzA[g] = __builtin_fmaf(p[0], hi_half(vmr[0]), __builtin_fmaf(p[1], hi_half(vmr[1]), pzA[g]));
       pzB[g] = __builtin_fmaf(p[2], hi_half(vmr[2]), __builtin_fmaf(p[3], hi_half(vmr[3]), pzB[g]));
-      // s_V * p' as fp16 with one rounding (fp16 metadata read in place)
-      pv[g] = h4{(_Float16)__builtin_fmaf(lo_half(vmr[0]), p[0], 0.0f),
-                 (_Float16)__builtin_fmaf(lo_half(vmr[1]), p[1], 0.0f),
-                 (_Float16)__builtin_fmaf(lo_half(vmr[2]), p[2], 0.0f),
-                 (_Float16)__builtin_fmaf(lo_half(vmr[3]), p[3], 0.0f)};
+      // s_V * p' as a two-piece fp16 operand (fp16 metadata read in place)
+      pv_operands(vmr, p, pv[g], pl[g]);
     }
     PHASE_FENCE();
-    pv_word<G, 0>(cur.v0.x, pv, o0, o1);
-    pv_word<G, 1>(cur.v0.y, pv, o0, o1);
-    pv_word<G, 2>(cur.v0.z, pv, o0, o1);
-    pv_word<G, 3>(cur.v0.w, pv, o0, o1);
-    pv_word<G, 4>(cur.v1.x, pv, o0, o1);
-    pv_word<G, 5>(cur.v1.y, pv, o0, o1);
-    pv_word<G, 6>(cur.v1.z, pv, o0, o1);
-    pv_word<G, 7>(cur.v1.w, pv, o0, o1);
+    pv_word<G, 0>(cur.v0.x, pv, pl, o0, o1);
+    pv_word<G, 1>(cur.v0.y, pv, pl, o0, o1);
+    pv_word<G, 2>(cur.v0.z, pv, pl, o0, o1);
+    pv_word<G, 3>(cur.v0.w, pv, pl, o0, o1);
+    pv_word<G, 4>(cur.v1.x, pv, pl, o0, o1);
+    pv_word<G, 5>(cur.v1.y, pv, pl, o0, o1);
+    pv_word<G, 6>(cur.v1.z, pv, pl, o0, o1);
+    pv_word<G, 7>(cur.v1.w, pv, pl, o0, o1);
   };
 
   for (int ti = ti0; ti < s_t1; ti += kDepth * WPB) {
@@ -1587,7 +1674,30 @@ struct WideSmem {
   float p[4][32];              // window: softmax weights [head][token]
   float pv[4][4][64];          // bf16-V splits: [wave][head][token] softmax weights of the tile
   float wm[4], wl[4], wa[4];   // window: running max, sum, rescale factor per head
+  uint32_t qlo[4][256];        // INT2 splits: low pieces of slice w's q operands, as published
 };
+
+// q operands of one 128-dim slice record for this lane (lane group pp =
+// lane / 16, head j = lane % 4): high pieces into registers, low pieces into
+// the slice's shared copy (read back through the returned pointer after the
+// caller's barrier).  The record was written by an earlier launch.
+__device__ inline const uint2* wide_q_operands(const DecodeArgs& a, int rec, uint32_t* qlo_smem, h4 (&qv)[8],
+                                               float& qsum, int& eq) {
+  const int lane = threadIdx.x & 63, j = lane & 3;
+  const __amdgpu_buffer_rsrc_t qr = plane_rsrc(a.qpub + (size_t)rec * kQPub, kQPub * 4);
+  const int vbase = (kQPubOps + 16 * (4 * (lane >> 4) + j)) * 4;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const u4 wv = __builtin_amdgcn_raw_buffer_load_b128(qr, vbase + 16 * i, 0, 0);
+    qv[2 * i] = as_h4(wv.x, wv.y);
+    qv[2 * i + 1] = as_h4(wv.z, wv.w);
+  }
+  qsum = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(qr, (512 + j) * 4, 0, 0));
+  eq = (int)__builtin_amdgcn_raw_buffer_load_b32(qr, (516 + j) * 4, 0, 0);
+  const u4 lw = __builtin_amdgcn_raw_buffer_load_b128(qr, (kQPubLo + 4 * lane) * 4, 0, 0);
+  *reinterpret_cast<u4*>(qlo_smem + 4 * lane) = lw;
+  return reinterpret_cast<const uint2*>(qlo_smem + 16 * (4 * (lane >> 4) + j));
+}
 
 // bf16 window tokens of one (sequence, kv head) with fp32 VALU arithmetic, in
 // 32-token passes.  Window blocks take chunks of win.chunk tokens of the sink
@@ -1837,18 +1947,8 @@ __device__ void wide_split_bf16v(const DecodeArgs& a, int bh, int b, int h, int 
   h4 qv[1][8];
   float qsum;
   int eq;
-  {
-    const __amdgpu_buffer_rsrc_t qr = plane_rsrc(a.qpub + (size_t)(bh * 4 + wave) * kQPub, kQPub * 4);
-    const int vbase = (kQPubOps + 16 * (4 * (lane >> 4) + j)) * 4;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const u4 wv = __builtin_amdgcn_raw_buffer_load_b128(qr, vbase + 16 * i, 0, 0);
-      qv[0][2 * i] = as_h4(wv.x, wv.y);
-      qv[0][2 * i + 1] = as_h4(wv.z, wv.w);
-    }
-    qsum = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(qr, (512 + j) * 4, 0, 0));
-    eq = (int)__builtin_amdgcn_raw_buffer_load_b32(qr, (516 + j) * 4, 0, 0);
-  }
+  const uint2* qlp[1] = {wide_q_operands(a, bh * 4 + wave, W.qlo[wave], qv[0], qsum, eq)};
+  __syncthreads();                        // W.qlo complete
   const float cK = ldexpf(1.0f, 24 - eq);
   const float zq = ldexpf(qsum, eq - 24);
   float m = NEG_INF, l = 0.0f;
@@ -1869,14 +1969,14 @@ __device__ void wide_split_bf16v(const DecodeArgs& a, int bh, int b, int h, int 
                                                     kStreamOnce);
     }
     f4 sa[1] = {{0, 0, 0, 0}};
-    qk_word<1>(cur.k0.x, qv, 0, sa);
-    qk_word<1>(cur.k0.y, qv, 1, sa);
-    qk_word<1>(cur.k0.z, qv, 2, sa);
-    qk_word<1>(cur.k0.w, qv, 3, sa);
-    qk_word<1>(cur.k1.x, qv, 4, sa);
-    qk_word<1>(cur.k1.y, qv, 5, sa);
-    qk_word<1>(cur.k1.z, qv, 6, sa);
-    qk_word<1>(cur.k1.w, qv, 7, sa);
+    qk_word<1>(cur.k0.x, qv, qlp, 0, sa);
+    qk_word<1>(cur.k0.y, qv, qlp, 1, sa);
+    qk_word<1>(cur.k0.z, qv, qlp, 2, sa);
+    qk_word<1>(cur.k0.w, qv, qlp, 3, sa);
+    qk_word<1>(cur.k1.x, qv, qlp, 4, sa);
+    qk_word<1>(cur.k1.y, qv, qlp, 5, sa);
+    qk_word<1>(cur.k1.z, qv, qlp, 6, sa);
+    qk_word<1>(cur.k1.w, qv, qlp, 7, sa);
     const uint32_t kmr[4] = {cur.km.x, cur.km.y, cur.km.z, cur.km.w};
     f4 part;
 #pragma unroll
@@ -2022,18 +2122,8 @@ void decode_wide_kernel(DecodeArgs a) {
   h4 qv[1][8];
   float qsum;
   int eq;
-  {
-    const __amdgpu_buffer_rsrc_t qr = plane_rsrc(a.qpub + (size_t)(bh * 4 + wave) * kQPub, kQPub * 4);
-    const int vbase = (kQPubOps + 16 * (4 * (lane >> 4) + j)) * 4;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const u4 wv = __builtin_amdgcn_raw_buffer_load_b128(qr, vbase + 16 * i, 0, 0);
-      qv[0][2 * i] = as_h4(wv.x, wv.y);
-      qv[0][2 * i + 1] = as_h4(wv.z, wv.w);
-    }
-    qsum = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(qr, (512 + j) * 4, 0, 0));
-    eq = (int)__builtin_amdgcn_raw_buffer_load_b32(qr, (516 + j) * 4, 0, 0);
-  }
+  const uint2* qlp[1] = {wide_q_operands(a, bh * 4 + wave, W.qlo[wave], qv[0], qsum, eq)};
+  __syncthreads();                        // W.qlo complete
   const float cK = ldexpf(1.0f, 24 - eq);
   const float zq = ldexpf(qsum, eq - 24);
   const float vmax = a.v.smax[bh];
@@ -2053,14 +2143,14 @@ void decode_wide_kernel(DecodeArgs a) {
   // (the same in every wave), this slice's PV
   auto process = [&](const TileRegs& cur, int t0, int buf) {
     f4 sa[1] = {{0, 0, 0, 0}};
-    qk_word<1>(cur.k0.x, qv, 0, sa);
-    qk_word<1>(cur.k0.y, qv, 1, sa);
-    qk_word<1>(cur.k0.z, qv, 2, sa);
-    qk_word<1>(cur.k0.w, qv, 3, sa);
-    qk_word<1>(cur.k1.x, qv, 4, sa);
-    qk_word<1>(cur.k1.y, qv, 5, sa);
-    qk_word<1>(cur.k1.z, qv, 6, sa);
-    qk_word<1>(cur.k1.w, qv, 7, sa);
+    qk_word<1>(cur.k0.x, qv, qlp, 0, sa);
+    qk_word<1>(cur.k0.y, qv, qlp, 1, sa);
+    qk_word<1>(cur.k0.z, qv, qlp, 2, sa);
+    qk_word<1>(cur.k0.w, qv, qlp, 3, sa);
+    qk_word<1>(cur.k1.x, qv, qlp, 4, sa);
+    qk_word<1>(cur.k1.y, qv, qlp, 5, sa);
+    qk_word<1>(cur.k1.z, qv, qlp, 6, sa);
+    qk_word<1>(cur.k1.w, qv, qlp, 7, sa);
     PHASE_FENCE();
     const uint32_t kmr[4] = {cur.km.x, cur.km.y, cur.km.z, cur.km.w};
     const uint32_t vmr[4] = {cur.vm.x, cur.vm.y, cur.vm.z, cur.vm.w};
@@ -2102,19 +2192,17 @@ void decode_wide_kernel(DecodeArgs a) {
     lB += p[2] + p[3];
     pzA = __builtin_fmaf(p[0], hi_half(vmr[0]), __builtin_fmaf(p[1], hi_half(vmr[1]), pzA));
     pzB = __builtin_fmaf(p[2], hi_half(vmr[2]), __builtin_fmaf(p[3], hi_half(vmr[3]), pzB));
-    const h4 pv1[1] = {h4{(_Float16)__builtin_fmaf(lo_half(vmr[0]), p[0], 0.0f),
-                          (_Float16)__builtin_fmaf(lo_half(vmr[1]), p[1], 0.0f),
-                          (_Float16)__builtin_fmaf(lo_half(vmr[2]), p[2], 0.0f),
-                          (_Float16)__builtin_fmaf(lo_half(vmr[3]), p[3], 0.0f)}};
+    h4 pv1[1], pl1[1];
+    pv_operands(vmr, p, pv1[0], pl1[0]);
     PHASE_FENCE();
-    pv_word<1, 0>(cur.v0.x, pv1, o0, o1);
-    pv_word<1, 1>(cur.v0.y, pv1, o0, o1);
-    pv_word<1, 2>(cur.v0.z, pv1, o0, o1);
-    pv_word<1, 3>(cur.v0.w, pv1, o0, o1);
-    pv_word<1, 4>(cur.v1.x, pv1, o0, o1);
-    pv_word<1, 5>(cur.v1.y, pv1, o0, o1);
-    pv_word<1, 6>(cur.v1.z, pv1, o0, o1);
-    pv_word<1, 7>(cur.v1.w, pv1, o0, o1);
+    pv_word<1, 0>(cur.v0.x, pv1, pl1, o0, o1);
+    pv_word<1, 1>(cur.v0.y, pv1, pl1, o0, o1);
+    pv_word<1, 2>(cur.v0.z, pv1, pl1, o0, o1);
+    pv_word<1, 3>(cur.v0.w, pv1, pl1, o0, o1);
+    pv_word<1, 4>(cur.v1.x, pv1, pl1, o0, o1);
+    pv_word<1, 5>(cur.v1.y, pv1, pl1, o0, o1);
+    pv_word<1, 6>(cur.v1.z, pv1, pl1, o0, o1);
+    pv_word<1, 7>(cur.v1.w, pv1, pl1, o0, o1);
   };
 
   int buf = 0;

@@ -88,6 +88,7 @@ struct oscar_kv {
   int32_t mfma_waves = 4;
   int resident = 1024;       // matrix-core kernel blocks resident at once on the device
   unsigned qwait_ticks = 2000;  // 20 us of the device wall clock (set from its rate at create)
+  int q_share = 1;           // 0: blocks never wait for the published q (test switch)
   bool prof_on = false;
   ProfClass prof[3];
 };
@@ -612,6 +613,7 @@ int launch_decode(oscar_kv* kv, int32_t layer, const void* q, void* out, int32_t
     if (++kv->epoch == 0) kv->epoch = 1;   // a flag never holds a future launch's number
     da.epoch = kv->epoch;
     da.qwait_ticks = kv->qwait_ticks;
+    da.q_self = kv->q_share ? 0 : 1;
     const long pk = prof_begin(kv, 0, stream);
     HIP_TRY(launch_decode_mfma(da, batch, kv->mfma_waves, stream));
     prof_end(kv, 0, pk, stream);
@@ -813,6 +815,13 @@ int oscar_kv_set_num_splits(oscar_kv* kv, int32_t num_splits) {
   if (num_splits < 0 || num_splits > kMaxSplits - kMaxWinSplits)
     return fail(OSCAR_ERR_INVALID_ARG, "num_splits must be in [0, 224]");
   kv->forced_splits = num_splits;
+  return OSCAR_OK;
+}
+
+int oscar_kv_set_q_share(oscar_kv* kv, int32_t share) {
+  if (!kv) return fail(OSCAR_ERR_INVALID_ARG, "handle is NULL");
+  if (share != 0 && share != 1) return fail(OSCAR_ERR_INVALID_ARG, "share must be 0 or 1");
+  kv->q_share = share;
   return OSCAR_OK;
 }
 

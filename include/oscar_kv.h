@@ -190,6 +190,14 @@ int oscar_kv_device_bytes(const oscar_kv* kv, size_t* bytes);
  * by the number of 64-token tiles.  Errors: INVALID_ARG. */
 int oscar_kv_set_num_splits(oscar_kv* kv, int32_t num_splits);
 
+/* q sharing inside the head_dim 128 matrix-core launch: 1 (default) = the
+ * first attention block of each (sequence, kv head) rotates q and publishes
+ * it, and the other blocks wait for it for a bounded time (20 us of the
+ * device wall clock) before rotating q themselves; 0 = no block waits, every
+ * attention block rotates q itself (the path a block takes when its wait runs
+ * out, for tests).  Both give the same q operands.  Errors: INVALID_ARG. */
+int oscar_kv_set_q_share(oscar_kv* kv, int32_t share);
+
 /* Select the decode kernel: 0 = automatic (fused MFMA kernel where supported),
  * 1 = the general VALU kernel for every shape.  Errors: INVALID_ARG. */
 int oscar_kv_set_decode_impl(oscar_kv* kv, int32_t impl);

@@ -2,7 +2,8 @@
 
 Recipe (also stated in the design notes):
   * seeds: numpy.random.default_rng([seed0, layer, role, *extra]);
-  * values: N(0, 1) per element, with outlier channels multiplied by 8; the
+  * values: N(0, 1) per element, with outlier channels multiplied by 8 (or
+    another factor where a test sweeps the value range); the
     outlier channels are drawn per layer (and per kv head in the "percent"
     mode) and shared by Q (through q head -> kv head), K and V;  heavy-tailed
     variant: Student-t with 3 degrees of freedom, unscaled;
@@ -67,20 +68,20 @@ def draw(shape, seed0: int, layer: int, role: str, dist: str = "normal", *extra:
 
 
 def kv_bits(batch: int, n: int, num_kv_heads: int, D: int, seed0: int, layer: int, role: str,
-            mask: np.ndarray, dist: str = "normal", chunk: int = 0) -> np.ndarray:
+            mask: np.ndarray, dist: str = "normal", chunk: int = 0, outlier_scale: float = 8.0) -> np.ndarray:
     """bf16 bits [batch, n, Hkv, D] for K (role 'k') or V (role 'v')."""
     x = draw((batch, n, num_kv_heads, D), seed0, layer, role, dist, chunk)
-    x = np.where(mask[None, None], x * 8.0, x)
+    x = np.where(mask[None, None], x * outlier_scale, x)
     return to_bf16_bits(x)
 
 
 def q_bits(batch: int, num_q_heads: int, num_kv_heads: int, D: int, seed0: int, layer: int,
-           mask: np.ndarray, dist: str = "normal", step: int = 0) -> np.ndarray:
+           mask: np.ndarray, dist: str = "normal", step: int = 0, outlier_scale: float = 8.0) -> np.ndarray:
     """bf16 bits [batch, Hq, D]; query head j shares kv head j // (Hq/Hkv)'s outliers."""
     x = draw((batch, num_q_heads, D), seed0, layer, "q", dist, step)
     gq = num_q_heads // num_kv_heads
     qmask = np.repeat(mask, gq, axis=0)
-    x = np.where(qmask[None], x * 8.0, x)
+    x = np.where(qmask[None], x * outlier_scale, x)
     return to_bf16_bits(x)
 
 

@@ -14,10 +14,33 @@ import oracle as orc
 import synth
 
 
+ATTN_TOL = 2e-3       # attention output against the oracle, relative L2
+
+
 def rel_l2(a, b) -> float:
     a = np.asarray(a, np.float64)
     b = np.asarray(b, np.float64)
     return float(np.linalg.norm(a - b) / max(np.linalg.norm(b), 1e-300))
+
+
+def row_errors(got, want) -> np.ndarray:
+    """Relative L2 error of every output row (one query head of one sequence,
+    or of one query position), over the last axis."""
+    g = np.asarray(got, np.float64)
+    w = np.asarray(want, np.float64)
+    g = g.reshape(-1, g.shape[-1])
+    w = w.reshape(-1, w.shape[-1])
+    return np.linalg.norm(g - w, axis=1) / np.maximum(np.linalg.norm(w, axis=1), 1e-300)
+
+
+def oracle_err(got, want, tol: float = ATTN_TOL) -> float:
+    """Relative L2 error of the whole output against the oracle's; asserts
+    on the way that every row is within tol on its own (a small error confined
+    to one head cannot hide in the norm of many)."""
+    rows = row_errors(got, want)
+    worst = float(rows.max())
+    assert worst <= tol, f"row {int(rows.argmax())}: rel L2 {worst:.3e} > {tol:.1e}"
+    return rel_l2(got, want)
 
 
 def say(*args):
@@ -41,6 +64,7 @@ class Shape:
     outliers: str = "fixed"
     dist: str = "normal"
     seed: int = 0
+    outlier_scale: float = 8.0
 
 
 def make_rotations(shape: Shape, kind: str):
@@ -58,18 +82,50 @@ def make_rotations(shape: Shape, kind: str):
         sp = np.zeros((D, D), np.float32)
         sp[np.arange(D), perm] = np.where(g.random(D) < 0.5, -1.0, 1.0)
         return np.stack([pbr] * L), np.stack([sp] * L)
+    if kind == "exact_layers":
+        # a different signed permutation per layer for K and for V: exact in
+        # fp32, so every stored bit of every layer is fixed by the inputs, and
+        # a layer that read another layer's rotation would differ
+        out = []
+        for role in ("rot_k", "rot_v"):
+            mats = []
+            for l in range(L):
+                g = synth.rng(shape.seed, l, role)
+                m = np.zeros((D, D), np.float32)
+                m[np.arange(D), g.permutation(D)] = np.where(g.random(D) < 0.5, -1.0, 1.0)
+                mats.append(m)
+            out.append(np.stack(mats))
+        return out[0], out[1]
     raise ValueError(kind)
 
 
 def inputs(shape: Shape, T: int, layer: int = 0, chunk: int = 0):
     mask = synth.outlier_mask(shape.D, shape.Hkv, shape.seed, layer, shape.outliers)
-    k = synth.kv_bits(shape.B, T, shape.Hkv, shape.D, shape.seed, layer, "k", mask, shape.dist, chunk)
-    v = synth.kv_bits(shape.B, T, shape.Hkv, shape.D, shape.seed, layer, "v", mask, shape.dist, chunk)
+    k = synth.kv_bits(shape.B, T, shape.Hkv, shape.D, shape.seed, layer, "k", mask, shape.dist, chunk,
+                      shape.outlier_scale)
+    v = synth.kv_bits(shape.B, T, shape.Hkv, shape.D, shape.seed, layer, "v", mask, shape.dist, chunk,
+                      shape.outlier_scale)
     return k, v, mask
 
 
 def query(shape: Shape, mask, layer: int = 0, step: int = 0):
-    return synth.q_bits(shape.B, shape.Hq, shape.Hkv, shape.D, shape.seed, layer, mask, shape.dist, step)
+    return synth.q_bits(shape.B, shape.Hq, shape.Hkv, shape.D, shape.seed, layer, mask, shape.dist, step,
+                        shape.outlier_scale)
+
+
+def compare_planes(gp, op, T, N, M, label):
+    """GPU export (canonical) vs oracle logical planes, bit for bit."""
+    if "full" in gp:
+        np.testing.assert_array_equal(gp["full"], op.win, err_msg=f"{label} bf16 plane")
+        return
+    np.testing.assert_array_equal(gp["codes"], orc.pack_codes(op.codes), err_msg=f"{label} codes")
+    np.testing.assert_array_equal(gp["s16"].view(np.uint16), op.s16.view(np.uint16), err_msg=f"{label} s16")
+    np.testing.assert_array_equal(gp["z16"].view(np.uint16), op.z16.view(np.uint16), err_msg=f"{label} z16")
+    for t in range(min(N, T)):
+        np.testing.assert_array_equal(gp["sink"][:, :, t], op.win[:, :, t], err_msg=f"{label} sink {t}")
+    if M > 0:
+        for t in range(max(N, T - M), T):
+            np.testing.assert_array_equal(gp["ring"][:, :, t % M], op.win[:, :, t], err_msg=f"{label} ring {t}")
 
 
 def gpu_cache(ok, shape: Shape, rk, rv, max_context: int, absorb_v: int = 0, hadamard: int = 0):

@@ -9,13 +9,11 @@ import pytest
 
 import oracle as orc
 import synth
-from tests.gpu_util import (Shape, gpu_cache, inputs, make_rotations, oracle_cache, oracle_on_exported, planes_from_export,
-                            query, rel_l2, say)
+from tests.gpu_util import (ATTN_TOL, Shape, compare_planes, gpu_cache, inputs, make_rotations, oracle_cache,
+                            oracle_err, oracle_on_exported, planes_from_export, query, rel_l2, say)
 
 torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
-
-ATTN_TOL = 2e-3
 
 
 @pytest.fixture(scope="module")
@@ -101,21 +99,6 @@ def test_quantize_rows_bitexact(ok, D, clip):
 # ------------------------------------------------------------------ append
 
 
-def _compare_planes(gp, op, T, N, M, label):
-    """GPU export (canonical) vs oracle logical planes, bit for bit."""
-    if "full" in gp:
-        np.testing.assert_array_equal(gp["full"], op.win, err_msg=f"{label} bf16 plane")
-        return
-    np.testing.assert_array_equal(gp["codes"], orc.pack_codes(op.codes), err_msg=f"{label} codes")
-    np.testing.assert_array_equal(gp["s16"].view(np.uint16), op.s16.view(np.uint16), err_msg=f"{label} s16")
-    np.testing.assert_array_equal(gp["z16"].view(np.uint16), op.z16.view(np.uint16), err_msg=f"{label} z16")
-    for t in range(min(N, T)):
-        np.testing.assert_array_equal(gp["sink"][:, :, t], op.win[:, :, t], err_msg=f"{label} sink {t}")
-    if M > 0:
-        for t in range(max(N, T - M), T):
-            np.testing.assert_array_equal(gp["ring"][:, :, t % M], op.win[:, :, t], err_msg=f"{label} ring {t}")
-
-
 @pytest.mark.parametrize("shape,chunks", [
     (Shape(B=2, Hq=4, Hkv=1, D=128, N=64, M=256), [1000, 1, 23, 1]),
     (Shape(B=1, Hq=8, Hkv=2, D=128, N=5, M=7), [3, 1, 1, 9, 64, 1]),
@@ -139,8 +122,8 @@ def test_append_exact_rotation_bitexact(ok, shape, chunks):
         t += n
     torch.cuda.synchronize()
     assert gc.length(0) == T
-    _compare_planes(gc.export(0, 0), oc.k[0], T, shape.N, shape.M, "K")
-    _compare_planes(gc.export(0, 1), oc.v[0], T, shape.N, shape.M, "V")
+    compare_planes(gc.export(0, 0), oc.k[0], T, shape.N, shape.M, "K")
+    compare_planes(gc.export(0, 1), oc.v[0], T, shape.N, shape.M, "V")
     gc.close()
 
 
@@ -217,7 +200,7 @@ def test_decode_tiny_identical_cache(ok, impl):
     qb = query(shape, mask)
     got = _decode(ok, gc, 0, qb, impl=impl)
     want = oracle_on_exported(gc, 0, qb, shape, rk, rv)
-    e = rel_l2(got, want)
+    e = oracle_err(got, want)
     say(f"  rel L2 {e:.3e}")
     assert e <= ATTN_TOL
     gc.close()
@@ -242,7 +225,7 @@ def test_decode_end_to_end_vs_oracle_cache(ok):
     gc2, rk2, rv2, *_ = _fill(ok, shape, T, rot="exact")
     oc2 = oracle_cache(shape, rk2, rv2)
     oc2.append(0, k, v)
-    e2 = rel_l2(_decode(ok, gc2, 0, qb), oc2.attend(0, qb))
+    e2 = oracle_err(_decode(ok, gc2, 0, qb), oc2.attend(0, qb))
     say(f"  end-to-end exact-rotation rel L2 {e2:.3e}")
     assert e2 <= ATTN_TOL
     gc.close()
@@ -260,7 +243,7 @@ def test_decode_window_edges(ok, T, N, M):
     qb = query(shape, mask)
     want = oracle_on_exported(gc, 0, qb, shape, rk, rv)
     for impl in (0, 1):
-        e = rel_l2(_decode(ok, gc, 0, qb, impl=impl), want)
+        e = oracle_err(_decode(ok, gc, 0, qb, impl=impl), want)
         say(f"  impl={impl} rel L2 {e:.3e}")
         assert e <= ATTN_TOL
     gc.close()
@@ -282,7 +265,7 @@ def test_decode_wide_window_edges(ok, T, N, M, gq, vdt):
     qb = query(shape, mask)
     want = oracle_on_exported(gc, 0, qb, shape, rk, rv)
     for impl in (0, 1):
-        e = rel_l2(_decode(ok, gc, 0, qb, impl=impl), want)
+        e = oracle_err(_decode(ok, gc, 0, qb, impl=impl), want)
         say(f"  impl={impl} rel L2 {e:.3e}")
         assert e <= ATTN_TOL
     gc.close()
@@ -306,7 +289,7 @@ def test_split_invariance(ok, impl, tol, gq, D, vdt):
         say(f"  splits={s} vs 1: {e:.2e}")
         assert e <= tol
     want = oracle_on_exported(gc, 0, qb, shape, rk, rv)
-    assert rel_l2(ref, want) <= ATTN_TOL
+    assert oracle_err(ref, want) <= ATTN_TOL
     gc.close()
 
 
@@ -323,7 +306,7 @@ def test_decode_shapes(ok, shape):
     gc, rk, rv, k, v, mask = _fill(ok, shape, 700)
     qb = query(shape, mask)
     want = oracle_on_exported(gc, 0, qb, shape, rk, rv)
-    e = rel_l2(_decode(ok, gc, 0, qb), want)
+    e = oracle_err(_decode(ok, gc, 0, qb), want)
     say(f"  rel L2 {e:.3e}")
     assert e <= ATTN_TOL
     gc.close()
@@ -373,7 +356,7 @@ def test_decode_after_many_single_appends(ok):
         if i % 7 == 0 or i == 29:
             qb = query(shape, mask, step=i)
             want = oracle_on_exported(gc, 0, qb, shape, rk, rv)
-            e = rel_l2(_decode(ok, gc, 0, qb), want)
+            e = oracle_err(_decode(ok, gc, 0, qb), want)
             assert e <= ATTN_TOL, (i, e)
     gc.close()
 
@@ -447,7 +430,7 @@ def test_decode_step_equals_append_then_decode(ok, shape, T0, steps):
         if i == 0 or i == steps - 1 or i % 16 == 0:
             _exports_equal(g1, g2, 0, shape.N, shape.M)
             want = oracle_on_exported(g1, 0, qb, shape, rk, rv)
-            eo = rel_l2(got, want)
+            eo = oracle_err(got, want)
             assert eo <= ATTN_TOL, (i, eo)
     say(f"  worst step-vs-separate rel L2 {worst:.2e}")
     g1.close()
@@ -472,11 +455,11 @@ def test_decode_step_exact_rotation_bitexact(ok):
         qb = query(shape, mask, step=i)
         got = _step(ok, gc, 0, k[:, t:t + 1], v[:, t:t + 1], qb)
         oc.append(0, k[:, t:t + 1], v[:, t:t + 1])
-        e = rel_l2(got, oc.attend(0, qb))
+        e = oracle_err(got, oc.attend(0, qb))
         assert e <= ATTN_TOL, (i, e)
     T = T0 + steps
-    _compare_planes(gc.export(0, 0), oc.k[0], T, shape.N, shape.M, "K")
-    _compare_planes(gc.export(0, 1), oc.v[0], T, shape.N, shape.M, "V")
+    compare_planes(gc.export(0, 0), oc.k[0], T, shape.N, shape.M, "K")
+    compare_planes(gc.export(0, 1), oc.v[0], T, shape.N, shape.M, "V")
     gc.close()
 
 
@@ -535,7 +518,7 @@ def test_full_size_32k_sampled(ok):
     assert rel_l2(got_step, got) <= 2 ** -12
     for b in (0, 15):
         want = oracle_on_exported(gc, 0, qb, shape, rk, rv, batch_idx=slice(b, b + 1))
-        e = rel_l2(got[b:b + 1], want)
+        e = oracle_err(got[b:b + 1], want)
         say(f"  seq {b}: rel L2 {e:.3e}")
         assert e <= ATTN_TOL
     gc.close()
@@ -560,7 +543,7 @@ def test_full_size_16k_batch1_sampled(ok):
         qb = query(shape, mask, step=i)
         got = _step(ok, gc, 0, k1, v1, qb)
     want = oracle_on_exported(gc, 0, qb, shape, rk, rv)
-    e = rel_l2(got, want)
+    e = oracle_err(got, want)
     say(f"  after 4 steps (T={gc.length(0)}): rel L2 {e:.3e}")
     assert e <= ATTN_TOL
     gc.close()
@@ -631,7 +614,7 @@ def test_prefill_attn_full_size_16k_sampled(ok):
     vp = planes_from_export(gc.export(0, 1), T, shape.N, shape.M)
     want = orc.prefill_attention(qb, kp, vp, rk[0], rv[0], shape.Hkv, shape.N, shape.M, 128, 0, 0,
                                  query_ids=ids)
-    e = rel_l2(got[:, ids], want)
+    e = oracle_err(got[:, ids], want)
     say(f"  sampled queries {ids}: rel L2 {e:.3e}")
     assert e <= ATTN_TOL
     gc.close()
@@ -659,7 +642,7 @@ def test_full_size_128k_gqa8_sampled(ok):
     assert rel_l2(got_step, got) <= 2 ** -12
     for b in (0, 7):
         want = oracle_on_exported(gc, 0, qb, shape, rk, rv, batch_idx=slice(b, b + 1))
-        e = rel_l2(got[b:b + 1], want)
+        e = oracle_err(got[b:b + 1], want)
         say(f"  seq {b}: rel L2 {e:.3e}")
         assert e <= ATTN_TOL
     gc.close()
@@ -685,7 +668,7 @@ def test_full_size_wide_64k_sampled(ok):
     got = _decode(ok, gc, 0, qb)
     for b in (0, 3):
         want = oracle_on_exported(gc, 0, qb, shape, rk, rv, batch_idx=slice(b, b + 1))
-        e = rel_l2(got[b:b + 1], want)
+        e = oracle_err(got[b:b + 1], want)
         say(f"  seq {b}: rel L2 {e:.3e}")
         assert e <= ATTN_TOL
     gc.close()
@@ -724,7 +707,7 @@ def test_full_size_wide_64k_vbf16_sampled(ok):
     got = _decode(ok, gc, 0, qb)
     for b in (0, 3):
         want = oracle_on_exported(gc, 0, qb, shape, rk, rv, batch_idx=slice(b, b + 1))
-        e = rel_l2(got[b:b + 1], want)
+        e = oracle_err(got[b:b + 1], want)
         say(f"  seq {b}: rel L2 {e:.3e}")
         assert e <= ATTN_TOL
     gc.close()
@@ -753,14 +736,14 @@ def test_absorbed_v_rotation(ok, shape, impl):
     got_a = _step(ok, ga, 0, k[:, T - 1:T], v[:, T - 1:T], qb)
     got_n = _step(ok, gn, 0, k[:, T - 1:T], v[:, T - 1:T], qb)
     want = oracle_on_exported(ga, 0, qb, shape, rk, rv, absorb_v=True)
-    e = rel_l2(got_a, want)
+    e = oracle_err(got_a, want)
     say(f"  step: rel L2 vs oracle o' {e:.3e}")
     assert e <= ATTN_TOL
     Rv = rv[0].astype(np.float64)
     assert rel_l2(got_a.astype(np.float64) @ Rv.T, got_n) <= 1e-5
     got_a = _decode(ok, ga, 0, qb, impl=impl)
     got_n = _decode(ok, gn, 0, qb, impl=impl)
-    e = rel_l2(got_a, want)
+    e = oracle_err(got_a, want)
     say(f"  decode impl={impl}: rel L2 vs oracle o' {e:.3e}")
     assert e <= ATTN_TOL
     assert rel_l2(got_a.astype(np.float64) @ Rv.T, got_n) <= 1e-5
@@ -808,11 +791,11 @@ def test_in_quant_hadamard(ok, shape):
     qb = query(shape, mask)
     got = _step(ok, gc, 0, k[:, T - 1:T], v[:, T - 1:T], qb)
     want = oracle_on_exported(gc, 0, qb, shape, rkh, rvh)
-    e = rel_l2(got, want)
+    e = oracle_err(got, want)
     say(f"  step: rel L2 vs oracle over the identical cache {e:.3e}")
     assert e <= ATTN_TOL
     got = _decode(ok, gc, 0, qb)
-    e = rel_l2(got, want)
+    e = oracle_err(got, want)
     say(f"  decode: rel L2 {e:.3e}")
     assert e <= ATTN_TOL
     oc = oracle_cache(shape, rkh, rvh)
@@ -824,7 +807,7 @@ def test_in_quant_hadamard(ok, shape):
         qp = _prefill_q(shape, mask, 50)
         gotp = _prefill_gpu(gc, qp)
         wantp = _prefill_oracle(gc, qp, shape, rkh, rvh)
-        e = rel_l2(gotp, wantp)
+        e = oracle_err(gotp, wantp)
         say(f"  prefill attention: rel L2 {e:.3e}")
         assert e <= ATTN_TOL
     gc.close()
@@ -888,7 +871,7 @@ def test_prefill_attn_vs_oracle(ok, shape, T0, n):
     qb = _prefill_q(shape, mask, n)
     got = _prefill_gpu(gc, qb)
     want = _prefill_oracle(gc, qb, shape, rk, rv)
-    e = rel_l2(got, want)
+    e = oracle_err(got, want)
     worst = max(rel_l2(got[:, i], want[:, i]) for i in range(n))
     say(f"  rel L2 {e:.3e} (worst query {worst:.3e})")
     assert e <= ATTN_TOL and worst <= ATTN_TOL
@@ -929,7 +912,7 @@ def test_prefill_attn_absorbed_and_dtypes(ok):
     qb = _prefill_q(shape, mask, n)
     got = _prefill_gpu(ga, qb)
     want = _prefill_oracle(ga, qb, shape, rk, rv, absorb_v=True)
-    assert rel_l2(got, want) <= ATTN_TOL
+    assert oracle_err(got, want) <= ATTN_TOL
     for dt, tol in ((1, 2.0 ** -8), (2, 2.0 ** -11)):
         o = _prefill_gpu(ga, qb, dt)
         assert np.abs(o - got).max() <= tol * np.abs(got).max() + 1e-6
@@ -980,7 +963,7 @@ def test_prefill_attn_after_decode_steps(ok):
     qb = _prefill_q(shape, mask, T - 500, step0=7)
     got = _prefill_gpu(gc, qb)
     want = _prefill_oracle(gc, qb, shape, rk, rv)
-    e = rel_l2(got, want)
+    e = oracle_err(got, want)
     say(f"  rel L2 {e:.3e}")
     assert e <= ATTN_TOL
     gc.close()
@@ -1023,7 +1006,7 @@ def test_softmax_scale_argument(ok, shape, impl):
                                    shape.k_dtype, shape.v_dtype)
     assert rel_l2(default, want) > 1e-2                 # the scale matters on this input
     for name, g in (("step", got_step), ("call", got)):
-        e = rel_l2(g, want)
+        e = oracle_err(g, want)
         say(f"  {name}: rel L2 {e:.3e}")
         assert e <= ATTN_TOL
     if D == 128:
@@ -1033,7 +1016,7 @@ def test_softmax_scale_argument(ok, shape, impl):
         torch.cuda.synchronize()
         wantp = orc.prefill_attention(qp, kp, vp, rk[0], rv[0], shape.Hkv, shape.N, shape.M, 128,
                                       shape.k_dtype, shape.v_dtype, scale=sc)
-        e = rel_l2(outp.cpu().numpy(), wantp)
+        e = oracle_err(outp.cpu().numpy(), wantp)
         say(f"  prefill: rel L2 {e:.3e}")
         assert e <= ATTN_TOL
     gc.close()
