@@ -21,7 +21,7 @@ ROOT = os.path.dirname(HERE)
 BUILD_DIR = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "liboscar_kv.so")
 
-SOURCES = ["append.hip", "decode.hip", "prefill.hip", "prefill_attn.hip", "oscar_kv.cpp"]
+SOURCES = ["append.hip", "decode.hip", "prefill.hip", "prefill_attn.hip", "scratch.hip", "oscar_kv.cpp"]
 # per-source extra flags: the decode kernels carry -inf but never NaN (NaN
 # inputs are outside the cache contract), so max/min need no NaN quieting
 EXTRA = {"decode.hip": ["-fno-honor-nans"]}

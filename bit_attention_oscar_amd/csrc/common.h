@@ -146,6 +146,7 @@ struct CombineArgs {
   void* out;
   int out_dtype;
   int B, Hq, Hkv, D, nslots;
+  int pstride;             // partial slots per (sequence, query head) in `partials` (>= nslots)
   int absorb_v;            // 1: write the merged o' (V-rotated basis), no un-rotation
 };
 
@@ -158,7 +159,8 @@ struct DecodeArgs {
   unsigned epoch;          // this launch's number (never 0)
   unsigned qwait_ticks;    // longest wait for the published q, in wall-clock ticks
   int q_self;              // 1: no block waits for the published q (each rotates it itself)
-  float* partials;         // [B][Hq][kMaxSplits][D+2]
+  float* partials;         // [B][Hq][pstride][D+2]
+  int pstride;             // partial slots per (sequence, query head)
   int Hq, Hkv, D, cap, N, M, T;
   int Gq, G;               // query heads per kv head; head groups of 4 (matrix-core kernel)
   SegPlan plan;            // INT2 range (matrix-core kernel) or all tokens (VALU kernel)
@@ -194,6 +196,13 @@ hipError_t launch_decode_wide(const DecodeArgs& a, int B, hipStream_t s);   // h
 hipError_t launch_stream_copy(const void* src, void* dst, size_t bytes, hipStream_t s);
 constexpr int kStreamReadBlocks = 8192;   // result words of the read calibration kernel
 hipError_t launch_stream_read(const void* src, size_t bytes, unsigned* out, hipStream_t s);
+// Working memory of the allocation-free decode call: a file-scope device array
+// of kStaticScratchBytes per GPU (scratch.hip).  static_scratch returns this
+// device's address of it (clearing its counter and flag regions on first use,
+// on `stream`) and the call's launch number.
+constexpr size_t kStaticScratchBytes = 16u << 20;
+constexpr size_t kCounterBytes = 256u << 10;          // 65536 (sequence, kv head) pairs
+hipError_t static_scratch(int device, hipStream_t stream, unsigned char** ptr, unsigned* epoch);
 hipError_t launch_export_codes(const uint8_t* stored, uint8_t* canon, int BH, int cap, int T, int D, int isv,
                                hipStream_t s);
 

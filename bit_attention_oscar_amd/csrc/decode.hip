@@ -292,7 +292,7 @@ __global__ __launch_bounds__(256) void decode_valu_kernel(DecodeArgs a) {
   }
   const int slot = a.plan.slot0 + split;
   for (int hq = 0; hq < Gq; ++hq) {
-    float* dst = a.partials + (((size_t)b * a.Hq + h * Gq + hq) * kMaxSplits + slot) * (D + 2);
+    float* dst = a.partials + (((size_t)b * a.Hq + h * Gq + hq) * a.pstride + slot) * (D + 2);
 #pragma unroll
     for (int c = 0; c < DC; ++c) {
       const int d = tid + 256 * c;
@@ -473,7 +473,7 @@ __device__ void combine_group(const CombineArgs& a, int bh, int cc = 0, int h_be
     // split weights: wave j handles head j; every (m, l) pair of a lane is
     // loaded in one round trip (at most kMaxSplits / 64 slots per lane)
     if (wave < nh) {
-      const float* P = a.partials + ((size_t)b * a.Hq + kvh * Gq + hc + wave) * kMaxSplits * (D + 2);
+      const float* P = a.partials + ((size_t)b * a.Hq + kvh * Gq + hc + wave) * a.pstride * (D + 2);
       constexpr int SPL = kMaxSplits / 64;
       float ms[SPL], ls[SPL];
 #pragma unroll
@@ -508,7 +508,7 @@ __device__ void combine_group(const CombineArgs& a, int bh, int cc = 0, int h_be
       const int j = idx / (D / 2), d = 2 * (idx - j * (D / 2));
       float acc0 = 0.0f, acc1 = 0.0f;
       if (j < nh) {
-        const float* P = a.partials + ((size_t)b * a.Hq + kvh * Gq + hc + j) * kMaxSplits * (D + 2);
+        const float* P = a.partials + ((size_t)b * a.Hq + kvh * Gq + hc + j) * a.pstride * (D + 2);
         for (int sl = 0; sl < a.nslots; sl += 32) {
           float v[32][2];
 #pragma unroll
@@ -849,7 +849,7 @@ __device__ void combine_fused(const CombineArgs& a, int bh, FusedSmem& S) {
 __device__ __forceinline__ void combine_group4(const CombineArgs& a, int b, int hq0, const RRows<128, 4>& rr, FusedSmem& S) {
   constexpr int D = 128, SB = 8;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const float* P = a.partials + ((size_t)b * a.Hq + hq0 + wave) * kMaxSplits * (D + 2);
+  const float* P = a.partials + ((size_t)b * a.Hq + hq0 + wave) * a.pstride * (D + 2);
   float M = NEG_INF, L = 0.0f, o0 = 0.0f, o1 = 0.0f;
   for (int s0 = 0; s0 < a.nslots; s0 += SB) {
     float ms[SB], ls[SB], x0[SB], x1[SB];
@@ -1170,7 +1170,7 @@ __device__ __forceinline__ void window_group(const DecodeArgs& a, int bh, int b,
   const int slot = a.win.slot0 + wblk;
   for (int idx = tid; idx < 4 * D; idx += 256) {
     const int j = idx >> 7, d = idx & 127;
-    float* dst = a.partials + (((size_t)b * a.Hq + hq0 + j) * kMaxSplits + slot) * (D + 2);
+    float* dst = a.partials + (((size_t)b * a.Hq + hq0 + j) * a.pstride + slot) * (D + 2);
     st_partial(dst + d, ((red[j * D + d] + red[(4 + j) * D + d]) + red[(8 + j) * D + d]) + red[(12 + j) * D + d]);
     if (d == 0) {
       st_partial(dst + D, wm[j]);
@@ -1572,7 +1572,7 @@ void decode_mfma_kernel(DecodeArgs a) {
           L = __builtin_fmaf(sl[w * 4 + r], sw, L);
         }
       }
-      float* dst = a.partials + (((size_t)b * a.Hq + hq_of(g) + r) * kMaxSplits + slot) * (D + 2);
+      float* dst = a.partials + (((size_t)b * a.Hq + hq_of(g) + r) * a.pstride + slot) * (D + 2);
       st_partial(dst + d, O);
       if (d == 0) {
         st_partial(dst + D, M);
@@ -1861,7 +1861,7 @@ __device__ void wide_window_block(const DecodeArgs& a, int bh, int b, int h, int
 #pragma unroll
     for (int j = 0; j < NH; ++j) {
       if (j >= a.Gq) break;
-      float* dst = a.partials + (((size_t)b * a.Hq + h * a.Gq + j) * kMaxSplits + slot) * (D + 2);
+      float* dst = a.partials + (((size_t)b * a.Hq + h * a.Gq + j) * a.pstride + slot) * (D + 2);
 #pragma unroll
       for (int k = 0; k < 8; ++k) dst[col + k] = o[j][k];
       if (wave == 0 && c == 0) {
@@ -2051,12 +2051,12 @@ __device__ void wide_split_bf16v(const DecodeArgs& a, int bh, int b, int h, int 
 #pragma unroll
     for (int jj = 0; jj < NH; ++jj) {
       if (jj >= a.Gq) break;
-      float* dst = a.partials + (((size_t)b * a.Hq + h * a.Gq + jj) * kMaxSplits + slot) * (D + 2);
+      float* dst = a.partials + (((size_t)b * a.Hq + h * a.Gq + jj) * a.pstride + slot) * (D + 2);
 #pragma unroll
       for (int k = 0; k < 8; ++k) dst[col + k] = o[jj][k];
     }
   if (wave == 0 && lane < a.Gq) {
-    float* dst = a.partials + (((size_t)b * a.Hq + h * a.Gq + lane) * kMaxSplits + slot) * (D + 2);
+    float* dst = a.partials + (((size_t)b * a.Hq + h * a.Gq + lane) * a.pstride + slot) * (D + 2);
     dst[D] = m;
     dst[D + 1] = lt;
   }
@@ -2224,7 +2224,7 @@ void decode_wide_kernel(DecodeArgs a) {
 #pragma unroll
   for (int r2 = 0; r2 < 4; ++r2) {
     if (r2 >= a.Gq) break;
-    float* dst = a.partials + (((size_t)b * a.Hq + h * a.Gq + r2) * kMaxSplits + slot) * (D + 2);
+    float* dst = a.partials + (((size_t)b * a.Hq + h * a.Gq + r2) * a.pstride + slot) * (D + 2);
     dst[128 * wave + 4 * blk + j] = __builtin_fmaf(o0[0][r2], cV, pzr[r2]);
     dst[128 * wave + 64 + 4 * blk + j] = __builtin_fmaf(o1[0][r2], cV, pzr[r2]);
     if (wave == 0 && lane == r2) {

@@ -509,11 +509,68 @@ int check_decode_args(const oscar_kv* kv, int32_t layer, const void* q, void* ou
   return OSCAR_OK;
 }
 
+// Device memory a decode-attention call works in besides the cache and its
+// inputs and outputs: the partial results (m, l, o') of its splits, the
+// per-(sequence, kv head) block counters and q-publication flags of the
+// one-launch kernel, the published q records, the rotated q of the general
+// kernel.  Either the handle's buffers (allocated at create) or the shared
+// static array of the allocation-free call.
+struct Scratch {
+  bool use_static = false;
+  unsigned char* base = nullptr;     // static array, this device's address
+  unsigned epoch = 0;                // launch number for the q flags (static array)
+};
+
+// Points the call's arguments at its working memory for `nslots` partial
+// slots per (sequence, query head).  Static array: fixed counter and flag
+// regions, then q records, rotated q and partials carved for this call;
+// CAPACITY when they do not fit.
+int bind_scratch(oscar_kv* kv, const Scratch& sc, int batch, int nslots, DecodeArgs& da, CombineArgs& ca,
+                 float** qrot = nullptr) {
+  const auto& c = kv->cfg;
+  if (!sc.use_static) {
+    if (qrot) *qrot = kv->qrot;
+    da.qrot = kv->qrot;
+    da.qpub = kv->qpub;
+    da.qflag = kv->qflag;
+    da.counters = kv->counters;
+    da.partials = kv->partials;
+    da.pstride = kMaxSplits;
+    ca.partials = kv->partials;
+    ca.pstride = kMaxSplits;
+    return OSCAR_OK;
+  }
+  const size_t BH = (size_t)batch * c.num_kv_heads, BHq = (size_t)batch * c.num_q_heads, D = c.head_dim;
+  const size_t qrecs = std::max(std::max((size_t)c.num_kv_heads, (size_t)c.num_q_heads / 4),
+                                D == 512 ? 4 * (size_t)c.num_kv_heads : (size_t)0);
+  auto up = [](size_t n) { return (n + 255) / 256 * 256; };
+  const size_t off_qpub = 2 * kCounterBytes;
+  const size_t off_qrot = off_qpub + up((size_t)batch * qrecs * kQPub * 4);
+  const size_t off_part = off_qrot + up(BHq * D * 4);
+  const size_t end = off_part + BHq * (size_t)nslots * (D + 2) * 4;
+  if (BH * 4 > kCounterBytes || end > kStaticScratchBytes)
+    return fail(OSCAR_ERR_CAPACITY, "the allocation-free decode call needs " + std::to_string(end) +
+                                        " bytes of working memory for this batch and split plan; its static "
+                                        "array holds " + std::to_string(kStaticScratchBytes) +
+                                        " (use oscar_int2_decode_attn)");
+  da.counters = reinterpret_cast<unsigned*>(sc.base);
+  da.qflag = reinterpret_cast<unsigned*>(sc.base + kCounterBytes);
+  da.qpub = reinterpret_cast<float*>(sc.base + off_qpub);
+  if (qrot) *qrot = reinterpret_cast<float*>(sc.base + off_qrot);
+  da.qrot = reinterpret_cast<float*>(sc.base + off_qrot);
+  da.partials = reinterpret_cast<float*>(sc.base + off_part);
+  da.pstride = nslots;
+  ca.partials = da.partials;
+  ca.pstride = nslots;
+  return OSCAR_OK;
+}
+
 // Enqueue decode attention of `layer` over T tokens.  With `app` set (matrix-
 // core shapes only) the same launch also appends that one token, which is then
 // the last of the T tokens.
 int launch_decode(oscar_kv* kv, int32_t layer, const void* q, void* out, int32_t out_dtype, int32_t batch,
-                  float softmax_scale, int T, const AppendArgs* app, hipStream_t stream) {
+                  float softmax_scale, int T, const AppendArgs* app, hipStream_t stream,
+                  const Scratch& sc = Scratch()) {
   const Layer& L = kv->layers[layer];
   HIP_TRY(hipSetDevice(kv->cfg.device));
   const auto& c = kv->cfg;
@@ -526,10 +583,6 @@ int launch_decode(oscar_kv* kv, int32_t layer, const void* q, void* out, int32_t
   DecodeArgs da{};
   da.k = plane_dev(kv, L.k, false);
   da.v = plane_dev(kv, L.v, true);
-  da.qrot = kv->qrot;
-  da.qpub = kv->qpub;
-  da.qflag = kv->qflag;
-  da.partials = kv->partials;
   da.Hq = Hq;
   da.Hkv = Hkv;
   da.D = D;
@@ -539,14 +592,12 @@ int launch_decode(oscar_kv* kv, int32_t layer, const void* q, void* out, int32_t
   da.T = T;
   da.Gq = Hq / Hkv;
   da.G = std::max(1, da.Gq / 4);
-  da.counters = kv->counters;
   da.q = static_cast<const uint16_t*>(q);
   da.rk = kv->rk + layer * DD;
   da.scale_log2 = scale * 1.4426950408889634f;
   da.app_blocks = app ? 2 : 0;
   if (app) da.app = *app;
   CombineArgs ca{};
-  ca.partials = kv->partials;
   ca.rvT = kv->rvT + layer * DD;
   ca.out = out;
   ca.out_dtype = out_dtype;
@@ -561,7 +612,8 @@ int launch_decode(oscar_kv* kv, int32_t layer, const void* q, void* out, int32_t
   const int sink_end = std::min(N, T);
   const int rec_begin = std::max(N, T - M);
   const int int2_lo = N, int2_hi = T - M;
-  const long pcall = prof_begin(kv, 1, stream);
+  int rc = OSCAR_OK;
+  const long pcall = sc.use_static ? -1 : prof_begin(kv, 1, stream);
   if (fast) {
     // one launch: [append blocks] + bf16 window blocks + INT2 splits, q rotated
     // in each attention block, merged by the last block of each (sequence, kv head)
@@ -609,12 +661,17 @@ int launch_decode(oscar_kv* kv, int32_t layer, const void* q, void* out, int32_t
     da.int2_lead = std::max(0, std::min(p.splits, kv->resident / std::max(1, BH) - (da.G == 2 ? 0 : da.app_blocks)));
     da.split_ramp = p.splits > 1 ? kSplitRamp : 0.0f;
     ca.nslots = p.splits + w.splits;
+    if ((rc = bind_scratch(kv, sc, batch, ca.nslots, da, ca))) return rc;
     da.comb = ca;
-    if (++kv->epoch == 0) kv->epoch = 1;   // a flag never holds a future launch's number
-    da.epoch = kv->epoch;
+    if (sc.use_static) {
+      da.epoch = sc.epoch;
+    } else {
+      if (++kv->epoch == 0) kv->epoch = 1;   // a flag never holds a future launch's number
+      da.epoch = kv->epoch;
+    }
     da.qwait_ticks = kv->qwait_ticks;
     da.q_self = kv->q_share ? 0 : 1;
-    const long pk = prof_begin(kv, 0, stream);
+    const long pk = sc.use_static ? -1 : prof_begin(kv, 0, stream);
     HIP_TRY(launch_decode_mfma(da, batch, kv->mfma_waves, stream));
     prof_end(kv, 0, pk, stream);
   } else if (wide_shape(kv)) {
@@ -647,29 +704,32 @@ int launch_decode(oscar_kv* kv, int32_t layer, const void* q, void* out, int32_t
     da.ring0 = M > 0 ? rec_begin % M : 0;
     da.split_ramp = 0.0f;
     ca.nslots = p.splits + w.splits;
+    if ((rc = bind_scratch(kv, sc, batch, ca.nslots, da, ca))) return rc;
     HIP_TRY(launch_wide_qrot(da, batch, stream));
-    const long pk = prof_begin(kv, 0, stream);
+    const long pk = sc.use_static ? -1 : prof_begin(kv, 0, stream);
     HIP_TRY(launch_decode_wide(da, batch, stream));
     prof_end(kv, 0, pk, stream);
     HIP_TRY(launch_combine(ca, stream));
   } else {
+    int want = kv->forced_splits > 0 ? kv->forced_splits
+                                     : std::max(1, std::min(64, 2048 / std::max(1, BH)));
+    want = std::min(want, kMaxSplits);
+    want = std::min(want, (T + kTile - 1) / kTile);
+    da.plan = make_plan(0, T, 0, 0, want, 0);
+    ca.nslots = da.plan.splits;
+    float* qrot = nullptr;
+    if ((rc = bind_scratch(kv, sc, batch, ca.nslots, da, ca, &qrot))) return rc;
     QRotArgs qa{};
     qa.q = static_cast<const uint16_t*>(q);
     qa.rk = kv->rk + layer * DD;
-    qa.qrot = kv->qrot;
+    qa.qrot = qrot;
     qa.B = batch;
     qa.Hq = Hq;
     qa.Hkv = Hkv;
     qa.D = D;
     qa.scale_log2 = da.scale_log2;
     HIP_TRY(launch_qrot(qa, stream));
-    int want = kv->forced_splits > 0 ? kv->forced_splits
-                                     : std::max(1, std::min(64, 2048 / std::max(1, BH)));
-    want = std::min(want, kMaxSplits);
-    want = std::min(want, (T + kTile - 1) / kTile);
-    da.plan = make_plan(0, T, 0, 0, want, 0);
     HIP_TRY(launch_decode_valu(da, batch, stream));
-    ca.nslots = da.plan.splits;
     HIP_TRY(launch_combine(ca, stream));
   }
   prof_end(kv, 1, pcall, stream);
@@ -688,6 +748,20 @@ int oscar_int2_decode_attn(oscar_kv* kv, int32_t layer, const void* q, void* out
   if (L.T == 0) return fail(OSCAR_ERR_INVALID_ARG, "layer holds no tokens");
   if (batch != L.batch) return fail(OSCAR_ERR_INVALID_ARG, "batch differs from the layer's batch");
   return launch_decode(kv, layer, q, out, out_dtype, batch, softmax_scale, L.T, nullptr, stream);
+}
+
+int oscar_int2_decode_attn_noalloc(oscar_kv* kv, int32_t layer, const void* q, void* out, int32_t out_dtype,
+                                   int32_t batch, float softmax_scale, hipStream_t stream) {
+  int rc = check_decode_args(kv, layer, q, out, out_dtype, softmax_scale);
+  if (rc) return rc;
+  const Layer& L = kv->layers[layer];
+  if (L.T == 0) return fail(OSCAR_ERR_INVALID_ARG, "layer holds no tokens");
+  if (batch != L.batch) return fail(OSCAR_ERR_INVALID_ARG, "batch differs from the layer's batch");
+  HIP_TRY(hipSetDevice(kv->cfg.device));
+  Scratch sc;
+  sc.use_static = true;
+  HIP_TRY(static_scratch(kv->cfg.device, stream, &sc.base, &sc.epoch));
+  return launch_decode(kv, layer, q, out, out_dtype, batch, softmax_scale, L.T, nullptr, stream, sc);
 }
 
 int oscar_prefill_attn(oscar_kv* kv, int32_t layer, const void* q, void* out, int32_t out_dtype,

@@ -32,7 +32,7 @@ EXPORTED = [
     "oscar_last_error", "oscar_kv_length", "oscar_kv_device_bytes", "oscar_kv_set_num_splits",
     "oscar_kv_set_decode_impl", "oscar_kv_export", "oscar_kv_append_dump", "oscar_quantize_rows",
     "oscar_kv_profile_enable", "oscar_kv_profile_read", "oscar_stream_copy", "oscar_stream_read",
-    "oscar_kv_decode_step", "oscar_prefill_attn", "oscar_kv_set_q_share",
+    "oscar_kv_decode_step", "oscar_prefill_attn", "oscar_kv_set_q_share", "oscar_int2_decode_attn_noalloc",
 ]
 
 
@@ -63,6 +63,7 @@ def load_library(path: str = LIB_PATH) -> C.CDLL:
         "oscar_kv_create": ([C.POINTER(oscar_kv_config), C.POINTER(vp)], C.c_int),
         "oscar_kv_append": ([vp, i32, vp, vp, i32, i32, vp], C.c_int),
         "oscar_int2_decode_attn": ([vp, i32, vp, vp, i32, i32, f32, vp], C.c_int),
+        "oscar_int2_decode_attn_noalloc": ([vp, i32, vp, vp, i32, i32, f32, vp], C.c_int),
         "oscar_kv_destroy": ([vp], C.c_int),
         "oscar_last_error": ([], C.c_char_p),
         "oscar_kv_length": ([vp, i32, C.POINTER(i32)], C.c_int),
@@ -125,6 +126,11 @@ def oscar_kv_append(kv, layer, k, v, batch, n_new, stream=None):
 def oscar_int2_decode_attn(kv, layer, q, out, out_dtype, batch, softmax_scale=0.0, stream=None):
     _check(_lib.oscar_int2_decode_attn(kv, layer, _ptr(q), _ptr(out), out_dtype, batch,
                                        float(softmax_scale), _stream(stream)))
+
+
+def oscar_int2_decode_attn_noalloc(kv, layer, q, out, out_dtype, batch, softmax_scale=0.0, stream=None):
+    _check(_lib.oscar_int2_decode_attn_noalloc(kv, layer, _ptr(q), _ptr(out), out_dtype, batch,
+                                               float(softmax_scale), _stream(stream)))
 
 
 def oscar_kv_decode_step(kv, layer, k, v, q, out, out_dtype, batch, softmax_scale=0.0, stream=None):
@@ -247,6 +253,9 @@ class KVCache:
 
     def decode_attn(self, layer, q, out, out_dtype=OUT_F32, softmax_scale=0.0, stream=None):
         oscar_int2_decode_attn(self.handle, layer, q, out, out_dtype, q.shape[0], softmax_scale, stream)
+
+    def decode_attn_noalloc(self, layer, q, out, out_dtype=OUT_F32, softmax_scale=0.0, stream=None):
+        oscar_int2_decode_attn_noalloc(self.handle, layer, q, out, out_dtype, q.shape[0], softmax_scale, stream)
 
     def prefill_attn(self, layer, q, out, out_dtype=OUT_F32, softmax_scale=0.0, stream=None):
         """Causal attention of the last q.shape[1] cached positions' queries over the cache."""

@@ -129,6 +129,27 @@ int oscar_int2_decode_attn(oscar_kv* kv, int32_t layer, const void* q, void* out
                            int32_t out_dtype, int32_t batch, float softmax_scale,
                            hipStream_t stream);
 
+/* oscar_int2_decode_attn for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation): same arguments, result and errors, and the same kernels, but
+ * the call's working memory (the splits' partial results, the q records, the
+ * block counters and flags) lives in a file-scope device array of 16 MiB per
+ * GPU instead of the handle's buffers.  The call allocates and frees nothing;
+ * the array is held by each GPU the library runs on until the process ends,
+ * and its counters are cleared once, at the first call on that GPU.
+ * Every call on a GPU shares that GPU's array: calls that overlap on one GPU
+ * (two streams, two threads, two handles) race and must be serialised by the
+ * caller.  Limit: batch x num_kv_heads <= 65536 and the call's q records,
+ * rotated q and batch x num_q_heads x (splits + window blocks) partial slots of
+ * (head_dim + 2) floats within 16 MiB less 512 KiB (the 32k, 128k and head_dim
+ * 512 benchmark shapes use under 8 MiB).
+ * Errors: as oscar_int2_decode_attn, plus CAPACITY (nothing enqueued) when the
+ * call's working memory exceeds the array, and HIP if the array's device
+ * address cannot be taken. */
+int oscar_int2_decode_attn_noalloc(oscar_kv* kv, int32_t layer, const void* q, void* out,
+                                   int32_t out_dtype, int32_t batch, float softmax_scale,
+                                   hipStream_t stream);
+
 /* One decode step of `layer` as serving runs it (a new token's K/V are
  * cached, then its query attends over every cached token, the new one
  * included; Qwen3-4B card "Run": INT2 cache with the fused flash-attention
