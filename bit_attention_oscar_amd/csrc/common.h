@@ -10,8 +10,8 @@ namespace oscar {
 constexpr int kGroup = 128;           // quantization group along head_dim
 constexpr int kTile = 64;             // tokens per decode tile / V storage block
 constexpr int kMaxSplits = 256;       // partial-result slots per (sequence, head)
-constexpr int kQPub = 4 * 128 + 8 + 512;  // published q of 4 query heads: fp32 q, sums, exponents,
-                                          // two-piece fp16 operands
+constexpr int kQPub = 4 * 128 + 8 + 1024;  // published q of 4 query heads: fp32 q, sums, exponents,
+                                           // two-piece fp16 operands in two instruction layouts
 constexpr int kMaxGq = 16;            // query heads per kv head handled by the VALU kernel
 
 // ---------------------------------------------------------------------------

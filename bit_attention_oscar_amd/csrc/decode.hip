@@ -19,6 +19,7 @@
 //                       4x4x4 f16 matrix-core QK^T and PV on raw codes
 //   combine_kernel      log-sum-exp merge of the splits and o = o' @ R_V^T
 #include <math.h>
+#include <type_traits>
 #include "append_impl.h"
 
 namespace oscar {
@@ -40,7 +41,7 @@ typedef float f4 __attribute__((ext_vector_type(4)));
 #define PHASE_FENCE() ((void)0)
 #endif
 #ifndef OSCAR_MFMA_WAVES_PER_EU
-#define OSCAR_MFMA_WAVES_PER_EU 4
+#define OSCAR_MFMA_WAVES_PER_EU 3
 #endif
 // Two head groups per wave hold twice the q operands and accumulators: 3 waves
 // per SIMD leave them room without spills.
@@ -655,6 +656,8 @@ struct FusedSmem {
   uint16_t newtok[2][128];     // bf16 window values of the token appended by this launch
   uint32_t qlo[2][256];        // low pieces of the q operands of up to two head groups
                                // (vector 4 pp + j at 16 (4 pp + j), as published)
+  uint32_t meta16[4][128];     // INT2 splits: per wave, the K and V scale|zero words of a tile
+  u4 qops[8][64];              // INT2 splits: q operand n of lane l (the same in every wave)
   float scratch[2688];
 };
 
@@ -777,7 +780,8 @@ __device__ inline void q_operand(const FusedSmem& S, int j, int pp, int w, int k
 //   [kQPubLo, +256)   the low pieces, same order
 constexpr int kQPubOps = 520;
 constexpr int kQPubLo = kQPubOps + 256;
-static_assert(kQPubLo + 256 <= kQPub, "published q layout");
+constexpr int kQPub16 = kQPubLo + 256;
+static_assert(kQPub16 + 512 <= kQPub, "published q layout");
 
 // Word i (0 <= i < 256) of the operand vectors of the block's 4 heads, as
 // published: vector v = i / 16 = 4 pp + j, operands 2 (i % 16) and
@@ -790,6 +794,26 @@ __device__ inline void q_operand_word(const FusedSmem& S, int i, uint32_t& hw, u
   q_operand(S, j, pp, (e + 1) >> 2, (e + 1) & 3, h1, l1);
   hw = (uint32_t)__builtin_bit_cast(uint16_t, h0) | ((uint32_t)__builtin_bit_cast(uint16_t, h1) << 16);
   lw = (uint32_t)__builtin_bit_cast(uint16_t, l0) | ((uint32_t)__builtin_bit_cast(uint16_t, l1) << 16);
+}
+
+typedef _Float16 h8 __attribute__((ext_vector_type(8)));
+// s_waitcnt operand (gfx9 encoding) that waits for lgkmcnt = 0 only: vmcnt and
+// expcnt at their maxima
+constexpr int kWaitLds = 0xc07f;
+
+// Two fp16 q operand items (2d, 2d + 1) of chunk kc for lane group g, head j,
+// piece `piece`: dims 16 w + 4 hf + d and 16 w + 8 + 4 hf + d (w = 2 g +
+// kc/2, hf = kc % 2), times 2^(eq - 2d), packed low | high.
+__device__ inline uint32_t q_operand16_pair(const FusedSmem& S, int j, int g, int piece, int kc, int d) {
+  const int w = 2 * g + (kc >> 1), hf = kc & 1;
+  uint32_t out = 0;
+#pragma unroll
+  for (int e = 0; e < 2; ++e) {
+    _Float16 hi, lo;
+    split_f16(ldexpf(S.qs[j][16 * w + 8 * e + 4 * hf + d], S.qeq[j] - 2 * d), hi, lo);
+    out |= (uint32_t)__builtin_bit_cast(uint16_t, piece ? lo : hi) << (16 * e);
+  }
+  return out;
 }
 
 // The first attention block of each (sequence, kv head) rotates q and
@@ -809,6 +833,13 @@ __device__ void publish_q(const DecodeArgs& a, int pidx, FusedSmem& S) {
     q_operand_word(S, tid, hw, lw);
     st_partial(dst + kQPubOps + tid, __uint_as_float(hw));
     st_partial(dst + kQPubLo + tid, __uint_as_float(lw));
+  }
+  // operands of the 16x16x32 products: vector (piece 4 + g) 4 + j holds
+  // word 4 kc + d = items (2d, 2d + 1) of chunk kc for lane group g, head j
+  for (int i = tid; i < 512; i += blockDim.x) {
+    const int v = i >> 4, wd = i & 15;
+    st_partial(dst + kQPub16 + i,
+               __uint_as_float(q_operand16_pair(S, v & 3, (v >> 2) & 3, v >> 4, wd >> 2, wd & 3)));
   }
 }
 
@@ -1258,6 +1289,514 @@ __device__ inline TileRegs load_tile(const TileStreams& s, int t0, int lane_c, i
   return r;
 }
 
+// ---------------------------------------------------------------------------
+// INT2 splits of the one-launch kernel on v_mfma_f32_16x16x32_f16
+// ---------------------------------------------------------------------------
+//
+// Lane l = 16 g + c (c = l % 16, g = l / 16).  The columns of both products
+// are head pieces: column c is query head 4 grp + j of the kv head (grp =
+// (c / 4) % 2, j = c % 4) as piece c / 8 (0: hi = fp16(x), 1: lo =
+// fp16(x - hi)); with 4 query heads per kv head the columns of grp 1 are zero.
+// The two pieces of an operand thus ride in columns that would otherwise be
+// padding.
+//
+// QK^T, per 64-token tile: 4 token blocks tb x 4 dim chunks kc.  Row r of
+// token block tb is token tau(tb, r) = 32 (tb/2) + 8 (r/4) + 4 (tb%2) + r%4 of
+// the tile.  A (lane (r, g)) = 8 codes of that token: code word 2 g + kc/2 of
+// its row, bytes 0 and 2 (even kc) or 1 and 3 (odd kc); item 2d + e is the
+// code at bit pair d of the e-th of those bytes, as the fp16 denormal
+// c 4^d 2^-24.  B (lane (c, g)) = the same dims of column c's q times
+// 2^(eq - 2d).  Output: lane (c, g) register i = dot of column c with token
+// tau(tb, 4 g + i).  Columns c and c + 8 (the pieces of one head) are added by
+// a row rotation; both lanes then hold the head's dot.
+//
+// PV, per tile: 2 token chunks tc x 8 dim blocks db.  K slot (g, i) of chunk
+// tc is token 32 tc + 8 g + i = tau(2 tc + i/4, 4 g + i%4): the very tokens
+// whose scores lane (c, g) holds, so B (lane (c, g)) = column c's piece of
+// s_V p for its own 8 tokens, with no data movement.  A (lane (r, g)) = the
+// codes of dim 16 db + r for those tokens: in the V tile, lane record
+// r + 16 (db % 4), word 4 tc + g, bytes 0 and 2 (db < 4) or 1 and 3; item i
+// sits at bit pair i/2, a factor 4^(i/2) that the weight carries as 4^-(i/2).
+// Output: lane (c, g) register i = dim 16 db + 4 g + i of column c.
+
+// 8 codes of a code word as a 16x16x32 operand: bytes (0, 2) for hf = 0 or
+// (1, 3) for hf = 1; dword d = bit pair d of both bytes (items 2d, 2d + 1).
+__device__ inline h8 codes8(uint32_t w, int hf) {
+  const uint32_t u = hf ? (w >> 8) : w;
+  const u4 v = {u & 0x00030003u, u & 0x000C000Cu, u & 0x00300030u, u & 0x00C000C0u};
+  return __builtin_bit_cast(h8, v);
+}
+
+// v plus the value of the lane 8 away within its row of 16 (lanes c and c + 8
+// both get the sum): one add with a row rotation on its source.
+__device__ inline float row_add8(float v) {
+  return v + __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x128, 0xF, 0xF, true));
+}
+// Maximum and sum over the four lane groups (lanes c, c + 16, c + 32, c + 48).
+__device__ inline float groups_max(float v) {
+  auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ inline float groups_sum(float v) {
+  auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+  r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// Row rotation by 4 within each row of 16, added: lane c gets v_c + v_(c+4 mod 16).
+__device__ inline float row_add4(float v) {
+  return v + __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x124, 0xF, 0xF, true));
+}
+__device__ inline float row_max4(float v) {
+  return fmaxf(v, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x124, 0xF, 0xF, true)));
+}
+
+// Four query heads per kv head (G = 1) use the K dimension of the QK^T product
+// for two token sets instead: k slots 0-15 (lane groups 0, 1) carry the dims
+// of row r's token of set A, slots 16-31 those of set B, and each column's q
+// fills only the slots of its own set (the other half is zero).  Column c is
+// then head j = c % 4 of set (c / 4) % 2 as piece c / 8, every lane's scores
+// are real (none belong to a zero column), and a tile is 2 token pairs tp x 8
+// instructions of 16 dims (word w' = 4 (g % 2) + wp of the token's code row,
+// half h).  Rows: token 32 set + 8 (r / 4) + 4 tp + r % 4.  Output: lane
+// (c, g) register i = token 32 set + 8 g + 4 tp + i of its column.  PV per
+// set: K slot (g, i) = token 32 set + 8 g + i, i = 4 tp + register, the
+// lane's own weights for the columns of that set and zero for the others;
+// the sets and the pieces are added after the tile loop.
+template <bool KS>
+struct Tile16 {
+  u4 kq[KS ? 2 : 1];       // KS: the 16-byte chunk g % 2 of the row of token pair tp's token
+  uint2 k[KS ? 1 : 4];     // plain: code words 2 g, 2 g + 1 of token tau(tb, c)
+  uint32_t v[4][2];        // V record words g and 4 + g of records c + 16 q
+  uint32_t km, vm;         // scale|zero of token t0 + lane (K, V)
+};
+
+// Loads of one tile for one lane; the scale|zero words are exchanged through
+// shared memory by the wave.
+template <bool KS>
+__device__ inline Tile16<KS> load_tile16(const TileStreams& st, int t0, int koff, int voff, int moff) {
+  Tile16<KS> r;
+  const int oc = t0 * 32, om = t0 * 4;
+  // in order of first use: the scale|zero words, the K codes, the V codes
+  r.km = __builtin_amdgcn_raw_buffer_load_b32(st.km, moff, om, 0);
+  r.vm = __builtin_amdgcn_raw_buffer_load_b32(st.vm, moff, om, 0);
+  if constexpr (KS) {
+#pragma unroll
+    for (int tp = 0; tp < 2; ++tp) r.kq[tp] = __builtin_amdgcn_raw_buffer_load_b128(st.kc, koff + 64 * tp, oc, kStreamOnce);
+  } else {
+#pragma unroll
+    for (int tb = 0; tb < 4; ++tb)
+      r.k[tb] = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(
+                                              st.kc, koff + 512 * (tb >> 1) + 64 * (tb & 1), oc, kStreamOnce));
+  }
+#pragma unroll
+  for (int q = 0; q < 4; ++q)
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf)
+      r.v[q][hf] = __builtin_amdgcn_raw_buffer_load_b32(st.vc, voff + 256 * q + 1024 * hf, oc, kStreamOnce);
+  return r;
+}
+
+// One INT2 split of the one-launch kernel (G head groups of 4 query heads).
+template <int G>
+__device__ void int2_split16(const DecodeArgs& a, int b, int h, int bh, int y, int split, FusedSmem& S) {
+  constexpr int D = 128, WPB = 4;
+  constexpr bool KS = G == 1;                     // token sets in the K dimension
+  constexpr int NOP = KS ? 8 : 4;                 // q operands per lane
+  constexpr int NV = KS ? 8 : 16;                 // scores per lane per tile
+  // wave index as a uniform value: the tile loop is controlled by scalar branches
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+  const int c = lane & 15, g = lane >> 4;
+  const int jh = c & 3, piece = c >> 3;
+  const int grp = KS ? 0 : (c >> 2) & 1;          // head group of the column
+  const int set = KS ? (c >> 2) & 1 : 0;          // token set of the column (KS)
+  const bool live = grp < G;                      // the column carries a query head
+  const int lo = a.plan.a0, hi = a.plan.b0;       // INT2 token range
+  const int tile_first = lo >> 6;
+  const int ntiles = ((hi - 1) >> 6) - tile_first + 1;
+  // Split s covers tiles [start(s), start(s + 1)): shares of the range whose
+  // weights fall linearly by a.split_ramp from the first split to the last
+  // (blocks dispatched later start later and get less)
+  auto split_start = [&](int s) -> int {
+    const int Sn = a.plan.splits;
+    if (s >= Sn) return ntiles;
+    const float fs = (float)s, al = a.split_ramp;
+    const float F = (fs * (1.0f + al) - al * fs * (fs - 1.0f) / (float)max(Sn - 1, 1)) / (float)Sn;
+    return min(ntiles, (int)(F * (float)ntiles));
+  };
+  const int s_t0 = split_start(split);
+  const int s_t1 = split_start(split + 1);
+  const int t_last = max(s_t1 - 1, 0);            // a valid tile for clamped loads
+  const int ti0 = s_t0 + wave;
+  const TileStreams st = tile_streams(a, bh);
+  auto tile_t0 = [&](int ti) { return (tile_first + ti) << 6; };
+  // lane parts of the load offsets (the per-token-block and per-record parts
+  // are constants)
+  const int koff = KS ? (g & 1) * 1024 + 16 * (32 * (g >> 1) + 8 * (c >> 2) + (c & 3))
+                      : (g >> 1) * 1024 + 8 * (g & 1) + 16 * (8 * (c >> 2) + (c & 3));
+  const int voff = 16 * c + 4 * g;
+  const int moff = 4 * lane;
+  // first of the 4 tokens (of the tile) whose scores register block tb / tp holds
+  auto tok_of = [&](int t) { return KS ? 32 * set + 8 * g + 4 * t : 32 * (t >> 1) + 8 * g + 4 * (t & 1); };
+
+  // q operands of this lane's column: attention block 0 rotates and
+  // publishes q (its loads issued before its first tile's); the others read
+  // the flag before their tile loads, then take the published operands, or
+  // rotate q themselves when the wait runs out.  Operand n of the published
+  // layout (32 dims: lane group gp, chunk kc) is taken as: plain, n = kc,
+  // gp = g; KS, instruction (wp, h) = n / 2, n % 2 takes lane group
+  // 2 (g % 2) + wp / 2, chunk 2 (wp % 2) + h, zero unless the column's set is
+  // the lane's (g / 2).
+  const bool self_rotate = y == 0;
+  auto hq_of = [&](int gg) { return h * 4 * G + 4 * gg; };   // first query head of group gg
+  auto op_src = [&](int n, int& gp, int& kc) {
+    if (KS) {
+      const int wp = n >> 1, hh = n & 1;
+      gp = 2 * (g & 1) + (wp >> 1);
+      kc = 2 * (wp & 1) + hh;
+    } else {
+      gp = g;
+      kc = n;
+    }
+  };
+  const bool op_live = live && (!KS || set == (g >> 1));
+  const float pm = (float)piece;                  // 1 in the lanes of low pieces
+  h8 qop[NOP];
+  float qsum = 0.0f;
+  int eq = 0;
+#pragma unroll
+  for (int n = 0; n < NOP; ++n) qop[n] = h8{0, 0, 0, 0, 0, 0, 0, 0};
+  auto operands_from_smem = [&](int gg) {
+    if (live && grp == gg) {
+      if (op_live) {
+#pragma unroll
+        for (int n = 0; n < NOP; ++n) {
+          int gp, kc;
+          op_src(n, gp, kc);
+          u4 v;
+          v.x = q_operand16_pair(S, jh, gp, piece, kc, 0);
+          v.y = q_operand16_pair(S, jh, gp, piece, kc, 1);
+          v.z = q_operand16_pair(S, jh, gp, piece, kc, 2);
+          v.w = q_operand16_pair(S, jh, gp, piece, kc, 3);
+          qop[n] = __builtin_bit_cast(h8, v);
+        }
+      }
+      qsum = S.qsum[jh];
+      eq = S.qeq[jh];
+    }
+  };
+  unsigned flag0 = 0;
+  Tile16<KS> r[kDepth];
+  if (self_rotate) {
+    const QRotLoads qload = q_rotation_loads(a, b, hq_of(0));
+    // with no tile registers live yet, the second group's loads go out in the
+    // same round trip as the first's
+    QRotLoads qload1;
+    if constexpr (G > 1) qload1 = q_rotation_loads(a, b, hq_of(1));
+    __builtin_amdgcn_sched_barrier(0);
+    q_rotation_finish(a, qload, S);
+    publish_q(a, bh * G, S);
+#pragma unroll
+    for (int gg = 1; gg < G; ++gg) {
+      operands_from_smem(gg - 1);
+      q_rotation_finish(a, qload1, S);
+      publish_q(a, bh * G + gg, S);
+    }
+    publish_flag(a, bh);
+#pragma unroll
+    for (int k = 0; k < kDepth; ++k)
+      r[k] = load_tile16<KS>(st, tile_t0(min(ti0 + k * WPB, t_last)), koff, voff, moff);
+    operands_from_smem(G - 1);
+  } else {
+    flag0 = first_flag_read(a, bh);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int k = 0; k < kDepth; ++k)
+      r[k] = load_tile16<KS>(st, tile_t0(min(ti0 + k * WPB, t_last)), koff, voff, moff);
+    __builtin_amdgcn_sched_barrier(0);
+    if (wait_published_q(a, bh, flag0, S)) {
+      if (live) {
+        const __amdgpu_buffer_rsrc_t qr = plane_rsrc(a.qpub + (size_t)(bh * G + grp) * kQPub, kQPub * 4);
+        if (op_live) {
+#pragma unroll
+          for (int n = 0; n < NOP; ++n) {
+            int gp, kc;
+            op_src(n, gp, kc);
+            const int vb = (kQPub16 + 16 * ((piece * 4 + gp) * 4 + jh) + 4 * kc) * 4;
+            qop[n] = __builtin_bit_cast(h8, __builtin_amdgcn_raw_buffer_load_b128(qr, vb, 0, kDeviceScope));
+          }
+        }
+        qsum = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(qr, (512 + jh) * 4, 0, kDeviceScope));
+        eq = (int)__builtin_amdgcn_raw_buffer_load_b32(qr, (516 + jh) * 4, 0, kDeviceScope);
+      }
+    } else {
+#pragma unroll
+      for (int gg = 0; gg < G; ++gg) {
+        if (gg > 0) __syncthreads();        // the previous group's S.qs has been read
+        block_rotate_q_chunked(a, b, hq_of(gg), S);
+        operands_from_smem(gg);
+      }
+    }
+  }
+  // the operands wait in shared memory (every wave of the block has the same
+  // ones; wave 0 writes them) and are read per tile: they would otherwise hold
+  // NOP x 4 registers through the tile loop
+  if (wave == 0) {
+#pragma unroll
+    for (int n = 0; n < NOP; ++n) S.qops[n][lane] = __builtin_bit_cast(u4, qop[n]);
+  }
+  __syncthreads();
+  const u4* qop_lds = &S.qops[0][lane];
+  // z: an offset of zero that the compiler cannot see through, taken once
+  // per tile, so that the operand reads stay in the tile loop instead of
+  // being hoisted into registers
+  auto qop_at = [&](int n, int z) { return __builtin_bit_cast(h8, qop_lds[n * 64 + z]); };
+  const float cK = ldexpf(1.0f, 24 - eq);         // undoes 2^eq and the 2^-24 code scale
+  const float zq = ldexpf(qsum, eq - 24);         // sum(q_rot) in units of the raw dot
+  const float vmax = a.v.smax[bh];
+  int ev2 = 0;
+  if (vmax > 0.0f) frexpf(vmax, &ev2);
+  // s_V * 2^ev < 2^15; capped so that p * 2^ev and its sums stay far from fp32
+  // overflow (a cap that binds only for V scales below 2^-45)
+  const int ev = (vmax > 0.0f) ? min(15 - ev2, 60) : 0;
+  const float cV = ldexpf(1.0f, 24 - ev);
+  // The softmax weight p of a token is computed as p' = p 2^(ev - 2s), s = the
+  // bit pair of its V code (2 (tb % 2) + i / 2 for register i of token block
+  // tb; 2 tp + i / 2 with token sets), so that s_V p' is the PV operand as it
+  // stands.  l and sum(p z_V) are kept per s and brought back at the end.
+  f4 ao[8];
+#pragma unroll
+  for (int db = 0; db < 8; ++db) ao[db] = f4{0, 0, 0, 0};
+  float m = NEG_INF, ls[4], pz[4], cs[4];
+#pragma unroll
+  for (int s = 0; s < 4; ++s) ls[s] = pz[s] = cs[s] = 0.0f;
+  uint32_t* msm = S.meta16[wave];                 // [0, 64) K, [64, 128) V scale|zero of the tile
+  constexpr int NB = KS ? 2 : 4;                  // register blocks of scores (tp or tb)
+  // Everything the set-up loaded (q operands, rotation rows, the first tiles)
+  // has arrived: the tile loop then starts with only its own tiles in flight,
+  // in the order it consumes them, and waits for exactly the oldest one.
+  __builtin_amdgcn_s_waitcnt(0);
+
+  // EDGE: the tile crosses the split's INT2 range [lo, hi) (its first or last
+  // tile): tokens outside it get no weight.  A separate instantiation keeps
+  // the masks out of the other tiles.
+  auto process = [&](const Tile16<KS>& cur, int t0, auto edge_tag) {
+    constexpr bool EDGE = decltype(edge_tag)::value;
+    const bool edge = t0 < lo || t0 + 64 > hi;
+    msm[lane] = cur.km;
+    msm[64 + lane] = cur.vm;
+    f4 acc[NB];
+#pragma unroll
+    for (int rb = 0; rb < NB; ++rb) acc[rb] = f4{0, 0, 0, 0};
+    // one operand read per instruction column, used by every register block;
+    // the reads run two operands ahead of their use
+    int z;
+    asm volatile("v_mov_b32 %0, 0" : "=v"(z));
+    h8 qbuf[NOP];
+    qbuf[0] = qop_at(0, z);
+    qbuf[1] = qop_at(1, z);
+#pragma unroll
+    for (int n = 0; n < NOP; ++n) {
+      if (n + 2 < NOP) qbuf[n + 2] = qop_at(n + 2, z);
+      const h8 qn = qbuf[n];
+#pragma unroll
+      for (int rb = 0; rb < NB; ++rb) {
+        uint32_t w;
+        if constexpr (KS) {
+          const uint32_t kw[4] = {cur.kq[rb].x, cur.kq[rb].y, cur.kq[rb].z, cur.kq[rb].w};
+          w = kw[n >> 1];
+        } else {
+          w = n < 2 ? cur.k[rb].x : cur.k[rb].y;
+        }
+        acc[rb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(codes8(w, n & 1), qn, acc[rb], 0, 0, 0);
+      }
+    }
+    // the wave's shared-memory writes above have completed (lgkmcnt(0) only:
+    // a memory fence would also wait for the next tile's loads in flight)
+    // before its lanes read each other's words; the wave barrier keeps the
+    // compiler from moving those reads above it
+    __builtin_amdgcn_s_waitcnt(kWaitLds);
+    __builtin_amdgcn_wave_barrier();
+    PHASE_FENCE();
+    float u[NB][4];
+    float tmax = NEG_INF;
+#pragma unroll
+    for (int rb = 0; rb < NB; ++rb) {
+      const int tok = tok_of(rb);
+      const u4 kmv = *reinterpret_cast<const u4*>(msm + tok);
+      const uint32_t kmr[4] = {kmv.x, kmv.y, kmv.z, kmv.w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float dot = row_add8(acc[rb][i]);   // hi + lo pieces
+        // s_K * dot + z_K * sum(q), fp16 metadata read in place
+        u[rb][i] = __builtin_fmaf(hi_half(kmr[i]), zq, __builtin_fmaf(lo_half(kmr[i]), dot, 0.0f));
+        tmax = fmaxf(tmax, u[rb][i]);
+      }
+    }
+    if (__builtin_expect(EDGE && edge, 0)) {
+      tmax = NEG_INF;
+#pragma unroll
+      for (int rb = 0; rb < NB; ++rb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          if ((unsigned)(t0 + tok_of(rb) + i - lo) >= (unsigned)(hi - lo)) u[rb][i] = NEG_INF;
+          tmax = fmaxf(tmax, u[rb][i]);
+        }
+    }
+    tmax *= cK;
+    // the head's maximum is only needed when some score exceeds its running
+    // maximum (every lane of a head holds that maximum)
+    if (__any(tmax > m)) {
+      const float mnew = fmaxf(m, groups_max(KS ? row_max4(tmax) : tmax));
+      const float alpha = __builtin_amdgcn_exp2f(m - mnew);
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        ls[s] *= alpha;
+        pz[s] *= alpha;
+        cs[s] = (float)(ev - 2 * s) - mnew;
+      }
+#pragma unroll
+      for (int db = 0; db < 8; ++db) ao[db] *= alpha;
+      m = mnew;
+    }
+    h8 pw[2];                                      // this column's piece of s_V p' (KS: of its set)
+#pragma unroll
+    for (int rb = 0; rb < NB; ++rb) {
+      const u4 vmv = *reinterpret_cast<const u4*>(msm + 64 + tok_of(rb));
+      const uint32_t vmr[4] = {vmv.x, vmv.y, vmv.z, vmv.w};
+      float x[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int s = KS ? 2 * rb + (i >> 1) : 2 * (rb & 1) + (i >> 1);
+        const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(cK, u[rb][i], cs[s]));
+        ls[s] += p;
+        pz[s] = __builtin_fmaf(p, hi_half(vmr[i]), pz[s]);
+        x[i] = __builtin_fmaf(lo_half(vmr[i]), p, 0.0f);   // s_V p' (fp16 scale read in place)
+      }
+      // this column's piece, two values at a time: hi = fp16(x); the low
+      // piece's lanes (pm = 1) take fp16(x - hi) instead
+#pragma unroll
+      for (int i = 0; i < 4; i += 2) {
+        const _Float16 h0 = (_Float16)x[i], h1 = (_Float16)x[i + 1];
+        const float y0 = __builtin_fmaf(-(float)h0, pm, x[i]);
+        const float y1 = __builtin_fmaf(-(float)h1, pm, x[i + 1]);
+        const int e = KS ? 4 * rb + i : 4 * (rb & 1) + i;
+        pw[KS ? 0 : rb >> 1][e] = (_Float16)y0;
+        pw[KS ? 0 : rb >> 1][e + 1] = (_Float16)y1;
+      }
+    }
+    PHASE_FENCE();
+    if constexpr (KS) {
+      const h8 zero = h8{0, 0, 0, 0, 0, 0, 0, 0};
+#pragma unroll
+      for (int s2 = 0; s2 < 2; ++s2) {
+        const h8 op = set == s2 ? pw[0] : zero;
+#pragma unroll
+        for (int db = 0; db < 8; ++db)
+          ao[db] = __builtin_amdgcn_mfma_f32_16x16x32_f16(codes8(cur.v[db & 3][s2], db >> 2), op, ao[db], 0, 0, 0);
+      }
+    } else {
+#pragma unroll
+      for (int tc = 0; tc < 2; ++tc)
+#pragma unroll
+        for (int db = 0; db < 8; ++db)
+          ao[db] = __builtin_amdgcn_mfma_f32_16x16x32_f16(codes8(cur.v[db & 3][tc], db >> 2), pw[tc], ao[db], 0, 0, 0);
+    }
+  };
+
+  // The wave's tiles are ti0 + WPB i, i < n; r[i % 2] holds tile i.  Every
+  // processed register set is reloaded at once with the tile two ahead, so
+  // the same loads are in flight on every path through the loop (the two
+  // tiles, oldest first) and each use waits for exactly its own loads; past
+  // the last tile the loads go through resources of zero length, which return
+  // zeros without touching memory.
+  static_assert(kDepth == 2, "two register sets of tile data");
+  const int n = s_t1 > ti0 ? (s_t1 - ti0 + WPB - 1) / WPB : 0;
+  auto tile_of = [&](int i) { return tile_t0(ti0 + WPB * i); };
+  TileStreams none = st;
+  none.kc = plane_rsrc(a.k.codes, 0);
+  none.km = plane_rsrc(a.k.meta, 0);
+  none.vm = plane_rsrc(a.v.meta, 0);
+  none.vc = plane_rsrc(a.v.codes, 0);
+  for (int i = 0; i < n; i += 2) {
+    process(r[0], tile_of(i), std::true_type{});
+    r[0] = load_tile16<KS>(i + 2 < n ? st : none, tile_of(min(i + 2, n - 1)), koff, voff, moff);
+    if (i + 1 >= n) break;
+    process(r[1], tile_of(i + 1), std::true_type{});
+    r[1] = load_tile16<KS>(i + 3 < n ? st : none, tile_of(min(i + 3, n - 1)), koff, voff, moff);
+  }
+
+  // pieces of PV added (lanes c and c + 8), with token sets also the two sets
+  // (lanes c and c + 4); l and sum(p z_V) over the lanes of the head, in true
+  // units
+  float lt = 0.0f, pzt = 0.0f;
+#pragma unroll
+  for (int s = 0; s < 4; ++s) {
+    lt = __builtin_fmaf(ldexpf(ls[s], 2 * s - ev), 1.0f, lt);
+    pzt = __builtin_fmaf(ldexpf(pz[s], 2 * s - ev), 1.0f, pzt);
+  }
+  if constexpr (KS) {
+    lt = row_add4(lt);
+    pzt = row_add4(pzt);
+  }
+  lt = groups_sum(lt);
+  pzt = groups_sum(pzt);
+#pragma unroll
+  for (int db = 0; db < 8; ++db)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      ao[db][i] = row_add8(ao[db][i]);
+      if constexpr (KS) ao[db][i] = row_add4(ao[db][i]);
+    }
+
+  static_assert(8 * WPB + WPB * 4 * D <= sizeof(S.scratch) / sizeof(float), "epilogue scratch");
+  float* sm = S.scratch;                 // [WPB][4]
+  float* sl = S.scratch + 4 * WPB;       // [WPB][4]
+  float* so = S.scratch + 8 * WPB;       // [WPB][4][D]
+  const int slot = a.plan.slot0 + split;
+  // lanes holding a head's totals: c < 4 (token sets), piece 0 of its group
+  const bool writer = KS ? c < 4 : piece == 0;
+#pragma unroll
+  for (int gg = 0; gg < G; ++gg) {
+    __syncthreads();                     // every wave is past its tile loop / the previous group's merge
+    if (writer && grp == gg) {
+      if (g == 0) {
+        sm[wave * 4 + jh] = m;
+        sl[wave * 4 + jh] = lt;
+      }
+#pragma unroll
+      for (int db = 0; db < 8; ++db)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) so[(wave * 4 + jh) * D + 16 * db + 4 * g + i] = __builtin_fmaf(ao[db][i], cV, pzt);
+    }
+    __syncthreads();
+    for (int idx = threadIdx.x; idx < 4 * D; idx += 64 * WPB) {
+      const int rr = idx / D, d = idx - rr * D;
+      float M = NEG_INF;
+#pragma unroll
+      for (int w = 0; w < WPB; ++w) M = fmaxf(M, sm[w * 4 + rr]);
+      float O = 0.0f, L = 0.0f;
+      if (M != NEG_INF) {
+#pragma unroll
+        for (int w = 0; w < WPB; ++w) {
+          const float sw = exp2f(sm[w * 4 + rr] - M);
+          O = __builtin_fmaf(so[(w * 4 + rr) * D + d], sw, O);
+          L = __builtin_fmaf(sl[w * 4 + rr], sw, L);
+        }
+      }
+      float* dst = a.partials + (((size_t)b * a.Hq + hq_of(gg) + rr) * a.pstride + slot) * (D + 2);
+      st_partial(dst + d, O);
+      if (d == 0) {
+        st_partial(dst + D, M);
+        st_partial(dst + D + 1, L);
+      }
+    }
+  }
+}
+
 // G: head groups of 4 query heads per kv head (G = Hq / Hkv / 4).  Every wave
 // scores a tile's tokens for all G groups: the codes are unpacked once and
 // feed G matrix-core chains.
@@ -1292,294 +1831,7 @@ void decode_mfma_kernel(DecodeArgs a) {
     return;
   }
   const int split = y < lead ? y : y - a.win_blocks;
-  // wave index as a uniform value: the tile loop is controlled by scalar branches
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
-  const int blk = lane >> 2, j = lane & 3;
-  const int lo = a.plan.a0, hi = a.plan.b0;       // INT2 token range
-  const int tile_first = lo >> 6;
-  const int ntiles = ((hi - 1) >> 6) - tile_first + 1;
-  // Split s covers tiles [start(s), start(s + 1)): shares of the range whose
-  // weights fall linearly by a.split_ramp from the first split to the last
-  // (blocks dispatched later start later and get less)
-  auto split_start = [&](int s) -> int {
-    const int S = a.plan.splits;
-    if (s >= S) return ntiles;
-    const float fs = (float)s, al = a.split_ramp;
-    const float F = (fs * (1.0f + al) - al * fs * (fs - 1.0f) / (float)max(S - 1, 1)) / (float)S;
-    return min(ntiles, (int)(F * (float)ntiles));
-  };
-  const int s_t0 = split_start(split);
-  const int s_t1 = split_start(split + 1);
-  const int t_last = max(s_t1 - 1, 0);            // a valid tile for clamped loads
-
-  // kDepth register sets in turn: the loads of a tile are issued kDepth - 1
-  // tiles before it is processed.
-  const int lane_c = lane * 16, lane_m = blk * 16;
-  const int ti0 = s_t0 + wave;
-  const TileStreams st = tile_streams(a, bh);
-  auto tile_t0 = [&](int ti) { return (tile_first + ti) << 6; };
-  // q: attention block 0 rotates and publishes it (its loads issued before
-  // its first tile's); the others read the flag before their tile loads and
-  // take the published operands.  Measured: every block rotating costs more
-  // than sharing; first-wave blocks rotating gave the same time as this.
-  const bool self_rotate = y == 0;
-  auto hq_of = [&](int g) { return h * 4 * G + 4 * g; };   // first query head of group g
-  // q operands: 8 words x 4 fp16 of head j of each group; lane group pp holds
-  // the k-slots of qk_dim(w, pp, k), each scaled by 2^eq 4^-(d % 4)
-  h4 qv[G][8];
-  int eq[G];
-  float qsum[G];
-  // (high pieces into registers; the low pieces into the block's shared copy,
-  // word i by thread i, read back after the barrier that ends the set-up)
-  auto operands_from_smem = [&](int g) {
-#pragma unroll
-    for (int w = 0; w < 8; ++w)
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        _Float16 hi, lo;
-        q_operand(S, j, lane >> 4, w, k, hi, lo);
-        qv[g][w][k] = hi;
-      }
-    for (int i = threadIdx.x; i < 256; i += 64 * WPB) {
-      uint32_t hw, lw;
-      q_operand_word(S, i, hw, lw);
-      S.qlo[g][i] = lw;
-    }
-    qsum[g] = S.qsum[j];
-    eq[g] = S.qeq[j];
-  };
-  // The first loads are unconditional (a wave with fewer tiles re-reads its
-  // split's last tile), so what was issued before them is waited for on its
-  // own.  A rotating block issues one tile before rotating (its R rows hold
-  // the registers of the other) and the rest after.
-  unsigned flag0 = 0;
-  TileRegs r[kDepth];
-  if (self_rotate) {
-    const QRotLoads qload = q_rotation_loads(a, b, hq_of(0));
-#if !OSCAR_PUBLISH_FIRST
-    __builtin_amdgcn_sched_barrier(0);
-    r[0] = load_tile(st, tile_t0(min(ti0, t_last)), lane_c, lane_m);
-#endif
-#if OSCAR_PUBLISH_FIRST
-    // with no tile registers live yet, the second group's loads go out in the
-    // same round trip as the first's
-    QRotLoads qload1;
-    if constexpr (G > 1) qload1 = q_rotation_loads(a, b, hq_of(1));
-#endif
-    __builtin_amdgcn_sched_barrier(0);
-    q_rotation_finish(a, qload, S);
-    publish_q(a, bh * G, S);
-#pragma unroll
-    for (int g = 1; g < G; ++g) {
-      operands_from_smem(g - 1);
-#if OSCAR_PUBLISH_FIRST
-      q_rotation_finish(a, qload1, S);
-#else
-      block_rotate_q_chunked(a, b, hq_of(g), S);
-#endif
-      publish_q(a, bh * G + g, S);
-    }
-    publish_flag(a, bh);
-#if OSCAR_PUBLISH_FIRST
-    r[0] = load_tile(st, tile_t0(min(ti0, t_last)), lane_c, lane_m);
-#endif
-#pragma unroll
-    for (int k = 1; k < kDepth; ++k) r[k] = load_tile(st, tile_t0(min(ti0 + k * WPB, t_last)), lane_c, lane_m);
-    operands_from_smem(G - 1);
-  } else {
-    flag0 = first_flag_read(a, bh);
-    __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int k = 0; k < kDepth; ++k) r[k] = load_tile(st, tile_t0(min(ti0 + k * WPB, t_last)), lane_c, lane_m);
-    __builtin_amdgcn_sched_barrier(0);
-    if (wait_published_q(a, bh, flag0, S)) {
-#pragma unroll
-      for (int g = 0; g < G; ++g) {
-        const __amdgpu_buffer_rsrc_t qr = plane_rsrc(a.qpub + (size_t)(bh * G + g) * kQPub, kQPub * 4);
-        const int vbase = (kQPubOps + 16 * (4 * (lane >> 4) + j)) * 4;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const u4 wv = __builtin_amdgcn_raw_buffer_load_b128(qr, vbase + 16 * i, 0, kDeviceScope);
-          qv[g][2 * i] = as_h4(wv.x, wv.y);
-          qv[g][2 * i + 1] = as_h4(wv.z, wv.w);
-        }
-        qsum[g] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(qr, (512 + j) * 4, 0, kDeviceScope));
-        eq[g] = (int)__builtin_amdgcn_raw_buffer_load_b32(qr, (516 + j) * 4, 0, kDeviceScope);
-        for (int i = threadIdx.x; i < 256; i += 64 * WPB)
-          S.qlo[g][i] = __builtin_amdgcn_raw_buffer_load_b32(qr, (kQPubLo + i) * 4, 0, kDeviceScope);
-      }
-    } else {
-#pragma unroll
-      for (int g = 0; g < G; ++g) {
-        if (g > 0) __syncthreads();        // the previous group's S.qs has been read
-        block_rotate_q_chunked(a, b, hq_of(g), S);
-        operands_from_smem(g);
-      }
-    }
-  }
-  __syncthreads();                         // S.qlo complete
-  const uint2* qlp[G];
-#pragma unroll
-  for (int g = 0; g < G; ++g) qlp[g] = reinterpret_cast<const uint2*>(&S.qlo[g][16 * (4 * (lane >> 4) + j)]);
-  float cK[G], zq[G];
-#pragma unroll
-  for (int g = 0; g < G; ++g) {
-    cK[g] = ldexpf(1.0f, 24 - eq[g]);              // undoes 2^eq and the 2^-24 code scale
-    zq[g] = ldexpf(qsum[g], eq[g] - 24);           // sum(q_rot) in units of the raw dot
-  }
-  const float vmax = a.v.smax[bh];
-  int ev2 = 0;
-  if (vmax > 0.0f) frexpf(vmax, &ev2);
-  // s_V * 2^ev < 2^15; capped so that p * 2^ev and its sums stay far from fp32
-  // overflow (a cap that binds only for V scales below 2^-45)
-  const int ev = (vmax > 0.0f) ? min(15 - ev2, 60) : 0;
-  // The softmax weights p of tokens 4 blk + r are computed pre-multiplied by
-  // 2^kA (r = 0, 1) or 2^(kA - 2) (r = 2, 3): 2^ev times the 4^-s of those
-  // tokens' bit position in the V tile, so that s_V * p' is the PV operand as
-  // it stands.  l and sum(p z_V) are kept in the same units per lane (r = 2, 3
-  // accumulated apart) and brought back by 2^-kA at the end.
-  const int kA = ev - 4 * (blk & 1);
-  const float kAf = (float)kA;
-  const float cV = ldexpf(1.0f, 24 - ev);
-
-  f4 o0[G], o1[G];
-  float m[G], lA[G], lB[G], pzA[G], pzB[G];
-  float cA[G], cB[G];                              // kA - m and kA - 2 - m
-#pragma unroll
-  for (int g = 0; g < G; ++g) {
-    o0[g] = f4{0, 0, 0, 0};
-    o1[g] = f4{0, 0, 0, 0};
-    m[g] = NEG_INF;
-    lA[g] = lB[g] = pzA[g] = pzB[g] = 0.0f;
-    cA[g] = cB[g] = 0.0f;
-  }
-
-  // one 64-token tile: QK^T on matrix cores, online softmax, PV on matrix cores
-  auto process = [&](const TileRegs& cur, int t0) {
-    f4 sc[G];
-#pragma unroll
-    for (int g = 0; g < G; ++g) sc[g] = f4{0, 0, 0, 0};
-    qk_word<G>(cur.k0.x, qv, qlp, 0, sc);
-    qk_word<G>(cur.k0.y, qv, qlp, 1, sc);
-    qk_word<G>(cur.k0.z, qv, qlp, 2, sc);
-    qk_word<G>(cur.k0.w, qv, qlp, 3, sc);
-    qk_word<G>(cur.k1.x, qv, qlp, 4, sc);
-    qk_word<G>(cur.k1.y, qv, qlp, 5, sc);
-    qk_word<G>(cur.k1.z, qv, qlp, 6, sc);
-    qk_word<G>(cur.k1.w, qv, qlp, 7, sc);
-    PHASE_FENCE();
-
-    const uint32_t kmr[4] = {cur.km.x, cur.km.y, cur.km.z, cur.km.w};
-    const uint32_t vmr[4] = {cur.vm.x, cur.vm.y, cur.vm.z, cur.vm.w};
-    const bool edge = t0 < lo || t0 + 64 > hi;     // boundary tile (wave-uniform)
-    h4 pv[G], pl[G];
-#pragma unroll
-    for (int g = 0; g < G; ++g) {
-      float u[4];
-#pragma unroll
-      for (int r = 0; r < 4; ++r)   // s_K * dot + z_K * sum(q), fp16 metadata read in place
-        u[r] = __builtin_fmaf(hi_half(kmr[r]), zq[g], __builtin_fmaf(lo_half(kmr[r]), sc[g][r], 0.0f));
-      if (edge) {
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int t = t0 + 4 * blk + r;
-          if (t < lo || t >= hi) u[r] = NEG_INF;
-        }
-      }
-      // The head-wide maximum is only needed when some score exceeds its head's
-      // running maximum (every lane of a head holds that maximum).
-      const float tmax = cK[g] * fmaxf(fmaxf(u[0], u[1]), fmaxf(u[2], u[3]));
-      if (__any(tmax > m[g])) {                    // some head's max moved: rescale
-        const float mnew = fmaxf(m[g], head_max(tmax));
-        const float alpha = __builtin_amdgcn_exp2f(m[g] - mnew);
-        lA[g] *= alpha;
-        lB[g] *= alpha;
-        pzA[g] *= alpha;
-        pzB[g] *= alpha;
-        const f4 al = {lane_value(alpha, 0), lane_value(alpha, 1), lane_value(alpha, 2), lane_value(alpha, 3)};
-        o0[g] *= al;
-        o1[g] *= al;
-        m[g] = mnew;
-        cA[g] = kAf - mnew;
-        cB[g] = cA[g] - 2.0f;
-      }
-      float p[4];
-      p[0] = __builtin_amdgcn_exp2f(__builtin_fmaf(cK[g], u[0], cA[g]));
-      p[1] = __builtin_amdgcn_exp2f(__builtin_fmaf(cK[g], u[1], cA[g]));
-      p[2] = __builtin_amdgcn_exp2f(__builtin_fmaf(cK[g], u[2], cB[g]));
-      p[3] = __builtin_amdgcn_exp2f(__builtin_fmaf(cK[g], u[3], cB[g]));
-      lA[g] += p[0] + p[1];
-      lB[g] += p[2] + p[3];
-      pzA[g] = __builtin_fmaf(p[0], hi_half(vmr[0]), __builtin_fmaf(p[1], hi_half(vmr[1]), pzA[g]));
-      pzB[g] = __builtin_fmaf(p[2], hi_half(vmr[2]), __builtin_fmaf(p[3], hi_half(vmr[3]), pzB[g]));
-      // s_V * p' as a two-piece fp16 operand (fp16 metadata read in place)
-      pv_operands(vmr, p, pv[g], pl[g]);
-    }
-    PHASE_FENCE();
-    pv_word<G, 0>(cur.v0.x, pv, pl, o0, o1);
-    pv_word<G, 1>(cur.v0.y, pv, pl, o0, o1);
-    pv_word<G, 2>(cur.v0.z, pv, pl, o0, o1);
-    pv_word<G, 3>(cur.v0.w, pv, pl, o0, o1);
-    pv_word<G, 4>(cur.v1.x, pv, pl, o0, o1);
-    pv_word<G, 5>(cur.v1.y, pv, pl, o0, o1);
-    pv_word<G, 6>(cur.v1.z, pv, pl, o0, o1);
-    pv_word<G, 7>(cur.v1.w, pv, pl, o0, o1);
-  };
-
-  for (int ti = ti0; ti < s_t1; ti += kDepth * WPB) {
-#pragma unroll
-    for (int k = 0; k < kDepth; ++k) {
-      const int t = ti + k * WPB;
-      if (t >= s_t1) break;
-      process(r[k], tile_t0(t));
-      if (t + kDepth * WPB < s_t1) r[k] = load_tile(st, tile_t0(t + kDepth * WPB), lane_c, lane_m);
-    }
-  }
-
-  static_assert(8 * WPB + WPB * 4 * D <= sizeof(S.scratch) / sizeof(float), "epilogue scratch");
-  float* sm = S.scratch;                 // [WPB][4]
-  float* sl = S.scratch + 4 * WPB;       // [WPB][4]
-  float* so = S.scratch + 8 * WPB;       // [WPB][4][D]
-  const int slot = a.plan.slot0 + split;
-#pragma unroll
-  for (int g = 0; g < G; ++g) {
-    // per-head totals of l and sum(p z_V) over the 16 lanes of each head
-    const float l = head_sum(ldexpf(__builtin_fmaf(4.0f, lB[g], lA[g]), -kA));
-    const float pz = head_sum(ldexpf(__builtin_fmaf(4.0f, pzB[g], pzA[g]), -kA));
-    if (g > 0) __syncthreads();          // the previous group's merge has read the scratch
-    if (lane < 4) {
-      sm[wave * 4 + lane] = m[g];
-      sl[wave * 4 + lane] = l;
-    }
-    const float pzr[4] = {lane_value(pz, 0), lane_value(pz, 1), lane_value(pz, 2), lane_value(pz, 3)};
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      so[(wave * 4 + r) * D + 4 * blk + j] = __builtin_fmaf(o0[g][r], cV, pzr[r]);
-      so[(wave * 4 + r) * D + 64 + 4 * blk + j] = __builtin_fmaf(o1[g][r], cV, pzr[r]);
-    }
-    __syncthreads();
-    for (int idx = threadIdx.x; idx < 4 * D; idx += 64 * WPB) {
-      const int r = idx / D, d = idx - r * D;
-      float M = NEG_INF;
-#pragma unroll
-      for (int w = 0; w < WPB; ++w) M = fmaxf(M, sm[w * 4 + r]);
-      float O = 0.0f, L = 0.0f;
-      if (M != NEG_INF) {
-#pragma unroll
-        for (int w = 0; w < WPB; ++w) {
-          const float sw = exp2f(sm[w * 4 + r] - M);
-          O = __builtin_fmaf(so[(w * 4 + r) * D + d], sw, O);
-          L = __builtin_fmaf(sl[w * 4 + r], sw, L);
-        }
-      }
-      float* dst = a.partials + (((size_t)b * a.Hq + hq_of(g) + r) * a.pstride + slot) * (D + 2);
-      st_partial(dst + d, O);
-      if (d == 0) {
-        st_partial(dst + D, M);
-        st_partial(dst + D + 1, L);
-      }
-    }
-  }
+  int2_split16<G>(a, b, h, bh, y, split, S);
   finish_block<G>(a, bh, S);
 }
 
