@@ -111,6 +111,12 @@ def fill_layer_device(cache, layer, B, Hkv, D, T, seed=0, dist="normal", outlier
     return mask
 
 
+def prefill_attention_keys(T, n):
+    """Keys the n queries of a chunk at the end of T cached positions attend to
+    (query i at position T - n + i sees positions 0 .. T - n + i)."""
+    return n * (T - n) + n * (n + 1) // 2
+
+
 def time_prefill_attention(cache, B, Hq, Hkv, D, T, n, reps=3):
     """Chunked-prefill attention of the last n cached positions' queries
     (oscar_prefill_attn) on layer 0, timed with HIP events; median of reps.
@@ -133,8 +139,7 @@ def time_prefill_attention(cache, B, Hq, Hkv, D, T, n, reps=3):
         torch.cuda.synchronize()
         ts.append(e0.elapsed_time(e1))
     ms = float(sorted(ts[1:])[len(ts[1:]) // 2])
-    keys = n * (T - n) + n * (n + 1) / 2
-    useful = 4.0 * D * B * Hq * keys
+    useful = 4.0 * D * B * Hq * prefill_attention_keys(T, n)
     return {"queries": n, "context": T, "median_ms": round(ms, 3),
             "useful_TFLOPs": round(useful / ms / 1e9, 1), "mfma_TFLOPs": round(2 * useful / ms / 1e9, 1),
             "mfma_peak_TFLOPs": 2500.0, "mfma_util": round(2 * useful / ms / 1e9 / 2500.0, 4),

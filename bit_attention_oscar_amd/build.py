@@ -65,5 +65,38 @@ def build(verbose: bool = False) -> str:
     return LIB
 
 
+SANITIZED_LIB = os.path.join(BUILD_DIR, "liboscar_kv_sanitized.so")
+
+
+def build_sanitized() -> str:
+    """The host library (oscar_kv.cpp) built with AddressSanitizer and
+    UndefinedBehaviorSanitizer on its host code only (each -fsanitize= after
+    -Xarch_host), linked with the kernels' objects of a normal build(): for
+    running the C-ABI argument checks under the sanitizers on the CPU.  Load
+    it with the sanitizer runtime preloaded (sanitizer_runtime())."""
+    if not all(os.path.exists(os.path.join(BUILD_DIR, src + ".o")) for src in SOURCES):
+        build()
+    cc = hipcc()
+    san = "-Xarch_host -fsanitize=address -Xarch_host -fsanitize=undefined".split()
+    obj = os.path.join(BUILD_DIR, "oscar_kv.cpp.sanitized.o")
+    flags = [f for f in COMMON_FLAGS if f != "-O3"] + ["-O1", "-g", "-fno-omit-frame-pointer"]
+    _run([cc, *flags, *san, "-c", os.path.join(CSRC, "oscar_kv.cpp"), "-o", obj])
+    objs = [os.path.join(BUILD_DIR, src + ".o") for src in SOURCES if src != "oscar_kv.cpp"] + [obj]
+    _run([cc, "--offload-arch=gfx950", "-shared", "-fPIC", *san, *objs, "-o", SANITIZED_LIB])
+    return SANITIZED_LIB
+
+
+def sanitizer_runtime() -> str:
+    """Path of the AddressSanitizer runtime of the HIP toolchain's clang."""
+    import glob
+    root = os.path.dirname(os.path.dirname(os.path.realpath(hipcc())))
+    for pat in (os.path.join(root, "lib", "llvm", "lib", "clang", "*", "lib", "linux", "libclang_rt.asan-x86_64.so"),
+                "/opt/rocm/lib/llvm/lib/clang/*/lib/linux/libclang_rt.asan-x86_64.so"):
+        hits = sorted(glob.glob(pat))
+        if hits:
+            return hits[-1]
+    raise RuntimeError("AddressSanitizer runtime not found")
+
+
 if __name__ == "__main__":
     print(build(verbose="-v" in sys.argv))

@@ -78,6 +78,14 @@ __host__ __device__ inline size_t row_offset(int bh, int rows, int t, int D) {
   return ((size_t)bh * rows + t) * (size_t)D;
 }
 
+// s_waitcnt operand (gfx9 encoding) that waits for lgkmcnt = 0 only (vmcnt and
+// expcnt at their maxima).  Lanes of one wave exchange values through shared
+// memory with this wait and a wave barrier: the wait completes the wave's own
+// shared-memory writes, the barrier keeps the compiler from moving the reads
+// above it.  A memory fence would do the same but also wait for every vector
+// memory load in flight (the next tiles), which these loops keep outstanding.
+constexpr int kWaitLds = 0xc07f;
+
 // ---------------------------------------------------------------------------
 // number formats
 // ---------------------------------------------------------------------------

@@ -11,12 +11,17 @@
 // that absorbs it into the output projection).
 //
 // Kernels:
-//   qrot_kernel         q_rot = q @ R_K * scale * log2(e) (fp32), per-group sums,
-//                       and the fp16 operand registers of the matrix-core kernel
+//   qrot_kernel         q_rot = q @ R_K * scale * log2(e) (fp32) for the general kernel
 //   decode_valu_kernel  general split-K kernel: any head_dim / GQA / dtype,
 //                       per-token precision chosen by position
-//   decode_mfma_kernel  INT2 range, head_dim 128, 4 query heads per kv head:
-//                       4x4x4 f16 matrix-core QK^T and PV on raw codes
+//   decode_mfma_kernel  head_dim 128, 4 or 8 query heads per kv head, INT2 K and
+//                       V: one launch per decode step (the step's append, q
+//                       rotation and publication, INT2 splits with 16x16x32 f16
+//                       matrix-core QK^T and PV on the raw codes and two-piece
+//                       q and softmax weights, bf16 window blocks, the merge
+//                       and V un-rotation by the last block)
+//   wide_qrot_kernel, wide_prologue_kernel, decode_wide_kernel
+//                       head_dim 512 (q records, INT2 K with INT2 or bf16 V)
 //   combine_kernel      log-sum-exp merge of the splits and o = o' @ R_V^T
 #include <math.h>
 #include <type_traits>
@@ -32,37 +37,13 @@ typedef float f4 __attribute__((ext_vector_type(4)));
 // Scheduling fence between the phases of a tile (QK^T / softmax / PV): keeps
 // the compiler from hoisting a whole tile of code conversions ahead of the
 // softmax, which raises register pressure.
-#ifndef OSCAR_PHASE_FENCE
-#define OSCAR_PHASE_FENCE 1
-#endif
-#if OSCAR_PHASE_FENCE
 #define PHASE_FENCE() __builtin_amdgcn_sched_barrier(0)
-#else
-#define PHASE_FENCE() ((void)0)
-#endif
-#ifndef OSCAR_MFMA_WAVES_PER_EU
-#define OSCAR_MFMA_WAVES_PER_EU 3
-#endif
-// Two head groups per wave hold twice the q operands and accumulators: 3 waves
-// per SIMD leave them room without spills.
-#ifndef OSCAR_MFMA_WAVES_PER_EU_G2
-#define OSCAR_MFMA_WAVES_PER_EU_G2 3
-#endif
+// Waves per SIMD of the one-launch kernel (its INT2 splits need about 160
+// registers: the PV accumulators, two tiles in flight, the softmax state).
+constexpr int kMfmaWavesPerEu = 3;
 // Register sets of tile data per wave: the loads of a tile are issued
 // kDepth - 1 tiles ahead of its processing.
-#ifndef OSCAR_TILE_DEPTH
-#define OSCAR_TILE_DEPTH 2
-#endif
-#ifndef OSCAR_WIDE_WIN_FIRST
-#define OSCAR_WIDE_WIN_FIRST 1
-#endif
-// The q-publishing block issues its first tile's loads after the flag: the
-// flag waits for every earlier memory operation of the block to complete, so
-// a tile issued before it would delay every waiting block by an HBM latency.
-#ifndef OSCAR_PUBLISH_FIRST
-#define OSCAR_PUBLISH_FIRST 1
-#endif
-constexpr int kDepth = OSCAR_TILE_DEPTH;
+constexpr int kDepth = 2;
 
 __device__ inline float wmax(float v) {
 #pragma unroll
@@ -654,8 +635,6 @@ struct FusedSmem {
   int qeq[4];                  // per-head exponent of the fp16 q operand
   int ready;                   // the published q of this launch is available
   uint16_t newtok[2][128];     // bf16 window values of the token appended by this launch
-  uint32_t qlo[2][256];        // low pieces of the q operands of up to two head groups
-                               // (vector 4 pp + j at 16 (4 pp + j), as published)
   uint32_t meta16[4][128];     // INT2 splits: per wave, the K and V scale|zero words of a tile
   u4 qops[8][64];              // INT2 splits: q operand n of lane l (the same in every wave)
   float scratch[2688];
@@ -797,9 +776,6 @@ __device__ inline void q_operand_word(const FusedSmem& S, int i, uint32_t& hw, u
 }
 
 typedef _Float16 h8 __attribute__((ext_vector_type(8)));
-// s_waitcnt operand (gfx9 encoding) that waits for lgkmcnt = 0 only: vmcnt and
-// expcnt at their maxima
-constexpr int kWaitLds = 0xc07f;
 
 // Two fp16 q operand items (2d, 2d + 1) of chunk kc for lane group g, head j,
 // piece `piece`: dims 16 w + 4 hf + d and 16 w + 8 + 4 hf + d (w = 2 g +
@@ -1014,7 +990,6 @@ __device__ inline int window_new_token(const DecodeArgs& a, int wblk) {
 }
 
 __device__ inline WinRows window_rows(const DecodeArgs& a, int bh, int vt0, int v_hi, int t_new) {
-  constexpr int D = 128;
   const int tid = threadIdx.x, n = min(64, v_hi - vt0);
   WinRows r;
   const int tok = tid >> 2, part = tid & 3;
@@ -1255,6 +1230,12 @@ struct TileStreams {
 
 constexpr int kBufferConfig = 0x00020000;   // raw 32-bit data, no swizzle (gfx9 family)
 
+// Cache policy bits of a buffer load: nt (every code byte is read once per
+// launch), and sc1 (coherent across the device, for data another block of the
+// same launch wrote).
+constexpr int kStreamOnce = 2;
+constexpr int kDeviceScope = 16;
+
 __device__ inline __amdgpu_buffer_rsrc_t plane_rsrc(const void* base, int bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes, kBufferConfig);
 }
@@ -1269,25 +1250,6 @@ __device__ inline TileStreams tile_streams(const DecodeArgs& a, int bh) {
   return s;
 }
 
-// Loads of the tile starting at token t0 (a multiple of 64).  Code streams:
-// lane l reads the 32 bytes of token t0 + l (K) and V record l of the tile as
-// two 16-byte pieces, each contiguous across the wave (lane_c = 16 l), with
-// the non-temporal hint (every code byte is read once per launch); metadata:
-// lane (blk, j) reads tokens t0 + 4 blk .. + 3.
-constexpr int kStreamOnce = 2;   // cache policy bits of a buffer load: nt
-constexpr int kDeviceScope = 16; // cache policy bits of a buffer load: sc1 (coherent across the device)
-
-__device__ inline TileRegs load_tile(const TileStreams& s, int t0, int lane_c, int lane_m) {
-  const int oc = t0 * 32, om = t0 * 4;
-  TileRegs r;
-  r.k0 = __builtin_amdgcn_raw_buffer_load_b128(s.kc, lane_c, oc, kStreamOnce);
-  r.k1 = __builtin_amdgcn_raw_buffer_load_b128(s.kc, lane_c + 1024, oc, kStreamOnce);
-  r.km = __builtin_amdgcn_raw_buffer_load_b128(s.km, lane_m, om, 0);
-  r.vm = __builtin_amdgcn_raw_buffer_load_b128(s.vm, lane_m, om, 0);
-  r.v0 = __builtin_amdgcn_raw_buffer_load_b128(s.vc, lane_c, oc, kStreamOnce);
-  r.v1 = __builtin_amdgcn_raw_buffer_load_b128(s.vc, lane_c + 1024, oc, kStreamOnce);
-  return r;
-}
 
 // ---------------------------------------------------------------------------
 // INT2 splits of the one-launch kernel on v_mfma_f32_16x16x32_f16
@@ -1406,7 +1368,6 @@ __device__ void int2_split16(const DecodeArgs& a, int b, int h, int bh, int y, i
   constexpr int D = 128, WPB = 4;
   constexpr bool KS = G == 1;                     // token sets in the K dimension
   constexpr int NOP = KS ? 8 : 4;                 // q operands per lane
-  constexpr int NV = KS ? 8 : 16;                 // scores per lane per tile
   // wave index as a uniform value: the tile loop is controlled by scalar branches
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int c = lane & 15, g = lane >> 4;
@@ -1506,6 +1467,9 @@ __device__ void int2_split16(const DecodeArgs& a, int b, int h, int bh, int y, i
       publish_q(a, bh * G + gg, S);
     }
     publish_flag(a, bh);
+    // the first tiles are issued after the flag: the flag waits for every
+    // earlier memory operation of the block, so tiles issued before it would
+    // delay every waiting block by an HBM latency
 #pragma unroll
     for (int k = 0; k < kDepth; ++k)
       r[k] = load_tile16<KS>(st, tile_t0(min(ti0 + k * WPB, t_last)), koff, voff, moff);
@@ -1614,10 +1578,7 @@ __device__ void int2_split16(const DecodeArgs& a, int b, int h, int bh, int y, i
         acc[rb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(codes8(w, n & 1), qn, acc[rb], 0, 0, 0);
       }
     }
-    // the wave's shared-memory writes above have completed (lgkmcnt(0) only:
-    // a memory fence would also wait for the next tile's loads in flight)
-    // before its lanes read each other's words; the wave barrier keeps the
-    // compiler from moving those reads above it
+    // the lanes read each other's words: the wave's writes complete first
     __builtin_amdgcn_s_waitcnt(kWaitLds);
     __builtin_amdgcn_wave_barrier();
     PHASE_FENCE();
@@ -1797,15 +1758,13 @@ __device__ void int2_split16(const DecodeArgs& a, int b, int h, int bh, int y, i
   }
 }
 
-// G: head groups of 4 query heads per kv head (G = Hq / Hkv / 4).  Every wave
-// scores a tile's tokens for all G groups: the codes are unpacked once and
-// feed G matrix-core chains.
+// The one-launch decode kernel of head_dim 128.  G: head groups of 4 query
+// heads per kv head (G = Hq / Hkv / 4); the INT2 splits serve every group in
+// one pass over the tiles (int2_split16).
 template <int WPB, int G>
 __global__ __launch_bounds__(64 * WPB)
-__attribute__((amdgpu_waves_per_eu(G == 1 ? OSCAR_MFMA_WAVES_PER_EU : OSCAR_MFMA_WAVES_PER_EU_G2,
-                                   G == 1 ? OSCAR_MFMA_WAVES_PER_EU : OSCAR_MFMA_WAVES_PER_EU_G2)))
+__attribute__((amdgpu_waves_per_eu(kMfmaWavesPerEu, kMfmaWavesPerEu)))
 void decode_mfma_kernel(DecodeArgs a) {
-  constexpr int D = 128;
   const int bh = blockIdx.x;
   const int b = bh / a.Hkv, h = bh - (bh / a.Hkv) * a.Hkv;
   __shared__ FusedSmem S;
@@ -2264,7 +2223,8 @@ __device__ void wide_split_bf16v(const DecodeArgs& a, int bh, int b, int h, int 
     l += (p[0] + p[1]) + (p[2] + p[3]);
     // weights to this wave's row of shared memory: head j, token 4 blk + rr
     *reinterpret_cast<f4*>(&W.pv[wave][j][4 * blk]) = f4{p[0], p[1], p[2], p[3]};
-    __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0): the wave's own writes are visible to its reads
+    __builtin_amdgcn_s_waitcnt(kWaitLds);   // the wave's own writes are visible to its reads
+    __builtin_amdgcn_wave_barrier();
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       const int tk = tq + 4 * i;
@@ -2329,7 +2289,6 @@ void decode_wide_kernel(DecodeArgs a) {
   const int b = bh / a.Hkv, h = bh - (bh / a.Hkv) * a.Hkv;
   __shared__ WideSmem W;
   const int y = (int)blockIdx.y;
-#if OSCAR_WIDE_WIN_FIRST
   // window blocks first: their passes are latency-bound, so they start early
   // and run beside the INT2 streaming
   if (y < a.win_blocks) {
@@ -2337,13 +2296,6 @@ void decode_wide_kernel(DecodeArgs a) {
     return;
   }
   const int split = y - a.win_blocks;
-#else
-  if (y >= a.plan.splits) {
-    wide_window_block<NH, VB>(a, bh, b, h, y - a.plan.splits, W);
-    return;
-  }
-  const int split = y;
-#endif
   if constexpr (VB) {
     wide_split_bf16v<NH>(a, bh, b, h, split, W);
     return;

@@ -18,6 +18,8 @@
 
 using namespace oscar;
 
+static_assert(sizeof(oscar_kv_dtype) == sizeof(int32_t), "enum fields of the config are 32-bit");
+
 namespace {
 
 thread_local std::string g_last_error;
@@ -59,10 +61,7 @@ struct ProfClass {
 constexpr size_t kProfMax = 8192;
 constexpr int kMaxWinSplits = 48;   // bf16 window blocks per (sequence, kv head)
 constexpr int kMinTilesPerWave = 3;  // INT2 tiles per wave below which splits are not added
-#ifndef OSCAR_SMALL_WIN_TOKENS
-#define OSCAR_SMALL_WIN_TOKENS 64
-#endif
-constexpr int kSmallWinTokens = OSCAR_SMALL_WIN_TOKENS;  // window tokens per block when the launch is small
+constexpr int kSmallWinTokens = 64;   // window tokens per block when the launch is small
 
 }  // namespace
 
@@ -169,8 +168,12 @@ int validate_config(const oscar_kv_config* c) {
     return fail(OSCAR_ERR_INVALID_ARG, "window sizes must be >= 0");
   if (!(c->k_clip > 0.0f && c->k_clip <= 1.0f) || !(c->v_clip > 0.0f && c->v_clip <= 1.0f))
     return fail(OSCAR_ERR_INVALID_ARG, "clip ratios must be in (0, 1]");
-  if ((c->k_dtype != OSCAR_KV_INT2 && c->k_dtype != OSCAR_KV_BF16) ||
-      (c->v_dtype != OSCAR_KV_INT2 && c->v_dtype != OSCAR_KV_BF16))
+  // the caller may have stored any integer in the enum fields: read their
+  // bits as int32 (reading an out-of-range value as the enum type is undefined)
+  int32_t kd, vd;
+  std::memcpy(&kd, &c->k_dtype, sizeof kd);
+  std::memcpy(&vd, &c->v_dtype, sizeof vd);
+  if ((kd != OSCAR_KV_INT2 && kd != OSCAR_KV_BF16) || (vd != OSCAR_KV_INT2 && vd != OSCAR_KV_BF16))
     return fail(OSCAR_ERR_INVALID_ARG, "unknown kv dtype");
   if ((long long)c->max_batch * c->num_q_heads > (1 << 30))
     return fail(OSCAR_ERR_INVALID_ARG, "batch x heads too large");
@@ -307,33 +310,18 @@ int do_append(oscar_kv* kv, int32_t layer, const void* k, const void* v, int32_t
 // Window tokens per window block (a multiple of 64).  At the 32k shape (320
 // window tokens) 192 and 256 measured best: 66 and 65 us per launch against
 // 70 us with 64 and 74 us with all 320 in one block.
-#ifndef OSCAR_WIN_TOKENS
-#define OSCAR_WIN_TOKENS 192
-#endif
-constexpr int kWinTokens = OSCAR_WIN_TOKENS;
-#ifndef OSCAR_WIN_TOKENS_G2
-#define OSCAR_WIN_TOKENS_G2 128
-#endif
-constexpr int kWinTokensG2 = OSCAR_WIN_TOKENS_G2;
+constexpr int kWinTokens = 192;
+constexpr int kWinTokensG2 = 128;       // 8 query heads per kv head (two head groups per window block)
 // head_dim 512: bf16 window tokens per window block (512 measured 524 against
 // 518 tokens/s for 256 at the wide-head 64k shape, 455 for 1024), INT2 blocks
 // per launch
-#ifndef OSCAR_WIDE_WIN_TOKENS
-#define OSCAR_WIDE_WIN_TOKENS 512
-#endif
-#ifndef OSCAR_WIDE_TARGET_BLOCKS
-#define OSCAR_WIDE_TARGET_BLOCKS 1536
-#endif
-constexpr int kWideWinTokens = OSCAR_WIDE_WIN_TOKENS;
-constexpr int kWideTargetBlocks = OSCAR_WIDE_TARGET_BLOCKS;
+constexpr int kWideWinTokens = 512;
+constexpr int kWideTargetBlocks = 1536;
 
 // Linear fall of INT2 split sizes from the first split to the last: blocks
 // dispatched later start later, so they get less.  At the 32k shape 0.4
 // measured best (65.1 us per launch; 66.5 with equal splits, 65.9 with 0.6).
-#ifndef OSCAR_SPLIT_RAMP
-#define OSCAR_SPLIT_RAMP 0.4f
-#endif
-constexpr float kSplitRamp = OSCAR_SPLIT_RAMP;
+constexpr float kSplitRamp = 0.4f;
 
 int auto_int2_splits(int BH, int ntiles, int waves) {
   const int target_blocks = 1536 * 4 / std::max(1, waves);

@@ -147,7 +147,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   qpart += __shfl_xor(qpart, 16);
   qpart += __shfl_xor(qpart, 32);
   if (lane < 16) S.qsum[16 * wave + m] = qpart;
-  // (the first tile's barrier orders these writes before their reads)
+  // (read back below by other lanes of the same wave, after an LDS wait and a
+  // wave barrier)
 
   // ---- key tiles
   // accumulator layout (S and O): register i of a 16 x 16 block is row
@@ -161,6 +162,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   // needs no causal mask: every score in it is finite
   const int p_min = T - a.n + i0;
   // per-row q sums in registers (rows of this wave, written by this wave)
+  __builtin_amdgcn_s_waitcnt(kWaitLds);
   __builtin_amdgcn_wave_barrier();
   float qs[4];
 #pragma unroll
@@ -351,8 +353,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       softmax_tile(std::integral_constant<bool, false>{});
     else
       softmax_tile(std::integral_constant<bool, true>{});
-    // each wave reads back only the rows of p s_V it wrote: its shared-memory
-    // operations complete in issue order, so no block barrier is needed
+    // each wave reads back only the rows of p s_V it wrote, so no block
+    // barrier is needed: an LDS wait and a wave barrier order the lanes
+    __builtin_amdgcn_s_waitcnt(kWaitLds);
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_s_setprio(1);
     // O += (p s_V) V: A = rows of p s_V (tokens 32 ks + kq .. + 8), B = V^T

@@ -13,7 +13,9 @@ import os
 import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "liboscar_kv.so")
+# the in-tree build; OSCAR_KV_LIBRARY selects another build of the same library
+# (the sanitized host build of the CPU tests)
+LIB_PATH = os.environ.get("OSCAR_KV_LIBRARY") or os.path.join(_HERE, "liboscar_kv.so")
 
 OSCAR_OK = 0
 OSCAR_ERR_INVALID_ARG = -1

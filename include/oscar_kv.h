@@ -101,13 +101,24 @@ typedef struct {
 
 typedef struct oscar_kv oscar_kv;
 
-/* Create a cache for cfg on cfg->device.  Copies the rotations, allocates
+/* Create a cache for cfg on cfg->device (the serving configuration of
+ * "OSCAR-RotationZoo", "How to use" step 2: per-layer K and V rotation files,
+ * K/V clip ratios, prefix/recent window sizes, int2 cache with quantization
+ * group 128; "File format": one head_dim x head_dim matrix per layer).
+ * Copies the rotations, allocates
  * every plane for max_batch x max_context tokens per layer and zeroes the
  * metadata.  May synchronise the device (set-up, not the hot path).
  * Errors: INVALID_ARG (bad field, NULL cfg/out), OUT_OF_MEMORY, HIP. */
 int oscar_kv_create(const oscar_kv_config* cfg, oscar_kv** out);
 
-/* Append n_new tokens to sequences 0..batch-1 of `layer` (all sequences of a
+/* The append path: each new post-RoPE K/V vector is rotated by its layer's
+ * matrix ("OSCAR-LLAMACPP-Qwen3-4B-Thinking-2507-INT2-KV", "Files": the
+ * rotation sits in the graph after RoPE), clipped per 128-group by the clip
+ * ratio and quantized to 2 bits ("OSCAR-RotationZoo", "How to use" step 2;
+ * the article's "How the offline rotation is fit": clipping thresholds bound
+ * the values before rounding), with bf16 copies of the first and last
+ * positions (Qwen3-4B card, "Run" env-var table).
+ * Append n_new tokens to sequences 0..batch-1 of `layer` (all sequences of a
  * layer hold the same number of tokens T_l; the first append on a layer fixes
  * its batch, later calls must pass the same batch).
  *   k, v: device bf16 [batch][n_new][Hkv][D], post-RoPE, un-rotated.
@@ -118,7 +129,14 @@ int oscar_kv_create(const oscar_kv_config* cfg, oscar_kv** out);
 int oscar_kv_append(oscar_kv* kv, int32_t layer, const void* k, const void* v,
                     int32_t batch, int32_t n_new, hipStream_t stream);
 
-/* One decode step of attention for `layer` over all T_l cached tokens.
+/* Decode attention over the mixed INT2 + bf16 cache, read directly by a
+ * fused kernel (Qwen3-4B card, "Run": the fused INT2 + f16 flash-attention;
+ * the article's "How the offline rotation is fit": no dequantize-then-attend
+ * pass), q rotated by R_K so that q k^T is unchanged ("OSCAR-LLAMACPP-Gemma-
+ * 4-12B-it-INT2-KV", the rotation paragraph below "Folders"), the output
+ * un-rotated by R_V^T ("OSCAR-RotationZoo", "How to use": V is stored
+ * rotated, hence the flag that absorbs its rotation).
+ * One decode step of attention for `layer` over all T_l cached tokens.
  *   q:   device bf16 [batch][Hq][D], post-RoPE, un-rotated;
  *   out: device [batch][Hq][D] of out_dtype, un-rotated (o = o' @ R_V^T);
  *   softmax_scale <= 0 selects 1/sqrt(D).
@@ -191,7 +209,8 @@ int oscar_kv_decode_step(oscar_kv* kv, int32_t layer, const void* k, const void*
 int oscar_prefill_attn(oscar_kv* kv, int32_t layer, const void* q, void* out, int32_t out_dtype,
                        int32_t batch, int32_t n_q, float softmax_scale, hipStream_t stream);
 
-/* Free every device allocation of the handle.  destroy(NULL) is OK. */
+/* Free every device allocation of the handle (the cache the create call
+ * configured).  destroy(NULL) is OK. */
 int oscar_kv_destroy(oscar_kv* kv);
 
 /* Thread-local text of the last failure ("" if none). */

@@ -50,9 +50,10 @@ def test_headline_bytes_per_call():
 
 @pytest.mark.parametrize("T,n", [(16384, 4096), (100, 100), (50, 1), (7, 3)])
 def test_prefill_key_count(T, n):
-    """The causal keys of a chunk of n queries at the end of T positions."""
+    """The bench's count of the causal keys of a chunk of n queries at the end
+    of T positions, against counting them one query at a time."""
     keys = sum(T - n + i + 1 for i in range(n))
-    assert n * (T - n) + n * (n + 1) / 2 == keys
+    assert bench.prefill_attention_keys(T, n) == keys
 
 
 def test_bench_refuses_more_than_one_gpu():
