@@ -37,7 +37,12 @@ Readings taken where the pages are silent (each is listed in the design notes):
   * prefill attention: the queries of the last n cached positions attend
     causally over the cache as it stands (windows of the current length);
   * in-quant Hadamard: fp32(R @ H), H the orthonormal Sylvester Walsh-Hadamard
-    matrix of order 128 on each 128-group.
+    matrix of order 128 on each 128-group;
+  * Lloyd-Max codebook (the switch of [Article] "Installing OSCAR..." and the
+    LM_RATIO of "Where OSCAR loses"): the 4-level quantizer of least mean
+    squared error for a Gaussian source, laid on each 128-group's mean and
+    standard deviation, the deviation scaled by LM_RATIO (parity unpinned
+    against the real kernels, which are not available).
 Parity status of every function is in the function docstring ("pinned by").
 """
 from __future__ import annotations
@@ -177,6 +182,133 @@ def dequantize_rows(codes: np.ndarray, s16: np.ndarray, z16: np.ndarray, group: 
     return (c * s[..., None] + z[..., None]).reshape(rows, D)
 
 
+# ----------------------------------------------------------------------------
+# Lloyd-Max codebook ([Article] "Installing OSCAR and running a first Qwen3-8B
+# calibration": the SGLANG_LLOYD_MAX switch; "Where OSCAR loses, and the cases
+# it is the wrong tool for": LM_RATIO = 1.16; "OSCAR against KIVI, QuaRot and
+# RotateKV on the same benchmark": OSCAR with Lloyd-Max).  The pages name the
+# codebook and the ratio only; the reading here is the classical one: the
+# Gaussian Lloyd-Max levels placed on the group's mean, in units of the
+# group's standard deviation times the ratio.
+# ----------------------------------------------------------------------------
+
+CODEBOOK_UNIFORM = 0
+CODEBOOK_LLOYD_MAX = 1
+
+# The 4-level quantizer of least mean squared error for a unit Gaussian source
+# (Max's table: levels +-0.4528 and +-1.510, decision thresholds 0 and +-0.9816,
+# mean squared error 0.1175), to the four decimals the codebook uses.  The
+# thresholds are the midpoints of neighbouring levels.
+LLOYD_MAX_LEVELS = (-1.5104, -0.4528, 0.4528, 1.5104)
+LLOYD_MAX_THRESHOLD = 0.9816
+
+
+def _phi(x):
+    return np.exp(-0.5 * x * x) / math.sqrt(2.0 * math.pi)
+
+
+def _Phi(x):
+    return 0.5 * (1.0 + np.vectorize(math.erf)(np.asarray(x, np.float64) / math.sqrt(2.0)))
+
+
+def lloyd_max_gaussian(levels: int = 4, iters: int = 500):
+    """Lloyd's iteration for the `levels`-level quantizer of a unit Gaussian in
+    float64: thresholds = midpoints of neighbouring levels, each level = the
+    mean of the Gaussian over its cell, E[X | a < X < b] = (phi(a) - phi(b)) /
+    (Phi(b) - Phi(a)).  Returns (levels, thresholds, mean squared error).
+    Pinned by: Max's published 4-level values, symmetry, and a local minimum
+    of the error against perturbed levels."""
+    y = np.linspace(-1.5, 1.5, levels)
+    for _ in range(iters):
+        t = 0.5 * (y[1:] + y[:-1])
+        a = np.concatenate([[-np.inf], t])
+        b = np.concatenate([t, [np.inf]])
+        pa = np.where(np.isinf(a), 0.0, _phi(np.where(np.isinf(a), 0.0, a)))
+        pb = np.where(np.isinf(b), 0.0, _phi(np.where(np.isinf(b), 0.0, b)))
+        y = (pa - pb) / (_Phi(b) - _Phi(a))
+    t = 0.5 * (y[1:] + y[:-1])
+    return y, t, gaussian_quantizer_mse(y, t)
+
+
+def gaussian_quantizer_mse(y, t) -> float:
+    """E[(X - q(X))^2] for a unit Gaussian X, q mapping cell (t_{k-1}, t_k) to
+    y_k, in closed form: E[X^2 1_cell] - 2 y E[X 1_cell] + y^2 P(cell)."""
+    y = np.asarray(y, np.float64)
+    a = np.concatenate([[-np.inf], np.asarray(t, np.float64)])
+    b = np.concatenate([np.asarray(t, np.float64), [np.inf]])
+    fa = np.where(np.isinf(a), 0.0, _phi(np.where(np.isinf(a), 0.0, a)))
+    fb = np.where(np.isinf(b), 0.0, _phi(np.where(np.isinf(b), 0.0, b)))
+    P = _Phi(b) - _Phi(a)
+    m1 = fa - fb                                   # E[X 1_cell]
+    az = np.where(np.isinf(a), 0.0, a)
+    bz = np.where(np.isinf(b), 0.0, b)
+    m2 = P + az * fa - bz * fb                     # E[X^2 1_cell]
+    return float(np.sum(m2 - 2.0 * y * m1 + y * y * P))
+
+
+def tree_sum_f32(a: np.ndarray) -> np.ndarray:
+    """Sum over the last axis (a power of two) in float32, pairwise in a fixed
+    order: first element i with element i + n/2, then the halves again, down
+    to one value (one rounding per add)."""
+    a = np.asarray(a, np.float32)
+    while a.shape[-1] > 1:
+        h = a.shape[-1] // 2
+        a = (a[..., :h] + a[..., h:]).astype(np.float32)
+    return a[..., 0]
+
+
+def quantize_rows_lloyd_max(x32: np.ndarray, group: int, ratio: float) -> QuantizedRows:
+    """Lloyd-Max INT2 quantization of fp32 rows, per group of G values, in IEEE
+    fp32 with one rounding per operation:
+        mu  = tree_sum(x) * (1/G)                 (G a power of two: exact scaling)
+        var = tree_sum((x - mu) * (x - mu)) * (1/G)
+        sd  = sqrt(var)                           (correctly rounded)
+        s   = r * sd, r = LM_RATIO as fp32;  s16, z16 = fp16(s), fp16(mu)
+        u   = (x - z) / s with z, s the stored fp16 values
+        c   = [u >= -tau] + [u >= 0] + [u >= tau], tau = fp32(0.9816)
+              (the nearest of the levels z + s l_k, l = LLOYD_MAX_LEVELS, ties
+              to the higher level); c = 0 everywhere if s16 == 0.
+    Pinned by: nearest-level brute force, the statistics against float64
+    mean and deviation, a hand-worked example in tests/golden, and the
+    levels against Lloyd's iteration.
+    """
+    x32 = canonical_zero(np.asarray(x32, dtype=np.float32))
+    rows, D = x32.shape
+    assert D % group == 0 and group & (group - 1) == 0
+    assert np.all(np.isfinite(x32)), "non-finite quantizer input is out of contract"
+    g = x32.reshape(rows, D // group, group)
+    inv_g = np.float32(1.0 / group)
+    mu = (tree_sum_f32(g) * inv_g).astype(np.float32)
+    d = (g - mu[..., None]).astype(np.float32)
+    var = (tree_sum_f32((d * d).astype(np.float32)) * inv_g).astype(np.float32)
+    sd = np.sqrt(var).astype(np.float32)
+    s = (np.float32(ratio) * sd).astype(np.float32)
+    assert np.all(np.abs(s) <= FP16_MAX) and np.all(np.abs(mu) <= FP16_MAX), \
+        "group statistics beyond fp16 metadata are out of contract"
+    s16 = s.astype(np.float16)
+    z16 = mu.astype(np.float16)
+    sf = s16.astype(np.float32)[..., None]
+    zf = z16.astype(np.float32)[..., None]
+    tau = np.float32(LLOYD_MAX_THRESHOLD)
+    with np.errstate(divide="ignore", invalid="ignore"):
+        u = ((g - zf).astype(np.float32) / sf).astype(np.float32)
+        c = (u >= -tau).astype(np.uint8) + (u >= 0).astype(np.uint8) + (u >= tau).astype(np.uint8)
+    c = np.where(sf == 0, 0, c)
+    return QuantizedRows(codes=c.reshape(rows, D).astype(np.uint8), s16=s16, z16=z16)
+
+
+def dequantize_rows_lloyd_max(codes: np.ndarray, s16: np.ndarray, z16: np.ndarray, group: int) -> np.ndarray:
+    """x_hat = z + s * l_c per group in float64, l_c the level of code c (the
+    fp32 value of LLOYD_MAX_LEVELS[c], widened)."""
+    codes = np.asarray(codes)
+    rows, D = codes.shape
+    lv = np.asarray(LLOYD_MAX_LEVELS, np.float32).astype(np.float64)
+    s = np.asarray(s16, dtype=np.float16).astype(np.float64)
+    z = np.asarray(z16, dtype=np.float16).astype(np.float64)
+    ell = lv[codes.astype(np.int64)].reshape(rows, D // group, group)
+    return (ell * s[..., None] + z[..., None]).reshape(rows, D)
+
+
 def pack_codes(codes: np.ndarray) -> np.ndarray:
     """4 codes per byte, little-endian 2-bit fields: code j -> byte j//4, bits 2*(j%4).
 
@@ -241,6 +373,7 @@ class OracleLayerPlanes:
     codes: np.ndarray | None
     s16: np.ndarray | None
     z16: np.ndarray | None
+    codebook: int = CODEBOOK_UNIFORM     # how codes map to values
 
 
 @dataclass
@@ -257,13 +390,17 @@ class OracleConfig:
     v_clip: float = 0.92
     k_dtype: int = KV_INT2
     v_dtype: int = KV_INT2
+    codebook: int = CODEBOOK_UNIFORM
+    lm_ratio: float = 1.16
 
 
 def append_planes(x_bits: np.ndarray, R32: np.ndarray, group: int, clip: float,
-                  dtype: int) -> OracleLayerPlanes:
+                  dtype: int, codebook: int = CODEBOOK_UNIFORM, lm_ratio: float = 1.16) -> OracleLayerPlanes:
     """Append step for a block of new tokens, bf16 bits [B, n, Hkv, D]:
     rotate (fp64), round to fp32 (quantizer input), bf16 window value, and,
-    for INT2, codes + fp16 scale/zero per group.  Returned in [B, Hkv, n, ...].
+    for INT2, codes + fp16 scale/zero per group (min/max quantizer with the
+    clip ratio, or the Lloyd-Max codebook with LM_RATIO).  Returned in
+    [B, Hkv, n, ...].
     """
     x32 = rotated_fp32(x_bits, R32)                      # [B, n, Hkv, D]
     x32 = np.ascontiguousarray(np.transpose(x32, (0, 2, 1, 3)))
@@ -271,12 +408,15 @@ def append_planes(x_bits: np.ndarray, R32: np.ndarray, group: int, clip: float,
     win = f32_to_bf16_bits(x32)
     if dtype == KV_BF16:
         return OracleLayerPlanes(x32, win, None, None, None)
-    q = quantize_rows(x32.reshape(-1, D), group, clip)
+    if codebook == CODEBOOK_LLOYD_MAX:
+        q = quantize_rows_lloyd_max(x32.reshape(-1, D), group, lm_ratio)
+    else:
+        q = quantize_rows(x32.reshape(-1, D), group, clip)
     return OracleLayerPlanes(
         x32, win,
         q.codes.reshape(B, H, n, D),
         q.s16.reshape(B, H, n, D // group),
-        q.z16.reshape(B, H, n, D // group))
+        q.z16.reshape(B, H, n, D // group), codebook)
 
 
 def _cat(a, b, axis=2):
@@ -307,8 +447,8 @@ class OracleKVCache:
 
     def append(self, layer: int, k_bits: np.ndarray, v_bits: np.ndarray) -> None:
         c = self.cfg
-        nk = append_planes(k_bits, self.rot_k[layer], c.group_size, c.k_clip, c.k_dtype)
-        nv = append_planes(v_bits, self.rot_v[layer], c.group_size, c.v_clip, c.v_dtype)
+        nk = append_planes(k_bits, self.rot_k[layer], c.group_size, c.k_clip, c.k_dtype, c.codebook, c.lm_ratio)
+        nv = append_planes(v_bits, self.rot_v[layer], c.group_size, c.v_clip, c.v_dtype, c.codebook, c.lm_ratio)
         self.k[layer] = nk if self.k[layer] is None else _join(self.k[layer], nk)
         self.v[layer] = nv if self.v[layer] is None else _join(self.v[layer], nv)
 
@@ -321,7 +461,7 @@ class OracleKVCache:
 
 def _join(a: OracleLayerPlanes, b: OracleLayerPlanes) -> OracleLayerPlanes:
     return OracleLayerPlanes(_cat(a.x32, b.x32), _cat(a.win, b.win), _cat(a.codes, b.codes),
-                             _cat(a.s16, b.s16), _cat(a.z16, b.z16))
+                             _cat(a.s16, b.s16), _cat(a.z16, b.z16), a.codebook)
 
 
 # ----------------------------------------------------------------------------
@@ -341,7 +481,8 @@ def mixed_values(planes: OracleLayerPlanes, b: int, h: int, T: int, N: int, M: i
     if dtype == KV_BF16:
         return win
     hp = high_precision_mask(T, N, M)
-    deq = dequantize_rows(planes.codes[b, h, :T], planes.s16[b, h, :T], planes.z16[b, h, :T], group)
+    deq_fn = dequantize_rows_lloyd_max if planes.codebook == CODEBOOK_LLOYD_MAX else dequantize_rows
+    deq = deq_fn(planes.codes[b, h, :T], planes.s16[b, h, :T], planes.z16[b, h, :T], group)
     return np.where(hp[:, None], win, deq)
 
 
@@ -446,7 +587,8 @@ def prefill_attention(q_bits: np.ndarray, kp: OracleLayerPlanes, vp: OracleLayer
 def planes_from_storage(packed_codes: np.ndarray | None, meta_s16: np.ndarray | None,
                         meta_z16: np.ndarray | None, sink_bits: np.ndarray,
                         ring_bits: np.ndarray, T: int, N: int, M: int,
-                        full_bits: np.ndarray | None = None) -> OracleLayerPlanes:
+                        full_bits: np.ndarray | None = None,
+                        codebook: int = CODEBOOK_UNIFORM) -> OracleLayerPlanes:
     """Build logical planes from a cache held as: packed codes [B, H, T, D/4],
     fp16 scale/zero [B, H, T, D/G], sink bf16 [B, H, N, D], recent ring bf16
     [B, H, M, D] (position t in slot t % M); or, for a BF16 plane, full bf16
@@ -466,7 +608,7 @@ def planes_from_storage(packed_codes: np.ndarray | None, meta_s16: np.ndarray | 
             win[:, :, t] = ring_bits[:, :, ring_slot(t, M)]
     return OracleLayerPlanes(np.zeros((B, H, T, D), np.float32), win, codes,
                              np.asarray(meta_s16[:, :, :T], np.float16),
-                             np.asarray(meta_z16[:, :, :T], np.float16))
+                             np.asarray(meta_z16[:, :, :T], np.float16), codebook)
 
 
 # ----------------------------------------------------------------------------

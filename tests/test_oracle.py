@@ -175,6 +175,126 @@ def test_quant_degenerate_groups():
     assert q.z16[2].view(np.uint16)[0] == 0
 
 
+# --------------------------------------------------------------------------- Lloyd-Max codebook
+
+
+def test_lloyd_max_levels_match_max_table():
+    """Lloyd's iteration on a unit Gaussian converges to the published 4-level
+    quantizer (Max 1960: levels +-0.4528, +-1.510; thresholds 0, +-0.9816;
+    mean squared error 0.1175), which the oracle's codebook constants carry."""
+    y, t, mse = orc.lloyd_max_gaussian()
+    np.testing.assert_allclose(y, _LM_TABLE, atol=6e-5)
+    np.testing.assert_allclose(t, [-0.9816, 0.0, 0.9816], atol=6e-5)
+    assert abs(mse - 0.1175) < 1e-4
+    np.testing.assert_array_equal(orc.LLOYD_MAX_LEVELS, _LM_TABLE)
+    assert orc.LLOYD_MAX_THRESHOLD == 0.9816
+    # the thresholds are the midpoints of the constants' levels
+    assert abs(0.5 * (_LM_TABLE[2] + _LM_TABLE[3]) - orc.LLOYD_MAX_THRESHOLD) < 1e-12
+
+
+def test_gaussian_quantizer_mse_closed_form():
+    """The closed-form error against numerical integration, and a local
+    minimum at the Lloyd-Max levels (perturbing any level raises it)."""
+    from scipy import integrate, stats
+    y = np.array(_LM_TABLE)
+    t = 0.5 * (y[1:] + y[:-1])
+    q = lambda x: y[np.searchsorted(t, x)]
+    num = integrate.quad(lambda x: (x - q(x)) ** 2 * stats.norm.pdf(x), -12, 12,
+                         points=list(t), limit=200)[0]
+    assert abs(orc.gaussian_quantizer_mse(y, t) - num) < 1e-9
+    y0, t0, m0 = orc.lloyd_max_gaussian()
+    for k in range(4):
+        for dv in (-0.01, 0.01):
+            yy = y0.copy()
+            yy[k] += dv
+            assert orc.gaussian_quantizer_mse(yy, t0) > m0
+
+
+def test_lloyd_max_worked_example():
+    gd = _read_golden("lloyd_max_worked_example.txt")
+    G = int(gd["group"][0])
+    x = np.array([float(v) for v in gd["x"]], np.float32)[None]
+    q = orc.quantize_rows_lloyd_max(x, G, float(gd["ratio"][0]))
+    assert float(q.s16[0, 0]) == float(gd["scale"][0])
+    assert float(q.z16[0, 0]) == float(gd["zero"][0])
+    np.testing.assert_array_equal(q.codes[0], [int(v) for v in gd["codes"]])
+    xh = orc.dequantize_rows_lloyd_max(q.codes, q.s16, q.z16, G)[0]
+    np.testing.assert_allclose(xh, [float(v) for v in gd["dequant"]], atol=6e-6)
+
+
+@pytest.mark.parametrize("ratio", [1.16, 1.0, 0.5])
+def test_lloyd_max_codes_are_nearest_levels(ratio):
+    """Brute force: every code is the nearest of z + s*level (fp64 distances,
+    the table's levels), s and z the stored fp16 values."""
+    G = 128
+    x = _rand_rows()
+    q = orc.quantize_rows_lloyd_max(x, G, ratio)
+    assert q.codes.max() <= 3
+    s = q.s16.astype(np.float64).repeat(G, axis=1)
+    z = q.z16.astype(np.float64).repeat(G, axis=1)
+    levels = z[..., None] + s[..., None] * np.array(_LM_TABLE)[None, None, :]
+    dist = np.abs(x.astype(np.float64)[..., None] - levels)
+    best = dist.argmin(-1)
+    d_sorted = np.sort(dist, axis=-1)
+    near_tie = (d_sorted[..., 1] - d_sorted[..., 0]) <= 1e-6 * np.maximum(s, 1e-30)
+    ok = (q.codes == best) | near_tie
+    assert ok.all(), np.argwhere(~ok)[:5]
+
+
+def test_lloyd_max_statistics():
+    """mu and the step against float64 mean and (population) standard
+    deviation: equal within fp32 rounding before the fp16 store."""
+    G = 128
+    x = _rand_rows()
+    ratio = 1.16
+    q = orc.quantize_rows_lloyd_max(x, G, ratio)
+    g = x.reshape(x.shape[0], -1, G).astype(np.float64)
+    mu, sd = g.mean(-1), g.std(-1)
+    scale = np.abs(g).max(-1)
+    assert np.all(np.abs(q.z16.astype(np.float64) - mu) <= 2.0 ** -11 * np.abs(mu) + 1e-6 * scale)
+    s = q.s16.astype(np.float64)
+    assert np.all(np.abs(s - ratio * sd) <= 2.0 ** -11 * ratio * sd + 1e-5 * scale)
+    # population (divide by G), not sample (G - 1), deviation
+    assert np.median(np.abs(s / (ratio * g.std(-1, ddof=1)) - 1)) > 2e-3
+
+
+def test_lloyd_max_error_matches_gaussian_theory():
+    """On Gaussian groups the mean squared dequantization error per unit
+    variance is the quantizer's closed form for levels scaled by the ratio
+    (0.1175 at ratio 1): pins levels, step and dequantization together."""
+    g = np.random.default_rng(17)
+    x = g.standard_normal((4000, 128)).astype(np.float32) * 3.0 + 1.5
+    for ratio in (1.0, 1.16):
+        q = orc.quantize_rows_lloyd_max(x, 128, ratio)
+        xh = orc.dequantize_rows_lloyd_max(q.codes, q.s16, q.z16, 128)
+        err = np.mean((xh - x.astype(np.float64)) ** 2) / 9.0
+        y = ratio * np.array(_LM_TABLE)
+        want = orc.gaussian_quantizer_mse(y, 0.5 * (y[1:] + y[:-1]))
+        assert abs(err - want) < 0.004, (ratio, err, want)
+    assert want > 0.1175
+
+
+def test_lloyd_max_degenerate_groups():
+    x = np.zeros((3, 128), np.float32)
+    x[1] = 2.5
+    x[2] = -0.0
+    q = orc.quantize_rows_lloyd_max(x, 128, 1.16)
+    assert np.all(q.codes == 0)
+    assert np.all(q.s16 == 0)
+    assert float(q.z16[1, 0]) == 2.5
+    assert q.z16[2].view(np.uint16)[0] == 0
+
+
+def test_lloyd_max_group_size():
+    """Two groups per row are quantized independently."""
+    x = _rand_rows(n=16, D=256)
+    q = orc.quantize_rows_lloyd_max(x, 128, 1.16)
+    for gi in range(2):
+        qq = orc.quantize_rows_lloyd_max(np.ascontiguousarray(x[:, 128 * gi:128 * (gi + 1)]), 128, 1.16)
+        np.testing.assert_array_equal(q.codes[:, 128 * gi:128 * (gi + 1)], qq.codes)
+        np.testing.assert_array_equal(q.s16[:, gi], qq.s16[:, 0])
+
+
 # --------------------------------------------------------------------------- windows
 
 
@@ -194,10 +314,10 @@ def test_window_sets(T, N, M):
 
 
 def _mk_cache(T, Hq=4, Hkv=2, D=128, N=3, M=4, seed=5, rot=True, k_dtype=0, v_dtype=0,
-              dist="normal", batch=2):
+              dist="normal", batch=2, codebook=0, lm_ratio=1.16):
     cfg = orc.OracleConfig(num_layers=1, batch=batch, num_q_heads=Hq, num_kv_heads=Hkv,
                            head_dim=D, sink_tokens=N, recent_tokens=M,
-                           k_dtype=k_dtype, v_dtype=v_dtype)
+                           k_dtype=k_dtype, v_dtype=v_dtype, codebook=codebook, lm_ratio=lm_ratio)
     rk = synth.rotations(1, D, seed, "rot_k") if rot else None
     rv = synth.rotations(1, D, seed, "rot_v") if rot else None
     c = orc.OracleKVCache(cfg, rk, rv)
@@ -281,10 +401,25 @@ def test_absorbed_v_rotation_output():
     np.testing.assert_allclose(oa @ Rv.T, want, rtol=1e-9, atol=1e-9)
 
 
-def _brute_attention(q_bits, k_bits, v_bits, rk, rv, Hkv, N, M, G, kclip, vclip, ntok=None):
+def _pairwise_f32(vals):
+    """fp32 sum of a power-of-two list, element i with i + n/2, halves again."""
+    a = [np.float32(v) for v in vals]
+    while len(a) > 1:
+        h = len(a) // 2
+        a = [np.float32(a[i] + a[i + h]) for i in range(h)]
+    return a[0]
+
+
+# the Gaussian Lloyd-Max levels as Max's table prints them (4 decimals)
+_LM_TABLE = (-1.5104, -0.4528, 0.4528, 1.5104)
+
+
+def _brute_attention(q_bits, k_bits, v_bits, rk, rv, Hkv, N, M, G, kclip, vclip, ntok=None,
+                     lm_ratio=None):
     """Pure-Python loops for tiny shapes, written straight from the definition.
     The windows are those of the full length T; the query attends over the
-    first ntok positions (all T by default)."""
+    first ntok positions (all T by default).  lm_ratio set: the Lloyd-Max
+    codebook (nearest of mu + s*level, s = ratio * sd) instead of min/max."""
     B, Hq, D = q_bits.shape
     T = k_bits.shape[1]
     ntok = T if ntok is None else ntok
@@ -303,6 +438,22 @@ def _brute_attention(q_bits, k_bits, v_bits, rk, rv, Hkv, N, M, G, kclip, vclip,
         res = []
         for g0 in range(0, D, G):
             grp = [float(v) + 0.0 for v in orc.canonical_zero(xr[g0:g0 + G])]
+            if lm_ratio is not None:
+                mu = np.float32(_pairwise_f32(grp) * np.float32(1.0 / G))
+                var = np.float32(_pairwise_f32([np.float32(np.float32(v - mu) * np.float32(v - mu))
+                                                for v in grp]) * np.float32(1.0 / G))
+                s = float(np.float16(np.float32(np.float32(lm_ratio) * np.float32(math.sqrt(var)))))
+                z = float(np.float16(mu))
+                lv = [float(np.float32(l)) for l in _LM_TABLE]
+                for val in grp:
+                    if s == 0.0:
+                        c = 0
+                    else:
+                        # nearest level, equal distances to the higher one
+                        d = [abs(val - (z + s * lv[cc])) for cc in range(4)]
+                        c = min(range(4), key=lambda cc: (d[cc], -cc))
+                    res.append(z + s * lv[c])
+                continue
             r = np.float32(clip)
             hi = np.float32(r * np.float32(max(grp)))
             lo = np.float32(r * np.float32(min(grp)))
@@ -342,6 +493,21 @@ def test_brute_force_tiny():
     got = c.attend(0, q)
     want = _brute_attention(q, k, v, rk[0], rv[0], Hkv, N, M, 128, 0.96, 0.92)
     np.testing.assert_allclose(got, want, rtol=1e-9, atol=1e-9)
+
+
+@pytest.mark.parametrize("ratio", [1.16, 1.0])
+def test_brute_force_tiny_lloyd_max(ratio):
+    """Lloyd-Max codebook, T <= 16, INT2 tokens present: vectorised oracle ==
+    loops that pick the nearest level by distance (not by the thresholds)."""
+    T, Hq, Hkv, D, N, M = 11, 4, 2, 128, 2, 3
+    c, q, k, v, rk, rv = _mk_cache(T, Hq, Hkv, D, N=N, M=M, batch=1, seed=23,
+                                   codebook=orc.CODEBOOK_LLOYD_MAX, lm_ratio=ratio)
+    got = c.attend(0, q)
+    want = _brute_attention(q, k, v, rk[0], rv[0], Hkv, N, M, 128, 0.96, 0.92, lm_ratio=ratio)
+    np.testing.assert_allclose(got, want, rtol=1e-9, atol=1e-9)
+    # and the codebook matters: the min/max quantizer gives another result
+    c2, *_ = _mk_cache(T, Hq, Hkv, D, N=N, M=M, batch=1, seed=23)
+    assert not np.allclose(c2.attend(0, q), got, rtol=1e-6, atol=0)
 
 
 def test_gqa_equals_replicated_mha():
