@@ -16,20 +16,27 @@ __global__ __launch_bounds__(64 * WAVES) void append_kernel(AppendArgs a) {
   const int g8 = (a.T_old >> 3) + (int)blockIdx.y;
   const int t_lo = NT == 1 ? a.T_old : max(a.T_old, g8 * 8);
   const int t_hi = NT == 1 ? a.T_old + 1 : min(a.T_new, g8 * 8 + 8);
-  append_block<D, WAVES, NT>(a, (int)blockIdx.x, blockIdx.z != 0, t_lo, t_hi, xs, part);
+  if (a.k.lm)
+    append_block<D, WAVES, NT, true>(a, (int)blockIdx.x, blockIdx.z != 0, t_lo, t_hi, xs, part);
+  else
+    append_block<D, WAVES, NT, false>(a, (int)blockIdx.x, blockIdx.z != 0, t_lo, t_hi, xs, part);
 }
 
 // One-token append at head_dim 512: grid (sequence x kv head, group, K/V).
 __global__ __launch_bounds__(256) void append_one_wide_kernel(AppendArgs a) {
   __shared__ float xs[512];
   __shared__ float part[4 * 128];
-  append_slice_block(a, (int)blockIdx.x, blockIdx.z != 0, (int)blockIdx.y, xs, part);
+  if (a.k.lm)
+    append_slice_block<true>(a, (int)blockIdx.x, blockIdx.z != 0, (int)blockIdx.y, xs, part);
+  else
+    append_slice_block<false>(a, (int)blockIdx.x, blockIdx.z != 0, (int)blockIdx.y, xs, part);
 }
 
-// Test hook: the quantizer of the multi-token append (the reciprocal fast path
-// with its exact fallback) on fp32 rows, canonical packing.
+// Test hook: the quantizer of the multi-token append (min/max codebook: the
+// reciprocal fast path with its exact fallback; Lloyd-Max codebook when lm) on
+// fp32 rows, canonical packing.
 template <int D>
-__global__ __launch_bounds__(64) void quantize_rows_kernel(const float* x, float clip, uint8_t* codes,
+__global__ __launch_bounds__(64) void quantize_rows_kernel(const float* x, float clip, int lm, uint8_t* codes,
                                                            uint32_t* meta) {
   constexpr int PER = D / 64;
   const int lane = threadIdx.x;
@@ -40,12 +47,19 @@ __global__ __launch_bounds__(64) void quantize_rows_kernel(const float* x, float
   uint32_t code[PER];
 #pragma unroll
   for (int g = 0; g < D / kGroup; ++g) {
-    const float mx = wave_max(fmaxf(v[2 * g], v[2 * g + 1]));
-    const float mn = wave_min(fminf(v[2 * g], v[2 * g + 1]));
-    const GroupQ q = group_params(mx, mn, clip);
-    const float inv = __builtin_amdgcn_rcpf(q.sf);
-    code[2 * g] = quant_code_fast(v[2 * g], q, inv);
-    code[2 * g + 1] = quant_code_fast(v[2 * g + 1], q, inv);
+    GroupQ q;
+    if (lm) {
+      q = lm_group_wave(v[2 * g], v[2 * g + 1], clip);
+      code[2 * g] = lm_code(v[2 * g], q);
+      code[2 * g + 1] = lm_code(v[2 * g + 1], q);
+    } else {
+      const float mx = wave_max(fmaxf(v[2 * g], v[2 * g + 1]));
+      const float mn = wave_min(fminf(v[2 * g], v[2 * g + 1]));
+      q = group_params(mx, mn, clip);
+      const float inv = __builtin_amdgcn_rcpf(q.sf);
+      code[2 * g] = quant_code_fast(v[2 * g], q, inv);
+      code[2 * g + 1] = quant_code_fast(v[2 * g + 1], q, inv);
+    }
     if (lane == 0) meta[row * (D / kGroup) + g] = q.packed;
   }
   store_canonical<PER>(code, lane, [&](int w) { return reinterpret_cast<uint32_t*>(codes + row * (D / 4) + 4 * w); });
@@ -146,13 +160,13 @@ hipError_t launch_append(const AppendArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
-hipError_t launch_quantize_rows(const float* x, int rows, int D, float clip, uint8_t* codes,
+hipError_t launch_quantize_rows(const float* x, int rows, int D, float clip, int lm, uint8_t* codes,
                                 uint32_t* meta, hipStream_t s) {
   if (rows == 0) return hipSuccess;
   if (D == 128)
-    hipLaunchKernelGGL(quantize_rows_kernel<128>, dim3(rows), dim3(64), 0, s, x, clip, codes, meta);
+    hipLaunchKernelGGL(quantize_rows_kernel<128>, dim3(rows), dim3(64), 0, s, x, clip, lm, codes, meta);
   else
-    hipLaunchKernelGGL(quantize_rows_kernel<512>, dim3(rows), dim3(64), 0, s, x, clip, codes, meta);
+    hipLaunchKernelGGL(quantize_rows_kernel<512>, dim3(rows), dim3(64), 0, s, x, clip, lm, codes, meta);
   return hipGetLastError();
 }
 

@@ -89,6 +89,52 @@ __device__ inline uint32_t quant_code_fast(float x, const GroupQ& g, float inv) 
   return (uint32_t)t;
 }
 
+// Lloyd-Max codebook (levels and threshold in common.h).  A group's
+// statistics are sums in one fixed pairwise order: element i with i + 64,
+// then with i + 32, ..., then with i + 1, each add rounded once, so that
+// every layout of the group's 128 values gives the same bits.
+
+// Sum of a group held two values per lane (dims lane and lane + 64): the first
+// add pairs i with i + 64 in-lane; lanes l and l ^ k then add the same two
+// values, so every lane ends with the same sum.
+__device__ inline float group_sum128(float a, float b) {
+  float s = as_f32(a + b);
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) s = as_f32(s + __shfl_xor(s, o));
+  return s;
+}
+
+// mean = sum / 128, variance = sum of squared deviations / 128 (division by a
+// power of two: exact), s = ratio * sqrt(variance) with the correctly rounded
+// square root; fp16 RNE of s and the mean.
+__device__ inline GroupQ lm_group_params(float mean, float sumsq, float ratio) {
+  const float var = as_f32(sumsq * 0.0078125f);
+  const float s = as_f32(ratio * as_f32(__builtin_sqrtf(var)));
+  const _Float16 s16 = (_Float16)s;
+  const _Float16 z16 = (_Float16)mean;
+  GroupQ g;
+  g.sf = (float)s16;
+  g.zf = (float)z16;
+  g.packed = (uint32_t)__builtin_bit_cast(uint16_t, s16) |
+             ((uint32_t)__builtin_bit_cast(uint16_t, z16) << 16);
+  return g;
+}
+
+// the level nearest to x among z + s * level(c): u = (x - z) / s (correctly
+// rounded), c = [u >= -tau] + [u >= 0] + [u >= tau]; 0 when s == 0.
+__device__ inline uint32_t lm_code(float x, const GroupQ& g) {
+  if (g.sf == 0.0f) return 0u;
+  const float u = as_f32(x - g.zf) / g.sf;
+  return (uint32_t)(u >= -kLmThreshold) + (uint32_t)(u >= 0.0f) + (uint32_t)(u >= kLmThreshold);
+}
+
+// Lloyd-Max parameters of a group held two per lane (dims lane, lane + 64).
+__device__ inline GroupQ lm_group_wave(float x0, float x1, float ratio) {
+  const float mean = as_f32(group_sum128(x0, x1) * 0.0078125f);
+  const float d0 = as_f32(x0 - mean), d1 = as_f32(x1 - mean);
+  return lm_group_params(mean, group_sum128(as_f32(d0 * d0), as_f32(d1 * d1)), ratio);
+}
+
 // Canonical packing through lane shuffles: lane l holds the code of dim
 // l + 64 i; word w (dims 16w..16w+15) is OR-reduced over the 16 lanes
 // 16 (w % 4) .. + 15 of element i = w / 4 and stored by its first lane at
@@ -200,7 +246,7 @@ __device__ inline float rot_sum(const float* part, int tk, int d) {
 // Wave 0's lane l owns dims l + 64 i, so it also owns the V tile bytes of those
 // dims for every token of the group (tiled-layout bytes are shared only among
 // tokens of one group of 8 at one dim, and one block handles the whole group).
-template <int D, int WAVES, int NT>
+template <int D, int WAVES, int NT, bool LM = false>
 __device__ inline void append_block(const AppendArgs& a, int bh, bool isv, int t_lo, int t_hi, float* xs,
                                     float* part) {
   constexpr int PER = D / 64;
@@ -270,11 +316,18 @@ __device__ inline void append_block(const AppendArgs& a, int bh, bool isv, int t
 #pragma unroll
     for (int g = 0; g < D / kGroup; ++g) {
       // group g = dims [128 g, 128 g + 128) = elements 2g, 2g+1 of every lane
-      const float mx = wave_max(fmaxf(x[2 * g], x[2 * g + 1]));
-      const float mn = wave_min(fminf(x[2 * g], x[2 * g + 1]));
-      const GroupQ q = group_params(mx, mn, P.clip);
-      code[2 * g] = quant_code(x[2 * g], q);
-      code[2 * g + 1] = quant_code(x[2 * g + 1], q);
+      GroupQ q;
+      if constexpr (LM) {
+        q = lm_group_wave(x[2 * g], x[2 * g + 1], P.clip);
+        code[2 * g] = lm_code(x[2 * g], q);
+        code[2 * g + 1] = lm_code(x[2 * g + 1], q);
+      } else {
+        const float mx = wave_max(fmaxf(x[2 * g], x[2 * g + 1]));
+        const float mn = wave_min(fminf(x[2 * g], x[2 * g + 1]));
+        q = group_params(mx, mn, P.clip);
+        code[2 * g] = quant_code(x[2 * g], q);
+        code[2 * g + 1] = quant_code(x[2 * g + 1], q);
+      }
       if (lane == 0) {
         P.meta[meta_index(bh, a.cap, t, g, D)] = q.packed;
         if (P.smax) atomicMax(reinterpret_cast<unsigned int*>(P.smax + bh), __float_as_uint(q.sf));
@@ -329,6 +382,7 @@ __device__ inline void rot_rows_cols2(const float* xs, int xstride, const float*
 // the group's statistics, codes, scale|zero word and window values follow.
 // Blocks of different groups touch disjoint bytes of every plane.  xs holds
 // 512 floats and part 4 * 128 floats of shared memory.
+template <bool LM = false>
 __device__ inline void append_slice_block(const AppendArgs& a, int bh, bool isv, int s, float* xs, float* part) {
   constexpr int D = 512;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
@@ -376,10 +430,19 @@ __device__ inline void append_slice_block(const AppendArgs& a, int bh, bool isv,
     P.ring[base + d0] = f32_to_bf16(x[0]);
     P.ring[base + d0 + 64] = f32_to_bf16(x[1]);
   }
-  const float mx = wave_max(fmaxf(x[0], x[1]));
-  const float mn = wave_min(fminf(x[0], x[1]));
-  const GroupQ q = group_params(mx, mn, P.clip);
-  const uint32_t code[2] = {quant_code(x[0], q), quant_code(x[1], q)};
+  GroupQ q;
+  uint32_t code[2];
+  if constexpr (LM) {
+    q = lm_group_wave(x[0], x[1], P.clip);
+    code[0] = lm_code(x[0], q);
+    code[1] = lm_code(x[1], q);
+  } else {
+    const float mx = wave_max(fmaxf(x[0], x[1]));
+    const float mn = wave_min(fminf(x[0], x[1]));
+    q = group_params(mx, mn, P.clip);
+    code[0] = quant_code(x[0], q);
+    code[1] = quant_code(x[1], q);
+  }
   if (lane == 0) {
     P.meta[meta_index(bh, a.cap, t, s, D)] = q.packed;
     if (P.smax) atomicMax(reinterpret_cast<unsigned int*>(P.smax + bh), __float_as_uint(q.sf));

@@ -105,6 +105,25 @@ __host__ __device__ inline uint16_t f32_to_bf16(float f) {
 }
 
 // ---------------------------------------------------------------------------
+// Lloyd-Max codebook: the 4-level quantizer of least mean squared error for a
+// unit Gaussian (Max's table: levels +-0.4528 and +-1.5104, decision
+// thresholds 0 and +-0.9816, the midpoints of neighbouring levels), placed on
+// a group's mean with the step s = LM_RATIO x the group's standard deviation
+// ("OSCAR: 2-bit KV Cache Quantization for SGLang and llama.cpp": the
+// Lloyd-Max switch in "Installing OSCAR and running a first Qwen3-8B
+// calibration", LM_RATIO = 1.16 in "Where OSCAR loses").  Code c stands for
+// z + s * level(c); the scale|zero word holds fp16 s and fp16 mean.
+// ---------------------------------------------------------------------------
+constexpr float kLmLevel0 = -1.5104f, kLmLevel1 = -0.4528f, kLmLevel2 = 0.4528f, kLmLevel3 = 1.5104f;
+constexpr float kLmThreshold = 0.9816f;
+
+__host__ __device__ inline float lm_level(uint32_t c) {
+  const float lo = (c & 1u) ? kLmLevel1 : kLmLevel0;
+  const float hi = (c & 1u) ? kLmLevel3 : kLmLevel2;
+  return (c & 2u) ? hi : lo;
+}
+
+// ---------------------------------------------------------------------------
 // launch arguments
 // ---------------------------------------------------------------------------
 
@@ -115,9 +134,10 @@ struct PlaneDev {
   uint16_t* ring;     // bf16 [B][Hkv][M][D]
   uint16_t* full;     // bf16 [B][Hkv][cap][D]; BF16 planes only
   float* smax;        // [B][Hkv] running max of stored scales (V only)
-  float clip;
+  float clip;         // clip ratio (min/max codebook) or LM_RATIO (Lloyd-Max codebook)
   int is_bf16;
   int tiled;          // 1 for the V code layout
+  int lm;             // 1: Lloyd-Max codebook (code c = z + s * lm_level(c)); 0: z + s * c
 };
 
 struct AppendArgs {
@@ -191,7 +211,7 @@ struct DecodeArgs {
 // launchers (defined in the .hip files); return hipGetLastError()
 hipError_t launch_append(const AppendArgs& a, hipStream_t s);
 hipError_t launch_append_prefill(const AppendArgs& a, hipStream_t s);   // n_new > 1, rotation on matrix cores
-hipError_t launch_quantize_rows(const float* x, int rows, int D, float clip, uint8_t* codes,
+hipError_t launch_quantize_rows(const float* x, int rows, int D, float clip, int lm, uint8_t* codes,
                                 uint32_t* meta, hipStream_t s);
 hipError_t launch_qrot(const QRotArgs& a, hipStream_t s);
 hipError_t launch_decode_valu(const DecodeArgs& a, int B, hipStream_t s);

@@ -12,7 +12,8 @@
 //
 // Kernels:
 //   qrot_kernel         q_rot = q @ R_K * scale * log2(e) (fp32) for the general kernel
-//   decode_valu_kernel  general split-K kernel: any head_dim / GQA / dtype,
+//   decode_valu_kernel  general split-K kernel: any head_dim / GQA / dtype /
+//                       codebook (the only one for the Lloyd-Max codebook),
 //                       per-token precision chosen by position
 //   decode_mfma_kernel  head_dim 128, 4 or 8 query heads per kv head, INT2 K and
 //                       V: one launch per decode step (the step's append, q
@@ -104,6 +105,12 @@ __global__ __launch_bounds__(256) void qrot_kernel(QRotArgs a) {
 // general VALU split-K kernel
 // ---------------------------------------------------------------------------
 
+// value of code c in units of the group's step: c (min/max codebook) or the
+// Lloyd-Max level
+__device__ inline float code_value(const PlaneDev& P, uint32_t c) {
+  return P.lm ? lm_level(c) : (float)c;
+}
+
 template <int D>
 __device__ inline void load_row_values(const PlaneDev& P, int bh, int t, int T, int N, int M, int cap,
                                        int d0, int n, float* out) {
@@ -130,13 +137,13 @@ __device__ inline void load_row_values(const PlaneDev& P, int bh, int t, int T, 
     for (int i = 0; i < n; i += 16) {
       const uint32_t w = *reinterpret_cast<const uint32_t*>(P.codes + kcode_byte(bh, cap, t, (d0 + i) / 4, D));
 #pragma unroll
-      for (int k = 0; k < 16; ++k) out[i + k] = __builtin_fmaf(s, (float)((w >> (2 * k)) & 3u), z);
+      for (int k = 0; k < 16; ++k) out[i + k] = __builtin_fmaf(s, code_value(P, (w >> (2 * k)) & 3u), z);
     }
   } else {
     for (int i = 0; i < n; ++i) {
       int bit;
       const size_t off = vcode_byte(bh, cap, t, d0 + i, D, &bit);
-      out[i] = __builtin_fmaf(s, (float)((P.codes[off] >> bit) & 3u), z);
+      out[i] = __builtin_fmaf(s, code_value(P, (P.codes[off] >> bit) & 3u), z);
     }
   }
 }
@@ -160,7 +167,7 @@ __device__ inline float load_value(const PlaneDev& P, int bh, int t, int T, int 
     const size_t off = vcode_byte(bh, cap, t, d, D, &bit);
     c = (P.codes[off] >> bit) & 3u;
   }
-  return __builtin_fmaf(s, (float)c, z);
+  return __builtin_fmaf(s, code_value(P, c), z);
 }
 
 __device__ inline int seg_token(const SegPlan& p, int vt) {

@@ -166,8 +166,13 @@ int validate_config(const oscar_kv_config* c) {
   if (c->max_context <= 0) return fail(OSCAR_ERR_INVALID_ARG, "max_context must be > 0");
   if (c->sink_tokens < 0 || c->recent_tokens < 0)
     return fail(OSCAR_ERR_INVALID_ARG, "window sizes must be >= 0");
-  if (!(c->k_clip > 0.0f && c->k_clip <= 1.0f) || !(c->v_clip > 0.0f && c->v_clip <= 1.0f))
+  if (c->codebook != OSCAR_CODEBOOK_UNIFORM && c->codebook != OSCAR_CODEBOOK_LLOYD_MAX)
+    return fail(OSCAR_ERR_INVALID_ARG, "codebook must be 0 (uniform) or 1 (Lloyd-Max)");
+  if (c->codebook == OSCAR_CODEBOOK_UNIFORM &&
+      (!(c->k_clip > 0.0f && c->k_clip <= 1.0f) || !(c->v_clip > 0.0f && c->v_clip <= 1.0f)))
     return fail(OSCAR_ERR_INVALID_ARG, "clip ratios must be in (0, 1]");
+  if (c->codebook == OSCAR_CODEBOOK_LLOYD_MAX && !(c->lm_ratio > 0.0f && c->lm_ratio <= 16.0f))
+    return fail(OSCAR_ERR_INVALID_ARG, "lm_ratio must be in (0, 16]");
   // the caller may have stored any integer in the enum fields: read their
   // bits as int32 (reading an out-of-range value as the enum type is undefined)
   int32_t kd, vd;
@@ -238,7 +243,8 @@ PlaneDev plane_dev(const oscar_kv* kv, const Plane& p, bool is_v) {
   d.ring = p.ring;
   d.full = p.full;
   d.smax = p.smax;
-  d.clip = is_v ? kv->cfg.v_clip : kv->cfg.k_clip;
+  d.lm = kv->cfg.codebook == OSCAR_CODEBOOK_LLOYD_MAX ? 1 : 0;
+  d.clip = d.lm ? kv->cfg.lm_ratio : (is_v ? kv->cfg.v_clip : kv->cfg.k_clip);
   d.is_bf16 = (is_v ? kv->cfg.v_dtype : kv->cfg.k_dtype) == OSCAR_KV_BF16;
   d.tiled = is_v ? 1 : 0;
   return d;
@@ -470,20 +476,22 @@ namespace {
 
 bool fast_shape(const oscar_kv* kv) {
   const auto& c = kv->cfg;
-  // the matrix-core kernel addresses one (sequence, kv head)'s code plane with
-  // 32-bit buffer offsets: cap * 32 bytes must fit
-  return kv->decode_impl == 0 && c.head_dim == 128 &&
+  // the matrix-core kernel takes the codes as their integer values (uniform
+  // codebook) and addresses one (sequence, kv head)'s code plane with 32-bit
+  // buffer offsets: cap * 32 bytes must fit
+  return kv->decode_impl == 0 && c.head_dim == 128 && c.codebook == OSCAR_CODEBOOK_UNIFORM &&
          (c.num_q_heads == 4 * c.num_kv_heads || c.num_q_heads == 8 * c.num_kv_heads) &&
          c.k_dtype == OSCAR_KV_INT2 && c.v_dtype == OSCAR_KV_INT2 && (long long)kv->cap * 32 <= INT32_MAX;
 }
 
 // head_dim 512 with at most 4 query heads per kv head, INT2 K, V INT2 or
-// bf16: the three-launch matrix-core path (32-bit buffer offsets: a (sequence,
+// bf16, uniform codebook: the three-launch matrix-core path (32-bit buffer offsets: a (sequence,
 // kv head)'s V plane, cap * 128 bytes INT2 or cap * 1024 bytes bf16, must fit)
 bool wide_shape(const oscar_kv* kv) {
   const auto& c = kv->cfg;
   const int gq = c.num_q_heads / c.num_kv_heads;
-  return kv->decode_impl == 0 && c.head_dim == 512 && (gq == 1 || gq == 2 || gq == 4) &&
+  return kv->decode_impl == 0 && c.head_dim == 512 && c.codebook == OSCAR_CODEBOOK_UNIFORM &&
+         (gq == 1 || gq == 2 || gq == 4) &&
          c.k_dtype == OSCAR_KV_INT2 && (long long)kv->cap * (c.v_dtype == OSCAR_KV_BF16 ? 1024 : 128) <= INT32_MAX;
 }
 
@@ -759,6 +767,8 @@ int oscar_prefill_attn(oscar_kv* kv, int32_t layer, const void* q, void* out, in
   const Layer& L = kv->layers[layer];
   const auto& c = kv->cfg;
   if (c.head_dim != 128) return fail(OSCAR_ERR_UNSUPPORTED, "prefill attention needs head_dim 128");
+  if (c.codebook != OSCAR_CODEBOOK_UNIFORM)
+    return fail(OSCAR_ERR_UNSUPPORTED, "prefill attention needs the uniform codebook");
   if (64 % (c.num_q_heads / c.num_kv_heads) != 0)
     return fail(OSCAR_ERR_UNSUPPORTED, "prefill attention needs a power-of-two number of query heads per kv head");
   if (L.T == 0) return fail(OSCAR_ERR_INVALID_ARG, "layer holds no tokens");
@@ -960,7 +970,19 @@ int oscar_quantize_rows(const float* x, int32_t rows, int32_t D, int32_t G, floa
   if (D != 128 && D != 512) return fail(OSCAR_ERR_UNSUPPORTED, "D must be 128 or 512");
   if (!(clip > 0.0f && clip <= 1.0f)) return fail(OSCAR_ERR_INVALID_ARG, "clip must be in (0, 1]");
   if (rows > 0 && (!x || !codes || !meta)) return fail(OSCAR_ERR_INVALID_ARG, "NULL pointer");
-  HIP_TRY(launch_quantize_rows(x, rows, D, clip, static_cast<uint8_t*>(codes), static_cast<uint32_t*>(meta),
+  HIP_TRY(launch_quantize_rows(x, rows, D, clip, 0, static_cast<uint8_t*>(codes), static_cast<uint32_t*>(meta),
+                               stream));
+  return OSCAR_OK;
+}
+
+int oscar_quantize_rows_lloyd_max(const float* x, int32_t rows, int32_t D, int32_t G, float ratio, void* codes,
+                                  void* meta, hipStream_t stream) {
+  if (rows < 0) return fail(OSCAR_ERR_INVALID_ARG, "rows must be >= 0");
+  if (G != kGroup) return fail(OSCAR_ERR_UNSUPPORTED, "group size must be 128");
+  if (D != 128 && D != 512) return fail(OSCAR_ERR_UNSUPPORTED, "D must be 128 or 512");
+  if (!(ratio > 0.0f && ratio <= 16.0f)) return fail(OSCAR_ERR_INVALID_ARG, "ratio must be in (0, 16]");
+  if (rows > 0 && (!x || !codes || !meta)) return fail(OSCAR_ERR_INVALID_ARG, "NULL pointer");
+  HIP_TRY(launch_quantize_rows(x, rows, D, ratio, 1, static_cast<uint8_t*>(codes), static_cast<uint32_t*>(meta),
                                stream));
   return OSCAR_OK;
 }

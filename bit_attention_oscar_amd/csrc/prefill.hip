@@ -42,6 +42,29 @@ __device__ inline float quad_min(float v) {
   return v;
 }
 
+__device__ inline float quad_xor1(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0xB1, 0xF, 0xF, false));
+}
+__device__ inline float quad_xor2(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x4E, 0xF, 0xF, false));
+}
+
+// Sum of a 128-value group held by a quad (lane p: values [32 p, 32 p + 32))
+// in the pairwise order of group_sum128: value i with i + 64 (lanes p and
+// p ^ 2), then with i + 32 (lanes p and p ^ 1), then the in-lane halves.
+__device__ inline float quad_sum128(const float (&x)[32]) {
+  float y[32];
+#pragma unroll
+  for (int j = 0; j < 32; ++j) y[j] = as_f32(x[j] + quad_xor2(x[j]));
+#pragma unroll
+  for (int j = 0; j < 32; ++j) y[j] = as_f32(y[j] + quad_xor1(y[j]));
+#pragma unroll
+  for (int h = 16; h >= 1; h >>= 1)
+#pragma unroll
+    for (int j = 0; j < h; ++j) y[j] = as_f32(y[j] + y[j + h]);
+  return y[0];
+}
+
 // Quantizer epilogue of one 64-token cache tile [t0, t0 + 64) of group g: the
 // rotated rows are in tile[64][132] (fp32).  Four lanes per row (thread tid:
 // row tid / 4, quad lane p = tid % 4); lane p takes the row's values [32 p,
@@ -56,6 +79,7 @@ __device__ inline float quad_min(float v) {
 // written whole.  Rows outside [T_old, T_new) are computed (their tile rows are
 // finite) but nothing of them is stored.  Returns this lane's largest stored V
 // scale (0 for K or bf16 planes).
+template <bool LM>
 __device__ float prefill_epilogue(const AppendArgs& a, const PlaneDev& P, float* dump, int bh, int b, int h, int g,
                                   int t0, float (*tile)[132], uint32_t (*crow)[8]) {
   const int D = a.D;
@@ -96,21 +120,38 @@ __device__ float prefill_epilogue(const AppendArgs& a, const PlaneDev& P, float*
   }
   if (P.is_bf16) return 0.0f;
 
-  float mx = x[0], mn = x[0];
-#pragma unroll
-  for (int j = 1; j < 32; ++j) {
-    mx = fmaxf(mx, x[j]);
-    mn = fminf(mn, x[j]);
-  }
-  mx = quad_max(mx);
-  mn = quad_min(mn);
-  const GroupQ q = group_params(mx, mn, P.clip);
-  const float inv = __builtin_amdgcn_rcpf(q.sf);
+  GroupQ q;
   uint32_t w0 = 0, w1 = 0;
+  if constexpr (LM) {
+    const float mean = as_f32(quad_sum128(x) * 0.0078125f);
+    float dd[32];
 #pragma unroll
-  for (int j = 0; j < 16; ++j) {
-    w0 |= quant_code_fast(x[j], q, inv) << (2 * j);
-    w1 |= quant_code_fast(x[16 + j], q, inv) << (2 * j);
+    for (int j = 0; j < 32; ++j) {
+      const float d = as_f32(x[j] - mean);
+      dd[j] = as_f32(d * d);
+    }
+    q = lm_group_params(mean, quad_sum128(dd), P.clip);
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      w0 |= lm_code(x[j], q) << (2 * j);
+      w1 |= lm_code(x[16 + j], q) << (2 * j);
+    }
+  } else {
+    float mx = x[0], mn = x[0];
+#pragma unroll
+    for (int j = 1; j < 32; ++j) {
+      mx = fmaxf(mx, x[j]);
+      mn = fminf(mn, x[j]);
+    }
+    mx = quad_max(mx);
+    mn = quad_min(mn);
+    q = group_params(mx, mn, P.clip);
+    const float inv = __builtin_amdgcn_rcpf(q.sf);
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      w0 |= quant_code_fast(x[j], q, inv) << (2 * j);
+      w1 |= quant_code_fast(x[16 + j], q, inv) << (2 * j);
+    }
   }
   float smax = 0.0f;
   if (live) {
@@ -183,7 +224,7 @@ struct PrefillSmem {
 // tile read the same input rows, so the block index is remapped to give the
 // four groups of one row tile consecutive slots on the same XCD: the rows come
 // from HBM once and from that L2 three times.
-template <int D>
+template <int D, bool LM>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void append_prefill_kernel(
     AppendArgs a, int row_tiles, int tiles_per_bh) {
   constexpr int KS = D / 32;           // reduction steps
@@ -310,7 +351,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
           for (int i = 0; i < 4; ++i) S.ep.tile[16 * rb + 4 * (lane >> 4) + i][16 * cb + m] = acc[rb][cb][i];
     }
     __syncthreads();
-    wsmax = fmaxf(wsmax, prefill_epilogue(a, P, dump, bh, b, h, g, th, S.ep.tile, S.ep.crow));
+    wsmax = fmaxf(wsmax, prefill_epilogue<LM>(a, P, dump, bh, b, h, g, th, S.ep.tile, S.ep.crow));
     __syncthreads();                     // the tile and codes are rewritten by the next quarter
   }
   wsmax = wave_max(wsmax);
@@ -327,10 +368,18 @@ hipError_t launch_append_prefill(const AppendArgs& a, hipStream_t s) {
   const int row_tiles = 2 * a.batch * a.Hkv * tiles;
   const int ng = a.D / 128;
   const unsigned blocks = (unsigned)((row_tiles + 7) / 8) * 8u * (unsigned)ng;
-  if (a.D == 128)
-    hipLaunchKernelGGL(append_prefill_kernel<128>, dim3(blocks), dim3(256), 0, s, a, row_tiles, tiles);
-  else
-    hipLaunchKernelGGL(append_prefill_kernel<512>, dim3(blocks), dim3(256), 0, s, a, row_tiles, tiles);
+  const bool lm = a.k.lm != 0;
+  if (a.D == 128) {
+    if (lm)
+      hipLaunchKernelGGL((append_prefill_kernel<128, true>), dim3(blocks), dim3(256), 0, s, a, row_tiles, tiles);
+    else
+      hipLaunchKernelGGL((append_prefill_kernel<128, false>), dim3(blocks), dim3(256), 0, s, a, row_tiles, tiles);
+  } else {
+    if (lm)
+      hipLaunchKernelGGL((append_prefill_kernel<512, true>), dim3(blocks), dim3(256), 0, s, a, row_tiles, tiles);
+    else
+      hipLaunchKernelGGL((append_prefill_kernel<512, false>), dim3(blocks), dim3(256), 0, s, a, row_tiles, tiles);
+  }
   return hipGetLastError();
 }
 

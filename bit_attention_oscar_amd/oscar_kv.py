@@ -28,6 +28,8 @@ KV_BF16 = 1
 OUT_F32 = 0
 OUT_BF16 = 1
 OUT_F16 = 2
+CODEBOOK_UNIFORM = 0
+CODEBOOK_LLOYD_MAX = 1
 
 EXPORTED = [
     "oscar_kv_create", "oscar_kv_append", "oscar_int2_decode_attn", "oscar_kv_destroy",
@@ -35,6 +37,7 @@ EXPORTED = [
     "oscar_kv_set_decode_impl", "oscar_kv_export", "oscar_kv_append_dump", "oscar_quantize_rows",
     "oscar_kv_profile_enable", "oscar_kv_profile_read", "oscar_stream_copy", "oscar_stream_read",
     "oscar_kv_decode_step", "oscar_prefill_attn", "oscar_kv_set_q_share", "oscar_int2_decode_attn_noalloc",
+    "oscar_quantize_rows_lloyd_max",
 ]
 
 
@@ -52,6 +55,7 @@ class oscar_kv_config(C.Structure):
         ("k_clip", C.c_float), ("v_clip", C.c_float), ("k_dtype", C.c_int32),
         ("v_dtype", C.c_int32), ("rot_k", C.POINTER(C.c_float)), ("rot_v", C.POINTER(C.c_float)),
         ("device", C.c_int32), ("absorb_v_rotation", C.c_int32), ("in_quant_hadamard", C.c_int32),
+        ("codebook", C.c_int32), ("lm_ratio", C.c_float),
     ]
 
 
@@ -76,6 +80,7 @@ def load_library(path: str = LIB_PATH) -> C.CDLL:
         "oscar_kv_export": ([vp, i32, i32, vp, vp, vp, vp], C.c_int),
         "oscar_kv_append_dump": ([vp, i32, vp, vp, i32, i32, vp, vp, vp], C.c_int),
         "oscar_quantize_rows": ([vp, i32, i32, i32, f32, vp, vp, vp], C.c_int),
+        "oscar_quantize_rows_lloyd_max": ([vp, i32, i32, i32, f32, vp, vp, vp], C.c_int),
         "oscar_kv_profile_enable": ([vp, i32], C.c_int),
         "oscar_kv_profile_read": ([vp, i32, C.POINTER(C.c_double), C.POINTER(C.c_int64)], C.c_int),
         "oscar_stream_copy": ([vp, vp, C.c_size_t, vp], C.c_int),
@@ -183,6 +188,11 @@ def oscar_quantize_rows(x, rows, D, G, clip, codes, meta, stream=None):
                                     _stream(stream)))
 
 
+def oscar_quantize_rows_lloyd_max(x, rows, D, G, ratio, codes, meta, stream=None):
+    _check(_lib.oscar_quantize_rows_lloyd_max(_ptr(x), rows, D, G, float(ratio), _ptr(codes), _ptr(meta),
+                                              _stream(stream)))
+
+
 def oscar_kv_profile_enable(kv, enable):
     _check(_lib.oscar_kv_profile_enable(kv, 1 if enable else 0))
 
@@ -217,7 +227,7 @@ class KVCache:
     def __init__(self, num_layers, max_batch, num_q_heads, num_kv_heads, head_dim, max_context,
                  sink_tokens, recent_tokens, group_size=128, k_clip=0.96, v_clip=0.92,
                  k_dtype=KV_INT2, v_dtype=KV_INT2, rot_k=None, rot_v=None, device=0, absorb_v_rotation=0,
-                 in_quant_hadamard=0):
+                 in_quant_hadamard=0, codebook=CODEBOOK_UNIFORM, lm_ratio=1.16):
         self.num_layers, self.max_batch = num_layers, max_batch
         self.num_q_heads, self.num_kv_heads, self.head_dim = num_q_heads, num_kv_heads, head_dim
         self.max_context, self.N, self.M, self.G = max_context, sink_tokens, recent_tokens, group_size
@@ -228,7 +238,7 @@ class KVCache:
         cfg = oscar_kv_config(num_layers, max_batch, num_q_heads, num_kv_heads, head_dim,
                               max_context, sink_tokens, recent_tokens, group_size, k_clip, v_clip,
                               k_dtype, v_dtype, fp(self._rk), fp(self._rv), device, absorb_v_rotation,
-                              in_quant_hadamard)
+                              in_quant_hadamard, codebook, lm_ratio)
         self.handle = oscar_kv_create(cfg)
 
     def close(self):

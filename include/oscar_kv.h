@@ -67,6 +67,19 @@ typedef enum { OSCAR_KV_INT2 = 0, OSCAR_KV_BF16 = 1 } oscar_kv_dtype;
 
 typedef enum { OSCAR_OUT_F32 = 0, OSCAR_OUT_BF16 = 1, OSCAR_OUT_F16 = 2 } oscar_out_dtype;
 
+/* How a 2-bit code maps to a value of its 128-group ("OSCAR: 2-bit KV Cache
+ * Quantization for SGLang and llama.cpp": the Lloyd-Max switch of "Installing
+ * OSCAR and running a first Qwen3-8B calibration" and LM_RATIO of "Where OSCAR
+ * loses, and the cases it is the wrong tool for").
+ *   UNIFORM:    z + s c, z = r min, s = r (max - min) / 3, r the clip ratio;
+ *   LLOYD_MAX:  z + s level(c), level = (-1.5104, -0.4528, 0.4528, 1.5104)
+ *               (the least-squared-error 4-level quantizer of a unit
+ *               Gaussian), z = the group's mean, s = LM_RATIO x its standard
+ *               deviation (population: sum of squares / 128); the code is the
+ *               nearest level (thresholds 0 and +-0.9816 on (x - z) / s,
+ *               ties to the higher code). */
+typedef enum { OSCAR_CODEBOOK_UNIFORM = 0, OSCAR_CODEBOOK_LLOYD_MAX = 1 } oscar_codebook;
+
 typedef struct {
   int32_t num_layers;
   int32_t max_batch;        /* sequences per layer                             */
@@ -97,6 +110,11 @@ typedef struct {
                               * with fast Walsh-Hadamard butterflies in fp64 and rounded
                               * once, so every later step (q rotation, window values, the
                               * quantizer, the V un-rotation by the transpose) is unchanged */
+  int32_t codebook;         /* oscar_codebook of both INT2 planes; 0 = UNIFORM       */
+  float lm_ratio;           /* LLOYD_MAX only: LM_RATIO in (0, 16]; pages: 1.16.  With
+                             * LLOYD_MAX, k_clip and v_clip are not used; decode
+                             * attention runs on the general (VALU) kernel and
+                             * oscar_prefill_attn returns UNSUPPORTED */
 } oscar_kv_config;
 
 typedef struct oscar_kv oscar_kv;
@@ -202,7 +220,7 @@ int oscar_kv_decode_step(oscar_kv* kv, int32_t layer, const void* k, const void*
  *   q:   device bf16 [batch][n_q][Hq][D], post-RoPE, un-rotated;
  *   out: device [batch][n_q][Hq][D] of out_dtype;
  *   softmax_scale <= 0 selects 1/sqrt(D).
- * head_dim 128 only (UNSUPPORTED otherwise).  Nothing is allocated; the cache
+ * head_dim 128 and the UNIFORM codebook only (UNSUPPORTED otherwise).  Nothing is allocated; the cache
  * is read only.
  * Errors: INVALID_ARG (including n_q < 1, n_q > T_l, batch != the layer's
  * batch), UNSUPPORTED, HIP. */
@@ -268,6 +286,11 @@ int oscar_kv_append_dump(oscar_kv* kv, int32_t layer, const void* k, const void*
  * Errors: INVALID_ARG (D or G unsupported, NULL pointer, rows < 0), HIP. */
 int oscar_quantize_rows(const float* x, int32_t rows, int32_t D, int32_t G, float clip,
                         void* codes, void* meta, hipStream_t stream);
+
+/* The same with the Lloyd-Max codebook and LM_RATIO `ratio` (0 < ratio <= 16):
+ * meta = {fp16 s, fp16 mean}. */
+int oscar_quantize_rows_lloyd_max(const float* x, int32_t rows, int32_t D, int32_t G, float ratio,
+                                  void* codes, void* meta, hipStream_t stream);
 
 /* Kernel timing with HIP events recorded on the caller's stream around the
  * launches of one kernel class: 0 = the INT2 split-K decode kernel, 1 = one

@@ -65,6 +65,8 @@ class Shape:
     dist: str = "normal"
     seed: int = 0
     outlier_scale: float = 8.0
+    codebook: int = 0          # 0: min/max with the clip ratios; 1: Lloyd-Max with lm_ratio
+    lm_ratio: float = 1.16
 
 
 def make_rotations(shape: Shape, kind: str):
@@ -131,21 +133,23 @@ def compare_planes(gp, op, T, N, M, label):
 def gpu_cache(ok, shape: Shape, rk, rv, max_context: int, absorb_v: int = 0, hadamard: int = 0):
     return ok.KVCache(shape.L, shape.B, shape.Hq, shape.Hkv, shape.D, max_context, shape.N, shape.M,
                       128, shape.k_clip, shape.v_clip, shape.k_dtype, shape.v_dtype, rk, rv, 0, absorb_v,
-                      hadamard)
+                      hadamard, shape.codebook, shape.lm_ratio)
 
 
 def oracle_cache(shape: Shape, rk, rv):
     cfg = orc.OracleConfig(num_layers=shape.L, batch=shape.B, num_q_heads=shape.Hq,
                            num_kv_heads=shape.Hkv, head_dim=shape.D, sink_tokens=shape.N,
                            recent_tokens=shape.M, k_clip=shape.k_clip, v_clip=shape.v_clip,
-                           k_dtype=shape.k_dtype, v_dtype=shape.v_dtype)
+                           k_dtype=shape.k_dtype, v_dtype=shape.v_dtype, codebook=shape.codebook,
+                           lm_ratio=shape.lm_ratio)
     return orc.OracleKVCache(cfg, rk, rv)
 
 
-def planes_from_export(exp: dict, T: int, N: int, M: int):
+def planes_from_export(exp: dict, T: int, N: int, M: int, codebook: int = 0):
     if "full" in exp:
         return orc.planes_from_storage(None, None, None, None, None, T, N, M, full_bits=exp["full"])
-    return orc.planes_from_storage(exp["codes"], exp["s16"], exp["z16"], exp["sink"], exp["ring"], T, N, M)
+    return orc.planes_from_storage(exp["codes"], exp["s16"], exp["z16"], exp["sink"], exp["ring"], T, N, M,
+                                   codebook=codebook)
 
 
 def oracle_on_exported(cache, layer, q_bits, shape: Shape, rk, rv, batch_idx=None, absorb_v=False):
@@ -154,8 +158,8 @@ def oracle_on_exported(cache, layer, q_bits, shape: Shape, rk, rv, batch_idx=Non
     ek, ev = cache.export(layer, 0), cache.export(layer, 1)
     sel = slice(None) if batch_idx is None else batch_idx
     sub = lambda e: {k: v[sel] for k, v in e.items()}
-    kp = planes_from_export(sub(ek), T, shape.N, shape.M)
-    vp = planes_from_export(sub(ev), T, shape.N, shape.M)
+    kp = planes_from_export(sub(ek), T, shape.N, shape.M, shape.codebook)
+    vp = planes_from_export(sub(ev), T, shape.N, shape.M, shape.codebook)
     D = shape.D
     Rk = rk[layer] if rk is not None else np.eye(D, dtype=np.float32)
     Rv = rv[layer] if rv is not None else np.eye(D, dtype=np.float32)

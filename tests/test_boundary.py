@@ -47,7 +47,7 @@ def _cfg(ok, **kw):
     ("head_dim", 96, -5), ("head_dim", 256, -5), ("group_size", 64, -5), ("max_context", 0, -1),
     ("sink_tokens", -1, -1), ("recent_tokens", -3, -1), ("k_clip", 0.0, -1), ("v_clip", 1.5, -1),
     ("k_dtype", 7, -1), ("num_q_heads", 64, -5), ("absorb_v_rotation", 2, -1),
-    ("in_quant_hadamard", 64, -1), ("in_quant_hadamard", 1, -1),
+    ("in_quant_hadamard", 64, -1), ("in_quant_hadamard", 1, -1), ("codebook", 2, -1), ("codebook", -1, -1),
 ])
 def test_create_rejects_bad_config(ok, field, value, code):
     cfg = _cfg(ok, **{field: value})
@@ -80,6 +80,32 @@ def test_null_arguments(ok):
 def test_quantize_rows_rejects(ok, rows, D, G, clip, code):
     rc = ok._lib.oscar_quantize_rows(None, rows, D, G, clip, None, None, None)
     assert rc == code, ok.oscar_last_error()
+
+
+@pytest.mark.parametrize("ratio,lm_ratio_code", [(0.0, -1), (-1.0, -1), (16.5, -1), (float("nan"), -1)])
+def test_lloyd_max_ratio_rejected(ok, ratio, lm_ratio_code):
+    """LM_RATIO outside (0, 16] is refused by create and by the quantizer hook;
+    with the Lloyd-Max codebook the clip ratios are not checked."""
+    cfg = _cfg(ok, codebook=1, lm_ratio=ratio, k_clip=0.0, v_clip=0.0)
+    h = C.c_void_p()
+    assert ok._lib.oscar_kv_create(C.byref(cfg), C.byref(h)) == lm_ratio_code
+    assert h.value is None
+    assert ok._lib.oscar_quantize_rows_lloyd_max(None, 4, 128, 128, ratio, None, None, None) == -1
+
+
+def test_lloyd_max_config_passes_validation(ok):
+    """A valid Lloyd-Max config (clip ratios zero: unused) gets past the argument
+    checks to device set-up."""
+    try:
+        import torch
+        if torch.cuda.is_available():
+            pytest.skip("a GPU is present")
+    except ImportError:
+        pass
+    cfg = _cfg(ok, codebook=1, lm_ratio=1.16, k_clip=0.0, v_clip=0.0)
+    h = C.c_void_p()
+    assert ok._lib.oscar_kv_create(C.byref(cfg), C.byref(h)) == ok.OSCAR_ERR_HIP
+    assert ok._lib.oscar_quantize_rows_lloyd_max(None, 0, 128, 128, 1.16, None, None, None) == ok.OSCAR_OK
 
 
 def test_quantize_rows_zero_rows_is_noop(ok):
