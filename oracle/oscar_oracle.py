@@ -42,7 +42,10 @@ Readings taken where the pages are silent (each is listed in the design notes):
     LM_RATIO of "Where OSCAR loses"): the 4-level quantizer of least mean
     squared error for a Gaussian source, laid on each 128-group's mean and
     standard deviation, the deviation scaled by LM_RATIO (parity unpinned
-    against the real kernels, which are not available).
+    against the real kernels, which are not available);
+  * ragged batches: each sequence holds its own number of tokens and its
+    windows follow its own length; a batch result is the one-sequence result
+    of every row.
 Parity status of every function is in the function docstring ("pinned by").
 """
 from __future__ import annotations
@@ -457,6 +460,47 @@ class OracleKVCache:
         return decode_attention(q_bits, self.k[layer], self.v[layer], self.rot_k[layer],
                                 self.rot_v[layer], c.num_kv_heads, c.sink_tokens,
                                 c.recent_tokens, c.group_size, c.k_dtype, c.v_dtype, scale)
+
+
+class OracleRaggedCache:
+    """A batch whose sequences hold different numbers of tokens (serving: each
+    request at its own length, "OSCAR-RotationZoo", "How to use" step 2, the
+    sglang server).  Each sequence is its own one-sequence cache: appends
+    address one sequence or every sequence of a batch, each at its own length,
+    and attention of sequence b reads its own T_b tokens with its own sink and
+    recent windows.  The result for a batch is, row by row, the one-sequence
+    result (there is no cross-sequence term in the method).
+    Pinned by: equal lengths give the batched cache's result bit for bit;
+    brute-force loops per sequence at lengths below, at and above N + M; a
+    code change in one sequence's only INT2 token moves that sequence alone."""
+
+    def __init__(self, cfg: OracleConfig, rot_k: np.ndarray | None, rot_v: np.ndarray | None):
+        self.cfg = cfg
+        one = OracleConfig(**{**cfg.__dict__, "batch": 1})
+        self.seqs = [OracleKVCache(one, rot_k, rot_v) for _ in range(cfg.batch)]
+
+    def length(self, layer: int, seq: int) -> int:
+        return self.seqs[seq].length(layer)
+
+    def append_seq(self, layer: int, seq: int, k_bits: np.ndarray, v_bits: np.ndarray) -> None:
+        """k_bits, v_bits: [n_new, Hkv, D] of sequence seq."""
+        self.seqs[seq].append(layer, k_bits[None], v_bits[None])
+
+    def append(self, layer: int, k_bits: np.ndarray, v_bits: np.ndarray) -> None:
+        """k_bits, v_bits: [batch, n_new, Hkv, D], sequence b at its own length."""
+        for b in range(k_bits.shape[0]):
+            self.append_seq(layer, b, k_bits[b], v_bits[b])
+
+    def reset_seq(self, seq: int) -> None:
+        c = self.seqs[seq]
+        c.k = [None] * len(c.k)
+        c.v = [None] * len(c.v)
+
+    def attend(self, layer: int, q_bits: np.ndarray, scale: float | None = None) -> np.ndarray:
+        """q_bits [batch, Hq, D] -> [batch, Hq, D]; every sequence of the batch
+        must hold at least one token."""
+        return np.concatenate([self.seqs[b].attend(layer, q_bits[b:b + 1], scale)
+                               for b in range(q_bits.shape[0])])
 
 
 def _join(a: OracleLayerPlanes, b: OracleLayerPlanes) -> OracleLayerPlanes:

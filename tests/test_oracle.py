@@ -510,6 +510,73 @@ def test_brute_force_tiny_lloyd_max(ratio):
     assert not np.allclose(c2.attend(0, q), got, rtol=1e-6, atol=0)
 
 
+# --------------------------------------------------------------------------- ragged batches
+
+
+def _ragged(lengths, Hq=4, Hkv=2, D=128, N=2, M=3, seed=31):
+    cfg = orc.OracleConfig(num_layers=1, batch=len(lengths), num_q_heads=Hq, num_kv_heads=Hkv, head_dim=D,
+                           sink_tokens=N, recent_tokens=M)
+    rk = synth.rotations(1, D, seed, "rot_k")
+    rv = synth.rotations(1, D, seed, "rot_v")
+    rc = orc.OracleRaggedCache(cfg, rk, rv)
+    mask = synth.outlier_mask(D, Hkv, seed, 0, "fixed", 2)
+    T = max(lengths)
+    k = synth.kv_bits(len(lengths), T, Hkv, D, seed, 0, "k", mask)
+    v = synth.kv_bits(len(lengths), T, Hkv, D, seed, 0, "v", mask)
+    for b, Tb in enumerate(lengths):
+        rc.append_seq(0, b, k[b, :Tb // 2], v[b, :Tb // 2])
+        rc.append_seq(0, b, k[b, Tb // 2:Tb], v[b, Tb // 2:Tb])
+    q = synth.q_bits(len(lengths), Hq, Hkv, D, seed, 0, mask)
+    return rc, q, k, v, rk, rv
+
+
+def test_ragged_equal_lengths_equals_batch():
+    """Equal lengths: the ragged cache is the batched cache, bit for bit."""
+    rc, q, k, v, rk, rv = _ragged([9, 9, 9])
+    cfg = orc.OracleConfig(num_layers=1, batch=3, num_q_heads=4, num_kv_heads=2, head_dim=128,
+                           sink_tokens=2, recent_tokens=3)
+    c = orc.OracleKVCache(cfg, rk, rv)
+    c.append(0, k[:, :4], v[:, :4])
+    c.append(0, k[:, 4:], v[:, 4:])
+    np.testing.assert_array_equal(rc.attend(0, q), c.attend(0, q))
+
+
+def test_ragged_each_sequence_brute_force():
+    """Lengths below, at and above N + M: every row equals pure-Python loops
+    over that sequence alone, with the windows of its own length."""
+    lengths = [3, 6, 11, 5]                      # N + M = 5: all-window, one INT2, several, none
+    rc, q, k, v, rk, rv = _ragged(lengths)
+    got = rc.attend(0, q)
+    for b, Tb in enumerate(lengths):
+        want = _brute_attention(q[b:b + 1], k[b:b + 1, :Tb], v[b:b + 1, :Tb], rk[0], rv[0], 2, 2, 3, 128,
+                                0.96, 0.92)
+        np.testing.assert_allclose(got[b:b + 1], want, rtol=1e-9, atol=1e-9)
+
+
+def test_ragged_windows_follow_own_length():
+    """Sequence 1 holds N + M + 1 tokens: its token N is its only INT2 token,
+    so changing that token's codes changes sequence 1's output and no other."""
+    rc, q, *_ = _ragged([4, 6, 11])
+    base = rc.attend(0, q)
+    kp = rc.seqs[1].k[0]
+    kp.codes[:, :, 2] = (kp.codes[:, :, 2] + 1) % 4
+    after = rc.attend(0, q)
+    assert not np.allclose(after[1], base[1], rtol=0, atol=0)
+    np.testing.assert_array_equal(after[[0, 2]], base[[0, 2]])
+    kp.codes[:, :, 2] = (kp.codes[:, :, 2] + 3) % 4
+    kp.codes[:, :, 3] = (kp.codes[:, :, 3] + 1) % 4         # token 3 is in the recent window
+    np.testing.assert_array_equal(rc.attend(0, q), base)
+
+
+def test_ragged_reset_sequence():
+    rc, q, k, v, *_ = _ragged([7, 10])
+    base = rc.attend(0, q)
+    rc.reset_seq(0)
+    assert rc.length(0, 0) == 0 and rc.length(0, 1) == 10
+    rc.append_seq(0, 0, k[0, :7], v[0, :7])
+    np.testing.assert_array_equal(rc.attend(0, q), base)
+
+
 def test_gqa_equals_replicated_mha():
     T, Hq, Hkv, D = 40, 8, 2, 128
     c, q, k, v, rk, rv = _mk_cache(T, Hq, Hkv, D, N=4, M=6)
