@@ -13,13 +13,15 @@ template <int D, int WAVES, int NT>
 __global__ __launch_bounds__(64 * WAVES) void append_kernel(AppendArgs a) {
   __shared__ float xs[NT * D];
   __shared__ float part[WAVES * NT * D];
-  const int g8 = (a.T_old >> 3) + (int)blockIdx.y;
-  const int t_lo = NT == 1 ? a.T_old : max(a.T_old, g8 * 8);
-  const int t_hi = NT == 1 ? a.T_old + 1 : min(a.T_new, g8 * 8 + 8);
+  const int2 tr = append_range(a, (int)blockIdx.x / a.Hkv);
+  const int g8 = (tr.x >> 3) + (int)blockIdx.y;
+  const int t_lo = NT == 1 ? tr.x : max(tr.x, g8 * 8);
+  const int t_hi = NT == 1 ? tr.x + 1 : min(tr.y, g8 * 8 + 8);
+  if (t_lo >= t_hi) return;            // ragged batch: this sequence has fewer 8-token groups
   if (a.k.lm)
-    append_block<D, WAVES, NT, true>(a, (int)blockIdx.x, blockIdx.z != 0, t_lo, t_hi, xs, part);
+    append_block<D, WAVES, NT, true>(a, (int)blockIdx.x, blockIdx.z != 0, t_lo, t_hi, tr.x, tr.y, xs, part);
   else
-    append_block<D, WAVES, NT, false>(a, (int)blockIdx.x, blockIdx.z != 0, t_lo, t_hi, xs, part);
+    append_block<D, WAVES, NT, false>(a, (int)blockIdx.x, blockIdx.z != 0, t_lo, t_hi, tr.x, tr.y, xs, part);
 }
 
 // One-token append at head_dim 512: grid (sequence x kv head, group, K/V).
@@ -63,6 +65,17 @@ __global__ __launch_bounds__(64) void quantize_rows_kernel(const float* x, float
     if (lane == 0) meta[row * (D / kGroup) + g] = q.packed;
   }
   store_canonical<PER>(code, lane, [&](int w) { return reinterpret_cast<uint32_t*>(codes + row * (D / 4) + 4 * w); });
+}
+
+__global__ __launch_bounds__(256) void set_lens_kernel(SetLensArgs a) {
+  const int i = (int)threadIdx.x;
+  if (i < a.n) a.lens[a.first + i] = a.vals[i];
+}
+
+hipError_t launch_set_lens(const SetLensArgs& a, hipStream_t s) {
+  if (a.n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(set_lens_kernel, dim3(1), dim3(kSetLensMax), 0, s, a);
+  return hipGetLastError();
 }
 
 // Canonical export of the stored K (isv = 0) or V codes: one thread per output byte.

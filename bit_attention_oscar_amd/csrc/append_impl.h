@@ -247,8 +247,8 @@ __device__ inline float rot_sum(const float* part, int tk, int d) {
 // dims for every token of the group (tiled-layout bytes are shared only among
 // tokens of one group of 8 at one dim, and one block handles the whole group).
 template <int D, int WAVES, int NT, bool LM = false>
-__device__ inline void append_block(const AppendArgs& a, int bh, bool isv, int t_lo, int t_hi, float* xs,
-                                    float* part) {
+__device__ inline void append_block(const AppendArgs& a, int bh, bool isv, int t_lo, int t_hi, int T_old, int T_new,
+                                    float* xs, float* part) {
   constexpr int PER = D / 64;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int b = bh / a.Hkv, h = bh - (bh / a.Hkv) * a.Hkv;
@@ -264,7 +264,7 @@ __device__ inline void append_block(const AppendArgs& a, int bh, bool isv, int t
       float v = 0.0f;
       if (tk < ntok) {
         const int t = t_lo + tk;
-        const size_t idx = (((size_t)b * a.n_new + (t - a.T_old)) * a.Hkv + h) * D + d;
+        const size_t idx = (((size_t)b * a.n_new + (t - T_old)) * a.Hkv + h) * D + d;
         v = bf16_to_f32(in[idx]);
       }
       xs[i] = v;
@@ -292,7 +292,7 @@ __device__ inline void append_block(const AppendArgs& a, int bh, bool isv, int t
 #pragma unroll
     for (int i = 0; i < PER; ++i) x[i] = rot_sum<D, WAVES, NT>(part, tk, lane + 64 * i);
     if (dump) {
-      const size_t base = (((size_t)b * a.n_new + (t - a.T_old)) * a.Hkv + h) * D;
+      const size_t base = (((size_t)b * a.n_new + (t - T_old)) * a.Hkv + h) * D;
 #pragma unroll
       for (int i = 0; i < PER; ++i) dump[base + lane + 64 * i] = x[i];
     }
@@ -307,7 +307,7 @@ __device__ inline void append_block(const AppendArgs& a, int bh, bool isv, int t
 #pragma unroll
       for (int i = 0; i < PER; ++i) P.sink[base + lane + 64 * i] = f32_to_bf16(x[i]);
     }
-    if (a.M > 0 && t >= a.N && t >= a.T_new - a.M) {
+    if (a.M > 0 && t >= a.N && t >= T_new - a.M) {
       const size_t base = row_offset(bh, a.M, t % a.M, D);
 #pragma unroll
       for (int i = 0; i < PER; ++i) P.ring[base + lane + 64 * i] = f32_to_bf16(x[i]);
@@ -391,7 +391,8 @@ __device__ inline void append_slice_block(const AppendArgs& a, int bh, bool isv,
   const uint16_t* in = isv ? a.vin : a.kin;
   const float* R = isv ? a.rv : a.rk;
   float* dump = isv ? a.vdump : a.kdump;
-  const int t = a.T_old;
+  const int2 tr = append_range(a, b);
+  const int t = tr.x;
   const size_t in_base = ((size_t)b * a.n_new * a.Hkv + h) * D;   // n_new == 1
   for (int i = tid; i < D; i += 256) xs[i] = bf16_to_f32(in[in_base + i]);
   __syncthreads();
@@ -425,7 +426,7 @@ __device__ inline void append_slice_block(const AppendArgs& a, int bh, bool isv,
     P.sink[base + d0] = f32_to_bf16(x[0]);
     P.sink[base + d0 + 64] = f32_to_bf16(x[1]);
   }
-  if (a.M > 0 && t >= a.N && t >= a.T_new - a.M) {
+  if (a.M > 0 && t >= a.N && t >= tr.y - a.M) {
     const size_t base = row_offset(bh, a.M, t % a.M, D);
     P.ring[base + d0] = f32_to_bf16(x[0]);
     P.ring[base + d0 + 64] = f32_to_bf16(x[1]);

@@ -151,7 +151,16 @@ struct AppendArgs {
   float* kdump;           // optional fp32 [batch][n_new][Hkv][D]
   float* vdump;
   int batch, n_new, Hkv, D, cap, N, M, T_old, T_new;
+  const int* lens;        // ragged batch: tokens of sequence b after this append ([batch], device);
+                          // null: every sequence goes from T_old to T_new
 };
+
+// Token counts of sequence b around an append: [T_old, T_new).
+__device__ inline int2 append_range(const AppendArgs& a, int b) {
+  if (!a.lens) return make_int2(a.T_old, a.T_new);
+  const int t1 = a.lens[b];
+  return make_int2(t1 - a.n_new, t1);
+}
 
 struct QRotArgs {
   const uint16_t* q;      // bf16 [B][Hq][D]
@@ -206,6 +215,10 @@ struct DecodeArgs {
   int win_blocks;          // window blocks of the launch (win.splits)
   int ring0;               // ring slot of the first recent token win.a1 (win.a1 % M)
   AppendArgs app;          // that append (n_new = 1); T above counts the new token
+  const int* lens;         // ragged batch: tokens of sequence b ([B], device, this launch's appended
+                           // token included); null: every sequence holds T.  With lens, T, plan and
+                           // win describe the longest sequence (grid and chunk sizes) and every
+                           // block derives its sequence's own token sets
 };
 
 // launchers (defined in the .hip files); return hipGetLastError()
@@ -231,6 +244,15 @@ hipError_t launch_stream_read(const void* src, size_t bytes, unsigned* out, hipS
 constexpr size_t kStaticScratchBytes = 16u << 20;
 constexpr size_t kCounterBytes = 256u << 10;          // 65536 (sequence, kv head) pairs
 hipError_t static_scratch(int device, hipStream_t stream, unsigned char** ptr, unsigned* epoch);
+// lens[first + i] = vals[i], i < n (n <= kSetLensMax): per-sequence token
+// counts written in stream order, the values travelling as kernel arguments
+constexpr int kSetLensMax = 256;
+struct SetLensArgs {
+  int* lens;
+  int first, n;
+  int vals[kSetLensMax];
+};
+hipError_t launch_set_lens(const SetLensArgs& a, hipStream_t s);
 hipError_t launch_export_codes(const uint8_t* stored, uint8_t* canon, int BH, int cap, int T, int D, int isv,
                                hipStream_t s);
 

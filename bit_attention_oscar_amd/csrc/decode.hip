@@ -202,7 +202,10 @@ __global__ __launch_bounds__(256) void decode_valu_kernel(DecodeArgs a) {
     for (int c = 0; c < DC; ++c) o[hq][c] = 0.0f;
   __syncthreads();
 
-  const int len = (a.plan.b0 - a.plan.a0) + (a.plan.b1 - a.plan.a1);
+  // tokens of this sequence (ragged batch: its own count; the plan then
+  // covers the longest sequence, [0, T) in one segment)
+  const int T = a.lens ? a.lens[b] : a.T;
+  const int len = a.lens ? T : (a.plan.b0 - a.plan.a0) + (a.plan.b1 - a.plan.a1);
   const int v_lo = split * a.plan.chunk;
   const int v_hi = min(v_lo + a.plan.chunk, len);
   constexpr int PART = D / 4;  // dims per thread in the score phase
@@ -218,7 +221,7 @@ __global__ __launch_bounds__(256) void decode_valu_kernel(DecodeArgs a) {
         const int t = seg_token(a.plan, vt);
         for (int c0 = 0; c0 < PART; c0 += 16) {
           float kv[16];
-          load_row_values<D>(a.k, bh, t, a.T, a.N, a.M, a.cap, part * PART + c0, 16, kv);
+          load_row_values<D>(a.k, bh, t, T, a.N, a.M, a.cap, part * PART + c0, 16, kv);
 #pragma unroll
           for (int hq = 0; hq < kMaxGq; ++hq) {
             if (hq < Gq) {
@@ -270,7 +273,7 @@ __global__ __launch_bounds__(256) void decode_valu_kernel(DecodeArgs a) {
       for (int c = 0; c < DC; ++c) {
         const int d = tid + 256 * c;
         if (d < D) {
-          const float vv = load_value<D>(a.v, bh, t, a.T, a.N, a.M, a.cap, d);
+          const float vv = load_value<D>(a.v, bh, t, T, a.N, a.M, a.cap, d);
 #pragma unroll
           for (int hq = 0; hq < kMaxGq; ++hq)
             if (hq < Gq) o[hq][c] = __builtin_fmaf(ps[hq][tk], vv, o[hq][c]);
@@ -604,13 +607,43 @@ __device__ inline int win_token(const SegPlan& w, int vt) {
   return vt < len0 ? w.a0 + vt : w.a1 + (vt - len0);
 }
 
+// The token sets of the block's sequence: its length, the end of its INT2
+// range [plan.a0, hi), its window segments [0, win.b0) and [win.a1, T) (with
+// the launch's chunk, splits and first slot) and the ring slot of win.a1.  In
+// a ragged batch every sequence has its own; the host's plan is that of the
+// longest, which sizes the grid, and blocks past a shorter sequence's tokens
+// find empty ranges.
+struct SeqView {
+  int T, hi, ring0;
+  SegPlan win;
+};
+
+__device__ inline SeqView seq_view(const DecodeArgs& a, int b) {
+  SeqView v;
+  v.win = a.win;
+  if (!a.lens) {
+    v.T = a.T;
+    v.hi = a.plan.b0;
+    v.ring0 = a.ring0;
+    return v;
+  }
+  const int T = a.lens[b];
+  v.T = T;
+  v.hi = max(a.N, T - a.M);
+  v.win.a0 = 0;
+  v.win.b0 = min(a.N, T);
+  v.win.a1 = min(T, max(a.N, T - a.M));        // below N tokens: empty
+  v.win.b1 = T;
+  v.ring0 = a.M > 0 ? v.win.a1 % a.M : 0;
+  return v;
+}
+
 // Row of window token t: sink row t, or ring slot t % M.  The recent tokens
-// are consecutive from win.a1, whose slot (ring0) the host computes, so no
-// division is needed.
-__device__ inline const uint16_t* win_row(const DecodeArgs& a, const PlaneDev& P, int bh, int t) {
+// are consecutive from win.a1, whose slot is ring0, so no division is needed.
+__device__ inline const uint16_t* win_row(const DecodeArgs& a, const SeqView& sv, const PlaneDev& P, int bh, int t) {
   constexpr int D = 128;
   if (t < a.N) return P.sink + row_offset(bh, a.N, t, D);
-  int slot = a.ring0 + (t - a.win.a1);
+  int slot = sv.ring0 + (t - sv.win.a1);
   if (slot >= a.M) slot -= a.M;
   return P.ring + row_offset(bh, a.M, slot, D);
 }
@@ -986,26 +1019,27 @@ struct WinRows {
   uint4 v[4];
 };
 
-__device__ inline int window_len(const DecodeArgs& a) {
-  return (a.win.b0 - a.win.a0) + (a.win.b1 - a.win.a1);
+__device__ inline int window_len(const SeqView& sv) {
+  return (sv.win.b0 - sv.win.a0) + (sv.win.b1 - sv.win.a1);
 }
 
-// the token appended by this launch when window block wblk holds it, else -1
-__device__ inline int window_new_token(const DecodeArgs& a, int wblk) {
-  const int len = window_len(a);
-  return (a.app_blocks > 0 && min(len, (wblk + 1) * a.win.chunk) == len) ? a.T - 1 : -1;
+// the token appended by this launch when window block wblk holds it (the
+// last window token), else -1
+__device__ inline int window_new_token(const DecodeArgs& a, const SeqView& sv, int wblk) {
+  const int len = window_len(sv);
+  return (a.app_blocks > 0 && wblk * sv.win.chunk < len && (wblk + 1) * sv.win.chunk >= len) ? sv.T - 1 : -1;
 }
 
-__device__ inline WinRows window_rows(const DecodeArgs& a, int bh, int vt0, int v_hi, int t_new) {
+__device__ inline WinRows window_rows(const DecodeArgs& a, const SeqView& sv, int bh, int vt0, int v_hi, int t_new) {
   const int tid = threadIdx.x, n = min(64, v_hi - vt0);
   WinRows r;
   const int tok = tid >> 2, part = tid & 3;
 #pragma unroll
   for (int i = 0; i < 4; ++i) r.k[i] = make_uint4(0, 0, 0, 0);
   if (tok < n) {
-    const int t = win_token(a.win, vt0 + tok);
+    const int t = win_token(sv.win, vt0 + tok);
     if (t != t_new) {
-      const uint4* rp = reinterpret_cast<const uint4*>(win_row(a, a.k, bh, t) + 32 * part);
+      const uint4* rp = reinterpret_cast<const uint4*>(win_row(a, sv, a.k, bh, t) + 32 * part);
 #pragma unroll
       for (int i = 0; i < 4; ++i) r.k[i] = rp[i];
     }
@@ -1016,17 +1050,17 @@ __device__ inline WinRows window_rows(const DecodeArgs& a, int bh, int vt0, int 
     const int tk = g + 16 * i;
     r.v[i] = make_uint4(0, 0, 0, 0);
     if (tk < n) {
-      const int t = win_token(a.win, vt0 + tk);
-      if (t != t_new) r.v[i] = *reinterpret_cast<const uint4*>(win_row(a, a.v, bh, t) + 8 * c);
+      const int t = win_token(sv.win, vt0 + tk);
+      if (t != t_new) r.v[i] = *reinterpret_cast<const uint4*>(win_row(a, sv, a.v, bh, t) + 8 * c);
     }
   }
   return r;
 }
 
 // The block's first pass of rows, issued before it waits for q.
-__device__ inline WinRows window_first_rows(const DecodeArgs& a, int bh, int wblk) {
-  const int v_lo = wblk * a.win.chunk;
-  return window_rows(a, bh, v_lo, min(window_len(a), v_lo + a.win.chunk), window_new_token(a, wblk));
+__device__ inline WinRows window_first_rows(const DecodeArgs& a, const SeqView& sv, int bh, int wblk) {
+  const int v_lo = wblk * sv.win.chunk;
+  return window_rows(a, sv, bh, v_lo, min(window_len(sv), v_lo + sv.win.chunk), window_new_token(a, sv, wblk));
 }
 
 // bf16 window tokens (sink + recent) of one (sequence, kv head), up to
@@ -1036,15 +1070,15 @@ __device__ inline WinRows window_first_rows(const DecodeArgs& a, int bh, int wbl
 // start; a later group loads its first pass's rows again, from cache, rather
 // than hold them in registers).  published: whether the launch's published q
 // is there.
-__device__ __forceinline__ void window_group(const DecodeArgs& a, int bh, int b, int hq0, int wblk, int t_new, FusedSmem& S,
-                             const WinRows& first);
+__device__ __forceinline__ void window_group(const DecodeArgs& a, const SeqView& sv, int bh, int b, int hq0, int wblk,
+                                             int t_new, FusedSmem& S, const WinRows& first);
 
 template <int G>
-__device__ void window_block(const DecodeArgs& a, int bh, int b, int h, int wblk, FusedSmem& S,
+__device__ void window_block(const DecodeArgs& a, const SeqView& sv, int bh, int b, int h, int wblk, FusedSmem& S,
                              const WinRows& first, bool published) {
   constexpr int D = 128;
   const int tid = threadIdx.x;
-  const int t_new = window_new_token(a, wblk);
+  const int t_new = window_new_token(a, sv, wblk);
   if (t_new >= 0) {
     for (int which = 0; which < 2; ++which) {
       const uint16_t* in = which ? a.app.vin : a.app.kin;
@@ -1060,23 +1094,23 @@ __device__ void window_block(const DecodeArgs& a, int bh, int b, int h, int wblk
     }
   }
   window_q_group(a, b, h, bh, 0, published, S);
-  window_group(a, bh, b, h * 4 * G, wblk, t_new, S, first);
+  window_group(a, sv, bh, b, h * 4 * G, wblk, t_new, S, first);
 #pragma unroll
   for (int g = 1; g < G; ++g) {
     __syncthreads();                  // shared memory is reused by the next group
-    const WinRows again = window_first_rows(a, bh, wblk);
+    const WinRows again = window_first_rows(a, sv, bh, wblk);
     window_q_group(a, b, h, bh, g, published, S);
-    window_group(a, bh, b, h * 4 * G + 4 * g, wblk, t_new, S, again);
+    window_group(a, sv, bh, b, h * 4 * G + 4 * g, wblk, t_new, S, again);
   }
 }
 
-__device__ __forceinline__ void window_group(const DecodeArgs& a, int bh, int b, int hq0, int wblk, int t_new, FusedSmem& S,
-                             const WinRows& first) {
+__device__ __forceinline__ void window_group(const DecodeArgs& a, const SeqView& sv, int bh, int b, int hq0, int wblk,
+                                             int t_new, FusedSmem& S, const WinRows& first) {
   constexpr int D = 128;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const int len = window_len(a);
-  const int v_lo = wblk * a.win.chunk;
-  const int v_hi = min(len, v_lo + a.win.chunk);
+  const int len = window_len(sv);
+  const int v_lo = wblk * sv.win.chunk;
+  const int v_hi = min(len, v_lo + sv.win.chunk);
   float* sc = S.scratch;               // [4][64]
   float* wm = S.scratch + 256;         // [4] running max
   float* wl = S.scratch + 260;         // [4] running sum
@@ -1096,13 +1130,13 @@ __device__ __forceinline__ void window_group(const DecodeArgs& a, int bh, int b,
   WinRows cur = first;
   for (int vt0 = v_lo; vt0 < v_hi; vt0 += 64) {
     const int n = min(64, v_hi - vt0);
-    if (vt0 != v_lo) cur = window_rows(a, bh, vt0, v_hi, t_new);
+    if (vt0 != v_lo) cur = window_rows(a, sv, bh, vt0, v_hi, t_new);
     {  // scores: 4 lanes per token, 32 dims each
       const int tok = tid >> 2, part = tid & 3;
       float dots[4] = {0.0f, 0.0f, 0.0f, 0.0f};
       if (tok < n) {
         uint4 us[4] = {cur.k[0], cur.k[1], cur.k[2], cur.k[3]};
-        if (win_token(a.win, vt0 + tok) == t_new) {
+        if (win_token(sv.win, vt0 + tok) == t_new) {
           const uint4* rp = reinterpret_cast<const uint4*>(&S.newtok[0][32 * part]);
           us[0] = rp[0]; us[1] = rp[1]; us[2] = rp[2]; us[3] = rp[3];
         }
@@ -1153,7 +1187,7 @@ __device__ __forceinline__ void window_group(const DecodeArgs& a, int bh, int b,
         const int tok = g + 16 * i;
         if (tok < n) {
           uint4 u = cur.v[i];
-          if (win_token(a.win, vt0 + tok) == t_new) u = *reinterpret_cast<const uint4*>(&S.newtok[1][8 * c]);
+          if (win_token(sv.win, vt0 + tok) == t_new) u = *reinterpret_cast<const uint4*>(&S.newtok[1][8 * c]);
           float x[8];
           bf16x8(u, x);
 #pragma unroll
@@ -1371,7 +1405,8 @@ __device__ inline Tile16<KS> load_tile16(const TileStreams& st, int t0, int koff
 
 // One INT2 split of the one-launch kernel (G head groups of 4 query heads).
 template <int G>
-__device__ void int2_split16(const DecodeArgs& a, int b, int h, int bh, int y, int split, FusedSmem& S) {
+__device__ void int2_split16(const DecodeArgs& a, const SeqView& sv, int b, int h, int bh, int y, int split,
+                             FusedSmem& S) {
   constexpr int D = 128, WPB = 4;
   constexpr bool KS = G == 1;                     // token sets in the K dimension
   constexpr int NOP = KS ? 8 : 4;                 // q operands per lane
@@ -1382,9 +1417,9 @@ __device__ void int2_split16(const DecodeArgs& a, int b, int h, int bh, int y, i
   const int grp = KS ? 0 : (c >> 2) & 1;          // head group of the column
   const int set = KS ? (c >> 2) & 1 : 0;          // token set of the column (KS)
   const bool live = grp < G;                      // the column carries a query head
-  const int lo = a.plan.a0, hi = a.plan.b0;       // INT2 token range
+  const int lo = a.plan.a0, hi = sv.hi;          // INT2 token range (empty in a short sequence)
   const int tile_first = lo >> 6;
-  const int ntiles = ((hi - 1) >> 6) - tile_first + 1;
+  const int ntiles = hi > lo ? ((hi - 1) >> 6) - tile_first + 1 : 0;
   // Split s covers tiles [start(s), start(s + 1)): shares of the range whose
   // weights fall linearly by a.split_ramp from the first split to the last
   // (blocks dispatched later start later and get less)
@@ -1781,23 +1816,25 @@ void decode_mfma_kernel(DecodeArgs a) {
   //   window blocks, the remaining INT2 splits.
   int y = (int)blockIdx.y;
   if (y < a.app_blocks) {
-    append_block<128, 4, 1>(a.app, bh, y == 1, a.app.T_old, a.app.T_old + 1, S.scratch, S.scratch + 128);
+    const int2 tr = append_range(a.app, b);
+    append_block<128, 4, 1>(a.app, bh, y == 1, tr.x, tr.x + 1, tr.x, tr.y, S.scratch, S.scratch + 128);
     return;
   }
+  const SeqView sv = seq_view(a, b);
   y -= a.app_blocks;
   // attention blocks: int2_lead INT2 splits, the window blocks, the other INT2
   // splits.  The lead splits fill the compute units first; the window blocks
   // start once slots free up, by when block 0 has published q.
   const int lead = a.int2_lead;
   if (y >= lead && y < lead + a.win_blocks) {
-    const WinRows rows = window_first_rows(a, bh, y - lead);   // in flight during the q wait
+    const WinRows rows = window_first_rows(a, sv, bh, y - lead);   // in flight during the q wait
     const bool published = window_q_ready(a, b, h, bh, y, S);
-    window_block<G>(a, bh, b, h, y - lead, S, rows, published);
+    window_block<G>(a, sv, bh, b, h, y - lead, S, rows, published);
     finish_block<G>(a, bh, S);
     return;
   }
   const int split = y < lead ? y : y - a.win_blocks;
-  int2_split16<G>(a, b, h, bh, y, split, S);
+  int2_split16<G>(a, sv, b, h, bh, y, split, S);
   finish_block<G>(a, bh, S);
 }
 
@@ -1929,8 +1966,11 @@ __device__ void wide_window_block(const DecodeArgs& a, int bh, int b, int h, int
   constexpr int D = 512, PT = 32, RI = PT / 4;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int tq = lane >> 4, c = lane & 15;
-  const int len0 = a.win.b0 - a.win.a0, len1 = a.win.b1 - a.win.a1;
-  const int nb0 = (len0 + a.win.chunk - 1) / a.win.chunk;
+  // the sequence's own segments; the split into sink and ring blocks is the
+  // launch's (that of the longest sequence)
+  const SeqView sv = seq_view(a, b);
+  const int len0 = sv.win.b0 - sv.win.a0, len1 = sv.win.b1 - sv.win.a1;
+  const int nb0 = ((a.win.b0 - a.win.a0) + a.win.chunk - 1) / a.win.chunk;
   const bool ring = wblk >= nb0;
   const int i_lo = (ring ? wblk - nb0 : wblk) * a.win.chunk;
   const int i_hi = min(ring ? len1 : len0, i_lo + a.win.chunk);
@@ -1946,8 +1986,8 @@ __device__ void wide_window_block(const DecodeArgs& a, int bh, int b, int h, int
   const __amdgpu_buffer_rsrc_t vp =
       VB ? plane_rsrc(a.v.full + row_offset(bh, a.cap, 0, D), a.cap * D * 2)
          : plane_rsrc(ring ? a.v.ring + row_offset(bh, a.M, 0, D) : a.v.sink + row_offset(bh, a.N, 0, D), nbytes);
-  const int pos0 = ring ? a.win.a1 + i_lo : a.win.a0 + i_lo;   // position of the block's first token
-  int row0 = ring ? a.ring0 + i_lo : a.win.a0 + i_lo;
+  const int pos0 = ring ? sv.win.a1 + i_lo : sv.win.a0 + i_lo;   // position of the block's first token
+  int row0 = ring ? sv.ring0 + i_lo : sv.win.a0 + i_lo;
   if (row0 >= rows) row0 -= rows;
   const int col = 128 * wave + 8 * c;
   // q of the slice (4 heads, fp32 x scale * log2 e) into shared memory; read
@@ -2129,9 +2169,9 @@ __device__ void wide_split_bf16v(const DecodeArgs& a, int bh, int b, int h, int 
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int blk = lane >> 2, j = lane & 3;
   const int tq = lane >> 4, c = lane & 15;
-  const int lo = a.plan.a0, hi = a.plan.b0;
+  const int lo = a.plan.a0, hi = a.lens ? max(a.N, a.lens[b] - a.M) : a.plan.b0;   // this sequence's INT2 range
   const int tile_first = lo >> 6;
-  const int ntiles = ((hi - 1) >> 6) - tile_first + 1;
+  const int ntiles = hi > lo ? ((hi - 1) >> 6) - tile_first + 1 : 0;
   const int S_ = a.plan.splits;
   auto split_start = [&](int s) -> int {
     if (s >= S_) return ntiles;
@@ -2309,9 +2349,9 @@ void decode_wide_kernel(DecodeArgs a) {
   }
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int blk = lane >> 2, j = lane & 3;
-  const int lo = a.plan.a0, hi = a.plan.b0;
+  const int lo = a.plan.a0, hi = a.lens ? max(a.N, a.lens[b] - a.M) : a.plan.b0;   // this sequence's INT2 range
   const int tile_first = lo >> 6;
-  const int ntiles = ((hi - 1) >> 6) - tile_first + 1;
+  const int ntiles = hi > lo ? ((hi - 1) >> 6) - tile_first + 1 : 0;
   auto split_start = [&](int s) -> int {
     const int S = a.plan.splits;
     if (s >= S) return ntiles;

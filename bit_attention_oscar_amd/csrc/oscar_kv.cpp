@@ -45,10 +45,16 @@ struct Plane {
   float* smax = nullptr;
 };
 
+// Token counts of a layer: every sequence has its own (lens, host side; the
+// host issues every append, so it knows them without reading the device).
+// T is the longest.  dlens is the device copy the kernels of a ragged batch
+// read; it matches lens for sequences [0, dev_synced).
 struct Layer {
   Plane k, v;
   int32_t T = 0;
-  int32_t batch = 0;
+  std::vector<int32_t> lens;
+  int* dlens = nullptr;
+  int32_t dev_synced = 0;
 };
 
 int round_up(int x, int m) { return (x + m - 1) / m * m; }
@@ -250,6 +256,57 @@ PlaneDev plane_dev(const oscar_kv* kv, const Plane& p, bool is_v) {
   return d;
 }
 
+// The planes of sequence `seq` alone, as those of a one-sequence batch: every
+// pointer advanced by seq x Hkv (sequence, kv head) strides of its layout.
+PlaneDev plane_dev_seq(const oscar_kv* kv, const Plane& p, bool is_v, int seq) {
+  PlaneDev d = plane_dev(kv, p, is_v);
+  const size_t bh = (size_t)seq * kv->cfg.num_kv_heads, D = kv->cfg.head_dim, cap = kv->cap;
+  if (d.codes) d.codes += bh * cap * (D / 4);           // K rows and V tiles: cap * D / 4 bytes per (b, h)
+  if (d.meta) d.meta += bh * (D / kGroup) * cap;
+  if (d.sink) d.sink += bh * kv->cfg.sink_tokens * D;
+  if (d.ring) d.ring += bh * kv->cfg.recent_tokens * D;
+  if (d.full) d.full += bh * cap * D;
+  if (d.smax) d.smax += bh;
+  return d;
+}
+
+// Lengths of sequences [0, batch): the longest, the shortest, all equal.
+struct BatchLens {
+  int max = 0, min = 0;
+  bool uniform = true;
+};
+
+BatchLens batch_lens(const Layer& L, int batch) {
+  BatchLens r;
+  r.max = r.min = L.lens[0];
+  for (int b = 1; b < batch; ++b) {
+    r.max = std::max(r.max, L.lens[b]);
+    r.min = std::min(r.min, L.lens[b]);
+  }
+  r.uniform = r.max == r.min;
+  return r;
+}
+
+// Writes lens[b] + add, b < batch, to the device copy (stream-ordered, the
+// values travel as kernel arguments, nothing waits).
+int upload_lens(Layer& L, int batch, int add, hipStream_t stream) {
+  for (int first = 0; first < batch; first += kSetLensMax) {
+    SetLensArgs a{};
+    a.lens = L.dlens;
+    a.first = first;
+    a.n = std::min(kSetLensMax, batch - first);
+    for (int i = 0; i < a.n; ++i) a.vals[i] = L.lens[first + i] + add;
+    HIP_TRY(launch_set_lens(a, stream));
+  }
+  return OSCAR_OK;
+}
+
+void advance_lens(Layer& L, int batch, int add, bool synced) {
+  for (int b = 0; b < batch; ++b) L.lens[b] += add;
+  L.T = *std::max_element(L.lens.begin(), L.lens.end());
+  L.dev_synced = synced ? batch : 0;
+}
+
 int check_layer(const oscar_kv* kv, int32_t layer) {
   if (!kv) return fail(OSCAR_ERR_INVALID_ARG, "handle is NULL");
   if (layer < 0 || layer >= kv->cfg.num_layers)
@@ -266,18 +323,26 @@ int do_append(oscar_kv* kv, int32_t layer, const void* k, const void* v, int32_t
     return fail(OSCAR_ERR_INVALID_ARG, "batch must be in [1, max_batch]");
   if (n_new <= 0) return fail(OSCAR_ERR_INVALID_ARG, "n_new must be > 0");
   Layer& L = kv->layers[layer];
-  if (L.T > 0 && batch != L.batch)
-    return fail(OSCAR_ERR_INVALID_ARG, "batch differs from the batch this layer was filled with");
-  if ((long long)L.T + n_new > kv->cfg.max_context)
+  const BatchLens bl = batch_lens(L, batch);
+  if ((long long)bl.max + n_new > kv->cfg.max_context)
     return fail(OSCAR_ERR_CAPACITY, "append of " + std::to_string(n_new) + " tokens to " +
-                                        std::to_string(L.T) + " exceeds max_context " +
+                                        std::to_string(bl.max) + " exceeds max_context " +
                                         std::to_string(kv->cfg.max_context));
-  const int groups = ((L.T + n_new - 1) >> 3) - (L.T >> 3) + 1;
-  if (groups > 65535) return fail(OSCAR_ERR_INVALID_ARG, "n_new too large for one call (max 524280)");
+  // a ragged batch sizes the grid for the worst alignment of a sequence's
+  // first new position (255 mod 256, so also 7 mod 8); each block then takes
+  // its own sequence's positions from the device lengths
+  const int T_old = bl.uniform ? bl.max : 255;
+  const int groups = ((T_old + n_new - 1) >> 3) - (T_old >> 3) + 1;
+  if (groups > 65535) return fail(OSCAR_ERR_INVALID_ARG, "n_new too large for one call (max 524272)");
   HIP_TRY(hipSetDevice(kv->cfg.device));
+  if (!bl.uniform) {
+    const int rc2 = upload_lens(L, batch, n_new, stream);
+    if (rc2) return rc2;
+  }
   AppendArgs a{};
   a.k = plane_dev(kv, L.k, false);
   a.v = plane_dev(kv, L.v, true);
+  a.lens = bl.uniform ? nullptr : L.dlens;
   a.kin = static_cast<const uint16_t*>(k);
   a.vin = static_cast<const uint16_t*>(v);
   const size_t DD = (size_t)kv->cfg.head_dim * kv->cfg.head_dim;
@@ -294,16 +359,63 @@ int do_append(oscar_kv* kv, int32_t layer, const void* k, const void* v, int32_t
   a.cap = kv->cap;
   a.N = kv->cfg.sink_tokens;
   a.M = kv->cfg.recent_tokens;
-  a.T_old = L.T;
-  a.T_new = L.T + n_new;
+  a.T_old = T_old;
+  a.T_new = T_old + n_new;
   const long ps = prof_begin(kv, 2, stream);
   if (n_new > 1)
     HIP_TRY(launch_append_prefill(a, stream));
   else
     HIP_TRY(launch_append(a, stream));
   prof_end(kv, 2, ps, stream);
-  L.T += n_new;
-  L.batch = batch;
+  advance_lens(L, batch, n_new, !bl.uniform);
+  return OSCAR_OK;
+}
+
+// Append n_new tokens to sequence `seq` alone: the append of a one-sequence
+// batch on that sequence's planes.
+int do_append_seq(oscar_kv* kv, int32_t layer, int32_t seq, const void* k, const void* v, int32_t n_new,
+                  hipStream_t stream) {
+  int rc = check_layer(kv, layer);
+  if (rc) return rc;
+  if (!k || !v) return fail(OSCAR_ERR_INVALID_ARG, "k/v pointer is NULL");
+  if (seq < 0 || seq >= kv->cfg.max_batch) return fail(OSCAR_ERR_INVALID_ARG, "seq must be in [0, max_batch)");
+  if (n_new <= 0) return fail(OSCAR_ERR_INVALID_ARG, "n_new must be > 0");
+  Layer& L = kv->layers[layer];
+  const int T0 = L.lens[seq];
+  if ((long long)T0 + n_new > kv->cfg.max_context)
+    return fail(OSCAR_ERR_CAPACITY, "append of " + std::to_string(n_new) + " tokens to " + std::to_string(T0) +
+                                        " exceeds max_context " + std::to_string(kv->cfg.max_context));
+  if (((T0 + n_new - 1) >> 3) - (T0 >> 3) + 1 > 65535)
+    return fail(OSCAR_ERR_INVALID_ARG, "n_new too large for one call (max 524272)");
+  HIP_TRY(hipSetDevice(kv->cfg.device));
+  AppendArgs a{};
+  a.k = plane_dev_seq(kv, L.k, false, seq);
+  a.v = plane_dev_seq(kv, L.v, true, seq);
+  a.kin = static_cast<const uint16_t*>(k);
+  a.vin = static_cast<const uint16_t*>(v);
+  const size_t DD = (size_t)kv->cfg.head_dim * kv->cfg.head_dim;
+  a.rk = kv->rk + layer * DD;
+  a.rv = kv->rv + layer * DD;
+  a.rk3 = kv->rk3 + layer * 3 * DD;
+  a.rv3 = kv->rv3 + layer * 3 * DD;
+  a.batch = 1;
+  a.n_new = n_new;
+  a.Hkv = kv->cfg.num_kv_heads;
+  a.D = kv->cfg.head_dim;
+  a.cap = kv->cap;
+  a.N = kv->cfg.sink_tokens;
+  a.M = kv->cfg.recent_tokens;
+  a.T_old = T0;
+  a.T_new = T0 + n_new;
+  const long ps = prof_begin(kv, 2, stream);
+  if (n_new > 1)
+    HIP_TRY(launch_append_prefill(a, stream));
+  else
+    HIP_TRY(launch_append(a, stream));
+  prof_end(kv, 2, ps, stream);
+  L.lens[seq] += n_new;
+  L.T = std::max(L.T, L.lens[seq]);
+  L.dev_synced = std::min(L.dev_synced, seq);
   return OSCAR_OK;
 }
 
@@ -383,6 +495,8 @@ int oscar_kv_create(const oscar_kv_config* cfg, oscar_kv** out) {
   for (int l = 0; l < L; ++l) {
     if ((rc = alloc_plane(kv, &kv->layers[l].k, cfg->k_dtype, false))) return bail(rc);
     if ((rc = alloc_plane(kv, &kv->layers[l].v, cfg->v_dtype, true))) return bail(rc);
+    kv->layers[l].lens.assign(cfg->max_batch, 0);
+    if ((rc = dev_alloc(kv, (void**)&kv->layers[l].dlens, (size_t)cfg->max_batch * sizeof(int)))) return bail(rc);
   }
   if ((rc = dev_alloc(kv, (void**)&kv->rk, L * DD * 4))) return bail(rc);
   if ((rc = dev_alloc(kv, (void**)&kv->rv, L * DD * 4))) return bail(rc);
@@ -468,6 +582,35 @@ int oscar_kv_append_dump(oscar_kv* kv, int32_t layer, const void* k, const void*
                          int32_t n_new, float* k_rot, float* v_rot, hipStream_t stream) {
   if (!k_rot || !v_rot) return fail(OSCAR_ERR_INVALID_ARG, "dump pointer is NULL");
   return do_append(kv, layer, k, v, batch, n_new, k_rot, v_rot, stream);
+}
+
+int oscar_kv_append_seq(oscar_kv* kv, int32_t layer, int32_t seq, const void* k, const void* v, int32_t n_new,
+                        hipStream_t stream) {
+  return do_append_seq(kv, layer, seq, k, v, n_new, stream);
+}
+
+int oscar_kv_reset_seq(oscar_kv* kv, int32_t seq, hipStream_t stream) {
+  if (!kv) return fail(OSCAR_ERR_INVALID_ARG, "handle is NULL");
+  if (seq < 0 || seq >= kv->cfg.max_batch) return fail(OSCAR_ERR_INVALID_ARG, "seq must be in [0, max_batch)");
+  HIP_TRY(hipSetDevice(kv->cfg.device));
+  const int Hkv = kv->cfg.num_kv_heads;
+  for (Layer& L : kv->layers) {
+    // the running V scale maximum restarts with the sequence's new tokens
+    if (L.v.smax) HIP_TRY(hipMemsetAsync(L.v.smax + (size_t)seq * Hkv, 0, Hkv * sizeof(float), stream));
+    L.lens[seq] = 0;
+    L.T = *std::max_element(L.lens.begin(), L.lens.end());
+    L.dev_synced = std::min(L.dev_synced, seq);
+  }
+  return OSCAR_OK;
+}
+
+int oscar_kv_seq_length(const oscar_kv* kv, int32_t layer, int32_t seq, int32_t* tokens) {
+  int rc = check_layer(kv, layer);
+  if (rc) return rc;
+  if (seq < 0 || seq >= kv->cfg.max_batch) return fail(OSCAR_ERR_INVALID_ARG, "seq must be in [0, max_batch)");
+  if (!tokens) return fail(OSCAR_ERR_INVALID_ARG, "tokens is NULL");
+  *tokens = kv->layers[layer].lens[seq];
+  return OSCAR_OK;
 }
 
 }  // extern "C"
@@ -563,10 +706,11 @@ int bind_scratch(oscar_kv* kv, const Scratch& sc, int batch, int nslots, DecodeA
 
 // Enqueue decode attention of `layer` over T tokens.  With `app` set (matrix-
 // core shapes only) the same launch also appends that one token, which is then
-// the last of the T tokens.
+// the last of the T tokens.  dlens (ragged batch): the device token counts of
+// the sequences, T then being the longest.
 int launch_decode(oscar_kv* kv, int32_t layer, const void* q, void* out, int32_t out_dtype, int32_t batch,
                   float softmax_scale, int T, const AppendArgs* app, hipStream_t stream,
-                  const Scratch& sc = Scratch()) {
+                  const Scratch& sc = Scratch(), const int* dlens = nullptr) {
   const Layer& L = kv->layers[layer];
   HIP_TRY(hipSetDevice(kv->cfg.device));
   const auto& c = kv->cfg;
@@ -593,6 +737,7 @@ int launch_decode(oscar_kv* kv, int32_t layer, const void* q, void* out, int32_t
   da.scale_log2 = scale * 1.4426950408889634f;
   da.app_blocks = app ? 2 : 0;
   if (app) da.app = *app;
+  da.lens = dlens;
   CombineArgs ca{};
   ca.rvT = kv->rvT + layer * DD;
   ca.out = out;
@@ -605,8 +750,9 @@ int launch_decode(oscar_kv* kv, int32_t layer, const void* q, void* out, int32_t
   const int BH = batch * Hkv;
 
   // token sets: sink [0, min(N,T)), recent [max(N, T-M), T), INT2 [N, T-M)
+  // (below N tokens the recent segment is empty: [T, T))
   const int sink_end = std::min(N, T);
-  const int rec_begin = std::max(N, T - M);
+  const int rec_begin = std::min(T, std::max(N, T - M));
   const int int2_lo = N, int2_hi = T - M;
   int rc = OSCAR_OK;
   const long pcall = sc.use_static ? -1 : prof_begin(kv, 1, stream);
@@ -732,49 +878,63 @@ int launch_decode(oscar_kv* kv, int32_t layer, const void* q, void* out, int32_t
   return OSCAR_OK;
 }
 
+// Decode attention of sequences [0, batch) over their current tokens: the
+// uniform launch, or for a ragged batch the device lengths (uploaded first
+// unless the device copy already holds them).
+int decode_attn(oscar_kv* kv, int32_t layer, const void* q, void* out, int32_t out_dtype, int32_t batch,
+                float softmax_scale, hipStream_t stream, Scratch sc) {
+  int rc = check_decode_args(kv, layer, q, out, out_dtype, softmax_scale);
+  if (rc) return rc;
+  if (batch <= 0 || batch > kv->cfg.max_batch) return fail(OSCAR_ERR_INVALID_ARG, "batch must be in [1, max_batch]");
+  Layer& L = kv->layers[layer];
+  const BatchLens bl = batch_lens(L, batch);
+  if (bl.min == 0) return fail(OSCAR_ERR_INVALID_ARG, "a sequence of the batch holds no tokens");
+  HIP_TRY(hipSetDevice(kv->cfg.device));
+  if (sc.use_static) HIP_TRY(static_scratch(kv->cfg.device, stream, &sc.base, &sc.epoch));
+  if (bl.uniform) return launch_decode(kv, layer, q, out, out_dtype, batch, softmax_scale, bl.max, nullptr, stream, sc);
+  if (L.dev_synced < batch) {
+    if ((rc = upload_lens(L, batch, 0, stream))) return rc;
+    L.dev_synced = batch;
+  }
+  return launch_decode(kv, layer, q, out, out_dtype, batch, softmax_scale, bl.max, nullptr, stream, sc, L.dlens);
+}
+
 }  // namespace
 
 extern "C" {
 
 int oscar_int2_decode_attn(oscar_kv* kv, int32_t layer, const void* q, void* out, int32_t out_dtype,
                            int32_t batch, float softmax_scale, hipStream_t stream) {
-  int rc = check_decode_args(kv, layer, q, out, out_dtype, softmax_scale);
-  if (rc) return rc;
-  const Layer& L = kv->layers[layer];
-  if (L.T == 0) return fail(OSCAR_ERR_INVALID_ARG, "layer holds no tokens");
-  if (batch != L.batch) return fail(OSCAR_ERR_INVALID_ARG, "batch differs from the layer's batch");
-  return launch_decode(kv, layer, q, out, out_dtype, batch, softmax_scale, L.T, nullptr, stream);
+  return decode_attn(kv, layer, q, out, out_dtype, batch, softmax_scale, stream, Scratch());
 }
 
 int oscar_int2_decode_attn_noalloc(oscar_kv* kv, int32_t layer, const void* q, void* out, int32_t out_dtype,
                                    int32_t batch, float softmax_scale, hipStream_t stream) {
-  int rc = check_decode_args(kv, layer, q, out, out_dtype, softmax_scale);
-  if (rc) return rc;
-  const Layer& L = kv->layers[layer];
-  if (L.T == 0) return fail(OSCAR_ERR_INVALID_ARG, "layer holds no tokens");
-  if (batch != L.batch) return fail(OSCAR_ERR_INVALID_ARG, "batch differs from the layer's batch");
-  HIP_TRY(hipSetDevice(kv->cfg.device));
   Scratch sc;
   sc.use_static = true;
-  HIP_TRY(static_scratch(kv->cfg.device, stream, &sc.base, &sc.epoch));
-  return launch_decode(kv, layer, q, out, out_dtype, batch, softmax_scale, L.T, nullptr, stream, sc);
+  return decode_attn(kv, layer, q, out, out_dtype, batch, softmax_scale, stream, sc);
 }
 
 int oscar_prefill_attn(oscar_kv* kv, int32_t layer, const void* q, void* out, int32_t out_dtype,
                        int32_t batch, int32_t n_q, float softmax_scale, hipStream_t stream) {
   int rc = check_decode_args(kv, layer, q, out, out_dtype, softmax_scale);
   if (rc) return rc;
-  const Layer& L = kv->layers[layer];
+  Layer& L = kv->layers[layer];
   const auto& c = kv->cfg;
   if (c.head_dim != 128) return fail(OSCAR_ERR_UNSUPPORTED, "prefill attention needs head_dim 128");
   if (c.codebook != OSCAR_CODEBOOK_UNIFORM)
     return fail(OSCAR_ERR_UNSUPPORTED, "prefill attention needs the uniform codebook");
   if (64 % (c.num_q_heads / c.num_kv_heads) != 0)
     return fail(OSCAR_ERR_UNSUPPORTED, "prefill attention needs a power-of-two number of query heads per kv head");
-  if (L.T == 0) return fail(OSCAR_ERR_INVALID_ARG, "layer holds no tokens");
-  if (batch != L.batch) return fail(OSCAR_ERR_INVALID_ARG, "batch differs from the layer's batch");
-  if (n_q < 1 || n_q > L.T) return fail(OSCAR_ERR_INVALID_ARG, "n_q must be in [1, tokens of the layer]");
+  if (batch <= 0 || batch > c.max_batch) return fail(OSCAR_ERR_INVALID_ARG, "batch must be in [1, max_batch]");
+  const BatchLens bl = batch_lens(L, batch);
+  if (n_q < 1 || n_q > bl.min)
+    return fail(OSCAR_ERR_INVALID_ARG, "n_q must be in [1, tokens of every sequence of the batch]");
   HIP_TRY(hipSetDevice(c.device));
+  if (!bl.uniform && L.dev_synced < batch) {
+    if ((rc = upload_lens(L, batch, 0, stream))) return rc;
+    L.dev_synced = batch;
+  }
   const size_t DD = (size_t)c.head_dim * c.head_dim;
   PrefillAttnArgs a{};
   a.k = plane_dev(kv, L.k, false);
@@ -793,7 +953,8 @@ int oscar_prefill_attn(oscar_kv* kv, int32_t layer, const void* q, void* out, in
   a.cap = kv->cap;
   a.N = c.sink_tokens;
   a.M = c.recent_tokens;
-  a.T = L.T;
+  a.T = bl.max;
+  a.lens = bl.uniform ? nullptr : L.dlens;
   const float scale = softmax_scale > 0.0f ? softmax_scale : 1.0f / std::sqrt((float)c.head_dim);
   a.scale_log2 = scale * 1.4426950408889634f;
   HIP_TRY(launch_prefill_attn(a, stream));
@@ -807,19 +968,19 @@ int oscar_kv_decode_step(oscar_kv* kv, int32_t layer, const void* k, const void*
   if (!k || !v) return fail(OSCAR_ERR_INVALID_ARG, "k/v pointer is NULL");
   if (batch <= 0 || batch > kv->cfg.max_batch) return fail(OSCAR_ERR_INVALID_ARG, "batch must be in [1, max_batch]");
   Layer& L = kv->layers[layer];
-  if (L.T > 0 && batch != L.batch)
-    return fail(OSCAR_ERR_INVALID_ARG, "batch differs from the batch this layer was filled with");
-  if ((long long)L.T + 1 > kv->cfg.max_context)
-    return fail(OSCAR_ERR_CAPACITY, "decode step at " + std::to_string(L.T) + " tokens exceeds max_context");
+  const BatchLens bl = batch_lens(L, batch);
+  if ((long long)bl.max + 1 > kv->cfg.max_context)
+    return fail(OSCAR_ERR_CAPACITY, "decode step at " + std::to_string(bl.max) + " tokens exceeds max_context");
   if (!(fast_shape(kv) && kv->cfg.recent_tokens >= 1) && !wide_shape(kv)) {
     // separate launches: the appended token is not a bf16 window token here or
     // the shape has no fused kernel (head_dim 512 fuses the append with its q
     // rotation launch instead)
     rc = do_append(kv, layer, k, v, batch, 1, nullptr, nullptr, stream);
     if (rc) return rc;
-    return launch_decode(kv, layer, q, out, out_dtype, batch, softmax_scale, L.T, nullptr, stream);
+    return decode_attn(kv, layer, q, out, out_dtype, batch, softmax_scale, stream, Scratch());
   }
   HIP_TRY(hipSetDevice(kv->cfg.device));
+  if (!bl.uniform && (rc = upload_lens(L, batch, 1, stream))) return rc;
   AppendArgs a{};
   a.k = plane_dev(kv, L.k, false);
   a.v = plane_dev(kv, L.v, true);
@@ -835,12 +996,12 @@ int oscar_kv_decode_step(oscar_kv* kv, int32_t layer, const void* k, const void*
   a.cap = kv->cap;
   a.N = kv->cfg.sink_tokens;
   a.M = kv->cfg.recent_tokens;
-  a.T_old = L.T;
-  a.T_new = L.T + 1;
-  rc = launch_decode(kv, layer, q, out, out_dtype, batch, softmax_scale, L.T + 1, &a, stream);
+  a.T_old = bl.max;
+  a.T_new = bl.max + 1;
+  a.lens = bl.uniform ? nullptr : L.dlens;
+  rc = launch_decode(kv, layer, q, out, out_dtype, batch, softmax_scale, bl.max + 1, &a, stream, Scratch(), a.lens);
   if (rc) return rc;
-  L.T += 1;
-  L.batch = batch;
+  advance_lens(L, batch, 1, !bl.uniform);
   return OSCAR_OK;
 }
 

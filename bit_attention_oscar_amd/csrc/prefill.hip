@@ -81,11 +81,11 @@ __device__ inline float quad_sum128(const float (&x)[32]) {
 // scale (0 for K or bf16 planes).
 template <bool LM>
 __device__ float prefill_epilogue(const AppendArgs& a, const PlaneDev& P, float* dump, int bh, int b, int h, int g,
-                                  int t0, float (*tile)[132], uint32_t (*crow)[8]) {
+                                  int t0, int T_old, int T_new, float (*tile)[132], uint32_t (*crow)[8]) {
   const int D = a.D;
   const int tid = threadIdx.x, r = tid >> 2, p = tid & 3;
   const int t = t0 + r;
-  const bool live = t >= a.T_old && t < a.T_new;
+  const bool live = t >= T_old && t < T_new;
   const int d0 = 128 * g;
   float x[32];
 #pragma unroll
@@ -96,9 +96,9 @@ __device__ float prefill_epilogue(const AppendArgs& a, const PlaneDev& P, float*
   }
   const bool to_full = P.is_bf16;
   const bool to_sink = !P.is_bf16 && t < a.N;
-  const bool to_ring = !P.is_bf16 && a.M > 0 && t >= a.N && t >= a.T_new - a.M;
+  const bool to_ring = !P.is_bf16 && a.M > 0 && t >= a.N && t >= T_new - a.M;
   if (live && dump) {
-    float* drow = dump + (((size_t)b * a.n_new + (t - a.T_old)) * a.Hkv + h) * D + d0 + 32 * p;
+    float* drow = dump + (((size_t)b * a.n_new + (t - T_old)) * a.Hkv + h) * D + d0 + 32 * p;
 #pragma unroll
     for (int i = 0; i < 8; ++i)
       *reinterpret_cast<f32x4*>(drow + 4 * i) = f32x4{x[4 * i], x[4 * i + 1], x[4 * i + 2], x[4 * i + 3]};
@@ -183,7 +183,7 @@ __device__ float prefill_epilogue(const AppendArgs& a, const PlaneDev& P, float*
     for (int qq = 0; qq < 4; ++qq) {
       const int tb = tb0 + 2 * (qq & 1) + 4 * (qq >> 1);
       const int tt = t0 + tb;
-      if (tt >= a.T_old && tt < a.T_new)
+      if (tt >= T_old && tt < T_new)
         byte |= ((crow[tb][ds >> 4] >> (2 * (ds & 15))) & 3u) << (2 * qq);
       else
         keep |= 3u << (2 * qq);
@@ -239,7 +239,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   const int bh = rem / tiles_per_bh, y = rem - (rem / tiles_per_bh) * tiles_per_bh;
   const int b = bh / a.Hkv, h = bh - (bh / a.Hkv) * a.Hkv;
   const bool isv = isv_i != 0;
-  const int t0 = ((a.T_old >> 8) + y) << 8;   // first position of the 256-token tile
+  const int2 tr = append_range(a, b);         // this sequence's new positions [tr.x, tr.y)
+  const int t0 = ((tr.x >> 8) + y) << 8;      // first position of the 256-token tile
+  if (t0 >= tr.y) return;                     // ragged batch: this sequence has fewer tiles
   const PlaneDev P = isv ? a.v : a.k;
   const uint16_t* in = isv ? a.vin : a.kin;
   const uint16_t* RT = isv ? a.rv3 : a.rk3;   // [3][D (column n)][D (row k)] bf16
@@ -249,7 +251,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   // Operands are read through buffer resources: one uniform base, a 32-bit
   // lane offset and a uniform step offset, so the loads hold few registers.
   // A: the lane's rows 64 wave + 16 rb + m, k offset kq within each step.
-  // Rows outside [T_old, T_new) read row T_old instead (always present): their
+  // Rows outside [tr.x, tr.y) read the first new row instead (always present): their
   // products are never stored (each output row depends on its own A row
   // only), and unconditional loads keep the wait counts static.
   const int m = lane & 15, kq = 8 * (lane >> 4);
@@ -259,7 +261,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 #pragma unroll
   for (int rb = 0; rb < 4; ++rb) {
     const int t = t0 + 64 * wave + 16 * rb + m;
-    const int row = (t >= a.T_old && t < a.T_new) ? t - a.T_old : 0;
+    const int row = (t >= tr.x && t < tr.y) ? t - tr.x : 0;
     aoff[rb] = ((row * a.Hkv + h) * D + kq) * 2;
   }
   // B staging: chunks i < 6 of 16 bytes per thread: piece i >> 1, column
@@ -340,7 +342,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   float wsmax = 0.0f;
   for (int qt = 0; qt < 4; ++qt) {
     const int th = t0 + 64 * qt;
-    const bool live = th < a.T_new && th + 64 > a.T_old;    // block-uniform
+    const bool live = th < tr.y && th + 64 > tr.x;          // block-uniform
     if (!live) continue;
     if (wave == qt) {
 #pragma unroll
@@ -351,7 +353,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
           for (int i = 0; i < 4; ++i) S.ep.tile[16 * rb + 4 * (lane >> 4) + i][16 * cb + m] = acc[rb][cb][i];
     }
     __syncthreads();
-    wsmax = fmaxf(wsmax, prefill_epilogue<LM>(a, P, dump, bh, b, h, g, th, S.ep.tile, S.ep.crow));
+    wsmax = fmaxf(wsmax, prefill_epilogue<LM>(a, P, dump, bh, b, h, g, th, tr.x, tr.y, S.ep.tile, S.ep.crow));
     __syncthreads();                     // the tile and codes are rewritten by the next quarter
   }
   wsmax = wave_max(wsmax);

@@ -15,6 +15,7 @@ struct PrefillAttnArgs {
   int absorb_v;
   int B, n, Hq, Hkv, Gq, cap, N, M, T;
   float scale_log2;        // softmax scale * log2(e)
+  const int* lens;         // ragged batch: tokens of sequence b ([B], device); null: every sequence holds T
 };
 
 // causal attention of the last n cached positions' queries; returns hipGetLastError()

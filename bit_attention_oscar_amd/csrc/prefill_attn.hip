@@ -103,7 +103,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   const int b = bh / a.Hkv, h = bh - (bh / a.Hkv) * a.Hkv;
   const int QB = 64 / a.Gq;                       // queries per block
   const int i0 = (int)blockIdx.y * QB;
-  const int T = a.T;
+  const int T = a.lens ? a.lens[b] : a.T;          // this sequence's tokens (ragged batch: its own)
   const int sink_end = min(a.N, T), rec_begin = max(a.N, T - a.M);
 
   // ---- q rows (bf16 -> fp32), rotation by R_K, scale x log2 e

@@ -37,7 +37,7 @@ EXPORTED = [
     "oscar_kv_set_decode_impl", "oscar_kv_export", "oscar_kv_append_dump", "oscar_quantize_rows",
     "oscar_kv_profile_enable", "oscar_kv_profile_read", "oscar_stream_copy", "oscar_stream_read",
     "oscar_kv_decode_step", "oscar_prefill_attn", "oscar_kv_set_q_share", "oscar_int2_decode_attn_noalloc",
-    "oscar_quantize_rows_lloyd_max",
+    "oscar_quantize_rows_lloyd_max", "oscar_kv_append_seq", "oscar_kv_reset_seq", "oscar_kv_seq_length",
 ]
 
 
@@ -81,6 +81,9 @@ def load_library(path: str = LIB_PATH) -> C.CDLL:
         "oscar_kv_append_dump": ([vp, i32, vp, vp, i32, i32, vp, vp, vp], C.c_int),
         "oscar_quantize_rows": ([vp, i32, i32, i32, f32, vp, vp, vp], C.c_int),
         "oscar_quantize_rows_lloyd_max": ([vp, i32, i32, i32, f32, vp, vp, vp], C.c_int),
+        "oscar_kv_append_seq": ([vp, i32, i32, vp, vp, i32, vp], C.c_int),
+        "oscar_kv_reset_seq": ([vp, i32, vp], C.c_int),
+        "oscar_kv_seq_length": ([vp, i32, i32, C.POINTER(i32)], C.c_int),
         "oscar_kv_profile_enable": ([vp, i32], C.c_int),
         "oscar_kv_profile_read": ([vp, i32, C.POINTER(C.c_double), C.POINTER(C.c_int64)], C.c_int),
         "oscar_stream_copy": ([vp, vp, C.c_size_t, vp], C.c_int),
@@ -188,6 +191,20 @@ def oscar_quantize_rows(x, rows, D, G, clip, codes, meta, stream=None):
                                     _stream(stream)))
 
 
+def oscar_kv_append_seq(kv, layer, seq, k, v, n_new, stream=None):
+    _check(_lib.oscar_kv_append_seq(kv, layer, seq, _ptr(k), _ptr(v), n_new, _stream(stream)))
+
+
+def oscar_kv_reset_seq(kv, seq, stream=None):
+    _check(_lib.oscar_kv_reset_seq(kv, seq, _stream(stream)))
+
+
+def oscar_kv_seq_length(kv, layer, seq):
+    t = C.c_int32()
+    _check(_lib.oscar_kv_seq_length(kv, layer, seq, C.byref(t)))
+    return t.value
+
+
 def oscar_quantize_rows_lloyd_max(x, rows, D, G, ratio, codes, meta, stream=None):
     _check(_lib.oscar_quantize_rows_lloyd_max(_ptr(x), rows, D, G, float(ratio), _ptr(codes), _ptr(meta),
                                               _stream(stream)))
@@ -258,6 +275,16 @@ class KVCache:
     def append(self, layer, k, v, stream=None):
         B, n = k.shape[0], k.shape[1]
         oscar_kv_append(self.handle, layer, k, v, B, n, stream)
+
+    def append_seq(self, layer, seq, k, v, stream=None):
+        """k, v: [n_new, Hkv, D] of sequence seq, appended at its own length."""
+        oscar_kv_append_seq(self.handle, layer, seq, k, v, k.shape[0], stream)
+
+    def reset_seq(self, seq, stream=None):
+        oscar_kv_reset_seq(self.handle, seq, stream)
+
+    def seq_length(self, layer, seq):
+        return oscar_kv_seq_length(self.handle, layer, seq)
 
     def append_dump(self, layer, k, v, k_rot, v_rot, stream=None):
         B, n = k.shape[0], k.shape[1]

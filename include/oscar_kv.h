@@ -136,14 +136,18 @@ int oscar_kv_create(const oscar_kv_config* cfg, oscar_kv** out);
  * the article's "How the offline rotation is fit": clipping thresholds bound
  * the values before rounding), with bf16 copies of the first and last
  * positions (Qwen3-4B card, "Run" env-var table).
- * Append n_new tokens to sequences 0..batch-1 of `layer` (all sequences of a
- * layer hold the same number of tokens T_l; the first append on a layer fixes
- * its batch, later calls must pass the same batch).
+ * Append n_new tokens to each of sequences 0..batch-1 of `layer`, each at its
+ * own length T_b (a ragged batch: the sequences of a layer may hold different
+ * numbers of tokens, as the requests of a serving batch do; sequences past
+ * `batch` are untouched).
  *   k, v: device bf16 [batch][n_new][Hkv][D], post-RoPE, un-rotated.
  * Per token and kv head: rotate, write the bf16 window copy if the position is
- * in the sink or among the last M positions after this append, quantize and
- * pack (INT2 planes) or store bf16 (BF16 planes).  T_l += n_new on success.
- * Errors: INVALID_ARG, CAPACITY (T_l + n_new > max_context), HIP. */
+ * in the sink or among the last M positions of its sequence after this append,
+ * quantize and pack (INT2 planes) or store bf16 (BF16 planes).  T_b += n_new
+ * on success.  The host knows every T_b (it issued every append); for a ragged
+ * batch the call first writes the new lengths to a device array of the handle
+ * with a small kernel on `stream` (values as kernel arguments: nothing waits).
+ * Errors: INVALID_ARG, CAPACITY (some T_b + n_new > max_context), HIP. */
 int oscar_kv_append(oscar_kv* kv, int32_t layer, const void* k, const void* v,
                     int32_t batch, int32_t n_new, hipStream_t stream);
 
@@ -154,13 +158,15 @@ int oscar_kv_append(oscar_kv* kv, int32_t layer, const void* k, const void* v,
  * 4-12B-it-INT2-KV", the rotation paragraph below "Folders"), the output
  * un-rotated by R_V^T ("OSCAR-RotationZoo", "How to use": V is stored
  * rotated, hence the flag that absorbs its rotation).
- * One decode step of attention for `layer` over all T_l cached tokens.
+ * One decode step of attention for `layer`: sequence b of the batch attends
+ * over its own T_b cached tokens with the windows of its own length (every
+ * sequence of the batch must hold at least one token).
  *   q:   device bf16 [batch][Hq][D], post-RoPE, un-rotated;
  *   out: device [batch][Hq][D] of out_dtype, un-rotated (o = o' @ R_V^T);
  *   softmax_scale <= 0 selects 1/sqrt(D).
  * The INT2 part runs as a split-K flash-decode; the partial results are merged
  * with a log-sum-exp combine that also undoes the V rotation.
- * Errors: INVALID_ARG (including T_l == 0 or batch != the layer's batch), HIP. */
+ * Errors: INVALID_ARG (including an empty sequence in the batch), HIP. */
 int oscar_int2_decode_attn(oscar_kv* kv, int32_t layer, const void* q, void* out,
                            int32_t out_dtype, int32_t batch, float softmax_scale,
                            hipStream_t stream);
@@ -210,10 +216,10 @@ int oscar_kv_decode_step(oscar_kv* kv, int32_t layer, const void* k, const void*
 
 /* Chunked-prefill attention over the mixed cache (RotationZoo "How to use":
  * the serving host runs a prefill backend beside the decode one).  The n_q
- * queries are those of the last n_q cached positions of `layer` (normally the
- * chunk just appended with oscar_kv_append): query i, at position
- * p = T_l - n_q + i, attends causally over positions [0, p] of the cache as it
- * stands, i.e. the sink and recent windows of the current length T_l read their
+ * queries are those of the last n_q cached positions of each sequence b of
+ * `layer` (normally the chunk just appended): query i, at position
+ * p = T_b - n_q + i, attends causally over positions [0, p] of the cache as it
+ * stands, i.e. the sink and recent windows of the current length T_b read their
  * bf16 values and every other position its INT2 codes with the group's scale
  * and zero.  q is rotated by R_K; the output is un-rotated by R_V^T (or left in
  * the V-rotated basis with absorb_v_rotation).
@@ -222,8 +228,8 @@ int oscar_kv_decode_step(oscar_kv* kv, int32_t layer, const void* k, const void*
  *   softmax_scale <= 0 selects 1/sqrt(D).
  * head_dim 128 and the UNIFORM codebook only (UNSUPPORTED otherwise).  Nothing is allocated; the cache
  * is read only.
- * Errors: INVALID_ARG (including n_q < 1, n_q > T_l, batch != the layer's
- * batch), UNSUPPORTED, HIP. */
+ * Errors: INVALID_ARG (including n_q < 1, n_q > some T_b of the batch),
+ * UNSUPPORTED, HIP. */
 int oscar_prefill_attn(oscar_kv* kv, int32_t layer, const void* q, void* out, int32_t out_dtype,
                        int32_t batch, int32_t n_q, float softmax_scale, hipStream_t stream);
 
@@ -236,8 +242,28 @@ const char* oscar_last_error(void);
 
 /* ---- inspection and test hooks (not part of the four-call contract) ---- */
 
-/* Tokens currently held by `layer`. */
+/* Tokens currently held by `layer`: the longest of its sequences (every
+ * sequence's count while the batch is uniform). */
 int oscar_kv_length(const oscar_kv* kv, int32_t layer, int32_t* tokens);
+
+/* ---- ragged batches: sequences at their own lengths ---- */
+
+/* Append n_new tokens to sequence `seq` alone (the prefill of one request into
+ * its slot), at its own length T_seq; the append path of oscar_kv_append.
+ *   k, v: device bf16 [n_new][Hkv][D], post-RoPE, un-rotated.
+ * Errors: INVALID_ARG (seq outside [0, max_batch), n_new < 1, NULL pointer),
+ * CAPACITY (T_seq + n_new > max_context), HIP. */
+int oscar_kv_append_seq(oscar_kv* kv, int32_t layer, int32_t seq, const void* k, const void* v,
+                        int32_t n_new, hipStream_t stream);
+
+/* Empty sequence `seq` in every layer (a finished request frees its slot);
+ * its next tokens start at position 0.  Enqueues a clear of the sequence's
+ * running V scale maximum on `stream` (a memset: not for graph capture).
+ * Errors: INVALID_ARG, HIP. */
+int oscar_kv_reset_seq(oscar_kv* kv, int32_t seq, hipStream_t stream);
+
+/* Tokens held by sequence `seq` of `layer`. */
+int oscar_kv_seq_length(const oscar_kv* kv, int32_t layer, int32_t seq, int32_t* tokens);
 
 /* Device bytes held by the handle. */
 int oscar_kv_device_bytes(const oscar_kv* kv, size_t* bytes);

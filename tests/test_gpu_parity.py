@@ -236,9 +236,13 @@ def test_decode_end_to_end_vs_oracle_cache(ok):
     (1, 64, 256), (40, 64, 256), (320, 64, 256), (321, 64, 256), (385, 64, 256),
     (1000, 0, 256), (1000, 64, 0), (1000, 0, 0), (777, 13, 29), (64, 0, 0), (65, 1, 0),
 ])
-def test_decode_window_edges(ok, T, N, M):
-    shape = Shape(B=2, Hq=4, Hkv=2, N=N, M=M)
-    say(f"[decode edges] T={T} N={N} M={M}")
+@pytest.mark.parametrize("gq", [2, 4, 8])
+def test_decode_window_edges(ok, T, N, M, gq):
+    """1, 2 and 4 query heads per kv head: the general kernel and the
+    one-launch matrix-core kernel (4 and 8), fewer tokens than the sink
+    included."""
+    shape = Shape(B=2, Hq=2 * gq, Hkv=2, N=N, M=M)
+    say(f"[decode edges] T={T} N={N} M={M} gq={gq}")
     gc, rk, rv, k, v, mask = _fill(ok, shape, T)
     qb = query(shape, mask)
     want = oracle_on_exported(gc, 0, qb, shape, rk, rv)
@@ -396,6 +400,7 @@ def _exports_equal(g1, g2, layer, N, M):
     (Shape(B=2, Hq=4, Hkv=1, N=64, M=256), 1000, 5),           # INT2 range + both windows
     (Shape(B=1, Hq=8, Hkv=2, N=4, M=20), 60, 70),              # ring wraps, tiles and 8-groups crossed
     (Shape(B=2, Hq=4, Hkv=2, N=8, M=16), 0, 30),               # from an empty cache: sink, then ring
+    (Shape(B=2, Hq=8, Hkv=2, N=8, M=16), 0, 30),               # the same on the one-launch kernel (fewer tokens than N first)
     (Shape(B=1, Hq=4, Hkv=1, N=0, M=1), 130, 3),               # window = the new token only
     (Shape(B=1, Hq=4, Hkv=1, N=64, M=256), 300, 4),            # every token still bf16
     (Shape(B=2, Hq=16, Hkv=2, N=8, M=40), 700, 6),             # GQA 8: two head groups per kv head
