@@ -13,6 +13,7 @@ constexpr int kMaxSplits = 256;       // partial-result slots per (sequence, hea
 constexpr int kQPub = 4 * 128 + 8 + 1024;  // published q of 4 query heads: fp32 q, sums, exponents,
                                            // two-piece fp16 operands in two instruction layouts
 constexpr int kMaxGq = 16;            // query heads per kv head handled by the VALU kernel
+constexpr int kMaxOneRound = 16;      // INT2 splits per (sequence, kv head) of a one-round launch
 
 // ---------------------------------------------------------------------------
 // Storage layout (per layer; b = sequence, h = kv head, t = position, d = dim)
@@ -190,12 +191,8 @@ struct CombineArgs {
 struct DecodeArgs {
   PlaneDev k, v;
   const float* qrot;       // rotated q of the general kernel
-  float* qpub;             // [B*Hkv*G][kQPub]: rotated q of each head group, published by the
-                           // first attention block of each (sequence, kv head) in a matrix-core launch
-  unsigned* qflag;         // [B*Hkv]: epoch of the launch whose q qpub holds
-  unsigned epoch;          // this launch's number (never 0)
-  unsigned qwait_ticks;    // longest wait for the published q, in wall-clock ticks
-  int q_self;              // 1: no block waits for the published q (each rotates it itself)
+  float* qpub;             // [B*Hkv*G][kQPub]: rotated q of each head group, written by the
+                           // prologue launch before the matrix-core attention launch
   float* partials;         // [B][Hq][pstride][D+2]
   int pstride;             // partial slots per (sequence, query head)
   int Hq, Hkv, D, cap, N, M, T;
@@ -209,10 +206,13 @@ struct DecodeArgs {
   const uint16_t* q;       // bf16 [B][Hq][D] (matrix-core launch rotates q itself)
   const float* rk;         // fp32 [D][D] of this layer
   float scale_log2;        // softmax scale * log2(e)
-  int app_blocks;          // 2 when the launch also appends this step's token, else 0
+  int app_blocks;          // 2 when the prologue launch also appends this step's token, else 0
   int int2_lead;           // INT2 splits dispatched before the window blocks
   float split_ramp;        // INT2 split sizes fall linearly by this fraction from first to last
   int win_blocks;          // window blocks of the launch (win.splits)
+  int one_round;           // 1: one block per INT2 split and nothing else, every block resident at
+                           // once; window chunks and the append are extra work of some splits
+  float share[kMaxOneRound + 1];   // one_round: INT2 tiles of splits [0, s) = share[s] x the range's tiles
   int ring0;               // ring slot of the first recent token win.a1 (win.a1 % M)
   AppendArgs app;          // that append (n_new = 1); T above counts the new token
   const int* lens;         // ragged batch: tokens of sequence b ([B], device, this launch's appended
@@ -230,6 +230,8 @@ hipError_t launch_qrot(const QRotArgs& a, hipStream_t s);
 hipError_t launch_decode_valu(const DecodeArgs& a, int B, hipStream_t s);
 hipError_t launch_decode_mfma(const DecodeArgs& a, int B, int waves_per_block, hipStream_t s);
 int decode_mfma_resident_blocks(int device, int G);   // blocks of the matrix-core kernel resident at once
+hipError_t launch_decode_prologue(const DecodeArgs& a, int B, hipStream_t s);  // head_dim 128: q records
+                                                                               // (and the step's append)
 hipError_t launch_combine(const CombineArgs& a, hipStream_t s);
 hipError_t launch_wide_qrot(const DecodeArgs& a, int B, hipStream_t s);     // head_dim 512: rotated q records
                                                                             // (and the step's append when a.app_blocks)
@@ -239,11 +241,11 @@ constexpr int kStreamReadBlocks = 8192;   // result words of the read calibratio
 hipError_t launch_stream_read(const void* src, size_t bytes, unsigned* out, hipStream_t s);
 // Working memory of the allocation-free decode call: a file-scope device array
 // of kStaticScratchBytes per GPU (scratch.hip).  static_scratch returns this
-// device's address of it (clearing its counter and flag regions on first use,
-// on `stream`) and the call's launch number.
+// device's address of it (clearing its counter region on first use, on
+// `stream`).
 constexpr size_t kStaticScratchBytes = 16u << 20;
 constexpr size_t kCounterBytes = 256u << 10;          // 65536 (sequence, kv head) pairs
-hipError_t static_scratch(int device, hipStream_t stream, unsigned char** ptr, unsigned* epoch);
+hipError_t static_scratch(int device, hipStream_t stream, unsigned char** ptr);
 // lens[first + i] = vals[i], i < n (n <= kSetLensMax): per-sequence token
 // counts written in stream order, the values travelling as kernel arguments
 constexpr int kSetLensMax = 256;

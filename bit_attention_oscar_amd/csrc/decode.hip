@@ -589,7 +589,7 @@ __device__ inline void finish_block(const DecodeArgs& a, int bh, FusedSmem& S) {
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   if (threadIdx.x == 0) {
-    const unsigned total = (unsigned)(a.plan.splits + a.win_blocks);
+    const unsigned total = (unsigned)(a.one_round ? a.plan.splits : a.plan.splits + a.win_blocks);
     const unsigned prev = __hip_atomic_fetch_add(a.counters + bh, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     is_last = (prev == total - 1u);
   }
@@ -673,8 +673,6 @@ struct FusedSmem {
   float qs[4][132];            // rotated q of the block's 4 heads (fp32, x scale*log2 e)
   float qsum[4];               // per-head sums of qs
   int qeq[4];                  // per-head exponent of the fp16 q operand
-  int ready;                   // the published q of this launch is available
-  uint16_t newtok[2][128];     // bf16 window values of the token appended by this launch
   uint32_t meta16[4][128];     // INT2 splits: per wave, the K and V scale|zero words of a tile
   u4 qops[8][64];              // INT2 splits: q operand n of lane l (the same in every wave)
   float scratch[2688];
@@ -750,37 +748,6 @@ __device__ void q_rotation_finish(const DecodeArgs& a, const QRotLoads& s, Fused
   __syncthreads();
 }
 
-__device__ inline void block_rotate_q(const DecodeArgs& a, int b, int hq0, FusedSmem& S) {
-  q_rotation_finish(a, q_rotation_loads(a, b, hq0), S);
-}
-
-// The same rotation with R_K read in chunks (few registers): for a block
-// whose tile registers are already live.  Identical arithmetic and bits.
-__device__ void block_rotate_q_chunked(const DecodeArgs& a, int b, int hq0, FusedSmem& S) {
-  constexpr int D = 128;
-  const int tid = threadIdx.x;
-  float* qraw = S.scratch;            // [4][128]
-  float* part = S.scratch + 512;      // [4 waves][4][128]
-  for (int i = tid; i < 4 * D; i += 256) qraw[i] = bf16_to_f32(a.q[((size_t)b * a.Hq + hq0) * D + i]);
-  __syncthreads();
-  rotate_rows<128, 4, 4>(qraw, a.rk, part, 4);
-  __syncthreads();
-  const int wave = tid >> 6, lane = tid & 63, j = wave;
-  const float v0 = rot_sum<128, 4, 4>(part, j, lane) * a.scale_log2;
-  const float v1 = rot_sum<128, 4, 4>(part, j, lane + 64) * a.scale_log2;
-  S.qs[j][lane] = v0;
-  S.qs[j][lane + 64] = v1;
-  const float sum = wsum(v0 + v1);
-  const float amax = wmax(fmaxf(fabsf(v0), fabsf(v1)));
-  int e2 = 0;
-  if (amax > 0.0f) frexpf(amax, &e2);
-  if (lane == 0) {
-    S.qsum[j] = sum;
-    S.qeq[j] = (amax > 0.0f) ? 15 - e2 : 0;
-  }
-  __syncthreads();
-}
-
 // fp16 matrix-core q operand pieces: element k of word w for lane group pp of
 // head j is x = q_rot[d] * 2^(eq - 2 (d % 4)) with d = qk_dim(w, pp, k), as
 // hi = fp16(x) and lo = fp16(x - hi).
@@ -832,10 +799,8 @@ __device__ inline uint32_t q_operand16_pair(const FusedSmem& S, int j, int g, in
   return out;
 }
 
-// The first attention block of each (sequence, kv head) rotates q and
-// publishes it for the other blocks of the launch: device-scope stores of
-// every head group (publish_q), a wait until they have completed, then this
-// launch's epoch in the flag (publish_flag).
+// The q record of one head group, written by the decode prologue launch for
+// the attention launch that follows it.
 __device__ void publish_q(const DecodeArgs& a, int pidx, FusedSmem& S) {
   float* dst = a.qpub + (size_t)pidx * kQPub;
   const int tid = threadIdx.x;
@@ -857,21 +822,6 @@ __device__ void publish_q(const DecodeArgs& a, int pidx, FusedSmem& S) {
     st_partial(dst + kQPub16 + i,
                __uint_as_float(q_operand16_pair(S, v & 3, (v >> 2) & 3, v >> 4, wd >> 2, wd & 3)));
   }
-}
-
-__device__ void publish_flag(const DecodeArgs& a, int bh) {
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
-  if (threadIdx.x == 0) __hip_atomic_store(a.qflag + bh, a.epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
-// Rotation (R_K read in chunks) and publication of every head group of (b, h).
-__device__ void rotate_and_publish(const DecodeArgs& a, int b, int h, int bh, FusedSmem& S) {
-  for (int g = 0; g < a.G; ++g) {
-    block_rotate_q_chunked(a, b, h * a.Gq + 4 * g, S);
-    publish_q(a, bh * a.G + g, S);
-  }
-  publish_flag(a, bh);
 }
 
 // Merge of the (m, l, o') partials of one (sequence, kv head) by the last
@@ -946,33 +896,6 @@ __device__ __forceinline__ void combine_group4(const CombineArgs& a, int b, int 
   __syncthreads();                        // os / part are rewritten by the next group
 }
 
-// Thread 0's first read of the flag, issued before a block's tile loads so
-// that waiting for it does not wait for them.
-__device__ inline unsigned first_flag_read(const DecodeArgs& a, int bh) {
-  return threadIdx.x == 0 ? __hip_atomic_load(a.qflag + bh, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 0u;
-}
-
-// Bounded wait for this launch's published q: thread 0 polls the flag for at
-// most a.qwait_ticks of the constant-rate wall clock, then gives up (the block
-// rotates q itself).  The wait always ends, whatever the dispatch order.
-// With a.q_self set (a host test switch) no block waits: every block that did
-// not publish takes the path of a block whose wait ran out.
-__device__ bool wait_published_q(const DecodeArgs& a, int bh, unsigned first, FusedSmem& S) {
-  if (threadIdx.x == 0) {
-    unsigned f = first;
-    if (f != a.epoch && !a.q_self) {
-      const long long t0 = wall_clock64();
-      do {
-        __builtin_amdgcn_s_sleep(4);
-        f = __hip_atomic_load(a.qflag + bh, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      } while (f != a.epoch && wall_clock64() - t0 < (long long)a.qwait_ticks);
-    }
-    S.ready = f == a.epoch && !a.q_self;
-  }
-  __syncthreads();
-  return S.ready != 0;
-}
-
 // fp32 published q of one head group into shared memory (window blocks).
 __device__ void load_published_q(const DecodeArgs& a, int pidx, FusedSmem& S) {
   const float* src = a.qpub + (size_t)pidx * kQPub;
@@ -984,24 +907,9 @@ __device__ void load_published_q(const DecodeArgs& a, int pidx, FusedSmem& S) {
   __syncthreads();
 }
 
-// q of a window block: attention block 0 rotates and publishes every head
-// group; the others take the published copy (bounded wait), or rotate q
-// themselves.  Returns whether the published copy is there.
-__device__ inline bool window_q_ready(const DecodeArgs& a, int b, int h, int bh, int y, FusedSmem& S) {
-  if (y == 0) {
-    rotate_and_publish(a, b, h, bh, S);
-    return true;
-  }
-  return wait_published_q(a, bh, first_flag_read(a, bh), S);
-}
-
 // q of head group g of a window block into shared memory.
-__device__ inline void window_q_group(const DecodeArgs& a, int b, int h, int bh, int g, bool published,
-                                      FusedSmem& S) {
-  if (published)
-    load_published_q(a, bh * a.G + g, S);
-  else
-    block_rotate_q_chunked(a, b, h * a.Gq + 4 * g, S);
+__device__ inline void window_q_group(const DecodeArgs& a, int bh, int g, FusedSmem& S) {
+  load_published_q(a, bh * a.G + g, S);
 }
 
 // Window blocks.  When the launch also appends a token, that token is the
@@ -1023,36 +931,23 @@ __device__ inline int window_len(const SeqView& sv) {
   return (sv.win.b0 - sv.win.a0) + (sv.win.b1 - sv.win.a1);
 }
 
-// the token appended by this launch when window block wblk holds it (the
-// last window token), else -1
-__device__ inline int window_new_token(const DecodeArgs& a, const SeqView& sv, int wblk) {
-  const int len = window_len(sv);
-  return (a.app_blocks > 0 && wblk * sv.win.chunk < len && (wblk + 1) * sv.win.chunk >= len) ? sv.T - 1 : -1;
-}
-
-__device__ inline WinRows window_rows(const DecodeArgs& a, const SeqView& sv, int bh, int vt0, int v_hi, int t_new) {
+__device__ inline WinRows window_rows(const DecodeArgs& a, const SeqView& sv, int bh, int vt0, int v_hi) {
   const int tid = threadIdx.x, n = min(64, v_hi - vt0);
   WinRows r;
   const int tok = tid >> 2, part = tid & 3;
 #pragma unroll
   for (int i = 0; i < 4; ++i) r.k[i] = make_uint4(0, 0, 0, 0);
   if (tok < n) {
-    const int t = win_token(sv.win, vt0 + tok);
-    if (t != t_new) {
-      const uint4* rp = reinterpret_cast<const uint4*>(win_row(a, sv, a.k, bh, t) + 32 * part);
+    const uint4* rp = reinterpret_cast<const uint4*>(win_row(a, sv, a.k, bh, win_token(sv.win, vt0 + tok)) + 32 * part);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) r.k[i] = rp[i];
-    }
+    for (int i = 0; i < 4; ++i) r.k[i] = rp[i];
   }
   const int g = tid >> 4, c = tid & 15;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int tk = g + 16 * i;
     r.v[i] = make_uint4(0, 0, 0, 0);
-    if (tk < n) {
-      const int t = win_token(sv.win, vt0 + tk);
-      if (t != t_new) r.v[i] = *reinterpret_cast<const uint4*>(win_row(a, sv, a.v, bh, t) + 8 * c);
-    }
+    if (tk < n) r.v[i] = *reinterpret_cast<const uint4*>(win_row(a, sv, a.v, bh, win_token(sv.win, vt0 + tk)) + 8 * c);
   }
   return r;
 }
@@ -1060,7 +955,7 @@ __device__ inline WinRows window_rows(const DecodeArgs& a, const SeqView& sv, in
 // The block's first pass of rows, issued before it waits for q.
 __device__ inline WinRows window_first_rows(const DecodeArgs& a, const SeqView& sv, int bh, int wblk) {
   const int v_lo = wblk * sv.win.chunk;
-  return window_rows(a, sv, bh, v_lo, min(window_len(sv), v_lo + sv.win.chunk), window_new_token(a, sv, wblk));
+  return window_rows(a, sv, bh, v_lo, min(window_len(sv), v_lo + sv.win.chunk));
 }
 
 // bf16 window tokens (sink + recent) of one (sequence, kv head), up to
@@ -1068,44 +963,27 @@ __device__ inline WinRows window_first_rows(const DecodeArgs& a, const SeqView& 
 // head group of 4 query heads in turn.  first: the first pass's rows, already
 // issued (later passes, and the passes of later groups, load theirs at their
 // start; a later group loads its first pass's rows again, from cache, rather
-// than hold them in registers).  published: whether the launch's published q
-// is there.
+// than hold them in registers).  q comes from the record the prologue launch
+// wrote.
 __device__ __forceinline__ void window_group(const DecodeArgs& a, const SeqView& sv, int bh, int b, int hq0, int wblk,
-                                             int t_new, FusedSmem& S, const WinRows& first);
+                                             FusedSmem& S, const WinRows& first);
 
 template <int G>
 __device__ void window_block(const DecodeArgs& a, const SeqView& sv, int bh, int b, int h, int wblk, FusedSmem& S,
-                             const WinRows& first, bool published) {
-  constexpr int D = 128;
-  const int tid = threadIdx.x;
-  const int t_new = window_new_token(a, sv, wblk);
-  if (t_new >= 0) {
-    for (int which = 0; which < 2; ++which) {
-      const uint16_t* in = which ? a.app.vin : a.app.kin;
-      float* xs = S.scratch;          // [128]
-      float* part = S.scratch + 128;  // [4][128]
-      const RRows<128, 4> rr = load_r_rows<128, 4>(which ? a.app.rv : a.app.rk);
-      if (tid < D) xs[tid] = bf16_to_f32(in[((size_t)b * a.Hkv + h) * D + tid]);
-      __syncthreads();
-      rotate_rows_regs<128, 4, 1>(xs, rr, part);
-      __syncthreads();
-      if (tid < D) S.newtok[which][tid] = f32_to_bf16(rot_sum<128, 4, 1>(part, 0, tid));
-      __syncthreads();
-    }
-  }
-  window_q_group(a, b, h, bh, 0, published, S);
-  window_group(a, sv, bh, b, h * 4 * G, wblk, t_new, S, first);
+                             const WinRows& first) {
+  window_q_group(a, bh, 0, S);
+  window_group(a, sv, bh, b, h * 4 * G, wblk, S, first);
 #pragma unroll
   for (int g = 1; g < G; ++g) {
     __syncthreads();                  // shared memory is reused by the next group
     const WinRows again = window_first_rows(a, sv, bh, wblk);
-    window_q_group(a, b, h, bh, g, published, S);
-    window_group(a, sv, bh, b, h * 4 * G + 4 * g, wblk, t_new, S, again);
+    window_q_group(a, bh, g, S);
+    window_group(a, sv, bh, b, h * 4 * G + 4 * g, wblk, S, again);
   }
 }
 
 __device__ __forceinline__ void window_group(const DecodeArgs& a, const SeqView& sv, int bh, int b, int hq0, int wblk,
-                                             int t_new, FusedSmem& S, const WinRows& first) {
+                                             FusedSmem& S, const WinRows& first) {
   constexpr int D = 128;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int len = window_len(sv);
@@ -1130,16 +1008,12 @@ __device__ __forceinline__ void window_group(const DecodeArgs& a, const SeqView&
   WinRows cur = first;
   for (int vt0 = v_lo; vt0 < v_hi; vt0 += 64) {
     const int n = min(64, v_hi - vt0);
-    if (vt0 != v_lo) cur = window_rows(a, sv, bh, vt0, v_hi, t_new);
+    if (vt0 != v_lo) cur = window_rows(a, sv, bh, vt0, v_hi);
     {  // scores: 4 lanes per token, 32 dims each
       const int tok = tid >> 2, part = tid & 3;
       float dots[4] = {0.0f, 0.0f, 0.0f, 0.0f};
       if (tok < n) {
-        uint4 us[4] = {cur.k[0], cur.k[1], cur.k[2], cur.k[3]};
-        if (win_token(sv.win, vt0 + tok) == t_new) {
-          const uint4* rp = reinterpret_cast<const uint4*>(&S.newtok[0][32 * part]);
-          us[0] = rp[0]; us[1] = rp[1]; us[2] = rp[2]; us[3] = rp[3];
-        }
+        const uint4 us[4] = {cur.k[0], cur.k[1], cur.k[2], cur.k[3]};
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           float x[8];
@@ -1186,10 +1060,8 @@ __device__ __forceinline__ void window_group(const DecodeArgs& a, const SeqView&
       for (int i = 0; i < 4; ++i) {
         const int tok = g + 16 * i;
         if (tok < n) {
-          uint4 u = cur.v[i];
-          if (win_token(sv.win, vt0 + tok) == t_new) u = *reinterpret_cast<const uint4*>(&S.newtok[1][8 * c]);
           float x[8];
-          bf16x8(u, x);
+          bf16x8(cur.v[i], x);
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
             const float p = sc[j * 64 + tok];
@@ -1272,10 +1144,8 @@ struct TileStreams {
 constexpr int kBufferConfig = 0x00020000;   // raw 32-bit data, no swizzle (gfx9 family)
 
 // Cache policy bits of a buffer load: nt (every code byte is read once per
-// launch), and sc1 (coherent across the device, for data another block of the
-// same launch wrote).
+// launch).
 constexpr int kStreamOnce = 2;
-constexpr int kDeviceScope = 16;
 
 __device__ inline __amdgpu_buffer_rsrc_t plane_rsrc(const void* base, int bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes, kBufferConfig);
@@ -1405,7 +1275,7 @@ __device__ inline Tile16<KS> load_tile16(const TileStreams& st, int t0, int koff
 
 // One INT2 split of the one-launch kernel (G head groups of 4 query heads).
 template <int G>
-__device__ void int2_split16(const DecodeArgs& a, const SeqView& sv, int b, int h, int bh, int y, int split,
+__device__ void int2_split16(const DecodeArgs& a, const SeqView& sv, int b, int h, int bh, int split,
                              FusedSmem& S) {
   constexpr int D = 128, WPB = 4;
   constexpr bool KS = G == 1;                     // token sets in the K dimension
@@ -1426,6 +1296,7 @@ __device__ void int2_split16(const DecodeArgs& a, const SeqView& sv, int b, int 
   auto split_start = [&](int s) -> int {
     const int Sn = a.plan.splits;
     if (s >= Sn) return ntiles;
+    if (a.one_round) return min(ntiles, (int)(a.share[s] * (float)ntiles));
     const float fs = (float)s, al = a.split_ramp;
     const float F = (fs * (1.0f + al) - al * fs * (fs - 1.0f) / (float)max(Sn - 1, 1)) / (float)Sn;
     return min(ntiles, (int)(F * (float)ntiles));
@@ -1445,15 +1316,11 @@ __device__ void int2_split16(const DecodeArgs& a, const SeqView& sv, int b, int 
   // first of the 4 tokens (of the tile) whose scores register block tb / tp holds
   auto tok_of = [&](int t) { return KS ? 32 * set + 8 * g + 4 * t : 32 * (t >> 1) + 8 * g + 4 * (t & 1); };
 
-  // q operands of this lane's column: attention block 0 rotates and
-  // publishes q (its loads issued before its first tile's); the others read
-  // the flag before their tile loads, then take the published operands, or
-  // rotate q themselves when the wait runs out.  Operand n of the published
-  // layout (32 dims: lane group gp, chunk kc) is taken as: plain, n = kc,
-  // gp = g; KS, instruction (wp, h) = n / 2, n % 2 takes lane group
-  // 2 (g % 2) + wp / 2, chunk 2 (wp % 2) + h, zero unless the column's set is
-  // the lane's (g / 2).
-  const bool self_rotate = y == 0;
+  // q operands of this lane's column, from the record the prologue launch
+  // wrote, loaded after the first tiles.  Operand n of the record's layout
+  // (32 dims: lane group gp, chunk kc) is taken as: plain, n = kc, gp = g;
+  // KS, instruction (wp, h) = n / 2, n % 2 takes lane group 2 (g % 2) + wp / 2,
+  // chunk 2 (wp % 2) + h, zero unless the column's set is the lane's (g / 2).
   auto hq_of = [&](int gg) { return h * 4 * G + 4 * gg; };   // first query head of group gg
   auto op_src = [&](int n, int& gp, int& kc) {
     if (KS) {
@@ -1472,80 +1339,24 @@ __device__ void int2_split16(const DecodeArgs& a, const SeqView& sv, int b, int 
   int eq = 0;
 #pragma unroll
   for (int n = 0; n < NOP; ++n) qop[n] = h8{0, 0, 0, 0, 0, 0, 0, 0};
-  auto operands_from_smem = [&](int gg) {
-    if (live && grp == gg) {
-      if (op_live) {
-#pragma unroll
-        for (int n = 0; n < NOP; ++n) {
-          int gp, kc;
-          op_src(n, gp, kc);
-          u4 v;
-          v.x = q_operand16_pair(S, jh, gp, piece, kc, 0);
-          v.y = q_operand16_pair(S, jh, gp, piece, kc, 1);
-          v.z = q_operand16_pair(S, jh, gp, piece, kc, 2);
-          v.w = q_operand16_pair(S, jh, gp, piece, kc, 3);
-          qop[n] = __builtin_bit_cast(h8, v);
-        }
-      }
-      qsum = S.qsum[jh];
-      eq = S.qeq[jh];
-    }
-  };
-  unsigned flag0 = 0;
   Tile16<KS> r[kDepth];
-  if (self_rotate) {
-    const QRotLoads qload = q_rotation_loads(a, b, hq_of(0));
-    // with no tile registers live yet, the second group's loads go out in the
-    // same round trip as the first's
-    QRotLoads qload1;
-    if constexpr (G > 1) qload1 = q_rotation_loads(a, b, hq_of(1));
-    __builtin_amdgcn_sched_barrier(0);
-    q_rotation_finish(a, qload, S);
-    publish_q(a, bh * G, S);
 #pragma unroll
-    for (int gg = 1; gg < G; ++gg) {
-      operands_from_smem(gg - 1);
-      q_rotation_finish(a, qload1, S);
-      publish_q(a, bh * G + gg, S);
-    }
-    publish_flag(a, bh);
-    // the first tiles are issued after the flag: the flag waits for every
-    // earlier memory operation of the block, so tiles issued before it would
-    // delay every waiting block by an HBM latency
+  for (int k = 0; k < kDepth; ++k)
+    r[k] = load_tile16<KS>(st, tile_t0(min(ti0 + k * WPB, t_last)), koff, voff, moff);
+  __builtin_amdgcn_sched_barrier(0);
+  if (live) {
+    const __amdgpu_buffer_rsrc_t qr = plane_rsrc(a.qpub + (size_t)(bh * G + grp) * kQPub, kQPub * 4);
+    if (op_live) {
 #pragma unroll
-    for (int k = 0; k < kDepth; ++k)
-      r[k] = load_tile16<KS>(st, tile_t0(min(ti0 + k * WPB, t_last)), koff, voff, moff);
-    operands_from_smem(G - 1);
-  } else {
-    flag0 = first_flag_read(a, bh);
-    __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int k = 0; k < kDepth; ++k)
-      r[k] = load_tile16<KS>(st, tile_t0(min(ti0 + k * WPB, t_last)), koff, voff, moff);
-    __builtin_amdgcn_sched_barrier(0);
-    if (wait_published_q(a, bh, flag0, S)) {
-      if (live) {
-        const __amdgpu_buffer_rsrc_t qr = plane_rsrc(a.qpub + (size_t)(bh * G + grp) * kQPub, kQPub * 4);
-        if (op_live) {
-#pragma unroll
-          for (int n = 0; n < NOP; ++n) {
-            int gp, kc;
-            op_src(n, gp, kc);
-            const int vb = (kQPub16 + 16 * ((piece * 4 + gp) * 4 + jh) + 4 * kc) * 4;
-            qop[n] = __builtin_bit_cast(h8, __builtin_amdgcn_raw_buffer_load_b128(qr, vb, 0, kDeviceScope));
-          }
-        }
-        qsum = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(qr, (512 + jh) * 4, 0, kDeviceScope));
-        eq = (int)__builtin_amdgcn_raw_buffer_load_b32(qr, (516 + jh) * 4, 0, kDeviceScope);
-      }
-    } else {
-#pragma unroll
-      for (int gg = 0; gg < G; ++gg) {
-        if (gg > 0) __syncthreads();        // the previous group's S.qs has been read
-        block_rotate_q_chunked(a, b, hq_of(gg), S);
-        operands_from_smem(gg);
+      for (int n = 0; n < NOP; ++n) {
+        int gp, kc;
+        op_src(n, gp, kc);
+        const int vb = (kQPub16 + 16 * ((piece * 4 + gp) * 4 + jh) + 4 * kc) * 4;
+        qop[n] = __builtin_bit_cast(h8, __builtin_amdgcn_raw_buffer_load_b128(qr, vb, 0, 0));
       }
     }
+    qsum = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(qr, (512 + jh) * 4, 0, 0));
+    eq = (int)__builtin_amdgcn_raw_buffer_load_b32(qr, (516 + jh) * 4, 0, 0);
   }
   // the operands wait in shared memory (every wave of the block has the same
   // ones; wave 0 writes them) and are read per tile: they would otherwise hold
@@ -1803,39 +1614,61 @@ __device__ void int2_split16(const DecodeArgs& a, const SeqView& sv, int b, int 
 // The one-launch decode kernel of head_dim 128.  G: head groups of 4 query
 // heads per kv head (G = Hq / Hkv / 4); the INT2 splits serve every group in
 // one pass over the tiles (int2_split16).
-template <int WPB, int G>
+template <int WPB, int G, bool ONE>
 __global__ __launch_bounds__(64 * WPB)
 __attribute__((amdgpu_waves_per_eu(kMfmaWavesPerEu, kMfmaWavesPerEu)))
 void decode_mfma_kernel(DecodeArgs a) {
   const int bh = blockIdx.x;
   const int b = bh / a.Hkv, h = bh - (bh / a.Hkv) * a.Hkv;
   __shared__ FusedSmem S;
-  // Block roles along y, in dispatch order:
-  //   [0, app_blocks)                 append of the new token (K, then V)
-  //   then the attention blocks: int2_lead INT2 splits, the win_blocks bf16
-  //   window blocks, the remaining INT2 splits.
-  int y = (int)blockIdx.y;
-  if (y < a.app_blocks) {
-    const int2 tr = append_range(a.app, b);
-    append_block<128, 4, 1>(a.app, bh, y == 1, tr.x, tr.x + 1, tr.x, tr.y, S.scratch, S.scratch + 128);
-    return;
-  }
+  const int y = (int)blockIdx.y;
   const SeqView sv = seq_view(a, b);
-  y -= a.app_blocks;
-  // attention blocks: int2_lead INT2 splits, the window blocks, the other INT2
-  // splits.  The lead splits fill the compute units first; the window blocks
-  // start once slots free up, by when block 0 has published q.
-  const int lead = a.int2_lead;
-  if (y >= lead && y < lead + a.win_blocks) {
-    const WinRows rows = window_first_rows(a, sv, bh, y - lead);   // in flight during the q wait
-    const bool published = window_q_ready(a, b, h, bh, y, S);
-    window_block<G>(a, sv, bh, b, h, y - lead, S, rows, published);
+  if constexpr (ONE) {
+    // One round: block y is INT2 split y; blocks 1 .. win_blocks first take
+    // window chunk y - 1.  The host sizes the INT2 shares so that every block
+    // ends at about the same time.
+    const int wblk = y - 1;
+    if (wblk >= 0 && wblk < a.win_blocks) {
+      const WinRows rows = window_first_rows(a, sv, bh, wblk);
+      window_block<G>(a, sv, bh, b, h, wblk, S, rows);
+      __syncthreads();                  // shared memory is reused below
+    }
+    int2_split16<G>(a, sv, b, h, bh, y, S);
     finish_block<G>(a, bh, S);
     return;
   }
-  const int split = y < lead ? y : y - a.win_blocks;
-  int2_split16<G>(a, sv, b, h, bh, y, split, S);
+  // Several rounds, in dispatch order: int2_lead INT2 splits, the win_blocks
+  // bf16 window blocks, the remaining INT2 splits (the lead splits fill the
+  // compute units first).
+  const int lead = a.int2_lead;
+  if (y >= lead && y < lead + a.win_blocks) {
+    const WinRows rows = window_first_rows(a, sv, bh, y - lead);
+    window_block<G>(a, sv, bh, b, h, y - lead, S, rows);
+    finish_block<G>(a, bh, S);
+    return;
+  }
+  int2_split16<G>(a, sv, b, h, bh, y < lead ? y : y - a.win_blocks, S);
   finish_block<G>(a, bh, S);
+}
+
+// The first launch of a decode call at head_dim 128: blocks y < G rotate head
+// group y's q and write its record (fp32 q, sums, exponents, the fp16 operand
+// pieces); blocks G and G + 1 append the step's token (K, V).  The attention
+// launch that follows in stream order reads both and waits for nothing.
+template <int G>
+__global__ __launch_bounds__(256) void decode_prologue_kernel(DecodeArgs a) {
+  __shared__ FusedSmem S;
+  const int bh = blockIdx.x;
+  const int b = bh / a.Hkv, h = bh - (bh / a.Hkv) * a.Hkv;
+  const int y = (int)blockIdx.y;
+  if (y < G) {
+    const QRotLoads ql = q_rotation_loads(a, b, h * 4 * G + 4 * y);
+    q_rotation_finish(a, ql, S);
+    publish_q(a, bh * G + y, S);
+    return;
+  }
+  const int2 tr = append_range(a.app, b);
+  append_block<128, 4, 1>(a.app, bh, y == G + 1, tr.x, tr.x + 1, tr.x, tr.y, S.scratch, S.scratch + 128);
 }
 
 // ---------------------------------------------------------------------------
@@ -2510,8 +2343,8 @@ hipError_t launch_decode_valu(const DecodeArgs& a, int B, hipStream_t s) {
 int decode_mfma_resident_blocks(int device, int G) {
   int per_cu = 0, cus = 0;
   const hipError_t e =
-      G == 2 ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, decode_mfma_kernel<4, 2>, 256, 0)
-             : hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, decode_mfma_kernel<4, 1>, 256, 0);
+      G == 2 ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, decode_mfma_kernel<4, 2, false>, 256, 0)
+             : hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, decode_mfma_kernel<4, 1, false>, 256, 0);
   if (e != hipSuccess || per_cu < 1) per_cu = 1;
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, device) != hipSuccess || cus < 1) cus = 1;
   return per_cu * cus;
@@ -2519,11 +2352,24 @@ int decode_mfma_resident_blocks(int device, int G) {
 
 hipError_t launch_decode_mfma(const DecodeArgs& a, int B, int waves_per_block, hipStream_t s) {
   (void)waves_per_block;   // the fused window blocks need 4 waves
-  dim3 grid((unsigned)(B * a.Hkv), (unsigned)(a.app_blocks + a.plan.splits + a.win_blocks));
+  dim3 grid((unsigned)(B * a.Hkv), (unsigned)(a.one_round ? a.plan.splits : a.plan.splits + a.win_blocks));
+  auto launch = [&](auto kernel) { hipLaunchKernelGGL(kernel, grid, dim3(256), 0, s, a); };
+  if (a.G == 2) {
+    if (a.one_round) launch(decode_mfma_kernel<4, 2, true>);
+    else launch(decode_mfma_kernel<4, 2, false>);
+  } else {
+    if (a.one_round) launch(decode_mfma_kernel<4, 1, true>);
+    else launch(decode_mfma_kernel<4, 1, false>);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_decode_prologue(const DecodeArgs& a, int B, hipStream_t s) {
+  dim3 grid((unsigned)(B * a.Hkv), (unsigned)(a.G + a.app_blocks));
   if (a.G == 2)
-    hipLaunchKernelGGL((decode_mfma_kernel<4, 2>), grid, dim3(256), 0, s, a);
+    hipLaunchKernelGGL((decode_prologue_kernel<2>), grid, dim3(256), 0, s, a);
   else
-    hipLaunchKernelGGL((decode_mfma_kernel<4, 1>), grid, dim3(256), 0, s, a);
+    hipLaunchKernelGGL((decode_prologue_kernel<1>), grid, dim3(256), 0, s, a);
   return hipGetLastError();
 }
 

@@ -83,8 +83,6 @@ struct oscar_kv {
   uint16_t* rv3 = nullptr; // [L][3][D][D] the same for R_V
   float* qrot = nullptr;   // [B][Hq][D]
   float* qpub = nullptr;    // [B][Hkv][G][kQPub]
-  unsigned* qflag = nullptr; // [B][Hkv]
-  unsigned epoch = 0;        // matrix-core launches so far (skips 0 on wrap)
   float* partials = nullptr; // [B][Hq][kMaxSplits][D+2]
   unsigned* counters = nullptr; // [B][Hkv] blocks finished in the current decode launch
   size_t bytes = 0;
@@ -92,8 +90,8 @@ struct oscar_kv {
   int32_t decode_impl = 0;
   int32_t mfma_waves = 4;
   int resident = 1024;       // matrix-core kernel blocks resident at once on the device
-  unsigned qwait_ticks = 2000;  // 20 us of the device wall clock (set from its rate at create)
-  int q_share = 1;           // 0: blocks never wait for the published q (test switch)
+  int one_round = 0;         // one-round launches: 0 when the batch fills the device, -1 never,
+                             // r >= 3 always, with r blocks per (sequence, kv head) (test switch)
   bool prof_on = false;
   ProfClass prof[3];
 };
@@ -419,12 +417,6 @@ int do_append_seq(oscar_kv* kv, int32_t layer, int32_t seq, const void* k, const
   return OSCAR_OK;
 }
 
-// Split count for the INT2 range: aim for about 8 resident waves per SIMD
-// worth of blocks (256 CUs x 4 SIMDs), never more tiles than exist.
-// INT2 splits per (sequence, kv head): about 6 blocks of 4 waves per compute
-// unit in total (measured at 32k context, B = 16, Hkv = 8: 8-12 splits beat 4,
-// 6 and 16; fewer blocks leave compute units idle in the tail, more blocks
-// repeat each block's fixed start-up and merge work).
 // Window tokens per window block (a multiple of 64).  At the 32k shape (320
 // window tokens) 192 and 256 measured best: 66 and 65 us per launch against
 // 70 us with 64 and 74 us with all 320 in one block.
@@ -441,9 +433,17 @@ constexpr int kWideTargetBlocks = 1536;
 // measured best (65.1 us per launch; 66.5 with equal splits, 65.9 with 0.6).
 constexpr float kSplitRamp = 0.4f;
 
-int auto_int2_splits(int BH, int ntiles, int waves) {
-  const int target_blocks = 1536 * 4 / std::max(1, waves);
-  int s = std::max(1, target_blocks / std::max(1, BH));
+// One-round launches: a window chunk's cost as a fraction of a split's INT2
+// share (the INT2 shares of the blocks that carry one shrink by it), and the
+// INT2 tiles per block below which the several-round plan is kept.
+constexpr float kOneRoundWinCost = 0.10f;
+constexpr int kOneRoundMinTiles = 16;
+
+// INT2 splits per (sequence, kv head): as many blocks as are resident at once
+// in total (measured at the 32k shape, q read from the prologue's records: 6
+// splits 82.4 us per launch against 87.9 with 12 and 83.5 with 4 or 5).
+int auto_int2_splits(int BH, int ntiles, int waves, int resident) {
+  int s = std::max(1, resident / std::max(1, BH));
   // at least kMinTilesPerWave tiles per wave: more splits only add merge slots
   s = std::min(s, std::max(1, ntiles / (std::max(1, waves) * kMinTilesPerWave)));
   return std::min(s, kMaxSplits - kMaxWinSplits);
@@ -547,18 +547,12 @@ int oscar_kv_create(const oscar_kv_config* cfg, oscar_kv** out) {
   // q records: one per 4 query heads (head_dim 128), one per 128-dim slice (head_dim 512)
   const size_t qrecs = std::max(std::max(Hkv, Hq / 4), D == 512 ? 4 * Hkv : (size_t)0);
   if ((rc = dev_alloc(kv, (void**)&kv->qpub, B * qrecs * kQPub * 4))) return bail(rc);
-  if ((rc = dev_alloc(kv, (void**)&kv->qflag, B * Hkv * sizeof(unsigned)))) return bail(rc);
-  if (hipMemset(kv->qflag, 0, B * Hkv * sizeof(unsigned)) != hipSuccess)
-    return bail(fail(OSCAR_ERR_HIP, "clearing the q flags failed"));
   if ((rc = dev_alloc(kv, (void**)&kv->partials, B * Hq * kMaxSplits * (D + 2) * 4))) return bail(rc);
   if ((rc = dev_alloc(kv, (void**)&kv->counters, B * Hkv * sizeof(unsigned)))) return bail(rc);
   if (hipMemset(kv->counters, 0, B * Hkv * sizeof(unsigned)) != hipSuccess)
     return bail(fail(OSCAR_ERR_HIP, "clearing the decode counters failed"));
   if (hipDeviceSynchronize() != hipSuccess) return bail(fail(OSCAR_ERR_HIP, "device sync after create failed"));
   kv->resident = decode_mfma_resident_blocks(cfg->device, std::max(1, (int)(Hq / Hkv / 4)));
-  int wall_khz = 0;
-  if (hipDeviceGetAttribute(&wall_khz, hipDeviceAttributeWallClockRate, cfg->device) == hipSuccess && wall_khz > 0)
-    kv->qwait_ticks = (unsigned)std::min<long long>(20LL * wall_khz / 1000, 1LL << 30);
   *out = kv;
   g_last_error.clear();
   return OSCAR_OK;
@@ -650,20 +644,19 @@ int check_decode_args(const oscar_kv* kv, int32_t layer, const void* q, void* ou
 
 // Device memory a decode-attention call works in besides the cache and its
 // inputs and outputs: the partial results (m, l, o') of its splits, the
-// per-(sequence, kv head) block counters and q-publication flags of the
-// one-launch kernel, the published q records, the rotated q of the general
-// kernel.  Either the handle's buffers (allocated at create) or the shared
-// static array of the allocation-free call.
+// per-(sequence, kv head) block counters of the one-launch kernel, the q
+// records its prologue launch writes, the rotated q of the general kernel.
+// Either the handle's buffers (allocated at create) or the shared static
+// array of the allocation-free call.
 struct Scratch {
   bool use_static = false;
   unsigned char* base = nullptr;     // static array, this device's address
-  unsigned epoch = 0;                // launch number for the q flags (static array)
 };
 
 // Points the call's arguments at its working memory for `nslots` partial
-// slots per (sequence, query head).  Static array: fixed counter and flag
-// regions, then q records, rotated q and partials carved for this call;
-// CAPACITY when they do not fit.
+// slots per (sequence, query head).  Static array: the fixed counter region,
+// then q records, rotated q and partials carved for this call; CAPACITY when
+// they do not fit.
 int bind_scratch(oscar_kv* kv, const Scratch& sc, int batch, int nslots, DecodeArgs& da, CombineArgs& ca,
                  float** qrot = nullptr) {
   const auto& c = kv->cfg;
@@ -671,7 +664,6 @@ int bind_scratch(oscar_kv* kv, const Scratch& sc, int batch, int nslots, DecodeA
     if (qrot) *qrot = kv->qrot;
     da.qrot = kv->qrot;
     da.qpub = kv->qpub;
-    da.qflag = kv->qflag;
     da.counters = kv->counters;
     da.partials = kv->partials;
     da.pstride = kMaxSplits;
@@ -683,7 +675,7 @@ int bind_scratch(oscar_kv* kv, const Scratch& sc, int batch, int nslots, DecodeA
   const size_t qrecs = std::max(std::max((size_t)c.num_kv_heads, (size_t)c.num_q_heads / 4),
                                 D == 512 ? 4 * (size_t)c.num_kv_heads : (size_t)0);
   auto up = [](size_t n) { return (n + 255) / 256 * 256; };
-  const size_t off_qpub = 2 * kCounterBytes;
+  const size_t off_qpub = kCounterBytes;
   const size_t off_qrot = off_qpub + up((size_t)batch * qrecs * kQPub * 4);
   const size_t off_part = off_qrot + up(BHq * D * 4);
   const size_t end = off_part + BHq * (size_t)nslots * (D + 2) * 4;
@@ -693,7 +685,6 @@ int bind_scratch(oscar_kv* kv, const Scratch& sc, int batch, int nslots, DecodeA
                                         "array holds " + std::to_string(kStaticScratchBytes) +
                                         " (use oscar_int2_decode_attn)");
   da.counters = reinterpret_cast<unsigned*>(sc.base);
-  da.qflag = reinterpret_cast<unsigned*>(sc.base + kCounterBytes);
   da.qpub = reinterpret_cast<float*>(sc.base + off_qpub);
   if (qrot) *qrot = reinterpret_cast<float*>(sc.base + off_qrot);
   da.qrot = reinterpret_cast<float*>(sc.base + off_qrot);
@@ -781,7 +772,7 @@ int launch_decode(oscar_kv* kv, int32_t layer, const void* q, void* out, int32_t
     if (int2_hi > int2_lo) {
       const int ntiles = ((int2_hi - 1) >> 6) - (int2_lo >> 6) + 1;
       const int waves = kv->mfma_waves;
-      int s = kv->forced_splits > 0 ? kv->forced_splits : auto_int2_splits(BH, ntiles, waves);
+      int s = kv->forced_splits > 0 ? kv->forced_splits : auto_int2_splits(BH, ntiles, waves, kv->resident);
       s = std::max(1, std::min(s, std::min(ntiles, kMaxSplits - kMaxWinSplits)));
       const int tps = (ntiles + s - 1) / s;
       p.a0 = int2_lo;
@@ -789,30 +780,57 @@ int launch_decode(oscar_kv* kv, int32_t layer, const void* q, void* out, int32_t
       p.chunk = tps * kTile;
       p.splits = (ntiles + tps - 1) / tps;
     }
+    // One round: when the batch fills the device (R = resident blocks per
+    // (sequence, kv head) between 3 and kMaxOneRound) every block is INT2
+    // split and stays resident from the start; the window chunks and the
+    // append ride on some of the splits (see decode_mfma_kernel).  Each block
+    // then pays the start-up latency (q, first tiles) once, and no second or
+    // third wave of blocks repeats it or leaves the device part idle at the end.
+    const int R = kv->one_round != 0 ? kv->one_round : (kv->forced_splits > 0 ? 0 : kv->resident / std::max(1, BH));
+    const int ntiles_all = int2_hi > int2_lo ? ((int2_hi - 1) >> 6) - (int2_lo >> 6) + 1 : 0;
+    // (automatic at 8 query heads per kv head only: measured 165 against 170
+    // us per launch at the 128k shape; at 4 heads, the 32k shape, 89.8
+    // against 82.4)
+    const bool one_round = kv->one_round >= 0 && R >= 3 && R <= kMaxOneRound &&
+                           (kv->one_round > 0 || (da.G == 2 && ntiles_all >= kOneRoundMinTiles * R));
+    if (one_round) {
+      p = SegPlan{};
+      p.a0 = int2_lo;
+      p.b0 = std::max(int2_lo, int2_hi);
+      p.splits = R;
+      w = hp_len > 0 ? make_plan(0, sink_end, rec_begin, T, R - 1, 0) : SegPlan{};
+      // INT2 weight of each split: the window blocks start theirs after a
+      // window chunk
+      float wsum = 0.0f, wt[kMaxOneRound];
+      for (int y = 0; y < R; ++y) {
+        wt[y] = 1.0f;
+        if (y >= 1 && y <= w.splits) wt[y] -= kOneRoundWinCost;
+        wsum += wt[y];
+      }
+      float acc = 0.0f;
+      for (int y = 0; y <= R; ++y) {
+        da.share[y] = y == R ? 1.0f : acc / wsum;
+        if (y < R) acc += wt[y];
+      }
+      da.one_round = 1;
+    }
     p.slot0 = w.splits;      // window partials first, then the INT2 splits
     w.slot0 = 0;
     da.plan = p;
     da.win = w;
     // INT2 splits that fill the first wave of resident blocks go before the
-    // window blocks (which then find q published instead of rotating it)
+    // window blocks
     da.win_blocks = w.splits;
     da.ring0 = M > 0 ? w.a1 % M : 0;
-    // (8 query heads per kv head: the append blocks' slots also go to INT2
-    // splits, measured 831 against 815 tokens/s at the 128k shape, alternating
-    // runs on one box; at 4 heads that costs 9% at the 32k shape)
-    da.int2_lead = std::max(0, std::min(p.splits, kv->resident / std::max(1, BH) - (da.G == 2 ? 0 : da.app_blocks)));
-    da.split_ramp = p.splits > 1 ? kSplitRamp : 0.0f;
+    da.int2_lead = std::max(0, std::min(p.splits, kv->resident / std::max(1, BH)));
+    da.split_ramp = p.splits > 1 && !one_round ? kSplitRamp : 0.0f;
     ca.nslots = p.splits + w.splits;
     if ((rc = bind_scratch(kv, sc, batch, ca.nslots, da, ca))) return rc;
     da.comb = ca;
-    if (sc.use_static) {
-      da.epoch = sc.epoch;
-    } else {
-      if (++kv->epoch == 0) kv->epoch = 1;   // a flag never holds a future launch's number
-      da.epoch = kv->epoch;
-    }
-    da.qwait_ticks = kv->qwait_ticks;
-    da.q_self = kv->q_share ? 0 : 1;
+    // the q records (and the step's append) in a launch of their own first:
+    // the attention launch then reads q at its start without waiting for it
+    HIP_TRY(launch_decode_prologue(da, batch, stream));
+    da.app_blocks = 0;
     const long pk = sc.use_static ? -1 : prof_begin(kv, 0, stream);
     HIP_TRY(launch_decode_mfma(da, batch, kv->mfma_waves, stream));
     prof_end(kv, 0, pk, stream);
@@ -890,7 +908,7 @@ int decode_attn(oscar_kv* kv, int32_t layer, const void* q, void* out, int32_t o
   const BatchLens bl = batch_lens(L, batch);
   if (bl.min == 0) return fail(OSCAR_ERR_INVALID_ARG, "a sequence of the batch holds no tokens");
   HIP_TRY(hipSetDevice(kv->cfg.device));
-  if (sc.use_static) HIP_TRY(static_scratch(kv->cfg.device, stream, &sc.base, &sc.epoch));
+  if (sc.use_static) HIP_TRY(static_scratch(kv->cfg.device, stream, &sc.base));
   if (bl.uniform) return launch_decode(kv, layer, q, out, out_dtype, batch, softmax_scale, bl.max, nullptr, stream, sc);
   if (L.dev_synced < batch) {
     if ((rc = upload_lens(L, batch, 0, stream))) return rc;
@@ -1051,10 +1069,11 @@ int oscar_kv_set_num_splits(oscar_kv* kv, int32_t num_splits) {
   return OSCAR_OK;
 }
 
-int oscar_kv_set_q_share(oscar_kv* kv, int32_t share) {
+int oscar_kv_set_one_round(oscar_kv* kv, int32_t blocks) {
   if (!kv) return fail(OSCAR_ERR_INVALID_ARG, "handle is NULL");
-  if (share != 0 && share != 1) return fail(OSCAR_ERR_INVALID_ARG, "share must be 0 or 1");
-  kv->q_share = share;
+  if (!(blocks == 0 || blocks == -1 || (blocks >= 3 && blocks <= kMaxOneRound)))
+    return fail(OSCAR_ERR_INVALID_ARG, "blocks must be 0, -1 or in [3, 16]");
+  kv->one_round = blocks;
   return OSCAR_OK;
 }
 

@@ -6,23 +6,23 @@
 //   [0, kCounterBytes)                  per-(sequence, kv head) block counters of the
 //                                       one-launch kernel; zero between calls (the
 //                                       last block of a launch resets its counter)
-//   [kCounterBytes, 2 kCounterBytes)    per-(sequence, kv head) q-publication flags
-//                                       (hold launch numbers; any stale value is older
-//                                       than the next call's number)
-//   [2 kCounterBytes, kStaticScratchBytes)   carved per call: q records, rotated q,
+//   [kCounterBytes, kStaticScratchBytes)   carved per call: q records, rotated q,
 //                                       partial results; nothing there must start at 0
-// The first two regions have fixed places, so a call never finds another
-// call's records where it expects zero counters.  Both are cleared once per
-// device, when the device's address of the array is first taken.
+// The counter region has a fixed place, so a call never finds another call's
+// records where it expects zero counters.  It is cleared once per device, when
+// the device's address of the array is first taken.
 #include <mutex>
 
 #include "common.h"
 
 namespace oscar {
 
-namespace {
+// The array itself: one copy on every GPU the library runs on, held until the
+// process ends.  In host code its name is only a stand-in, never a device
+// address: the device's address comes from hipGetSymbolAddress below.
+static __device__ __align__(256) unsigned char scratch[kStaticScratchBytes];
 
-__device__ __align__(256) unsigned char scratch[kStaticScratchBytes];
+namespace {
 
 __global__ __launch_bounds__(256) void clear_words_kernel(unsigned* p, size_t n) {
   for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (size_t)gridDim.x * 256) p[i] = 0u;
@@ -31,11 +31,10 @@ __global__ __launch_bounds__(256) void clear_words_kernel(unsigned* p, size_t n)
 constexpr int kMaxDevices = 64;
 std::mutex g_mu;
 unsigned char* g_ptr[kMaxDevices] = {};
-unsigned g_epoch[kMaxDevices] = {};
 
 }  // namespace
 
-hipError_t static_scratch(int device, hipStream_t stream, unsigned char** ptr, unsigned* epoch) {
+hipError_t static_scratch(int device, hipStream_t stream, unsigned char** ptr) {
   if (device < 0 || device >= kMaxDevices) return hipErrorInvalidDevice;
   std::lock_guard<std::mutex> lock(g_mu);
   if (!g_ptr[device]) {
@@ -45,16 +44,14 @@ hipError_t static_scratch(int device, hipStream_t stream, unsigned char** ptr, u
     hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
     if (e != hipSuccess) return e;
     if (!p) return hipErrorInvalidSymbol;
-    const size_t words = 2 * kCounterBytes / 4;
+    const size_t words = kCounterBytes / 4;
     hipLaunchKernelGGL(clear_words_kernel, dim3((unsigned)((words + 255) / 256)), dim3(256), 0, stream,
                        static_cast<unsigned*>(p), words);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     g_ptr[device] = static_cast<unsigned char*>(p);
   }
-  if (++g_epoch[device] == 0) g_epoch[device] = 1;   // a flag never holds a future call's number
   *ptr = g_ptr[device];
-  *epoch = g_epoch[device];
   return hipSuccess;
 }
 

@@ -36,8 +36,9 @@ EXPORTED = [
     "oscar_last_error", "oscar_kv_length", "oscar_kv_device_bytes", "oscar_kv_set_num_splits",
     "oscar_kv_set_decode_impl", "oscar_kv_export", "oscar_kv_append_dump", "oscar_quantize_rows",
     "oscar_kv_profile_enable", "oscar_kv_profile_read", "oscar_stream_copy", "oscar_stream_read",
-    "oscar_kv_decode_step", "oscar_prefill_attn", "oscar_kv_set_q_share", "oscar_int2_decode_attn_noalloc",
+    "oscar_kv_decode_step", "oscar_prefill_attn", "oscar_int2_decode_attn_noalloc",
     "oscar_quantize_rows_lloyd_max", "oscar_kv_append_seq", "oscar_kv_reset_seq", "oscar_kv_seq_length",
+    "oscar_kv_set_one_round",
 ]
 
 
@@ -76,7 +77,7 @@ def load_library(path: str = LIB_PATH) -> C.CDLL:
         "oscar_kv_device_bytes": ([vp, C.POINTER(C.c_size_t)], C.c_int),
         "oscar_kv_set_num_splits": ([vp, i32], C.c_int),
         "oscar_kv_set_decode_impl": ([vp, i32], C.c_int),
-        "oscar_kv_set_q_share": ([vp, i32], C.c_int),
+        "oscar_kv_set_one_round": ([vp, i32], C.c_int),
         "oscar_kv_export": ([vp, i32, i32, vp, vp, vp, vp], C.c_int),
         "oscar_kv_append_dump": ([vp, i32, vp, vp, i32, i32, vp, vp, vp], C.c_int),
         "oscar_quantize_rows": ([vp, i32, i32, i32, f32, vp, vp, vp], C.c_int),
@@ -177,8 +178,8 @@ def oscar_kv_set_decode_impl(kv, impl):
     _check(_lib.oscar_kv_set_decode_impl(kv, impl))
 
 
-def oscar_kv_set_q_share(kv, share):
-    _check(_lib.oscar_kv_set_q_share(kv, share))
+def oscar_kv_set_one_round(kv, blocks):
+    _check(_lib.oscar_kv_set_one_round(kv, blocks))
 
 
 def oscar_kv_append_dump(kv, layer, k, v, batch, n_new, k_rot, v_rot, stream=None):
@@ -310,8 +311,8 @@ class KVCache:
     def set_decode_impl(self, impl):
         oscar_kv_set_decode_impl(self.handle, impl)
 
-    def set_q_share(self, share):
-        oscar_kv_set_q_share(self.handle, share)
+    def set_one_round(self, blocks):
+        oscar_kv_set_one_round(self.handle, blocks)
 
     def device_bytes(self):
         return oscar_kv_device_bytes(self.handle)

@@ -175,7 +175,7 @@ int oscar_int2_decode_attn(oscar_kv* kv, int32_t layer, const void* q, void* out
  * (code under HIP graph capture, tight serving loops, harnesses that forbid
  * allocation): same arguments, result and errors, and the same kernels, but
  * the call's working memory (the splits' partial results, the q records, the
- * block counters and flags) lives in a file-scope device array of 16 MiB per
+ * block counters) lives in a file-scope device array of 16 MiB per
  * GPU instead of the handle's buffers.  The call allocates and frees nothing;
  * the array is held by each GPU the library runs on until the process ends,
  * and its counters are cleared once, at the first call on that GPU.
@@ -265,6 +265,14 @@ int oscar_kv_reset_seq(oscar_kv* kv, int32_t seq, hipStream_t stream);
 /* Tokens held by sequence `seq` of `layer`. */
 int oscar_kv_seq_length(const oscar_kv* kv, int32_t layer, int32_t seq, int32_t* tokens);
 
+/* Test switch of the one-launch decode kernel's schedule: 0 (default) puts
+ * every block of a launch on the device at once (one INT2 split per block,
+ * window chunks and the step's append carried by some of them) when the batch
+ * fills the device, with resident-blocks / (batch x Hkv) blocks per (sequence,
+ * kv head); -1 never does; 3..16 always does, with that many blocks per
+ * (sequence, kv head).  Errors: INVALID_ARG. */
+int oscar_kv_set_one_round(oscar_kv* kv, int32_t blocks);
+
 /* Device bytes held by the handle. */
 int oscar_kv_device_bytes(const oscar_kv* kv, size_t* bytes);
 
@@ -273,14 +281,6 @@ int oscar_kv_device_bytes(const oscar_kv* kv, size_t* bytes);
  * kernel), in [0, 208]; 0 restores the automatic choice.  The count is capped
  * by the number of 64-token tiles.  Errors: INVALID_ARG. */
 int oscar_kv_set_num_splits(oscar_kv* kv, int32_t num_splits);
-
-/* q sharing inside the head_dim 128 matrix-core launch: 1 (default) = the
- * first attention block of each (sequence, kv head) rotates q and publishes
- * it, and the other blocks wait for it for a bounded time (20 us of the
- * device wall clock) before rotating q themselves; 0 = no block waits, every
- * attention block rotates q itself (the path a block takes when its wait runs
- * out, for tests).  Both give the same q operands.  Errors: INVALID_ARG. */
-int oscar_kv_set_q_share(oscar_kv* kv, int32_t share);
 
 /* Select the decode kernel: 0 = automatic (fused MFMA kernel where supported),
  * 1 = the general VALU kernel for every shape.  Errors: INVALID_ARG. */
