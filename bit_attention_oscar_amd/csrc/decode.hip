@@ -581,7 +581,7 @@ template <int D, int WAVES>
 struct RRows;
 template <int G>
 __device__ void combine_fused(const CombineArgs& a, int bh, FusedSmem& S);
-__device__ __forceinline__ void combine_group4(const CombineArgs& a, int b, int hq0, const RRows<128, 4>& rr, FusedSmem& S);
+__device__ __forceinline__ void combine_group4(const CombineArgs& a, int b, int hq0, FusedSmem& S);
 
 template <int G>
 __device__ inline void finish_block(const DecodeArgs& a, int bh, FusedSmem& S) {
@@ -826,55 +826,95 @@ __device__ void publish_q(const DecodeArgs& a, int pidx, FusedSmem& S) {
 
 // Merge of the (m, l, o') partials of one (sequence, kv head) by the last
 // block of the matrix-core launch, then o = o' @ R_V^T (4 query heads per kv
-// head, head_dim 128).  Wave j merges head j: lane l owns dims l and l + 64
-// and loads 8 slots at a time (their m and l, the same words in every lane,
-// and its two o' values) in one round trip, merging into a running maximum.
-// The rotation splits its reduction over e across the four waves and adds the
-// partial sums in a fixed order; its R_V^T rows are loaded first, in flight
-// with the partials.
+// head, head_dim 128; combine_group4).  The rotation splits its reduction
+// over e across the four waves and adds the partial sums in a fixed order.
 template <int G>
 __device__ void combine_fused(const CombineArgs& a, int bh, FusedSmem& S) {
   constexpr int D = 128;
   const int b = bh / a.Hkv, kvh = bh - (bh / a.Hkv) * a.Hkv;
-  RRows<D, 4> rr;
-  if (!a.absorb_v) rr = load_r_rows<D, 4>(a.rvT);
 #pragma unroll
-  for (int g = 0; g < G; ++g) combine_group4(a, b, kvh * 4 * G + 4 * g, rr, S);
+  for (int g = 0; g < G; ++g) combine_group4(a, b, kvh * 4 * G + 4 * g, S);
 }
 
-// Merge and un-rotation of query heads hq0 .. hq0 + 3.
-__device__ __forceinline__ void combine_group4(const CombineArgs& a, int b, int hq0, const RRows<128, 4>& rr, FusedSmem& S) {
-  constexpr int D = 128, SB = 8;
+// Merge and un-rotation of query heads hq0 .. hq0 + 3.  Up to 8 slots: wave j
+// merges head j in one round trip (lane l: dims l and l + 64, with every
+// slot's m and l), the R_V^T rows loaded beside the partials.  More slots (the
+// small-batch shapes, many window blocks): three dependent steps whatever the
+// count (up to 256): every slot's m and l of the four heads into shared memory
+// in one round trip; per head (wave) the maximum, the sum and each slot's
+// weight; then o' = sum of weight x o'_s with 32 slots' loads in flight per
+// round trip; the R_V^T rows after that.
+__device__ __forceinline__ void combine_group4(const CombineArgs& a, int b, int hq0, FusedSmem& S) {
+  constexpr int D = 128, SF = 8, SB = 32;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const float* P = a.partials + ((size_t)b * a.Hq + hq0 + wave) * a.pstride * (D + 2);
-  float M = NEG_INF, L = 0.0f, o0 = 0.0f, o1 = 0.0f;
-  for (int s0 = 0; s0 < a.nslots; s0 += SB) {
-    float ms[SB], ls[SB], x0[SB], x1[SB];
+  const int ns = a.nslots;
+  const float* P0 = a.partials + ((size_t)b * a.Hq + hq0) * a.pstride * (D + 2);
+  const float* P = P0 + (size_t)wave * a.pstride * (D + 2);
+  float o0 = 0.0f, o1 = 0.0f, L = 0.0f;
+  RRows<D, 4> rr;
+  if (ns <= SF) {
+    if (!a.absorb_v) rr = load_r_rows<D, 4>(a.rvT);
+    float ms[SF], ls[SF], x0[SF], x1[SF];
 #pragma unroll
-    for (int u = 0; u < SB; ++u) {
-      const float* p = P + (size_t)min(s0 + u, a.nslots - 1) * (D + 2);
+    for (int u = 0; u < SF; ++u) {
+      const float* p = P + (size_t)min(u, ns - 1) * (D + 2);
       ms[u] = ld_partial<true>(p + D);
       ls[u] = ld_partial<true>(p + D + 1);
       x0[u] = ld_partial<true>(p + lane);
       x1[u] = ld_partial<true>(p + lane + 64);
     }
-    float mb = M;
+    float M = NEG_INF;
 #pragma unroll
-    for (int u = 0; u < SB; ++u)
-      if (s0 + u < a.nslots) mb = fmaxf(mb, ms[u]);
-    if (mb == NEG_INF) continue;                    // no token in these slots yet
-    const float keep = exp2f(M - mb);               // 0 while M is -inf
-    L *= keep;
-    o0 *= keep;
-    o1 *= keep;
+    for (int u = 0; u < SF; ++u)
+      if (u < ns) M = fmaxf(M, ms[u]);
 #pragma unroll
-    for (int u = 0; u < SB; ++u) {
-      const float w = (s0 + u < a.nslots && ms[u] != NEG_INF) ? exp2f(ms[u] - mb) : 0.0f;
+    for (int u = 0; u < SF; ++u) {
+      const float w = (u < ns && ms[u] != NEG_INF) ? exp2f(ms[u] - M) : 0.0f;
       L = __builtin_fmaf(ls[u], w, L);
       o0 = __builtin_fmaf(x0[u], w, o0);
       o1 = __builtin_fmaf(x1[u], w, o1);
     }
-    M = mb;
+  } else {
+    static_assert(4 * 2 * kMaxSplits <= sizeof(S.scratch) / sizeof(float), "merge weights");
+    float* wm = S.scratch;                // [4][ns]: m, then the slot weight
+    float* wl = S.scratch + 4 * ns;       // [4][ns]: l
+    for (int i = tid; i < 4 * ns; i += 256) {
+      const int j = i / ns, sl = i - j * ns;
+      const float* p = P0 + ((size_t)j * a.pstride + sl) * (D + 2);
+      wm[i] = ld_partial<true>(p + D);
+      wl[i] = ld_partial<true>(p + D + 1);
+    }
+    __syncthreads();
+    float mx = NEG_INF;
+    for (int sl = lane; sl < ns; sl += 64) mx = fmaxf(mx, wm[wave * ns + sl]);
+    const float M = wmax(mx);
+    float lsum = 0.0f;
+    for (int sl = lane; sl < ns; sl += 64) {
+      const float m = wm[wave * ns + sl];
+      const float w = m == NEG_INF ? 0.0f : exp2f(m - M);
+      lsum = __builtin_fmaf(wl[wave * ns + sl], w, lsum);
+      wm[wave * ns + sl] = w;
+    }
+    L = wsum(lsum);
+    __builtin_amdgcn_s_waitcnt(kWaitLds);  // the wave's weights, written by its own lanes, are read below
+    __builtin_amdgcn_wave_barrier();
+    for (int s0 = 0; s0 < ns; s0 += SB) {
+      float x0[SB], x1[SB];
+#pragma unroll
+      for (int u = 0; u < SB; ++u) {
+        const float* p = P + (size_t)min(s0 + u, ns - 1) * (D + 2);
+        x0[u] = ld_partial<true>(p + lane);
+        x1[u] = ld_partial<true>(p + lane + 64);
+      }
+#pragma unroll
+      for (int u = 0; u < SB; ++u) {
+        const float w = s0 + u < ns ? wm[wave * ns + s0 + u] : 0.0f;
+        o0 = __builtin_fmaf(x0[u], w, o0);
+        o1 = __builtin_fmaf(x1[u], w, o1);
+      }
+    }
+    __syncthreads();                      // every wave is done with the weights (scratch is reused)
+    if (!a.absorb_v) rr = load_r_rows<D, 4>(a.rvT);
   }
   const float inv = 1.0f / L;
   if (a.absorb_v) {                       // o' in the V-rotated basis
