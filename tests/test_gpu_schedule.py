@@ -1,8 +1,8 @@
-"""The one-launch decode kernel's one-round schedule (every block of a launch
-resident at once: one INT2 split per block, the window chunks and the step's
-append carried by some splits) against the oracle and against the
-several-round schedule, at small shapes where only the test switch turns it on
-(at the benchmark shapes the batch fills the device and it is the default)."""
+"""The head_dim-128 attention launch's one-round schedule (every block of the
+launch resident at once: one INT2 split per block, the window chunks carried
+by the first splits) against the oracle and against the several-round
+schedule, at small shapes where only the test switch turns it on (by default
+it serves 8 query heads per kv head when the batch fills the device)."""
 import numpy as np
 import pytest
 
@@ -61,8 +61,8 @@ def test_one_round_decode(ok, gq, T, N, M, R):
 
 @pytest.mark.parametrize("gq,R", [(4, 3), (4, 6), (8, 5), (4, 16)])
 def test_one_round_decode_steps(ok, gq, R):
-    """Fused decode steps (the append in blocks R - 2 and R - 1) from an empty
-    cache through the sink, the ring's wrap and into the INT2 range: the stored
+    """Decode steps (the append in the prologue launch) from an empty cache
+    through the sink, the ring's wrap and into the INT2 range: the stored
     cache bit-equal to a twin filled by separate calls, outputs within the bar."""
     shape = Shape(B=2, Hq=2 * gq, Hkv=2, N=8, M=24)
     say(f"[one round steps] gq={gq} R={R}")
