@@ -208,7 +208,6 @@ struct DecodeArgs {
   float scale_log2;        // softmax scale * log2(e)
   int app_blocks;          // 2 when the prologue launch also appends this step's token, else 0
   int int2_lead;           // INT2 splits dispatched before the window blocks
-  float split_ramp;        // INT2 split sizes fall linearly by this fraction from first to last
   int win_blocks;          // window blocks of the launch (win.splits)
   int one_round;           // 1: one block per INT2 split and nothing else, every block resident at
                            // once; window chunks and the append are extra work of some splits

@@ -39,12 +39,17 @@ typedef float f4 __attribute__((ext_vector_type(4)));
 // the compiler from hoisting a whole tile of code conversions ahead of the
 // softmax, which raises register pressure.
 #define PHASE_FENCE() __builtin_amdgcn_sched_barrier(0)
-// Waves per SIMD of the one-launch kernel (its INT2 splits need about 160
-// registers: the PV accumulators, two tiles in flight, the softmax state).
+// Waves per SIMD of the head_dim-128 attention kernel (its INT2 splits need
+// about 160 registers: the PV accumulators, the tiles in flight, the softmax
+// state).
 constexpr int kMfmaWavesPerEu = 3;
 // Register sets of tile data per wave: the loads of a tile are issued
-// kDepth - 1 tiles ahead of its processing.
+// kDepth - 1 tiles ahead of its processing (head_dim 512 kernels).
 constexpr int kDepth = 2;
+// The same for the head_dim-128 INT2 splits: three sets (two tiles in flight
+// while one is processed) measured 69.6 against 70.8 us per launch at the 32k
+// shape; four sets at 2 waves per SIMD 69.0, five or more no faster.
+constexpr int kDepth16 = 3;
 
 __device__ inline float wmax(float v) {
 #pragma unroll
@@ -1330,16 +1335,13 @@ __device__ void int2_split16(const DecodeArgs& a, const SeqView& sv, int b, int 
   const int lo = a.plan.a0, hi = sv.hi;          // INT2 token range (empty in a short sequence)
   const int tile_first = lo >> 6;
   const int ntiles = hi > lo ? ((hi - 1) >> 6) - tile_first + 1 : 0;
-  // Split s covers tiles [start(s), start(s + 1)): shares of the range whose
-  // weights fall linearly by a.split_ramp from the first split to the last
-  // (blocks dispatched later start later and get less)
+  // Split s covers tiles [start(s), start(s + 1)): equal shares of the range
+  // (one round: the host's shares)
   auto split_start = [&](int s) -> int {
     const int Sn = a.plan.splits;
     if (s >= Sn) return ntiles;
     if (a.one_round) return min(ntiles, (int)(a.share[s] * (float)ntiles));
-    const float fs = (float)s, al = a.split_ramp;
-    const float F = (fs * (1.0f + al) - al * fs * (fs - 1.0f) / (float)max(Sn - 1, 1)) / (float)Sn;
-    return min(ntiles, (int)(F * (float)ntiles));
+    return s * ntiles / Sn;
   };
   const int s_t0 = split_start(split);
   const int s_t1 = split_start(split + 1);
@@ -1379,9 +1381,9 @@ __device__ void int2_split16(const DecodeArgs& a, const SeqView& sv, int b, int 
   int eq = 0;
 #pragma unroll
   for (int n = 0; n < NOP; ++n) qop[n] = h8{0, 0, 0, 0, 0, 0, 0, 0};
-  Tile16<KS> r[kDepth];
+  Tile16<KS> r[kDepth16];
 #pragma unroll
-  for (int k = 0; k < kDepth; ++k)
+  for (int k = 0; k < kDepth16; ++k)
     r[k] = load_tile16<KS>(st, tile_t0(min(ti0 + k * WPB, t_last)), koff, voff, moff);
   __builtin_amdgcn_sched_barrier(0);
   if (live) {
@@ -1561,13 +1563,12 @@ __device__ void int2_split16(const DecodeArgs& a, const SeqView& sv, int b, int 
     }
   };
 
-  // The wave's tiles are ti0 + WPB i, i < n; r[i % 2] holds tile i.  Every
-  // processed register set is reloaded at once with the tile two ahead, so
-  // the same loads are in flight on every path through the loop (the two
-  // tiles, oldest first) and each use waits for exactly its own loads; past
-  // the last tile the loads go through resources of zero length, which return
-  // zeros without touching memory.
-  static_assert(kDepth == 2, "two register sets of tile data");
+  // The wave's tiles are ti0 + WPB i, i < n; r[i % kDepth16] holds tile i.
+  // Every processed register set is reloaded at once with the tile kDepth16
+  // ahead, so the same loads are in flight on every path through the loop
+  // (kDepth16 tiles, oldest first) and each use waits for exactly its own
+  // loads; past the last tile the loads go through resources of zero length,
+  // which return zeros without touching memory.
   const int n = s_t1 > ti0 ? (s_t1 - ti0 + WPB - 1) / WPB : 0;
   auto tile_of = [&](int i) { return tile_t0(ti0 + WPB * i); };
   TileStreams none = st;
@@ -1575,12 +1576,14 @@ __device__ void int2_split16(const DecodeArgs& a, const SeqView& sv, int b, int 
   none.km = plane_rsrc(a.k.meta, 0);
   none.vm = plane_rsrc(a.v.meta, 0);
   none.vc = plane_rsrc(a.v.codes, 0);
-  for (int i = 0; i < n; i += 2) {
-    process(r[0], tile_of(i), std::true_type{});
-    r[0] = load_tile16<KS>(i + 2 < n ? st : none, tile_of(min(i + 2, n - 1)), koff, voff, moff);
-    if (i + 1 >= n) break;
-    process(r[1], tile_of(i + 1), std::true_type{});
-    r[1] = load_tile16<KS>(i + 3 < n ? st : none, tile_of(min(i + 3, n - 1)), koff, voff, moff);
+  for (int i = 0; i < n; i += kDepth16) {
+#pragma unroll
+    for (int k = 0; k < kDepth16; ++k) {
+      if (i + k >= n) break;
+      process(r[k], tile_of(i + k), std::true_type{});
+      r[k] = load_tile16<KS>(i + k + kDepth16 < n ? st : none, tile_of(min(i + k + kDepth16, n - 1)), koff, voff,
+                             moff);
+    }
   }
 
   // pieces of PV added (lanes c and c + 8), with token sets also the two sets
@@ -2046,12 +2049,7 @@ __device__ void wide_split_bf16v(const DecodeArgs& a, int bh, int b, int h, int 
   const int tile_first = lo >> 6;
   const int ntiles = hi > lo ? ((hi - 1) >> 6) - tile_first + 1 : 0;
   const int S_ = a.plan.splits;
-  auto split_start = [&](int s) -> int {
-    if (s >= S_) return ntiles;
-    const float fs = (float)s, al = a.split_ramp;
-    const float F = (fs * (1.0f + al) - al * fs * (fs - 1.0f) / (float)max(S_ - 1, 1)) / (float)S_;
-    return min(ntiles, (int)(F * (float)ntiles));
-  };
+  auto split_start = [&](int s) -> int { return s >= S_ ? ntiles : s * ntiles / S_; };
   const int s_t0 = split_start(split);
   const int s_t1 = split_start(split + 1);
   const int t_last = max(s_t1 - 1, 0);
@@ -2227,10 +2225,7 @@ void decode_wide_kernel(DecodeArgs a) {
   const int ntiles = hi > lo ? ((hi - 1) >> 6) - tile_first + 1 : 0;
   auto split_start = [&](int s) -> int {
     const int S = a.plan.splits;
-    if (s >= S) return ntiles;
-    const float fs = (float)s, al = a.split_ramp;
-    const float F = (fs * (1.0f + al) - al * fs * (fs - 1.0f) / (float)max(S - 1, 1)) / (float)S;
-    return min(ntiles, (int)(F * (float)ntiles));
+    return s >= S ? ntiles : s * ntiles / S;
   };
   const int s_t0 = split_start(split);
   const int s_t1 = split_start(split + 1);

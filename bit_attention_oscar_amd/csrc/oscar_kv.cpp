@@ -90,8 +90,8 @@ struct oscar_kv {
   int32_t decode_impl = 0;
   int32_t mfma_waves = 4;
   int resident = 1024;       // matrix-core kernel blocks resident at once on the device
-  int one_round = 0;         // one-round launches: 0 when the batch fills the device, -1 never,
-                             // r >= 3 always, with r blocks per (sequence, kv head) (test switch)
+  int one_round = 0;         // one-round launches (test switch): r >= 3 always, with r blocks per
+                             // (sequence, kv head); 0 or -1 never
   bool prof_on = false;
   ProfClass prof[3];
 };
@@ -428,16 +428,15 @@ constexpr int kWinTokensG2 = 128;       // 8 query heads per kv head (two head g
 constexpr int kWideWinTokens = 512;
 constexpr int kWideTargetBlocks = 1536;
 
-// Linear fall of INT2 split sizes from the first split to the last: blocks
-// dispatched later start later, so they get less.  At the 32k shape 0.4
-// measured best (65.1 us per launch; 66.5 with equal splits, 65.9 with 0.6).
-constexpr float kSplitRamp = 0.4f;
+// INT2 splits get equal shares of the range.  (Shares falling linearly from
+// the first split to the last, for blocks dispatched later, measured slower
+// with three tiles in flight per wave: 69.2 against 67.7 us per launch at the
+// 32k shape with a fall of 0.4, 22.0 against 21.2 us at the 16k shape.)
 
-// One-round launches: a window chunk's cost as a fraction of a split's INT2
-// share (the INT2 shares of the blocks that carry one shrink by it), and the
-// INT2 tiles per block below which the several-round plan is kept.
+// One-round launches (a test switch): a window chunk's cost as a fraction of
+// a split's INT2 share (the INT2 shares of the blocks that carry one shrink by
+// it).
 constexpr float kOneRoundWinCost = 0.10f;
-constexpr int kOneRoundMinTiles = 16;
 
 // INT2 splits per (sequence, kv head): as many blocks as are resident at once
 // in total (measured at the 32k shape, q read from the prologue's records: 6
@@ -780,19 +779,13 @@ int launch_decode(oscar_kv* kv, int32_t layer, const void* q, void* out, int32_t
       p.chunk = tps * kTile;
       p.splits = (ntiles + tps - 1) / tps;
     }
-    // One round: when the batch fills the device (R = resident blocks per
-    // (sequence, kv head) between 3 and kMaxOneRound) every block is INT2
-    // split and stays resident from the start; the window chunks and the
-    // append ride on some of the splits (see decode_mfma_kernel).  Each block
-    // then pays the start-up latency (q, first tiles) once, and no second or
-    // third wave of blocks repeats it or leaves the device part idle at the end.
-    const int R = kv->one_round != 0 ? kv->one_round : (kv->forced_splits > 0 ? 0 : kv->resident / std::max(1, BH));
-    const int ntiles_all = int2_hi > int2_lo ? ((int2_hi - 1) >> 6) - (int2_lo >> 6) + 1 : 0;
-    // (automatic at 8 query heads per kv head only: measured 165 against 170
-    // us per launch at the 128k shape; at 4 heads, the 32k shape, 89.8
-    // against 82.4)
-    const bool one_round = kv->one_round >= 0 && R >= 3 && R <= kMaxOneRound &&
-                           (kv->one_round > 0 || (da.G == 2 && ntiles_all >= kOneRoundMinTiles * R));
+    // One round (test switch, R blocks per (sequence, kv head)): every block
+    // is an INT2 split and the window chunks ride on splits 1 .. w (see
+    // decode_mfma_kernel).  Never automatic: with three tiles in flight per
+    // wave it measured 145.9 against 142.8 us per launch at the 128k shape,
+    // and slower at the 32k shape too.
+    const int R = kv->one_round;
+    const bool one_round = R >= 3 && R <= kMaxOneRound;
     if (one_round) {
       p = SegPlan{};
       p.a0 = int2_lo;
@@ -823,7 +816,6 @@ int launch_decode(oscar_kv* kv, int32_t layer, const void* q, void* out, int32_t
     da.win_blocks = w.splits;
     da.ring0 = M > 0 ? w.a1 % M : 0;
     da.int2_lead = std::max(0, std::min(p.splits, kv->resident / std::max(1, BH)));
-    da.split_ramp = p.splits > 1 && !one_round ? kSplitRamp : 0.0f;
     ca.nslots = p.splits + w.splits;
     if ((rc = bind_scratch(kv, sc, batch, ca.nslots, da, ca))) return rc;
     da.comb = ca;
@@ -862,7 +854,6 @@ int launch_decode(oscar_kv* kv, int32_t layer, const void* q, void* out, int32_t
     da.win = w;
     da.win_blocks = w.splits;
     da.ring0 = M > 0 ? rec_begin % M : 0;
-    da.split_ramp = 0.0f;
     ca.nslots = p.splits + w.splits;
     if ((rc = bind_scratch(kv, sc, batch, ca.nslots, da, ca))) return rc;
     HIP_TRY(launch_wide_qrot(da, batch, stream));

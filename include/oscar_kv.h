@@ -265,12 +265,11 @@ int oscar_kv_reset_seq(oscar_kv* kv, int32_t seq, hipStream_t stream);
 /* Tokens held by sequence `seq` of `layer`. */
 int oscar_kv_seq_length(const oscar_kv* kv, int32_t layer, int32_t seq, int32_t* tokens);
 
-/* Test switch of the one-launch decode kernel's schedule: 0 (default) puts
- * every block of a launch on the device at once (one INT2 split per block,
- * window chunks and the step's append carried by some of them) when the batch
- * fills the device, with resident-blocks / (batch x Hkv) blocks per (sequence,
- * kv head); -1 never does; 3..16 always does, with that many blocks per
- * (sequence, kv head).  Errors: INVALID_ARG. */
+/* Test switch of the head_dim-128 attention launch's schedule: 3..16 puts
+ * every block of a launch on the device at once, with that many blocks per
+ * (sequence, kv head) (one INT2 split per block, window chunks carried by
+ * some of them); 0 (default) and -1 keep the several-round schedule (INT2
+ * splits first, then the window blocks).  Errors: INVALID_ARG. */
 int oscar_kv_set_one_round(oscar_kv* kv, int32_t blocks);
 
 /* Device bytes held by the handle. */

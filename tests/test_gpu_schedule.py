@@ -1,8 +1,7 @@
 """The head_dim-128 attention launch's one-round schedule (every block of the
 launch resident at once: one INT2 split per block, the window chunks carried
 by the first splits) against the oracle and against the several-round
-schedule, at small shapes where only the test switch turns it on (by default
-it serves 8 query heads per kv head when the batch fills the device)."""
+schedule (it runs only when the test switch turns it on)."""
 import numpy as np
 import pytest
 
