@@ -841,44 +841,59 @@ __device__ void combine_fused(const CombineArgs& a, int bh, FusedSmem& S) {
   for (int g = 0; g < G; ++g) combine_group4(a, b, kvh * 4 * G + 4 * g, S);
 }
 
-// Merge and un-rotation of query heads hq0 .. hq0 + 3.  Up to 8 slots: wave j
-// merges head j in one round trip (lane l: dims l and l + 64, with every
-// slot's m and l), the R_V^T rows loaded beside the partials.  More slots (the
-// small-batch shapes, many window blocks): three dependent steps whatever the
-// count (up to 256): every slot's m and l of the four heads into shared memory
-// in one round trip; per head (wave) the maximum, the sum and each slot's
-// weight; then o' = sum of weight x o'_s with 32 slots' loads in flight per
-// round trip; the R_V^T rows after that.
+// One-round-trip merge of up to SF slots for head `wave` (lane l: dims l and
+// l + 64): lane s < ns loads slot s's m and l, every lane loads its two dims of
+// every slot's o', all in flight together; the slot weights are formed in the
+// lanes that hold them and read by every lane (v_readlane), and o' is summed in
+// slot order.
+template <int SF>
+__device__ __forceinline__ void merge_slots_one_trip(const float* P, int ns, int lane, float& o0, float& o1,
+                                                     float& L) {
+  constexpr int D = 128;
+  const float* ps = P + (size_t)min(lane, ns - 1) * (D + 2);
+  const float ml = ld_partial<true>(ps + D);
+  const float ll = ld_partial<true>(ps + D + 1);
+  float x0[SF], x1[SF];
+#pragma unroll
+  for (int u = 0; u < SF; ++u) {
+    const float* p = P + (size_t)min(u, ns - 1) * (D + 2);
+    x0[u] = ld_partial<true>(p + lane);
+    x1[u] = ld_partial<true>(p + lane + 64);
+  }
+  const bool mine = lane < ns && ml != NEG_INF;
+  const float M = wmax(mine ? ml : NEG_INF);
+  const float w = mine ? exp2f(ml - M) : 0.0f;
+  L = wsum(mine ? ll * w : 0.0f);
+#pragma unroll
+  for (int u = 0; u < SF; ++u) {
+    if (u < ns) {
+      const float wu = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w), u));
+      o0 = __builtin_fmaf(x0[u], wu, o0);
+      o1 = __builtin_fmaf(x1[u], wu, o1);
+    }
+  }
+}
+
+// Merge and un-rotation of query heads hq0 .. hq0 + 3.  Up to 32 slots: one
+// round trip (merge_slots_one_trip), wave j merging head j, the R_V^T rows
+// loaded beside the partials.  More slots (the small-batch shapes, many
+// window blocks): three dependent steps whatever the count (up to 256):
+// every slot's m and l of the four heads into shared memory in one round
+// trip; per head (wave) the maximum, the sum and each slot's weight; then
+// o' = sum of weight x o'_s with 32 slots' loads in flight per round trip;
+// the R_V^T rows after that.
 __device__ __forceinline__ void combine_group4(const CombineArgs& a, int b, int hq0, FusedSmem& S) {
-  constexpr int D = 128, SF = 8, SB = 32;
+  constexpr int D = 128, SB = 32;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int ns = a.nslots;
   const float* P0 = a.partials + ((size_t)b * a.Hq + hq0) * a.pstride * (D + 2);
   const float* P = P0 + (size_t)wave * a.pstride * (D + 2);
   float o0 = 0.0f, o1 = 0.0f, L = 0.0f;
   RRows<D, 4> rr;
-  if (ns <= SF) {
+  if (ns <= 32) {
     if (!a.absorb_v) rr = load_r_rows<D, 4>(a.rvT);
-    float ms[SF], ls[SF], x0[SF], x1[SF];
-#pragma unroll
-    for (int u = 0; u < SF; ++u) {
-      const float* p = P + (size_t)min(u, ns - 1) * (D + 2);
-      ms[u] = ld_partial<true>(p + D);
-      ls[u] = ld_partial<true>(p + D + 1);
-      x0[u] = ld_partial<true>(p + lane);
-      x1[u] = ld_partial<true>(p + lane + 64);
-    }
-    float M = NEG_INF;
-#pragma unroll
-    for (int u = 0; u < SF; ++u)
-      if (u < ns) M = fmaxf(M, ms[u]);
-#pragma unroll
-    for (int u = 0; u < SF; ++u) {
-      const float w = (u < ns && ms[u] != NEG_INF) ? exp2f(ms[u] - M) : 0.0f;
-      L = __builtin_fmaf(ls[u], w, L);
-      o0 = __builtin_fmaf(x0[u], w, o0);
-      o1 = __builtin_fmaf(x1[u], w, o1);
-    }
+    if (ns <= 8) merge_slots_one_trip<8>(P, ns, lane, o0, o1, L);
+    else merge_slots_one_trip<32>(P, ns, lane, o0, o1, L);
   } else {
     static_assert(4 * 2 * kMaxSplits <= sizeof(S.scratch) / sizeof(float), "merge weights");
     float* wm = S.scratch;                // [4][ns]: m, then the slot weight
