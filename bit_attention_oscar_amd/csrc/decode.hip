@@ -1316,6 +1316,7 @@ __device__ inline Tile16<KS> load_tile16(const TileStreams& st, int t0, int koff
   // in order of first use: the scale|zero words, the K codes, the V codes
   r.km = __builtin_amdgcn_raw_buffer_load_b32(st.km, moff, om, 0);
   r.vm = __builtin_amdgcn_raw_buffer_load_b32(st.vm, moff, om, 0);
+  __builtin_amdgcn_sched_barrier(0);    // keeps the issue order (loads return in it)
   if constexpr (KS) {
 #pragma unroll
     for (int tp = 0; tp < 2; ++tp) r.kq[tp] = __builtin_amdgcn_raw_buffer_load_b128(st.kc, koff + 64 * tp, oc, kStreamOnce);
@@ -1396,14 +1397,12 @@ __device__ void int2_split16(const DecodeArgs& a, const SeqView& sv, int b, int 
   int eq = 0;
 #pragma unroll
   for (int n = 0; n < NOP; ++n) qop[n] = h8{0, 0, 0, 0, 0, 0, 0, 0};
-  Tile16<KS> r[kDepth16];
-#pragma unroll
-  for (int k = 0; k < kDepth16; ++k)
-    r[k] = load_tile16<KS>(st, tile_t0(min(ti0 + k * WPB, t_last)), koff, voff, moff);
-  __builtin_amdgcn_sched_barrier(0);
+  // q first (the prologue launch wrote it: it comes back from cache ahead of
+  // the tiles, and the loads return in issue order), so the first tile's work
+  // waits for q and that tile only, not for the tiles behind it
   if (live) {
     const __amdgpu_buffer_rsrc_t qr = plane_rsrc(a.qpub + (size_t)(bh * G + grp) * kQPub, kQPub * 4);
-    if (op_live) {
+    if (op_live && wave == 0) {
 #pragma unroll
       for (int n = 0; n < NOP; ++n) {
         int gp, kc;
@@ -1414,6 +1413,13 @@ __device__ void int2_split16(const DecodeArgs& a, const SeqView& sv, int b, int 
     }
     qsum = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(qr, (512 + jh) * 4, 0, 0));
     eq = (int)__builtin_amdgcn_raw_buffer_load_b32(qr, (516 + jh) * 4, 0, 0);
+  }
+  const float vmax = a.v.smax[bh];
+  Tile16<KS> r[kDepth16];
+#pragma unroll
+  for (int k = 0; k < kDepth16; ++k) {
+    r[k] = load_tile16<KS>(st, tile_t0(min(ti0 + k * WPB, t_last)), koff, voff, moff);
+    __builtin_amdgcn_sched_barrier(0);
   }
   // the operands wait in shared memory (every wave of the block has the same
   // ones; wave 0 writes them) and are read per tile: they would otherwise hold
@@ -1430,7 +1436,6 @@ __device__ void int2_split16(const DecodeArgs& a, const SeqView& sv, int b, int 
   auto qop_at = [&](int n, int z) { return __builtin_bit_cast(h8, qop_lds[n * 64 + z]); };
   const float cK = ldexpf(1.0f, 24 - eq);         // undoes 2^eq and the 2^-24 code scale
   const float zq = ldexpf(qsum, eq - 24);         // sum(q_rot) in units of the raw dot
-  const float vmax = a.v.smax[bh];
   int ev2 = 0;
   if (vmax > 0.0f) frexpf(vmax, &ev2);
   // s_V * 2^ev < 2^15; capped so that p * 2^ev and its sums stay far from fp32
@@ -1449,10 +1454,8 @@ __device__ void int2_split16(const DecodeArgs& a, const SeqView& sv, int b, int 
   for (int s = 0; s < 4; ++s) ls[s] = pz[s] = cs[s] = 0.0f;
   uint32_t* msm = S.meta16[wave];                 // [0, 64) K, [64, 128) V scale|zero of the tile
   constexpr int NB = KS ? 2 : 4;                  // register blocks of scores (tp or tb)
-  // Everything the set-up loaded (q operands, rotation rows, the first tiles)
-  // has arrived: the tile loop then starts with only its own tiles in flight,
-  // in the order it consumes them, and waits for exactly the oldest one.
-  __builtin_amdgcn_s_waitcnt(0);
+  // The tile loop starts with only its own tiles in flight, in the order it
+  // consumes them, and each use waits for exactly the oldest one.
 
   // EDGE: the tile crosses the split's INT2 range [lo, hi) (its first or last
   // tile): tokens outside it get no weight.  A separate instantiation keeps
@@ -1591,11 +1594,14 @@ __device__ void int2_split16(const DecodeArgs& a, const SeqView& sv, int b, int 
   none.km = plane_rsrc(a.k.meta, 0);
   none.vm = plane_rsrc(a.v.meta, 0);
   none.vc = plane_rsrc(a.v.codes, 0);
+  // Rounds of kDepth16 tiles whose middle has no exit (a missing tile is
+  // skipped, its reload still issued), so every path reaches the loop head
+  // with the same loads in flight in the same order, and the first tile of a
+  // round waits for its own loads only.
   for (int i = 0; i < n; i += kDepth16) {
 #pragma unroll
     for (int k = 0; k < kDepth16; ++k) {
-      if (i + k >= n) break;
-      process(r[k], tile_of(i + k), std::true_type{});
+      if (i + k < n) process(r[k], tile_of(i + k), std::true_type{});
       r[k] = load_tile16<KS>(i + k + kDepth16 < n ? st : none, tile_of(min(i + k + kDepth16, n - 1)), koff, voff,
                              moff);
     }
