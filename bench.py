@@ -122,9 +122,12 @@ def time_prefill_attention(cache, B, Hq, Hkv, D, T, n, reps=3):
     (oscar_prefill_attn) on layer 0, timed with HIP events; median of reps.
     Useful flops: QK^T and PV over each query's causal prefix, 4 D per
     (query head, key); the matrix cores do twice that (q and p s_V each enter
-    as two bf16 pieces)."""
+    as two bf16 pieces).  head_dim 512 times at most 512 queries (a 4096-query
+    chunk at 64k context is seconds of work)."""
     import torch
-    if D != 128 or n <= 0:
+    if D == 512:
+        n = min(n, 512)
+    if D not in (128, 512) or n <= 0:
         return None
     g = torch.Generator(device="cuda")
     g.manual_seed(12345)
@@ -143,7 +146,7 @@ def time_prefill_attention(cache, B, Hq, Hkv, D, T, n, reps=3):
     return {"queries": n, "context": T, "median_ms": round(ms, 3),
             "useful_TFLOPs": round(useful / ms / 1e9, 1), "mfma_TFLOPs": round(2 * useful / ms / 1e9, 1),
             "mfma_peak_TFLOPs": 2500.0, "mfma_util": round(2 * useful / ms / 1e9 / 2500.0, 4),
-            "kernel": "prefill_attn_kernel"}
+            "kernel": "prefill_attn_kernel" if D == 128 else "prefill_attn_wide_kernel"}
 
 
 def int2_bytes_per_token_head(D):

@@ -936,11 +936,13 @@ int oscar_prefill_attn(oscar_kv* kv, int32_t layer, const void* q, void* out, in
   if (rc) return rc;
   Layer& L = kv->layers[layer];
   const auto& c = kv->cfg;
-  if (c.head_dim != 128) return fail(OSCAR_ERR_UNSUPPORTED, "prefill attention needs head_dim 128");
   if (c.codebook != OSCAR_CODEBOOK_UNIFORM)
     return fail(OSCAR_ERR_UNSUPPORTED, "prefill attention needs the uniform codebook");
-  if (64 % (c.num_q_heads / c.num_kv_heads) != 0)
-    return fail(OSCAR_ERR_UNSUPPORTED, "prefill attention needs a power-of-two number of query heads per kv head");
+  // query rows per block: 64 at head_dim 128, 16 at 512
+  const int rows = c.head_dim == 128 ? 64 : 16;
+  if (rows % (c.num_q_heads / c.num_kv_heads) != 0)
+    return fail(OSCAR_ERR_UNSUPPORTED, "prefill attention needs a power-of-two number of query heads per kv head, at "
+                                       "most " + std::to_string(rows));
   if (batch <= 0 || batch > c.max_batch) return fail(OSCAR_ERR_INVALID_ARG, "batch must be in [1, max_batch]");
   const BatchLens bl = batch_lens(L, batch);
   if (n_q < 1 || n_q > bl.min)
@@ -969,6 +971,7 @@ int oscar_prefill_attn(oscar_kv* kv, int32_t layer, const void* q, void* out, in
   a.N = c.sink_tokens;
   a.M = c.recent_tokens;
   a.T = bl.max;
+  a.D = c.head_dim;
   a.lens = bl.uniform ? nullptr : L.dlens;
   const float scale = softmax_scale > 0.0f ? softmax_scale : 1.0f / std::sqrt((float)c.head_dim);
   a.scale_log2 = scale * 1.4426950408889634f;

@@ -14,6 +14,7 @@ struct PrefillAttnArgs {
   const float* rvT;        // fp32 [D][D]: rvT[e][d] = R_V[d][e]
   int absorb_v;
   int B, n, Hq, Hkv, Gq, cap, N, M, T;
+  int D;                   // head_dim: 128 or 512
   float scale_log2;        // softmax scale * log2(e)
   const int* lens;         // ragged batch: tokens of sequence b ([B], device); null: every sequence holds T
 };

@@ -226,8 +226,9 @@ int oscar_kv_decode_step(oscar_kv* kv, int32_t layer, const void* k, const void*
  *   q:   device bf16 [batch][n_q][Hq][D], post-RoPE, un-rotated;
  *   out: device [batch][n_q][Hq][D] of out_dtype;
  *   softmax_scale <= 0 selects 1/sqrt(D).
- * head_dim 128 and the UNIFORM codebook only (UNSUPPORTED otherwise).  Nothing is allocated; the cache
- * is read only.
+ * head_dim 128 (up to 64 query heads per kv head) or 512 (up to 16), a
+ * power-of-two number of query heads per kv head, and the UNIFORM codebook
+ * (UNSUPPORTED otherwise).  Nothing is allocated; the cache is read only.
  * Errors: INVALID_ARG (including n_q < 1, n_q > some T_b of the batch),
  * UNSUPPORTED, HIP. */
 int oscar_prefill_attn(oscar_kv* kv, int32_t layer, const void* q, void* out, int32_t out_dtype,

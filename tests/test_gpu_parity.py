@@ -626,6 +626,34 @@ def test_prefill_attn_full_size_16k_sampled(ok):
 
 
 @pytest.mark.slow
+def test_prefill_attn_wide_16k_sampled(ok):
+    """Chunked-prefill attention at head_dim 512 with the wide-head model's
+    heads and windows (Hq=16, Hkv=8, sink 512, recent 2048) at 16k context,
+    batch 1: 256 queries of the last positions; the first, middle and last
+    queries of the chunk, every head, against the oracle over the exported
+    cache."""
+    from bench import fill_layer_device
+    shape = Shape(B=1, Hq=16, Hkv=8, D=512, N=512, M=2048, outliers="percent")
+    T, n = 16384, 256
+    say("[prefill attention wide 16k] filling")
+    rk, rv = make_rotations(shape, "haar")
+    gc = gpu_cache(ok, shape, rk, rv, T + 64)
+    fill_layer_device(gc, 0, shape.B, shape.Hkv, shape.D, T, seed=0, dist="normal", outliers="percent")
+    mask = synth.outlier_mask(shape.D, shape.Hkv, 0, 0, "percent")
+    qb = _prefill_q(shape, mask, n)
+    got = _prefill_gpu(gc, qb)
+    ids = [0, 1, n // 2, n - 2, n - 1]
+    kp = planes_from_export(gc.export(0, 0), T, shape.N, shape.M)
+    vp = planes_from_export(gc.export(0, 1), T, shape.N, shape.M)
+    want = orc.prefill_attention(qb, kp, vp, rk[0], rv[0], shape.Hkv, shape.N, shape.M, 128, 0, 0,
+                                 query_ids=ids)
+    e = oracle_err(got[:, ids], want)
+    say(f"  sampled queries {ids}: rel L2 {e:.3e}")
+    assert e <= ATTN_TOL
+    gc.close()
+
+
+@pytest.mark.slow
 def test_full_size_128k_gqa8_sampled(ok):
     """The 128k-context GQA-8 shape (B=8, Hq=64, Hkv=8, D=128, N=64, M=256,
     Student-t(3) values) on one layer, filled on the device, one fused step
@@ -862,6 +890,17 @@ def _prefill_oracle(gc, qb, shape, rk, rv, absorb_v=False):
     (Shape(B=1, Hq=8, Hkv=2, N=16, M=64), 63, 80),              # at position 63: tile 0 unmasked, exactly full
     (Shape(B=1, Hq=8, Hkv=2, N=16, M=64), 62, 81),              # at position 62: tile 0 still masked
     (Shape(B=2, Hq=2, Hkv=2, N=0, M=0), 127, 64),               # 1 head, at position 127: two unmasked INT2 tiles first
+    # head_dim 512 (16 query rows per block, 32-token key tiles)
+    (Shape(B=1, Hq=4, Hkv=2, D=512, N=16, M=64), 300, 70),      # 2 query heads per kv head
+    (Shape(B=2, Hq=2, Hkv=2, D=512, N=16, M=64), 200, 33),      # 1 per kv head
+    (Shape(B=1, Hq=8, Hkv=2, D=512, N=16, M=64, v_dtype=1), 250, 40),   # 4 per kv head, bf16 V plane
+    (Shape(B=1, Hq=4, Hkv=2, D=512, N=0, M=0), 100, 50),        # no windows
+    (Shape(B=1, Hq=4, Hkv=2, D=512, N=40, M=60), 0, 70),        # all window
+    (Shape(B=1, Hq=32, Hkv=2, D=512, N=16, M=64), 120, 9),      # 16 per kv head (one query per block)
+    (Shape(B=1, Hq=4, Hkv=2, D=512, N=3, M=500), 600, 45),      # recent window longer than the chunk
+    (Shape(B=1, Hq=4, Hkv=2, D=512, N=16, M=64), 31, 40),       # first query at position 31: tile 0 unmasked
+    (Shape(B=1, Hq=4, Hkv=2, D=512, N=16, M=64), 30, 41),       # at position 30: tile 0 masked
+    (Shape(B=1, Hq=4, Hkv=2, D=512, N=16, M=64, k_dtype=1), 150, 30),   # bf16 K plane
 ])
 def test_prefill_attn_vs_oracle(ok, shape, T0, n):
     """Chunked-prefill attention through the C ABI against the oracle over the
@@ -904,11 +943,12 @@ def test_prefill_attn_last_query_is_decode(ok):
     gc.close()
 
 
-def test_prefill_attn_absorbed_and_dtypes(ok):
+@pytest.mark.parametrize("D", [128, 512])
+def test_prefill_attn_absorbed_and_dtypes(ok, D):
     """absorb_v_rotation = 1 returns o' (the oracle's o'); bf16 and fp16
     outputs are the fp32 output rounded."""
-    shape = Shape(B=1, Hq=8, Hkv=2, N=16, M=64)
-    say("[prefill attention] absorbed V rotation, output dtypes")
+    shape = Shape(B=1, Hq=8, Hkv=2, D=D, N=16, M=64)
+    say(f"[prefill attention] absorbed V rotation, output dtypes, D={D}")
     rk, rv = make_rotations(shape, "haar")
     T0, n = 300, 90
     k, v, mask = inputs(shape, T0 + n)
@@ -926,7 +966,8 @@ def test_prefill_attn_absorbed_and_dtypes(ok):
 
 def test_prefill_attn_rejects(ok):
     """Argument checks before anything is enqueued: n_q beyond the cached
-    tokens, a batch other than the layer's, head_dim 512."""
+    tokens, a batch other than the layer's, a number of query heads per kv
+    head that does not divide the 16 query rows of a head_dim-512 block."""
     shape = Shape(B=1, Hq=8, Hkv=2, N=16, M=64)
     rk, rv = make_rotations(shape, "haar")
     k, v, mask = inputs(shape, 40)
@@ -939,12 +980,12 @@ def test_prefill_attn_rejects(ok):
     with pytest.raises(ok.OscarError):
         ok.oscar_prefill_attn(gc.handle, 0, q, out, 0, 2, 4)
     gc.close()
-    wide = Shape(B=1, Hq=4, Hkv=2, D=512, N=16, M=64)
+    wide = Shape(B=1, Hq=6, Hkv=2, D=512, N=16, M=64)
     gw = gpu_cache(ok, wide, None, None, 64)
     kw, vw, _ = inputs(wide, 10)
     gw.append(0, dev(kw), dev(vw))
-    qw = torch.zeros((1, 2, 4, 512), dtype=torch.bfloat16, device="cuda")
-    ow = torch.zeros((1, 2, 4, 512), dtype=torch.float32, device="cuda")
+    qw = torch.zeros((1, 2, 6, 512), dtype=torch.bfloat16, device="cuda")
+    ow = torch.zeros((1, 2, 6, 512), dtype=torch.float32, device="cuda")
     with pytest.raises(ok.OscarError):
         gw.prefill_attn(0, qw, ow)
     gw.close()

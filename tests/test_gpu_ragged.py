@@ -190,12 +190,13 @@ def test_ragged_batch_append(ok, shape, n):
     gc.close()
 
 
-def test_ragged_prefill_attn(ok):
+@pytest.mark.parametrize("D", [128, 512])
+def test_ragged_prefill_attn(ok, D):
     """Prefill attention over a ragged batch: the last n_q positions of each
     sequence attend causally over that sequence's own tokens."""
-    shape = Shape(B=3, Hq=8, Hkv=2, D=128, N=16, M=64)
-    lengths = [130, 700, 90]
-    n_q = 70
+    shape = Shape(B=3, Hq=8, Hkv=2, D=D, N=16, M=64)
+    lengths = [130, 700, 90] if D == 128 else [70, 300, 45]
+    n_q = 70 if D == 128 else 40
     rk, rv = make_rotations(shape, "haar")
     k, v, mask = inputs(shape, max(lengths))
     gc = gpu_cache(ok, shape, rk, rv, max(lengths))
