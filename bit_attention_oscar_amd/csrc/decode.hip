@@ -436,6 +436,12 @@ __device__ inline float ld_partial(const float* p) {
   if (COHERENT) return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   return *p;
 }
+// two consecutive partial floats (8-byte aligned) in one device-scope load
+__device__ inline float2 ld_partial2(const float* p) {
+  const uint64_t v = __hip_atomic_load(reinterpret_cast<const uint64_t*>(p), __ATOMIC_RELAXED,
+                                       __HIP_MEMORY_SCOPE_AGENT);
+  return make_float2(__uint_as_float((uint32_t)v), __uint_as_float((uint32_t)(v >> 32)));
+}
 
 // One output element in the requested dtype.
 __device__ inline void store_out(const CombineArgs& a, size_t o, float v) {
@@ -841,25 +847,20 @@ __device__ void combine_fused(const CombineArgs& a, int bh, FusedSmem& S) {
   for (int g = 0; g < G; ++g) combine_group4(a, b, kvh * 4 * G + 4 * g, S);
 }
 
-// One-round-trip merge of up to SF slots for head `wave` (lane l: dims l and
-// l + 64): lane s < ns loads slot s's m and l, every lane loads its two dims of
-// every slot's o', all in flight together; the slot weights are formed in the
-// lanes that hold them and read by every lane (v_readlane), and o' is summed in
-// slot order.
+// One-round-trip merge of up to SF slots for head `wave` (lane l: dims 2 l and
+// 2 l + 1): lane s < ns loads slot s's m and l, every lane loads its two dims of
+// every slot's o' (one 8-byte load each), all in flight together; the slot
+// weights are formed in the lanes that hold them and read by every lane
+// (v_readlane), and o' is summed in slot order.
 template <int SF>
 __device__ __forceinline__ void merge_slots_one_trip(const float* P, int ns, int lane, float& o0, float& o1,
                                                      float& L) {
   constexpr int D = 128;
-  const float* ps = P + (size_t)min(lane, ns - 1) * (D + 2);
-  const float ml = ld_partial<true>(ps + D);
-  const float ll = ld_partial<true>(ps + D + 1);
-  float x0[SF], x1[SF];
+  const float2 mlp = ld_partial2(P + (size_t)min(lane, ns - 1) * (D + 2) + D);
+  const float ml = mlp.x, ll = mlp.y;
+  float2 x[SF];
 #pragma unroll
-  for (int u = 0; u < SF; ++u) {
-    const float* p = P + (size_t)min(u, ns - 1) * (D + 2);
-    x0[u] = ld_partial<true>(p + lane);
-    x1[u] = ld_partial<true>(p + lane + 64);
-  }
+  for (int u = 0; u < SF; ++u) x[u] = ld_partial2(P + (size_t)min(u, ns - 1) * (D + 2) + 2 * lane);
   const bool mine = lane < ns && ml != NEG_INF;
   const float M = wmax(mine ? ml : NEG_INF);
   const float w = mine ? exp2f(ml - M) : 0.0f;
@@ -868,15 +869,15 @@ __device__ __forceinline__ void merge_slots_one_trip(const float* P, int ns, int
   for (int u = 0; u < SF; ++u) {
     if (u < ns) {
       const float wu = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w), u));
-      o0 = __builtin_fmaf(x0[u], wu, o0);
-      o1 = __builtin_fmaf(x1[u], wu, o1);
+      o0 = __builtin_fmaf(x[u].x, wu, o0);
+      o1 = __builtin_fmaf(x[u].y, wu, o1);
     }
   }
 }
 
-// Merge and un-rotation of query heads hq0 .. hq0 + 3.  Up to 32 slots: one
-// round trip (merge_slots_one_trip), wave j merging head j, the R_V^T rows
-// loaded beside the partials.  More slots (the small-batch shapes, many
+// Merge and un-rotation of query heads hq0 .. hq0 + 3 (wave j merges head j,
+// lane l dims 2 l and 2 l + 1).  Up to 32 slots: one round trip
+// (merge_slots_one_trip), the R_V^T rows loaded beside the partials.  More slots (the small-batch shapes, many
 // window blocks): three dependent steps whatever the count (up to 256):
 // every slot's m and l of the four heads into shared memory in one round
 // trip; per head (wave) the maximum, the sum and each slot's weight; then
@@ -919,18 +920,14 @@ __device__ __forceinline__ void combine_group4(const CombineArgs& a, int b, int 
     __builtin_amdgcn_s_waitcnt(kWaitLds);  // the wave's weights, written by its own lanes, are read below
     __builtin_amdgcn_wave_barrier();
     for (int s0 = 0; s0 < ns; s0 += SB) {
-      float x0[SB], x1[SB];
+      float2 x[SB];
 #pragma unroll
-      for (int u = 0; u < SB; ++u) {
-        const float* p = P + (size_t)min(s0 + u, ns - 1) * (D + 2);
-        x0[u] = ld_partial<true>(p + lane);
-        x1[u] = ld_partial<true>(p + lane + 64);
-      }
+      for (int u = 0; u < SB; ++u) x[u] = ld_partial2(P + (size_t)min(s0 + u, ns - 1) * (D + 2) + 2 * lane);
 #pragma unroll
       for (int u = 0; u < SB; ++u) {
         const float w = s0 + u < ns ? wm[wave * ns + s0 + u] : 0.0f;
-        o0 = __builtin_fmaf(x0[u], w, o0);
-        o1 = __builtin_fmaf(x1[u], w, o1);
+        o0 = __builtin_fmaf(x[u].x, w, o0);
+        o1 = __builtin_fmaf(x[u].y, w, o1);
       }
     }
     __syncthreads();                      // every wave is done with the weights (scratch is reused)
@@ -938,14 +935,14 @@ __device__ __forceinline__ void combine_group4(const CombineArgs& a, int b, int 
   }
   const float inv = 1.0f / L;
   if (a.absorb_v) {                       // o' in the V-rotated basis
-    store_out(a, ((size_t)b * a.Hq + hq0 + wave) * D + lane, o0 * inv);
-    store_out(a, ((size_t)b * a.Hq + hq0 + wave) * D + lane + 64, o1 * inv);
+    store_out(a, ((size_t)b * a.Hq + hq0 + wave) * D + 2 * lane, o0 * inv);
+    store_out(a, ((size_t)b * a.Hq + hq0 + wave) * D + 2 * lane + 1, o1 * inv);
     return;
   }
   float* os = S.scratch;                  // [4][128]
   float* part = S.scratch + 4 * D;        // [4 waves][4][128]
-  os[wave * D + lane] = o0 * inv;
-  os[wave * D + lane + 64] = o1 * inv;
+  os[wave * D + 2 * lane] = o0 * inv;
+  os[wave * D + 2 * lane + 1] = o1 * inv;
   __syncthreads();
   rotate_rows_regs<D, 4, 4>(os, rr, part);
   __syncthreads();
