@@ -2041,12 +2041,15 @@ __device__ inline TileStreams wide_tile_streams(const DecodeArgs& a, int bh, int
 __device__ inline TileRegs wide_load_tile(const TileStreams& s, int t0, int lane_c, int lane_m) {
   const int oc = t0 * 128, om = t0 * 4;
   TileRegs r;
+  // in order of first use (loads return in issue order)
   r.k0 = __builtin_amdgcn_raw_buffer_load_b128(s.kc, lane_c, oc, kStreamOnce);
   r.k1 = __builtin_amdgcn_raw_buffer_load_b128(s.kc, lane_c + 1024, oc, kStreamOnce);
   r.km = __builtin_amdgcn_raw_buffer_load_b128(s.km, lane_m, om, 0);
   r.vm = __builtin_amdgcn_raw_buffer_load_b128(s.vm, lane_m, om, 0);
+  __builtin_amdgcn_sched_barrier(0);
   r.v0 = __builtin_amdgcn_raw_buffer_load_b128(s.vc, lane_c, oc, kStreamOnce);
   r.v1 = __builtin_amdgcn_raw_buffer_load_b128(s.vc, lane_c + 1024, oc, kStreamOnce);
+  __builtin_amdgcn_sched_barrier(0);
   return r;
 }
 
@@ -2251,19 +2254,20 @@ void decode_wide_kernel(DecodeArgs a) {
   const TileStreams st = wide_tile_streams(a, bh, wave);
   const int lane_c = 2048 * wave + lane * 16, lane_m = blk * 16;
   auto tile_t0 = [&](int ti) { return (tile_first + ti) << 6; };
-  TileRegs r[kDepth];
-#pragma unroll
-  for (int k = 0; k < kDepth; ++k) r[k] = wide_load_tile(st, tile_t0(min(s_t0 + k, t_last)), lane_c, lane_m);
-
   // this slice's q operands (written by the rotation launch before this one)
+  // and the V-scale maximum first: the first tile's work then waits for them
+  // and that tile only (loads return in issue order)
   h4 qv[1][8];
   float qsum;
   int eq;
   const uint2* qlp[1] = {wide_q_operands(a, bh * 4 + wave, W.qlo[wave], qv[0], qsum, eq)};
+  const float vmax = a.v.smax[bh];
+  TileRegs r[kDepth];
+#pragma unroll
+  for (int k = 0; k < kDepth; ++k) r[k] = wide_load_tile(st, tile_t0(min(s_t0 + k, t_last)), lane_c, lane_m);
   __syncthreads();                        // W.qlo complete
   const float cK = ldexpf(1.0f, 24 - eq);
   const float zq = ldexpf(qsum, eq - 24);
-  const float vmax = a.v.smax[bh];
   int ev2 = 0;
   if (vmax > 0.0f) frexpf(vmax, &ev2);
   const int ev = (vmax > 0.0f) ? min(15 - ev2, 60) : 0;
@@ -2342,15 +2346,26 @@ void decode_wide_kernel(DecodeArgs a) {
     pv_word<1, 7>(cur.v1.w, pv1, pl1, o0, o1);
   };
 
+  // Rounds of kDepth tiles with no exit in the middle (a missing tile is
+  // skipped, its reload still issued, through zero-length resources past the
+  // split's last tile): every path reaches the loop head with the same loads
+  // in flight in the same order, so a tile's work waits for its own loads
+  // only (with an exit after each tile the loop head waited for every load)
+  TileStreams none = st;
+  none.kc = plane_rsrc(a.k.codes, 0);
+  none.km = plane_rsrc(a.k.meta, 0);
+  none.vm = plane_rsrc(a.v.meta, 0);
+  none.vc = plane_rsrc(a.v.codes, 0);
   int buf = 0;
   for (int ti = s_t0; ti < s_t1; ti += kDepth) {
 #pragma unroll
     for (int k = 0; k < kDepth; ++k) {
       const int t = ti + k;
-      if (t >= s_t1) break;
-      process(r[k], tile_t0(t), buf);
-      buf ^= 1;
-      if (t + kDepth < s_t1) r[k] = wide_load_tile(st, tile_t0(t + kDepth), lane_c, lane_m);
+      if (t < s_t1) {
+        process(r[k], tile_t0(t), buf);
+        buf ^= 1;
+      }
+      r[k] = wide_load_tile(t + kDepth < s_t1 ? st : none, tile_t0(min(t + kDepth, t_last)), lane_c, lane_m);
     }
   }
 
