@@ -2083,21 +2083,27 @@ __device__ void wide_split_bf16v(const DecodeArgs& a, int bh, int b, int h, int 
   struct KRegs {
     u4 k0, k1, km;
   };
-  auto load_k = [&](int t0) {
+  // past the split's last tile the loads go through zero-length resources
+  TileStreams none = st;
+  none.kc = plane_rsrc(a.k.codes, 0);
+  none.km = plane_rsrc(a.k.meta, 0);
+  auto load_k = [&](int t0, bool live_tile = true) {
+    const TileStreams& s = live_tile ? st : none;
     KRegs r;
-    r.k0 = __builtin_amdgcn_raw_buffer_load_b128(st.kc, lane_c, t0 * 128, kStreamOnce);
-    r.k1 = __builtin_amdgcn_raw_buffer_load_b128(st.kc, lane_c + 1024, t0 * 128, kStreamOnce);
-    r.km = __builtin_amdgcn_raw_buffer_load_b128(st.km, lane_m, t0 * 4, 0);
+    r.k0 = __builtin_amdgcn_raw_buffer_load_b128(s.kc, lane_c, t0 * 128, kStreamOnce);
+    r.k1 = __builtin_amdgcn_raw_buffer_load_b128(s.kc, lane_c + 1024, t0 * 128, kStreamOnce);
+    r.km = __builtin_amdgcn_raw_buffer_load_b128(s.km, lane_m, t0 * 4, 0);
     return r;
   };
-  KRegs r[kDepth];
-#pragma unroll
-  for (int k = 0; k < kDepth; ++k) r[k] = load_k(tile_t0(min(s_t0 + k, t_last)));
-
+  // q operands first (loads return in issue order: the first tile's work
+  // then waits for q and that tile only)
   h4 qv[1][8];
   float qsum;
   int eq;
   const uint2* qlp[1] = {wide_q_operands(a, bh * 4 + wave, W.qlo[wave], qv[0], qsum, eq)};
+  KRegs r[kDepth];
+#pragma unroll
+  for (int k = 0; k < kDepth; ++k) r[k] = load_k(tile_t0(min(s_t0 + k, t_last)));
   __syncthreads();                        // W.qlo complete
   const float cK = ldexpf(1.0f, 24 - eq);
   const float zq = ldexpf(qsum, eq - 24);
@@ -2179,13 +2185,13 @@ __device__ void wide_split_bf16v(const DecodeArgs& a, int bh, int b, int h, int 
     }
   };
 
+  // rounds of kDepth tiles with no exit in the middle (as in the INT2 splits)
   for (int ti = s_t0; ti < s_t1; ti += kDepth) {
 #pragma unroll
     for (int k = 0; k < kDepth; ++k) {
       const int t = ti + k;
-      if (t >= s_t1) break;
-      process(r[k], tile_t0(t));
-      if (t + kDepth < s_t1) r[k] = load_k(tile_t0(t + kDepth));
+      if (t < s_t1) process(r[k], tile_t0(t));
+      r[k] = load_k(tile_t0(min(t + kDepth, t_last)), t + kDepth < s_t1);
     }
   }
 
