@@ -240,50 +240,29 @@ __device__ inline float rot_sum(const float* part, int tk, int d) {
   return v + 0.0f;   // -0 -> +0
 }
 
-// Append of tokens [t_lo, t_hi) (at most NT, all in one 8-token group) of one
-// (sequence, kv head) to plane K (isv = false) or V.  Block = 64 * WAVES
-// threads; xs holds NT*D floats and part WAVES*NT*D floats of shared memory.
-// Wave 0's lane l owns dims l + 64 i, so it also owns the V tile bytes of those
-// dims for every token of the group (tiled-layout bytes are shared only among
-// tokens of one group of 8 at one dim, and one block handles the whole group).
-template <int D, int WAVES, int NT, bool LM = false>
-__device__ inline void append_block(const AppendArgs& a, int bh, bool isv, int t_lo, int t_hi, int T_old, int T_new,
-                                    float* xs, float* part) {
+// A bf16 window value (sink or ring row).  CW: a device-scope store, visible
+// to blocks on every XCD once it completes, for a launch whose other blocks
+// read the row after this one signals them.
+template <bool CW>
+__device__ inline void put_window(uint16_t* p, float x) {
+  if constexpr (CW)
+    __hip_atomic_store(p, f32_to_bf16(x), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  else
+    *p = f32_to_bf16(x);
+}
+
+// Wave 0's part of an append, after the rotation: for each token, the rotated
+// row from the partial sums in part (rot_sum), the window rows, the group
+// statistics, codes and scale|zero words.  vbyte: with one token, the V code
+// bytes of the lane's dims, loaded beforehand.
+template <int D, int WAVES, int NT, bool LM, bool CW>
+__device__ inline void append_tail(const AppendArgs& a, int bh, bool isv, int t_lo, int ntok, int T_old, int T_new,
+                                   const float* part, const uint8_t (&vbyte)[D / 64]) {
   constexpr int PER = D / 64;
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int lane = threadIdx.x & 63;
   const int b = bh / a.Hkv, h = bh - (bh / a.Hkv) * a.Hkv;
   const PlaneDev P = isv ? a.v : a.k;
-  const uint16_t* in = isv ? a.vin : a.kin;
-  const float* R = isv ? a.rv : a.rk;
   float* dump = isv ? a.vdump : a.kdump;
-  const int ntok = t_hi - t_lo;
-
-  auto load_inputs = [&]() {
-    for (int i = tid; i < NT * D; i += 64 * WAVES) {
-      const int tk = i / D, d = i - (i / D) * D;
-      float v = 0.0f;
-      if (tk < ntok) {
-        const int t = t_lo + tk;
-        const size_t idx = (((size_t)b * a.n_new + (t - T_old)) * a.Hkv + h) * D + d;
-        v = bf16_to_f32(in[idx]);
-      }
-      xs[i] = v;
-    }
-  };
-  if constexpr (D == 128 && WAVES == 4) {
-    // R rows and inputs in one round trip
-    const RRows<D, WAVES> rr = load_r_rows<D, WAVES>(R);
-    load_inputs();
-    __syncthreads();
-    rotate_rows_regs<D, WAVES, NT>(xs, rr, part);
-  } else {
-    load_inputs();
-    __syncthreads();
-    rotate_rows<D, WAVES, NT>(xs, R, part, ntok);
-  }
-  __syncthreads();
-  if (wave != 0) return;
-
 #pragma unroll
   for (int tk = 0; tk < NT; ++tk) {
     if (tk >= ntok) break;
@@ -305,12 +284,12 @@ __device__ inline void append_block(const AppendArgs& a, int bh, bool isv, int t
     if (t < a.N) {
       const size_t base = row_offset(bh, a.N, t, D);
 #pragma unroll
-      for (int i = 0; i < PER; ++i) P.sink[base + lane + 64 * i] = f32_to_bf16(x[i]);
+      for (int i = 0; i < PER; ++i) put_window<CW>(P.sink + base + lane + 64 * i, x[i]);
     }
     if (a.M > 0 && t >= a.N && t >= T_new - a.M) {
       const size_t base = row_offset(bh, a.M, t % a.M, D);
 #pragma unroll
-      for (int i = 0; i < PER; ++i) P.ring[base + lane + 64 * i] = f32_to_bf16(x[i]);
+      for (int i = 0; i < PER; ++i) put_window<CW>(P.ring + base + lane + 64 * i, x[i]);
     }
     uint32_t code[PER];
 #pragma unroll
@@ -342,11 +321,114 @@ __device__ inline void append_block(const AppendArgs& a, int bh, bool isv, int t
       for (int i = 0; i < PER; ++i) {
         int bit;
         const size_t off = vcode_byte(bh, a.cap, t, lane + 64 * i, D, &bit);
-        const uint8_t old = P.codes[off];
+        const uint8_t old = NT == 1 ? vbyte[i] : P.codes[off];
         P.codes[off] = (uint8_t)((old & ~(3u << bit)) | (code[i] << bit));
       }
     }
   }
+}
+
+// Append of tokens [t_lo, t_hi) (at most NT, all in one 8-token group) of one
+// (sequence, kv head) to plane K (isv = false) or V.  Block = 64 * WAVES
+// threads; xs holds NT*D floats and part WAVES*NT*D floats of shared memory.
+// Wave 0's lane l owns dims l + 64 i, so it also owns the V tile bytes of those
+// dims for every token of the group (tiled-layout bytes are shared only among
+// tokens of one group of 8 at one dim, and one block handles the whole group).
+// With one token (NT = 1) those bytes are loaded together with the inputs, so
+// that their rewrite needs no second memory round trip.  CW: the window rows
+// are written with device-scope stores (put_window).
+template <int D, int WAVES, int NT, bool LM = false, bool CW = false>
+__device__ inline void append_block(const AppendArgs& a, int bh, bool isv, int t_lo, int t_hi, int T_old, int T_new,
+                                    float* xs, float* part) {
+  constexpr int PER = D / 64;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int b = bh / a.Hkv, h = bh - (bh / a.Hkv) * a.Hkv;
+  const PlaneDev P = isv ? a.v : a.k;
+  const uint16_t* in = isv ? a.vin : a.kin;
+  const float* R = isv ? a.rv : a.rk;
+  const int ntok = t_hi - t_lo;
+  uint8_t vbyte[PER];                  // NT = 1, tiled plane: the code bytes of the token's dims
+#pragma unroll
+  for (int i = 0; i < PER; ++i) vbyte[i] = 0;
+  if constexpr (NT == 1) {
+    if (wave == 0 && ntok > 0 && !P.is_bf16 && P.tiled) {
+#pragma unroll
+      for (int i = 0; i < PER; ++i) {
+        int bit;
+        vbyte[i] = P.codes[vcode_byte(bh, a.cap, t_lo, lane + 64 * i, D, &bit)];
+      }
+    }
+  }
+
+  auto load_inputs = [&]() {
+    for (int i = tid; i < NT * D; i += 64 * WAVES) {
+      const int tk = i / D, d = i - (i / D) * D;
+      float v = 0.0f;
+      if (tk < ntok) {
+        const int t = t_lo + tk;
+        const size_t idx = (((size_t)b * a.n_new + (t - T_old)) * a.Hkv + h) * D + d;
+        v = bf16_to_f32(in[idx]);
+      }
+      xs[i] = v;
+    }
+  };
+  if constexpr (D == 128 && WAVES == 4) {
+    // R rows and inputs in one round trip
+    const RRows<D, WAVES> rr = load_r_rows<D, WAVES>(R);
+    load_inputs();
+    __syncthreads();
+    rotate_rows_regs<D, WAVES, NT>(xs, rr, part);
+  } else {
+    load_inputs();
+    __syncthreads();
+    rotate_rows<D, WAVES, NT>(xs, R, part, ntok);
+  }
+  __syncthreads();
+  if (wave != 0) return;
+  append_tail<D, WAVES, NT, LM, CW>(a, bh, isv, t_lo, ntok, T_old, T_new, part, vbyte);
+}
+
+// One-token append at head_dim 128 (4 waves) in two steps, for a block that
+// issues other loads between them: append_one_loads issues every load the
+// append needs (this lane's R rows as load_r_rows takes them, the token's
+// input value in threads < 128, wave 0's V code bytes); append_one_finish does
+// the rest exactly as append_block<128, 4, 1> does (same rotation, same bits).
+struct AppendOneLoads {
+  RRows<128, 4> rr;
+  float x;
+  uint8_t vbyte[2];
+};
+
+__device__ __forceinline__ AppendOneLoads append_one_loads(const AppendArgs& a, int bh, bool isv, int t, int T_old) {
+  constexpr int D = 128;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int b = bh / a.Hkv, h = bh - (bh / a.Hkv) * a.Hkv;
+  const PlaneDev P = isv ? a.v : a.k;
+  const uint16_t* in = isv ? a.vin : a.kin;
+  AppendOneLoads L;
+  L.vbyte[0] = L.vbyte[1] = 0;
+  if (wave == 0 && !P.is_bf16 && P.tiled) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      int bit;
+      L.vbyte[i] = P.codes[vcode_byte(bh, a.cap, t, lane + 64 * i, D, &bit)];
+    }
+  }
+  L.rr = load_r_rows<D, 4>(isv ? a.rv : a.rk);
+  L.x = 0.0f;
+  if (tid < D) L.x = bf16_to_f32(in[(((size_t)b * a.n_new + (t - T_old)) * a.Hkv + h) * D + tid]);
+  return L;
+}
+
+template <bool CW>
+__device__ __forceinline__ void append_one_finish(const AppendArgs& a, int bh, bool isv, int t, int T_old, int T_new,
+                                         const AppendOneLoads& L, float* xs, float* part) {
+  if (threadIdx.x < 128) xs[threadIdx.x] = L.x;
+  __syncthreads();
+  rotate_rows_regs<128, 4, 1>(xs, L.rr, part);
+  __syncthreads();
+  if ((threadIdx.x >> 6) != 0) return;
+  append_tail<128, 4, 1, false, CW>(a, bh, isv, t, 1, T_old, T_new, part, L.vbyte);
 }
 
 // acc[j][c] += xs[j * xstride + e] * R[e][col + c] for e in [e0, e0 + EW)

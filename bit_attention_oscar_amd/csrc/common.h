@@ -192,7 +192,8 @@ struct DecodeArgs {
   PlaneDev k, v;
   const float* qrot;       // rotated q of the general kernel
   float* qpub;             // [B*Hkv*G][kQPub]: rotated q of each head group, written by the
-                           // prologue launch before the matrix-core attention launch
+                           // prologue launch before an attention launch that does not rotate
+                           // q itself (head_dim 128), or by the q rotation launch (512)
   float* partials;         // [B][Hq][pstride][D+2]
   int pstride;             // partial slots per (sequence, query head)
   int Hq, Hkv, D, cap, N, M, T;
@@ -206,7 +207,12 @@ struct DecodeArgs {
   const uint16_t* q;       // bf16 [B][Hq][D] (matrix-core launch rotates q itself)
   const float* rk;         // fp32 [D][D] of this layer
   float scale_log2;        // softmax scale * log2(e)
-  int app_blocks;          // 2 when the prologue launch also appends this step's token, else 0
+  int app_blocks;          // 2 when the launch also appends this step's token, else 0; a
+                           // self-rotating head_dim-128 launch then points app.v.smax at a
+                           // per-(sequence, kv head) pending slot (zero between launches)
+  int self_rotate;         // head_dim 128: 1 = the attention launch is the whole call (every
+                           // block rotates its q; the window block holding a step's token
+                           // appends it); 0 = decode_prologue_kernel ran first
   int int2_lead;           // INT2 splits dispatched before the window blocks
   int win_blocks;          // window blocks of the launch (win.splits)
   int one_round;           // 1: one block per INT2 split and nothing else, every block resident at
@@ -228,9 +234,9 @@ hipError_t launch_quantize_rows(const float* x, int rows, int D, float clip, int
 hipError_t launch_qrot(const QRotArgs& a, hipStream_t s);
 hipError_t launch_decode_valu(const DecodeArgs& a, int B, hipStream_t s);
 hipError_t launch_decode_mfma(const DecodeArgs& a, int B, int waves_per_block, hipStream_t s);
-int decode_mfma_resident_blocks(int device, int G);   // blocks of the matrix-core kernel resident at once
 hipError_t launch_decode_prologue(const DecodeArgs& a, int B, hipStream_t s);  // head_dim 128: q records
                                                                                // (and the step's append)
+int decode_mfma_resident_blocks(int device, int G);   // blocks of the matrix-core kernel resident at once
 hipError_t launch_combine(const CombineArgs& a, hipStream_t s);
 hipError_t launch_wide_qrot(const DecodeArgs& a, int B, hipStream_t s);     // head_dim 512: rotated q records
                                                                             // (and the step's append when a.app_blocks)

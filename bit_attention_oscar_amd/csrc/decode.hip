@@ -25,6 +25,7 @@
 //                       head_dim 512 (q records, INT2 K with INT2 or bf16 V)
 //   combine_kernel      log-sum-exp merge of the splits and o = o' @ R_V^T
 #include <math.h>
+#include <algorithm>
 #include <type_traits>
 #include "append_impl.h"
 
@@ -607,7 +608,19 @@ __device__ inline void finish_block(const DecodeArgs& a, int bh, FusedSmem& S) {
   __syncthreads();
   if (!is_last) return;
   combine_fused<G>(a.comb, bh, S);
-  if (threadIdx.x == 0) a.counters[bh] = 0u;
+  if (threadIdx.x == 0) {
+    if (a.app_blocks > 0) {
+      // the appended token's V scale joins the running maximum only now, when
+      // no block of the launch reads the maximum any more (the block that
+      // appended counted itself after its stores completed)
+      unsigned* pend = reinterpret_cast<unsigned*>(a.app.v.smax + bh);
+      const unsigned sf = __hip_atomic_load(pend, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_fetch_max(reinterpret_cast<unsigned*>(a.v.smax + bh), sf, __ATOMIC_RELAXED,
+                             __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(pend, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    __hip_atomic_store(a.counters + bh, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
 }
 
 // bf16 window tokens (sink + recent) of one (sequence, kv head): one block of
@@ -716,7 +729,7 @@ __device__ inline QRotLoads q_rotation_loads(const DecodeArgs& a, int b, int hq0
   return s;
 }
 
-__device__ void q_rotation_finish(const DecodeArgs& a, const QRotLoads& s, FusedSmem& S) {
+__device__ __forceinline__ void q_rotation_finish(const DecodeArgs& a, const QRotLoads& s, FusedSmem& S) {
   constexpr int D = 128;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   float* qraw = S.scratch;            // [4][128]
@@ -810,9 +823,9 @@ __device__ inline uint32_t q_operand16_pair(const FusedSmem& S, int j, int g, in
   return out;
 }
 
-// The q record of one head group, written by the decode prologue launch for
-// the attention launch that follows it.
-__device__ void publish_q(const DecodeArgs& a, int pidx, FusedSmem& S) {
+// The q record of one head group, written by a producer block of the decode
+// launch for its attention blocks.
+__device__ __forceinline__ void publish_q(const DecodeArgs& a, int pidx, FusedSmem& S) {
   float* dst = a.qpub + (size_t)pidx * kQPub;
   const int tid = threadIdx.x;
   for (int i = tid; i < 4 * 128; i += blockDim.x) st_partial(dst + i, S.qs[i >> 7][i & 127]);
@@ -841,7 +854,6 @@ __device__ void publish_q(const DecodeArgs& a, int pidx, FusedSmem& S) {
 // over e across the four waves and adds the partial sums in a fixed order.
 template <int G>
 __device__ void combine_fused(const CombineArgs& a, int bh, FusedSmem& S) {
-  constexpr int D = 128;
   const int b = bh / a.Hkv, kvh = bh - (bh / a.Hkv) * a.Hkv;
 #pragma unroll
   for (int g = 0; g < G; ++g) combine_group4(a, b, kvh * 4 * G + 4 * g, S);
@@ -964,21 +976,24 @@ __device__ void load_published_q(const DecodeArgs& a, int pidx, FusedSmem& S) {
   __syncthreads();
 }
 
-// q of head group g of a window block into shared memory.
+// q of head group g of a window block into shared memory (S.qs, S.qsum,
+// S.qeq): SELF, rotated by the block itself (R_K rows and the raw q in one
+// round trip); else from the record of the prologue launch.
+template <bool SELF>
 __device__ inline void window_q_group(const DecodeArgs& a, int bh, int g, FusedSmem& S) {
-  load_published_q(a, bh * a.G + g, S);
+  if constexpr (SELF) {
+    const int b = bh / a.Hkv, h = bh - (bh / a.Hkv) * a.Hkv;
+    const QRotLoads ql = q_rotation_loads(a, b, h * 4 * a.G + 4 * g);
+    q_rotation_finish(a, ql, S);
+  } else {
+    load_published_q(a, bh * a.G + g, S);
+  }
 }
 
-// Window blocks.  When the launch also appends a token, that token is the
-// last window position; its window value is computed by the window block from
-// the input with the append's own arithmetic instead of being read back (the
-// append blocks write it in this same launch).
-//
 // Row loads of one 64-token pass of a window block: the K pieces a thread
 // scores (token tid/4, dims 32 (tid%4) .. +32) and the V pieces it
-// accumulates (tokens tid/16 + 16 i, dims 8 (tid%16) .. +8).  Rows of the
-// token appended in this launch are not loaded (the block computes them);
-// slots past the pass are zero.
+// accumulates (tokens tid/16 + 16 i, dims 8 (tid%16) .. +8); slots past the
+// pass are zero.
 struct WinRows {
   uint4 k[4];
   uint4 v[4];
@@ -1020,21 +1035,20 @@ __device__ inline WinRows window_first_rows(const DecodeArgs& a, const SeqView& 
 // head group of 4 query heads in turn.  first: the first pass's rows, already
 // issued (later passes, and the passes of later groups, load theirs at their
 // start; a later group loads its first pass's rows again, from cache, rather
-// than hold them in registers).  q comes from the record the prologue launch
-// wrote.
+// than hold them in registers).  q: window_q_group.
 __device__ __forceinline__ void window_group(const DecodeArgs& a, const SeqView& sv, int bh, int b, int hq0, int wblk,
                                              FusedSmem& S, const WinRows& first);
 
-template <int G>
+template <int G, bool SELF>
 __device__ void window_block(const DecodeArgs& a, const SeqView& sv, int bh, int b, int h, int wblk, FusedSmem& S,
                              const WinRows& first) {
-  window_q_group(a, bh, 0, S);
+  window_q_group<SELF>(a, bh, 0, S);
   window_group(a, sv, bh, b, h * 4 * G, wblk, S, first);
 #pragma unroll
   for (int g = 1; g < G; ++g) {
     __syncthreads();                  // shared memory is reused by the next group
     const WinRows again = window_first_rows(a, sv, bh, wblk);
-    window_q_group(a, bh, g, S);
+    window_q_group<SELF>(a, bh, g, S);
     window_group(a, sv, bh, b, h * 4 * G + 4 * g, wblk, S, again);
   }
 }
@@ -1332,7 +1346,7 @@ __device__ inline Tile16<KS> load_tile16(const TileStreams& st, int t0, int koff
 }
 
 // One INT2 split of the one-launch kernel (G head groups of 4 query heads).
-template <int G>
+template <int G, bool SELF>
 __device__ void int2_split16(const DecodeArgs& a, const SeqView& sv, int b, int h, int bh, int split,
                              FusedSmem& S) {
   constexpr int D = 128, WPB = 4;
@@ -1344,7 +1358,6 @@ __device__ void int2_split16(const DecodeArgs& a, const SeqView& sv, int b, int 
   const int jh = c & 3, piece = c >> 3;
   const int grp = KS ? 0 : (c >> 2) & 1;          // head group of the column
   const int set = KS ? (c >> 2) & 1 : 0;          // token set of the column (KS)
-  const bool live = grp < G;                      // the column carries a query head
   const int lo = a.plan.a0, hi = sv.hi;          // INT2 token range (empty in a short sequence)
   const int tile_first = lo >> 6;
   const int ntiles = hi > lo ? ((hi - 1) >> 6) - tile_first + 1 : 0;
@@ -1371,59 +1384,99 @@ __device__ void int2_split16(const DecodeArgs& a, const SeqView& sv, int b, int 
   // first of the 4 tokens (of the tile) whose scores register block tb / tp holds
   auto tok_of = [&](int t) { return KS ? 32 * set + 8 * g + 4 * t : 32 * (t >> 1) + 8 * g + 4 * (t & 1); };
 
-  // q operands of this lane's column, from the record the prologue launch
-  // wrote, loaded after the first tiles.  Operand n of the record's layout
-  // (32 dims: lane group gp, chunk kc) is taken as: plain, n = kc, gp = g;
-  // KS, instruction (wp, h) = n / 2, n % 2 takes lane group 2 (g % 2) + wp / 2,
-  // chunk 2 (wp % 2) + h, zero unless the column's set is the lane's (g / 2).
+  // q operands of this lane's column, in shared memory (every wave has the
+  // same ones; they would otherwise hold NOP x 4 registers through the tile
+  // loop), read per tile.  Operand n (32 dims: lane group gp, chunk kc) is
+  // taken as: plain, n = kc, gp = the lane's group; KS, instruction (wp, h) =
+  // n / 2, n % 2 takes lane group 2 (g % 2) + wp / 2, chunk 2 (wp % 2) + h,
+  // zero unless the column's set is the lane's (g / 2).
   auto hq_of = [&](int gg) { return h * 4 * G + 4 * gg; };   // first query head of group gg
-  auto op_src = [&](int n, int& gp, int& kc) {
+  auto op_src = [&](int n, int lg, int& gp, int& kc) {
     if (KS) {
       const int wp = n >> 1, hh = n & 1;
-      gp = 2 * (g & 1) + (wp >> 1);
+      gp = 2 * (lg & 1) + (wp >> 1);
       kc = 2 * (wp & 1) + hh;
     } else {
-      gp = g;
+      gp = lg;
       kc = n;
     }
   };
-  const bool op_live = live && (!KS || set == (g >> 1));
   const float pm = (float)piece;                  // 1 in the lanes of low pieces
-  h8 qop[NOP];
   float qsum = 0.0f;
   int eq = 0;
+  float vmax;
+  Tile16<KS> r[kDepth16];
+  if constexpr (SELF) {
+    // The block rotates q itself.  The V scale maximum as it stood before
+    // this launch (a step's append folds its token's scale in at the end of
+    // the launch: every INT2 token was appended earlier), the rotation's loads
+    // (R_K rows, the raw q), the first tile (the appended token lies at least
+    // a tile past the INT2 range), the rotation and each head group's
+    // operands while that tile is in flight, then the other tiles.
+    vmax = a.v.smax[bh];
+    QRotLoads ql = q_rotation_loads(a, b, hq_of(0));
+    r[0] = load_tile16<KS>(st, tile_t0(min(ti0, t_last)), koff, voff, moff);
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-  for (int n = 0; n < NOP; ++n) qop[n] = h8{0, 0, 0, 0, 0, 0, 0, 0};
-  // q first (the prologue launch wrote it: it comes back from cache ahead of
-  // the tiles, and the loads return in issue order), so the first tile's work
-  // waits for q and that tile only, not for the tiles behind it
-  if (live) {
+    for (int gg = 0; gg < G; ++gg) {
+      if (gg == 1) {                              // group 1's raw q (R_K rows as for group 0)
+        const uint16_t* qb = a.q + ((size_t)b * a.Hq + hq_of(1)) * D;
+        ql.q0 = bf16_to_f32(qb[threadIdx.x]);
+        ql.q1 = bf16_to_f32(qb[threadIdx.x + 256]);
+        __syncthreads();                          // group 0's operands are written
+      }
+      q_rotation_finish(a, ql, S);                // S.qs, S.qsum, S.qeq of group gg
+      if (grp == gg) {
+        qsum = S.qsum[jh];
+        eq = S.qeq[jh];
+      }
+      for (int e = threadIdx.x; e < NOP * 64; e += 64 * WPB) {
+        const int n = e >> 6, l = e & 63, lc = l & 15, lg = l >> 4;
+        if ((KS ? 0 : (lc >> 2) & 1) != gg) continue;
+        u4 w = {0u, 0u, 0u, 0u};
+        if (!KS || ((lc >> 2) & 1) == (lg >> 1)) {
+          int gp, kc;
+          op_src(n, lg, gp, kc);
+#pragma unroll
+          for (int d = 0; d < 4; ++d) w[d] = q_operand16_pair(S, lc & 3, gp, lc >> 3, kc, d);
+        }
+        S.qops[n][l] = w;
+      }
+    }
+#pragma unroll
+    for (int k = 1; k < kDepth16; ++k) {
+      r[k] = load_tile16<KS>(st, tile_t0(min(ti0 + k * WPB, t_last)), koff, voff, moff);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  } else {
+    // q from the record the prologue launch wrote, first: it comes back from
+    // cache ahead of the tiles, and the loads return in issue order, so the
+    // first tile's work waits for q and that tile only
+    h8 qop[NOP];
+#pragma unroll
+    for (int n = 0; n < NOP; ++n) qop[n] = h8{0, 0, 0, 0, 0, 0, 0, 0};
     const __amdgpu_buffer_rsrc_t qr = plane_rsrc(a.qpub + (size_t)(bh * G + grp) * kQPub, kQPub * 4);
-    if (op_live && wave == 0) {
+    if ((!KS || set == (g >> 1)) && wave == 0) {
 #pragma unroll
       for (int n = 0; n < NOP; ++n) {
         int gp, kc;
-        op_src(n, gp, kc);
+        op_src(n, g, gp, kc);
         const int vb = (kQPub16 + 16 * ((piece * 4 + gp) * 4 + jh) + 4 * kc) * 4;
         qop[n] = __builtin_bit_cast(h8, __builtin_amdgcn_raw_buffer_load_b128(qr, vb, 0, 0));
       }
     }
     qsum = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(qr, (512 + jh) * 4, 0, 0));
     eq = (int)__builtin_amdgcn_raw_buffer_load_b32(qr, (516 + jh) * 4, 0, 0);
-  }
-  const float vmax = a.v.smax[bh];
-  Tile16<KS> r[kDepth16];
+    vmax = a.v.smax[bh];
 #pragma unroll
-  for (int k = 0; k < kDepth16; ++k) {
-    r[k] = load_tile16<KS>(st, tile_t0(min(ti0 + k * WPB, t_last)), koff, voff, moff);
-    __builtin_amdgcn_sched_barrier(0);
-  }
-  // the operands wait in shared memory (every wave of the block has the same
-  // ones; wave 0 writes them) and are read per tile: they would otherwise hold
-  // NOP x 4 registers through the tile loop
-  if (wave == 0) {
+    for (int k = 0; k < kDepth16; ++k) {
+      r[k] = load_tile16<KS>(st, tile_t0(min(ti0 + k * WPB, t_last)), koff, voff, moff);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    if (wave == 0) {
 #pragma unroll
-    for (int n = 0; n < NOP; ++n) S.qops[n][lane] = __builtin_bit_cast(u4, qop[n]);
+      for (int n = 0; n < NOP; ++n) S.qops[n][lane] = __builtin_bit_cast(u4, qop[n]);
+    }
   }
   __syncthreads();
   const u4* qop_lds = &S.qops[0][lane];
@@ -1672,10 +1725,42 @@ __device__ void int2_split16(const DecodeArgs& a, const SeqView& sv, int b, int 
   }
 }
 
-// The one-launch decode kernel of head_dim 128.  G: head groups of 4 query
-// heads per kv head (G = Hq / Hkv / 4); the INT2 splits serve every group in
-// one pass over the tiles (int2_split16).
-template <int WPB, int G, bool ONE>
+// Window role.  SELF: in a decode step the block whose chunk holds the
+// appended token (the last window position of the sequence) first appends it
+// to K and V with the one-token append's code (R_K and R_V rows and both
+// inputs in one round trip; the window rows with device-scope stores; the V
+// scale goes to a pending slot, which the merging block folds into the
+// running maximum), then loads its rows.  Every other window block issues its
+// first pass's rows first thing.
+template <int G, bool SELF>
+__device__ __forceinline__ void window_role(const DecodeArgs& a, const SeqView& sv, int bh, int b, int h, int wblk,
+                                            FusedSmem& S) {
+  if constexpr (SELF) {
+    const int first = wblk * sv.win.chunk;
+    const bool newest = a.app_blocks > 0 && window_len(sv) - 1 >= first && window_len(sv) - 1 < first + sv.win.chunk;
+    if (newest) {
+      const int2 tr = append_range(a.app, b);
+      const AppendOneLoads kl = append_one_loads(a.app, bh, false, tr.x, tr.x);
+      const AppendOneLoads vl = append_one_loads(a.app, bh, true, tr.x, tr.x);
+      append_one_finish<true>(a.app, bh, false, tr.x, tr.x, tr.y, kl, S.scratch, S.scratch + 128);
+      __syncthreads();
+      append_one_finish<true>(a.app, bh, true, tr.x, tr.x, tr.y, vl, S.scratch, S.scratch + 128);
+      __builtin_amdgcn_s_waitcnt(0);            // the rows are written before any thread reads them
+      __syncthreads();
+    }
+  }
+  const WinRows rows = window_first_rows(a, sv, bh, wblk);
+  window_block<G, SELF>(a, sv, bh, b, h, wblk, S, rows);
+}
+
+// The attention launch of head_dim 128.  G: head groups of 4 query heads per
+// kv head (G = Hq / Hkv / 4); the INT2 splits serve every group in one pass
+// over the tiles (int2_split16).  SELF: the launch is the whole call: every
+// block rotates its q itself and a step's token is appended by the window
+// block that holds it.  Else decode_prologue_kernel ran first (q records, the
+// append).  No block waits for another; the last block of a (sequence, kv
+// head) to finish merges.
+template <int WPB, int G, bool ONE, bool SELF>
 __global__ __launch_bounds__(64 * WPB)
 __attribute__((amdgpu_waves_per_eu(kMfmaWavesPerEu, kMfmaWavesPerEu)))
 void decode_mfma_kernel(DecodeArgs a) {
@@ -1690,11 +1775,10 @@ void decode_mfma_kernel(DecodeArgs a) {
     // ends at about the same time.
     const int wblk = y - 1;
     if (wblk >= 0 && wblk < a.win_blocks) {
-      const WinRows rows = window_first_rows(a, sv, bh, wblk);
-      window_block<G>(a, sv, bh, b, h, wblk, S, rows);
+      window_role<G, SELF>(a, sv, bh, b, h, wblk, S);
       __syncthreads();                  // shared memory is reused below
     }
-    int2_split16<G>(a, sv, b, h, bh, y, S);
+    int2_split16<G, SELF>(a, sv, b, h, bh, y, S);
     finish_block<G>(a, bh, S);
     return;
   }
@@ -1703,19 +1787,19 @@ void decode_mfma_kernel(DecodeArgs a) {
   // compute units first).
   const int lead = a.int2_lead;
   if (y >= lead && y < lead + a.win_blocks) {
-    const WinRows rows = window_first_rows(a, sv, bh, y - lead);
-    window_block<G>(a, sv, bh, b, h, y - lead, S, rows);
+    window_role<G, SELF>(a, sv, bh, b, h, y - lead, S);
     finish_block<G>(a, bh, S);
     return;
   }
-  int2_split16<G>(a, sv, b, h, bh, y < lead ? y : y - a.win_blocks, S);
+  int2_split16<G, SELF>(a, sv, b, h, bh, y < lead ? y : y - a.win_blocks, S);
   finish_block<G>(a, bh, S);
 }
 
-// The first launch of a decode call at head_dim 128: blocks y < G rotate head
-// group y's q and write its record (fp32 q, sums, exponents, the fp16 operand
-// pieces); blocks G and G + 1 append the step's token (K, V).  The attention
-// launch that follows in stream order reads both and waits for nothing.
+// The first launch of a decode call at head_dim 128 when the attention launch
+// does not rotate q itself: blocks y < G rotate head group y's q and write its
+// record (fp32 q, sums, exponents, the fp16 operand pieces); blocks G and G +
+// 1 append the step's token (K, V).  The attention launch that follows in
+// stream order reads both and waits for nothing.
 template <int G>
 __global__ __launch_bounds__(256) void decode_prologue_kernel(DecodeArgs a) {
   __shared__ FusedSmem S;
@@ -2417,8 +2501,8 @@ hipError_t launch_decode_valu(const DecodeArgs& a, int B, hipStream_t s) {
 int decode_mfma_resident_blocks(int device, int G) {
   int per_cu = 0, cus = 0;
   const hipError_t e =
-      G == 2 ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, decode_mfma_kernel<4, 2, false>, 256, 0)
-             : hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, decode_mfma_kernel<4, 1, false>, 256, 0);
+      G == 2 ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, decode_mfma_kernel<4, 2, false, false>, 256, 0)
+             : hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, decode_mfma_kernel<4, 1, false, false>, 256, 0);
   if (e != hipSuccess || per_cu < 1) per_cu = 1;
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, device) != hipSuccess || cus < 1) cus = 1;
   return per_cu * cus;
@@ -2429,11 +2513,13 @@ hipError_t launch_decode_mfma(const DecodeArgs& a, int B, int waves_per_block, h
   dim3 grid((unsigned)(B * a.Hkv), (unsigned)(a.one_round ? a.plan.splits : a.plan.splits + a.win_blocks));
   auto launch = [&](auto kernel) { hipLaunchKernelGGL(kernel, grid, dim3(256), 0, s, a); };
   if (a.G == 2) {
-    if (a.one_round) launch(decode_mfma_kernel<4, 2, true>);
-    else launch(decode_mfma_kernel<4, 2, false>);
+    if (a.one_round) launch(decode_mfma_kernel<4, 2, true, false>);
+    else if (a.self_rotate) launch(decode_mfma_kernel<4, 2, false, true>);
+    else launch(decode_mfma_kernel<4, 2, false, false>);
   } else {
-    if (a.one_round) launch(decode_mfma_kernel<4, 1, true>);
-    else launch(decode_mfma_kernel<4, 1, false>);
+    if (a.one_round) launch(decode_mfma_kernel<4, 1, true, false>);
+    else if (a.self_rotate) launch(decode_mfma_kernel<4, 1, false, true>);
+    else launch(decode_mfma_kernel<4, 1, false, false>);
   }
   return hipGetLastError();
 }

@@ -85,10 +85,13 @@ struct oscar_kv {
   float* qrot = nullptr;   // [B][Hq][D]
   float* qpub = nullptr;    // [B][Hkv][G][kQPub]
   float* partials = nullptr; // [B][Hq][kMaxSplits][D+2]
-  unsigned* counters = nullptr; // [B][Hkv] blocks finished in the current decode launch
+  unsigned* counters = nullptr; // [B][Hkv] blocks finished and producer steps done in the current
+                                // decode launch (head_dim 128)
+  float* vmax_pending = nullptr;  // [B][Hkv] V scale of the token a head_dim-128 decode step
+                                  // appends, until its launch's merge folds it into smax
   size_t bytes = 0;
   int32_t forced_splits = 0;
-  int32_t decode_impl = 0;
+  int32_t decode_impl = 0;   // oscar_kv_set_decode_impl
   int32_t mfma_waves = 4;
   int resident = 1024;       // matrix-core kernel blocks resident at once on the device
   int one_round = 0;         // one-round launches (test switch): r >= 3 always, with r blocks per
@@ -440,7 +443,7 @@ constexpr int kWideTargetBlocks = 1536;
 constexpr float kOneRoundWinCost = 0.10f;
 
 // INT2 splits per (sequence, kv head): as many blocks as are resident at once
-// in total (measured at the 32k shape, q read from the prologue's records: 6
+// in total (measured at the 32k shape with two tiles in flight per wave: 6
 // splits 82.4 us per launch against 87.9 with 12 and 83.5 with 4 or 5).
 int auto_int2_splits(int BH, int ntiles, int waves, int resident) {
   int s = std::max(1, resident / std::max(1, BH));
@@ -549,7 +552,9 @@ int oscar_kv_create(const oscar_kv_config* cfg, oscar_kv** out) {
   if ((rc = dev_alloc(kv, (void**)&kv->qpub, B * qrecs * kQPub * 4))) return bail(rc);
   if ((rc = dev_alloc(kv, (void**)&kv->partials, B * Hq * kMaxSplits * (D + 2) * 4))) return bail(rc);
   if ((rc = dev_alloc(kv, (void**)&kv->counters, B * Hkv * sizeof(unsigned)))) return bail(rc);
-  if (hipMemset(kv->counters, 0, B * Hkv * sizeof(unsigned)) != hipSuccess)
+  if ((rc = dev_alloc(kv, (void**)&kv->vmax_pending, B * Hkv * sizeof(float)))) return bail(rc);
+  if (hipMemset(kv->counters, 0, B * Hkv * sizeof(unsigned)) != hipSuccess ||
+      hipMemset(kv->vmax_pending, 0, B * Hkv * sizeof(float)) != hipSuccess)
     return bail(fail(OSCAR_ERR_HIP, "clearing the decode counters failed"));
   if (hipDeviceSynchronize() != hipSuccess) return bail(fail(OSCAR_ERR_HIP, "device sync after create failed"));
   kv->resident = decode_mfma_resident_blocks(cfg->device, std::max(1, (int)(Hq / Hkv / 4)));
@@ -616,7 +621,7 @@ bool fast_shape(const oscar_kv* kv) {
   // the matrix-core kernel takes the codes as their integer values (uniform
   // codebook) and addresses one (sequence, kv head)'s code plane with 32-bit
   // buffer offsets: cap * 32 bytes must fit
-  return kv->decode_impl == 0 && c.head_dim == 128 && c.codebook == OSCAR_CODEBOOK_UNIFORM &&
+  return kv->decode_impl != 1 && c.head_dim == 128 && c.codebook == OSCAR_CODEBOOK_UNIFORM &&
          (c.num_q_heads == 4 * c.num_kv_heads || c.num_q_heads == 8 * c.num_kv_heads) &&
          c.k_dtype == OSCAR_KV_INT2 && c.v_dtype == OSCAR_KV_INT2 && (long long)kv->cap * 32 <= INT32_MAX;
 }
@@ -627,7 +632,7 @@ bool fast_shape(const oscar_kv* kv) {
 bool wide_shape(const oscar_kv* kv) {
   const auto& c = kv->cfg;
   const int gq = c.num_q_heads / c.num_kv_heads;
-  return kv->decode_impl == 0 && c.head_dim == 512 && c.codebook == OSCAR_CODEBOOK_UNIFORM &&
+  return kv->decode_impl != 1 && c.head_dim == 512 && c.codebook == OSCAR_CODEBOOK_UNIFORM &&
          (gq == 1 || gq == 2 || gq == 4) &&
          c.k_dtype == OSCAR_KV_INT2 && (long long)kv->cap * (c.v_dtype == OSCAR_KV_BF16 ? 1024 : 128) <= INT32_MAX;
 }
@@ -644,8 +649,9 @@ int check_decode_args(const oscar_kv* kv, int32_t layer, const void* q, void* ou
 
 // Device memory a decode-attention call works in besides the cache and its
 // inputs and outputs: the partial results (m, l, o') of its splits, the
-// per-(sequence, kv head) block counters of the one-launch kernel, the q
-// records its prologue launch writes, the rotated q of the general kernel.
+// per-(sequence, kv head) counters of the head_dim-128 launch, the q records
+// (written by that launch's producer blocks, or by the q rotation launch at
+// head_dim 512), the rotated q of the general kernel.
 // Either the handle's buffers (allocated at create) or the shared static
 // array of the allocation-free call.
 struct Scratch {
@@ -748,8 +754,9 @@ int launch_decode(oscar_kv* kv, int32_t layer, const void* q, void* out, int32_t
   int rc = OSCAR_OK;
   const long pcall = sc.use_static ? -1 : prof_begin(kv, 1, stream);
   if (fast) {
-    // one launch: [append blocks] + bf16 window blocks + INT2 splits, q rotated
-    // in each attention block, merged by the last block of each (sequence, kv head)
+    // bf16 window blocks and INT2 splits in one launch, merged by the last
+    // block of each (sequence, kv head); q records (and a step's append) by a
+    // prologue launch first, or by the launch's own blocks
     const int hp_len = sink_end + (T - rec_begin);
     SegPlan w{};
     if (hp_len > 0) {
@@ -825,10 +832,28 @@ int launch_decode(oscar_kv* kv, int32_t layer, const void* q, void* out, int32_t
     ca.nslots = p.splits + w.splits;
     if ((rc = bind_scratch(kv, sc, batch, ca.nslots, da, ca))) return rc;
     da.comb = ca;
-    // the q records (and the step's append) in a launch of their own first:
-    // the attention launch then reads q at its start without waiting for it
-    HIP_TRY(launch_decode_prologue(da, batch, stream));
-    da.app_blocks = 0;
+    // One launch when every block of it is resident at once: each block
+    // rotates its q itself and the window block that holds a step's token
+    // appends it (a ring of at least a tile keeps that token out of the INT2
+    // tiles the launch reads).  Measured at the 16k shape (256 blocks): 1400
+    // against 1173 tokens/s with the prologue launch, which with the gap
+    // between the two launches costs about 5 us per layer.  With more blocks
+    // than are resident the window blocks run last and the rotation is
+    // repeated in every block: at the 32k shape the one launch measured 73.4
+    // us against 66.6 plus the prologue, no faster; the prologue launch then
+    // writes q records (and appends) first.
+    const long blocks = (long)BH * (one_round ? p.splits : p.splits + w.splits);
+    const bool self = !one_round && kv->decode_impl != 2 && (!app || M >= kTile) &&
+                      (kv->decode_impl == 3 || blocks <= kv->resident);
+    da.self_rotate = self ? 1 : 0;
+    if (self && app) {
+      if (sc.use_static) return fail(OSCAR_ERR_INVALID_ARG, "the allocation-free call does not append");
+      da.app.v.smax = kv->vmax_pending;
+    }
+    if (!self) {
+      HIP_TRY(launch_decode_prologue(da, batch, stream));
+      da.app_blocks = 0;
+    }
     const long pk = sc.use_static ? -1 : prof_begin(kv, 0, stream);
     HIP_TRY(launch_decode_mfma(da, batch, kv->mfma_waves, stream));
     prof_end(kv, 0, pk, stream);
@@ -1079,7 +1104,7 @@ int oscar_kv_set_one_round(oscar_kv* kv, int32_t blocks) {
 
 int oscar_kv_set_decode_impl(oscar_kv* kv, int32_t impl) {
   if (!kv) return fail(OSCAR_ERR_INVALID_ARG, "handle is NULL");
-  if (impl != 0 && impl != 1) return fail(OSCAR_ERR_INVALID_ARG, "impl must be 0 or 1");
+  if (impl < 0 || impl > 3) return fail(OSCAR_ERR_INVALID_ARG, "impl must be 0, 1, 2 or 3");
   kv->decode_impl = impl;
   return OSCAR_OK;
 }

@@ -282,8 +282,13 @@ int oscar_kv_device_bytes(const oscar_kv* kv, size_t* bytes);
  * by the number of 64-token tiles.  Errors: INVALID_ARG. */
 int oscar_kv_set_num_splits(oscar_kv* kv, int32_t num_splits);
 
-/* Select the decode kernel: 0 = automatic (fused MFMA kernel where supported),
- * 1 = the general VALU kernel for every shape.  Errors: INVALID_ARG. */
+/* Select the decode kernel: 0 = automatic (matrix-core kernels where
+ * supported), 1 = the general VALU kernel for every shape.  Test switches of
+ * the head_dim-128 matrix-core path: 2 = always a q-record launch before the
+ * attention launch, 3 = always one launch whose blocks rotate q themselves
+ * (a decode step appends in it when recent_tokens >= 64).  Automatic uses the
+ * one launch when all of its blocks are resident at once.  Errors:
+ * INVALID_ARG. */
 int oscar_kv_set_decode_impl(oscar_kv* kv, int32_t impl);
 
 /* Copy one plane of `layer` to host memory in canonical layout, for all

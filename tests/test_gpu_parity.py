@@ -187,7 +187,7 @@ def _fill(ok, shape, T, rot="haar", extra=8, chunks=None):
     return gc, rk, rv, k, v, mask
 
 
-@pytest.mark.parametrize("impl", [0, 1])
+@pytest.mark.parametrize("impl", [0, 1, 2, 3])
 def test_decode_tiny_identical_cache(ok, impl):
     """Tiny workload: 1 layer, B=1, Hq=4, Hkv=1, D=128, 1024 tokens appended,
     then one decode step with its append; attention vs the oracle over the
@@ -246,10 +246,15 @@ def test_decode_window_edges(ok, T, N, M, gq):
     gc, rk, rv, k, v, mask = _fill(ok, shape, T)
     qb = query(shape, mask)
     want = oracle_on_exported(gc, 0, qb, shape, rk, rv)
-    for impl in (0, 1):
-        e = oracle_err(_decode(ok, gc, 0, qb, impl=impl), want)
+    got = {}
+    for impl in (0, 1, 2, 3):
+        got[impl] = _decode(ok, gc, 0, qb, impl=impl)
+        e = oracle_err(got[impl], want)
         say(f"  impl={impl} rel L2 {e:.3e}")
         assert e <= ATTN_TOL
+    # q records from the prologue launch or q rotated in every block: the same
+    # arithmetic, the same bits
+    np.testing.assert_array_equal(got[2], got[3])
     gc.close()
 
 
@@ -280,6 +285,8 @@ def test_decode_wide_window_edges(ok, T, N, M, gq, vdt):
     (0, 2 ** -12),    # matrix-core kernel: p*s_V enters as fp16 relative to each
                       # split's running max, so splits move its rounding points;
                       # bounded by fp16's half-ulp
+    (2, 2 ** -12),    # the same with q records from a launch of their own
+    (3, 2 ** -12),    # the same with q rotated in every block
 ])
 @pytest.mark.parametrize("gq,D,vdt", [(4, 128, 0), (8, 128, 0), (2, 512, 0), (2, 512, 1)])
 def test_split_invariance(ok, impl, tol, gq, D, vdt):
@@ -398,21 +405,24 @@ def _exports_equal(g1, g2, layer, N, M):
 
 @pytest.mark.parametrize("shape,T0,steps", [
     (Shape(B=2, Hq=4, Hkv=1, N=64, M=256), 1000, 5),           # INT2 range + both windows
-    (Shape(B=1, Hq=8, Hkv=2, N=4, M=20), 60, 70),              # ring wraps, tiles and 8-groups crossed
-    (Shape(B=2, Hq=4, Hkv=2, N=8, M=16), 0, 30),               # from an empty cache: sink, then ring
-    (Shape(B=2, Hq=8, Hkv=2, N=8, M=16), 0, 30),               # the same on the one-launch kernel (fewer tokens than N first)
-    (Shape(B=1, Hq=4, Hkv=1, N=0, M=1), 130, 3),               # window = the new token only
+    (Shape(B=1, Hq=8, Hkv=2, N=4, M=68), 60, 80),              # ring wraps, tiles and 8-groups crossed
+    (Shape(B=2, Hq=8, Hkv=2, N=8, M=64), 0, 90),               # from an empty cache: sink, ring, INT2 range
+    (Shape(B=1, Hq=16, Hkv=2, N=4, M=64), 0, 80),              # the same with two head groups per kv head
+    (Shape(B=3, Hq=12, Hkv=3, N=16, M=100), 400, 5),           # 9 (sequence, kv head) pairs: blocks of one on several XCDs
     (Shape(B=1, Hq=4, Hkv=1, N=64, M=256), 300, 4),            # every token still bf16
-    (Shape(B=2, Hq=16, Hkv=2, N=8, M=40), 700, 6),             # GQA 8: two head groups per kv head
-    (Shape(B=1, Hq=8, Hkv=1, N=3, M=5), 66, 40),               # GQA 8, ring wraps, tile edges crossed
+    (Shape(B=2, Hq=16, Hkv=2, N=8, M=64), 700, 6),             # GQA 8: two head groups per kv head
+    (Shape(B=2, Hq=4, Hkv=2, N=8, M=16), 0, 30),               # ring under a tile: the append in the q-record launch
+    (Shape(B=1, Hq=4, Hkv=1, N=0, M=1), 130, 3),               # window = the new token only (append in the q-record launch)
+    (Shape(B=1, Hq=8, Hkv=1, N=3, M=5), 66, 40),               # GQA 8, ring wraps, tile edges crossed (the same)
     (Shape(B=2, Hq=4, Hkv=2, D=512, N=8, M=16), 0, 40),        # head_dim 512 from an empty cache, ring wraps
     (Shape(B=1, Hq=4, Hkv=2, D=512, N=8, M=16, v_dtype=1), 60, 10),  # head_dim 512, V kept bf16
 ])
 def test_decode_step_equals_append_then_decode(ok, shape, T0, steps):
-    """The fused step (append and attention in one launch) against the two
-    separate calls on a twin cache: identical stored cache bit for bit, output
-    within the matrix-core kernel's fp16 half-ulp, and within the attention bar
-    of the oracle over the exported cache."""
+    """The step (at head_dim 128 and these sizes: one launch that also appends,
+    with a ring of at least a tile; else the q-record launch appends) against
+    the two separate calls on a twin cache: identical stored cache bit for
+    bit, output within the matrix-core kernel's fp16 half-ulp, and within the
+    attention bar of the oracle over the exported cache."""
     say(f"[decode step] {shape} T0={T0} steps={steps}")
     rk, rv = make_rotations(shape, "haar")
     k, v, mask = inputs(shape, T0 + steps)
@@ -440,6 +450,47 @@ def test_decode_step_equals_append_then_decode(ok, shape, T0, steps):
     say(f"  worst step-vs-separate rel L2 {worst:.2e}")
     g1.close()
     g2.close()
+
+
+@pytest.mark.parametrize("shape,T0,steps", [
+    (Shape(B=2, Hq=8, Hkv=2, N=8, M=64), 0, 90),               # sink, ring, its wrap, INT2 range
+    (Shape(B=3, Hq=24, Hkv=3, N=16, M=100), 300, 6),           # two head groups, 9 (sequence, kv head) pairs
+])
+def test_decode_step_both_launch_forms(ok, shape, T0, steps):
+    """The step as one launch (q rotated in every block, the append by the
+    window block holding the token) against the q-record launch followed by
+    the attention launch, on twin caches: the stored caches identical bit for
+    bit (V scales included, through the next steps' outputs), outputs within
+    the fp16 half-ulp (the one launch scales V by the running maximum from
+    before its own token)."""
+    say(f"[decode step forms] {shape} T0={T0} steps={steps}")
+    rk, rv = make_rotations(shape, "haar")
+    k, v, mask = inputs(shape, T0 + steps)
+    g3 = gpu_cache(ok, shape, rk, rv, T0 + steps + 3)
+    g2 = gpu_cache(ok, shape, rk, rv, T0 + steps + 3)
+    g3.set_decode_impl(3)
+    g2.set_decode_impl(2)
+    if T0:
+        for g in (g2, g3):
+            g.append(0, dev(k[:, :T0]), dev(v[:, :T0]))
+    worst = 0.0
+    for i in range(steps):
+        t = T0 + i
+        qb = query(shape, mask, step=i)
+        o3 = _step(ok, g3, 0, k[:, t:t + 1], v[:, t:t + 1], qb)
+        o2 = _step(ok, g2, 0, k[:, t:t + 1], v[:, t:t + 1], qb)
+        e = rel_l2(o3, o2)
+        worst = max(worst, e)
+        assert e <= 2 ** -12, (i, e)
+        if i == steps - 1 or i % 32 == 0:
+            _exports_equal(g3, g2, 0, shape.N, shape.M)
+            assert oracle_err(o3, oracle_on_exported(g3, 0, qb, shape, rk, rv)) <= ATTN_TOL
+    # decode attention after the steps: the same running V maximum on both
+    qb = query(shape, mask, step=steps)
+    np.testing.assert_array_equal(_decode(ok, g3, 0, qb, impl=2), _decode(ok, g2, 0, qb, impl=2))
+    say(f"  worst one-launch vs two-launch rel L2 {worst:.2e}")
+    g2.close()
+    g3.close()
 
 
 def test_decode_step_exact_rotation_bitexact(ok):

@@ -91,6 +91,8 @@ def _fill_seqs(gc, oc, shape, lengths, k, v, chunk=None):
 # and a tile or 8-token group boundary crossed at different places
 CASES = [
     (Shape(B=5, Hq=4, Hkv=1, D=128, N=8, M=16), [3, 25, 300, 64, 129]),          # 4 query heads per kv head
+    (Shape(B=5, Hq=4, Hkv=1, D=128, N=8, M=64), [3, 25, 300, 64, 129]),          # the step's append in the attention launch
+    (Shape(B=4, Hq=16, Hkv=2, D=128, N=8, M=70), [49, 700, 5, 200]),             # the same, two head groups
     (Shape(B=4, Hq=16, Hkv=2, D=128, N=8, M=40), [49, 700, 5, 200]),             # 8 query heads per kv head
     (Shape(B=3, Hq=4, Hkv=2, D=128, N=4, M=20), [25, 1, 190]),                   # 2 per kv head: general kernel
     (Shape(B=3, Hq=4, Hkv=2, D=512, N=16, M=40), [57, 400, 9]),                  # head_dim 512

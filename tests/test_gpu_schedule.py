@@ -58,13 +58,15 @@ def test_one_round_decode(ok, gq, T, N, M, R):
     gc.close()
 
 
-@pytest.mark.parametrize("gq,R", [(4, 3), (4, 6), (8, 5), (4, 16)])
-def test_one_round_decode_steps(ok, gq, R):
-    """Decode steps (the append in the prologue launch) from an empty cache
-    through the sink, the ring's wrap and into the INT2 range: the stored
-    cache bit-equal to a twin filled by separate calls, outputs within the bar."""
-    shape = Shape(B=2, Hq=2 * gq, Hkv=2, N=8, M=24)
-    say(f"[one round steps] gq={gq} R={R}")
+@pytest.mark.parametrize("gq,R,M", [(4, 3, 24), (4, 6, 64), (8, 5, 64), (4, 16, 24), (8, 3, 70)])
+def test_one_round_decode_steps(ok, gq, R, M):
+    """Decode steps from an empty cache through the sink, the ring's wrap and
+    into the INT2 range (a ring of at least a tile: the append by producer
+    blocks of the attention launch; under a tile: in a launch of its own): the
+    stored cache bit-equal to a twin filled by separate calls, outputs within
+    the bar."""
+    shape = Shape(B=2, Hq=2 * gq, Hkv=2, N=8, M=M)
+    say(f"[one round steps] gq={gq} R={R} M={M}")
     rk, rv = make_rotations(shape, "haar")
     steps = 100
     k, v, mask = inputs(shape, steps)
