@@ -400,10 +400,10 @@ def main():
     # dominant kernel: the decode attention launch (INT2 splits on matrix cores,
     # bf16 window blocks; at head_dim 128 also the last-block combine); it reads
     # every KV byte of the call.  Its duration comes from the HIP events the
-    # library records around it on its launch stream (at head_dim 128 the
-    # launch also writes the q records and appends the step's token; at
-    # head_dim 512 the q-record launch before it and the merge launch after it
-    # are outside them and in the whole-job rate)
+    # library records around it on its launch stream (a q-record launch
+    # before it, when there is one, and at head_dim 512 the merge launch after
+    # it, are outside them and in the whole-job rate; a one-launch call at
+    # head_dim 128 also rotates q and appends inside it)
     roof = None
     if k_n > 0:
         avg_ms = k_ms / k_n
