@@ -457,6 +457,37 @@ __device__ inline void rot_rows_cols2(const float* xs, int xstride, const float*
   }
 }
 
+// N rows of R (e0 .. e0 + N - 1, row length D) at columns col and col + 1,
+// one 8-byte load per row, all issued together: a wave's share of a product
+// whose reduction over e is split N rows per wave.
+template <int N>
+struct RowsN {
+  float2 r[N];
+};
+
+template <int N>
+__device__ inline RowsN<N> load_rows(const float* R, int D, int e0, int col) {
+  RowsN<N> rr;
+  const float* Rp = R + (size_t)e0 * D + col;
+#pragma unroll
+  for (int e = 0; e < N; ++e) rr.r[e] = *reinterpret_cast<const float2*>(Rp + (size_t)e * D);
+  return rr;
+}
+
+// acc[j][c] += xs[j * xstride + e0 + e] * rows.r[e] (column c), e ascending
+// (fused multiply-adds)
+template <int NX, int N>
+__device__ inline void fma_rows(const float* xs, int xstride, int e0, const RowsN<N>& rr, float (&acc)[NX][2]) {
+#pragma unroll
+  for (int e = 0; e < N; ++e)
+#pragma unroll
+    for (int j = 0; j < NX; ++j) {
+      const float x = xs[j * xstride + e0 + e];
+      acc[j][0] = __builtin_fmaf(x, rr.r[e].x, acc[j][0]);
+      acc[j][1] = __builtin_fmaf(x, rr.r[e].y, acc[j][1]);
+    }
+}
+
 // One-token append, head_dim 512, split by quantization group: the block
 // computes dims [128 s, 128 s + 128) (group s) of one token row of plane K
 // (isv = false) or V for one (sequence, kv head).  The rotation is the one of

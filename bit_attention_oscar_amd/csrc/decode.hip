@@ -576,6 +576,91 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
   combine_group<D, false, CC>(a, (int)blockIdx.x, (int)blockIdx.y, h0, min(h0 + HB, a.Hq / a.Hkv));
 }
 
+// Merge and V un-rotation at head_dim 512: block (sequence x kv head, column
+// chunk cc of 128, query head j of the kv head), 8 waves, one memory round
+// trip for every load: wave w's R_Vᵀ rows [64 w, 64 w + 64) at the block's
+// columns 2 lane, 2 lane + 1; wave 0's (m, l) of every slot (lane s: slots s,
+// s + 64, ...); and o': thread t (t % 256 = dim pair p, t / 256 = slot group
+// g) loads dims 2p, 2p + 1 of slots [32 g, 32 g + 32) of each round of 64
+// slots.  The weighted sums of the two slot groups are added in group order,
+// the 8 waves' partial products in wave order.
+__global__ __launch_bounds__(512) void combine_wide_kernel(CombineArgs a) {
+  constexpr int D = 512, NC = 128, WAVES = 8, RW = D / WAVES, SG = 512 / 256, SU = 64 / SG;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int bh = (int)blockIdx.x, c0 = (int)blockIdx.y * NC, j = (int)blockIdx.z;
+  const int b = bh / a.Hkv, kvh = bh - (bh / a.Hkv) * a.Hkv;
+  const int Gq = a.Hq / a.Hkv, hq = kvh * Gq + j, ns = a.nslots;
+  const float* P = a.partials + ((size_t)b * a.Hq + hq) * a.pstride * (D + 2);
+  __shared__ float wsl[kMaxSplits + 64];  // m, then the slot weight
+  __shared__ float wll[kMaxSplits + 64];  // l
+  __shared__ float linv;
+  __shared__ float os[SG][D];
+  __shared__ float part[WAVES][NC];
+  const RowsN<RW> rr = load_rows<RW>(a.rvT, D, RW * wave, c0 + 2 * lane);
+  const int pr = tid & 255, grp = tid >> 8;
+  float o0 = 0.0f, o1 = 0.0f;
+  for (int s0 = 0; s0 < ns; s0 += 64) {
+    float2 v[SU];
+#pragma unroll
+    for (int u = 0; u < SU; ++u)
+      v[u] = ld_partial2(P + (size_t)min(s0 + SU * grp + u, ns - 1) * (D + 2) + 2 * pr);
+    if (s0 == 0) {
+      if (wave == 0) {
+        // slot weights relative to the maximum m, and 1 / l (lane s: slots
+        // s, s + 64, ...; one round of loads up to 64 slots)
+        float mx = NEG_INF;
+        for (int i = 0; 64 * i < ns; ++i) {
+          const int sl = lane + 64 * i;
+          const float2 t = ld_partial2(P + (size_t)min(sl, ns - 1) * (D + 2) + D);
+          wsl[sl] = t.x;
+          wll[sl] = t.y;
+          if (sl < ns) mx = fmaxf(mx, t.x);
+        }
+        const float M = wmax(mx);
+        float L = 0.0f;
+        for (int i = 0; 64 * i < ns; ++i) {
+          const int sl = lane + 64 * i;
+          const float m = wsl[sl];
+          const float w = (sl >= ns || m == NEG_INF) ? 0.0f : exp2f(m - M);
+          wsl[sl] = w;
+          L = __builtin_fmaf(wll[sl], w, L);
+        }
+        L = wsum(L);
+        if (lane == 0) linv = 1.0f / L;
+      }
+      __syncthreads();
+    }
+#pragma unroll
+    for (int u = 0; u < SU; ++u) {
+      const int sl = s0 + SU * grp + u;
+      const float w = sl < ns ? wsl[sl] : 0.0f;
+      o0 = __builtin_fmaf(v[u].x, w, o0);
+      o1 = __builtin_fmaf(v[u].y, w, o1);
+    }
+  }
+  os[grp][2 * pr] = o0;
+  os[grp][2 * pr + 1] = o1;
+  __syncthreads();
+  if (tid < D) os[0][tid] = (os[0][tid] + os[1][tid]) * linv;
+  __syncthreads();
+  const size_t orow = ((size_t)b * a.Hq + hq) * D;
+  if (a.absorb_v) {                       // o' in the V-rotated basis, this block's columns
+    if (tid < NC) store_out(a, orow + c0 + tid, os[0][c0 + tid]);
+    return;
+  }
+  float acc[1][2] = {{0.0f, 0.0f}};
+  fma_rows<1, RW>(&os[0][0], 0, RW * wave, rr, acc);
+  part[wave][2 * lane] = acc[0][0];
+  part[wave][2 * lane + 1] = acc[0][1];
+  __syncthreads();
+  if (tid < NC) {
+    float v = part[0][tid];
+#pragma unroll
+    for (int w = 1; w < WAVES; ++w) v = v + part[w][tid];
+    store_out(a, orow + c0 + tid, v);
+  }
+}
+
 // Partial results of the matrix-core launch are written with device-scope
 // stores, which complete at the level shared by all XCDs.
 __device__ inline void st_partial(float* p, float v) {
@@ -2562,8 +2647,8 @@ hipError_t launch_combine(const CombineArgs& a, hipStream_t s) {
   if (a.D == 128)
     hipLaunchKernelGGL((combine_kernel<128, 1, kMaxGq>), dim3((unsigned)(a.B * a.Hkv)), dim3(256), 0, s, a);
   else
-    hipLaunchKernelGGL((combine_kernel<512, 4, 1>), dim3((unsigned)(a.B * a.Hkv), 4, (unsigned)(a.Hq / a.Hkv)),
-                       dim3(256), 0, s, a);
+    hipLaunchKernelGGL(combine_wide_kernel, dim3((unsigned)(a.B * a.Hkv), 4, (unsigned)(a.Hq / a.Hkv)),
+                       dim3(512), 0, s, a);
   return hipGetLastError();
 }
 
