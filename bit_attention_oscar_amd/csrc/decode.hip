@@ -1496,8 +1496,8 @@ __device__ void int2_split16(const DecodeArgs& a, const SeqView& sv, int b, int 
     // this launch (a step's append folds its token's scale in at the end of
     // the launch: every INT2 token was appended earlier), the rotation's loads
     // (R_K rows, the raw q), the first tile (the appended token lies at least
-    // a tile past the INT2 range), the rotation and each head group's
-    // operands while that tile is in flight, then the other tiles.
+    // a tile past the INT2 range), the rotation while that tile is in flight,
+    // the other tiles, then each head group's operands.
     vmax = a.v.smax[bh];
     QRotLoads ql = q_rotation_loads(a, b, hq_of(0));
     r[0] = load_tile16<KS>(st, tile_t0(min(ti0, t_last)), koff, voff, moff);
@@ -1511,10 +1511,27 @@ __device__ void int2_split16(const DecodeArgs& a, const SeqView& sv, int b, int 
         __syncthreads();                          // group 0's operands are written
       }
       q_rotation_finish(a, ql, S);                // S.qs, S.qsum, S.qeq of group gg
+      if (gg == G - 1) {
+        // the R rows are dead: the other tiles go out before the operands
+#pragma unroll
+        for (int k = 1; k < kDepth16; ++k) {
+          r[k] = load_tile16<KS>(st, tile_t0(min(ti0 + k * WPB, t_last)), koff, voff, moff);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
       if (grp == gg) {
         qsum = S.qsum[jh];
         eq = S.qeq[jh];
       }
+      // the group's 512 distinct operand words (the record's layout: word
+      // 16 ((piece 4 + lane group) 4 + head) + 4 chunk + d), each formed once,
+      // then every lane's copies of them
+      uint32_t* stage = reinterpret_cast<uint32_t*>(S.scratch);   // free after the rotation
+      for (int i = threadIdx.x; i < 512; i += 64 * WPB) {
+        const int v = i >> 4, wd = i & 15;
+        stage[i] = q_operand16_pair(S, v & 3, (v >> 2) & 3, v >> 4, wd >> 2, wd & 3);
+      }
+      __syncthreads();
       for (int e = threadIdx.x; e < NOP * 64; e += 64 * WPB) {
         const int n = e >> 6, l = e & 63, lc = l & 15, lg = l >> 4;
         if ((KS ? 0 : (lc >> 2) & 1) != gg) continue;
@@ -1522,16 +1539,10 @@ __device__ void int2_split16(const DecodeArgs& a, const SeqView& sv, int b, int 
         if (!KS || ((lc >> 2) & 1) == (lg >> 1)) {
           int gp, kc;
           op_src(n, lg, gp, kc);
-#pragma unroll
-          for (int d = 0; d < 4; ++d) w[d] = q_operand16_pair(S, lc & 3, gp, lc >> 3, kc, d);
+          w = *reinterpret_cast<const u4*>(stage + 16 * (((lc >> 3) * 4 + gp) * 4 + (lc & 3)) + 4 * kc);
         }
         S.qops[n][l] = w;
       }
-    }
-#pragma unroll
-    for (int k = 1; k < kDepth16; ++k) {
-      r[k] = load_tile16<KS>(st, tile_t0(min(ti0 + k * WPB, t_last)), koff, voff, moff);
-      __builtin_amdgcn_sched_barrier(0);
     }
   } else {
     // q from the record the prologue launch wrote, first: it comes back from
