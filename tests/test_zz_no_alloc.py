@@ -36,20 +36,23 @@ def _both(gc, qb):
     return outs
 
 
-@pytest.mark.parametrize("Hq,Hkv,D,vdt", [
-    (8, 2, 128, 0),      # one-launch matrix-core kernel, 4 query heads per kv head
-    (16, 2, 128, 0),     # two head groups
-    (4, 2, 512, 0),      # head_dim 512
-    (4, 2, 512, 1),      # head_dim 512, V kept bf16
-    (2, 2, 128, 0),      # general kernel
+@pytest.mark.parametrize("Hq,Hkv,D,vdt,impl", [
+    (8, 2, 128, 0, 0),   # matrix-core kernel, 4 query heads per kv head (one launch at these sizes)
+    (16, 2, 128, 0, 0),  # two head groups
+    (8, 2, 128, 0, 2),   # q records in the static array, from a launch of their own
+    (16, 2, 128, 0, 2),  # the same, two head groups
+    (4, 2, 512, 0, 0),   # head_dim 512
+    (4, 2, 512, 1, 0),   # head_dim 512, V kept bf16
+    (2, 2, 128, 0, 0),   # general kernel
 ])
-def test_noalloc_equals_decode_attn(ok, Hq, Hkv, D, vdt):
+def test_noalloc_equals_decode_attn(ok, Hq, Hkv, D, vdt, impl):
     caches = []
     for B, T in ((4, 3000), (2, 500)):
         shape = Shape(B=B, Hq=Hq, Hkv=Hkv, D=D, N=64, M=256, v_dtype=vdt)
         rk, rv = make_rotations(shape, "haar")
         k, v, mask = inputs(shape, T)
         gc = gpu_cache(ok, shape, rk, rv, T)
+        gc.set_decode_impl(impl)
         gc.append(0, dev(k), dev(v))
         caches.append((shape, gc, rk, rv, mask))
     for i in (0, 1, 0):                       # larger, smaller, larger again
@@ -58,7 +61,7 @@ def test_noalloc_equals_decode_attn(ok, Hq, Hkv, D, vdt):
         ref, got = _both(gc, qb)
         assert np.array_equal(got, ref), f"call {i}: differs from oscar_int2_decode_attn"
         e = oracle_err(got, oracle_on_exported(gc, 0, qb, shape, rk, rv))
-        say(f"[noalloc] Hq={Hq} Hkv={Hkv} D={D} v_dtype={vdt} B={shape.B}: identical, rel L2 {e:.3e}")
+        say(f"[noalloc] Hq={Hq} Hkv={Hkv} D={D} v_dtype={vdt} impl={impl} B={shape.B}: identical, rel L2 {e:.3e}")
     for _, gc, *_ in caches:
         gc.close()
 
