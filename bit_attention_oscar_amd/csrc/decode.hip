@@ -869,10 +869,13 @@ __device__ inline void q_operand(const FusedSmem& S, int j, int pp, int w, int k
 // index (b Hkv + h) G + g, kQPub floats:
 //   [0, 512)          fp32 rotated q of the 4 heads, head-major
 //   [512, 516)        per-head sums; [516, 520) per-head exponents eq (int bits)
-//   [kQPubOps, +256)  high pieces of the fp16 matrix-core operands: vector
-//                     4 pp + j holds the 32 values (word w, slot k at 4 w + k)
-//                     of lane group pp, head j (16 words per vector)
+//   [kQPubOps, +256)  head_dim 512 records: high pieces of the fp16 operands
+//                     of the 4x4x4 products: vector 4 pp + j holds the 32
+//                     values (word w, slot k at 4 w + k) of lane group pp,
+//                     head j (16 words per vector)
 //   [kQPubLo, +256)   the low pieces, same order
+//   [kQPub16, +512)   head_dim 128 records: both pieces of the operands of the
+//                     16x16x32 products (publish_q)
 constexpr int kQPubOps = 520;
 constexpr int kQPubLo = kQPubOps + 256;
 constexpr int kQPub16 = kQPubLo + 256;
@@ -908,8 +911,11 @@ __device__ inline uint32_t q_operand16_pair(const FusedSmem& S, int j, int g, in
   return out;
 }
 
-// The q record of one head group, written by a producer block of the decode
-// launch for its attention blocks.
+// The q record of one head group, written by the q-record launch for the
+// attention launch: the fp32 part and the operand pieces of the instruction
+// shape that launch uses (FOUR: the 4x4x4 products of the head_dim-512
+// kernels; else the 16x16x32 products of the head_dim-128 kernel).
+template <bool FOUR>
 __device__ __forceinline__ void publish_q(const DecodeArgs& a, int pidx, FusedSmem& S) {
   float* dst = a.qpub + (size_t)pidx * kQPub;
   const int tid = threadIdx.x;
@@ -918,18 +924,21 @@ __device__ __forceinline__ void publish_q(const DecodeArgs& a, int pidx, FusedSm
     st_partial(dst + 512 + tid, S.qsum[tid]);
     st_partial(dst + 516 + tid, __int_as_float(S.qeq[tid]));
   }
-  if (tid < 256) {                      // one word (two fp16 operands) of each piece per thread
-    uint32_t hw, lw;
-    q_operand_word(S, tid, hw, lw);
-    st_partial(dst + kQPubOps + tid, __uint_as_float(hw));
-    st_partial(dst + kQPubLo + tid, __uint_as_float(lw));
-  }
-  // operands of the 16x16x32 products: vector (piece 4 + g) 4 + j holds
-  // word 4 kc + d = items (2d, 2d + 1) of chunk kc for lane group g, head j
-  for (int i = tid; i < 512; i += blockDim.x) {
-    const int v = i >> 4, wd = i & 15;
-    st_partial(dst + kQPub16 + i,
-               __uint_as_float(q_operand16_pair(S, v & 3, (v >> 2) & 3, v >> 4, wd >> 2, wd & 3)));
+  if constexpr (FOUR) {
+    if (tid < 256) {                    // one word (two fp16 operands) of each piece per thread
+      uint32_t hw, lw;
+      q_operand_word(S, tid, hw, lw);
+      st_partial(dst + kQPubOps + tid, __uint_as_float(hw));
+      st_partial(dst + kQPubLo + tid, __uint_as_float(lw));
+    }
+  } else {
+    // operands of the 16x16x32 products: vector (piece 4 + g) 4 + j holds
+    // word 4 kc + d = items (2d, 2d + 1) of chunk kc for lane group g, head j
+    for (int i = tid; i < 512; i += blockDim.x) {
+      const int v = i >> 4, wd = i & 15;
+      st_partial(dst + kQPub16 + i,
+                 __uint_as_float(q_operand16_pair(S, v & 3, (v >> 2) & 3, v >> 4, wd >> 2, wd & 3)));
+    }
   }
 }
 
@@ -1905,7 +1914,7 @@ __global__ __launch_bounds__(256) void decode_prologue_kernel(DecodeArgs a) {
   if (y < G) {
     const QRotLoads ql = q_rotation_loads(a, b, h * 4 * G + 4 * y);
     q_rotation_finish(a, ql, S);
-    publish_q(a, bh * G + y, S);
+    publish_q<false>(a, bh * G + y, S);
     return;
   }
   const int2 tr = append_range(a.app, b);
@@ -1971,7 +1980,7 @@ __device__ void wide_qrot_block(const DecodeArgs& a, int bh, int s, FusedSmem& S
     }
   }
   __syncthreads();
-  publish_q(a, bh * 4 + s, S);
+  publish_q<true>(a, bh * 4 + s, S);
 }
 
 // Grid: (sequence x kv head, slice).
