@@ -195,21 +195,20 @@ int oscar_int2_decode_attn_noalloc(oscar_kv* kv, int32_t layer, const void* q, v
 /* One decode step of `layer` as serving runs it (a new token's K/V are
  * cached, then its query attends over every cached token, the new one
  * included; Qwen3-4B card "Run": INT2 cache with the fused flash-attention
- * decode).  Same result, arguments and errors as oscar_kv_append(k, v,
- * n_new = 1) followed by oscar_int2_decode_attn(q, out); the stored cache is
- * identical bit for bit.
+ * decode).  Same arguments and errors as oscar_kv_append(k, v, n_new = 1)
+ * followed by oscar_int2_decode_attn(q, out), and the stored cache is
+ * identical bit for bit; the output is the same attention within the
+ * matrix-core kernel's fp16 operand rounding (see below).
  *   k, v: device bf16 [batch][1][Hkv][D]; q, out as in decode_attn.
  * Where the shape has the head_dim 128 matrix-core kernel (4 or 8 query heads
- * per kv head, INT2 K and V) and recent_tokens >= 1, append and attention run
- * in one launch.  The new token is then a bf16 window token: the attention
- * blocks compute its window value from k, v themselves, and of what the
- * append writes they read only bytes whose bits for other tokens it leaves
- * unchanged (a V code tile it shares with older tokens) or a running maximum
- * that only grows (the V scale maximum, which only sets a power-of-two operand
- * scale), so every order of the blocks gives a correct result.  At head_dim
- * 512 (matrix-core path) the append runs in the same launch as the q
- * rotation, before the attention launch.  Other shapes run the two calls'
- * launches in turn. */
+ * per kv head, INT2 K and V) and recent_tokens >= 1: when every block of the
+ * attention launch is resident at once and recent_tokens >= 64, one launch
+ * does it all (the window block holding the new token appends it; the INT2
+ * blocks scale V by the running V-scale maximum from before the token, which
+ * the launch then raises), else a short launch appends and writes the q
+ * records before the attention launch.  At head_dim 512 (matrix-core path)
+ * the append runs in the same launch as the q rotation, before the attention
+ * launch.  Other shapes run the two calls' launches in turn. */
 int oscar_kv_decode_step(oscar_kv* kv, int32_t layer, const void* k, const void* v, const void* q,
                          void* out, int32_t out_dtype, int32_t batch, float softmax_scale,
                          hipStream_t stream);
