@@ -63,8 +63,10 @@ def _fill_layers(gc, shape, data, T0, oc=None):
 
 
 LAYER_SHAPES = [
-    (Shape(L=3, B=2, Hq=8, Hkv=2, N=16, M=48), 700, 5),            # 4 query heads per kv head: one-launch step
+    (Shape(L=3, B=2, Hq=8, Hkv=2, N=16, M=48), 700, 5),            # 4 query heads per kv head (step: q-record launch appends)
+    (Shape(L=3, B=2, Hq=8, Hkv=2, N=16, M=64), 700, 5),            # the step in one launch (ring of a tile)
     (Shape(L=3, B=1, Hq=16, Hkv=2, N=8, M=40), 500, 4),            # 8 per kv head: two head groups
+    (Shape(L=3, B=1, Hq=16, Hkv=2, N=8, M=72), 500, 4),            # the same, step in one launch
     (Shape(L=3, B=2, Hq=4, Hkv=2, D=512, N=16, M=32), 300, 4),     # head_dim 512, INT2 V
     (Shape(L=3, B=1, Hq=4, Hkv=2, D=512, N=16, M=32, v_dtype=1), 300, 3),  # head_dim 512, V kept bf16
     (Shape(L=3, B=2, Hq=2, Hkv=2, N=16, M=32), 300, 3),            # 1 per kv head: general kernel
@@ -108,7 +110,7 @@ def test_layers_in_bench_order_exact(ok, shape, T0, steps):
     gc.close()
 
 
-@pytest.mark.parametrize("shape,T0,steps", LAYER_SHAPES[:4])
+@pytest.mark.parametrize("shape,T0,steps", LAYER_SHAPES[:-1])
 def test_layers_in_bench_order_haar(ok, shape, T0, steps):
     """The same order with a different Haar rotation per layer: each step's
     output on the first and last layers against the oracle over the exported
