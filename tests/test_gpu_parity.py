@@ -552,11 +552,14 @@ def test_decode_step_other_shapes(ok, shape):
 
 
 @pytest.mark.slow
-def test_full_size_32k_sampled(ok):
+@pytest.mark.parametrize("impl", [0, 3])
+def test_full_size_32k_sampled(ok, impl):
     """The 32k-context benchmark shape (B=16, Hq=32, Hkv=8, D=128, N=64,
     M=256) on one layer, filled on the device, decoded in the benchmark's
-    launch configuration; sequences 0 and 15 checked against the oracle over
-    the exported cache."""
+    launch configuration (impl 0: a q-record launch first at this size) and
+    as one launch whose blocks rotate q themselves (impl 3: more blocks than
+    are resident, the window blocks running last); sequences 0 and 15 checked
+    against the oracle over the exported cache."""
     from bench import fill_layer_device
     shape = Shape(B=16, Hq=32, Hkv=8, D=128, N=64, M=256, outliers="percent")
     T = 32768
@@ -567,9 +570,10 @@ def test_full_size_32k_sampled(ok):
     mask = synth.outlier_mask(shape.D, shape.Hkv, 0, 0, "percent")
     k1, v1, _ = inputs(shape, 1, chunk=99)
     qb = query(shape, mask, step=1)
-    # the fused step (what the benchmark times), then the attention call alone
+    # the step (what the benchmark times), then the attention call alone
+    gc.set_decode_impl(impl)
     got_step = _step(ok, gc, 0, k1, v1, qb)
-    got = _decode(ok, gc, 0, qb)
+    got = _decode(ok, gc, 0, qb, impl=impl)
     say(f"  step vs attention call: {rel_l2(got_step, got):.2e}")
     assert rel_l2(got_step, got) <= 2 ** -12
     for b in (0, 15):
@@ -581,10 +585,12 @@ def test_full_size_32k_sampled(ok):
 
 
 @pytest.mark.slow
-def test_full_size_16k_batch1_sampled(ok):
+@pytest.mark.parametrize("impl", [0, 2])
+def test_full_size_16k_batch1_sampled(ok, impl):
     """The 16k-context batch-1 shape (B=1, Hq=32, Hkv=8, D=128, N=512,
-    M=2048) on one layer, filled on the device, then several fused steps in
-    the benchmark's launch configuration; every head against the oracle over
+    M=2048) on one layer, filled on the device, then several steps in the
+    benchmark's launch configuration (impl 0: one launch at this size) and
+    with a q-record launch first (impl 2); every head against the oracle over
     the exported cache after the last step."""
     from bench import fill_layer_device
     shape = Shape(B=1, Hq=32, Hkv=8, D=128, N=512, M=2048, outliers="percent")
@@ -594,6 +600,7 @@ def test_full_size_16k_batch1_sampled(ok):
     gc = gpu_cache(ok, shape, rk, rv, T + 64)
     fill_layer_device(gc, 0, shape.B, shape.Hkv, shape.D, T, seed=0, dist="normal", outliers="percent")
     mask = synth.outlier_mask(shape.D, shape.Hkv, 0, 0, "percent")
+    gc.set_decode_impl(impl)
     for i in range(4):
         k1, v1, _ = inputs(shape, 1, chunk=90 + i)
         qb = query(shape, mask, step=i)
