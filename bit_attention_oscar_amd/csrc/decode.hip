@@ -15,15 +15,18 @@
 //   decode_valu_kernel  general split-K kernel: any head_dim / GQA / dtype /
 //                       codebook (the only one for the Lloyd-Max codebook),
 //                       per-token precision chosen by position
-//   decode_mfma_kernel  head_dim 128, 4 or 8 query heads per kv head, INT2 K and
-//                       V: one launch per decode step (the step's append, q
-//                       rotation and publication, INT2 splits with 16x16x32 f16
-//                       matrix-core QK^T and PV on the raw codes and two-piece
-//                       q and softmax weights, bf16 window blocks, the merge
-//                       and V un-rotation by the last block)
+//   decode_prologue_kernel, decode_mfma_kernel
+//                       head_dim 128, 4 or 8 query heads per kv head, INT2 K and
+//                       V: INT2 splits with 16x16x32 f16 matrix-core QK^T and
+//                       PV on the raw codes and two-piece q and softmax
+//                       weights, bf16 window blocks, the merge and V
+//                       un-rotation by the last block; q and a decode step's
+//                       append either from the prologue launch or inside the
+//                       attention launch (every block rotating its own q)
 //   wide_qrot_kernel, wide_prologue_kernel, decode_wide_kernel
 //                       head_dim 512 (q records, INT2 K with INT2 or bf16 V)
-//   combine_kernel      log-sum-exp merge of the splits and o = o' @ R_V^T
+//   combine_kernel, combine_wide_kernel
+//                       log-sum-exp merge of the splits and o = o' @ R_V^T
 #include <math.h>
 #include <algorithm>
 #include <type_traits>
@@ -776,7 +779,7 @@ __device__ inline void bf16x8(const uint4 u, float* x) {
   }
 }
 
-// Shared memory of the fused launch; each block role uses its own regions and
+// Shared memory of the head_dim-128 launches; each block role uses its own regions and
 // the scratch area is reused phase by phase.
 struct FusedSmem {
   float qs[4][132];            // rotated q of the block's 4 heads (fp32, x scale*log2 e)
@@ -1328,7 +1331,7 @@ __device__ inline TileStreams tile_streams(const DecodeArgs& a, int bh) {
 
 
 // ---------------------------------------------------------------------------
-// INT2 splits of the one-launch kernel on v_mfma_f32_16x16x32_f16
+// INT2 splits of the head_dim-128 attention kernel on v_mfma_f32_16x16x32_f16
 // ---------------------------------------------------------------------------
 //
 // Lane l = 16 g + c (c = l % 16, g = l / 16).  The columns of both products
@@ -1439,7 +1442,7 @@ __device__ inline Tile16<KS> load_tile16(const TileStreams& st, int t0, int koff
   return r;
 }
 
-// One INT2 split of the one-launch kernel (G head groups of 4 query heads).
+// One INT2 split of the head_dim-128 attention kernel (G head groups of 4 query heads).
 template <int G, bool SELF>
 __device__ void int2_split16(const DecodeArgs& a, const SeqView& sv, int b, int h, int bh, int split,
                              FusedSmem& S) {

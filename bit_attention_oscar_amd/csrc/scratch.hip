@@ -4,7 +4,7 @@
 //
 // Layout of the array (byte offsets):
 //   [0, kCounterBytes)                  per-(sequence, kv head) block counters of the
-//                                       one-launch kernel; zero between calls (the
+//                                       head_dim-128 attention kernel; zero between calls (the
 //                                       last block of a launch resets its counter)
 //   [kCounterBytes, kStaticScratchBytes)   carved per call: q records, rotated q,
 //                                       partial results; nothing there must start at 0
