@@ -80,12 +80,23 @@ __host__ __device__ inline size_t row_offset(int bh, int rows, int t, int D) {
 }
 
 // s_waitcnt operand (gfx9 encoding) that waits for lgkmcnt = 0 only (vmcnt and
-// expcnt at their maxima).  Lanes of one wave exchange values through shared
-// memory with this wait and a wave barrier: the wait completes the wave's own
-// shared-memory writes, the barrier keeps the compiler from moving the reads
-// above it.  A memory fence would do the same but also wait for every vector
-// memory load in flight (the next tiles), which these loops keep outstanding.
+// expcnt at their maxima).
 constexpr int kWaitLds = 0xc07f;
+
+// Lanes of one wave exchange values through shared memory: every lane's
+// earlier shared-memory writes are complete and visible to every lane's later
+// reads.  The wavefront-scope release and acquire fences order the accesses in
+// the language's memory model and keep the compiler from moving them across
+// (at that scope they emit no instruction); the wait completes the wave's own
+// writes, which the hardware then serves in order.  A fence of wider scope
+// would also wait for every vector memory load in flight (the next tiles),
+// which these loops keep outstanding.
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_s_waitcnt(kWaitLds);
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
 
 // ---------------------------------------------------------------------------
 // number formats

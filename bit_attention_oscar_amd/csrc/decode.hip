@@ -1026,8 +1026,7 @@ __device__ __forceinline__ void combine_group4(const CombineArgs& a, int b, int 
       wm[wave * ns + sl] = w;
     }
     L = wsum(lsum);
-    __builtin_amdgcn_s_waitcnt(kWaitLds);  // the wave's weights, written by its own lanes, are read below
-    __builtin_amdgcn_wave_barrier();
+    wave_lds_sync();  // the wave's weights, written by its own lanes, are read below
     for (int s0 = 0; s0 < ns; s0 += SB) {
       float2 x[SB];
 #pragma unroll
@@ -1650,8 +1649,7 @@ __device__ void int2_split16(const DecodeArgs& a, const SeqView& sv, int b, int 
       }
     }
     // the lanes read each other's words: the wave's writes complete first
-    __builtin_amdgcn_s_waitcnt(kWaitLds);
-    __builtin_amdgcn_wave_barrier();
+    wave_lds_sync();
     PHASE_FENCE();
     float u[NB][4];
     float tmax = NEG_INF;
@@ -2360,8 +2358,7 @@ __device__ void wide_split_bf16v(const DecodeArgs& a, int bh, int b, int h, int 
     l += (p[0] + p[1]) + (p[2] + p[3]);
     // weights to this wave's row of shared memory: head j, token 4 blk + rr
     *reinterpret_cast<f4*>(&W.pv[wave][j][4 * blk]) = f4{p[0], p[1], p[2], p[3]};
-    __builtin_amdgcn_s_waitcnt(kWaitLds);   // the wave's own writes are visible to its reads
-    __builtin_amdgcn_wave_barrier();
+    wave_lds_sync();   // the wave's own writes are visible to its reads
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       const int tk = tq + 4 * i;

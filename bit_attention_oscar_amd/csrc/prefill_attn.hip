@@ -162,8 +162,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   // needs no causal mask: every score in it is finite
   const int p_min = T - a.n + i0;
   // per-row q sums in registers (rows of this wave, written by this wave)
-  __builtin_amdgcn_s_waitcnt(kWaitLds);
-  __builtin_amdgcn_wave_barrier();
+  wave_lds_sync();
   float qs[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) qs[i] = S.qsum[16 * wave + 4 * (lane >> 4) + i];
@@ -355,8 +354,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       softmax_tile(std::integral_constant<bool, true>{});
     // each wave reads back only the rows of p s_V it wrote, so no block
     // barrier is needed: an LDS wait and a wave barrier order the lanes
-    __builtin_amdgcn_s_waitcnt(kWaitLds);
-    __builtin_amdgcn_wave_barrier();
+    wave_lds_sync();
     __builtin_amdgcn_s_setprio(1);
     // O += (p s_V) V: A = rows of p s_V (tokens 32 ks + kq .. + 8), B = V^T
 #pragma unroll
@@ -456,12 +454,6 @@ struct alignas(16) PAWideSmem {
   float ks[4][32], kz[4][32], vs[4][32], vz[4][32];   // per group: scale and zero of the tile's tokens
   float qsum[4][16];                                   // per group and row: sum of q over the slice
 };
-
-// the wave's own shared-memory writes are visible to its lanes
-__device__ inline void wave_lds_sync() {
-  __builtin_amdgcn_s_waitcnt(kWaitLds);
-  __builtin_amdgcn_wave_barrier();
-}
 
 // row r of a 16-row block -> query index (clamped to the last query)
 __device__ inline int row_query16(const PrefillAttnArgs& a, int i0, int r) { return min(i0 + r / a.Gq, a.n - 1); }
