@@ -1870,6 +1870,13 @@ template <int WPB, int G, bool ONE, bool SELF>
 __global__ __launch_bounds__(64 * WPB)
 __attribute__((amdgpu_waves_per_eu(kMfmaWavesPerEu, kMfmaWavesPerEu)))
 void decode_mfma_kernel(DecodeArgs a) {
+  // The set-up below reads these arguments one after another (the sequence's
+  // length, then its token sets, then the block's role); naming them first
+  // issues their scalar loads together, one round trip instead of several.
+  asm volatile("" ::"s"(a.Hkv), "s"(a.lens), "s"(a.N), "s"(a.M), "s"(a.T), "s"(a.int2_lead), "s"(a.win_blocks),
+               "s"(a.ring0));
+  asm volatile("" ::"s"(a.plan.a0), "s"(a.plan.b0), "s"(a.plan.a1), "s"(a.plan.b1), "s"(a.plan.chunk),
+               "s"(a.win.a0), "s"(a.win.b0), "s"(a.win.a1), "s"(a.win.b1), "s"(a.win.chunk));
   const int bh = blockIdx.x;
   const int b = bh / a.Hkv, h = bh - (bh / a.Hkv) * a.Hkv;
   __shared__ FusedSmem S;
